@@ -1,0 +1,248 @@
+"""Benchmark of the SparDA decode hot path on one MI355X.
+
+One step = Forecast block scoring of every compressed key window, top-k block
+choice and GQA block-sparse attention over the chosen blocks, for one layer of
+the batched 128K-context decode workload (B=16, T=131072, 32 query / 8 KV
+heads, d=128, 64-token blocks, top-64), inputs resident in HBM. Prints one
+JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Timing: W untimed steps, then K steps between two HIP events on the stream the
+kernels run on, with a device synchronisation on both sides. Input sets rotate
+(3 independent sets) so no step finds its data in the 256 MB last-level cache.
+Per-kernel averages come from their own event-bracketed loops.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode steps/s/layer at 128K ctx (select+sparse attn); % of HBM peak GB/s"
+HBM_PEAK_GBPS = 8000.0
+N_SETS = 3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w) -> dict:
+    """Bytes each kernel must move for one layer-step (bf16 = 2 B)."""
+    e = 2
+    rows = w.B * w.Hkv
+    kc = rows * w.W * w.d * e
+    f = rows * w.d * e
+    q = w.B * w.Hq * w.d * e
+    o = q
+    scores = rows * w.nB * 4
+    idx = rows * w.k * 4
+    kv = 2 * rows * w.k * 64 * w.d * e
+    return {
+        "select_forecast": kc + f + scores,
+        "select_multihead": kc + q + scores,
+        "topk": scores + idx,
+        "attention": kv + q + idx + o,
+        "step": kc + f + scores + (scores + idx) + (kv + q + idx + o),
+    }
+
+
+def time_loop(fn, iters: int, stream) -> float:
+    """Average ms of fn(i) over iters eager launches, HIP events on `stream`."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(iters):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def time_graph(fn, per_graph: int, replays: int) -> float:
+    """Average ms per fn(i) call: fn(0..per_graph-1) captured once in a HIP graph
+    (no host launch cost inside), replayed `replays` times between HIP events on
+    the replay stream."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(per_graph):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            fn(i)
+    stream = torch.cuda.current_stream()
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(replays):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / (replays * per_graph)
+
+
+def cpu_baseline(w, sets, n_rows: int = 4) -> dict:
+    """The fp64 oracle (as is) on a bounded sample: n_rows (sequence, KV head)
+    rows of the first input set, each a full row of the step."""
+    import numpy as np
+    import oracle
+    from tests import parity
+    from threadpoolctl import threadpool_limits
+    s = sets[0]
+    rows = [(0, 0), (5, 3), (10, 6), (15, 7), (3, 1), (12, 4)][:n_rows]
+    prep = []
+    for b, h in rows:
+        prep.append((parity.to_f64(s["F"][b, h]), parity.to_f64(s["Kc"][b, h]),
+                     parity.to_f64(s["Q"][b, h * w.G:(h + 1) * w.G]),
+                     parity.to_f64(s["K"][b, h]), parity.to_f64(s["V"][b, h])))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for F, Kc, Q, K, V in prep:
+            sc = oracle.select_forecast_tile(F, Kc, [w.q_start], w.T, w.scale)
+            idx = oracle.topk_row(sc, w.k)
+            J = oracle.selected_keys(idx, w.q_start)
+            for g in range(w.G):
+                oracle.attend(Q[g, 0], K[J], V[J], w.scale)
+    dt = time.perf_counter() - t0
+    per_row = dt / len(prep)
+    return {"value": 1.0 / (per_row * w.B * w.Hkv), "unit": "steps/s/layer", "cores": 1, "kind": "oracle",
+            "sample": f"{len(prep)} of {w.B * w.Hkv} (sequence, KV head) rows of one step (Forecast select + "
+                      f"top-{w.k} + attention for the {w.G} heads), fp64 numpy, 1 thread, {dt:.2f} s; "
+                      f"scaled to the full step"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-iters", type=int, default=100)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this path is built and timed on a single "
+              f"MI355X; sharding across GPUs is not implemented.", file=sys.stderr)
+        return 2
+
+    import torch
+    import kv_block_selection_amd as kbs
+    import synth.gpu as sg
+    from synth import workloads as wl
+
+    kbs.load()
+    w = wl.C3_DECODE_128K
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating {N_SETS} input sets of {w.name}")
+    sets = []
+    for i in range(N_SETS):
+        wi = wl.scaled(w, seed=w.seed + 1000 * i)
+        s = {n: sg.tensor(wi.recipe(n), wi.shape(n), dev) for n in ("Q", "F", "K", "V")}
+        s["Kc"] = kbs.compress_keys(s["K"])
+        s["scores"] = torch.empty((w.B, w.Hkv, 1, w.nB), dtype=torch.float32, device=dev)
+        s["idx"] = torch.empty((w.B, w.Hkv, 1, w.k), dtype=torch.int32, device=dev)
+        s["out"] = torch.empty_like(s["Q"])
+        sets.append(s)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ws_attn = torch.empty(max(1, kbs.workspace_bytes(kbs.OP_BLOCK_SPARSE_ATTN, w.B, w.Hq, w.Hkv, 1, w.T, w.k)),
+                          dtype=torch.uint8, device=dev)
+    ws_mh = torch.empty(max(1, kbs.workspace_bytes(kbs.OP_SELECT_MULTIHEAD, w.B, w.Hq, w.Hkv, 1, w.T)),
+                        dtype=torch.uint8, device=dev)
+
+    def sel(i):
+        s = sets[i % N_SETS]
+        kbs.select_forecast(s["F"], s["Kc"], w.T, w.q_start, out=s["scores"])
+
+    def sel_mh(i):
+        s = sets[i % N_SETS]
+        kbs.select_multihead(s["Q"], s["Kc"], w.T, w.q_start, out=s["scores"], ws=ws_mh)
+
+    def topk(i):
+        s = sets[i % N_SETS]
+        kbs.topk_blocks(s["scores"], w.k, out=s["idx"])
+
+    def attn(i):
+        s = sets[i % N_SETS]
+        kbs.block_sparse_attn(s["Q"], s["K"], s["V"], s["idx"], w.T, w.q_start, out=s["out"], ws=ws_attn)
+
+    def step(i):
+        sel(i)
+        topk(i)
+        attn(i)
+
+    log("[bench] warmup (eager)")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step_eager = time_loop(step, args.steps, stream)
+    log(f"[bench] eager step {ms_step_eager * 1e3:.1f} us; timing {args.steps} steps through a HIP graph")
+    per_graph = 3 * N_SETS
+    replays = max(1, args.steps // per_graph)
+    ms_step = time_graph(step, per_graph, replays)
+    steps_timed = replays * per_graph
+    log(f"[bench] graph step {ms_step * 1e3:.1f} us; per-kernel graphs")
+    kr = max(1, args.kernel_iters // per_graph)
+    ms = {"select_forecast": time_graph(sel, per_graph, kr), "topk": time_graph(topk, per_graph, kr),
+          "attention": time_graph(attn, per_graph, kr), "select_multihead": time_graph(sel_mh, per_graph, kr)}
+    for i in range(N_SETS):  # leave each set's Forecast scores / idx in place
+        step(i)
+    torch.cuda.synchronize()
+
+    nbytes = algorithmic_bytes(w)
+    gbps = {k: nbytes[k] / (ms[k] * 1e-3) / 1e9 for k in ms}
+    dominant = max(("select_forecast", "attention"), key=lambda k: ms[k])
+    step_gbps = nbytes["step"] / (ms_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_step, 2),
+        "unit": "steps/s/layer",
+        "n_gpus": 1,
+        "steps": steps_timed,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.description, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
+                   "block": w.block, "top_k": w.k, "selector": "forecast", "input_sets_rotated": N_SETS},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(gbps[dominant], 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps[dominant] / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+        "step_hbm_GBps": round(step_gbps, 1),
+        "step_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "ms_per_step_eager": round(ms_step_eager, 5),
+        "kernel_us": {k: round(v * 1e3, 2) for k, v in ms.items()},
+        "kernel_GBps": {k: round(v, 1) for k, v in gbps.items()},
+        "selection_us": {"forecast": round((ms["select_forecast"] + ms["topk"]) * 1e3, 2),
+                         "multihead": round((ms["select_multihead"] + ms["topk"]) * 1e3, 2)},
+        "forecast_vs_multihead_select_speedup": round(ms["select_multihead"] / ms["select_forecast"], 3),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle sample)")
+        result["cpu_baseline"] = cpu_baseline(w, sets)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

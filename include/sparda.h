@@ -1,0 +1,178 @@
+/*
+ * sparda.h - C ABI of libsparda.so: SparDA's decoupled KV-block selection and
+ * block-sparse attention on one AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (cited by page and section):
+ *  [P1] bittide.aicompass.dev - summary post on SparDA and the arXiv abstract of
+ *       "SparDA: Sparse Decoupled Attention for Efficient Long-Context LLM
+ *       Inference" (arXiv:2606.04511).
+ *  [P2] techwalker.com - article on SparDA; sections 一 (problem), 二 (Forecast),
+ *       三 (implementation), 四 (training), 五 (experiments).
+ *  [P3] 10100.com - commentary on arXiv:2606.04511; sections 痛点, 解法.
+ *
+ * Conventions shared by every call
+ *  - Pointers are device pointers unless named host_*. Tensors are dense,
+ *    row-major, 16-byte aligned. Shapes are given in brackets, outermost first.
+ *  - dtype: SPARDA_F32 or SPARDA_BF16 for q/k/v/f/k_cmp/out (block scores are
+ *    always float32, indices int32). Arithmetic accumulates in float32.
+ *  - Supported geometry (v1): d = 128, block = 64, kernel = 32, stride = 16,
+ *    tile = 64, T % 64 == 0, T >= 64, Hq % Hkv == 0, Tq == 1 or Tq % 64 == 0,
+ *    q_start + Tq == T (the chunk ends at the newest token).
+ *    W = (T - kernel)/stride + 1 windows, nB = T/block blocks,
+ *    nTiles = ceil(Tq/tile) query tiles (1 for decode).
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream). Arguments are validated on the host before anything is
+ *    enqueued; on error nothing is launched. Device faults surface at the
+ *    caller's next synchronisation.
+ *  - Ownership: the caller owns every buffer, including the workspace `ws`
+ *    (size from sparda_workspace_bytes); the library keeps no pointer after a
+ *    call returns and allocates no device memory. Buffers must stay alive
+ *    until the enqueued work completes. Calls on different streams that share
+ *    a workspace race; ordering across streams is the caller's (events).
+ *  - Return: SPARDA_OK (0) or an error status; sparda_last_error() then
+ *    holds a message for the calling thread. No C++ exception crosses the ABI.
+ */
+#ifndef SPARDA_H
+#define SPARDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum sparda_status {
+  SPARDA_OK = 0,
+  SPARDA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, inconsistent sizes */
+  SPARDA_ERR_UNSUPPORTED = 2,  /* valid request outside the supported set */
+  SPARDA_ERR_WORKSPACE = 3,    /* ws_bytes smaller than sparda_workspace_bytes */
+  SPARDA_ERR_HIP = 4           /* a HIP runtime call failed at enqueue time */
+};
+
+enum sparda_dtype { SPARDA_F32 = 0, SPARDA_BF16 = 1 };
+
+enum sparda_kv_mode {
+  SPARDA_KV_CACHE = 0,   /* k, v: the layer's cache [B, Hkv, T, d]; blocks read at idx */
+  SPARDA_KV_STAGING = 1  /* k, v: staging [B, Hkv, k, block, d]; slot j holds block idx[.., j] */
+};
+
+enum sparda_op {
+  SPARDA_OP_SELECT_FORECAST = 1,
+  SPARDA_OP_SELECT_MULTIHEAD = 2,
+  SPARDA_OP_BLOCK_SPARSE_ATTN = 3
+};
+
+/*
+ * Step 1 - compressed keys. [P2] 四: at inference the keys are compressed
+ * into windows of kernel 32 and stride 16; the pooling is the arithmetic mean.
+ *   k      [B, Hkv, T, d]   keys of one layer
+ *   k_cmp  [B, Hkv, W, d]   out: k_cmp[w] = mean of k[stride*w .. stride*w + kernel - 1]
+ * Only complete windows are formed. float32 sums; bf16 output rounds to
+ * nearest-even.
+ */
+int sparda_compress_keys(const void* k, void* k_cmp, int dtype, int B, int Hkv, int T, int d,
+                         int kernel, int stride, void* stream);
+
+/*
+ * Step 2 - Forecast block scoring. [P1] paragraph on one Forecast head per GQA
+ * group; [P2] 二; [P3] 解法: one Forecast vector per GQA group scores the
+ * compressed keys directly - no per-query-head loop, no softmax.
+ *   f           [B, Hkv, Tq, d]        Forecast vectors (query i at position q_start + i)
+ *   k_cmp       [B, Hkv, W, d]
+ *   blk_scores  [B, Hkv, nTiles, nB]   out (float32)
+ * Window score s[i, w] = scale * f[i] . k_cmp[w]. Window w is visible to the
+ * query at position p when stride*w + kernel - 1 <= p. Block score of a query
+ * = max of s over the visible windows whose token span meets the block; a
+ * tile's score = max over its queries; -inf marks a block with no visible
+ * window (not a candidate). Decode is Tq = 1, q_start = T - 1.
+ * ws: none needed (ws may be NULL, ws_bytes 0).
+ */
+int sparda_select_forecast(const void* f, const void* k_cmp, float* blk_scores, int dtype, int B,
+                           int Hkv, int Tq, int q_start, int T, int d, int kernel, int stride,
+                           int block, int tile, float scale, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * Step 2' - the original multi-head selector (comparison path). [P1]
+ * paragraph on the standard selector; [P3] 痛点: every query head of the GQA
+ * group scores every candidate, softmax per head, then the sum over the group.
+ *   q           [B, Hq, Tq, d]       query heads; head qh belongs to KV head qh / (Hq/Hkv)
+ *   k_cmp       [B, Hkv, W, d]
+ *   blk_scores  [B, Hkv, nTiles, nB] out (float32), pooled and tiled as for the Forecast
+ * Per query and head, softmax over that query's visible windows of
+ * scale * q . k_cmp[w]; S[w] = sum over the group's heads; block and tile
+ * pooling by max as above.
+ * ws: sparda_workspace_bytes(SPARDA_OP_SELECT_MULTIHEAD, ...) bytes.
+ */
+int sparda_select_multihead(const void* q, const void* k_cmp, float* blk_scores, int dtype, int B,
+                            int Hq, int Hkv, int Tq, int q_start, int T, int d, int kernel,
+                            int stride, int block, int tile, float scale, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
+ * Step 3 - top-k blocks. [P1] paragraph on block-sparse attention: score the
+ * KV cache by block and keep the top-k blocks.
+ *   blk_scores [rows, nB] float32 (rows = B*Hkv*nTiles), idx [rows, k] int32 out.
+ * Candidates are the finite scores; ranked by score (higher first), ties to the
+ * lower block index; the first min(k, #candidates) are written in ascending
+ * block order, the rest of the row is -1. Scores must not be NaN.
+ * Supported: 1 <= k <= nB <= 8192.
+ */
+int sparda_topk_blocks(const float* blk_scores, int32_t* idx, int rows, int nB, int k,
+                       void* stream);
+
+/*
+ * Step 4 - GQA block-sparse attention. [P1] paragraphs on block-sparse
+ * attention and on the next layer attending with its own queries over the
+ * blocks chosen for it; [P3] 解法.
+ *   q     [B, Hq, Tq, d]
+ *   k, v  kv_mode SPARDA_KV_CACHE:   [B, Hkv, T, d]
+ *         kv_mode SPARDA_KV_STAGING: [B, Hkv, k, block, d], slot j = block idx[b, h, 0, j] (Tq = 1 only)
+ *   idx   [B, Hkv, nTiles, k] int32, -1 = unused slot
+ *   out   [B, Hq, Tq, d] (dtype of q)
+ * Query i (position p = q_start + i) of head qh attends, with softmax of
+ * scale * q . k_j, over every key j <= p of the blocks listed for its KV head
+ * and tile. Duplicate indices are not allowed. A query with no key gets 0.
+ * ws: sparda_workspace_bytes(SPARDA_OP_BLOCK_SPARSE_ATTN, ...) bytes.
+ */
+int sparda_block_sparse_attn(const void* q, const void* k, const void* v, int kv_mode,
+                             const int32_t* idx, void* out, int dtype, int B, int Hq, int Hkv,
+                             int Tq, int q_start, int T, int d, int block, int tile, int k_sel,
+                             float scale, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Step 5 - lookahead prefetch of the selected blocks from host memory.
+ * [P1] paragraph on prefetching on a separate stream; [P2] 二 and 三: the blocks
+ * the Forecast picks for the next layer are pulled from CPU memory into GPU
+ * memory by a persistent kernel with a small, batch-dependent number of
+ * workgroups, overlapped with the current layer; the indices never leave the GPU.
+ *   host_k, host_v  [B, Hkv, nB*block, d] pinned host memory (hipHostMalloc),
+ *                   read by the kernel over the host link
+ *   idx             [B, Hkv, k] int32 device memory, -1 = leave the slot untouched
+ *   stage_k/stage_v [B, Hkv, k, block, d] device memory, out: a bit copy
+ *   num_workgroups  0 = library default (16 if B < 32 else 32), else 1..4096
+ * Enqueued on side_stream; order it against producers and consumers of idx
+ * and the staging buffers with events.
+ */
+int sparda_prefetch_blocks(const void* host_k, const void* host_v, const int32_t* idx,
+                           void* stage_k, void* stage_v, int dtype, int B, int Hkv, int nB,
+                           int block, int d, int k_sel, int num_workgroups, void* side_stream);
+
+/* Workspace bytes the call `op` needs for these sizes (0 when none). */
+size_t sparda_workspace_bytes(int op, int B, int Hq, int Hkv, int Tq, int T, int d, int k_sel);
+
+/* Static text for a status code. */
+const char* sparda_status_string(int status);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* sparda_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int sparda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARDA_H */

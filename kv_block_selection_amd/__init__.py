@@ -1,0 +1,209 @@
+"""Python binding of libsparda.so: SparDA block selection and block-sparse
+attention on MI355X.
+
+Argument marshalling only: every step runs in the HIP kernels of libsparda.so,
+reached through its C ABI (include/sparda.h). torch supplies device memory and
+the current stream. There is no fallback: if the library is missing, ``load()``
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparda.so")
+
+SPARDA_OK = 0
+SPARDA_F32 = 0
+SPARDA_BF16 = 1
+KV_CACHE = 0
+KV_STAGING = 1
+OP_SELECT_FORECAST = 1
+OP_SELECT_MULTIHEAD = 2
+OP_BLOCK_SPARSE_ATTN = 3
+
+HEAD_DIM = 128
+BLOCK = 64
+KERNEL = 32
+STRIDE = 16
+TILE = 64
+
+_c = ctypes
+_vp, _i, _f, _sz = _c.c_void_p, _c.c_int, _c.c_float, _c.c_size_t
+
+# name -> (restype, argtypes), exactly as declared in include/sparda.h
+SIGNATURES = {
+    "sparda_compress_keys": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "sparda_select_forecast": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
+    "sparda_select_multihead": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz,
+                                     _vp]),
+    "sparda_topk_blocks": (_i, [_vp, _vp, _i, _i, _i, _vp]),
+    "sparda_block_sparse_attn": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f,
+                                      _vp, _sz, _vp]),
+    "sparda_prefetch_blocks": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "sparda_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "sparda_status_string": (_c.c_char_p, [_i]),
+    "sparda_last_error": (_c.c_char_p, []),
+    "sparda_version": (_i, []),
+}
+
+_LIB = None
+
+
+class SpardaError(RuntimeError):
+    def __init__(self, status: int, call: str, message: str):
+        self.status = status
+        super().__init__(f"{call}: {_LIB.sparda_status_string(status).decode()}: {message}")
+
+
+def load() -> ctypes.CDLL:
+    """Load libsparda.so (built in-tree); raises if it is not built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m kv_block_selection_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def _call(name: str, *args) -> None:
+    lib = load()
+    st = getattr(lib, name)(*args)
+    if st != SPARDA_OK:
+        raise SpardaError(st, name, lib.sparda_last_error().decode())
+
+
+# ------------------------------------------------------------ torch glue ----
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return SPARDA_F32
+    if t.dtype == torch.bfloat16:
+        return SPARDA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t, stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return s.cuda_stream
+
+
+def num_windows(T: int) -> int:
+    return (T - KERNEL) // STRIDE + 1
+
+
+def workspace_bytes(op: int, B: int, Hq: int, Hkv: int, Tq: int, T: int, k: int = 0) -> int:
+    return int(load().sparda_workspace_bytes(op, B, Hq, Hkv, Tq, T, HEAD_DIM, k))
+
+
+def _workspace(ws, nbytes: int, like):
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace has {ws.numel() * ws.element_size()} bytes, needs {nbytes}")
+    return ws, ws.numel() * ws.element_size()
+
+
+# ------------------------------------------------------------- the calls ----
+def compress_keys(k, out=None, stream=None):
+    """K [B, Hkv, T, 128] -> mean-pooled windows [B, Hkv, W, 128] (kernel 32, stride 16)."""
+    torch = _torch()
+    B, Hkv, T, d = k.shape
+    if out is None:
+        out = torch.empty((B, Hkv, num_windows(T), d), dtype=k.dtype, device=k.device)
+    _call("sparda_compress_keys", _ptr(k), _ptr(out), _dtype_code(k), B, Hkv, T, d, KERNEL, STRIDE,
+          _stream(k, stream))
+    return out
+
+
+def select_forecast(f, k_cmp, T: int, q_start: int, scale: float | None = None, out=None, stream=None):
+    """Forecast block scores [B, Hkv, nTiles, nB] (float32) for F [B, Hkv, Tq, 128]."""
+    torch = _torch()
+    B, Hkv, Tq, d = f.shape
+    scale = d ** -0.5 if scale is None else scale
+    n_tiles = -(-Tq // TILE)
+    if out is None:
+        out = torch.empty((B, Hkv, n_tiles, T // BLOCK), dtype=torch.float32, device=f.device)
+    _call("sparda_select_forecast", _ptr(f), _ptr(k_cmp), _ptr(out), _dtype_code(f), B, Hkv, Tq, q_start, T, d,
+          KERNEL, STRIDE, BLOCK, TILE, scale, None, 0, _stream(f, stream))
+    return out
+
+
+def select_multihead(q, k_cmp, T: int, q_start: int, scale: float | None = None, out=None, ws=None,
+                     stream=None):
+    """Multi-head-selector block scores [B, Hkv, nTiles, nB] (float32) for Q [B, Hq, Tq, 128]."""
+    torch = _torch()
+    B, Hq, Tq, d = q.shape
+    Hkv = k_cmp.shape[1]
+    scale = d ** -0.5 if scale is None else scale
+    n_tiles = -(-Tq // TILE)
+    if out is None:
+        out = torch.empty((B, Hkv, n_tiles, T // BLOCK), dtype=torch.float32, device=q.device)
+    ws, nbytes = _workspace(ws, workspace_bytes(OP_SELECT_MULTIHEAD, B, Hq, Hkv, Tq, T), q)
+    _call("sparda_select_multihead", _ptr(q), _ptr(k_cmp), _ptr(out), _dtype_code(q), B, Hq, Hkv, Tq, q_start, T,
+          d, KERNEL, STRIDE, BLOCK, TILE, scale, _ptr(ws), nbytes, _stream(q, stream))
+    return out
+
+
+def topk_blocks(scores, k: int, out=None, stream=None):
+    """Top-k block indices [..., k] int32 (ascending, -1 padded) of float32 scores [..., nB]."""
+    torch = _torch()
+    nB = scores.shape[-1]
+    rows = scores.numel() // nB if nB else 0
+    if out is None:
+        out = torch.empty(tuple(scores.shape[:-1]) + (k,), dtype=torch.int32, device=scores.device)
+    _call("sparda_topk_blocks", _ptr(scores), _ptr(out), rows, nB, k, _stream(scores, stream))
+    return out
+
+
+def block_sparse_attn(q, k, v, idx, T: int, q_start: int, scale: float | None = None, kv_mode: int = KV_CACHE,
+                      out=None, ws=None, stream=None):
+    """GQA block-sparse attention; O [B, Hq, Tq, 128] in q's dtype."""
+    torch = _torch()
+    B, Hq, Tq, d = q.shape
+    Hkv = k.shape[1]
+    k_sel = idx.shape[-1]
+    scale = d ** -0.5 if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    ws, nbytes = _workspace(ws, workspace_bytes(OP_BLOCK_SPARSE_ATTN, B, Hq, Hkv, Tq, T, k_sel), q)
+    _call("sparda_block_sparse_attn", _ptr(q), _ptr(k), _ptr(v), kv_mode, _ptr(idx), _ptr(out), _dtype_code(q), B,
+          Hq, Hkv, Tq, q_start, T, d, BLOCK, TILE, k_sel, scale, _ptr(ws), nbytes, _stream(q, stream))
+    return out
+
+
+def prefetch_blocks(host_k, host_v, idx, stage_k, stage_v, num_workgroups: int = 0, stream=None):
+    """Gather the blocks idx [B, Hkv, k] of pinned host K/V [B, Hkv, T, 128] into
+    device staging [B, Hkv, k, 64, 128], on ``stream`` (default: current)."""
+    B, Hkv, T, d = host_k.shape
+    if not (host_k.is_pinned() and host_v.is_pinned()):
+        raise ValueError("host_k / host_v must be pinned host tensors")
+    k_sel = idx.shape[-1]
+    _call("sparda_prefetch_blocks", host_k.data_ptr(), host_v.data_ptr(), _ptr(idx), _ptr(stage_k), _ptr(stage_v),
+          _dtype_code(host_k), B, Hkv, T // BLOCK, BLOCK, d, k_sel, num_workgroups, _stream(idx, stream))
+    return stage_k, stage_v

@@ -1,0 +1,295 @@
+// C ABI of libsparda.so: argument validation on the host, then dispatch to the
+// kernels. Nothing is enqueued when validation fails; no C++ exception leaves
+// this file.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <cmath>
+#include <string>
+
+#include "launch.h"
+#include "sparda.h"
+
+#define SPARDA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SPARDA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SPARDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define CHECK(cond, status, ...) \
+  do {                           \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+#define CHECK_PTR(p)                                                                 \
+  do {                                                                               \
+    if ((p) == nullptr) return fail(SPARDA_ERR_INVALID_ARG, "%s is NULL", #p);       \
+    if (!aligned16(p)) return fail(SPARDA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+int check_dtype(int dtype) {
+  if (dtype != SPARDA_F32 && dtype != SPARDA_BF16)
+    return fail(SPARDA_ERR_INVALID_ARG, "dtype %d is neither SPARDA_F32 nor SPARDA_BF16", dtype);
+  return SPARDA_OK;
+}
+
+// Geometry shared by selection and attention.
+int check_geometry(int B, int Hq, int Hkv, int Tq, int q_start, int T, int d) {
+  CHECK(B >= 0, SPARDA_ERR_INVALID_ARG, "B = %d < 0", B);
+  CHECK(Hkv >= 1 && Hq >= 1, SPARDA_ERR_INVALID_ARG, "head counts must be >= 1 (Hq %d, Hkv %d)", Hq, Hkv);
+  CHECK(Hq % Hkv == 0, SPARDA_ERR_INVALID_ARG, "Hq %d is not a multiple of Hkv %d", Hq, Hkv);
+  const int G = Hq / Hkv;
+  CHECK(G == 1 || G == 2 || G == 4 || G == 8, SPARDA_ERR_UNSUPPORTED, "GQA group %d not in {1,2,4,8}", G);
+  CHECK(d == sparda::kHeadDim, SPARDA_ERR_UNSUPPORTED, "head dim %d != 128", d);
+  CHECK(T >= sparda::kBlock && T % sparda::kBlock == 0, SPARDA_ERR_UNSUPPORTED,
+        "T = %d must be a positive multiple of 64", T);
+  CHECK(Tq >= 1, SPARDA_ERR_INVALID_ARG, "Tq = %d < 1", Tq);
+  CHECK(Tq == 1 || Tq % sparda::kTile == 0, SPARDA_ERR_UNSUPPORTED, "Tq = %d is neither 1 nor a multiple of 64", Tq);
+  CHECK(q_start >= 0 && (long)q_start + Tq == T, SPARDA_ERR_INVALID_ARG,
+        "the query chunk must end at the newest token: q_start %d + Tq %d != T %d", q_start, Tq, T);
+  CHECK((long)B * Hkv <= 65535, SPARDA_ERR_UNSUPPORTED, "B*Hkv = %ld exceeds 65535", (long)B * Hkv);
+  return SPARDA_OK;
+}
+
+int check_select_params(int kernel, int stride, int block, int tile, float scale) {
+  CHECK(kernel == sparda::kKernel && stride == sparda::kStride, SPARDA_ERR_UNSUPPORTED,
+        "compression kernel/stride %d/%d != 32/16", kernel, stride);
+  CHECK(block == sparda::kBlock, SPARDA_ERR_UNSUPPORTED, "block %d != 64", block);
+  CHECK(tile == sparda::kTile, SPARDA_ERR_UNSUPPORTED, "tile %d != 64", tile);
+  CHECK(std::isfinite(scale), SPARDA_ERR_INVALID_ARG, "scale is not finite");
+  return SPARDA_OK;
+}
+
+sparda::SelectDims select_dims(int B, int Hq, int Hkv, int Tq, int q_start, int T, float scale) {
+  sparda::SelectDims s;
+  s.B = B;
+  s.Hq = Hq;
+  s.Hkv = Hkv;
+  s.Tq = Tq;
+  s.q_start = q_start;
+  s.T = T;
+  s.W = (T - sparda::kKernel) / sparda::kStride + 1;
+  s.nB = T / sparda::kBlock;
+  s.n_tiles = (Tq + sparda::kTile - 1) / sparda::kTile;
+  s.scale = scale;
+  return s;
+}
+
+sparda::AttnDims attn_dims(int B, int Hq, int Hkv, int Tq, int q_start, int T, int k, float scale,
+                           int kv_mode) {
+  sparda::AttnDims a;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Tq = Tq;
+  a.q_start = q_start;
+  a.T = T;
+  a.nB = T / sparda::kBlock;
+  a.n_tiles = (Tq + sparda::kTile - 1) / sparda::kTile;
+  a.k = k;
+  a.scale = scale;
+  a.kv_mode = kv_mode;
+  return a;
+}
+
+size_t ws_bytes_for(int op, int B, int Hq, int Hkv, int Tq, int T, int k) {
+  if (B <= 0 || Hkv <= 0 || Hq <= 0 || T < sparda::kBlock) return 0;
+  const int q_start = T - Tq;
+  switch (op) {
+    case SPARDA_OP_SELECT_FORECAST:
+      return 0;
+    case SPARDA_OP_SELECT_MULTIHEAD:
+      if (Tq == 1) return sparda::multihead_decode_ws_bytes(select_dims(B, Hq, Hkv, Tq, q_start, T, 1.f));
+      return 0;
+    case SPARDA_OP_BLOCK_SPARSE_ATTN:
+      if (Tq == 1) return sparda::decode_attn_ws_bytes(attn_dims(B, Hq, Hkv, Tq, q_start, T, k, 1.f, 0));
+      return 0;
+    default:
+      return 0;
+  }
+}
+
+}  // namespace
+
+SPARDA_EXPORT int sparda_version(void) { return 100; }  // 0.1.0
+
+SPARDA_EXPORT const char* sparda_status_string(int status) {
+  switch (status) {
+    case SPARDA_OK: return "SPARDA_OK";
+    case SPARDA_ERR_INVALID_ARG: return "SPARDA_ERR_INVALID_ARG";
+    case SPARDA_ERR_UNSUPPORTED: return "SPARDA_ERR_UNSUPPORTED";
+    case SPARDA_ERR_WORKSPACE: return "SPARDA_ERR_WORKSPACE";
+    case SPARDA_ERR_HIP: return "SPARDA_ERR_HIP";
+    default: return "SPARDA_ERR_UNKNOWN";
+  }
+}
+
+SPARDA_EXPORT const char* sparda_last_error(void) { return g_last_error.c_str(); }
+
+SPARDA_EXPORT size_t sparda_workspace_bytes(int op, int B, int Hq, int Hkv, int Tq, int T, int d, int k_sel) {
+  (void)d;
+  return ws_bytes_for(op, B, Hq, Hkv, Tq, T, k_sel);
+}
+
+SPARDA_EXPORT int sparda_compress_keys(const void* k, void* k_cmp, int dtype, int B, int Hkv, int T, int d,
+                                       int kernel, int stride, void* stream) {
+  if (int e = check_dtype(dtype)) return e;
+  CHECK(B >= 0 && Hkv >= 1, SPARDA_ERR_INVALID_ARG, "B %d / Hkv %d out of range", B, Hkv);
+  CHECK(d == sparda::kHeadDim, SPARDA_ERR_UNSUPPORTED, "head dim %d != 128", d);
+  CHECK(kernel == sparda::kKernel && stride == sparda::kStride, SPARDA_ERR_UNSUPPORTED,
+        "compression kernel/stride %d/%d != 32/16", kernel, stride);
+  CHECK(T >= sparda::kBlock && T % sparda::kBlock == 0, SPARDA_ERR_UNSUPPORTED,
+        "T = %d must be a positive multiple of 64", T);
+  if (B == 0) return ok();
+  CHECK_PTR(k);
+  CHECK_PTR(k_cmp);
+  const int W = (T - kernel) / stride + 1;
+  return hip_status(sparda::launch_compress(k, k_cmp, dtype == SPARDA_BF16, B * Hkv, T, W, (hipStream_t)stream),
+                    "compress_keys launch");
+}
+
+SPARDA_EXPORT int sparda_select_forecast(const void* f, const void* k_cmp, float* blk_scores, int dtype, int B,
+                                         int Hkv, int Tq, int q_start, int T, int d, int kernel, int stride,
+                                         int block, int tile, float scale, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (int e = check_dtype(dtype)) return e;
+  if (int e = check_geometry(B, Hkv, Hkv, Tq, q_start, T, d)) return e;
+  if (int e = check_select_params(kernel, stride, block, tile, scale)) return e;
+  if (B == 0) return ok();
+  CHECK_PTR(f);
+  CHECK_PTR(k_cmp);
+  CHECK_PTR(blk_scores);
+  const sparda::SelectDims sd = select_dims(B, Hkv, Hkv, Tq, q_start, T, scale);
+  if (Tq != 1) return fail(SPARDA_ERR_UNSUPPORTED, "select_forecast: Tq > 1 (prefill) is not built yet");
+  return hip_status(sparda::launch_select_forecast_decode(f, k_cmp, blk_scores, dtype == SPARDA_BF16, sd,
+                                                          (hipStream_t)stream),
+                    "select_forecast launch");
+}
+
+SPARDA_EXPORT int sparda_select_multihead(const void* q, const void* k_cmp, float* blk_scores, int dtype, int B,
+                                          int Hq, int Hkv, int Tq, int q_start, int T, int d, int kernel,
+                                          int stride, int block, int tile, float scale, void* ws,
+                                          size_t ws_bytes, void* stream) {
+  if (int e = check_dtype(dtype)) return e;
+  if (int e = check_geometry(B, Hq, Hkv, Tq, q_start, T, d)) return e;
+  if (int e = check_select_params(kernel, stride, block, tile, scale)) return e;
+  if (B == 0) return ok();
+  CHECK_PTR(q);
+  CHECK_PTR(k_cmp);
+  CHECK_PTR(blk_scores);
+  const size_t need = ws_bytes_for(SPARDA_OP_SELECT_MULTIHEAD, B, Hq, Hkv, Tq, T, 0);
+  CHECK(ws_bytes >= need, SPARDA_ERR_WORKSPACE, "select_multihead needs %zu workspace bytes, got %zu", need, ws_bytes);
+  if (need) CHECK_PTR(ws);
+  const sparda::SelectDims sd = select_dims(B, Hq, Hkv, Tq, q_start, T, scale);
+  if (Tq != 1) return fail(SPARDA_ERR_UNSUPPORTED, "select_multihead: Tq > 1 (prefill) is not built yet");
+  return hip_status(sparda::launch_select_multihead_decode(q, k_cmp, blk_scores, dtype == SPARDA_BF16, sd, ws,
+                                                           (hipStream_t)stream),
+                    "select_multihead launch");
+}
+
+SPARDA_EXPORT int sparda_topk_blocks(const float* blk_scores, int32_t* idx, int rows, int nB, int k, void* stream) {
+  CHECK(rows >= 0, SPARDA_ERR_INVALID_ARG, "rows = %d < 0", rows);
+  CHECK(nB >= 1 && nB <= 8192, SPARDA_ERR_UNSUPPORTED, "nB = %d outside 1..8192", nB);
+  CHECK(k >= 1 && k <= nB, SPARDA_ERR_INVALID_ARG, "k = %d outside 1..nB (%d)", k, nB);
+  CHECK(rows <= 2147483647, SPARDA_ERR_UNSUPPORTED, "too many rows");
+  if (rows == 0) return ok();
+  CHECK(blk_scores != nullptr && ((uintptr_t)blk_scores & 3u) == 0, SPARDA_ERR_INVALID_ARG,
+        "blk_scores is NULL or not 4-byte aligned");
+  CHECK(idx != nullptr && ((uintptr_t)idx & 3u) == 0, SPARDA_ERR_INVALID_ARG, "idx is NULL or not 4-byte aligned");
+  return hip_status(sparda::launch_topk(blk_scores, idx, rows, nB, k, (hipStream_t)stream), "topk launch");
+}
+
+SPARDA_EXPORT int sparda_block_sparse_attn(const void* q, const void* k, const void* v, int kv_mode,
+                                           const int32_t* idx, void* out, int dtype, int B, int Hq, int Hkv,
+                                           int Tq, int q_start, int T, int d, int block, int tile, int k_sel,
+                                           float scale, void* ws, size_t ws_bytes, void* stream) {
+  if (int e = check_dtype(dtype)) return e;
+  if (int e = check_geometry(B, Hq, Hkv, Tq, q_start, T, d)) return e;
+  CHECK(block == sparda::kBlock, SPARDA_ERR_UNSUPPORTED, "block %d != 64", block);
+  CHECK(tile == sparda::kTile, SPARDA_ERR_UNSUPPORTED, "tile %d != 64", tile);
+  CHECK(std::isfinite(scale), SPARDA_ERR_INVALID_ARG, "scale is not finite");
+  CHECK(kv_mode == SPARDA_KV_CACHE || kv_mode == SPARDA_KV_STAGING, SPARDA_ERR_INVALID_ARG, "kv_mode %d", kv_mode);
+  CHECK(k_sel >= 1 && k_sel <= T / sparda::kBlock, SPARDA_ERR_INVALID_ARG, "k = %d outside 1..nB (%d)", k_sel,
+        T / sparda::kBlock);
+  CHECK(kv_mode == SPARDA_KV_CACHE || Tq == 1, SPARDA_ERR_UNSUPPORTED, "staging mode is decode-only (Tq = 1)");
+  if (B == 0) return ok();
+  CHECK_PTR(q);
+  CHECK_PTR(k);
+  CHECK_PTR(v);
+  CHECK_PTR(out);
+  CHECK(idx != nullptr && ((uintptr_t)idx & 3u) == 0, SPARDA_ERR_INVALID_ARG, "idx is NULL or not 4-byte aligned");
+  const size_t need = ws_bytes_for(SPARDA_OP_BLOCK_SPARSE_ATTN, B, Hq, Hkv, Tq, T, k_sel);
+  CHECK(ws_bytes >= need, SPARDA_ERR_WORKSPACE, "block_sparse_attn needs %zu workspace bytes, got %zu", need,
+        ws_bytes);
+  if (need) CHECK_PTR(ws);
+  const sparda::AttnDims ad = attn_dims(B, Hq, Hkv, Tq, q_start, T, k_sel, scale, kv_mode);
+  if (Tq != 1) return fail(SPARDA_ERR_UNSUPPORTED, "block_sparse_attn: Tq > 1 (prefill) is not built yet");
+  return hip_status(sparda::launch_attn_decode(q, k, v, idx, out, dtype == SPARDA_BF16, ad, ws, (hipStream_t)stream),
+                    "block_sparse_attn launch");
+}
+
+namespace {
+// Pinned, mapped host memory: returns the device-side address or nullptr.
+const void* mapped_host_ptr(const void* p) {
+  hipPointerAttribute_t attr;
+  const hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (attr.type != hipMemoryTypeHost) return nullptr;
+  return attr.devicePointer;
+}
+}  // namespace
+
+SPARDA_EXPORT int sparda_prefetch_blocks(const void* host_k, const void* host_v, const int32_t* idx,
+                                         void* stage_k, void* stage_v, int dtype, int B, int Hkv, int nB,
+                                         int block, int d, int k_sel, int num_workgroups, void* side_stream) {
+  if (int e = check_dtype(dtype)) return e;
+  CHECK(B >= 0 && Hkv >= 1, SPARDA_ERR_INVALID_ARG, "B %d / Hkv %d out of range", B, Hkv);
+  CHECK(block == sparda::kBlock, SPARDA_ERR_UNSUPPORTED, "block %d != 64", block);
+  CHECK(d == sparda::kHeadDim, SPARDA_ERR_UNSUPPORTED, "head dim %d != 128", d);
+  CHECK(nB >= 1, SPARDA_ERR_INVALID_ARG, "nB = %d < 1", nB);
+  CHECK(k_sel >= 1 && k_sel <= nB, SPARDA_ERR_INVALID_ARG, "k = %d outside 1..nB (%d)", k_sel, nB);
+  CHECK(num_workgroups >= 0 && num_workgroups <= 4096, SPARDA_ERR_INVALID_ARG, "num_workgroups %d outside 0..4096",
+        num_workgroups);
+  if (B == 0) return ok();
+  CHECK_PTR(host_k);
+  CHECK_PTR(host_v);
+  CHECK_PTR(stage_k);
+  CHECK_PTR(stage_v);
+  CHECK(idx != nullptr && ((uintptr_t)idx & 3u) == 0, SPARDA_ERR_INVALID_ARG, "idx is NULL or not 4-byte aligned");
+  const void* dk = mapped_host_ptr(host_k);
+  const void* dv = mapped_host_ptr(host_v);
+  CHECK(dk != nullptr, SPARDA_ERR_INVALID_ARG, "host_k is not pinned host memory (use hipHostMalloc)");
+  CHECK(dv != nullptr, SPARDA_ERR_INVALID_ARG, "host_v is not pinned host memory (use hipHostMalloc)");
+  const int nwg = num_workgroups ? num_workgroups : (B < 32 ? 16 : 32);
+  return hip_status(sparda::launch_prefetch(dk, dv, idx, stage_k, stage_v, dtype == SPARDA_BF16 ? 2 : 4, B, Hkv,
+                                            nB, k_sel, nwg, (hipStream_t)side_stream),
+                    "prefetch_blocks launch");
+}

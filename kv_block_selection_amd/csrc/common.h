@@ -1,0 +1,157 @@
+// Internal helpers shared by the libsparda kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "launch.h"
+
+namespace sparda {
+
+constexpr int kWave = 64;
+
+// 16 bytes of a row: 8 bf16 or 4 fp32 values.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+struct F32Tag {};
+struct BF16Tag {};
+
+template <typename Tag> struct DT;
+template <> struct DT<F32Tag> {
+  static constexpr int kElems = 4;  // per 16-byte vector
+  static constexpr int kBytes = 4;
+};
+template <> struct DT<BF16Tag> {
+  static constexpr int kElems = 8;
+  static constexpr int kBytes = 2;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 pair packed in a dword (lo = a, hi = b).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Expand a 16-byte vector into fp32 values.
+template <typename Tag>
+__device__ __forceinline__ void unpack(const u32x4& v, float* out);
+template <>
+__device__ __forceinline__ void unpack<BF16Tag>(const u32x4& v, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = bf16_lo(v[i]);
+    out[2 * i + 1] = bf16_hi(v[i]);
+  }
+}
+template <>
+__device__ __forceinline__ void unpack<F32Tag>(const u32x4& v, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(v[i]);
+}
+
+// Pack fp32 values into a 16-byte vector in storage format.
+template <typename Tag>
+__device__ __forceinline__ u32x4 pack(const float* in);
+template <>
+__device__ __forceinline__ u32x4 pack<BF16Tag>(const float* in) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack_bf16(in[2 * i], in[2 * i + 1]);
+  return r;
+}
+template <>
+__device__ __forceinline__ u32x4 pack<F32Tag>(const float* in) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __float_as_uint(in[i]);
+  return r;
+}
+
+// Dot product of two 16-byte vectors, fp32 accumulation.
+template <typename Tag>
+__device__ __forceinline__ float dot16(const u32x4& a, const u32x4& b, float acc);
+template <>
+__device__ __forceinline__ float dot16<BF16Tag>(const u32x4& a, const u32x4& b, float acc) {
+  // Each element goes through a scalar first: __builtin_bit_cast applied to a
+  // vector-element lvalue reads element 0 (the whole vector's storage).
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = a[i], y = b[i];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y),
+                                          acc, false);
+  }
+  return acc;
+}
+template <>
+__device__ __forceinline__ float dot16<F32Tag>(const u32x4& a, const u32x4& b, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = fmaf(__uint_as_float(a[i]), __uint_as_float(b[i]), acc);
+  return acc;
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x4 load16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void store16(void* p, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// ---- cross-lane reductions (DPP within a 16-lane row) ----
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Butterfly over the 16 lanes of a DPP row: xor 1, xor 2, then half-mirror and
+// mirror. Every step pairs lanes symmetrically, so all 16 lanes end with the
+// bitwise-identical sum.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);  // row_half_mirror
+  x += dpp<0x140>(x);  // row_mirror
+  return x;
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x140>(x));
+  return x;
+}
+__device__ __forceinline__ float xor_shfl(float x, int mask) {
+  return __shfl_xor(x, mask, kWave);
+}
+// Sum over a group of LANES (16 or 32) consecutive lanes; every lane gets it.
+template <int LANES>
+__device__ __forceinline__ float group_sum(float x) {
+  x = row16_sum(x);
+  if constexpr (LANES == 32) x += xor_shfl(x, 16);
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row16_sum(x);
+  x += xor_shfl(x, 16);
+  x += xor_shfl(x, 32);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = row16_max(x);
+  x = fmaxf(x, xor_shfl(x, 16));
+  x = fmaxf(x, xor_shfl(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+}  // namespace sparda

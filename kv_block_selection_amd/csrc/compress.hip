@@ -1,0 +1,82 @@
+// Step 1: mean-pooled key windows, kernel 32 and stride 16 (techwalker.com
+// article on SparDA, section 四: compressed-key windows used at inference).
+//
+// HBM-bound stream: read K once, write K_cmp (1/16 of K). A 16-lane group
+// (bf16; 32 lanes for fp32) owns one (row, window chunk) and walks its tokens
+// in order; each lane keeps 8 (or 4) channels. Each 16-token half-window sum is
+// formed once and shared by the two windows that contain it. Per load
+// instruction a wave reads 4 (bf16) or 2 (fp32) whole 256-byte token rows:
+// 1 KiB contiguous per row group, fully used.
+#include "common.h"
+#include "launch.h"
+
+namespace sparda {
+
+constexpr int kCompressChunk = 32;  // windows per lane group
+
+template <typename Tag>
+__global__ __launch_bounds__(256) void compress_kernel(const uint8_t* __restrict__ k,
+                                                       uint8_t* __restrict__ kc, int rows, int T,
+                                                       int W, int chunks_per_row) {
+  constexpr int E = DT<Tag>::kElems;
+  constexpr int LPR = kHeadDim / E;        // lanes per token row
+  constexpr int GPB = 256 / LPR;           // lane groups per workgroup
+  constexpr int RB = kHeadDim * DT<Tag>::kBytes;  // row bytes
+  const int lane_in_row = threadIdx.x % LPR;
+  const long group = (long)blockIdx.x * GPB + threadIdx.x / LPR;
+  if (group >= (long)rows * chunks_per_row) return;
+  const long row = group / chunks_per_row;
+  const int w0 = (int)(group % chunks_per_row) * kCompressChunk;
+  const int w1 = min(W, w0 + kCompressChunk);
+
+  const uint8_t* src = k + row * (long)T * RB + lane_in_row * 16;
+  uint8_t* dst = kc + row * (long)W * RB + lane_in_row * 16;
+
+  // half-window h covers tokens [16h, 16h+16)
+  auto half_sum = [&](int h, float* acc) {
+    u32x4 v[kStride];
+#pragma unroll
+    for (int t = 0; t < kStride; ++t) v[t] = load16_nt(src + (long)(h * kStride + t) * RB);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int t = 0; t < kStride; ++t) {
+      float x[E];
+      unpack<Tag>(v[t], x);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += x[e];
+    }
+  };
+
+  float prev[E], next[E];
+  half_sum(w0, prev);
+  for (int w = w0; w < w1; ++w) {
+    half_sum(w + 1, next);
+    float m[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      m[e] = (prev[e] + next[e]) * (1.0f / kKernel);
+      prev[e] = next[e];
+    }
+    store16(dst + (long)w * RB, pack<Tag>(m));
+  }
+}
+
+hipError_t launch_compress(const void* k, void* kc, bool bf16, int rows, int T, int W, hipStream_t s) {
+  const int chunks = (W + kCompressChunk - 1) / kCompressChunk;
+  const long groups = (long)rows * chunks;
+  if (bf16) {
+    const int gpb = 256 / (kHeadDim / DT<BF16Tag>::kElems);
+    dim3 grid((unsigned)((groups + gpb - 1) / gpb));
+    hipLaunchKernelGGL(compress_kernel<BF16Tag>, grid, dim3(256), 0, s, (const uint8_t*)k,
+                       (uint8_t*)kc, rows, T, W, chunks);
+  } else {
+    const int gpb = 256 / (kHeadDim / DT<F32Tag>::kElems);
+    dim3 grid((unsigned)((groups + gpb - 1) / gpb));
+    hipLaunchKernelGGL(compress_kernel<F32Tag>, grid, dim3(256), 0, s, (const uint8_t*)k,
+                       (uint8_t*)kc, rows, T, W, chunks);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sparda

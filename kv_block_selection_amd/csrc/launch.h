@@ -1,0 +1,53 @@
+// Internal launchers (host side) called by the C ABI layer in api.cpp, which
+// has already validated every argument.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sparda {
+
+// Supported geometry: head dim, KV block, compression window and stride, query tile.
+constexpr int kHeadDim = 128;
+constexpr int kBlock = 64;
+constexpr int kKernel = 32;
+constexpr int kStride = 16;
+constexpr int kTile = 64;
+
+struct SelectDims {
+  int B, Hq, Hkv, Tq, q_start, T, W, nB, n_tiles;
+  float scale;
+};
+
+struct AttnDims {
+  int B, Hq, Hkv, Tq, q_start, T, nB, n_tiles, k;
+  float scale;
+  int kv_mode;
+};
+
+// compress.hip
+hipError_t launch_compress(const void* k, void* kc, bool bf16, int rows, int T, int W, hipStream_t s);
+
+// select_decode.hip
+hipError_t launch_select_forecast_decode(const void* f, const void* kc, float* scores, bool bf16,
+                                         const SelectDims& d, hipStream_t s);
+size_t multihead_decode_ws_bytes(const SelectDims& d);
+hipError_t launch_select_multihead_decode(const void* q, const void* kc, float* scores, bool bf16,
+                                          const SelectDims& d, void* ws, hipStream_t s);
+
+// topk.hip
+hipError_t launch_topk(const float* scores, int32_t* idx, int rows, int nB, int k, hipStream_t s);
+
+// attn_decode.hip
+int decode_attn_splits(const AttnDims& d);
+size_t decode_attn_ws_bytes(const AttnDims& d);
+hipError_t launch_attn_decode(const void* q, const void* k, const void* v, const int32_t* idx,
+                              void* out, bool bf16, const AttnDims& d, void* ws, hipStream_t s);
+
+// prefetch.hip
+hipError_t launch_prefetch(const void* host_k, const void* host_v, const int32_t* idx, void* stage_k,
+                           void* stage_v, int elem_bytes, int B, int Hkv, int nB, int k,
+                           int num_workgroups, hipStream_t s);
+
+}  // namespace sparda

@@ -1,0 +1,275 @@
+// Step 2 at decode (one query per sequence): block scoring from compressed keys.
+//
+// Forecast selector (bittide.aicompass.dev summary post, paragraph on one
+// Forecast head per GQA group; techwalker.com article, section 二): one vector
+// per KV head scores every window, no softmax. Multi-head selector (same post,
+// paragraph on the standard selector; 10100.com commentary, section 痛点): every
+// query head of the group scores every window, softmax per head, group sum.
+//
+// Both are HBM-bound GEMVs over K_cmp [rows, W, 128]. A workgroup owns a run of
+// whole blocks plus the one window before it (block b meets windows
+// 4b-1 .. 4b+3), so it finishes its block scores with no exchange between
+// workgroups. 16 lanes hold one 256-byte window row (8 bf16 each); a wave reads
+// 4 rows (1 KiB contiguous) per load. The dot products use v_dot2_f32_bf16 and a
+// DPP butterfly across the 16 lanes.
+//
+// The multi-head selector needs each head's softmax normaliser over all
+// windows before it can sum heads, so it runs in two passes: (1) logits to the
+// workspace plus per-chunk (max, sum of exp); (2) combine the chunk statistics,
+// normalise, sum over the group, pool into blocks.
+#include "common.h"
+#include "launch.h"
+
+namespace sparda {
+
+constexpr int kFselBlocks = 32;   // blocks per workgroup, Forecast pass
+constexpr int kMhChunk = 256;     // windows per workgroup, multi-head pass 1
+constexpr int kMhPoolBlocks = 64; // blocks per workgroup, multi-head pass 2
+
+template <typename Tag>
+struct RowGeom {
+  static constexpr int E = DT<Tag>::kElems;
+  static constexpr int LPR = kHeadDim / E;   // lanes per 128-channel row
+  static constexpr int SLOTS = 256 / LPR;    // rows per 256-thread pass
+  static constexpr int RB = kHeadDim * DT<Tag>::kBytes;
+};
+
+// ---------------------------------------------------------------- Forecast --
+template <typename Tag>
+__global__ __launch_bounds__(256) void fsel_decode_kernel(const uint8_t* __restrict__ f,
+                                                          const uint8_t* __restrict__ kc,
+                                                          float* __restrict__ scores, int W, int nB,
+                                                          int n_vis, float scale) {
+  using R = RowGeom<Tag>;
+  constexpr int NWIN = 4 * kFselBlocks + 1;
+  constexpr int ITER = (NWIN + R::SLOTS - 1) / R::SLOTS;
+  __shared__ float s_win[ITER * R::SLOTS];
+
+  const long row = blockIdx.y;
+  const int beta0 = blockIdx.x * kFselBlocks;
+  const int nblk = min(kFselBlocks, nB - beta0);
+  const int nwin = 4 * nblk + 1;
+  const int wstart = 4 * beta0 - 1;
+  const int lane = threadIdx.x % R::LPR;
+  const int slot = threadIdx.x / R::LPR;
+
+  const u32x4 fv = load16(f + row * R::RB + lane * 16);
+  const uint8_t* base = kc + row * (long)W * R::RB + lane * 16;
+
+  u32x4 kv[ITER];
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int lw = it * R::SLOTS + slot;
+    const int w = wstart + lw;
+    const bool ok = lw < nwin && w >= 0 && w < n_vis;
+    kv[it] = ok ? load16_nt(base + (long)w * R::RB) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int lw = it * R::SLOTS + slot;
+    const int w = wstart + lw;
+    const bool ok = lw < nwin && w >= 0 && w < n_vis;
+    const float s = group_sum<R::LPR>(dot16<Tag>(fv, kv[it], 0.f));
+    if (lane == 0) s_win[lw] = ok ? s * scale : -INFINITY;
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < nblk) {
+    float m = s_win[4 * t];
+#pragma unroll
+    for (int j = 1; j < 5; ++j) m = fmaxf(m, s_win[4 * t + j]);
+    scores[row * nB + beta0 + t] = m;
+  }
+}
+
+hipError_t launch_select_forecast_decode(const void* f, const void* kc, float* scores, bool bf16,
+                                         const SelectDims& d, hipStream_t s) {
+  const int n_vis = min(d.W, (d.q_start - kKernel + 1) >= 0 ? (d.q_start - kKernel + 1) / kStride + 1 : 0);
+  dim3 grid((d.nB + kFselBlocks - 1) / kFselBlocks, d.B * d.Hkv);
+  if (bf16)
+    hipLaunchKernelGGL(fsel_decode_kernel<BF16Tag>, grid, dim3(256), 0, s, (const uint8_t*)f,
+                       (const uint8_t*)kc, scores, d.W, d.nB, n_vis, d.scale);
+  else
+    hipLaunchKernelGGL(fsel_decode_kernel<F32Tag>, grid, dim3(256), 0, s, (const uint8_t*)f,
+                       (const uint8_t*)kc, scores, d.W, d.nB, n_vis, d.scale);
+  return hipGetLastError();
+}
+
+// -------------------------------------------------------------- multi-head --
+struct MhWs {
+  float* logits;  // [rows, G, W]
+  float2* stats;  // [rows, chunks, G] (max, sum of exp)
+};
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static MhWs mh_ws(void* ws, const SelectDims& d) {
+  const int G = d.Hq / d.Hkv;
+  const size_t rows = (size_t)d.B * d.Hkv;
+  MhWs r;
+  r.logits = (float*)ws;
+  r.stats = (float2*)((char*)ws + align256(rows * G * d.W * sizeof(float)));
+  return r;
+}
+
+size_t multihead_decode_ws_bytes(const SelectDims& d) {
+  const int G = d.Hq / d.Hkv;
+  const size_t rows = (size_t)d.B * d.Hkv;
+  const size_t chunks = (d.W + kMhChunk - 1) / kMhChunk;
+  return align256(rows * G * d.W * sizeof(float)) + align256(rows * chunks * G * sizeof(float2));
+}
+
+__device__ __forceinline__ float block_reduce_max(float v, float* red) {
+  v = wave_max(v);
+  const int wid = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) red[wid] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < (int)blockDim.x / kWave; ++i) r = fmaxf(r, red[i]);
+  return r;
+}
+__device__ __forceinline__ float block_reduce_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int wid = threadIdx.x / kWave;
+  __syncthreads();
+  if (threadIdx.x % kWave == 0) red[wid] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < (int)blockDim.x / kWave; ++i) r += red[i];
+  return r;
+}
+
+template <typename Tag, int G>
+__global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __restrict__ q,
+                                                           const uint8_t* __restrict__ kc, MhWs ws,
+                                                           int W, int n_vis, int chunks, float scale) {
+  using R = RowGeom<Tag>;
+  constexpr int ITER = kMhChunk / R::SLOTS;
+  __shared__ float s_log[G][kMhChunk];
+  __shared__ float red[4];
+
+  const long row = blockIdx.y;  // (b, kv head)
+  const int chunk = blockIdx.x;
+  const int w0 = chunk * kMhChunk;
+  const int lane = threadIdx.x % R::LPR;
+  const int slot = threadIdx.x / R::LPR;
+
+  u32x4 qv[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) qv[g] = load16(q + (row * G + g) * R::RB + lane * 16);
+  const uint8_t* base = kc + row * (long)W * R::RB + lane * 16;
+
+  u32x4 kv[ITER];
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int w = w0 + it * R::SLOTS + slot;
+    kv[it] = (w < n_vis) ? load16_nt(base + (long)w * R::RB) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int lw = it * R::SLOTS + slot;
+    const bool ok = w0 + lw < n_vis;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float s = group_sum<R::LPR>(dot16<Tag>(qv[g], kv[it], 0.f));
+      if (lane == g % R::LPR) s_log[g][lw] = ok ? s * scale : -INFINITY;
+    }
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int w = w0 + t;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float x = s_log[g][t];
+    const float m = block_reduce_max(x, red);
+    const float e = (m == -INFINITY || x == -INFINITY) ? 0.f : fast_exp(x - m);
+    const float z = block_reduce_sum(e, red);
+    if (w < W) ws.logits[(row * G + g) * W + w] = x;
+    if (t == 0) ws.stats[(row * chunks + chunk) * G + g] = make_float2(m, z);
+  }
+}
+
+template <typename Tag, int G>
+__global__ __launch_bounds__(256) void mhsel_pool_kernel(MhWs ws, float* __restrict__ scores,
+                                                         int W, int nB, int n_vis, int chunks) {
+  constexpr int NWIN = 4 * kMhPoolBlocks + 1;
+  __shared__ float s_sum[NWIN];
+  __shared__ float s_m[G], s_iz[G];
+  const long row = blockIdx.y;
+  const int beta0 = blockIdx.x * kMhPoolBlocks;
+  const int nblk = min(kMhPoolBlocks, nB - beta0);
+  const int nwin = 4 * nblk + 1;
+  const int wstart = 4 * beta0 - 1;
+
+  if (threadIdx.x < G) {
+    const int g = threadIdx.x;
+    float m = -INFINITY;
+    for (int c = 0; c < chunks; ++c) m = fmaxf(m, ws.stats[(row * chunks + c) * G + g].x);
+    float z = 0.f;
+    for (int c = 0; c < chunks; ++c) {
+      const float2 st = ws.stats[(row * chunks + c) * G + g];
+      if (st.x != -INFINITY) z += st.y * fast_exp(st.x - m);
+    }
+    s_m[g] = m;
+    s_iz[g] = 1.f / z;
+  }
+  __syncthreads();
+  for (int lw = threadIdx.x; lw < nwin; lw += blockDim.x) {
+    const int w = wstart + lw;
+    float S = -INFINITY;
+    if (w >= 0 && w < n_vis) {
+      S = 0.f;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        S += fast_exp(ws.logits[(row * G + g) * W + w] - s_m[g]) * s_iz[g];
+    }
+    s_sum[lw] = S;
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < nblk) {
+    float m = s_sum[4 * t];
+#pragma unroll
+    for (int j = 1; j < 5; ++j) m = fmaxf(m, s_sum[4 * t + j]);
+    scores[row * nB + beta0 + t] = m;
+  }
+}
+
+template <typename Tag, int G>
+static void launch_mh(const void* q, const void* kc, float* scores, const SelectDims& d, MhWs w,
+                      int n_vis, hipStream_t s) {
+  const int chunks = (d.W + kMhChunk - 1) / kMhChunk;
+  const int rows = d.B * d.Hkv;
+  hipLaunchKernelGGL((mhsel_logits_kernel<Tag, G>), dim3(chunks, rows), dim3(256), 0, s,
+                     (const uint8_t*)q, (const uint8_t*)kc, w, d.W, n_vis, chunks, d.scale);
+  hipLaunchKernelGGL((mhsel_pool_kernel<Tag, G>),
+                     dim3((d.nB + kMhPoolBlocks - 1) / kMhPoolBlocks, rows), dim3(256), 0, s, w,
+                     scores, d.W, d.nB, n_vis, chunks);
+}
+
+hipError_t launch_select_multihead_decode(const void* q, const void* kc, float* scores, bool bf16,
+                                          const SelectDims& d, void* ws, hipStream_t s) {
+  const int n_vis = min(d.W, (d.q_start - kKernel + 1) >= 0 ? (d.q_start - kKernel + 1) / kStride + 1 : 0);
+  const MhWs w = mh_ws(ws, d);
+  const int G = d.Hq / d.Hkv;
+#define SPARDA_MH(TAG, GG) launch_mh<TAG, GG>(q, kc, scores, d, w, n_vis, s)
+#define SPARDA_MH_G(TAG)                  \
+  switch (G) {                            \
+    case 1: SPARDA_MH(TAG, 1); break;     \
+    case 2: SPARDA_MH(TAG, 2); break;     \
+    case 4: SPARDA_MH(TAG, 4); break;     \
+    case 8: SPARDA_MH(TAG, 8); break;     \
+    default: return hipErrorInvalidValue; \
+  }
+  if (bf16) {
+    SPARDA_MH_G(BF16Tag)
+  } else {
+    SPARDA_MH_G(F32Tag)
+  }
+#undef SPARDA_MH_G
+#undef SPARDA_MH
+  return hipGetLastError();
+}
+
+}  // namespace sparda

@@ -1,0 +1,122 @@
+"""The C ABI of libsparda.so without a GPU: the library loads, exports every
+entry point include/sparda.h declares, and rejects bad arguments on the host
+with a status code and a message before anything is enqueued."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_block_selection_amd as kbs
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "sparda.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparda_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kbs.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in kbs.SIGNATURES, f"binding lacks {n}"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sparda_version() == 100
+    assert lib.sparda_status_string(0) == b"SPARDA_OK"
+    assert lib.sparda_status_string(1) == b"SPARDA_ERR_INVALID_ARG"
+    assert lib.sparda_status_string(3) == b"SPARDA_ERR_WORKSPACE"
+    assert lib.sparda_status_string(99) == b"SPARDA_ERR_UNKNOWN"
+
+
+P = 1 << 20  # a 16-byte-aligned dummy address; never dereferenced (validation fails first)
+
+
+def _sel(lib, **kw):
+    a = dict(f=P, kc=P, s=P, dtype=1, B=1, Hkv=8, Tq=1, q_start=4095, T=4096, d=128, kernel=32, stride=16, block=64,
+             tile=64, scale=0.088)
+    a.update(kw)
+    return lib.sparda_select_forecast(a["f"], a["kc"], a["s"], a["dtype"], a["B"], a["Hkv"], a["Tq"], a["q_start"],
+                                      a["T"], a["d"], a["kernel"], a["stride"], a["block"], a["tile"], a["scale"],
+                                      None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=7), 1, b"dtype"),
+    (dict(d=64), 2, b"head dim"),
+    (dict(T=4000, q_start=3999), 2, b"multiple of 64"),
+    (dict(q_start=100), 1, b"newest token"),
+    (dict(kernel=16), 2, b"kernel/stride"),
+    (dict(block=128), 2, b"block"),
+    (dict(tile=32), 2, b"tile"),
+    (dict(Tq=3, q_start=4093), 2, b"Tq"),
+    (dict(f=0), 1, b"f is NULL"),
+    (dict(kc=P + 4), 1, b"aligned"),
+    (dict(scale=float("inf")), 1, b"scale"),
+])
+def test_select_forecast_validation(lib, kw, status, needle):
+    assert _sel(lib, **kw) == status
+    assert needle in lib.sparda_last_error()
+
+
+def test_validation_messages_are_thread_local_and_cleared(lib):
+    assert _sel(lib, dtype=9) == 1
+    assert lib.sparda_last_error() != b""
+    assert _sel(lib, B=0) == 0  # empty batch: valid no-op, nothing launched
+    assert lib.sparda_last_error() == b""
+
+
+def test_multihead_and_attention_validation(lib):
+    st = lib.sparda_select_multihead(P, P, P, 1, 1, 12, 8, 1, 4095, 4096, 128, 32, 16, 64, 64, 0.1, None, 0, None)
+    assert st == 1 and b"multiple" in lib.sparda_last_error()
+    st = lib.sparda_select_multihead(P, P, P, 1, 1, 48, 8, 1, 4095, 4096, 128, 32, 16, 64, 64, 0.1, None, 0, None)
+    assert st == 2 and b"group" in lib.sparda_last_error()
+    need = lib.sparda_workspace_bytes(kbs.OP_SELECT_MULTIHEAD, 1, 32, 8, 1, 4096, 128, 0)
+    assert need > 0
+    st = lib.sparda_select_multihead(P, P, P, 1, 1, 32, 8, 1, 4095, 4096, 128, 32, 16, 64, 64, 0.1, P, need - 1, None)
+    assert st == 3 and b"workspace" in lib.sparda_last_error()
+    # attention: k out of range, bad kv_mode, staging with a prefill chunk
+    a = lambda **kw: lib.sparda_block_sparse_attn(
+        P, P, P, kw.get("mode", 0), P, P, 1, 1, 32, 8, kw.get("Tq", 1), 4096 - kw.get("Tq", 1), 4096, 128, 64, 64,
+        kw.get("k", 64), 0.1, P, 1 << 30, None)
+    assert a(k=0) == 1 and b"k = 0" in lib.sparda_last_error()
+    assert a(k=65) == 1
+    assert a(mode=2) == 1 and b"kv_mode" in lib.sparda_last_error()
+    assert a(mode=1, Tq=64) == 2 and b"staging" in lib.sparda_last_error()
+
+
+def test_topk_and_prefetch_validation(lib):
+    assert lib.sparda_topk_blocks(P, P, 4, 0, 1, None) == 2
+    assert lib.sparda_topk_blocks(P, P, 4, 8193, 1, None) == 2
+    assert lib.sparda_topk_blocks(P, P, 4, 64, 65, None) == 1
+    assert lib.sparda_topk_blocks(P, P, -1, 64, 4, None) == 1
+    assert lib.sparda_topk_blocks(0, P, 4, 64, 4, None) == 1
+    assert lib.sparda_prefetch_blocks(P, P, P, P, P, 1, 2, 8, 2048, 64, 128, 64, 5000, None) == 1
+    assert lib.sparda_prefetch_blocks(P, P, P, P, P, 1, 2, 8, 2048, 32, 128, 64, 0, None) == 2
+    assert lib.sparda_prefetch_blocks(0, P, P, P, P, 1, 2, 8, 2048, 64, 128, 64, 0, None) == 1
+
+
+def test_workspace_sizes(lib):
+    # decode attention splits a row's blocks over workgroups: partial outputs + (max, sum)
+    n = lib.sparda_workspace_bytes(kbs.OP_BLOCK_SPARSE_ATTN, 16, 32, 8, 1, 131072, 128, 64)
+    assert n > 0 and n % 256 == 0
+    assert lib.sparda_workspace_bytes(kbs.OP_SELECT_FORECAST, 16, 32, 8, 1, 131072, 128, 64) == 0
+    assert lib.sparda_workspace_bytes(99, 16, 32, 8, 1, 131072, 128, 64) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(kbs, "_LIB", None)
+    monkeypatch.setattr(kbs, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        kbs.load()
