@@ -20,7 +20,51 @@
 
 namespace sparda {
 
-constexpr int kAttnTargetWaves = 4096;  // aim: ~16 waves per CU over the grid
+constexpr int kAttnTargetWaves = 2048;  // 8 resident waves per CU at ~200 VGPRs
+constexpr int kAttnMaxSplits = 64;
+
+// Reduce-scatter of G partial dot products over the 16 lanes of a key row.
+// Lane c keeps its query slots in the order head = slot XOR mask(c), with
+// mask(c) built from lane bits 3 and 2. Then a lane and its row_ror:8 partner
+// (bit 3 flipped) exchange half of their slots, a lane and its half-mirror
+// partner (bit 2 flipped) exchange half of the rest, and a quad butterfly
+// finishes the sum: each lane ends with the full score of head mask(c), and the
+// four lanes that share a head hold bitwise-identical values.
+template <int G>
+__device__ __forceinline__ int slot_head(int slot, int c) {
+  if constexpr (G == 1) {
+    return 0;
+  } else if constexpr (G == 2) {
+    return slot ^ ((c >> 3) & 1);
+  } else {
+    const int mask = (((c >> 3) & 1) << 1) | ((c >> 2) & 1);
+    return (slot & ~3) | ((slot & 3) ^ mask);  // G = 8: two independent groups of 4
+  }
+}
+
+template <int G>
+__device__ __forceinline__ void reduce_scatter16(const float* part, float* out) {
+  if constexpr (G == 1) {
+    out[0] = row16_sum(part[0]);
+  } else if constexpr (G == 2) {
+    float a = part[0] + dpp<0x128>(part[1]);  // row_ror:8
+    a += dpp<0x141>(a);                       // row_half_mirror
+    a += dpp<0xB1>(a);
+    a += dpp<0x4E>(a);
+    out[0] = a;
+  } else {
+#pragma unroll
+    for (int grp = 0; grp < G / 4; ++grp) {
+      const float* pp = part + 4 * grp;
+      const float a0 = pp[0] + dpp<0x128>(pp[2]);
+      const float a1 = pp[1] + dpp<0x128>(pp[3]);
+      float b = a0 + dpp<0x141>(a1);
+      b += dpp<0xB1>(b);
+      b += dpp<0x4E>(b);
+      out[grp] = b;
+    }
+  }
+}
 
 template <typename Tag, int G>
 __global__ __launch_bounds__(64) void attn_decode_kernel(
@@ -33,6 +77,7 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(
   constexpr int KPI = kWave / LPK;   // keys per load instruction
   constexpr int NIT = kBlock / KPI;  // load instructions per block
   constexpr int RB = kHeadDim * DT<Tag>::kBytes;
+  constexpr int GR = G < 4 ? 1 : G / 4;  // scores each lane holds after the reduce-scatter
   __shared__ float s_p[kBlock * G];
 
   const long row = blockIdx.y;
@@ -41,9 +86,9 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(
   const int c = lane % LPK;
   const int r = lane / LPK;
 
-  u32x4 qv[G];
+  u32x4 qs[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) qv[g] = load16(q + (row * G + g) * RB + c * 16);
+  for (int s = 0; s < G; ++s) qs[s] = load16(q + (row * G + slot_head<G>(s, c & 15)) * RB + c * 16);
 
   float acc[G][E];
   float m_run[G], l_run[G];
@@ -57,29 +102,51 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(
 
   const int j0 = split * bps;
   const int j1 = min(k, j0 + bps);
-  for (int j = j0; j < j1; ++j) {
-    const int beta = idx[row * k + j];
-    if (beta < 0 || beta >= nB) continue;  // -1 padding; out-of-range ignored
-    const int nvalid = min(kBlock, p - beta * kBlock + 1);
-    if (nvalid <= 0) continue;
-    const long tok0 = kv_mode == 0 ? row * (long)T + (long)beta * kBlock : (row * k + j) * (long)kBlock;
-    const uint8_t* kb = kbuf + tok0 * RB + c * 16;
-    const uint8_t* vb = vbuf + tok0 * RB + c * 16;
+  const int32_t* idx_row = idx + row * k;
+  auto next_valid = [&](int j) {
+    for (; j < j1; ++j) {
+      const int b = idx_row[j];
+      if (b >= 0 && b < nB && b * kBlock <= p) break;  // -1 padding / out of range / future block
+    }
+    return j;
+  };
+  auto tok0_of = [&](int j, int beta) -> long {
+    return kv_mode == 0 ? row * (long)T + (long)beta * kBlock : (row * k + j) * (long)kBlock;
+  };
 
-    u32x4 kv[NIT], vv[NIT];
+  u32x4 kv[NIT], vv[NIT];
+  int j = next_valid(j0);
+  if (j < j1) {
+    const uint8_t* kb = kbuf + tok0_of(j, idx_row[j]) * RB + c * 16;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) kv[it] = load16_nt(kb + (it * KPI + r) * RB);
+  }
+  while (j < j1) {
+    const int beta = idx_row[j];
+    const int nvalid = min(kBlock, p - beta * kBlock + 1);
+    const uint8_t* vb = vbuf + tok0_of(j, beta) * RB + c * 16;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) vv[it] = load16_nt(vb + (it * KPI + r) * RB);
 
-    // scores -> LDS [key][g]
+    // QK: scores -> LDS [key][g]
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int key = it * KPI + r;
+      float part[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float s = group_sum<LPK>(dot16<Tag>(qv[g], kv[it], 0.f));
-        if (c == g) s_p[key * G + g] = key < nvalid ? s * scale : -INFINITY;
+      for (int s = 0; s < G; ++s) part[s] = dot16<Tag>(qs[s], kv[it], 0.f);
+      if constexpr (LPK == 32) {  // fp32: 32 lanes per key; fold the upper 16 first
+#pragma unroll
+        for (int s = 0; s < G; ++s) part[s] += xor_shfl(part[s], 16);
+      }
+      float sc[GR];
+      reduce_scatter16<G>(part, sc);
+      constexpr int HL = G >= 4 ? 4 : (G == 2 ? 8 : 16);  // lanes per head after the scatter
+      if ((c & (HL - 1)) == 0 && c < 16) {
+        const int h = (c & 15) / HL;
+#pragma unroll
+        for (int gr = 0; gr < GR; ++gr)
+          s_p[key * G + 4 * gr + h] = key < nvalid ? sc[gr] * scale : -INFINITY;
       }
     }
     __syncthreads();
@@ -97,6 +164,13 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(
       s_p[lane * G + g] = pr;
     }
     __syncthreads();
+    // prefetch the next block's keys while the values are consumed
+    const int jn = next_valid(j + 1);
+    if (jn < j1) {
+      const uint8_t* kb = kbuf + tok0_of(jn, idx_row[jn]) * RB + c * 16;
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) kv[it] = load16_nt(kb + (it * KPI + r) * RB);
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -115,6 +189,7 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(
         for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pg[g], v[e], acc[g][e]);
     }
     __syncthreads();
+    j = jn;
   }
 
   // reduce the KPI key rows
@@ -151,33 +226,60 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(
   }
 }
 
-// One workgroup per (row, head): thread = output channel.
+// One 256-thread workgroup per row merges the row's splits for all G heads:
+// weights exp(m_s - M) / L per (split, head) go to LDS first, then every
+// output channel sums its splits with independent loads.
 template <typename Tag>
-__global__ __launch_bounds__(kHeadDim) void attn_combine_kernel(const float* __restrict__ part_o,
-                                                                const float2* __restrict__ part_ml,
-                                                                uint8_t* __restrict__ out, int G,
-                                                                int splits) {
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                           const float2* __restrict__ part_ml,
+                                                           uint8_t* __restrict__ out, int G,
+                                                           int splits) {
+  __shared__ float2 s_ml[kAttnMaxSplits * 8];
+  __shared__ float s_w[kAttnMaxSplits * 8];
+  __shared__ float s_M[8], s_iL[8];
   const long row = blockIdx.x;
-  const int g = blockIdx.y;
-  const int ch = threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[(row * splits + s) * G + g].x);
-  float L = 0.f, O = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      const float2 ml = part_ml[(row * splits + s) * G + g];
-      if (ml.x == -INFINITY) continue;
-      const float w = fast_exp(ml.x - M);
-      L += ml.y * w;
-      O += part_o[(((row * splits + s) * G + g) * kHeadDim) + ch] * w;
-    }
+  const int t = threadIdx.x;
+  const int n = splits * G;
+  for (int i = t; i < n; i += 256) s_ml[i] = part_ml[row * n + i];
+  __syncthreads();
+  if (t < G) {
+    float M = -INFINITY;
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, s_ml[s * G + t].x);
+    float L = 0.f;
+    if (M != -INFINITY)
+      for (int s = 0; s < splits; ++s) {
+        const float2 ml = s_ml[s * G + t];
+        if (ml.x != -INFINITY) L += ml.y * fast_exp(ml.x - M);
+      }
+    s_M[t] = M;
+    s_iL[t] = L > 0.f ? 1.f / L : 0.f;
   }
-  const float o = L > 0.f ? O / L : 0.f;
-  const long off = (row * G + g) * kHeadDim + ch;
-  if constexpr (DT<Tag>::kBytes == 2) {
-    reinterpret_cast<__bf16*>(out)[off] = (__bf16)o;
-  } else {
-    reinterpret_cast<float*>(out)[off] = o;
+  __syncthreads();
+  for (int i = t; i < n; i += 256) {
+    const float2 ml = s_ml[i];
+    const int g = i % G;
+    s_w[i] = ml.x == -INFINITY ? 0.f : fast_exp(ml.x - s_M[g]) * s_iL[g];
+  }
+  __syncthreads();
+  for (int o = t; o < G * kHeadDim; o += 256) {
+    const int g = o / kHeadDim;
+    const float* src = part_o + (row * splits * G + g) * kHeadDim + (o % kHeadDim);
+    float acc = 0.f;
+    int s = 0;
+    for (; s + 8 <= splits; s += 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = src[(long)(s + u) * G * kHeadDim];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc = fmaf(x[u], s_w[(s + u) * G + g], acc);
+    }
+    for (; s < splits; ++s) acc = fmaf(src[(long)s * G * kHeadDim], s_w[s * G + g], acc);
+    const long off = row * G * kHeadDim + o;
+    if constexpr (DT<Tag>::kBytes == 2) {
+      reinterpret_cast<__bf16*>(out)[off] = (__bf16)acc;
+    } else {
+      reinterpret_cast<float*>(out)[off] = acc;
+    }
   }
 }
 
@@ -186,6 +288,7 @@ int decode_attn_splits(const AttnDims& d) {
   long want = (kAttnTargetWaves + rows - 1) / rows;
   if (want < 1) want = 1;
   if (want > d.k) want = d.k;
+  if (want > kAttnMaxSplits) want = kAttnMaxSplits;
   // equal block ranges
   const int bps = (int)((d.k + want - 1) / want);
   return (d.k + bps - 1) / bps;
@@ -218,8 +321,8 @@ static void launch_attn_g(const void* q, const void* k, const void* v, const int
                      (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, part_o, part_ml,
                      (uint8_t*)out, d.T, d.nB, d.k, d.kv_mode, d.q_start, bps, splits, d.scale);
   if (splits > 1)
-    hipLaunchKernelGGL(attn_combine_kernel<Tag>, dim3(rows, G), dim3(kHeadDim), 0, s, part_o,
-                       part_ml, (uint8_t*)out, G, splits);
+    hipLaunchKernelGGL(attn_combine_kernel<Tag>, dim3(rows), dim3(256), 0, s, part_o, part_ml,
+                       (uint8_t*)out, G, splits);
 }
 
 hipError_t launch_attn_decode(const void* q, const void* k, const void* v, const int32_t* idx,

@@ -202,17 +202,25 @@ __global__ __launch_bounds__(256) void mhsel_pool_kernel(MhWs ws, float* __restr
   const int nwin = 4 * nblk + 1;
   const int wstart = 4 * beta0 - 1;
 
-  if (threadIdx.x < G) {
-    const int g = threadIdx.x;
-    float m = -INFINITY;
-    for (int c = 0; c < chunks; ++c) m = fmaxf(m, ws.stats[(row * chunks + c) * G + g].x);
-    float z = 0.f;
-    for (int c = 0; c < chunks; ++c) {
-      const float2 st = ws.stats[(row * chunks + c) * G + g];
-      if (st.x != -INFINITY) z += st.y * fast_exp(st.x - m);
+  // Combine the per-chunk (max, sum of exp) of each head: one wave per head,
+  // lanes read chunks in parallel.
+  {
+    const int lane = threadIdx.x % kWave;
+    for (int g = threadIdx.x / kWave; g < G; g += (int)blockDim.x / kWave) {
+      float m = -INFINITY;
+      for (int c = lane; c < chunks; c += kWave) m = fmaxf(m, ws.stats[(row * chunks + c) * G + g].x);
+      m = wave_max(m);
+      float z = 0.f;
+      for (int c = lane; c < chunks; c += kWave) {
+        const float2 st = ws.stats[(row * chunks + c) * G + g];
+        if (st.x != -INFINITY) z += st.y * fast_exp(st.x - m);
+      }
+      z = wave_sum(z);
+      if (lane == 0) {
+        s_m[g] = m;
+        s_iz[g] = 1.f / z;
+      }
     }
-    s_m[g] = m;
-    s_iz[g] = 1.f / z;
   }
   __syncthreads();
   for (int lw = threadIdx.x; lw < nwin; lw += blockDim.x) {

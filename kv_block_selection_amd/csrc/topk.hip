@@ -3,13 +3,14 @@
 // keep the top-k).
 //
 // One 256-thread workgroup per row. Scores become order-preserving 32-bit keys
-// (larger key <=> larger score; -inf and padding become key 0). A 4-pass
-// MSB-first radix select (8-bit digits, LDS histograms) finds the k-th largest
-// key K* and how many keys equal to K* must be taken. Thread t owns the
+// (larger key <=> larger score; -0 ranks as +0; -inf and padding become key 0).
+// A 4-pass MSB-first radix select (8-bit digits, LDS histograms) finds the k-th
+// largest key K* and how many keys equal to K* must be taken. Thread t owns the
 // contiguous index range [t*NPT, (t+1)*NPT), so exclusive scans in thread order
 // are scans in block-index order: they rank the ties (lower index first) and
 // give every selected block its output slot, which makes the output ascending
-// without a sort. Exact: the result depends only on the input bits.
+// without a sort. Scans are DPP wave scans plus one LDS exchange of the four
+// wave totals. Exact: the result depends only on the input bits.
 #include "common.h"
 #include "launch.h"
 
@@ -21,28 +22,30 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive scan over 256 threads (Hillis-Steele in LDS); returns the total too.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* buf, int& total) {
-  const int t = threadIdx.x;
-  buf[t] = v;
+// Exclusive scan over the 256 threads in thread order; also returns the total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& total) {
+  const int lane = threadIdx.x % kWave;
+  const int wid = threadIdx.x / kWave;
+  const int incl = wave_incl_scan(v);
+  if (lane == kWave - 1) wave_tot[wid] = incl;
   __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int add = t >= off ? buf[t - off] : 0;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int t = wave_tot[w];
+    before += w < wid ? t : 0;
+    total += t;
   }
-  const int incl = buf[t];
-  total = buf[255];
   __syncthreads();
-  return incl - v;
+  return before + incl - v;
 }
 
 template <int NPT>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores,
                                                    int32_t* __restrict__ idx, int nB, int k) {
   __shared__ int hist[256];
-  __shared__ int scan_buf[256];
+  __shared__ int wave_tot[4];
   __shared__ uint32_t s_digit;
   __shared__ int s_above;
 
@@ -59,12 +62,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
     n_cand_local += key[j] != 0u;
   }
   int n_cand;
-  block_exclusive_scan(n_cand_local, scan_buf, n_cand);
+  block_exclusive_scan(n_cand_local, wave_tot, n_cand);
   const int kk = min(k, n_cand);
 
   uint32_t prefix = 0, pmask = 0;
-  int remaining = kk;  // how many of the still-open keys must be taken
-  if (kk > 0) {
+  int remaining = kk;  // how many keys that match the prefix must still be taken
+  if (kk > 0 && kk < n_cand) {
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
       hist[t] = 0;
@@ -73,10 +76,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
       for (int j = 0; j < NPT; ++j)
         if (key[j] != 0u && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 255u], 1);
       __syncthreads();
-      // suffix sums: above(d) = #keys in digits > d
-      const int h = hist[255 - t];  // thread t handles digit 255 - t
+      // thread t handles digit 255 - t: above = #matching keys in larger digits
+      const int h = hist[255 - t];
       int tot;
-      const int above = block_exclusive_scan(h, scan_buf, tot);
+      const int above = block_exclusive_scan(h, wave_tot, tot);
       if (above < remaining && remaining <= above + h) {
         s_digit = 255u - (uint32_t)t;
         s_above = above;
@@ -85,24 +88,28 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
       prefix |= s_digit << shift;
       pmask |= 255u << shift;
       remaining -= s_above;
-      __syncthreads();
+      // the next pass rewrites hist only after its own barrier; s_digit and
+      // s_above are rewritten only after the barriers inside the next scan
     }
   }
-  const uint32_t kstar = prefix;  // k-th largest key (when kk > 0)
+  // kk == n_cand: every candidate is taken (K* = smallest candidate key is not
+  // needed: take all keys != 0).
+  const bool take_all = kk == n_cand;
+  const uint32_t kstar = prefix;
 
   // Rank the keys equal to K* in index order; take the first `remaining`.
   int eq_local = 0;
 #pragma unroll
-  for (int j = 0; j < NPT; ++j) eq_local += (kk > 0 && key[j] == kstar);
+  for (int j = 0; j < NPT; ++j) eq_local += (!take_all && key[j] == kstar);
   int eq_total;
-  int eq_rank = block_exclusive_scan(eq_local, scan_buf, eq_total);
+  int eq_rank = block_exclusive_scan(eq_local, wave_tot, eq_total);
   bool sel[NPT];
   int sel_local = 0;
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
     bool s = false;
-    if (kk > 0 && key[j] != 0u) {
-      if (key[j] > kstar) {
+    if (key[j] != 0u) {
+      if (take_all || key[j] > kstar) {
         s = true;
       } else if (key[j] == kstar) {
         s = eq_rank < remaining;
@@ -113,7 +120,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
     sel_local += s;
   }
   int sel_total;
-  int pos = block_exclusive_scan(sel_local, scan_buf, sel_total);
+  int pos = block_exclusive_scan(sel_local, wave_tot, sel_total);
   int32_t* dst = idx + row * k;
 #pragma unroll
   for (int j = 0; j < NPT; ++j)
