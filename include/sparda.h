@@ -134,7 +134,8 @@ int sparda_topk_blocks(const float* blk_scores, int32_t* idx, int rows, int nB, 
  * Query i (position p = q_start + i) of head qh attends, with softmax of
  * scale * q . k_j, over every key j <= p of the blocks listed for its KV head
  * and tile. Duplicate indices are not allowed. A query with no key gets 0.
- * ws: sparda_workspace_bytes(SPARDA_OP_BLOCK_SPARSE_ATTN, ...) bytes.
+ * ws: sparda_workspace_bytes(SPARDA_OP_BLOCK_SPARSE_ATTN, ...) bytes (partial
+ * results of the block ranges a row is split into; no initial contents needed).
  */
 int sparda_block_sparse_attn(const void* q, const void* k, const void* v, int kv_mode,
                              const int32_t* idx, void* out, int dtype, int B, int Hq, int Hkv,

@@ -15,12 +15,19 @@
 //   PV  - the same lane layout over V; each lane accumulates G x 8 outputs for
 //         its key row, reading p[key][0..G) from LDS as one broadcast.
 // A combine kernel merges the per-split (max, sum, unnormalised output).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace sparda {
 
-constexpr int kAttnTargetWaves = 2048;  // 8 resident waves per CU at ~200 VGPRs
+#ifndef SPARDA_ATTN_TARGET_WAVES
+#define SPARDA_ATTN_TARGET_WAVES 2048
+#endif
+// Split a decode batch's rows into block ranges until the grid holds about this
+// many one-wave workgroups (8 resident per CU at ~250 VGPRs).
+constexpr int kAttnTargetWaves = SPARDA_ATTN_TARGET_WAVES;
 constexpr int kAttnMaxSplits = 64;
 
 // Reduce-scatter of G partial dot products over the 16 lanes of a key row.
@@ -66,8 +73,13 @@ __device__ __forceinline__ void reduce_scatter16(const float* part, float* out) 
   }
 }
 
+#ifndef SPARDA_ATTN_WAVES_PER_EU
+#define SPARDA_ATTN_WAVES_PER_EU 2
+#endif
+
 template <typename Tag, int G>
-__global__ __launch_bounds__(64) void attn_decode_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SPARDA_ATTN_WAVES_PER_EU)))
+void attn_decode_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ kbuf, const uint8_t* __restrict__ vbuf,
     const int32_t* __restrict__ idx, float* __restrict__ part_o, float2* __restrict__ part_ml,
     uint8_t* __restrict__ out, int T, int nB, int k, int kv_mode, int p, int bps, int splits,
@@ -75,13 +87,16 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(
   constexpr int E = DT<Tag>::kElems;
   constexpr int LPK = kHeadDim / E;  // lanes per key row
   constexpr int KPI = kWave / LPK;   // keys per load instruction
-  constexpr int NIT = kBlock / KPI;  // load instructions per block
+  constexpr int CK = 32;             // keys per pipeline stage (half a block)
+  constexpr int NIT = CK / KPI;      // load instructions per stage
   constexpr int RB = kHeadDim * DT<Tag>::kBytes;
   constexpr int GR = G < 4 ? 1 : G / 4;  // scores each lane holds after the reduce-scatter
-  __shared__ float s_p[kBlock * G];
+  constexpr bool kBf16 = DT<Tag>::kBytes == 2;
+  __shared__ float s_p[CK * G];          // scores (and fp32 probabilities)
+  __shared__ uint32_t s_p2[CK / 2 * G];  // bf16 probability pairs
 
-  const long row = blockIdx.y;
-  const int split = blockIdx.x;
+  const long row = blockIdx.x;  // rows on the fast axis: a row's splits share an XCD
+  const int split = blockIdx.y;
   const int lane = threadIdx.x;
   const int c = lane % LPK;
   const int r = lane / LPK;
@@ -101,32 +116,35 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(
   }
 
   const int j0 = split * bps;
-  const int j1 = min(k, j0 + bps);
+  const int j1 = min(k, j0 + bps);  // >= j0 + 1: every split owns at least one slot
   const int32_t* idx_row = idx + row * k;
-  auto next_valid = [&](int j) {
-    for (; j < j1; ++j) {
-      const int b = idx_row[j];
-      if (b >= 0 && b < nB && b * kBlock <= p) break;  // -1 padding / out of range / future block
-    }
-    return j;
+  // Stage q = half h of slot j0 + q/2: its first token and its number of valid
+  // keys. Padding, out-of-range and wholly-future slots read block 0 of the
+  // row (a valid address) with every key masked.
+  auto stage_of = [&](int q, int& nvalid) -> long {
+    const int j = j0 + (q >> 1);
+    const int h = q & 1;
+    const int b = idx_row[j];
+    const bool ok = b >= 0 && b < nB && b * kBlock <= p;
+    nvalid = ok ? max(0, min(CK, p - b * kBlock - h * CK + 1)) : 0;
+    const long base = kv_mode != 0 ? (row * k + j) * (long)kBlock : row * (long)T + (long)(ok ? b : 0) * kBlock;
+    return base + h * CK;
   };
-  auto tok0_of = [&](int j, int beta) -> long {
-    return kv_mode == 0 ? row * (long)T + (long)beta * kBlock : (row * k + j) * (long)kBlock;
-  };
+  const int nstage = 2 * (j1 - j0);
 
   u32x4 kv[NIT], vv[NIT];
-  int j = next_valid(j0);
-  if (j < j1) {
-    const uint8_t* kb = kbuf + tok0_of(j, idx_row[j]) * RB + c * 16;
+  int nvalid;
+  long tok0 = stage_of(0, nvalid);
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) kv[it] = load16_nt(kb + (it * KPI + r) * RB);
-  }
-  while (j < j1) {
-    const int beta = idx_row[j];
-    const int nvalid = min(kBlock, p - beta * kBlock + 1);
-    const uint8_t* vb = vbuf + tok0_of(j, beta) * RB + c * 16;
+  for (int it = 0; it < NIT; ++it) kv[it] = load16_nt(kbuf + (tok0 + it * KPI + r) * RB + c * 16);
+
+  // One stage of 32 keys: V loads go out first, then QK on the keys already in
+  // flight, the online softmax, the next stage's key loads (PREFETCH), then PV.
+  // The last stage is peeled so that every load in the steady-state body is
+  // unconditional and the compiler's wait counts stay exact.
+  auto body = [&](int q, auto prefetch) {
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) vv[it] = load16_nt(vb + (it * KPI + r) * RB);
+    for (int it = 0; it < NIT; ++it) vv[it] = load16_nt(vbuf + (tok0 + it * KPI + r) * RB + c * 16);
 
     // QK: scores -> LDS [key][g]
 #pragma unroll
@@ -150,47 +168,88 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(
       }
     }
     __syncthreads();
-    // online softmax, lane = key
-    float alpha[G];
+    // online softmax, lane = key (lanes 32..63 idle)
+    float alpha[G], pr[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float s = s_p[lane * G + g];
+      const float s = lane < CK ? s_p[lane * G + g] : -INFINITY;
       const float mb = wave_max(s);
-      const float mn = fmaxf(m_run[g], mb);  // finite: key 0 of the block is always valid
-      alpha[g] = fast_exp(m_run[g] - mn);    // exp(-inf) = 0 on the first block
-      const float pr = fast_exp(s - mn);
-      l_run[g] = l_run[g] * alpha[g] + wave_sum(pr);
+      const float mn = fmaxf(m_run[g], mb);
+      const bool none = mn == -INFINITY;  // no valid key seen yet
+      alpha[g] = none ? 1.f : fast_exp(m_run[g] - mn);
+      pr[g] = none ? 0.f : fast_exp(s - mn);
+      l_run[g] = l_run[g] * alpha[g] + wave_sum(pr[g]);
       m_run[g] = mn;
-      s_p[lane * G + g] = pr;
+    }
+    if constexpr (kBf16) {
+      // bf16 pairs (p[key], p[key + 4]) for the keys with key % 8 < 4; the
+      // partner sits 4 lanes up in the same DPP row (row_ror:12)
+      float up[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) up[g] = dpp<0x12C>(pr[g]);
+      if ((lane & 4) == 0 && lane < CK) {
+        const int slot = (lane >> 3) * 4 + (lane & 3);
+#pragma unroll
+        for (int g = 0; g < G; ++g) s_p2[slot * G + g] = pack_bf16(pr[g], up[g]);
+      }
+    } else {
+      if (lane < CK) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) s_p[lane * G + g] = pr[g];
+      }
     }
     __syncthreads();
-    // prefetch the next block's keys while the values are consumed
-    const int jn = next_valid(j + 1);
-    if (jn < j1) {
-      const uint8_t* kb = kbuf + tok0_of(jn, idx_row[jn]) * RB + c * 16;
+    if constexpr (decltype(prefetch)::value) {
+      tok0 = stage_of(q + 1, nvalid);
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) kv[it] = load16_nt(kb + (it * KPI + r) * RB);
+      for (int it = 0; it < NIT; ++it) kv[it] = load16_nt(kbuf + (tok0 + it * KPI + r) * RB + c * 16);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[g][e] *= alpha[g];
+    if constexpr (kBf16) {
+      // PV on packed pairs: keys 8jp + r and 8jp + 4 + r come from loads 2jp
+      // and 2jp + 1; v_perm_b32 interleaves their channels, v_dot2 applies the
+      // pair of probabilities
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int key = it * KPI + r;
-      float v[E];
-      unpack<Tag>(vv[it], v);
-      float pg[G];
+      for (int jp = 0; jp < NIT / 2; ++jp) {
+        uint32_t pp[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) pg[g] = s_p[key * G + g];
+        for (int g = 0; g < G; ++g) pp[g] = s_p2[(jp * 4 + r) * G + g];
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t a = vv[2 * jp][i], b = vv[2 * jp + 1][i];
+          const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x05040100u);  // channel 2i of both keys
+          const uint32_t hi = __builtin_amdgcn_perm(b, a, 0x07060302u);  // channel 2i + 1
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pg[g], v[e], acc[g][e]);
+          for (int g = 0; g < G; ++g) {
+            const bf16x2 pg = __builtin_bit_cast(bf16x2, pp[g]);
+            acc[g][2 * i] = __builtin_amdgcn_fdot2_f32_bf16(pg, __builtin_bit_cast(bf16x2, lo), acc[g][2 * i], false);
+            acc[g][2 * i + 1] =
+                __builtin_amdgcn_fdot2_f32_bf16(pg, __builtin_bit_cast(bf16x2, hi), acc[g][2 * i + 1], false);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int key = it * KPI + r;
+        float v[E];
+        unpack<Tag>(vv[it], v);
+        float pg[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) pg[g] = s_p[key * G + g];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pg[g], v[e], acc[g][e]);
+      }
     }
     __syncthreads();
-    j = jn;
-  }
+  };
+  for (int q = 0; q < nstage - 1; ++q) body(q, std::true_type{});
+  body(nstage - 1, std::false_type{});
 
   // reduce the KPI key rows
 #pragma unroll
@@ -201,85 +260,75 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(
       for (int m = LPK; m < kWave; m <<= 1) x += xor_shfl(x, m);
       acc[g][e] = x;
     }
-  if (r != 0) return;
 
   if (splits == 1) {
     // final: normalise and store in the storage dtype
+    if (r == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float inv = l_run[g] > 0.f ? 1.f / l_run[g] : 0.f;
-      float o[E];
+      for (int g = 0; g < G; ++g) {
+        const float inv = l_run[g] > 0.f ? 1.f / l_run[g] : 0.f;
+        float o[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) o[e] = acc[g][e] * inv;
-      store16(out + (row * G + g) * RB + c * 16, pack<Tag>(o));
+        for (int e = 0; e < E; ++e) o[e] = acc[g][e] * inv;
+        store16(out + (row * G + g) * RB + c * 16, pack<Tag>(o));
+      }
     }
     return;
   }
   const long ps = row * splits + split;
+  if (r == 0) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float* po = part_o + ((ps * G + g) * kHeadDim) + c * E;
+    for (int g = 0; g < G; ++g) {
+      float* po = part_o + ((ps * G + g) * kHeadDim) + c * E;
 #pragma unroll
-    for (int e = 0; e < E; e += 4)
-      *reinterpret_cast<float4*>(po + e) = make_float4(acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]);
-    if (c == 0) part_ml[ps * G + g] = make_float2(m_run[g], l_run[g]);
+      for (int e = 0; e < E; e += 4)
+        *reinterpret_cast<float4*>(po + e) = make_float4(acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]);
+      if (c == 0) part_ml[ps * G + g] = make_float2(m_run[g], l_run[g]);
+    }
   }
 }
 
-// One 256-thread workgroup per row merges the row's splits for all G heads:
-// weights exp(m_s - M) / L per (split, head) go to LDS first, then every
-// output channel sums its splits with independent loads.
-template <typename Tag>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
-                                                           const float2* __restrict__ part_ml,
-                                                           uint8_t* __restrict__ out, int G,
-                                                           int splits) {
-  __shared__ float2 s_ml[kAttnMaxSplits * 8];
-  __shared__ float s_w[kAttnMaxSplits * 8];
-  __shared__ float s_M[8], s_iL[8];
+// Merge the splits of one (row, head): thread = output channel. All the
+// row's (max, sum) pairs and the channel's partial sums are loaded in one
+// batch (independent loads), so the kernel costs one memory round trip.
+template <typename Tag, int MAXS>
+__global__ __launch_bounds__(kHeadDim) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                                const float2* __restrict__ part_ml,
+                                                                uint8_t* __restrict__ out, int G,
+                                                                int splits) {
   const long row = blockIdx.x;
-  const int t = threadIdx.x;
-  const int n = splits * G;
-  for (int i = t; i < n; i += 256) s_ml[i] = part_ml[row * n + i];
-  __syncthreads();
-  if (t < G) {
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, s_ml[s * G + t].x);
-    float L = 0.f;
-    if (M != -INFINITY)
-      for (int s = 0; s < splits; ++s) {
-        const float2 ml = s_ml[s * G + t];
-        if (ml.x != -INFINITY) L += ml.y * fast_exp(ml.x - M);
+  const int g = blockIdx.y;
+  const int ch = threadIdx.x;
+  float2 ml[MAXS];
+  float po[MAXS];
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {
+    if (s < splits) {
+      ml[s] = part_ml[(row * splits + s) * G + g];
+      po[s] = part_o[((row * splits + s) * G + g) * kHeadDim + ch];
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s)
+    if (s < splits) M = fmaxf(M, ml[s].x);
+  float L = 0.f, O = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) {
+      if (s < splits && ml[s].x != -INFINITY) {
+        const float w = fast_exp(ml[s].x - M);
+        L = fmaf(ml[s].y, w, L);
+        O = fmaf(po[s], w, O);
       }
-    s_M[t] = M;
-    s_iL[t] = L > 0.f ? 1.f / L : 0.f;
-  }
-  __syncthreads();
-  for (int i = t; i < n; i += 256) {
-    const float2 ml = s_ml[i];
-    const int g = i % G;
-    s_w[i] = ml.x == -INFINITY ? 0.f : fast_exp(ml.x - s_M[g]) * s_iL[g];
-  }
-  __syncthreads();
-  for (int o = t; o < G * kHeadDim; o += 256) {
-    const int g = o / kHeadDim;
-    const float* src = part_o + (row * splits * G + g) * kHeadDim + (o % kHeadDim);
-    float acc = 0.f;
-    int s = 0;
-    for (; s + 8 <= splits; s += 8) {
-      float x[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = src[(long)(s + u) * G * kHeadDim];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc = fmaf(x[u], s_w[(s + u) * G + g], acc);
     }
-    for (; s < splits; ++s) acc = fmaf(src[(long)s * G * kHeadDim], s_w[s * G + g], acc);
-    const long off = row * G * kHeadDim + o;
-    if constexpr (DT<Tag>::kBytes == 2) {
-      reinterpret_cast<__bf16*>(out)[off] = (__bf16)acc;
-    } else {
-      reinterpret_cast<float*>(out)[off] = acc;
-    }
+  }
+  const float o = L > 0.f ? O / L : 0.f;
+  const long off = (row * G + g) * kHeadDim + ch;
+  if constexpr (DT<Tag>::kBytes == 2) {
+    reinterpret_cast<__bf16*>(out)[off] = (__bf16)o;
+  } else {
+    reinterpret_cast<float*>(out)[off] = o;
   }
 }
 
@@ -296,6 +345,7 @@ int decode_attn_splits(const AttnDims& d) {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workspace: [partial outputs][partial (max, sum)], 256-byte aligned.
 size_t decode_attn_ws_bytes(const AttnDims& d) {
   const int splits = decode_attn_splits(d);
   if (splits == 1) return 0;
@@ -317,12 +367,18 @@ static void launch_attn_g(const void* q, const void* k, const void* v, const int
     part_o = (float*)ws;
     part_ml = (float2*)((char*)ws + align256(n * kHeadDim * sizeof(float)));
   }
-  hipLaunchKernelGGL((attn_decode_kernel<Tag, G>), dim3(splits, rows), dim3(kWave), 0, s,
+  hipLaunchKernelGGL((attn_decode_kernel<Tag, G>), dim3(rows, splits), dim3(kWave), 0, s,
                      (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, part_o, part_ml,
                      (uint8_t*)out, d.T, d.nB, d.k, d.kv_mode, d.q_start, bps, splits, d.scale);
-  if (splits > 1)
-    hipLaunchKernelGGL(attn_combine_kernel<Tag>, dim3(rows), dim3(256), 0, s, part_o, part_ml,
-                       (uint8_t*)out, G, splits);
+  if (splits > 1) {
+    const dim3 grid(rows, G);
+    if (splits <= 16)
+      hipLaunchKernelGGL((attn_combine_kernel<Tag, 16>), grid, dim3(kHeadDim), 0, s, part_o, part_ml,
+                         (uint8_t*)out, G, splits);
+    else
+      hipLaunchKernelGGL((attn_combine_kernel<Tag, kAttnMaxSplits>), grid, dim3(kHeadDim), 0, s, part_o,
+                         part_ml, (uint8_t*)out, G, splits);
+  }
 }
 
 hipError_t launch_attn_decode(const void* q, const void* k, const void* v, const int32_t* idx,

@@ -45,8 +45,8 @@ __global__ __launch_bounds__(256) void fsel_decode_kernel(const uint8_t* __restr
   constexpr int ITER = (NWIN + R::SLOTS - 1) / R::SLOTS;
   __shared__ float s_win[ITER * R::SLOTS];
 
-  const long row = blockIdx.y;
-  const int beta0 = blockIdx.x * kFselBlocks;
+  const long row = blockIdx.x;  // rows on the fast axis: a row's chunks share an XCD
+  const int beta0 = blockIdx.y * kFselBlocks;
   const int nblk = min(kFselBlocks, nB - beta0);
   const int nwin = 4 * nblk + 1;
   const int wstart = 4 * beta0 - 1;
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void fsel_decode_kernel(const uint8_t* __restr
 hipError_t launch_select_forecast_decode(const void* f, const void* kc, float* scores, bool bf16,
                                          const SelectDims& d, hipStream_t s) {
   const int n_vis = min(d.W, (d.q_start - kKernel + 1) >= 0 ? (d.q_start - kKernel + 1) / kStride + 1 : 0);
-  dim3 grid((d.nB + kFselBlocks - 1) / kFselBlocks, d.B * d.Hkv);
+  dim3 grid(d.B * d.Hkv, (d.nB + kFselBlocks - 1) / kFselBlocks);
   if (bf16)
     hipLaunchKernelGGL(fsel_decode_kernel<BF16Tag>, grid, dim3(256), 0, s, (const uint8_t*)f,
                        (const uint8_t*)kc, scores, d.W, d.nB, n_vis, d.scale);

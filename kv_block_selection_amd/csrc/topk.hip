@@ -3,14 +3,19 @@
 // keep the top-k).
 //
 // One 256-thread workgroup per row. Scores become order-preserving 32-bit keys
-// (larger key <=> larger score; -0 ranks as +0; -inf and padding become key 0).
-// A 4-pass MSB-first radix select (8-bit digits, LDS histograms) finds the k-th
-// largest key K* and how many keys equal to K* must be taken. Thread t owns the
-// contiguous index range [t*NPT, (t+1)*NPT), so exclusive scans in thread order
-// are scans in block-index order: they rank the ties (lower index first) and
-// give every selected block its output slot, which makes the output ascending
-// without a sort. Scans are DPP wave scans plus one LDS exchange of the four
-// wave totals. Exact: the result depends only on the input bits.
+// (larger key <=> larger score; -0 ranks as +0; -inf and padding become key 0,
+// never taken). A block reduction gives the candidate count and the smallest
+// and largest candidate keys; the radix select then runs on x = key - kmin, so
+// its first digit already splits the row's actual range (float keys of one
+// row share their top bits, which would put every key in one or two bins).
+// Each pass histograms the next <= 8 bits of x among the keys that match the
+// prefix fixed so far (per-wave LDS histograms), one wave scans the bins and
+// fixes the digit holding the k-th largest; it stops as soon as that digit is
+// taken whole. Thread t owns the contiguous index range [t*NPT, (t+1)*NPT); one
+// packed exclusive scan in thread order (above-prefix count in the low 16
+// bits, equal-prefix count in the high 16) gives every selected block its
+// output slot, ranks ties by lower index, and keeps the output ascending
+// without a sort. Exact: the result depends only on the input bits.
 #include "common.h"
 #include "launch.h"
 
@@ -22,110 +27,156 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive scan over the 256 threads in thread order; also returns the total.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& total) {
-  const int lane = threadIdx.x % kWave;
-  const int wid = threadIdx.x / kWave;
-  const int incl = wave_incl_scan(v);
-  if (lane == kWave - 1) wave_tot[wid] = incl;
-  __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const int t = wave_tot[w];
-    before += w < wid ? t : 0;
-    total += t;
-  }
-  __syncthreads();
-  return before + incl - v;
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  for (int m = 1; m < kWave; m <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, m, kWave));
+  return v;
 }
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  for (int m = 1; m < kWave; m <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, kWave));
+  return v;
+}
+__device__ __forceinline__ int wave_isum(int v) {
+  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+struct TopkShared {
+  int hist[2][4][256];  // [ping-pong][wave][digit]
+  int wave_tot[4];
+  uint32_t wave_min[4], wave_max[4];
+  int wave_cnt[4];
+  uint32_t digit;
+  int above, done;
+};
 
 template <int NPT>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores,
                                                    int32_t* __restrict__ idx, int nB, int k) {
-  __shared__ int hist[256];
-  __shared__ int wave_tot[4];
-  __shared__ uint32_t s_digit;
-  __shared__ int s_above;
-
+  __shared__ TopkShared sh;
   const long row = blockIdx.x;
   const int t = threadIdx.x;
+  const int lane = t % kWave;
+  const int wid = t / kWave;
   const float* src = scores + row * nB;
 
   uint32_t key[NPT];
-  int n_cand_local = 0;
+  int cnt = 0;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
     const int b = t * NPT + j;
     key[j] = b < nB ? order_key(src[b]) : 0u;
-    n_cand_local += key[j] != 0u;
-  }
-  int n_cand;
-  block_exclusive_scan(n_cand_local, wave_tot, n_cand);
-  const int kk = min(k, n_cand);
-
-  uint32_t prefix = 0, pmask = 0;
-  int remaining = kk;  // how many keys that match the prefix must still be taken
-  if (kk > 0 && kk < n_cand) {
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      hist[t] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < NPT; ++j)
-        if (key[j] != 0u && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 255u], 1);
-      __syncthreads();
-      // thread t handles digit 255 - t: above = #matching keys in larger digits
-      const int h = hist[255 - t];
-      int tot;
-      const int above = block_exclusive_scan(h, wave_tot, tot);
-      if (above < remaining && remaining <= above + h) {
-        s_digit = 255u - (uint32_t)t;
-        s_above = above;
-      }
-      __syncthreads();
-      prefix |= s_digit << shift;
-      pmask |= 255u << shift;
-      remaining -= s_above;
-      // the next pass rewrites hist only after its own barrier; s_digit and
-      // s_above are rewritten only after the barriers inside the next scan
+    if (key[j] != 0u) {
+      ++cnt;
+      kmin = min(kmin, key[j]);
+      kmax = max(kmax, key[j]);
     }
   }
-  // kk == n_cand: every candidate is taken (K* = smallest candidate key is not
-  // needed: take all keys != 0).
-  const bool take_all = kk == n_cand;
-  const uint32_t kstar = prefix;
-
-  // Rank the keys equal to K* in index order; take the first `remaining`.
-  int eq_local = 0;
 #pragma unroll
-  for (int j = 0; j < NPT; ++j) eq_local += (!take_all && key[j] == kstar);
-  int eq_total;
-  int eq_rank = block_exclusive_scan(eq_local, wave_tot, eq_total);
-  bool sel[NPT];
-  int sel_local = 0;
+  for (int w = 0; w < 4; ++w) sh.hist[0][w][t] = 0;
+  cnt = wave_isum(cnt);
+  kmin = wave_umin(kmin);
+  kmax = wave_umax(kmax);
+  if (lane == 0) {
+    sh.wave_cnt[wid] = cnt;
+    sh.wave_min[wid] = kmin;
+    sh.wave_max[wid] = kmax;
+  }
+  __syncthreads();
+  int n_cand = 0;
+  kmin = 0xFFFFFFFFu;
+  kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    n_cand += sh.wave_cnt[w];
+    kmin = min(kmin, sh.wave_min[w]);
+    kmax = max(kmax, sh.wave_max[w]);
+  }
+  const int kk = min(k, n_cand);
+  const bool take_all = kk == n_cand;  // includes the empty row
+
+  // radix select on x = key - kmin over the bits below `lo`
+  uint32_t prefix = 0;
+  int remaining = kk;
+  int lo = take_all ? 0 : 32 - __clz(kmax - kmin);
+  int cur = 0;
+  while (lo > 0) {
+    const int sft = max(lo - 8, 0);
+    const uint32_t dmask = (1u << (lo - sft)) - 1u;
+    const uint32_t phi = lo >= 32 ? 0u : prefix >> lo;
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      if (key[j] != 0u) {
+        const uint32_t x = key[j] - kmin;
+        if ((lo >= 32 ? 0u : x >> lo) == phi) atomicAdd(&sh.hist[cur][wid][(x >> sft) & dmask], 1);
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) sh.hist[cur ^ 1][w][t] = 0;
+    __syncthreads();
+    if (wid == 0) {
+      // lane handles digits 255-4*lane .. 252-4*lane (descending)
+      int h[4], sum = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 255 - 4 * lane - i;
+        h[i] = sh.hist[cur][0][d] + sh.hist[cur][1][d] + sh.hist[cur][2][d] + sh.hist[cur][3][d];
+        sum += h[i];
+      }
+      int above = wave_incl_scan(sum) - sum;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (above < remaining && remaining <= above + h[i]) {
+          sh.digit = (uint32_t)(255 - 4 * lane - i);
+          sh.above = above;
+          sh.done = remaining == above + h[i];  // the whole digit is taken
+        }
+        above += h[i];
+      }
+    }
+    __syncthreads();
+    prefix |= sh.digit << sft;
+    remaining -= sh.above;
+    lo = sft;
+    cur ^= 1;
+    if (sh.done) break;
+    // sh.digit / above / done are rewritten only after the next pass's first barrier
+  }
+
+  // Packed scan: low 16 bits = keys above the prefix, high 16 = keys equal to it.
+  const uint32_t plo = lo >= 32 ? 0u : prefix >> lo;
+  int gt = 0, eq = 0;
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
-    bool s = false;
     if (key[j] != 0u) {
-      if (take_all || key[j] > kstar) {
-        s = true;
-      } else if (key[j] == kstar) {
-        s = eq_rank < remaining;
+      const uint32_t top = lo >= 32 ? 0u : (key[j] - kmin) >> lo;
+      gt += top > plo;
+      eq += top == plo;
+    }
+  }
+  const int packed = gt | (eq << 16);
+  const int incl = wave_incl_scan(packed);
+  if (lane == kWave - 1) sh.wave_tot[wid] = incl;
+  __syncthreads();
+  int before = incl - packed;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) before += w < wid ? sh.wave_tot[w] : 0;
+  int eq_rank = before >> 16;
+  int pos = (before & 0xFFFF) + min(eq_rank, remaining);
+  int32_t* dst = idx + row * k;
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    if (key[j] != 0u) {
+      const uint32_t top = lo >= 32 ? 0u : (key[j] - kmin) >> lo;
+      if (top > plo) {
+        dst[pos++] = t * NPT + j;
+      } else if (top == plo) {
+        if (eq_rank < remaining) dst[pos++] = t * NPT + j;
         ++eq_rank;
       }
     }
-    sel[j] = s;
-    sel_local += s;
   }
-  int sel_total;
-  int pos = block_exclusive_scan(sel_local, wave_tot, sel_total);
-  int32_t* dst = idx + row * k;
-#pragma unroll
-  for (int j = 0; j < NPT; ++j)
-    if (sel[j]) dst[pos++] = t * NPT + j;
-  for (int p = kk + t; p < k; p += 256) dst[p] = -1;
+  for (int q = kk + t; q < k; q += 256) dst[q] = -1;
 }
 
 hipError_t launch_topk(const float* scores, int32_t* idx, int rows, int nB, int k, hipStream_t s) {

@@ -1,0 +1,126 @@
+"""GPU parity at full workload sizes (sampled rows against the fp64 oracle),
+workspace reuse across calls, and HIP-graph replay against eager execution."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth.gpu as sg
+from synth import workloads as wl
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def gen(w, name, layer=0):
+    return sg.tensor(w.recipe(name, layer), w.shape(name), DEV)
+
+
+def bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+def test_attention_workspace_reuse_across_calls(gpu):
+    """One workspace buffer serves successive calls with different inputs."""
+    w = wl.C2_DECODE_32K
+    K, V = gen(w, "K"), gen(w, "V")
+    nbytes = gpu.workspace_bytes(gpu.OP_BLOCK_SPARSE_ATTN, w.B, w.Hq, w.Hkv, 1, w.T, w.k)
+    ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device=DEV)  # no initial contents needed
+    K64, V64 = parity.to_f64(K), parity.to_f64(V)
+    rng = np.random.default_rng(3)
+    for call in range(3):
+        Q = sg.tensor(wl.scaled(w, seed=100 + call).recipe("Q"), w.shape("Q"), DEV)
+        idx_np = np.stack([np.sort(rng.choice(w.nB, w.k, replace=False)) for _ in range(w.B * w.Hkv)])
+        idx_np = idx_np.reshape(w.B, w.Hkv, 1, w.k).astype(np.int32)
+        out = gpu.block_sparse_attn(Q, K, V, torch.from_numpy(idx_np).to(DEV), w.T, w.q_start, ws=ws)
+        torch.cuda.synchronize()
+        ref = oracle.block_sparse_attention(parity.to_f64(Q), K64, V64, idx_np, w.q_start, w.scale)
+        err = parity.check_attention(parity.to_f64(out), ref, parity.ATTN_ATOL_BF16)
+        say(f"call {call}: err {err:.2e}")
+
+
+def test_graph_replay_matches_eager(gpu):
+    """A decode step captured in a HIP graph gives the eager bits on every replay,
+    with eager work and synchronisations between replays."""
+    w = wl.C2_DECODE_32K
+    Q, K, V, F = gen(w, "Q"), gen(w, "K"), gen(w, "V"), gen(w, "F")
+    Kc = gpu.compress_keys(K)
+    scores = torch.empty((w.B, w.Hkv, 1, w.nB), dtype=torch.float32, device=DEV)
+    idx = torch.empty((w.B, w.Hkv, 1, w.k), dtype=torch.int32, device=DEV)
+    out = torch.empty_like(Q)
+    ws = torch.zeros(gpu.workspace_bytes(gpu.OP_BLOCK_SPARSE_ATTN, w.B, w.Hq, w.Hkv, 1, w.T, w.k),
+                     dtype=torch.uint8, device=DEV)
+
+    def step():
+        gpu.select_forecast(F, Kc, w.T, w.q_start, out=scores)
+        gpu.topk_blocks(scores, w.k, out=idx)
+        gpu.block_sparse_attn(Q, K, V, idx, w.T, w.q_start, out=out, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_s, ref_i, ref_o = scores.clone(), idx.clone(), out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        scores.fill_(-1.0)
+        idx.fill_(-7)
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(scores, ref_s), f"replay {rep}: scores"
+        assert torch.equal(idx, ref_i), f"replay {rep}: idx"
+        assert torch.equal(bits(out), bits(ref_o)), f"replay {rep}: attention"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(bits(out), bits(ref_o))
+
+
+def test_c3_full_size_sampled_parity(gpu):
+    """The 128K-context batch-16 decode workload, in the launch configuration the
+    benchmark times; the oracle recomputes sampled (sequence, KV head) rows."""
+    w = wl.C3_DECODE_128K
+    say("generating", w.name)
+    Q, K, V, F = gen(w, "Q"), gen(w, "K"), gen(w, "V"), gen(w, "F")
+    Kc = gpu.compress_keys(K)
+    sf = gpu.select_forecast(F, Kc, w.T, w.q_start)
+    sm = gpu.select_multihead(Q, Kc, w.T, w.q_start)
+    idx = gpu.topk_blocks(sf, w.k)
+    idx_m = gpu.topk_blocks(sm, w.k)
+    ws = torch.zeros(gpu.workspace_bytes(gpu.OP_BLOCK_SPARSE_ATTN, w.B, w.Hq, w.Hkv, 1, w.T, w.k),
+                     dtype=torch.uint8, device=DEV)
+    out = gpu.block_sparse_attn(Q, K, V, idx, w.T, w.q_start, ws=ws)
+    torch.cuda.synchronize()
+    # properties at full size
+    idx_np = idx.cpu().numpy()
+    assert np.all(np.diff(idx_np, axis=-1) > 0) and idx_np.min() >= 0 and idx_np.max() < w.nB
+    assert torch.isfinite(out.float()).all()
+    for b, h in [(0, 0), (7, 3), (15, 7)]:
+        say("row", b, h)
+        k64 = parity.to_f64(K[b, h])
+        parity.check_compress(parity.to_f64(Kc[b, h]), oracle.compress_keys(k64), "bf16")
+        kc64 = parity.to_f64(Kc[b, h])
+        ref_f = oracle.select_forecast_tile(parity.to_f64(F[b, h]), kc64, [w.q_start], w.T, w.scale)
+        parity.check_scores(parity.to_f64(sf[b, h, 0])[None], ref_f[None])
+        parity.check_topk_band(idx_np[b, h, 0][None], ref_f[None], w.k)
+        q_rows = parity.to_f64(Q[b, h * w.G:(h + 1) * w.G])
+        ref_m = oracle.select_multihead_tile(q_rows, kc64, [w.q_start], w.T, w.scale)
+        parity.check_scores(parity.to_f64(sm[b, h, 0])[None], ref_m[None])
+        parity.check_topk_band(idx_m.cpu().numpy()[b, h, 0][None], ref_m[None], w.k)
+        J = oracle.selected_keys(idx_np[b, h, 0], w.q_start)
+        v64 = parity.to_f64(V[b, h])
+        for g in range(w.G):
+            ref_o = oracle.attend(q_rows[g, 0], k64[J], v64[J], w.scale)
+            parity.check_attention(parity.to_f64(out[b, h * w.G + g, 0]), ref_o, parity.ATTN_ATOL_BF16)
