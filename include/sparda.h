@@ -85,7 +85,8 @@ int sparda_compress_keys(const void* k, void* k_cmp, int dtype, int B, int Hkv, 
  * query at position p when stride*w + kernel - 1 <= p. Block score of a query
  * = max of s over the visible windows whose token span meets the block; a
  * tile's score = max over its queries; -inf marks a block with no visible
- * window (not a candidate). Decode is Tq = 1, q_start = T - 1.
+ * window (not a candidate). Decode is Tq = 1, q_start = T - 1. A chunk of
+ * queries (Tq a multiple of 64) runs on the matrix cores and needs bf16.
  * ws: none needed (ws may be NULL, ws_bytes 0).
  */
 int sparda_select_forecast(const void* f, const void* k_cmp, float* blk_scores, int dtype, int B,
@@ -134,6 +135,8 @@ int sparda_topk_blocks(const float* blk_scores, int32_t* idx, int rows, int nB, 
  * Query i (position p = q_start + i) of head qh attends, with softmax of
  * scale * q . k_j, over every key j <= p of the blocks listed for its KV head
  * and tile. Duplicate indices are not allowed. A query with no key gets 0.
+ * A chunk of queries (Tq a multiple of 64) runs on the matrix cores and needs
+ * bf16 in cache mode.
  * ws: sparda_workspace_bytes(SPARDA_OP_BLOCK_SPARSE_ATTN, ...) bytes (partial
  * results of the block ranges a row is split into; no initial contents needed).
  */

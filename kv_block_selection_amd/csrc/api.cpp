@@ -185,7 +185,12 @@ SPARDA_EXPORT int sparda_select_forecast(const void* f, const void* k_cmp, float
   CHECK_PTR(k_cmp);
   CHECK_PTR(blk_scores);
   const sparda::SelectDims sd = select_dims(B, Hkv, Hkv, Tq, q_start, T, scale);
-  if (Tq != 1) return fail(SPARDA_ERR_UNSUPPORTED, "select_forecast: Tq > 1 (prefill) is not built yet");
+  if (Tq != 1) {
+    CHECK(dtype == SPARDA_BF16, SPARDA_ERR_UNSUPPORTED, "select_forecast: a query chunk (Tq > 1) needs bf16 inputs");
+    CHECK((long)B * Hkv <= 2147483647L && sd.n_tiles <= 65535, SPARDA_ERR_UNSUPPORTED, "grid too large");
+    return hip_status(sparda::launch_select_forecast_prefill(f, k_cmp, blk_scores, sd, (hipStream_t)stream),
+                      "select_forecast launch");
+  }
   return hip_status(sparda::launch_select_forecast_decode(f, k_cmp, blk_scores, dtype == SPARDA_BF16, sd,
                                                           (hipStream_t)stream),
                     "select_forecast launch");
@@ -248,7 +253,12 @@ SPARDA_EXPORT int sparda_block_sparse_attn(const void* q, const void* k, const v
         ws_bytes);
   if (need) CHECK_PTR(ws);
   const sparda::AttnDims ad = attn_dims(B, Hq, Hkv, Tq, q_start, T, k_sel, scale, kv_mode);
-  if (Tq != 1) return fail(SPARDA_ERR_UNSUPPORTED, "block_sparse_attn: Tq > 1 (prefill) is not built yet");
+  if (Tq != 1) {
+    CHECK(dtype == SPARDA_BF16, SPARDA_ERR_UNSUPPORTED, "block_sparse_attn: a query chunk (Tq > 1) needs bf16 inputs");
+    CHECK(ad.n_tiles <= 65535, SPARDA_ERR_UNSUPPORTED, "too many query tiles");
+    return hip_status(sparda::launch_attn_prefill(q, k, v, idx, out, ad, (hipStream_t)stream),
+                      "block_sparse_attn launch");
+  }
   return hip_status(sparda::launch_attn_decode(q, k, v, idx, out, dtype == SPARDA_BF16, ad, ws, (hipStream_t)stream),
                     "block_sparse_attn launch");
 }

@@ -1,0 +1,264 @@
+// Step 4 for a chunk of queries (prefill): GQA block-sparse attention of each
+// 64-query tile over the blocks selected for that tile (bittide.aicompass.dev
+// summary post, paragraph on block-sparse attention; techwalker.com article,
+// section 五: in prefill block-sparse attention is the main cost).
+//
+// Dense contractions per selected block, on the matrix cores
+// (v_mfma_f32_32x32x16_bf16). One workgroup owns one (sequence, KV head, query
+// tile); wave g computes head g of the GQA group for the tile's 64 queries, so
+// all G heads share every K/V block staged in LDS.
+//   S^T = K Q^T  (keys x queries): each lane owns one query column, so the
+//                online-softmax statistics of a query stay in one lane (plus
+//                its partner 32 lanes away);
+//   O^T += V^T P^T: P^T is the S^T accumulator itself, rounded to bf16 in
+//                register order. The MFMA k index then runs over the keys in
+//                the accumulator's row order (groups of 4); V^T fragments are
+//                read from LDS in that same order, so the sum is unchanged.
+// K and V blocks arrive in LDS by direct global->LDS loads one block ahead (K
+// rows granule-swizzled and double-buffered; V row-major, then transposed
+// LDS->LDS into V^T with row stride 72 keys). A workgroup holds at most 4
+// heads; a group of 8 runs as two workgroups.
+#include "common.h"
+#include "launch.h"
+
+namespace sparda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace {
+
+constexpr int kRowB = kHeadDim * 2;         // bytes per bf16 row
+constexpr int kKBytes = kBlock * kRowB;     // one K block in LDS
+constexpr int kVtStride = kBlock + 8;       // V^T row stride in elements (144 B)
+constexpr int kVtBytes = kHeadDim * kVtStride * 2;
+
+__device__ __forceinline__ bf16x8 as_v8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ int swz(int r, int g) { return r * kRowB + ((g ^ (r & 15)) << 4); }
+
+template <int NT>
+__device__ __forceinline__ void load_k_lds(const uint8_t* __restrict__ src_block, uint8_t* dst) {
+  // 64 rows x 16 granules = 1024 slots; NT threads, one 16-byte slot each per step
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int it = 0; it < 1024 / NT; ++it) {
+    const int pos = (it * (NT / kWave) + wave) * kWave + lane;
+    const int r = pos >> 4;
+    const int g = (pos & 15) ^ (r & 15);
+    __builtin_amdgcn_global_load_lds(src_block + r * kRowB + g * 16,
+                                     (__attribute__((address_space(3))) void*)(dst + (it * (NT / kWave) + wave) * kWave * 16),
+                                     16, 0, 0);
+  }
+}
+
+}  // namespace
+
+template <int HPW>
+__global__ __launch_bounds__(64 * HPW) void attn_prefill_kernel(
+    const uint8_t* __restrict__ q, const uint8_t* __restrict__ kbuf, const uint8_t* __restrict__ vbuf,
+    const int32_t* __restrict__ idx, uint8_t* __restrict__ out, int G, int Tq, int q_start, int T, int nB,
+    int n_tiles, int k, float scale) {
+  constexpr int NT = 64 * HPW;  // threads: one wave per head of the workgroup's head group
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[2][kKBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[kKBytes];  // raw V block, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt[kHeadDim * kVtStride];
+
+  const long row = blockIdx.x;  // (b, kv head)
+  const int tile = blockIdx.y;
+  const int g = blockIdx.z * HPW + threadIdx.x / kWave;  // head within the GQA group
+  const int lane = threadIdx.x % kWave;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int q0 = tile * kTile;
+  const int p_first = q_start + q0;  // position of the tile's first query
+  const int32_t* sel = idx + (row * n_tiles + tile) * (long)k;
+
+  // Q fragments (B operand of S^T = K Q^T): head g, 2 query tiles x 8 k-steps
+  const long qrow0 = (row * G + g) * (long)Tq + q0;
+  u32x4 qf[2][8];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const uint8_t* src = q + (qrow0 + 32 * n + l32) * kRowB + half * 16;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[n][s] = load16(src + s * 32);
+  }
+
+  f32x16 o[4][2];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) o[dt][n] = f32x16{};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+  // compact the usable slots: valid, in range, not wholly after the tile
+  auto usable = [&](int j) {
+    const int b = sel[j];
+    return b >= 0 && b < nB && b * kBlock <= p_first + kTile - 1;
+  };
+  int j = 0;
+  while (j < k && !usable(j)) ++j;
+  // V block: direct global->LDS copy (row-major), then transposed LDS->LDS
+  auto load_v_lds = [&](int b) {
+    const uint8_t* src = vbuf + (row * (long)T + (long)b * kBlock) * kRowB;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int it = 0; it < 1024 / NT; ++it) {
+      const int base = (it * (NT / kWave) + wave) * kWave;
+      __builtin_amdgcn_global_load_lds(src + (base + lane) * 16,
+                                       (__attribute__((address_space(3))) void*)(s_v + base * 16), 16, 0, 0);
+    }
+  };
+  auto transpose_v = [&]() {
+#pragma unroll
+    for (int it = 0; it < 1024 / NT; ++it) {
+      const int slot = it * NT + threadIdx.x;  // key = slot / 16, 8 channels from (slot % 16) * 8
+      const int key = slot >> 4;
+      const int d0 = (slot & 15) * 8;
+      const u32x4 w4 = *reinterpret_cast<const u32x4*>(s_v + slot * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = w4[e];
+        s_vt[(d0 + 2 * e) * kVtStride + key] = (uint16_t)(w & 0xFFFFu);
+        s_vt[(d0 + 2 * e + 1) * kVtStride + key] = (uint16_t)(w >> 16);
+      }
+    }
+  };
+  if (j < k) {
+    load_k_lds<NT>(kbuf + (row * (long)T + (long)sel[j] * kBlock) * kRowB, s_k[0]);
+    load_v_lds(sel[j]);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+
+  // Everything issued at the top of an iteration (the next block's K and V,
+  // straight into LDS) is awaited with a full drain after this block's
+  // compute, so the overlap never depends on counting outstanding loads.
+  int buf = 0;
+  while (j < k) {
+    const int b = sel[j];
+    int jn = j + 1;
+    while (jn < k && !usable(jn)) ++jn;
+    transpose_v();   // this block's V -> V^T
+    __syncthreads(); // V^T complete; the raw V buffer is free again
+    if (jn < k) {
+      load_k_lds<NT>(kbuf + (row * (long)T + (long)sel[jn] * kBlock) * kRowB, s_k[buf ^ 1]);
+      load_v_lds(sel[jn]);
+    }
+
+    // S^T = K Q^T: 2 key tiles x 2 query tiles
+    f32x16 sacc[2][2];
+#pragma unroll
+    for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) sacc[mk][n] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int mk = 0; mk < 2; ++mk) {
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(s_k[buf] + swz(32 * mk + l32, 2 * s + half));
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          sacc[mk][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8(ka), as_v8(qf[n][s]), sacc[mk][n], 0, 0, 0);
+      }
+    }
+    // causal mask, scale, online softmax per query column
+    const int key_base = b * kBlock;
+    uint32_t pp[2][2][8];  // bf16 pairs of P^T, [n][mk][dword]
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int pq = p_first + 32 * n + l32;  // this lane's query position
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key_base + 32 * mk + 8 * (r >> 2) + 4 * half + (r & 3);
+          const float x = key <= pq ? sacc[mk][n][r] * scale : -INFINITY;
+          sacc[mk][n][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, xor_shfl(mx, 32));
+      const float mn = fmaxf(m_run[n], mx);
+      const bool none = mn == -INFINITY;
+      const float alpha = none ? 1.f : fast_exp(m_run[n] - mn);
+      float sum = 0.f;
+#pragma unroll
+      for (int mk = 0; mk < 2; ++mk) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = none ? 0.f : fast_exp(sacc[mk][n][r] - mn);
+          const float p1 = none ? 0.f : fast_exp(sacc[mk][n][r + 1] - mn);
+          sum += p0 + p1;
+          pp[n][mk][r >> 1] = pack_bf16(p0, p1);
+        }
+      }
+      sum += xor_shfl(sum, 32);
+      l_run[n] = l_run[n] * alpha + sum;
+      m_run[n] = mn;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt][n] *= alpha;
+    }
+    // O^T += V^T P^T over 4 k-steps of 16 keys (2 per key tile)
+#pragma unroll
+    for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int kb = 32 * mk + 16 * s + 4 * half;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const uint16_t* vrow = s_vt + (32 * dt + l32) * kVtStride;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kb);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kb + 8);
+          const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+          for (int n = 0; n < 2; ++n) {
+            const u32x4 pb = {pp[n][mk][4 * s], pp[n][mk][4 * s + 1], pp[n][mk][4 * s + 2], pp[n][mk][4 * s + 3]};
+            o[dt][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8(va), as_v8(pb), o[dt][n], 0, 0, 0);
+          }
+        }
+      }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the next block has landed
+    __syncthreads();                           // and this block's LDS reads are done
+    buf ^= 1;
+    j = jn;
+  }
+
+  // O = O^T / l, written as 4 consecutive channels (8 B) per accumulator group
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const float inv = l_run[n] > 0.f ? 1.f / l_run[n] : 0.f;
+    uint8_t* dst = out + (qrow0 + 32 * n + l32) * kRowB;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d = 32 * dt + 8 * rg + 4 * half;
+        uint2 v;
+        v.x = pack_bf16(o[dt][n][4 * rg] * inv, o[dt][n][4 * rg + 1] * inv);
+        v.y = pack_bf16(o[dt][n][4 * rg + 2] * inv, o[dt][n][4 * rg + 3] * inv);
+        *reinterpret_cast<uint2*>(dst + d * 2) = v;
+      }
+  }
+}
+
+hipError_t launch_attn_prefill(const void* q, const void* k, const void* v, const int32_t* idx, void* out,
+                               const AttnDims& d, hipStream_t s) {
+  const int G = d.Hq / d.Hkv;
+  const int hpw = G < 4 ? G : 4;  // heads per workgroup; G = 8 runs as two groups of 4
+  const dim3 grid(d.B * d.Hkv, d.n_tiles, G / hpw);
+#define SPARDA_AP(HPW)                                                                                          \
+  hipLaunchKernelGGL(attn_prefill_kernel<HPW>, grid, dim3(64 * HPW), 0, s, (const uint8_t*)q, (const uint8_t*)k, \
+                     (const uint8_t*)v, idx, (uint8_t*)out, G, d.Tq, d.q_start, d.T, d.nB, d.n_tiles, d.k, d.scale)
+  switch (hpw) {
+    case 1: SPARDA_AP(1); break;
+    case 2: SPARDA_AP(2); break;
+    case 4: SPARDA_AP(4); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef SPARDA_AP
+  return hipGetLastError();
+}
+
+}  // namespace sparda

@@ -162,6 +162,11 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory loads are
+// outstanding and leaves the other counters alone (gfx9 encoding: vmcnt bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
 __device__ __forceinline__ float fast_exp(float x) {
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }

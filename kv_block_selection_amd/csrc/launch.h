@@ -36,6 +36,10 @@ size_t multihead_decode_ws_bytes(const SelectDims& d);
 hipError_t launch_select_multihead_decode(const void* q, const void* kc, float* scores, bool bf16,
                                           const SelectDims& d, void* ws, hipStream_t s);
 
+// select_prefill.hip (bf16, Tq % 64 == 0)
+hipError_t launch_select_forecast_prefill(const void* f, const void* kc, float* scores, const SelectDims& d,
+                                          hipStream_t s);
+
 // topk.hip
 hipError_t launch_topk(const float* scores, int32_t* idx, int rows, int nB, int k, hipStream_t s);
 
@@ -44,6 +48,10 @@ int decode_attn_splits(const AttnDims& d);
 size_t decode_attn_ws_bytes(const AttnDims& d);
 hipError_t launch_attn_decode(const void* q, const void* k, const void* v, const int32_t* idx,
                               void* out, bool bf16, const AttnDims& d, void* ws, hipStream_t s);
+
+// attn_prefill.hip (bf16, cache mode, Tq % 64 == 0)
+hipError_t launch_attn_prefill(const void* q, const void* k, const void* v, const int32_t* idx, void* out,
+                               const AttnDims& d, hipStream_t s);
 
 // prefetch.hip
 hipError_t launch_prefetch(const void* host_k, const void* host_v, const int32_t* idx, void* stage_k,

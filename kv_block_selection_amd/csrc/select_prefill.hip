@@ -1,0 +1,149 @@
+// Step 2 for a chunk of queries (prefill): Forecast block scoring of every
+// 64-query tile (bittide.aicompass.dev summary post, paragraph on one Forecast
+// head per GQA group; techwalker.com article, sections 二 and 五: in prefill the
+// gain comes from the cheaper selection itself).
+//
+// A dense contraction: per KV head, F [Tq x 128] times K_cmp^T [128 x W], so it
+// runs on the matrix cores (v_mfma_f32_32x32x16_bf16). One 256-thread
+// workgroup owns one (sequence, KV head, query tile) and sweeps the windows in
+// chunks of 128:
+//   * the chunk's compressed keys (128 x 256 B) land in LDS through direct
+//     global->LDS loads, double-buffered; each 16-byte granule of row r is
+//     stored at position (granule ^ (r & 15)), so the fragment reads of 16
+//     consecutive rows hit 16 different bank groups;
+//   * wave w computes the 64 x 32 score block of windows [32w, 32w + 32) for
+//     the tile's 64 queries, with the tile's F fragments held in registers;
+//   * each window's score is masked where the window is not visible to the
+//     query, and reduced to the max over the tile's queries (in-lane, then one
+//     swap of the two lane halves);
+//   * block b takes the max over windows 4b-1 .. 4b+3: chunk c finishes blocks
+//     32c .. 32c+31, reusing the previous chunk's last window (a one-window
+//     carry), so no window is computed twice and no workgroup waits on another.
+#include "common.h"
+#include "launch.h"
+
+namespace sparda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kChunkW = 128;                 // windows per chunk
+constexpr int kRowBytes = kHeadDim * 2;      // bf16 row
+constexpr int kChunkBytes = kChunkW * kRowBytes;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Byte offset of logical granule g (16 B) of row r inside a swizzled tile.
+__device__ __forceinline__ int swz(int r, int g) { return r * kRowBytes + ((g ^ (r & 15)) << 4); }
+
+// Direct global->LDS load of chunk rows [w0, w0 + 128) of one (b, h) row of
+// K_cmp into `dst`. Lane l of a wave instruction fills LDS bytes
+// [base + 16 l, base + 16 l + 16); it reads the global granule that the
+// swizzle maps there. Rows at or beyond W read row W-1 (masked later).
+__device__ __forceinline__ void load_chunk_lds(const uint8_t* __restrict__ kc_row, int W, int w0,
+                                               uint8_t* dst) {
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int it = 0; it < kChunkBytes / (4 * kWave * 16); ++it) {  // 8 instructions per wave
+    const int pos = (it * 4 + wave) * kWave + lane;                // 16-byte slot in the tile
+    const int r = pos >> 4;
+    const int g = (pos & 15) ^ (r & 15);
+    const int w = min(w0 + r, W - 1);
+    const uint8_t* src = kc_row + (long)w * kRowBytes + g * 16;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + (it * 4 + wave) * kWave * 16),
+                                     16, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(256) void fsel_prefill_kernel(const uint8_t* __restrict__ f,
+                                                           const uint8_t* __restrict__ kc,
+                                                           float* __restrict__ scores, int Tq,
+                                                           int q_start, int W, int nB, int n_tiles,
+                                                           float scale) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_kc[2][kChunkBytes];
+  __shared__ float s_cmax[kChunkW + 1];  // [0] = carry: last window of the previous chunk
+
+  const long row = blockIdx.x;  // (b, h): rows on the fast axis share an XCD
+  const int tile = blockIdx.y;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const uint8_t* kc_row = kc + row * (long)W * kRowBytes;
+  const int q0 = tile * kTile;  // first query of the tile (relative to the chunk)
+
+  // F fragments: A operand of the 64 x 128 tile, 2 M-tiles x 8 k-steps
+  u32x4 fa[2][8];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int q = min(q0 + 32 * m + l32, Tq - 1);
+    const uint8_t* src = f + (row * Tq + q) * (long)kRowBytes + half * 16;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) fa[m][s] = load16(src + s * 32);
+  }
+  // visibility: window w is visible to query position p iff 16 w + 31 <= p
+  int vis_lim[2][16];  // per accumulator row: number of visible windows
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int q = q0 + 32 * m + 8 * (r >> 2) + 4 * half + (r & 3);
+      const int p = q_start + min(q, Tq - 1);
+      vis_lim[m][r] = p >= kKernel - 1 ? min(W, (p - kKernel + 1) / kStride + 1) : 0;
+    }
+
+  const int nchunks = (W + kChunkW - 1) / kChunkW;
+  if (threadIdx.x == 0) s_cmax[0] = -INFINITY;
+  load_chunk_lds(kc_row, W, 0, s_kc[0]);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  // The next chunk's loads go out at the top of an iteration and are awaited
+  // with a full drain after this chunk's compute.
+  for (int c = 0; c < nchunks; ++c) {
+    if (c + 1 < nchunks) load_chunk_lds(kc_row, W, (c + 1) * kChunkW, s_kc[(c + 1) & 1]);
+    const uint8_t* tileb = s_kc[c & 1];
+    f32x16 acc0 = {}, acc1 = {};
+    const int wr = 32 * wave + l32;  // this lane's window row in the chunk
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const u32x4 b = *reinterpret_cast<const u32x4*>(tileb + swz(wr, 2 * s + half));
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[0][s]), as_bf16x8(b), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[1][s]), as_bf16x8(b), acc1, 0, 0, 0);
+    }
+    // column (window) max over the tile's visible queries
+    const int w = c * kChunkW + wr;
+    float cm = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (w < vis_lim[0][r]) cm = fmaxf(cm, acc0[r] * scale);
+      if (w < vis_lim[1][r]) cm = fmaxf(cm, acc1[r] * scale);
+    }
+    cm = fmaxf(cm, xor_shfl(cm, 32));
+    if (half == 0) s_cmax[1 + wr] = cm;
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < kChunkW / 4) {
+      const int b = c * (kChunkW / 4) + t;
+      if (b < nB) {
+        float m = s_cmax[4 * t];
+#pragma unroll
+        for (int j = 1; j < 5; ++j) m = fmaxf(m, s_cmax[4 * t + j]);
+        scores[(row * n_tiles + tile) * (long)nB + b] = m;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the next chunk has landed
+    __syncthreads();
+    if (t == 0) s_cmax[0] = s_cmax[kChunkW];
+  }
+}
+
+hipError_t launch_select_forecast_prefill(const void* f, const void* kc, float* scores, const SelectDims& d,
+                                          hipStream_t s) {
+  dim3 grid(d.B * d.Hkv, d.n_tiles);
+  hipLaunchKernelGGL(fsel_prefill_kernel, grid, dim3(256), 0, s, (const uint8_t*)f, (const uint8_t*)kc, scores,
+                     d.Tq, d.q_start, d.W, d.nB, d.n_tiles, d.scale);
+  return hipGetLastError();
+}
+
+}  // namespace sparda

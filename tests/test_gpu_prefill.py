@@ -1,0 +1,120 @@
+"""GPU parity of the prefill path (a chunk of queries, 64-query tiles):
+Forecast scoring on the matrix cores, top-k per tile, and block-sparse
+attention on the matrix cores, against the fp64 oracle through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth.gpu as sg
+from synth import workloads as wl
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def prefill(T, Tq, B=1, Hq=8, Hkv=2, k=5, seed=21, offsets=True):
+    return wl.Workload(name="prefill", description="prefill", dtype="bf16", B=B, Hq=Hq, Hkv=Hkv, T=T, d=128, Tq=Tq,
+                       q_start=T - Tq, k=k, seed=seed, block_offsets=offsets)
+
+
+def gen(w, name):
+    return sg.tensor(w.recipe(name), w.shape(name), DEV)
+
+
+CASES = [prefill(64 * 37, 128), prefill(64 * 37, 64 * 37, k=7), prefill(2048, 64, B=2), prefill(4096, 1024, k=16)]
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: f"T{w.T}-Tq{w.Tq}-B{w.B}")
+def test_select_forecast_prefill_parity(gpu, w):
+    say("prefill select", w.T, w.Tq)
+    K, F = gen(w, "K"), gen(w, "F")
+    Kc = gpu.compress_keys(K)
+    s = gpu.select_forecast(F, Kc, w.T, w.q_start)
+    torch.cuda.synchronize()
+    assert s.shape == (w.B, w.Hkv, w.n_tiles, w.nB)
+    ref = oracle.select_forecast(parity.to_f64(F), parity.to_f64(Kc), w.T, w.q_start, w.scale)
+    worst = parity.check_scores(parity.to_f64(s), ref)
+    idx = gpu.topk_blocks(s, w.k)
+    banded = parity.check_topk_band(idx.cpu().numpy(), ref, w.k)
+    say(f"  worst rel err {worst:.2e}, banded rows {banded}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("k", [1, 6])
+def test_attention_prefill_parity(gpu, G, k):
+    w = prefill(64 * 37, 192, Hq=2 * G, k=k, seed=30 + G)
+    say("prefill attention G", G, "k", k)
+    Q, K, V = gen(w, "Q"), gen(w, "K"), gen(w, "V")
+    rng = np.random.default_rng(G * 10 + k)
+    idx = np.full((w.B, w.Hkv, w.n_tiles, k), -1, dtype=np.int32)
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            for t in range(w.n_tiles):
+                last = (w.q_start + 64 * t + 63) // 64  # the tile's own (diagonal) block
+                pool = np.arange(last)  # earlier blocks; the diagonal one is always added
+                picks = rng.choice(pool, min(k - 1, pool.size), replace=False)
+                picks = np.sort(np.append(picks, last))  # distinct, and the causal mask is exercised
+                idx[b, h, t, : picks.size] = picks
+    if k > 2:
+        idx[0, 0, 0, 1] = -1  # an unused slot in the middle
+    out = gpu.block_sparse_attn(Q, K, V, torch.from_numpy(idx).to(DEV), w.T, w.q_start)
+    torch.cuda.synchronize()
+    ref = oracle.block_sparse_attention(parity.to_f64(Q), parity.to_f64(K), parity.to_f64(V), idx, w.q_start, w.scale)
+    err = parity.check_attention(parity.to_f64(out), ref, parity.ATTN_ATOL_BF16)
+    say(f"  max abs err {err:.2e}")
+
+
+def test_prefill_step_end_to_end(gpu):
+    """select -> top-k per tile -> attention for a whole prefill from position 0."""
+    w = prefill(2048, 2048, Hq=8, Hkv=2, k=6, seed=41)
+    Q, K, V, F = gen(w, "Q"), gen(w, "K"), gen(w, "V"), gen(w, "F")
+    Kc = gpu.compress_keys(K)
+    s = gpu.select_forecast(F, Kc, w.T, w.q_start)
+    idx = gpu.topk_blocks(s, w.k)
+    out = gpu.block_sparse_attn(Q, K, V, idx, w.T, w.q_start)
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    ref_s = oracle.select_forecast(parity.to_f64(F), parity.to_f64(Kc), w.T, w.q_start, w.scale)
+    parity.check_topk_band(idx_np, ref_s, w.k)
+    # early tiles have fewer candidates than k: padding must be -1
+    assert (idx_np[..., 0, 1:] == -1).all()
+    ref = oracle.block_sparse_attention(parity.to_f64(Q), parity.to_f64(K), parity.to_f64(V), idx_np, w.q_start,
+                                        w.scale)
+    parity.check_attention(parity.to_f64(out), ref, parity.ATTN_ATOL_BF16)
+
+
+def test_c5_full_size_sampled_parity(gpu):
+    """The 4096-query chunk at the end of a 128K context; sampled tiles."""
+    w = wl.C5_PREFILL
+    say("generating", w.name)
+    Q, K, V, F = gen(w, "Q"), gen(w, "K"), gen(w, "V"), gen(w, "F")
+    Kc = gpu.compress_keys(K)
+    s = gpu.select_forecast(F, Kc, w.T, w.q_start)
+    idx = gpu.topk_blocks(s, w.k)
+    out = gpu.block_sparse_attn(Q, K, V, idx, w.T, w.q_start)
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    assert idx_np.min() >= 0 and np.all(np.diff(idx_np, axis=-1) > 0)
+    assert torch.isfinite(out.float()).all()
+    for h, t in [(0, 0), (3, 31), (7, 63)]:
+        say("head", h, "tile", t)
+        kc64 = parity.to_f64(Kc[0, h])
+        pos = [w.q_start + 64 * t + i for i in range(64)]
+        f64 = parity.to_f64(F[0, h, 64 * t:64 * t + 64])
+        ref_s = oracle.select_forecast_tile(f64, kc64, pos, w.T, w.scale)
+        parity.check_scores(parity.to_f64(s[0, h, t])[None], ref_s[None])
+        parity.check_topk_band(idx_np[0, h, t][None], ref_s[None], w.k)
+        k64, v64 = parity.to_f64(K[0, h]), parity.to_f64(V[0, h])
+        for g in range(w.G):
+            qh = h * w.G + g
+            for i in (0, 17, 63):
+                J = oracle.selected_keys(idx_np[0, h, t], pos[i])
+                ref_o = oracle.attend(parity.to_f64(Q[0, qh, 64 * t + i]), k64[J], v64[J], w.scale)
+                parity.check_attention(parity.to_f64(out[0, qh, 64 * t + i]), ref_o, parity.ATTN_ATOL_BF16)
