@@ -7,6 +7,8 @@ heads, d=128, 64-token blocks, top-64), inputs resident in HBM. Prints one
 JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --workload offload   # two-layer step, layer-1 KV in pinned host memory
+    python bench.py --workload prefill   # 4096-query chunk at 128K on the matrix cores
 
 Timing: W untimed steps, then K steps between two HIP events on the stream the
 kernels run on, with a device synchronisation on both sides. Input sets rotate
@@ -171,6 +173,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=("decode", "offload", "prefill"), default="decode",
+                    help="decode: the batch-16 128K decode step (the headline line); offload: the batch-64 two-layer "
+                         "step with lookahead prefetch from pinned host memory; prefill: a 4096-query chunk at 128K")
     ap.add_argument("--kernel-iters", type=int, default=100)
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (torch copy_) ten times, as the known-size reference "
@@ -181,6 +186,14 @@ def main() -> int:
               f"MI355X; sharding across GPUs is not implemented.", file=sys.stderr)
         return 2
 
+    if args.workload == "offload":
+        return bench_offload(args)
+    if args.workload == "prefill":
+        return bench_prefill(args)
+    return bench_decode(args)
+
+
+def bench_decode(args) -> int:
     import torch
     import kv_block_selection_amd as kbs
     import synth.gpu as sg
@@ -288,6 +301,186 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle sample)")
         result["cpu_baseline"] = cpu_baseline(w, sets)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+HOST_LINK_PEAK_GBPS = 63.0   # PCIe 5.0 x16, one direction
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_offload(args) -> int:
+    """Two-layer decode step at B=64, T=128K with layer 1's KV (32 GiB) in pinned
+    host memory: both selections, layer 0's attention from HBM overlapped with
+    the gather of layer 1's selected blocks over the host link on a side stream,
+    then layer 1's attention from staging. Also times each part alone, a plain
+    1 GiB pinned host-to-device copy, and a sweep of the gather's workgroups."""
+    import torch
+    import kv_block_selection_amd as kbs
+    from kv_block_selection_amd.lookahead import LookaheadStep
+    from synth import workloads as wl
+    from synth.offload import offload_layers
+
+    kbs.load()
+    w = wl.C4_OFFLOAD
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating {w.name} (32 GiB KV in HBM, 32 GiB pinned host)")
+    l0, l1 = offload_layers(w, kbs.compress_keys, dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    st = LookaheadStep(w.B, w.Hq, w.Hkv, w.T, w.k, torch.bfloat16, dev)
+    T, q = w.T, w.q_start
+    link_bytes = 2 * w.B * w.Hkv * w.k * w.block * w.d * 2
+
+    def step(i):
+        st.step(l0, l1, stream)
+
+    def select(i):
+        st.select(l0, l1, stream)
+
+    def attn0(i):
+        kbs.block_sparse_attn(l0["Q"], l0["K"], l0["V"], st.idx0, T, q, out=st.out0, ws=st.ws, stream=stream)
+
+    def attn1(i):
+        kbs.block_sparse_attn(l1["Q"], st.stage_k, st.stage_v, st.idx1, T, q, kv_mode=kbs.KV_STAGING,
+                              out=st.out1, ws=st.ws, stream=stream)
+
+    def gather(nwg):
+        return lambda i: kbs.prefetch_blocks(l1["host_K"], l1["host_V"], st.idx1.view(w.B, w.Hkv, w.k),
+                                             st.stage_k, st.stage_v, num_workgroups=nwg, stream=stream)
+
+    log("[bench] warmup")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    n = max(5, args.steps)
+    ms_step = time_loop(step, n, stream)
+    log(f"[bench] step {ms_step:.3f} ms; parts alone")
+    parts = {"select_both_layers": time_loop(select, n, stream), "attn_layer0_hbm": time_loop(attn0, n, stream),
+             "gather_layer1": time_loop(gather(0), n, stream), "attn_layer1_staging": time_loop(attn1, n, stream)}
+    host = l1["host_K"].view(-1).view(torch.uint8)[: 1 << 30]
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    ms_copy = time_loop(lambda i: dst.copy_(host, non_blocking=True), max(5, n // 4), stream)
+    del dst
+    sweep = {}
+    for nwg in (8, 16, 32, 64, 128, 256):
+        st.num_workgroups = nwg
+        g = time_loop(gather(nwg), max(5, n // 4), stream)
+        s_ms = time_loop(step, max(5, n // 4), stream)
+        sweep[nwg] = {"gather_ms": round(g, 4), "gather_GBps": round(link_bytes / (g * 1e-3) / 1e9, 2),
+                      "step_ms": round(s_ms, 4)}
+        log(f"[bench] gather with {nwg} workgroups: {g:.3f} ms, step {s_ms:.3f} ms")
+    st.num_workgroups = 0
+    # the gather waits only for layer 1's selection; layer 0's selection and
+    # attention can hide behind it
+    serial = sum(parts.values())
+    hideable = min(parts["select_both_layers"] / 2 + parts["attn_layer0_hbm"], parts["gather_layer1"])
+    link_gbps = link_bytes / (parts["gather_layer1"] * 1e-3) / 1e9
+    result = {
+        "metric": "offloaded decode steps/s/layer at 128K ctx, B=64, two layers with lookahead prefetch",
+        "value": round(2e3 / ms_step, 3),
+        "unit": "steps/s/layer",
+        "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.description, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
+                   "block": w.block, "top_k": w.k, "layers": 2, "gather_workgroups": "library default"},
+        "roofline": {"bound": "host_link", "kernel": "prefetch", "achieved": round(link_gbps, 2),
+                     "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s", "frac": round(link_gbps / HOST_LINK_PEAK_GBPS, 4),
+                     "traffic": None},
+        "link_bytes_per_step": link_bytes,
+        "h2d_memcpy_1GiB_GBps": round((1 << 30) / (ms_copy * 1e-3) / 1e9, 2),
+        "parts_ms": {k: round(v, 4) for k, v in parts.items()},
+        "serial_ms": round(serial, 4),
+        "overlap_hidden_frac": round((serial - ms_step) / hideable, 3) if hideable > 0 else None,
+        "overlap_note": "hideable = layer 0 selection (half of both selections) + layer 0 attention",
+        "workgroup_sweep": sweep,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def prefill_flops(w, idx) -> dict:
+    """Algorithmic flops of the chunk: Forecast scoring of every visible
+    (query, window) pair, and attention over every selected key at or before
+    each query (QK and PV, 2 x 128 flops each)."""
+    import numpy as np
+    pos = w.q_start + np.arange(w.Tq)
+    vis = np.where(pos >= w.kernel - 1, np.minimum(w.W, (pos - w.kernel + 1) // w.stride + 1), 0)
+    sel = 2 * w.d * int(vis.sum()) * w.B * w.Hkv
+    keys = 0
+    for t in range(w.n_tiles):
+        p = pos[t * w.tile:(t + 1) * w.tile]
+        blk = idx[:, :, t, :]                                   # [B, Hkv, k]
+        valid = blk >= 0
+        start = 64 * np.where(valid, blk, 0)
+        cnt = np.clip(p[None, None, None, :] - start[..., None] + 1, 0, 64) * valid[..., None]
+        keys += int(cnt.sum())
+    return {"select_forecast": sel, "attention": 4 * w.d * keys * w.G}
+
+
+def bench_prefill(args) -> int:
+    """A 4096-query chunk at the end of a 128K context (B=1, 32/8 heads): Forecast
+    scoring of every 64-query tile, top-64 per tile, block-sparse attention,
+    each on the matrix cores except top-k; inputs resident in HBM."""
+    import torch
+    import kv_block_selection_amd as kbs
+    import synth.gpu as sg
+    from synth import workloads as wl
+
+    kbs.load()
+    w = wl.C5_PREFILL
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating {w.name}")
+    s = {n: sg.tensor(w.recipe(n), w.shape(n), dev) for n in ("Q", "F", "K", "V")}
+    Kc = kbs.compress_keys(s["K"])
+    scores = torch.empty((w.B, w.Hkv, w.n_tiles, w.nB), dtype=torch.float32, device=dev)
+    idx = torch.empty((w.B, w.Hkv, w.n_tiles, w.k), dtype=torch.int32, device=dev)
+    out = torch.empty_like(s["Q"])
+    stream = torch.cuda.current_stream(dev)
+
+    def sel(i):
+        kbs.select_forecast(s["F"], Kc, w.T, w.q_start, out=scores)
+
+    def topk(i):
+        kbs.topk_blocks(scores, w.k, out=idx)
+
+    def attn(i):
+        kbs.block_sparse_attn(s["Q"], s["K"], s["V"], idx, w.T, w.q_start, out=out)
+
+    def step(i):
+        sel(i)
+        topk(i)
+        attn(i)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    n = max(5, args.steps)
+    ms_step = time_loop(step, n, stream)
+    ms = {"select_forecast": time_loop(sel, n, stream), "topk": time_loop(topk, n, stream),
+          "attention": time_loop(attn, n, stream)}
+    step(0)
+    torch.cuda.synchronize()
+    fl = prefill_flops(w, idx.cpu().numpy())
+    tf = {k: fl[k] / (ms[k] * 1e-3) / 1e12 for k in fl}
+    result = {
+        "metric": "chunked-prefill chunks/s at 128K ctx (4096 queries, select+sparse attn)",
+        "value": round(1e3 / ms_step, 3),
+        "unit": "chunks/s",
+        "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.description, "B": w.B, "T": w.T, "Tq": w.Tq, "q_start": w.q_start, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "d": w.d, "block": w.block, "tile": w.tile, "top_k": w.k},
+        "roofline": {"bound": "mfma", "kernel": "attention", "achieved": round(tf["attention"], 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf["attention"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "kernel_us": {k: round(v * 1e3, 2) for k, v in ms.items()},
+        "algorithmic_gflop": {k: round(v / 1e9, 3) for k, v in fl.items()},
+        "kernel_TFLOPs": {k: round(v, 1) for k, v in tf.items()},
+        "mfma_utilisation": {k: round(v / MFMA_BF16_PEAK_TFLOPS, 4) for k, v in tf.items()},
+    }
     print(json.dumps(result), flush=True)
     return 0
 
