@@ -416,7 +416,9 @@ def prefill_flops(w, idx) -> dict:
         start = 64 * np.where(valid, blk, 0)
         cnt = np.clip(p[None, None, None, :] - start[..., None] + 1, 0, 64) * valid[..., None]
         keys += int(cnt.sum())
-    return {"select_forecast": sel, "attention": 4 * w.d * keys * w.G}
+    # the multi-head selector scores every (query, head, visible window) twice:
+    # once for the softmax normalisers, once for the normalised group sums
+    return {"select_forecast": sel, "select_multihead": 2 * w.G * sel, "attention": 4 * w.d * keys * w.G}
 
 
 def bench_prefill(args) -> int:
@@ -449,6 +451,9 @@ def bench_prefill(args) -> int:
     def attn(i):
         kbs.block_sparse_attn(s["Q"], s["K"], s["V"], idx, w.T, w.q_start, out=out)
 
+    def sel_mh(i):
+        kbs.select_multihead(s["Q"], Kc, w.T, w.q_start, out=scores)
+
     def step(i):
         sel(i)
         topk(i)
@@ -460,7 +465,7 @@ def bench_prefill(args) -> int:
     n = max(5, args.steps)
     ms_step = time_loop(step, n, stream)
     ms = {"select_forecast": time_loop(sel, n, stream), "topk": time_loop(topk, n, stream),
-          "attention": time_loop(attn, n, stream)}
+          "attention": time_loop(attn, n, stream), "select_multihead": time_loop(sel_mh, n, stream)}
     step(0)
     torch.cuda.synchronize()
     fl = prefill_flops(w, idx.cpu().numpy())
@@ -480,6 +485,10 @@ def bench_prefill(args) -> int:
         "algorithmic_gflop": {k: round(v / 1e9, 3) for k, v in fl.items()},
         "kernel_TFLOPs": {k: round(v, 1) for k, v in tf.items()},
         "mfma_utilisation": {k: round(v / MFMA_BF16_PEAK_TFLOPS, 4) for k, v in tf.items()},
+        "selection_us": {"forecast": round((ms["select_forecast"] + ms["topk"]) * 1e3, 2),
+                         "multihead": round((ms["select_multihead"] + ms["topk"]) * 1e3, 2)},
+        "forecast_vs_multihead_select_speedup": round(ms["select_multihead"] / ms["select_forecast"], 3),
+        "multihead_exp_per_chunk": 2 * w.G * prefill_flops(w, idx.cpu().numpy())["select_forecast"] // (2 * w.d),
     }
     print(json.dumps(result), flush=True)
     return 0

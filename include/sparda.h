@@ -104,7 +104,10 @@ int sparda_select_forecast(const void* f, const void* k_cmp, float* blk_scores, 
  * Per query and head, softmax over that query's visible windows of
  * scale * q . k_cmp[w]; S[w] = sum over the group's heads; block and tile
  * pooling by max as above.
- * ws: sparda_workspace_bytes(SPARDA_OP_SELECT_MULTIHEAD, ...) bytes.
+ * ws: sparda_workspace_bytes(SPARDA_OP_SELECT_MULTIHEAD, ...) bytes (decode:
+ * the logits and per-chunk softmax statistics; no initial contents needed).
+ * A chunk of queries (Tq a multiple of 64) runs on the matrix cores, needs
+ * bf16 and no workspace: it sweeps k_cmp twice (normalisers, then group sums).
  */
 int sparda_select_multihead(const void* q, const void* k_cmp, float* blk_scores, int dtype, int B,
                             int Hq, int Hkv, int Tq, int q_start, int T, int d, int kernel,

@@ -211,7 +211,12 @@ SPARDA_EXPORT int sparda_select_multihead(const void* q, const void* k_cmp, floa
   CHECK(ws_bytes >= need, SPARDA_ERR_WORKSPACE, "select_multihead needs %zu workspace bytes, got %zu", need, ws_bytes);
   if (need) CHECK_PTR(ws);
   const sparda::SelectDims sd = select_dims(B, Hq, Hkv, Tq, q_start, T, scale);
-  if (Tq != 1) return fail(SPARDA_ERR_UNSUPPORTED, "select_multihead: Tq > 1 (prefill) is not built yet");
+  if (Tq != 1) {
+    CHECK(dtype == SPARDA_BF16, SPARDA_ERR_UNSUPPORTED, "select_multihead: a query chunk (Tq > 1) needs bf16 inputs");
+    CHECK(sd.n_tiles <= 65535, SPARDA_ERR_UNSUPPORTED, "grid too large");
+    return hip_status(sparda::launch_select_multihead_prefill(q, k_cmp, blk_scores, sd, (hipStream_t)stream),
+                      "select_multihead launch");
+  }
   return hip_status(sparda::launch_select_multihead_decode(q, k_cmp, blk_scores, dtype == SPARDA_BF16, sd, ws,
                                                            (hipStream_t)stream),
                     "select_multihead launch");

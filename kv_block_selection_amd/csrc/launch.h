@@ -40,6 +40,10 @@ hipError_t launch_select_multihead_decode(const void* q, const void* kc, float* 
 hipError_t launch_select_forecast_prefill(const void* f, const void* kc, float* scores, const SelectDims& d,
                                           hipStream_t s);
 
+// mhsel_prefill.hip (bf16, Tq % 64 == 0)
+hipError_t launch_select_multihead_prefill(const void* q, const void* kc, float* scores, const SelectDims& d,
+                                           hipStream_t s);
+
 // topk.hip
 hipError_t launch_topk(const float* scores, int32_t* idx, int rows, int nB, int k, hipStream_t s);
 

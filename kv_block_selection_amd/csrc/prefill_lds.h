@@ -1,0 +1,58 @@
+// Staging of compressed-key chunks in LDS for the prefill selectors: 128
+// windows x 128 bf16 channels (32 KiB) per chunk, loaded straight from global
+// memory into LDS, with a granule swizzle so the matrix-core fragment reads of
+// 16 consecutive rows hit 16 different bank groups.
+#pragma once
+
+#include "common.h"
+#include "launch.h"
+
+namespace sparda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kChunkW = 128;                 // windows per chunk
+constexpr int kRowBytes = kHeadDim * 2;      // one bf16 row
+constexpr int kChunkBytes = kChunkW * kRowBytes;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Byte offset of logical 16-byte granule g of row r inside a swizzled chunk.
+__device__ __forceinline__ int swz(int r, int g) { return r * kRowBytes + ((g ^ (r & 15)) << 4); }
+
+// Direct global->LDS load of rows [w0, w0 + 128) of one (b, h) row of K_cmp
+// into `dst` by a workgroup of NWAVES waves. Lane l of a wave instruction fills
+// LDS bytes [base + 16 l, base + 16 l + 16) from the global granule the swizzle
+// maps there. Rows at or beyond W read row W - 1 (callers mask them).
+template <int NWAVES>
+__device__ __forceinline__ void load_chunk_lds(const uint8_t* __restrict__ kc_row, int W, int w0, uint8_t* dst) {
+  static_assert(kChunkBytes % (NWAVES * kWave * 16) == 0, "chunk must split evenly over the waves");
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int it = 0; it < kChunkBytes / (NWAVES * kWave * 16); ++it) {
+    const int pos = (it * NWAVES + wave) * kWave + lane;  // 16-byte slot in the chunk
+    const int r = pos >> 4;
+    const int g = (pos & 15) ^ (r & 15);
+    const int w = min(w0 + r, W - 1);
+    const uint8_t* src = kc_row + (long)w * kRowBytes + g * 16;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + (it * NWAVES + wave) * kWave * 16),
+                                     16, 0, 0);
+  }
+}
+
+// Fragment of a chunk row for a 32x32x16 MFMA operand whose rows (A) or columns
+// (B) are windows: lane l reads window row `r` (= 32 * tile + l % 32), channels
+// [16 s + 8 (l / 32), +8).
+__device__ __forceinline__ u32x4 chunk_frag(const uint8_t* chunk, int r, int s, int half) {
+  return *reinterpret_cast<const u32x4*>(chunk + swz(r, 2 * s + half));
+}
+
+// Number of compressed windows visible to the query at position p: window w
+// is visible iff every token of it is at or before p, i.e. 16 w + 31 <= p.
+__device__ __forceinline__ int visible_windows(int p, int W) {
+  return p >= kKernel - 1 ? min(W, (p - kKernel + 1) / kStride + 1) : 0;
+}
+
+}  // namespace sparda

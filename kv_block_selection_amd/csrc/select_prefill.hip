@@ -19,42 +19,9 @@
 //   * block b takes the max over windows 4b-1 .. 4b+3: chunk c finishes blocks
 //     32c .. 32c+31, reusing the previous chunk's last window (a one-window
 //     carry), so no window is computed twice and no workgroup waits on another.
-#include "common.h"
-#include "launch.h"
+#include "prefill_lds.h"
 
 namespace sparda {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-constexpr int kChunkW = 128;                 // windows per chunk
-constexpr int kRowBytes = kHeadDim * 2;      // bf16 row
-constexpr int kChunkBytes = kChunkW * kRowBytes;
-
-__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
-
-// Byte offset of logical granule g (16 B) of row r inside a swizzled tile.
-__device__ __forceinline__ int swz(int r, int g) { return r * kRowBytes + ((g ^ (r & 15)) << 4); }
-
-// Direct global->LDS load of chunk rows [w0, w0 + 128) of one (b, h) row of
-// K_cmp into `dst`. Lane l of a wave instruction fills LDS bytes
-// [base + 16 l, base + 16 l + 16); it reads the global granule that the
-// swizzle maps there. Rows at or beyond W read row W-1 (masked later).
-__device__ __forceinline__ void load_chunk_lds(const uint8_t* __restrict__ kc_row, int W, int w0,
-                                               uint8_t* dst) {
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-#pragma unroll
-  for (int it = 0; it < kChunkBytes / (4 * kWave * 16); ++it) {  // 8 instructions per wave
-    const int pos = (it * 4 + wave) * kWave + lane;                // 16-byte slot in the tile
-    const int r = pos >> 4;
-    const int g = (pos & 15) ^ (r & 15);
-    const int w = min(w0 + r, W - 1);
-    const uint8_t* src = kc_row + (long)w * kRowBytes + g * 16;
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + (it * 4 + wave) * kWave * 16),
-                                     16, 0, 0);
-  }
-}
 
 __global__ __launch_bounds__(256) void fsel_prefill_kernel(const uint8_t* __restrict__ f,
                                                            const uint8_t* __restrict__ kc,
@@ -89,25 +56,24 @@ __global__ __launch_bounds__(256) void fsel_prefill_kernel(const uint8_t* __rest
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int q = q0 + 32 * m + 8 * (r >> 2) + 4 * half + (r & 3);
-      const int p = q_start + min(q, Tq - 1);
-      vis_lim[m][r] = p >= kKernel - 1 ? min(W, (p - kKernel + 1) / kStride + 1) : 0;
+      vis_lim[m][r] = visible_windows(q_start + min(q, Tq - 1), W);
     }
 
   const int nchunks = (W + kChunkW - 1) / kChunkW;
   if (threadIdx.x == 0) s_cmax[0] = -INFINITY;
-  load_chunk_lds(kc_row, W, 0, s_kc[0]);
+  load_chunk_lds<4>(kc_row, W, 0, s_kc[0]);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
   // The next chunk's loads go out at the top of an iteration and are awaited
   // with a full drain after this chunk's compute.
   for (int c = 0; c < nchunks; ++c) {
-    if (c + 1 < nchunks) load_chunk_lds(kc_row, W, (c + 1) * kChunkW, s_kc[(c + 1) & 1]);
+    if (c + 1 < nchunks) load_chunk_lds<4>(kc_row, W, (c + 1) * kChunkW, s_kc[(c + 1) & 1]);
     const uint8_t* tileb = s_kc[c & 1];
     f32x16 acc0 = {}, acc1 = {};
     const int wr = 32 * wave + l32;  // this lane's window row in the chunk
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const u32x4 b = *reinterpret_cast<const u32x4*>(tileb + swz(wr, 2 * s + half));
+      const u32x4 b = chunk_frag(tileb, wr, s, half);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[0][s]), as_bf16x8(b), acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[1][s]), as_bf16x8(b), acc1, 0, 0, 0);
     }

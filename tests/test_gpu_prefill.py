@@ -46,6 +46,46 @@ def test_select_forecast_prefill_parity(gpu, w):
     say(f"  worst rel err {worst:.2e}, banded rows {banded}")
 
 
+@pytest.mark.parametrize("w", CASES, ids=lambda w: f"T{w.T}-Tq{w.Tq}-B{w.B}")
+def test_select_multihead_prefill_parity(gpu, w):
+    say("prefill multihead select", w.T, w.Tq)
+    Q, K = gen(w, "Q"), gen(w, "K")
+    Kc = gpu.compress_keys(K)
+    s = gpu.select_multihead(Q, Kc, w.T, w.q_start)
+    torch.cuda.synchronize()
+    assert s.shape == (w.B, w.Hkv, w.n_tiles, w.nB)
+    ref = oracle.select_multihead(parity.to_f64(Q), parity.to_f64(Kc), w.T, w.q_start, w.scale)
+    worst = parity.check_scores(parity.to_f64(s), ref)
+    banded = parity.check_topk_band(gpu.topk_blocks(s, w.k).cpu().numpy(), ref, w.k)
+    say(f"  worst rel err {worst:.2e}, banded rows {banded}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 8])
+def test_select_multihead_prefill_groups(gpu, G):
+    """Every group size; 5 tiles, so the workgroups that hold several tiles
+    (G < 4) end with a partial one."""
+    w = prefill(64 * 21, 320, Hq=2 * G, k=4, seed=50 + G)
+    say("prefill multihead select G", G)
+    Q, K = gen(w, "Q"), gen(w, "K")
+    Kc = gpu.compress_keys(K)
+    s = gpu.select_multihead(Q, Kc, w.T, w.q_start)
+    torch.cuda.synchronize()
+    ref = oracle.select_multihead(parity.to_f64(Q), parity.to_f64(Kc), w.T, w.q_start, w.scale)
+    worst = parity.check_scores(parity.to_f64(s), ref)
+    parity.check_topk_band(gpu.topk_blocks(s, w.k).cpu().numpy(), ref, w.k)
+    say(f"  worst rel err {worst:.2e}")
+
+
+def test_select_multihead_prefill_is_deterministic(gpu):
+    w = prefill(4096, 1024, k=16, seed=61)
+    Q, K = gen(w, "Q"), gen(w, "K")
+    Kc = gpu.compress_keys(K)
+    a = gpu.select_multihead(Q, Kc, w.T, w.q_start)
+    b = gpu.select_multihead(Q, Kc, w.T, w.q_start)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 @pytest.mark.parametrize("k", [1, 6])
 def test_attention_prefill_parity(gpu, G, k):
@@ -97,7 +137,9 @@ def test_c5_full_size_sampled_parity(gpu):
     Q, K, V, F = gen(w, "Q"), gen(w, "K"), gen(w, "V"), gen(w, "F")
     Kc = gpu.compress_keys(K)
     s = gpu.select_forecast(F, Kc, w.T, w.q_start)
+    sm = gpu.select_multihead(Q, Kc, w.T, w.q_start)
     idx = gpu.topk_blocks(s, w.k)
+    idx_m = gpu.topk_blocks(sm, w.k).cpu().numpy()
     out = gpu.block_sparse_attn(Q, K, V, idx, w.T, w.q_start)
     torch.cuda.synchronize()
     idx_np = idx.cpu().numpy()
@@ -111,6 +153,10 @@ def test_c5_full_size_sampled_parity(gpu):
         ref_s = oracle.select_forecast_tile(f64, kc64, pos, w.T, w.scale)
         parity.check_scores(parity.to_f64(s[0, h, t])[None], ref_s[None])
         parity.check_topk_band(idx_np[0, h, t][None], ref_s[None], w.k)
+        q_rows = parity.to_f64(Q[0, h * w.G:(h + 1) * w.G, 64 * t:64 * t + 64])
+        ref_m = oracle.select_multihead_tile(q_rows, kc64, pos, w.T, w.scale)
+        parity.check_scores(parity.to_f64(sm[0, h, t])[None], ref_m[None])
+        parity.check_topk_band(idx_m[0, h, t][None], ref_m[None], w.k)
         k64, v64 = parity.to_f64(K[0, h]), parity.to_f64(V[0, h])
         for g in range(w.G):
             qh = h * w.G + g
