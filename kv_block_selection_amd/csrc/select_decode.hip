@@ -22,7 +22,10 @@
 
 namespace sparda {
 
-constexpr int kFselBlocks = 32;   // blocks per workgroup, Forecast pass
+#ifndef SPARDA_FSEL_BLOCKS
+#define SPARDA_FSEL_BLOCKS 16
+#endif
+constexpr int kFselBlocks = SPARDA_FSEL_BLOCKS;  // blocks per workgroup, Forecast pass
 constexpr int kMhChunk = 256;     // windows per workgroup, multi-head pass 1
 constexpr int kMhPoolBlocks = 64; // blocks per workgroup, multi-head pass 2
 

@@ -4,13 +4,17 @@
 //
 // One 256-thread workgroup per row. Scores become order-preserving 32-bit keys
 // (larger key <=> larger score; -0 ranks as +0; -inf and padding become key 0,
-// never taken). A block reduction gives the candidate count and the smallest
-// and largest candidate keys; the radix select then runs on x = key - kmin, so
-// its first digit already splits the row's actual range (float keys of one
-// row share their top bits, which would put every key in one or two bins).
-// Each pass histograms the next <= 8 bits of x among the keys that match the
-// prefix fixed so far (per-wave LDS histograms), one wave scans the bins and
-// fixes the digit holding the k-th largest; it stops as soon as that digit is
+// never taken). Every key at or above a lower bound L of the k-th largest key
+// is kept, the rest dropped: each wave takes the ceil(k/4)-th largest of its
+// lanes' maxima (a ballot search over the bits where those maxima differ, cut
+// short after 8 bits, which only lowers it), so each wave holds at least
+// ceil(k/4) keys at or above its value and L, the smallest of the four, has at
+// least k keys at or above it. A block reduction gives the candidate count and
+// the largest key; the radix select then runs on x = key - L over the few
+// keys left. Each pass histograms the next <= 8 bits of x among the keys that
+// match the prefix fixed so far (per-wave LDS histograms, three buffers in
+// rotation), and every wave scans the bins itself to fix the digit holding the
+// k-th largest, so a pass needs one barrier; it stops as soon as that digit is
 // taken whole. Thread t owns the contiguous index range [t*NPT, (t+1)*NPT); one
 // packed exclusive scan in thread order (above-prefix count in the low 16
 // bits, equal-prefix count in the high 16) gives every selected block its
@@ -27,26 +31,58 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+// Wave reductions: a butterfly inside each 16-lane DPP row, then the four row
+// results read as scalars.
 __device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
-  for (int m = 1; m < kWave; m <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, m, kWave));
-  return v;
+  v = min(v, dppu<0xB1>(v));
+  v = min(v, dppu<0x4E>(v));
+  v = min(v, dppu<0x141>(v));
+  v = min(v, dppu<0x140>(v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
-  for (int m = 1; m < kWave; m <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, kWave));
-  return v;
+  v = max(v, dppu<0xB1>(v));
+  v = max(v, dppu<0x4E>(v));
+  v = max(v, dppu<0x141>(v));
+  v = max(v, dppu<0x140>(v));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 __device__ __forceinline__ int wave_isum(int v) {
-  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+  uint32_t u = (uint32_t)v;
+  u += dppu<0xB1>(u);
+  u += dppu<0x4E>(u);
+  u += dppu<0x141>(u);
+  u += dppu<0x140>(u);
+  return (int)(__builtin_amdgcn_readlane(u, 0) + __builtin_amdgcn_readlane(u, 16) + __builtin_amdgcn_readlane(u, 32) +
+               __builtin_amdgcn_readlane(u, 48));
+}
+
+// A value v with at least r lanes of the wave holding x >= v, and v no larger
+// than the r-th largest x: a bitwise search from the highest bit where the
+// lanes' x differ, stopped after `bits` bits (the bits below stay 0).
+__device__ __forceinline__ uint32_t wave_rank_bound(uint32_t x, int r, int bits) {
+  const uint32_t hi = wave_umax(x), lo = wave_umin(x);
+  if (hi == lo) return hi;
+  const int top = 31 - __clz(hi ^ lo);
+  uint32_t v = top == 31 ? 0u : (hi >> (top + 1)) << (top + 1);  // the bits all lanes share
+  for (int b = top; b >= 0 && b > top - bits; --b) {
+    const uint32_t cand = v | (1u << b);
+    if (__popcll(__ballot(x >= cand)) >= r) v = cand;
+  }
   return v;
 }
 
 struct TopkShared {
-  int hist[2][4][256];  // [ping-pong][wave][digit]
+  int hist[3][4][256];  // [rotation][wave][digit]
   int wave_tot[4];
-  uint32_t wave_min[4], wave_max[4];
+  uint32_t wave_max[4], wave_bound[4];
   int wave_cnt[4];
-  uint32_t digit;
-  int above, done;
 };
 
 template <int NPT>
@@ -61,86 +97,93 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
 
   uint32_t key[NPT];
   int cnt = 0;
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  uint32_t kmax = 0u;
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
     const int b = t * NPT + j;
     key[j] = b < nB ? order_key(src[b]) : 0u;
-    if (key[j] != 0u) {
-      ++cnt;
-      kmin = min(kmin, key[j]);
-      kmax = max(kmax, key[j]);
-    }
+    cnt += key[j] != 0u;
+    kmax = max(kmax, key[j]);
   }
 #pragma unroll
   for (int w = 0; w < 4; ++w) sh.hist[0][w][t] = 0;
+  const int rnk = (k + 3) / 4;
+  const uint32_t wbound = rnk <= kWave ? wave_rank_bound(kmax, rnk, 8) : 0u;  // kmax: this thread's largest
   cnt = wave_isum(cnt);
-  kmin = wave_umin(kmin);
-  kmax = wave_umax(kmax);
+  const uint32_t wmax = wave_umax(kmax);
   if (lane == 0) {
     sh.wave_cnt[wid] = cnt;
-    sh.wave_min[wid] = kmin;
-    sh.wave_max[wid] = kmax;
+    sh.wave_max[wid] = wmax;
+    sh.wave_bound[wid] = wbound;
   }
   __syncthreads();
   int n_cand = 0;
-  kmin = 0xFFFFFFFFu;
   kmax = 0u;
+  uint32_t lb = 0xFFFFFFFFu;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     n_cand += sh.wave_cnt[w];
-    kmin = min(kmin, sh.wave_min[w]);
     kmax = max(kmax, sh.wave_max[w]);
+    lb = min(lb, sh.wave_bound[w]);
   }
   const int kk = min(k, n_cand);
   const bool take_all = kk == n_cand;  // includes the empty row
+  // keys below the bound cannot be among the k largest (the bound is 0 when a
+  // wave had too few candidates, and then nothing is dropped)
+  lb = max(lb, 1u);
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) key[j] = key[j] >= lb ? key[j] : 0u;
 
-  // radix select on x = key - kmin over the bits below `lo`
+  // radix select on x = key - lb over the bits below `lo`
   uint32_t prefix = 0;
   int remaining = kk;
-  int lo = take_all ? 0 : 32 - __clz(kmax - kmin);
+  int lo = take_all ? 0 : 32 - __clz(kmax - lb);
   int cur = 0;
   while (lo > 0) {
     const int sft = max(lo - 8, 0);
     const uint32_t dmask = (1u << (lo - sft)) - 1u;
     const uint32_t phi = lo >= 32 ? 0u : prefix >> lo;
+    const int nxt = cur == 2 ? 0 : cur + 1;
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
       if (key[j] != 0u) {
-        const uint32_t x = key[j] - kmin;
+        const uint32_t x = key[j] - lb;
         if ((lo >= 32 ? 0u : x >> lo) == phi) atomicAdd(&sh.hist[cur][wid][(x >> sft) & dmask], 1);
       }
     }
+    // the buffer for the next pass was last read two passes ago, before the
+    // previous pass's barrier
 #pragma unroll
-    for (int w = 0; w < 4; ++w) sh.hist[cur ^ 1][w][t] = 0;
+    for (int w = 0; w < 4; ++w) sh.hist[nxt][w][t] = 0;
     __syncthreads();
-    if (wid == 0) {
-      // lane handles digits 255-4*lane .. 252-4*lane (descending)
-      int h[4], sum = 0;
+    // every wave: lane handles digits 255-4*lane .. 252-4*lane (descending)
+    int h[4], sum = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 255 - 4 * lane - i;
-        h[i] = sh.hist[cur][0][d] + sh.hist[cur][1][d] + sh.hist[cur][2][d] + sh.hist[cur][3][d];
-        sum += h[i];
-      }
-      int above = wave_incl_scan(sum) - sum;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (above < remaining && remaining <= above + h[i]) {
-          sh.digit = (uint32_t)(255 - 4 * lane - i);
-          sh.above = above;
-          sh.done = remaining == above + h[i];  // the whole digit is taken
-        }
-        above += h[i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int d = 255 - 4 * lane - i;
+      h[i] = sh.hist[cur][0][d] + sh.hist[cur][1][d] + sh.hist[cur][2][d] + sh.hist[cur][3][d];
+      sum += h[i];
     }
-    __syncthreads();
-    prefix |= sh.digit << sft;
-    remaining -= sh.above;
+    int above = wave_incl_scan(sum) - sum;
+    bool hit = false;
+    uint32_t my_digit = 0;
+    int my_above = 0, my_done = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (above < remaining && remaining <= above + h[i]) {
+        hit = true;
+        my_digit = (uint32_t)(255 - 4 * lane - i);
+        my_above = above;
+        my_done = remaining == above + h[i];  // the whole digit is taken
+      }
+      above += h[i];
+    }
+    const int src_lane = __ffsll(__ballot(hit)) - 1;  // exactly one lane holds the digit
+    prefix |= (uint32_t)__builtin_amdgcn_readlane((int)my_digit, src_lane) << sft;
+    remaining -= __builtin_amdgcn_readlane(my_above, src_lane);
     lo = sft;
-    cur ^= 1;
-    if (sh.done) break;
-    // sh.digit / above / done are rewritten only after the next pass's first barrier
+    cur = nxt;
+    if (__builtin_amdgcn_readlane(my_done, src_lane)) break;
   }
 
   // Packed scan: low 16 bits = keys above the prefix, high 16 = keys equal to it.
@@ -149,7 +192,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
     if (key[j] != 0u) {
-      const uint32_t top = lo >= 32 ? 0u : (key[j] - kmin) >> lo;
+      const uint32_t top = lo >= 32 ? 0u : (key[j] - lb) >> lo;
       gt += top > plo;
       eq += top == plo;
     }
@@ -167,7 +210,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
     if (key[j] != 0u) {
-      const uint32_t top = lo >= 32 ? 0u : (key[j] - kmin) >> lo;
+      const uint32_t top = lo >= 32 ? 0u : (key[j] - lb) >> lo;
       if (top > plo) {
         dst[pos++] = t * NPT + j;
       } else if (top == plo) {
