@@ -155,7 +155,7 @@ void attn_decode_kernel(
       for (int s = 0; s < G; ++s) part[s] = dot16<Tag>(qs[s], kv[it], 0.f);
       if constexpr (LPK == 32) {  // fp32: 32 lanes per key; fold the upper 16 first
 #pragma unroll
-        for (int s = 0; s < G; ++s) part[s] += xor_shfl(part[s], 16);
+        for (int s = 0; s < G; ++s) part[s] = sum16(part[s]);
       }
       float sc[GR];
       reduce_scatter16<G>(part, sc);
@@ -257,8 +257,8 @@ void attn_decode_kernel(
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       float x = acc[g][e];
-      for (int m = LPK; m < kWave; m <<= 1) x += xor_shfl(x, m);
-      acc[g][e] = x;
+      if constexpr (LPK == 16) x = sum16(x);
+      acc[g][e] = sum32(x);
     }
 
   if (splits == 1) {

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(64 * HPW) void attn_prefill_kernel(
           sacc[mk][n][r] = x;
           mx = fmaxf(mx, x);
         }
-      mx = fmaxf(mx, xor_shfl(mx, 32));
+      mx = max32(mx);
       const float mn = fmaxf(m_run[n], mx);
       const bool none = mn == -INFINITY;
       const float alpha = none ? 1.f : fast_exp(m_run[n] - mn);
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(64 * HPW) void attn_prefill_kernel(
           pp[n][mk][r >> 1] = pack_bf16(p0, p1);
         }
       }
-      sum += xor_shfl(sum, 32);
+      sum = sum32(sum);
       l_run[n] = l_run[n] * alpha + sum;
       m_run[n] = mn;
 #pragma unroll

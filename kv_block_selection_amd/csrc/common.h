@@ -127,28 +127,51 @@ __device__ __forceinline__ float row16_max(float x) {
   x = fmaxf(x, dpp<0x140>(x));
   return x;
 }
-__device__ __forceinline__ float xor_shfl(float x, int mask) {
-  return __shfl_xor(x, mask, kWave);
+// Lanes l and l ^ 16 (l ^ 32) exchange values with one VALU instruction,
+// v_permlane16_swap (v_permlane32_swap), instead of a round trip through the
+// LDS crossbar. `lo` is always the lower lane's value, so a pair reduction
+// (lo + hi, max(lo, hi)) is bitwise the same in both lanes.
+struct LanePair {
+  float lo, hi;
+};
+__device__ __forceinline__ LanePair pair16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ LanePair pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float sum16(float x) {
+  const LanePair p = pair16(x);
+  return p.lo + p.hi;
+}
+__device__ __forceinline__ float sum32(float x) {
+  const LanePair p = pair32(x);
+  return p.lo + p.hi;
+}
+__device__ __forceinline__ float max16(float x) {
+  const LanePair p = pair16(x);
+  return fmaxf(p.lo, p.hi);
+}
+__device__ __forceinline__ float max32(float x) {
+  const LanePair p = pair32(x);
+  return fmaxf(p.lo, p.hi);
+}
+// The value held by lane l ^ 32 (waves start at multiples of 64 threads).
+__device__ __forceinline__ float partner32(float x) {
+  const LanePair p = pair32(x);
+  return (threadIdx.x & 32) ? p.lo : p.hi;
 }
 // Sum over a group of LANES (16 or 32) consecutive lanes; every lane gets it.
 template <int LANES>
 __device__ __forceinline__ float group_sum(float x) {
   x = row16_sum(x);
-  if constexpr (LANES == 32) x += xor_shfl(x, 16);
+  if constexpr (LANES == 32) x = sum16(x);
   return x;
 }
-__device__ __forceinline__ float wave_sum(float x) {
-  x = row16_sum(x);
-  x += xor_shfl(x, 16);
-  x += xor_shfl(x, 32);
-  return x;
-}
-__device__ __forceinline__ float wave_max(float x) {
-  x = row16_max(x);
-  x = fmaxf(x, xor_shfl(x, 16));
-  x = fmaxf(x, xor_shfl(x, 32));
-  return x;
-}
+__device__ __forceinline__ float wave_sum(float x) { return sum32(sum16(row16_sum(x))); }
+__device__ __forceinline__ float wave_max(float x) { return max32(max16(row16_max(x))); }
 
 // Inclusive prefix sum over the 64 lanes of a wave (DPP: row shifts, then
 // row broadcasts 15 and 31).

@@ -40,8 +40,6 @@ struct MhLayout {
   static constexpr int kQPerWave = 64 / G;
 };
 
-__device__ __forceinline__ float shfl32(float x) { return __shfl_xor(x, 32, kWave); }
-
 template <int G>
 __global__ __launch_bounds__(MhLayout<G>::kThreads) void mhsel_prefill_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc, float* __restrict__ scores, int Tq, int q_start,
@@ -152,7 +150,7 @@ __global__ __launch_bounds__(MhLayout<G>::kThreads) void mhsel_prefill_kernel(
   // The two lane halves hold different windows of the same column.
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
-    const float mo = shfl32(m_run[n]), zo = shfl32(z_run[n]);
+    const float mo = partner32(m_run[n]), zo = partner32(z_run[n]);
     const float mn = fmaxf(m_run[n], mo);
     const float ms = mn == -INFINITY ? 0.f : mn;
     const float z = z_run[n] * __builtin_amdgcn_exp2f(m_run[n] - ms) + zo * __builtin_amdgcn_exp2f(mo - ms);
@@ -203,7 +201,7 @@ __global__ __launch_bounds__(MhLayout<G>::kThreads) void mhsel_prefill_kernel(
             float sum = __builtin_amdgcn_exp2f(acc[m][n][r0] * sl2 - offr[m][r0]);
 #pragma unroll
             for (int u = 1; u < kRegsPerQ; ++u) sum += __builtin_amdgcn_exp2f(acc[m][n][r0 + u] * sl2 - offr[m][r0 + u]);
-            if constexpr (G == 8) sum += shfl32(sum);  // heads 4..7 sit in the other lane half
+            if constexpr (G == 8) sum = sum32(sum);  // heads 4..7 sit in the other lane half
             if (masked) {
               const int rowc = 32 * m + 8 * (r0 >> 2) + 4 * half + (r0 & 3);
               sum = w < visible_windows(q_start + qbase + rowc / G, W) ? sum : -INFINITY;
@@ -211,7 +209,7 @@ __global__ __launch_bounds__(MhLayout<G>::kThreads) void mhsel_prefill_kernel(
             best = fmaxf(best, sum);
           }
         }
-        if constexpr (G != 8) best = fmaxf(best, shfl32(best));  // the other half holds other queries
+        if constexpr (G != 8) best = max32(best);  // the other half holds other queries
         if (half == 0) s_cm[wave][wl] = best;
       }
     }

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void fsel_prefill_kernel(const uint8_t* __rest
       if (w < vis_lim[0][r]) cm = fmaxf(cm, acc0[r] * scale);
       if (w < vis_lim[1][r]) cm = fmaxf(cm, acc1[r] * scale);
     }
-    cm = fmaxf(cm, xor_shfl(cm, 32));
+    cm = max32(cm);
     if (half == 0) s_cmax[1 + wr] = cm;
     __syncthreads();
     const int t = threadIdx.x;
