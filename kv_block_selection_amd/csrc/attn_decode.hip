@@ -332,6 +332,60 @@ __global__ __launch_bounds__(kHeadDim) void attn_combine_kernel(const float* __r
   }
 }
 
+// The same merge with one workgroup per row: thread = (head, 4 channels),
+// float4 partial loads and one 8-byte bf16 store (or 16-byte fp32) per thread.
+#ifndef SPARDA_COMBINE_ROW
+#define SPARDA_COMBINE_ROW 1
+#endif
+template <typename Tag, int MAXS>
+__global__ __launch_bounds__(256) void attn_combine_row_kernel(const float* __restrict__ part_o,
+                                                               const float2* __restrict__ part_ml,
+                                                               uint8_t* __restrict__ out, int G, int splits) {
+  const long row = blockIdx.x;
+  const int g = threadIdx.x / (kHeadDim / 4);
+  const int ch = (threadIdx.x % (kHeadDim / 4)) * 4;
+  if (g >= G) return;
+  float2 ml[MAXS];
+  float4 po[MAXS];
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {
+    if (s < splits) {
+      ml[s] = part_ml[(row * splits + s) * G + g];
+      po[s] = *reinterpret_cast<const float4*>(part_o + ((row * splits + s) * G + g) * kHeadDim + ch);
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s)
+    if (s < splits) M = fmaxf(M, ml[s].x);
+  float L = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) {
+      if (s < splits && ml[s].x != -INFINITY) {
+        const float w = fast_exp(ml[s].x - M);
+        L = fmaf(ml[s].y, w, L);
+        O[0] = fmaf(po[s].x, w, O[0]);
+        O[1] = fmaf(po[s].y, w, O[1]);
+        O[2] = fmaf(po[s].z, w, O[2]);
+        O[3] = fmaf(po[s].w, w, O[3]);
+      }
+    }
+  }
+  float o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = L > 0.f ? O[e] / L : 0.f;
+  const long off = (row * G + g) * kHeadDim + ch;
+  if constexpr (DT<Tag>::kBytes == 2) {
+    uint2 v;
+    v.x = pack_bf16(o[0], o[1]);
+    v.y = pack_bf16(o[2], o[3]);
+    *reinterpret_cast<uint2*>(out + off * 2) = v;
+  } else {
+    *reinterpret_cast<float4*>(out + off * 4) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 int decode_attn_splits(const AttnDims& d) {
   const long rows = (long)d.B * d.Hkv;
   long want = (kAttnTargetWaves + rows - 1) / rows;
@@ -370,7 +424,14 @@ static void launch_attn_g(const void* q, const void* k, const void* v, const int
   hipLaunchKernelGGL((attn_decode_kernel<Tag, G>), dim3(rows, splits), dim3(kWave), 0, s,
                      (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, part_o, part_ml,
                      (uint8_t*)out, d.T, d.nB, d.k, d.kv_mode, d.q_start, bps, splits, d.scale);
-  if (splits > 1) {
+  if (splits > 1 && SPARDA_COMBINE_ROW && G * (kHeadDim / 4) <= 256) {
+    if (splits <= 16)
+      hipLaunchKernelGGL((attn_combine_row_kernel<Tag, 16>), dim3(rows), dim3(G * (kHeadDim / 4)), 0, s, part_o,
+                         part_ml, (uint8_t*)out, G, splits);
+    else
+      hipLaunchKernelGGL((attn_combine_row_kernel<Tag, kAttnMaxSplits>), dim3(rows), dim3(G * (kHeadDim / 4)), 0, s,
+                         part_o, part_ml, (uint8_t*)out, G, splits);
+  } else if (splits > 1) {
     const dim3 grid(rows, G);
     if (splits <= 16)
       hipLaunchKernelGGL((attn_combine_kernel<Tag, 16>), grid, dim3(kHeadDim), 0, s, part_o, part_ml,
