@@ -14,9 +14,12 @@
 //                register order. The MFMA k index then runs over the keys in
 //                the accumulator's row order (groups of 4); V^T fragments are
 //                read from LDS in that same order, so the sum is unchanged.
-// K and V blocks arrive in LDS by direct global->LDS loads one block ahead (K
-// rows granule-swizzled and double-buffered; V row-major, then transposed
-// LDS->LDS into V^T with row stride 72 keys). A workgroup holds at most 4
+// K and V blocks arrive in LDS by direct global->LDS loads one block ahead,
+// double-buffered, rows granule-swizzled (16-byte granule g of row r sits at
+// g ^ (r & 15)). V^T fragments come straight from row-major V through the LDS
+// transpose read ds_read_b64_tr_b16: within each group of 16 lanes, source lane
+// 4e + q points at 4 consecutive channels of key kbase + e, and lane j receives
+// channel dbase + j of keys kbase .. kbase + 3. A workgroup holds at most 4
 // heads; a group of 8 runs as two workgroups.
 #include "common.h"
 #include "launch.h"
@@ -25,16 +28,32 @@ namespace sparda {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
 constexpr int kRowB = kHeadDim * 2;         // bytes per bf16 row
-constexpr int kKBytes = kBlock * kRowB;     // one K block in LDS
-constexpr int kVtStride = kBlock + 8;       // V^T row stride in elements (144 B)
-constexpr int kVtBytes = kHeadDim * kVtStride * 2;
+constexpr int kKBytes = kBlock * kRowB;     // one K (or V) block in LDS
 
 __device__ __forceinline__ bf16x8 as_v8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ int swz(int r, int g) { return r * kRowB + ((g ^ (r & 15)) << 4); }
+
+// Two transposed 8-byte reads of a swizzled V block give the V^T MFMA fragment
+// of keys {kb .. kb+3, kb+8 .. kb+11} at channel dbase + (lane % 16), where the
+// lane's 16-lane group fixes kb and dbase.
+__device__ __forceinline__ u32x4 vt_frag(const uint8_t* vblk, int kb, int dbase, int lane) {
+  const int r = lane & 15;
+  const int key = kb + (r >> 2);
+  const int ch = dbase + 4 * (r & 3);
+  const int off = (ch & 7) * 2;  // 0 or 8 bytes into the granule
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(vblk + key * kRowB + (((ch >> 3) ^ (key & 15)) << 4) + off));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(vblk + (key + 8) * kRowB + (((ch >> 3) ^ ((key + 8) & 15)) << 4) + off));
+  const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+  return u32x4{ua.x, ua.y, ub.x, ub.y};
+}
 
 template <int NT>
 __device__ __forceinline__ void load_k_lds(const uint8_t* __restrict__ src_block, uint8_t* dst) {
@@ -61,8 +80,7 @@ __global__ __launch_bounds__(64 * HPW) void attn_prefill_kernel(
     int n_tiles, int k, float scale) {
   constexpr int NT = 64 * HPW;  // threads: one wave per head of the workgroup's head group
   __shared__ __attribute__((aligned(16))) uint8_t s_k[2][kKBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[kKBytes];  // raw V block, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[kHeadDim * kVtStride];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[2][kKBytes];
 
   const long row = blockIdx.x;  // (b, kv head)
   const int tile = blockIdx.y;
@@ -98,36 +116,9 @@ __global__ __launch_bounds__(64 * HPW) void attn_prefill_kernel(
   };
   int j = 0;
   while (j < k && !usable(j)) ++j;
-  // V block: direct global->LDS copy (row-major), then transposed LDS->LDS
-  auto load_v_lds = [&](int b) {
-    const uint8_t* src = vbuf + (row * (long)T + (long)b * kBlock) * kRowB;
-    const int wave = threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
-#pragma unroll
-    for (int it = 0; it < 1024 / NT; ++it) {
-      const int base = (it * (NT / kWave) + wave) * kWave;
-      __builtin_amdgcn_global_load_lds(src + (base + lane) * 16,
-                                       (__attribute__((address_space(3))) void*)(s_v + base * 16), 16, 0, 0);
-    }
-  };
-  auto transpose_v = [&]() {
-#pragma unroll
-    for (int it = 0; it < 1024 / NT; ++it) {
-      const int slot = it * NT + threadIdx.x;  // key = slot / 16, 8 channels from (slot % 16) * 8
-      const int key = slot >> 4;
-      const int d0 = (slot & 15) * 8;
-      const u32x4 w4 = *reinterpret_cast<const u32x4*>(s_v + slot * 16);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t w = w4[e];
-        s_vt[(d0 + 2 * e) * kVtStride + key] = (uint16_t)(w & 0xFFFFu);
-        s_vt[(d0 + 2 * e + 1) * kVtStride + key] = (uint16_t)(w >> 16);
-      }
-    }
-  };
   if (j < k) {
     load_k_lds<NT>(kbuf + (row * (long)T + (long)sel[j] * kBlock) * kRowB, s_k[0]);
-    load_v_lds(sel[j]);
+    load_k_lds<NT>(vbuf + (row * (long)T + (long)sel[j] * kBlock) * kRowB, s_v[0]);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
@@ -140,11 +131,9 @@ __global__ __launch_bounds__(64 * HPW) void attn_prefill_kernel(
     const int b = sel[j];
     int jn = j + 1;
     while (jn < k && !usable(jn)) ++jn;
-    transpose_v();   // this block's V -> V^T
-    __syncthreads(); // V^T complete; the raw V buffer is free again
-    if (jn < k) {
+    if (jn < k) {  // buffers buf ^ 1 were last read before the previous barrier
       load_k_lds<NT>(kbuf + (row * (long)T + (long)sel[jn] * kBlock) * kRowB, s_k[buf ^ 1]);
-      load_v_lds(sel[jn]);
+      load_k_lds<NT>(vbuf + (row * (long)T + (long)sel[jn] * kBlock) * kRowB, s_v[buf ^ 1]);
     }
 
     // S^T = K Q^T: 2 key tiles x 2 query tiles
@@ -208,10 +197,8 @@ __global__ __launch_bounds__(64 * HPW) void attn_prefill_kernel(
         const int kb = 32 * mk + 16 * s + 4 * half;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const uint16_t* vrow = s_vt + (32 * dt + l32) * kVtStride;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kb);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kb + 8);
-          const u32x4 va = {lo.x, lo.y, hi.x, hi.y};
+          // lane group (lane / 16): channels 32 dt + 16 ((lane / 16) % 2) .. +15
+          const u32x4 va = vt_frag(s_v[buf], kb, 32 * dt + 16 * ((lane >> 4) & 1), lane);
 #pragma unroll
           for (int n = 0; n < 2; ++n) {
             const u32x4 pb = {pp[n][mk][4 * s], pp[n][mk][4 * s + 1], pp[n][mk][4 * s + 2], pp[n][mk][4 * s + 3]};
