@@ -152,33 +152,47 @@ __global__ __launch_bounds__(64 * HPW) void attn_prefill_kernel(
           sacc[mk][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8(ka), as_v8(qf[n][s]), sacc[mk][n], 0, 0, 0);
       }
     }
-    // causal mask, scale, online softmax per query column
+    // online softmax per query column, on raw scores: the reference m_run is
+    // kept in raw units and p = exp2(x * c - m * c) with c = scale * log2(e).
+    // Only a block that reaches the tile's own positions needs the causal
+    // mask (and the guard for a query that sees no key yet); the others are
+    // wholly visible to every query of the tile.
     const int key_base = b * kBlock;
+    const float c2 = scale * 1.4426950408889634f;
+    const bool diag = key_base + kBlock - 1 > p_first;
     uint32_t pp[2][2][8];  // bf16 pairs of P^T, [n][mk][dword]
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int pq = p_first + 32 * n + l32;  // this lane's query position
       float mx = -INFINITY;
+      if (diag) {
 #pragma unroll
-      for (int mk = 0; mk < 2; ++mk)
+        for (int mk = 0; mk < 2; ++mk)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key_base + 32 * mk + 8 * (r >> 2) + 4 * half + (r & 3);
-          const float x = key <= pq ? sacc[mk][n][r] * scale : -INFINITY;
-          sacc[mk][n][r] = x;
-          mx = fmaxf(mx, x);
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int key = key_base + 32 * mk + 8 * (r >> 2) + 4 * half + (r & 3);
+            const float x = key <= pq ? sacc[mk][n][r] : -INFINITY;
+            sacc[mk][n][r] = x;
+            mx = fmaxf(mx, x);
+          }
+      } else {
+#pragma unroll
+        for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mk][n][r]);
+      }
       mx = max32(mx);
       const float mn = fmaxf(m_run[n], mx);
-      const bool none = mn == -INFINITY;
-      const float alpha = none ? 1.f : fast_exp(m_run[n] - mn);
+      const bool none = mn == -INFINITY;  // only possible on a diagonal block
+      const float alpha = m_run[n] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run[n] - mn) * c2);
+      const float mc = none ? 0.f : mn * c2;
       float sum = 0.f;
 #pragma unroll
       for (int mk = 0; mk < 2; ++mk) {
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = none ? 0.f : fast_exp(sacc[mk][n][r] - mn);
-          const float p1 = none ? 0.f : fast_exp(sacc[mk][n][r + 1] - mn);
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[mk][n][r], c2, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[mk][n][r + 1], c2, -mc));
           sum += p0 + p1;
           pp[n][mk][r >> 1] = pack_bf16(p0, p1);
         }
