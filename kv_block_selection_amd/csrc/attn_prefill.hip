@@ -14,8 +14,11 @@
 //                register order. The MFMA k index then runs over the keys in
 //                the accumulator's row order (groups of 4); V^T fragments are
 //                read from LDS in that same order, so the sum is unchanged.
-// K and V blocks arrive in LDS by direct global->LDS loads one block ahead,
-// double-buffered, rows granule-swizzled (16-byte granule g of row r sits at
+// Each 64-key block is worked as two 32-key halves in a software pipeline: the
+// matrix cores compute the scores of the next half while the vector ALUs run
+// the softmax of the current one, then its PV products. K and V blocks arrive
+// in LDS by direct global->LDS loads a block ahead (three K buffers, two V
+// buffers), rows granule-swizzled (16-byte granule g of row r sits at
 // g ^ (r & 15)). V^T fragments come straight from row-major V through the LDS
 // transpose read ds_read_b64_tr_b16: within each group of 16 lanes, source lane
 // 4e + q points at 4 consecutive channels of key kbase + e, and lane j receives
@@ -79,7 +82,7 @@ __global__ __launch_bounds__(64 * HPW) void attn_prefill_kernel(
     const int32_t* __restrict__ idx, uint8_t* __restrict__ out, int G, int Tq, int q_start, int T, int nB,
     int n_tiles, int k, float scale) {
   constexpr int NT = 64 * HPW;  // threads: one wave per head of the workgroup's head group
-  __shared__ __attribute__((aligned(16))) uint8_t s_k[2][kKBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[3][kKBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[2][kKBytes];
 
   const long row = blockIdx.x;  // (b, kv head)
@@ -109,121 +112,142 @@ __global__ __launch_bounds__(64 * HPW) void attn_prefill_kernel(
     for (int n = 0; n < 2; ++n) o[dt][n] = f32x16{};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
-  // compact the usable slots: valid, in range, not wholly after the tile
+  // usable slots: valid, in range, not wholly after the tile
   auto usable = [&](int j) {
     const int b = sel[j];
     return b >= 0 && b < nB && b * kBlock <= p_first + kTile - 1;
   };
-  int j = 0;
-  while (j < k && !usable(j)) ++j;
-  if (j < k) {
-    load_k_lds<NT>(kbuf + (row * (long)T + (long)sel[j] * kBlock) * kRowB, s_k[0]);
-    load_k_lds<NT>(vbuf + (row * (long)T + (long)sel[j] * kBlock) * kRowB, s_v[0]);
-  }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();
-
-  // Everything issued at the top of an iteration (the next block's K and V,
-  // straight into LDS) is awaited with a full drain after this block's
-  // compute, so the overlap never depends on counting outstanding loads.
-  int buf = 0;
-  while (j < k) {
-    const int b = sel[j];
-    int jn = j + 1;
-    while (jn < k && !usable(jn)) ++jn;
-    if (jn < k) {  // buffers buf ^ 1 were last read before the previous barrier
-      load_k_lds<NT>(kbuf + (row * (long)T + (long)sel[jn] * kBlock) * kRowB, s_k[buf ^ 1]);
-      load_k_lds<NT>(vbuf + (row * (long)T + (long)sel[jn] * kBlock) * kRowB, s_v[buf ^ 1]);
-    }
-
-    // S^T = K Q^T: 2 key tiles x 2 query tiles
-    f32x16 sacc[2][2];
+  auto next_usable = [&](int j) {
+    while (j < k && !usable(j)) ++j;
+    return j;
+  };
+  auto load_block = [&](const uint8_t* base, int j, uint8_t* dst) {
+    load_k_lds<NT>(base + (row * (long)T + (long)sel[j] * kBlock) * kRowB, dst);
+  };
+  // S^T for key half h (keys 32h .. 32h+31 of the block) x both query tiles
+  auto scores_half = [&](const uint8_t* kblk, int h, f32x16 (&sa)[2]) {
 #pragma unroll
-    for (int mk = 0; mk < 2; ++mk)
-#pragma unroll
-      for (int n = 0; n < 2; ++n) sacc[mk][n] = f32x16{};
+    for (int n = 0; n < 2; ++n) sa[n] = f32x16{};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(kblk + swz(32 * h + l32, 2 * s + half));
 #pragma unroll
-      for (int mk = 0; mk < 2; ++mk) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(s_k[buf] + swz(32 * mk + l32, 2 * s + half));
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-          sacc[mk][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8(ka), as_v8(qf[n][s]), sacc[mk][n], 0, 0, 0);
-      }
+      for (int n = 0; n < 2; ++n)
+        sa[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8(ka), as_v8(qf[n][s]), sa[n], 0, 0, 0);
     }
-    // online softmax per query column, on raw scores: the reference m_run is
-    // kept in raw units and p = exp2(x * c - m * c) with c = scale * log2(e).
-    // Only a block that reaches the tile's own positions needs the causal
-    // mask (and the guard for a query that sees no key yet); the others are
-    // wholly visible to every query of the tile.
-    const int key_base = b * kBlock;
-    const float c2 = scale * 1.4426950408889634f;
-    const bool diag = key_base + kBlock - 1 > p_first;
-    uint32_t pp[2][2][8];  // bf16 pairs of P^T, [n][mk][dword]
+  };
+  // Online softmax of one key half per query column, on raw scores: the
+  // reference m_run is kept in raw units and p = exp2(x * c - m * c) with
+  // c = scale * log2(e). Only a block that reaches the tile's own positions
+  // needs the causal mask (and the guard for a query that sees no key yet).
+  // The reference moves only when a score exceeds it by more than 2^8 in exp2
+  // units, so most halves leave the accumulators alone; numerator and
+  // denominator share it, so the result does not depend on where it sits.
+  const float c2 = scale * 1.4426950408889634f;
+  auto softmax_half = [&](f32x16 (&sa)[2], int key0, bool diag, uint32_t (&ph)[2][8]) {
+    float alphas[2];
+    bool rescale = false;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int pq = p_first + 32 * n + l32;  // this lane's query position
       float mx = -INFINITY;
       if (diag) {
 #pragma unroll
-        for (int mk = 0; mk < 2; ++mk)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key_base + 32 * mk + 8 * (r >> 2) + 4 * half + (r & 3);
-            const float x = key <= pq ? sacc[mk][n][r] : -INFINITY;
-            sacc[mk][n][r] = x;
-            mx = fmaxf(mx, x);
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const float x = key <= pq ? sa[n][r] : -INFINITY;
+          sa[n][r] = x;
+          mx = fmaxf(mx, x);
+        }
       } else {
 #pragma unroll
-        for (int mk = 0; mk < 2; ++mk)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[mk][n][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[n][r]);
       }
       mx = max32(mx);
-      const float mn = fmaxf(m_run[n], mx);
+      const bool grow = (mx - m_run[n]) * c2 > 8.f || (m_run[n] == -INFINITY && mx != -INFINITY);
+      const float mn = grow ? mx : m_run[n];
       const bool none = mn == -INFINITY;  // only possible on a diagonal block
-      const float alpha = m_run[n] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run[n] - mn) * c2);
+      const float alpha = grow && m_run[n] != -INFINITY ? __builtin_amdgcn_exp2f((m_run[n] - mn) * c2) : 1.f;
+      rescale |= alpha != 1.f;
       const float mc = none ? 0.f : mn * c2;
       float sum = 0.f;
 #pragma unroll
-      for (int mk = 0; mk < 2; ++mk) {
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[mk][n][r], c2, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[mk][n][r + 1], c2, -mc));
-          sum += p0 + p1;
-          pp[n][mk][r >> 1] = pack_bf16(p0, p1);
-        }
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sa[n][r], c2, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sa[n][r + 1], c2, -mc));
+        sum += p0 + p1;
+        ph[n][r >> 1] = pack_bf16(p0, p1);
       }
       sum = sum32(sum);
       l_run[n] = l_run[n] * alpha + sum;
       m_run[n] = mn;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt][n] *= alpha;
+      alphas[n] = alpha;
     }
-    // O^T += V^T P^T over 4 k-steps of 16 keys (2 per key tile)
+    if (__ballot(rescale)) {  // wave-uniform; lanes that keep their reference have alpha 1
 #pragma unroll
-    for (int mk = 0; mk < 2; ++mk)
+      for (int n = 0; n < 2; ++n)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int kb = 32 * mk + 16 * s + 4 * half;
+        for (int dt = 0; dt < 4; ++dt) o[dt][n] *= alphas[n];
+    }
+  };
+  // O^T += V^T P^T for key half h: 2 k-steps of 16 keys
+  auto pv_half = [&](const uint8_t* vblk, int h, const uint32_t (&ph)[2][8]) {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          // lane group (lane / 16): channels 32 dt + 16 ((lane / 16) % 2) .. +15
-          const u32x4 va = vt_frag(s_v[buf], kb, 32 * dt + 16 * ((lane >> 4) & 1), lane);
+    for (int s = 0; s < 2; ++s) {
+      const int kb = 32 * h + 16 * s + 4 * half;
 #pragma unroll
-          for (int n = 0; n < 2; ++n) {
-            const u32x4 pb = {pp[n][mk][4 * s], pp[n][mk][4 * s + 1], pp[n][mk][4 * s + 2], pp[n][mk][4 * s + 3]};
-            o[dt][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8(va), as_v8(pb), o[dt][n], 0, 0, 0);
-          }
+      for (int dt = 0; dt < 4; ++dt) {
+        // lane group (lane / 16): channels 32 dt + 16 ((lane / 16) % 2) .. +15
+        const u32x4 va = vt_frag(vblk, kb, 32 * dt + 16 * ((lane >> 4) & 1), lane);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const u32x4 pb = {ph[n][4 * s], ph[n][4 * s + 1], ph[n][4 * s + 2], ph[n][4 * s + 3]};
+          o[dt][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8(va), as_v8(pb), o[dt][n], 0, 0, 0);
         }
       }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the next block has landed
-    __syncthreads();                           // and this block's LDS reads are done
-    buf ^= 1;
-    j = jn;
+    }
+  };
+
+  // Usable blocks t = 0, 1, ...: K(t) in s_k[t % 3], V(t) in s_v[t % 2].
+  // Iteration t issues K(t+2) (into the buffer of K(t-1)) and V(t+1) (into
+  // the buffer of V(t-1)), both last read before the previous barrier, and
+  // drains them at its end: they are first read in iteration t+1.
+  int jc = next_usable(0);
+  int jn = jc < k ? next_usable(jc + 1) : k;
+  if (jc < k) {
+    load_block(kbuf, jc, s_k[0]);
+    load_block(vbuf, jc, s_v[0]);
+  }
+  if (jn < k) load_block(kbuf, jn, s_k[1]);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  f32x16 sa0[2], sa1[2];  // scores of the half being normalised / being computed
+  if (jc < k) scores_half(s_k[0], 0, sa0);
+
+  int t = 0, kc = 0;  // kc = t % 3
+  while (jc < k) {
+    const int kn = kc == 2 ? 0 : kc + 1, kn2 = kn == 2 ? 0 : kn + 1;
+    const int vc = t & 1;
+    const int jn2 = jn < k ? next_usable(jn + 1) : k;
+    if (jn2 < k) load_block(kbuf, jn2, s_k[kn2]);
+    if (jn < k) load_block(vbuf, jn, s_v[vc ^ 1]);
+    const int key_base = sel[jc] * kBlock;
+    const bool diag = key_base + kBlock - 1 > p_first;
+    uint32_t ph[2][8];
+    // half 0: scores of half 1 on the matrix cores, softmax of half 0 on the ALUs
+    scores_half(s_k[kc], 1, sa1);
+    softmax_half(sa0, key_base, diag, ph);
+    pv_half(s_v[vc], 0, ph);
+    // half 1: scores of the next block's half 0 (its K landed last iteration)
+    if (jn < k) scores_half(s_k[kn], 0, sa0);
+    softmax_half(sa1, key_base + 32, diag, ph);
+    pv_half(s_v[vc], 1, ph);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // K(t+2) and V(t+1) have landed
+    __syncthreads();                           // and this iteration's LDS reads are done
+    jc = jn;
+    jn = jn2;
+    kc = kn;
+    ++t;
   }
 
   // O = O^T / l, written as 4 consecutive channels (8 B) per accumulator group
