@@ -123,8 +123,8 @@ def _workspace(ws, nbytes: int, like):
     if nbytes == 0:
         return None, 0
     if ws is None:
-        # zero-filled: split counters in the attention workspace start at zero
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=like.device)
+        # no initial contents are needed (every byte read is written first by the same call)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=like.device)
     if ws.numel() * ws.element_size() < nbytes:
         raise ValueError(f"workspace has {ws.numel() * ws.element_size()} bytes, needs {nbytes}")
     return ws, ws.numel() * ws.element_size()
