@@ -35,6 +35,11 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dppu(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
+// Value of lane `l` (read as a scalar), kept unsigned: readlane itself is
+// typed int, and the keys compare as unsigned.
+__device__ __forceinline__ uint32_t lane_u(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
 // Wave reductions: a butterfly inside each 16-lane DPP row, then the four row
 // results read as scalars.
 __device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
@@ -42,16 +47,14 @@ __device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
   v = min(v, dppu<0x4E>(v));
   v = min(v, dppu<0x141>(v));
   v = min(v, dppu<0x140>(v));
-  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+  return min(min(lane_u(v, 0), lane_u(v, 16)), min(lane_u(v, 32), lane_u(v, 48)));
 }
 __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
   v = max(v, dppu<0xB1>(v));
   v = max(v, dppu<0x4E>(v));
   v = max(v, dppu<0x141>(v));
   v = max(v, dppu<0x140>(v));
-  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+  return max(max(lane_u(v, 0), lane_u(v, 16)), max(lane_u(v, 32), lane_u(v, 48)));
 }
 __device__ __forceinline__ int wave_isum(int v) {
   uint32_t u = (uint32_t)v;
@@ -59,8 +62,7 @@ __device__ __forceinline__ int wave_isum(int v) {
   u += dppu<0x4E>(u);
   u += dppu<0x141>(u);
   u += dppu<0x140>(u);
-  return (int)(__builtin_amdgcn_readlane(u, 0) + __builtin_amdgcn_readlane(u, 16) + __builtin_amdgcn_readlane(u, 32) +
-               __builtin_amdgcn_readlane(u, 48));
+  return (int)(lane_u(u, 0) + lane_u(u, 16) + lane_u(u, 32) + lane_u(u, 48));
 }
 
 // A value v with at least r lanes of the wave holding x >= v, and v no larger
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
       above += h[i];
     }
     const int src_lane = __ffsll(__ballot(hit)) - 1;  // exactly one lane holds the digit
-    prefix |= (uint32_t)__builtin_amdgcn_readlane((int)my_digit, src_lane) << sft;
+    prefix |= lane_u(my_digit, src_lane) << sft;
     remaining -= __builtin_amdgcn_readlane(my_above, src_lane);
     lo = sft;
     cur = nxt;
@@ -211,10 +213,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
   for (int j = 0; j < NPT; ++j) {
     if (key[j] != 0u) {
       const uint32_t top = lo >= 32 ? 0u : (key[j] - lb) >> lo;
+      // pos < kk holds by construction; the test keeps a row inside its k slots
       if (top > plo) {
-        dst[pos++] = t * NPT + j;
+        if (pos < kk) dst[pos] = t * NPT + j;
+        ++pos;
       } else if (top == plo) {
-        if (eq_rank < remaining) dst[pos++] = t * NPT + j;
+        if (eq_rank < remaining && pos < kk) dst[pos++] = t * NPT + j;
         ++eq_rank;
       }
     }

@@ -157,6 +157,31 @@ def test_topk_signed_zero_tie(gpu):
     np.testing.assert_array_equal(idx, [[0, 2], [0, 1]])
 
 
+@pytest.mark.parametrize("nB", [5, 37, 100, 1000])
+def test_topk_mixed_sign_lane_groups(gpu, nB):
+    """Rows where some 16-lane groups of the wave see only negative scores and
+    others see positive ones (the unsigned order of the keys must hold across
+    groups), short rows that leave lanes empty, and sentinels after the output
+    that no row may overwrite."""
+    rng = np.random.default_rng(1000 + nB)
+    rows, k = 8, 4
+    s = -np.abs(rng.standard_normal((rows, nB))).astype(np.float32) - 0.5
+    npt = (nB + 255) // 256
+    for r in range(rows):
+        # positive scores only in blocks owned by one 16-lane group of one wave
+        lanes = np.arange(16) + 16 * (r % 4) + 64 * ((r // 4) % 4)
+        blk = (lanes[:, None] * npt + np.arange(npt)[None, :]).ravel()
+        blk = blk[blk < nB]
+        s[r, blk[: max(1, len(blk) // 2)]] = np.abs(rng.standard_normal(max(1, len(blk) // 2))) + 0.5
+    s[1, nB // 3] = -np.inf
+    for kk in (1, k, min(nB, 20)):
+        out = torch.full((rows + 1, kk), -7, dtype=torch.int32, device=DEV)
+        gpu.topk_blocks(torch.from_numpy(s).to(DEV), kk, out=out[:rows])
+        got = out.cpu().numpy()
+        assert (got[rows] == -7).all(), "top-k wrote past its output"
+        np.testing.assert_array_equal(got[:rows], oracle.topk_blocks(s.astype(np.float64), kk), err_msg=f"k={kk}")
+
+
 # -------------------------------------------------------------- attention ---
 def _attention_case(kbs, w, idx_np):
     Q, K, V = gen(w, "Q"), gen(w, "K"), gen(w, "V")
