@@ -17,9 +17,15 @@
  *    always float32, indices int32). Arithmetic accumulates in float32.
  *  - Supported geometry (v1): d = 128, block = 64, kernel = 32, stride = 16,
  *    tile = 64, T % 64 == 0, T >= 64, Hq % Hkv == 0, Tq == 1 or Tq % 64 == 0,
- *    q_start + Tq == T (the chunk ends at the newest token).
- *    W = (T - kernel)/stride + 1 windows, nB = T/block blocks,
- *    nTiles = ceil(Tq/tile) query tiles (1 for decode).
+ *    q_start + Tq <= T. W = (T - kernel)/stride + 1 windows, nB = T/block
+ *    blocks, nTiles = ceil(Tq/tile) query tiles (1 for decode).
+ *  - T is the extent of the KV cache rows (tokens stored per row); queries sit
+ *    at positions q_start .. q_start + Tq - 1. Everything is causal by
+ *    position: windows, blocks and keys after a query's position take no part
+ *    in its scores or its attention, so a cache may be allocated with room to
+ *    grow and filled as decoding proceeds (the chunk need not end at T).
+ *    Positions after the newest query may hold any finite values: their
+ *    scores are masked, and their values enter only with weight 0.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream). Arguments are validated on the host before anything is
  *    enqueued; on error nothing is launched. Device faults surface at the
@@ -75,6 +81,22 @@ int sparda_compress_keys(const void* k, void* k_cmp, int dtype, int B, int Hkv, 
                          int kernel, int stride, void* stream);
 
 /*
+ * Step 1, incremental: the windows [w_begin, w_end) only, for a KV cache that
+ * grows while decoding ([P2] 四 for the windows; the cache grows by one token
+ * per step, so window w becomes complete once the sequence holds
+ * stride*w + kernel tokens).
+ *   k      [B, Hkv, T_cap, d]  cache rows of capacity T_cap tokens
+ *   k_cmp  [B, Hkv, W_cap, d]  out; windows outside [w_begin, w_end) are left untouched
+ * Window w needs tokens stride*w .. stride*w + kernel - 1, so
+ * stride*(w_end - 1) + kernel <= T_cap is required. The arithmetic is that of
+ * sparda_compress_keys: on the same tokens the two give the same bits.
+ * Errors: SPARDA_ERR_INVALID_ARG for a range outside the capacities; the rest
+ * as sparda_compress_keys. An empty range or batch is a valid no-op.
+ */
+int sparda_compress_windows(const void* k, void* k_cmp, int dtype, int B, int Hkv, int T_cap, int W_cap,
+                            int d, int kernel, int stride, int w_begin, int w_end, void* stream);
+
+/*
  * Step 2 - Forecast block scoring. [P1] paragraph on one Forecast head per GQA
  * group; [P2] 二; [P3] 解法: one Forecast vector per GQA group scores the
  * compressed keys directly - no per-query-head loop, no softmax.
@@ -85,7 +107,7 @@ int sparda_compress_keys(const void* k, void* k_cmp, int dtype, int B, int Hkv, 
  * query at position p when stride*w + kernel - 1 <= p. Block score of a query
  * = max of s over the visible windows whose token span meets the block; a
  * tile's score = max over its queries; -inf marks a block with no visible
- * window (not a candidate). Decode is Tq = 1, q_start = T - 1. A chunk of
+ * window (not a candidate). Decode is Tq = 1 at position q_start. A chunk of
  * queries (Tq a multiple of 64) runs on the matrix cores and needs bf16.
  * ws: none needed (ws may be NULL, ws_bytes 0).
  */

@@ -35,6 +35,7 @@ _vp, _i, _f, _sz = _c.c_void_p, _c.c_int, _c.c_float, _c.c_size_t
 # name -> (restype, argtypes), exactly as declared in include/sparda.h
 SIGNATURES = {
     "sparda_compress_keys": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "sparda_compress_windows": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "sparda_select_forecast": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
     "sparda_select_multihead": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz,
                                      _vp]),
@@ -140,6 +141,18 @@ def compress_keys(k, out=None, stream=None):
     _call("sparda_compress_keys", _ptr(k), _ptr(out), _dtype_code(k), B, Hkv, T, d, KERNEL, STRIDE,
           _stream(k, stream))
     return out
+
+
+def compress_windows(k, k_cmp, w_begin: int, w_end: int, stream=None):
+    """Windows [w_begin, w_end) of K cache rows [B, Hkv, T_cap, 128] into k_cmp
+    [B, Hkv, W_cap, 128] (the other windows are left as they are)."""
+    B, Hkv, T_cap, d = k.shape
+    W_cap = k_cmp.shape[2]
+    if k_cmp.shape[:2] != (B, Hkv) or k_cmp.dtype != k.dtype:
+        raise ValueError("k_cmp must be [B, Hkv, W_cap, 128] in k's dtype")
+    _call("sparda_compress_windows", _ptr(k), _ptr(k_cmp), _dtype_code(k), B, Hkv, T_cap, W_cap, d, KERNEL, STRIDE,
+          w_begin, w_end, _stream(k, stream))
+    return k_cmp
 
 
 def select_forecast(f, k_cmp, T: int, q_start: int, scale: float | None = None, out=None, stream=None):

@@ -68,8 +68,8 @@ int check_geometry(int B, int Hq, int Hkv, int Tq, int q_start, int T, int d) {
         "T = %d must be a positive multiple of 64", T);
   CHECK(Tq >= 1, SPARDA_ERR_INVALID_ARG, "Tq = %d < 1", Tq);
   CHECK(Tq == 1 || Tq % sparda::kTile == 0, SPARDA_ERR_UNSUPPORTED, "Tq = %d is neither 1 nor a multiple of 64", Tq);
-  CHECK(q_start >= 0 && (long)q_start + Tq == T, SPARDA_ERR_INVALID_ARG,
-        "the query chunk must end at the newest token: q_start %d + Tq %d != T %d", q_start, Tq, T);
+  CHECK(q_start >= 0 && (long)q_start + Tq <= T, SPARDA_ERR_INVALID_ARG,
+        "the query chunk must lie inside the cache: q_start %d + Tq %d > T %d", q_start, Tq, T);
   CHECK((long)B * Hkv <= 65535, SPARDA_ERR_UNSUPPORTED, "B*Hkv = %ld exceeds 65535", (long)B * Hkv);
   return SPARDA_OK;
 }
@@ -167,8 +167,29 @@ SPARDA_EXPORT int sparda_compress_keys(const void* k, void* k_cmp, int dtype, in
   CHECK_PTR(k);
   CHECK_PTR(k_cmp);
   const int W = (T - kernel) / stride + 1;
-  return hip_status(sparda::launch_compress(k, k_cmp, dtype == SPARDA_BF16, B * Hkv, T, W, (hipStream_t)stream),
+  return hip_status(sparda::launch_compress(k, k_cmp, dtype == SPARDA_BF16, B * Hkv, T, W, 0, W, (hipStream_t)stream),
                     "compress_keys launch");
+}
+
+SPARDA_EXPORT int sparda_compress_windows(const void* k, void* k_cmp, int dtype, int B, int Hkv, int T_cap, int W_cap,
+                                          int d, int kernel, int stride, int w_begin, int w_end, void* stream) {
+  if (int e = check_dtype(dtype)) return e;
+  CHECK(B >= 0 && Hkv >= 1, SPARDA_ERR_INVALID_ARG, "B %d / Hkv %d out of range", B, Hkv);
+  CHECK(d == sparda::kHeadDim, SPARDA_ERR_UNSUPPORTED, "head dim %d != 128", d);
+  CHECK(kernel == sparda::kKernel && stride == sparda::kStride, SPARDA_ERR_UNSUPPORTED,
+        "compression kernel/stride %d/%d != 32/16", kernel, stride);
+  CHECK(T_cap >= kernel && W_cap >= 1, SPARDA_ERR_INVALID_ARG, "T_cap %d / W_cap %d too small", T_cap, W_cap);
+  CHECK(0 <= w_begin && w_begin <= w_end && w_end <= W_cap, SPARDA_ERR_INVALID_ARG,
+        "window range [%d, %d) not inside [0, W_cap = %d)", w_begin, w_end, W_cap);
+  CHECK(w_end == 0 || (long)stride * (w_end - 1) + kernel <= T_cap, SPARDA_ERR_INVALID_ARG,
+        "window %d needs tokens up to %ld, beyond T_cap = %d", w_end - 1, (long)stride * (w_end - 1) + kernel - 1,
+        T_cap);
+  if (B == 0 || w_begin == w_end) return ok();
+  CHECK_PTR(k);
+  CHECK_PTR(k_cmp);
+  return hip_status(sparda::launch_compress(k, k_cmp, dtype == SPARDA_BF16, B * Hkv, T_cap, W_cap, w_begin, w_end,
+                                            (hipStream_t)stream),
+                    "compress_windows launch");
 }
 
 SPARDA_EXPORT int sparda_select_forecast(const void* f, const void* k_cmp, float* blk_scores, int dtype, int B,

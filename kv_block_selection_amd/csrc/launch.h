@@ -26,8 +26,9 @@ struct AttnDims {
   int kv_mode;
 };
 
-// compress.hip
-hipError_t launch_compress(const void* k, void* kc, bool bf16, int rows, int T, int W, hipStream_t s);
+// compress.hip: windows [w_begin, w_end) of rows holding T tokens and W windows
+hipError_t launch_compress(const void* k, void* kc, bool bf16, int rows, int T, int W, int w_begin, int w_end,
+                           hipStream_t s);
 
 // select_decode.hip
 hipError_t launch_select_forecast_decode(const void* f, const void* kc, float* scores, bool bf16,

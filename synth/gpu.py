@@ -50,7 +50,7 @@ def _table(device):
     import torch
     key = str(device)
     if key not in _TABLES:
-        _TABLES[key] = torch.from_numpy(np.ascontiguousarray(normal_table())).to(device)
+        _TABLES[key] = torch.from_numpy(np.array(normal_table(), copy=True)).to(device)
     return _TABLES[key]
 
 

@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in kbs.SIGNATURES, f"binding lacks {n}"
@@ -56,7 +56,7 @@ def _sel(lib, **kw):
     (dict(dtype=7), 1, b"dtype"),
     (dict(d=64), 2, b"head dim"),
     (dict(T=4000, q_start=3999), 2, b"multiple of 64"),
-    (dict(q_start=100), 1, b"newest token"),
+    (dict(q_start=4096), 1, b"inside the cache"),
     (dict(kernel=16), 2, b"kernel/stride"),
     (dict(block=128), 2, b"block"),
     (dict(tile=32), 2, b"tile"),
@@ -120,3 +120,24 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kbs, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         kbs.load()
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(w_begin=5, w_end=4), 1, b"window range"),
+    (dict(w_end=300), 1, b"window range"),
+    (dict(T_cap=100, w_end=8), 1, b"beyond T_cap"),
+    (dict(T_cap=16), 1, b"too small"),
+    (dict(d=64), 2, b"head dim"),
+    (dict(k=0), 1, b"k is NULL"),
+])
+def test_compress_windows_validation(lib, args, status, needle):
+    a = dict(k=P, kc=P, dtype=1, B=2, Hkv=8, T_cap=4096, W_cap=255, d=128, kernel=32, stride=16, w_begin=0, w_end=255)
+    a.update(args)
+    st = lib.sparda_compress_windows(a["k"], a["kc"], a["dtype"], a["B"], a["Hkv"], a["T_cap"], a["W_cap"], a["d"],
+                                     a["kernel"], a["stride"], a["w_begin"], a["w_end"], None)
+    assert st == status
+    assert needle in lib.sparda_last_error()
+
+
+def test_compress_windows_empty_range_is_a_no_op(lib):
+    assert lib.sparda_compress_windows(P, P, 1, 2, 8, 4096, 255, 128, 32, 16, 7, 7, None) == 0
