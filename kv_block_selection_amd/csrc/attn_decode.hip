@@ -10,8 +10,11 @@
 //   QK  - 16 lanes hold one key row (8 bf16 each), a wave reads 4 keys (1 KiB)
 //         per load; G dot products per key via v_dot2_f32_bf16 and a DPP
 //         butterfly; scores go to LDS as [key][G].
-//   softmax - lane l takes key l: block max and sum per head by wave
-//         reductions, running (max, sum) per head (online softmax).
+//   softmax - lane l takes key l. The running max of a head moves only when
+//         a score exceeds it by more than 8 ln 2 (a ballot, wave-uniform), so
+//         probabilities stay <= 2^8 and most stages need neither a wave max
+//         nor a rescale; each lane keeps its own running sum, reduced over
+//         the wave once at the end.
 //   PV  - the same lane layout over V; each lane accumulates G x 8 outputs for
 //         its key row, reading p[key][0..G) from LDS as one broadcast.
 // A combine kernel merges the per-split (max, sum, unnormalised output).
@@ -29,6 +32,7 @@ namespace sparda {
 // many one-wave workgroups (8 resident per CU at ~250 VGPRs).
 constexpr int kAttnTargetWaves = SPARDA_ATTN_TARGET_WAVES;
 constexpr int kAttnMaxSplits = 64;
+constexpr float kLazyGrow = 5.545177444479562f;  // 8 ln 2
 
 // Reduce-scatter of G partial dot products over the 16 lanes of a key row.
 // Lane c keeps its query slots in the order head = slot XOR mask(c), with
@@ -173,13 +177,15 @@ void attn_decode_kernel(
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float s = lane < CK ? s_p[lane * G + g] : -INFINITY;
-      const float mb = wave_max(s);
-      const float mn = fmaxf(m_run[g], mb);
-      const bool none = mn == -INFINITY;  // no valid key seen yet
-      alpha[g] = none ? 1.f : fast_exp(m_run[g] - mn);
-      pr[g] = none ? 0.f : fast_exp(s - mn);
-      l_run[g] = l_run[g] * alpha[g] + wave_sum(pr[g]);
-      m_run[g] = mn;
+      alpha[g] = 1.f;
+      if (__ballot(s > m_run[g] + kLazyGrow) != 0) {  // -inf + c stays -inf: the first finite score moves it
+        const float mn = fmaxf(m_run[g], wave_max(s));
+        alpha[g] = fast_exp(m_run[g] - mn);  // 0 while no valid key was seen
+        l_run[g] *= alpha[g];
+        m_run[g] = mn;
+      }
+      pr[g] = m_run[g] == -INFINITY ? 0.f : fast_exp(s - m_run[g]);
+      l_run[g] += pr[g];  // this lane's keys only
     }
     if constexpr (kBf16) {
       // bf16 pairs (p[key], p[key + 4]) for the keys with key % 8 < 4; the
@@ -205,9 +211,12 @@ void attn_decode_kernel(
       for (int it = 0; it < NIT; ++it) kv[it] = load16_nt(kbuf + (tok0 + it * KPI + r) * RB + c * 16);
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
+      if (alpha[g] != 1.f) {  // wave-uniform
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[g][e] *= alpha[g];
+        for (int e = 0; e < E; ++e) acc[g][e] *= alpha[g];
+      }
+    }
     if constexpr (kBf16) {
       // PV on packed pairs: keys 8jp + r and 8jp + 4 + r come from loads 2jp
       // and 2jp + 1; v_perm_b32 interleaves their channels, v_dot2 applies the
@@ -251,6 +260,8 @@ void attn_decode_kernel(
   for (int q = 0; q < nstage - 1; ++q) body(q, std::true_type{});
   body(nstage - 1, std::false_type{});
 
+#pragma unroll
+  for (int g = 0; g < G; ++g) l_run[g] = wave_sum(l_run[g]);
   // reduce the KPI key rows
 #pragma unroll
   for (int g = 0; g < G; ++g)
