@@ -97,13 +97,18 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
   const int wid = t / kWave;
   const float* src = scores + row * nB;
 
+  // All NPT loads go out before any is used: the index is clamped into the
+  // row (nB >= 1) and the padding masked afterwards, since a guarded load
+  // would wait for each value in turn.
+  float x[NPT];
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) x[j] = src[min(t * NPT + j, nB - 1)];
   uint32_t key[NPT];
   int cnt = 0;
   uint32_t kmax = 0u;
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
-    const int b = t * NPT + j;
-    key[j] = b < nB ? order_key(src[b]) : 0u;
+    key[j] = t * NPT + j < nB ? order_key(x[j]) : 0u;
     cnt += key[j] != 0u;
     kmax = max(kmax, key[j]);
   }
