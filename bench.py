@@ -212,7 +212,15 @@ def bench_decode(args) -> int:
         s["scores"] = torch.empty((w.B, w.Hkv, 1, w.nB), dtype=torch.float32, device=dev)
         s["idx"] = torch.empty((w.B, w.Hkv, 1, w.k), dtype=torch.int32, device=dev)
         s["out"] = torch.empty_like(s["Q"])
+        # the newest token of every sequence again, for the cache-append timings
+        s["Knew1"] = s["K"][:, :, w.T - 1:].contiguous()
+        s["Vnew1"] = s["V"][:, :, w.T - 1:].contiguous()
+        s["Knew2"] = s["K"][:, :, w.T - 2:w.T - 1].contiguous()
+        s["Vnew2"] = s["V"][:, :, w.T - 2:w.T - 1].contiguous()
         sets.append(s)
+    pos_last = torch.full((w.B,), w.q_start, dtype=torch.int32, device=dev)
+    len_win = torch.full((w.B,), w.T - 1, dtype=torch.int32, device=dev)  # token T-1 completes window W-1
+    len_nowin = torch.full((w.B,), w.T - 2, dtype=torch.int32, device=dev)  # token T-2 completes none
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     ws_attn = torch.zeros(max(1, kbs.workspace_bytes(kbs.OP_BLOCK_SPARSE_ATTN, w.B, w.Hq, w.Hkv, 1, w.T, w.k)),
@@ -241,6 +249,23 @@ def bench_decode(args) -> int:
         topk(i)
         attn(i)
 
+    # Decode-time state maintenance: append the step's token to K, V and
+    # compress the window it completes (every 16th step) or none. The tokens
+    # written are the ones already there, so the inputs stay as they are.
+    def append_win(i):
+        s = sets[i % N_SETS]
+        kbs.append_kv(s["Knew1"], s["Vnew1"], s["K"], s["V"], len_win, k_cmp=s["Kc"])
+
+    def append_nowin(i):
+        s = sets[i % N_SETS]
+        kbs.append_kv(s["Knew2"], s["Vnew2"], s["K"], s["V"], len_nowin, k_cmp=s["Kc"])
+
+    def step_q_pos(i):  # the same step with per-sequence positions (all at T - 1)
+        s = sets[i % N_SETS]
+        kbs.select_forecast(s["F"], s["Kc"], w.T, 0, out=s["scores"], q_pos=pos_last)
+        kbs.topk_blocks(s["scores"], w.k, out=s["idx"])
+        kbs.block_sparse_attn(s["Q"], s["K"], s["V"], s["idx"], w.T, 0, out=s["out"], ws=ws_attn, q_pos=pos_last)
+
     log("[bench] warmup (eager)")
     for i in range(args.warmup):
         step(i)
@@ -255,6 +280,9 @@ def bench_decode(args) -> int:
     kr = max(1, args.kernel_iters // per_graph)
     ms = {"select_forecast": time_graph(sel, per_graph, kr), "topk": time_graph(topk, per_graph, kr),
           "attention": time_graph(attn, per_graph, kr), "select_multihead": time_graph(sel_mh, per_graph, kr)}
+    ms_extra = {"append_kv_with_window": time_graph(append_win, per_graph, kr),
+                "append_kv": time_graph(append_nowin, per_graph, kr),
+                "step_with_q_pos": time_graph(step_q_pos, per_graph, kr)}
     for i in range(N_SETS):  # leave each set's Forecast scores / idx in place
         step(i)
     torch.cuda.synchronize()
@@ -290,6 +318,7 @@ def bench_decode(args) -> int:
         "selection_us": {"forecast": round((ms["select_forecast"] + ms["topk"]) * 1e3, 2),
                          "multihead": round((ms["select_multihead"] + ms["topk"]) * 1e3, 2)},
         "forecast_vs_multihead_select_speedup": round(ms["select_multihead"] / ms["select_forecast"], 3),
+        "state_maintenance_us": {k: round(v * 1e3, 2) for k, v in ms_extra.items()},
     }
     if args.calibration_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -458,6 +487,23 @@ def bench_prefill(args) -> int:
         sel(i)
         topk(i)
         attn(i)
+
+    # Decode-time state maintenance: append the step's token to K, V and
+    # compress the window it completes (every 16th step) or none. The tokens
+    # written are the ones already there, so the inputs stay as they are.
+    def append_win(i):
+        s = sets[i % N_SETS]
+        kbs.append_kv(s["Knew1"], s["Vnew1"], s["K"], s["V"], len_win, k_cmp=s["Kc"])
+
+    def append_nowin(i):
+        s = sets[i % N_SETS]
+        kbs.append_kv(s["Knew2"], s["Vnew2"], s["K"], s["V"], len_nowin, k_cmp=s["Kc"])
+
+    def step_q_pos(i):  # the same step with per-sequence positions (all at T - 1)
+        s = sets[i % N_SETS]
+        kbs.select_forecast(s["F"], s["Kc"], w.T, 0, out=s["scores"], q_pos=pos_last)
+        kbs.topk_blocks(s["scores"], w.k, out=s["idx"])
+        kbs.block_sparse_attn(s["Q"], s["K"], s["V"], s["idx"], w.T, 0, out=s["out"], ws=ws_attn, q_pos=pos_last)
 
     for i in range(args.warmup):
         step(i)

@@ -26,6 +26,12 @@
  *    grow and filled as decoding proceeds (the chunk need not end at T).
  *    Positions after the newest query may hold any finite values: their
  *    scores are masked, and their values enter only with weight 0.
+ *  - Ragged decode batches: the decode calls (Tq = 1) of steps 2, 2' and 4
+ *    take q_pos, NULL or a device int32 array [B] holding each sequence's own
+ *    query position; q_start is then not used. Positions are read on the
+ *    device and clamped to [-1, T - 1]; -1 (or less) means an empty sequence
+ *    (no candidate block, output 0). With q_pos NULL every sequence sits at
+ *    q_start. A chunk of queries (Tq > 1) needs q_pos NULL.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream). Arguments are validated on the host before anything is
  *    enqueued; on error nothing is launched. Device faults surface at the
@@ -97,6 +103,30 @@ int sparda_compress_windows(const void* k, void* k_cmp, int dtype, int B, int Hk
                             int d, int kernel, int stride, int w_begin, int w_end, void* stream);
 
 /*
+ * Decode-time state maintenance: append tokens to the caches and compress the
+ * windows they complete, in one launch ([P2] 四 for the windows; the cache
+ * grows by one token per decode step).
+ *   k_new, v_new      [B, Hkv, n_new, d]   the new tokens' keys and values
+ *   k_cache, v_cache  [B, Hkv, T_cap, d]   caches of capacity T_cap tokens
+ *   k_cmp             [B, Hkv, W_cap, d]   compressed keys, or NULL (no windows)
+ *   seq_len           device int32 [B]: tokens each sequence holds before the
+ *                     call; its new tokens go to positions seq_len[b] ..
+ *                     seq_len[b] + n_new - 1. The call does not change it.
+ *   status            device int32, or NULL: 1 is OR-ed in when a sequence's
+ *                     tokens do not fit (seq_len[b] < 0 or seq_len[b] + n_new >
+ *                     T_cap); that sequence's rows are then left untouched.
+ * Window w is written when position stride*w + kernel - 1 is among the new
+ * ones (and w < W_cap), with the bits sparda_compress_keys would give for the
+ * same keys; its earlier keys come from the cache. Rows of the caches outside
+ * the new positions and the other windows are not touched.
+ * Errors: as sparda_compress_windows for geometry; n_new outside 0..T_cap is
+ * SPARDA_ERR_INVALID_ARG; B = 0 or n_new = 0 is a valid no-op.
+ */
+int sparda_append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache, void* k_cmp,
+                     const int* seq_len, int* status, int dtype, int B, int Hkv, int n_new, int T_cap,
+                     int W_cap, int d, int kernel, int stride, void* stream);
+
+/*
  * Step 2 - Forecast block scoring. [P1] paragraph on one Forecast head per GQA
  * group; [P2] 二; [P3] 解法: one Forecast vector per GQA group scores the
  * compressed keys directly - no per-query-head loop, no softmax.
@@ -107,13 +137,14 @@ int sparda_compress_windows(const void* k, void* k_cmp, int dtype, int B, int Hk
  * query at position p when stride*w + kernel - 1 <= p. Block score of a query
  * = max of s over the visible windows whose token span meets the block; a
  * tile's score = max over its queries; -inf marks a block with no visible
- * window (not a candidate). Decode is Tq = 1 at position q_start. A chunk of
+ * window (not a candidate). Decode is Tq = 1 at position q_start (or each
+ * sequence's q_pos entry, see the conventions above). A chunk of
  * queries (Tq a multiple of 64) runs on the matrix cores and needs bf16.
  * ws: none needed (ws may be NULL, ws_bytes 0).
  */
 int sparda_select_forecast(const void* f, const void* k_cmp, float* blk_scores, int dtype, int B,
-                           int Hkv, int Tq, int q_start, int T, int d, int kernel, int stride,
-                           int block, int tile, float scale, void* ws, size_t ws_bytes,
+                           int Hkv, int Tq, int q_start, const int* q_pos, int T, int d, int kernel,
+                           int stride, int block, int tile, float scale, void* ws, size_t ws_bytes,
                            void* stream);
 
 /*
@@ -132,8 +163,8 @@ int sparda_select_forecast(const void* f, const void* k_cmp, float* blk_scores, 
  * bf16 and no workspace: it sweeps k_cmp twice (normalisers, then group sums).
  */
 int sparda_select_multihead(const void* q, const void* k_cmp, float* blk_scores, int dtype, int B,
-                            int Hq, int Hkv, int Tq, int q_start, int T, int d, int kernel,
-                            int stride, int block, int tile, float scale, void* ws,
+                            int Hq, int Hkv, int Tq, int q_start, const int* q_pos, int T, int d,
+                            int kernel, int stride, int block, int tile, float scale, void* ws,
                             size_t ws_bytes, void* stream);
 
 /*
@@ -167,8 +198,8 @@ int sparda_topk_blocks(const float* blk_scores, int32_t* idx, int rows, int nB, 
  */
 int sparda_block_sparse_attn(const void* q, const void* k, const void* v, int kv_mode,
                              const int32_t* idx, void* out, int dtype, int B, int Hq, int Hkv,
-                             int Tq, int q_start, int T, int d, int block, int tile, int k_sel,
-                             float scale, void* ws, size_t ws_bytes, void* stream);
+                             int Tq, int q_start, const int* q_pos, int T, int d, int block, int tile,
+                             int k_sel, float scale, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Step 5 - lookahead prefetch of the selected blocks from host memory.

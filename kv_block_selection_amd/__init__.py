@@ -36,12 +36,14 @@ _vp, _i, _f, _sz = _c.c_void_p, _c.c_int, _c.c_float, _c.c_size_t
 SIGNATURES = {
     "sparda_compress_keys": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "sparda_compress_windows": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
-    "sparda_select_forecast": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp]),
-    "sparda_select_multihead": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz,
-                                     _vp]),
+    "sparda_append_kv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "sparda_select_forecast": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _i, _i, _f, _vp, _sz,
+                                    _vp]),
+    "sparda_select_multihead": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _i, _i, _f, _vp,
+                                     _sz, _vp]),
     "sparda_topk_blocks": (_i, [_vp, _vp, _i, _i, _i, _vp]),
-    "sparda_block_sparse_attn": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f,
-                                      _vp, _sz, _vp]),
+    "sparda_block_sparse_attn": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _i,
+                                      _f, _vp, _sz, _vp]),
     "sparda_prefetch_blocks": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "sparda_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "sparda_status_string": (_c.c_char_p, [_i]),
@@ -155,21 +157,55 @@ def compress_windows(k, k_cmp, w_begin: int, w_end: int, stream=None):
     return k_cmp
 
 
-def select_forecast(f, k_cmp, T: int, q_start: int, scale: float | None = None, out=None, stream=None):
-    """Forecast block scores [B, Hkv, nTiles, nB] (float32) for F [B, Hkv, Tq, 128]."""
+def _positions(q_pos, B: int):
+    """Per-sequence query positions: None, or an int32 device tensor [B]."""
+    torch = _torch()
+    if q_pos is None:
+        return None
+    if q_pos.dtype != torch.int32 or q_pos.numel() != B:
+        raise ValueError(f"q_pos must be an int32 tensor of {B} positions")
+    return _ptr(q_pos)
+
+
+def append_kv(k_new, v_new, k_cache, v_cache, seq_len, k_cmp=None, status=None, stream=None):
+    """Write k_new/v_new [B, Hkv, n_new, 128] into the caches [B, Hkv, T_cap, 128]
+    at positions seq_len[b] .. seq_len[b] + n_new - 1 (seq_len: int32 device [B],
+    not changed) and compress into k_cmp [B, Hkv, W_cap, 128] every window the
+    new tokens complete. status (int32 device [1], optional) gets 1 OR-ed in when
+    a sequence's tokens do not fit; that sequence is left untouched."""
+    torch = _torch()
+    B, Hkv, n_new, d = k_new.shape
+    T_cap = k_cache.shape[2]
+    W_cap = k_cmp.shape[2] if k_cmp is not None else 0
+    for t in (v_new, k_cache, v_cache) + ((k_cmp,) if k_cmp is not None else ()):
+        if t.dtype != k_new.dtype or t.shape[:2] != (B, Hkv) or t.shape[3] != d:
+            raise ValueError("k_new, v_new, caches and k_cmp must share dtype, [B, Hkv] and d")
+    if v_new.shape != k_new.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("k_new/v_new and k_cache/v_cache must have equal shapes")
+    if seq_len.dtype != torch.int32 or seq_len.numel() != B:
+        raise ValueError(f"seq_len must be an int32 tensor of {B} lengths")
+    if status is not None and status.dtype != torch.int32:
+        raise ValueError("status must be int32")
+    _call("sparda_append_kv", _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_cmp), _ptr(seq_len),
+          _ptr(status), _dtype_code(k_new), B, Hkv, n_new, T_cap, W_cap, d, KERNEL, STRIDE, _stream(k_new, stream))
+
+
+def select_forecast(f, k_cmp, T: int, q_start: int, scale: float | None = None, out=None, stream=None, q_pos=None):
+    """Forecast block scores [B, Hkv, nTiles, nB] (float32) for F [B, Hkv, Tq, 128].
+    q_pos (int32 device [B], decode only) gives each sequence its own position."""
     torch = _torch()
     B, Hkv, Tq, d = f.shape
     scale = d ** -0.5 if scale is None else scale
     n_tiles = -(-Tq // TILE)
     if out is None:
         out = torch.empty((B, Hkv, n_tiles, T // BLOCK), dtype=torch.float32, device=f.device)
-    _call("sparda_select_forecast", _ptr(f), _ptr(k_cmp), _ptr(out), _dtype_code(f), B, Hkv, Tq, q_start, T, d,
-          KERNEL, STRIDE, BLOCK, TILE, scale, None, 0, _stream(f, stream))
+    _call("sparda_select_forecast", _ptr(f), _ptr(k_cmp), _ptr(out), _dtype_code(f), B, Hkv, Tq, q_start,
+          _positions(q_pos, B), T, d, KERNEL, STRIDE, BLOCK, TILE, scale, None, 0, _stream(f, stream))
     return out
 
 
 def select_multihead(q, k_cmp, T: int, q_start: int, scale: float | None = None, out=None, ws=None,
-                     stream=None):
+                     stream=None, q_pos=None):
     """Multi-head-selector block scores [B, Hkv, nTiles, nB] (float32) for Q [B, Hq, Tq, 128]."""
     torch = _torch()
     B, Hq, Tq, d = q.shape
@@ -179,8 +215,8 @@ def select_multihead(q, k_cmp, T: int, q_start: int, scale: float | None = None,
     if out is None:
         out = torch.empty((B, Hkv, n_tiles, T // BLOCK), dtype=torch.float32, device=q.device)
     ws, nbytes = _workspace(ws, workspace_bytes(OP_SELECT_MULTIHEAD, B, Hq, Hkv, Tq, T), q)
-    _call("sparda_select_multihead", _ptr(q), _ptr(k_cmp), _ptr(out), _dtype_code(q), B, Hq, Hkv, Tq, q_start, T,
-          d, KERNEL, STRIDE, BLOCK, TILE, scale, _ptr(ws), nbytes, _stream(q, stream))
+    _call("sparda_select_multihead", _ptr(q), _ptr(k_cmp), _ptr(out), _dtype_code(q), B, Hq, Hkv, Tq, q_start,
+          _positions(q_pos, B), T, d, KERNEL, STRIDE, BLOCK, TILE, scale, _ptr(ws), nbytes, _stream(q, stream))
     return out
 
 
@@ -196,7 +232,7 @@ def topk_blocks(scores, k: int, out=None, stream=None):
 
 
 def block_sparse_attn(q, k, v, idx, T: int, q_start: int, scale: float | None = None, kv_mode: int = KV_CACHE,
-                      out=None, ws=None, stream=None):
+                      out=None, ws=None, stream=None, q_pos=None):
     """GQA block-sparse attention; O [B, Hq, Tq, 128] in q's dtype."""
     torch = _torch()
     B, Hq, Tq, d = q.shape
@@ -207,7 +243,8 @@ def block_sparse_attn(q, k, v, idx, T: int, q_start: int, scale: float | None = 
         out = torch.empty_like(q)
     ws, nbytes = _workspace(ws, workspace_bytes(OP_BLOCK_SPARSE_ATTN, B, Hq, Hkv, Tq, T, k_sel), q)
     _call("sparda_block_sparse_attn", _ptr(q), _ptr(k), _ptr(v), kv_mode, _ptr(idx), _ptr(out), _dtype_code(q), B,
-          Hq, Hkv, Tq, q_start, T, d, BLOCK, TILE, k_sel, scale, _ptr(ws), nbytes, _stream(q, stream))
+          Hq, Hkv, Tq, q_start, _positions(q_pos, B), T, d, BLOCK, TILE, k_sel, scale, _ptr(ws), nbytes,
+          _stream(q, stream))
     return out
 
 

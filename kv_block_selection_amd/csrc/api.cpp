@@ -83,6 +83,13 @@ int check_select_params(int kernel, int stride, int block, int tile, float scale
   return SPARDA_OK;
 }
 
+int check_q_pos(const int* q_pos, int Tq) {
+  if (q_pos == nullptr) return SPARDA_OK;
+  CHECK(Tq == 1, SPARDA_ERR_UNSUPPORTED, "per-sequence positions (q_pos) need Tq = 1, got Tq = %d", Tq);
+  CHECK(((uintptr_t)q_pos & 3u) == 0, SPARDA_ERR_INVALID_ARG, "q_pos is not 4-byte aligned");
+  return SPARDA_OK;
+}
+
 sparda::SelectDims select_dims(int B, int Hq, int Hkv, int Tq, int q_start, int T, float scale) {
   sparda::SelectDims s;
   s.B = B;
@@ -92,6 +99,7 @@ sparda::SelectDims select_dims(int B, int Hq, int Hkv, int Tq, int q_start, int 
   s.q_start = q_start;
   s.T = T;
   s.W = (T - sparda::kKernel) / sparda::kStride + 1;
+  s.q_pos = nullptr;
   s.nB = T / sparda::kBlock;
   s.n_tiles = (Tq + sparda::kTile - 1) / sparda::kTile;
   s.scale = scale;
@@ -107,6 +115,7 @@ sparda::AttnDims attn_dims(int B, int Hq, int Hkv, int Tq, int q_start, int T, i
   a.Tq = Tq;
   a.q_start = q_start;
   a.T = T;
+  a.q_pos = nullptr;
   a.nB = T / sparda::kBlock;
   a.n_tiles = (Tq + sparda::kTile - 1) / sparda::kTile;
   a.k = k;
@@ -192,9 +201,37 @@ SPARDA_EXPORT int sparda_compress_windows(const void* k, void* k_cmp, int dtype,
                     "compress_windows launch");
 }
 
+SPARDA_EXPORT int sparda_append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache, void* k_cmp,
+                                   const int* seq_len, int* status, int dtype, int B, int Hkv, int n_new, int T_cap,
+                                   int W_cap, int d, int kernel, int stride, void* stream) {
+  if (int e = check_dtype(dtype)) return e;
+  CHECK(B >= 0 && Hkv >= 1, SPARDA_ERR_INVALID_ARG, "B %d / Hkv %d out of range", B, Hkv);
+  CHECK(d == sparda::kHeadDim, SPARDA_ERR_UNSUPPORTED, "head dim %d != 128", d);
+  CHECK(kernel == sparda::kKernel && stride == sparda::kStride, SPARDA_ERR_UNSUPPORTED,
+        "compression kernel/stride %d/%d != 32/16", kernel, stride);
+  CHECK(T_cap >= 1, SPARDA_ERR_INVALID_ARG, "T_cap = %d < 1", T_cap);
+  CHECK(n_new >= 0 && n_new <= T_cap, SPARDA_ERR_INVALID_ARG, "n_new = %d outside 0..T_cap (%d)", n_new, T_cap);
+  CHECK(k_cmp == nullptr || W_cap >= 1, SPARDA_ERR_INVALID_ARG, "W_cap = %d < 1 with k_cmp given", W_cap);
+  CHECK((long)B * Hkv <= 2147483647L, SPARDA_ERR_UNSUPPORTED, "B*Hkv too large");
+  CHECK(sparda::append_grid_y(dtype == SPARDA_BF16, n_new, k_cmp != nullptr) <= 65535, SPARDA_ERR_UNSUPPORTED,
+        "n_new = %d too large for one call", n_new);
+  if (B == 0 || n_new == 0) return ok();
+  CHECK_PTR(k_new);
+  CHECK_PTR(v_new);
+  CHECK_PTR(k_cache);
+  CHECK_PTR(v_cache);
+  if (k_cmp != nullptr) CHECK_PTR(k_cmp);
+  CHECK(seq_len != nullptr && ((uintptr_t)seq_len & 3u) == 0, SPARDA_ERR_INVALID_ARG,
+        "seq_len is NULL or not 4-byte aligned");
+  CHECK(((uintptr_t)status & 3u) == 0, SPARDA_ERR_INVALID_ARG, "status is not 4-byte aligned");
+  return hip_status(sparda::launch_append_kv(k_new, v_new, k_cache, v_cache, k_cmp, seq_len, status,
+                                             dtype == SPARDA_BF16, B, Hkv, n_new, T_cap, W_cap, (hipStream_t)stream),
+                    "append_kv launch");
+}
+
 SPARDA_EXPORT int sparda_select_forecast(const void* f, const void* k_cmp, float* blk_scores, int dtype, int B,
-                                         int Hkv, int Tq, int q_start, int T, int d, int kernel, int stride,
-                                         int block, int tile, float scale, void* ws, size_t ws_bytes,
+                                         int Hkv, int Tq, int q_start, const int* q_pos, int T, int d, int kernel,
+                                         int stride, int block, int tile, float scale, void* ws, size_t ws_bytes,
                                          void* stream) {
   (void)ws;
   (void)ws_bytes;
@@ -205,7 +242,9 @@ SPARDA_EXPORT int sparda_select_forecast(const void* f, const void* k_cmp, float
   CHECK_PTR(f);
   CHECK_PTR(k_cmp);
   CHECK_PTR(blk_scores);
-  const sparda::SelectDims sd = select_dims(B, Hkv, Hkv, Tq, q_start, T, scale);
+  if (int e = check_q_pos(q_pos, Tq)) return e;
+  sparda::SelectDims sd = select_dims(B, Hkv, Hkv, Tq, q_start, T, scale);
+  sd.q_pos = q_pos;
   if (Tq != 1) {
     CHECK(dtype == SPARDA_BF16, SPARDA_ERR_UNSUPPORTED, "select_forecast: a query chunk (Tq > 1) needs bf16 inputs");
     CHECK((long)B * Hkv <= 2147483647L && sd.n_tiles <= 65535, SPARDA_ERR_UNSUPPORTED, "grid too large");
@@ -218,8 +257,8 @@ SPARDA_EXPORT int sparda_select_forecast(const void* f, const void* k_cmp, float
 }
 
 SPARDA_EXPORT int sparda_select_multihead(const void* q, const void* k_cmp, float* blk_scores, int dtype, int B,
-                                          int Hq, int Hkv, int Tq, int q_start, int T, int d, int kernel,
-                                          int stride, int block, int tile, float scale, void* ws,
+                                          int Hq, int Hkv, int Tq, int q_start, const int* q_pos, int T, int d,
+                                          int kernel, int stride, int block, int tile, float scale, void* ws,
                                           size_t ws_bytes, void* stream) {
   if (int e = check_dtype(dtype)) return e;
   if (int e = check_geometry(B, Hq, Hkv, Tq, q_start, T, d)) return e;
@@ -231,7 +270,9 @@ SPARDA_EXPORT int sparda_select_multihead(const void* q, const void* k_cmp, floa
   const size_t need = ws_bytes_for(SPARDA_OP_SELECT_MULTIHEAD, B, Hq, Hkv, Tq, T, 0);
   CHECK(ws_bytes >= need, SPARDA_ERR_WORKSPACE, "select_multihead needs %zu workspace bytes, got %zu", need, ws_bytes);
   if (need) CHECK_PTR(ws);
-  const sparda::SelectDims sd = select_dims(B, Hq, Hkv, Tq, q_start, T, scale);
+  if (int e = check_q_pos(q_pos, Tq)) return e;
+  sparda::SelectDims sd = select_dims(B, Hq, Hkv, Tq, q_start, T, scale);
+  sd.q_pos = q_pos;
   if (Tq != 1) {
     CHECK(dtype == SPARDA_BF16, SPARDA_ERR_UNSUPPORTED, "select_multihead: a query chunk (Tq > 1) needs bf16 inputs");
     CHECK(sd.n_tiles <= 65535, SPARDA_ERR_UNSUPPORTED, "grid too large");
@@ -257,8 +298,8 @@ SPARDA_EXPORT int sparda_topk_blocks(const float* blk_scores, int32_t* idx, int 
 
 SPARDA_EXPORT int sparda_block_sparse_attn(const void* q, const void* k, const void* v, int kv_mode,
                                            const int32_t* idx, void* out, int dtype, int B, int Hq, int Hkv,
-                                           int Tq, int q_start, int T, int d, int block, int tile, int k_sel,
-                                           float scale, void* ws, size_t ws_bytes, void* stream) {
+                                           int Tq, int q_start, const int* q_pos, int T, int d, int block, int tile,
+                                           int k_sel, float scale, void* ws, size_t ws_bytes, void* stream) {
   if (int e = check_dtype(dtype)) return e;
   if (int e = check_geometry(B, Hq, Hkv, Tq, q_start, T, d)) return e;
   CHECK(block == sparda::kBlock, SPARDA_ERR_UNSUPPORTED, "block %d != 64", block);
@@ -278,7 +319,9 @@ SPARDA_EXPORT int sparda_block_sparse_attn(const void* q, const void* k, const v
   CHECK(ws_bytes >= need, SPARDA_ERR_WORKSPACE, "block_sparse_attn needs %zu workspace bytes, got %zu", need,
         ws_bytes);
   if (need) CHECK_PTR(ws);
-  const sparda::AttnDims ad = attn_dims(B, Hq, Hkv, Tq, q_start, T, k_sel, scale, kv_mode);
+  if (int e = check_q_pos(q_pos, Tq)) return e;
+  sparda::AttnDims ad = attn_dims(B, Hq, Hkv, Tq, q_start, T, k_sel, scale, kv_mode);
+  ad.q_pos = q_pos;
   if (Tq != 1) {
     CHECK(dtype == SPARDA_BF16, SPARDA_ERR_UNSUPPORTED, "block_sparse_attn: a query chunk (Tq > 1) needs bf16 inputs");
     CHECK(ad.n_tiles <= 65535, SPARDA_ERR_UNSUPPORTED, "too many query tiles");

@@ -86,8 +86,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SPARDA_ATTN_
 void attn_decode_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ kbuf, const uint8_t* __restrict__ vbuf,
     const int32_t* __restrict__ idx, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    uint8_t* __restrict__ out, int T, int nB, int k, int kv_mode, int p, int bps, int splits,
-    float scale) {
+    uint8_t* __restrict__ out, int T, int nB, int k, int kv_mode, int p_all, const int* __restrict__ q_pos,
+    int hkv, int bps, int splits, float scale) {
   constexpr int E = DT<Tag>::kElems;
   constexpr int LPK = kHeadDim / E;  // lanes per key row
   constexpr int KPI = kWave / LPK;   // keys per load instruction
@@ -101,6 +101,7 @@ void attn_decode_kernel(
 
   const long row = blockIdx.x;  // rows on the fast axis: a row's splits share an XCD
   const int split = blockIdx.y;
+  const int p = row_position(q_pos, row, hkv, p_all, T);  // the row's query position
   const int lane = threadIdx.x;
   const int c = lane % LPK;
   const int r = lane / LPK;
@@ -434,7 +435,7 @@ static void launch_attn_g(const void* q, const void* k, const void* v, const int
   }
   hipLaunchKernelGGL((attn_decode_kernel<Tag, G>), dim3(rows, splits), dim3(kWave), 0, s,
                      (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, part_o, part_ml,
-                     (uint8_t*)out, d.T, d.nB, d.k, d.kv_mode, d.q_start, bps, splits, d.scale);
+                     (uint8_t*)out, d.T, d.nB, d.k, d.kv_mode, d.q_start, d.q_pos, d.Hkv, bps, splits, d.scale);
   if (splits > 1 && SPARDA_COMBINE_ROW && G * (kHeadDim / 4) <= 256) {
     if (splits <= 16)
       hipLaunchKernelGGL((attn_combine_row_kernel<Tag, 16>), dim3(rows), dim3(G * (kHeadDim / 4)), 0, s, part_o,

@@ -16,6 +16,20 @@ constexpr int kWave = 64;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// Number of compressed windows visible to the query at position p: window w
+// is visible iff every token of it is at or before p, i.e. 16 w + 31 <= p.
+__device__ __forceinline__ int visible_windows(int p, int W) {
+  return p >= kKernel - 1 ? min(W, (p - kKernel + 1) / kStride + 1) : 0;
+}
+
+// Query position of the (sequence, KV head) row `row` of a decode call: the
+// sequence's own entry of q_pos when given (clamped to [-1, T - 1]; -1 leaves
+// nothing visible), else the shared position p.
+__device__ __forceinline__ int row_position(const int* q_pos, long row, int hkv, int p, int T) {
+  if (q_pos == nullptr) return p;
+  return min(max(q_pos[row / hkv], -1), T - 1);
+}
+
 struct F32Tag {};
 struct BF16Tag {};
 

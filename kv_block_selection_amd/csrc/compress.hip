@@ -12,6 +12,7 @@
 // 1 KiB contiguous per row group, fully used.
 #include "common.h"
 #include "launch.h"
+#include "window_mean.h"
 
 namespace sparda {
 
@@ -37,31 +38,16 @@ __global__ __launch_bounds__(256) void compress_kernel(const uint8_t* __restrict
 
   // half-window h covers tokens [16h, 16h+16)
   auto half_sum = [&](int h, float* acc) {
-    u32x4 v[kStride];
-#pragma unroll
-    for (int t = 0; t < kStride; ++t) v[t] = load16_nt(src + (long)(h * kStride + t) * RB);
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
-#pragma unroll
-    for (int t = 0; t < kStride; ++t) {
-      float x[E];
-      unpack<Tag>(v[t], x);
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += x[e];
-    }
+    half_window_sum<Tag>([&](int t) { return src + (long)(h * kStride + t) * RB; }, acc);
   };
 
   float prev[E], next[E];
   half_sum(w0, prev);
   for (int w = w0; w < w1; ++w) {
     half_sum(w + 1, next);
-    float m[E];
+    store16(dst + (long)w * RB, window_from_halves<Tag>(prev, next));
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      m[e] = (prev[e] + next[e]) * (1.0f / kKernel);
-      prev[e] = next[e];
-    }
-    store16(dst + (long)w * RB, pack<Tag>(m));
+    for (int e = 0; e < E; ++e) prev[e] = next[e];
   }
 }
 

@@ -18,17 +18,27 @@ constexpr int kTile = 64;
 struct SelectDims {
   int B, Hq, Hkv, Tq, q_start, T, W, nB, n_tiles;
   float scale;
+  const int* q_pos;  // decode only: per-sequence query positions [B], or NULL
 };
 
 struct AttnDims {
   int B, Hq, Hkv, Tq, q_start, T, nB, n_tiles, k;
   float scale;
   int kv_mode;
+  const int* q_pos;  // decode only: per-sequence query positions [B], or NULL
 };
 
 // compress.hip: windows [w_begin, w_end) of rows holding T tokens and W windows
 hipError_t launch_compress(const void* k, void* kc, bool bf16, int rows, int T, int W, int w_begin, int w_end,
                            hipStream_t s);
+
+// append.hip: write n_new tokens per row at the sequence's length and
+// compress the windows they complete (k_cmp may be NULL)
+hipError_t launch_append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache, void* k_cmp,
+                            const int* seq_len, int* status, bool bf16, int B, int Hkv, int n_new, int T_cap,
+                            int W_cap, hipStream_t s);
+
+int append_grid_y(bool bf16, int n_new, bool with_windows);  // workgroups per row
 
 // select_decode.hip
 hipError_t launch_select_forecast_decode(const void* f, const void* kc, float* scores, bool bf16,

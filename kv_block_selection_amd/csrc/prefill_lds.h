@@ -49,10 +49,4 @@ __device__ __forceinline__ u32x4 chunk_frag(const uint8_t* chunk, int r, int s, 
   return *reinterpret_cast<const u32x4*>(chunk + swz(r, 2 * s + half));
 }
 
-// Number of compressed windows visible to the query at position p: window w
-// is visible iff every token of it is at or before p, i.e. 16 w + 31 <= p.
-__device__ __forceinline__ int visible_windows(int p, int W) {
-  return p >= kKernel - 1 ? min(W, (p - kKernel + 1) / kStride + 1) : 0;
-}
-
 }  // namespace sparda

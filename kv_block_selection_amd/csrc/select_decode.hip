@@ -42,13 +42,15 @@ template <typename Tag>
 __global__ __launch_bounds__(256) void fsel_decode_kernel(const uint8_t* __restrict__ f,
                                                           const uint8_t* __restrict__ kc,
                                                           float* __restrict__ scores, int W, int nB,
-                                                          int n_vis, float scale) {
+                                                          int n_vis, const int* __restrict__ q_pos, int hkv,
+                                                          int T, float scale) {
   using R = RowGeom<Tag>;
   constexpr int NWIN = 4 * kFselBlocks + 1;
   constexpr int ITER = (NWIN + R::SLOTS - 1) / R::SLOTS;
   __shared__ float s_win[ITER * R::SLOTS];
 
   const long row = blockIdx.x;  // rows on the fast axis: a row's chunks share an XCD
+  if (q_pos != nullptr) n_vis = visible_windows(row_position(q_pos, row, hkv, 0, T), W);
   const int beta0 = blockIdx.y * kFselBlocks;
   const int nblk = min(kFselBlocks, nB - beta0);
   const int nwin = 4 * nblk + 1;
@@ -91,10 +93,10 @@ hipError_t launch_select_forecast_decode(const void* f, const void* kc, float* s
   dim3 grid(d.B * d.Hkv, (d.nB + kFselBlocks - 1) / kFselBlocks);
   if (bf16)
     hipLaunchKernelGGL(fsel_decode_kernel<BF16Tag>, grid, dim3(256), 0, s, (const uint8_t*)f,
-                       (const uint8_t*)kc, scores, d.W, d.nB, n_vis, d.scale);
+                       (const uint8_t*)kc, scores, d.W, d.nB, n_vis, d.q_pos, d.Hkv, d.T, d.scale);
   else
     hipLaunchKernelGGL(fsel_decode_kernel<F32Tag>, grid, dim3(256), 0, s, (const uint8_t*)f,
-                       (const uint8_t*)kc, scores, d.W, d.nB, n_vis, d.scale);
+                       (const uint8_t*)kc, scores, d.W, d.nB, n_vis, d.q_pos, d.Hkv, d.T, d.scale);
   return hipGetLastError();
 }
 
@@ -146,13 +148,15 @@ __device__ __forceinline__ float block_reduce_sum(float v, float* red) {
 template <typename Tag, int G>
 __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __restrict__ q,
                                                            const uint8_t* __restrict__ kc, MhWs ws,
-                                                           int W, int n_vis, int chunks, float scale) {
+                                                           int W, int n_vis, const int* __restrict__ q_pos,
+                                                           int hkv, int T, int chunks, float scale) {
   using R = RowGeom<Tag>;
   constexpr int ITER = kMhChunk / R::SLOTS;
   __shared__ float s_log[G][kMhChunk];
   __shared__ float red[4];
 
   const long row = blockIdx.y;  // (b, kv head)
+  if (q_pos != nullptr) n_vis = visible_windows(row_position(q_pos, row, hkv, 0, T), W);
   const int chunk = blockIdx.x;
   const int w0 = chunk * kMhChunk;
   const int lane = threadIdx.x % R::LPR;
@@ -195,11 +199,14 @@ __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __rest
 
 template <typename Tag, int G>
 __global__ __launch_bounds__(256) void mhsel_pool_kernel(MhWs ws, float* __restrict__ scores,
-                                                         int W, int nB, int n_vis, int chunks) {
+                                                         int W, int nB, int n_vis,
+                                                         const int* __restrict__ q_pos, int hkv, int T,
+                                                         int chunks) {
   constexpr int NWIN = 4 * kMhPoolBlocks + 1;
   __shared__ float s_sum[NWIN];
   __shared__ float s_m[G], s_iz[G];
   const long row = blockIdx.y;
+  if (q_pos != nullptr) n_vis = visible_windows(row_position(q_pos, row, hkv, 0, T), W);
   const int beta0 = blockIdx.x * kMhPoolBlocks;
   const int nblk = min(kMhPoolBlocks, nB - beta0);
   const int nwin = 4 * nblk + 1;
@@ -253,10 +260,10 @@ static void launch_mh(const void* q, const void* kc, float* scores, const Select
   const int chunks = (d.W + kMhChunk - 1) / kMhChunk;
   const int rows = d.B * d.Hkv;
   hipLaunchKernelGGL((mhsel_logits_kernel<Tag, G>), dim3(chunks, rows), dim3(256), 0, s,
-                     (const uint8_t*)q, (const uint8_t*)kc, w, d.W, n_vis, chunks, d.scale);
+                     (const uint8_t*)q, (const uint8_t*)kc, w, d.W, n_vis, d.q_pos, d.Hkv, d.T, chunks, d.scale);
   hipLaunchKernelGGL((mhsel_pool_kernel<Tag, G>),
                      dim3((d.nB + kMhPoolBlocks - 1) / kMhPoolBlocks, rows), dim3(256), 0, s, w,
-                     scores, d.W, d.nB, n_vis, chunks);
+                     scores, d.W, d.nB, n_vis, d.q_pos, d.Hkv, d.T, chunks);
 }
 
 hipError_t launch_select_multihead_decode(const void* q, const void* kc, float* scores, bool bf16,

@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in kbs.SIGNATURES, f"binding lacks {n}"
@@ -44,12 +44,12 @@ P = 1 << 20  # a 16-byte-aligned dummy address; never dereferenced (validation f
 
 
 def _sel(lib, **kw):
-    a = dict(f=P, kc=P, s=P, dtype=1, B=1, Hkv=8, Tq=1, q_start=4095, T=4096, d=128, kernel=32, stride=16, block=64,
-             tile=64, scale=0.088)
+    a = dict(f=P, kc=P, s=P, dtype=1, B=1, Hkv=8, Tq=1, q_start=4095, q_pos=None, T=4096, d=128, kernel=32,
+             stride=16, block=64, tile=64, scale=0.088)
     a.update(kw)
     return lib.sparda_select_forecast(a["f"], a["kc"], a["s"], a["dtype"], a["B"], a["Hkv"], a["Tq"], a["q_start"],
-                                      a["T"], a["d"], a["kernel"], a["stride"], a["block"], a["tile"], a["scale"],
-                                      None, 0, None)
+                                      a["q_pos"], a["T"], a["d"], a["kernel"], a["stride"], a["block"], a["tile"],
+                                      a["scale"], None, 0, None)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -64,6 +64,8 @@ def _sel(lib, **kw):
     (dict(f=0), 1, b"f is NULL"),
     (dict(kc=P + 4), 1, b"aligned"),
     (dict(scale=float("inf")), 1, b"scale"),
+    (dict(Tq=64, q_start=0, q_pos=P), 2, b"q_pos"),
+    (dict(q_pos=P + 2), 1, b"q_pos is not 4-byte aligned"),
 ])
 def test_select_forecast_validation(lib, kw, status, needle):
     assert _sel(lib, **kw) == status
@@ -78,22 +80,29 @@ def test_validation_messages_are_thread_local_and_cleared(lib):
 
 
 def test_multihead_and_attention_validation(lib):
-    st = lib.sparda_select_multihead(P, P, P, 1, 1, 12, 8, 1, 4095, 4096, 128, 32, 16, 64, 64, 0.1, None, 0, None)
+    st = lib.sparda_select_multihead(P, P, P, 1, 1, 12, 8, 1, 4095, None, 4096, 128, 32, 16, 64, 64, 0.1, None, 0,
+                                     None)
     assert st == 1 and b"multiple" in lib.sparda_last_error()
-    st = lib.sparda_select_multihead(P, P, P, 1, 1, 48, 8, 1, 4095, 4096, 128, 32, 16, 64, 64, 0.1, None, 0, None)
+    st = lib.sparda_select_multihead(P, P, P, 1, 1, 48, 8, 1, 4095, None, 4096, 128, 32, 16, 64, 64, 0.1, None, 0,
+                                     None)
     assert st == 2 and b"group" in lib.sparda_last_error()
     need = lib.sparda_workspace_bytes(kbs.OP_SELECT_MULTIHEAD, 1, 32, 8, 1, 4096, 128, 0)
     assert need > 0
-    st = lib.sparda_select_multihead(P, P, P, 1, 1, 32, 8, 1, 4095, 4096, 128, 32, 16, 64, 64, 0.1, P, need - 1, None)
+    st = lib.sparda_select_multihead(P, P, P, 1, 1, 32, 8, 1, 4095, None, 4096, 128, 32, 16, 64, 64, 0.1, P,
+                                     need - 1, None)
     assert st == 3 and b"workspace" in lib.sparda_last_error()
+    st = lib.sparda_select_multihead(P, P, P, 1, 1, 32, 8, 64, 0, P, 4096, 128, 32, 16, 64, 64, 0.1, P, 1 << 30,
+                                     None)
+    assert st == 2 and b"q_pos" in lib.sparda_last_error()
     # attention: k out of range, bad kv_mode, staging with a prefill chunk
     a = lambda **kw: lib.sparda_block_sparse_attn(
-        P, P, P, kw.get("mode", 0), P, P, 1, 1, 32, 8, kw.get("Tq", 1), 4096 - kw.get("Tq", 1), 4096, 128, 64, 64,
-        kw.get("k", 64), 0.1, P, 1 << 30, None)
+        P, P, P, kw.get("mode", 0), P, P, 1, 1, 32, 8, kw.get("Tq", 1), 4096 - kw.get("Tq", 1), kw.get("q_pos"),
+        4096, 128, 64, 64, kw.get("k", 64), 0.1, P, 1 << 30, None)
     assert a(k=0) == 1 and b"k = 0" in lib.sparda_last_error()
     assert a(k=65) == 1
     assert a(mode=2) == 1 and b"kv_mode" in lib.sparda_last_error()
     assert a(mode=1, Tq=64) == 2 and b"staging" in lib.sparda_last_error()
+    assert a(Tq=64, q_pos=P) == 2 and b"q_pos" in lib.sparda_last_error()
 
 
 def test_topk_and_prefetch_validation(lib):
@@ -141,3 +150,40 @@ def test_compress_windows_validation(lib, args, status, needle):
 
 def test_compress_windows_empty_range_is_a_no_op(lib):
     assert lib.sparda_compress_windows(P, P, 1, 2, 8, 4096, 255, 128, 32, 16, 7, 7, None) == 0
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(dtype=5), 1, b"dtype"),
+    (dict(d=256), 2, b"head dim"),
+    (dict(stride=32), 2, b"kernel/stride"),
+    (dict(n_new=-1), 1, b"n_new"),
+    (dict(n_new=5000), 1, b"n_new"),
+    (dict(T_cap=0), 1, b"T_cap"),
+    (dict(W_cap=0), 1, b"W_cap"),
+    (dict(kn=0), 1, b"k_new is NULL"),
+    (dict(vc=P + 8), 1, b"v_cache is not 16-byte aligned"),
+    (dict(kc=P + 4), 1, b"k_cmp is not 16-byte aligned"),
+    (dict(seq=0), 1, b"seq_len"),
+    (dict(status=P + 2), 1, b"status"),
+    (dict(B=-1), 1, b"B -1"),
+])
+def test_append_kv_validation(lib, args, status, needle):
+    a = dict(kn=P, vn=P, kcache=P, vc=P, kc=P, seq=P, status=None, dtype=1, B=2, Hkv=8, n_new=1, T_cap=4096,
+             W_cap=255, d=128, kernel=32, stride=16)
+    a.update(args)
+    st = lib.sparda_append_kv(a["kn"], a["vn"], a["kcache"], a["vc"], a["kc"], a["seq"], a["status"], a["dtype"],
+                              a["B"], a["Hkv"], a["n_new"], a["T_cap"], a["W_cap"], a["d"], a["kernel"],
+                              a["stride"], None)
+    assert st == status
+    assert needle in lib.sparda_last_error()
+
+
+def test_append_kv_empty_is_a_noop(lib):
+    # no tokens, or no sequences: nothing is launched and no pointer is read
+    assert lib.sparda_append_kv(None, None, None, None, None, None, None, 1, 2, 8, 0, 4096, 255, 128, 32, 16,
+                                None) == 0
+    assert lib.sparda_append_kv(None, None, None, None, None, None, None, 1, 0, 8, 1, 4096, 255, 128, 32, 16,
+                                None) == 0
+    # no compressed keys: W_cap is not used
+    assert lib.sparda_append_kv(None, None, None, None, None, None, None, 1, 0, 8, 1, 4096, 0, 128, 32, 16,
+                                None) == 0

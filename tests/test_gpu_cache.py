@@ -37,6 +37,11 @@ def bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
 
 
+def raw(t):
+    """Integer view of the bits (equal NaNs compare equal)."""
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
 def spoil_after(t, pos):
     """Overwrite cache rows at token positions > pos with GARBAGE (a copy)."""
     t = t.clone()
@@ -174,3 +179,142 @@ def test_decode_loop_growing_cache(gpu):
     full = gpu.compress_keys(K_true)
     torch.cuda.synchronize()
     assert torch.equal(bits(Kc[:, :, :compressed]), bits(full[:, :, :compressed]))
+
+
+# ------------------------------------------------ append, ragged sequences ---
+def _gather_new(K_true, L, n):
+    """The n tokens of each sequence b starting at L[b]: [B, Hkv, n, d]."""
+    return torch.stack([K_true[b, :, L[b]:L[b] + n] for b in range(len(L))]).contiguous()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("n_new,lens", [(1, [31, 100, 767, 0]), (16, [0, 15, 752, 17]), (37, [0, 47, 731, 300])])
+def test_append_kv_tokens_and_windows(gpu, dtype, n_new, lens):
+    """Each sequence's n_new tokens land at its own length; every window they
+    complete equals the full compression bit for bit; nothing else changes.
+    Cache slots at or after a sequence's length hold NaN before the call, so a
+    window that read one would be NaN."""
+    w = cache_workload(dtype, T=64 * 12, B=4, Hkv=2, seed=91)
+    T_cap, W_cap = w.T, w.W
+    say("append", dtype, "n_new", n_new, "lengths", lens)
+    K_true, V_true = gen(w, "K"), gen(w, "V")
+    K, V = K_true.clone(), V_true.clone()
+    for b, L in enumerate(lens):
+        K[b, :, L:] = float("nan")
+        V[b, :, L:] = float("nan")
+    Kc = torch.full((w.B, w.Hkv, W_cap, w.d), -3.0, dtype=K.dtype, device=DEV)
+    K0, V0, Kc0 = K.clone(), V.clone(), Kc.clone()
+    seq_len = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gpu.append_kv(_gather_new(K_true, lens, n_new), _gather_new(V_true, lens, n_new), K, V, seq_len, k_cmp=Kc,
+                  status=status)
+    full = gpu.compress_keys(K_true)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    expK, expV, expKc = K0.clone(), V0.clone(), Kc0.clone()
+    for b, L in enumerate(lens):
+        expK[b, :, L:L + n_new] = K_true[b, :, L:L + n_new]
+        expV[b, :, L:L + n_new] = V_true[b, :, L:L + n_new]
+        done = [x for x in range(W_cap) if L <= 16 * x + 31 <= L + n_new - 1]
+        for x in done:
+            expKc[b, :, x] = full[b, :, x]
+    # bitwise, NaN slots included
+    assert torch.equal(raw(K), raw(expK))
+    assert torch.equal(raw(V), raw(expV))
+    assert torch.equal(raw(Kc), raw(expKc))
+
+
+def test_append_kv_overflow_leaves_sequence_untouched(gpu):
+    w = cache_workload("bf16", T=64 * 4, B=3, Hkv=2, seed=92)
+    K, V = gen(w, "K"), gen(w, "V")
+    Kc = gpu.compress_keys(K)
+    K0, V0, Kc0 = K.clone(), V.clone(), Kc.clone()
+    n_new = 8
+    kn = torch.ones((w.B, w.Hkv, n_new, w.d), dtype=K.dtype, device=DEV)
+    lens = [w.T - n_new, w.T - n_new + 1, -1]  # fits exactly; one token too many; negative
+    seq_len = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gpu.append_kv(kn, kn, K, V, seq_len, k_cmp=Kc, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1
+    assert torch.equal(bits(K[0, :, -n_new:]), bits(kn[0])) and torch.equal(bits(K[0, :, :-n_new]), bits(K0[0, :, :-n_new]))
+    for b in (1, 2):
+        assert torch.equal(bits(K[b]), bits(K0[b])) and torch.equal(bits(V[b]), bits(V0[b]))
+        assert torch.equal(bits(Kc[b]), bits(Kc0[b]))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_ragged_decode_loop(gpu, dtype):
+    """Sequences of different lengths in one batch: each step appends one token
+    per sequence (append_kv, which also compresses completed windows), then
+    selects, takes the top-k and attends at each sequence's own position
+    (q_pos). Checked against the oracle run sequence by sequence."""
+    w = cache_workload(dtype, T=64 * 24, B=4, Hkv=2, Hq=8, k=6, seed=93)
+    lens0 = [40, 333, 700, 1300]
+    steps = 24
+    K_true, V_true = gen(w, "K"), gen(w, "V")
+    Q_all = sg.tensor(wl.scaled(w, seed=94).recipe("Q"), (w.B, w.Hq, steps, w.d), DEV)
+    F_all = sg.tensor(wl.scaled(w, seed=94).recipe("F"), (w.B, w.Hkv, steps, w.d), DEV)
+    K = torch.full_like(K_true, GARBAGE)
+    V = torch.full_like(V_true, GARBAGE)
+    Kc = torch.full((w.B, w.Hkv, w.W, w.d), GARBAGE, dtype=K.dtype, device=DEV)
+    # prefill: every sequence's first lens0[b] tokens, through append_kv as well
+    for b, L in enumerate(lens0):
+        one = torch.tensor([0], dtype=torch.int32, device=DEV)
+        gpu.append_kv(K_true[b:b + 1, :, :L].contiguous(), V_true[b:b + 1, :, :L].contiguous(), K[b:b + 1], V[b:b + 1],
+                      one, k_cmp=Kc[b:b + 1])
+    seq_len = torch.tensor(lens0, dtype=torch.int32, device=DEV)
+    k64, v64 = parity.to_f64(K_true), parity.to_f64(V_true)
+    kc64_true = oracle.compress_keys(k64)
+    tol = parity.ATTN_ATOL_BF16 if dtype == "bf16" else 1e-4
+    for i in range(steps):
+        lens = [lens0[b] + i for b in range(w.B)]
+        gpu.append_kv(_gather_new(K_true, lens, 1), _gather_new(V_true, lens, 1), K, V, seq_len, k_cmp=Kc)
+        q_pos = seq_len.clone()  # each query sits at its sequence's new token
+        Q, F = Q_all[:, :, i:i + 1].contiguous(), F_all[:, :, i:i + 1].contiguous()
+        s = gpu.select_forecast(F, Kc, w.T, 0, q_pos=q_pos)
+        sm = gpu.select_multihead(Q, Kc, w.T, 0, q_pos=q_pos)
+        idx = gpu.topk_blocks(s, w.k)
+        out = gpu.block_sparse_attn(Q, K, V, idx, w.T, 0, q_pos=q_pos)
+        seq_len += 1
+        if i % 5 == 0 or i == steps - 1:
+            torch.cuda.synchronize()
+            kc64 = parity.to_f64(Kc)
+            idx_np = idx.cpu().numpy()
+            F64, Q64, s64, sm64, o64 = (parity.to_f64(x) for x in (F, Q, s, sm, out))
+            for b, p in enumerate(lens):
+                sl = slice(b, b + 1)
+                ref_s = oracle.select_forecast(F64[sl], kc64[sl], w.T, p, w.scale)
+                parity.check_scores(s64[sl], ref_s)
+                parity.check_scores(s64[sl], oracle.select_forecast(F64[sl], kc64_true[sl], w.T, p, w.scale),
+                                    rtol=1e-2 if dtype == "bf16" else 1e-3)
+                parity.check_scores(sm64[sl], oracle.select_multihead(Q64[sl], kc64[sl], w.T, p, w.scale))
+                parity.check_topk_band(idx_np[sl], ref_s, w.k)
+                ref_o = oracle.block_sparse_attention(Q64[sl], k64[sl], v64[sl], idx_np[sl], p, w.scale)
+                parity.check_attention(o64[sl], ref_o, tol)
+            say(f"ragged step {i}: positions {lens}")
+    torch.cuda.synchronize()
+    full = gpu.compress_keys(K_true)
+    for b in range(w.B):
+        n = oracle.visible_window_count(lens0[b] + steps - 1, w.W)
+        assert torch.equal(bits(Kc[b, :, :n]), bits(full[b, :, :n]))
+
+
+def test_empty_sequence_position(gpu):
+    """q_pos = -1 marks a sequence with no tokens: no candidate block, top-k
+    all -1, attention output 0; its neighbours are unaffected."""
+    w = cache_workload("bf16", T=64 * 8, B=2, Hkv=2, Hq=8, k=4, seed=95)
+    Q, K, V, F = gen(w, "Q"), gen(w, "K"), gen(w, "V"), gen(w, "F")
+    Kc = gpu.compress_keys(K)
+    q_pos = torch.tensor([-1, 300], dtype=torch.int32, device=DEV)
+    s = gpu.select_forecast(F, Kc, w.T, 0, q_pos=q_pos)
+    idx = gpu.topk_blocks(s, w.k)
+    out = gpu.block_sparse_attn(Q, K, V, idx, w.T, 0, q_pos=q_pos)
+    torch.cuda.synchronize()
+    assert torch.isneginf(s[0]).all() and (idx[0] == -1).all() and not torch.any(out[0].float() != 0)
+    ref_s = oracle.select_forecast(parity.to_f64(F)[1:], parity.to_f64(Kc)[1:], w.T, 300, w.scale)
+    parity.check_scores(parity.to_f64(s)[1:], ref_s)
+    idx_np = idx.cpu().numpy()
+    ref_o = oracle.block_sparse_attention(parity.to_f64(Q)[1:], parity.to_f64(K)[1:], parity.to_f64(V)[1:],
+                                          idx_np[1:], 300, w.scale)
+    parity.check_attention(parity.to_f64(out)[1:], ref_o, parity.ATTN_ATOL_BF16)
