@@ -488,23 +488,6 @@ def bench_prefill(args) -> int:
         topk(i)
         attn(i)
 
-    # Decode-time state maintenance: append the step's token to K, V and
-    # compress the window it completes (every 16th step) or none. The tokens
-    # written are the ones already there, so the inputs stay as they are.
-    def append_win(i):
-        s = sets[i % N_SETS]
-        kbs.append_kv(s["Knew1"], s["Vnew1"], s["K"], s["V"], len_win, k_cmp=s["Kc"])
-
-    def append_nowin(i):
-        s = sets[i % N_SETS]
-        kbs.append_kv(s["Knew2"], s["Vnew2"], s["K"], s["V"], len_nowin, k_cmp=s["Kc"])
-
-    def step_q_pos(i):  # the same step with per-sequence positions (all at T - 1)
-        s = sets[i % N_SETS]
-        kbs.select_forecast(s["F"], s["Kc"], w.T, 0, out=s["scores"], q_pos=pos_last)
-        kbs.topk_blocks(s["scores"], w.k, out=s["idx"])
-        kbs.block_sparse_attn(s["Q"], s["K"], s["V"], s["idx"], w.T, 0, out=s["out"], ws=ws_attn, q_pos=pos_last)
-
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
