@@ -5,8 +5,10 @@
 //
 // Dense contractions per selected block, on the matrix cores
 // (v_mfma_f32_32x32x16_bf16). One workgroup owns one (sequence, KV head, query
-// tile); wave g computes head g of the GQA group for the tile's 64 queries, so
-// all G heads share every K/V block staged in LDS.
+// tile); each wave computes one head of the GQA group for 32 of the tile's 64
+// queries (two waves per head), so all G heads share every K/V block staged in
+// LDS, and a wave's registers (O^T accumulators, Q fragments, scores) fit two
+// waves per SIMD: one wave's softmax then runs beside another's MFMAs.
 //   S^T = K Q^T  (keys x queries): each lane owns one query column, so the
 //                online-softmax statistics of a query stay in one lane (plus
 //                its partner 32 lanes away);
@@ -18,8 +20,11 @@
 // matrix cores compute the scores of the next half while the vector ALUs run
 // the softmax of the current one, then its PV products. K and V blocks arrive
 // in LDS by direct global->LDS loads a block ahead (three K buffers, two V
-// buffers), rows granule-swizzled (16-byte granule g of row r sits at
-// g ^ (r & 15)). V^T fragments come straight from row-major V through the LDS
+// buffers; 80 KiB), rows granule-swizzled so that both fragment reads are free
+// of bank conflicts: 16-byte granule g of K row r sits at g ^ (r & 15) (a K
+// fragment read takes one granule of 16 consecutive rows), of V row r at
+// g ^ 4 (r & 3) (a transposed V read takes 4 consecutive granules of 4
+// consecutive rows). V^T fragments come straight from row-major V through the LDS
 // transpose read ds_read_b64_tr_b16: within each group of 16 lanes, source lane
 // 4e + q points at 4 consecutive channels of key kbase + e, and lane j receives
 // channel dbase + j of keys kbase .. kbase + 3. A workgroup holds at most 4
@@ -40,6 +45,7 @@ constexpr int kKBytes = kBlock * kRowB;     // one K (or V) block in LDS
 
 __device__ __forceinline__ bf16x8 as_v8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ int swz(int r, int g) { return r * kRowB + ((g ^ (r & 15)) << 4); }
+__device__ __forceinline__ int v_swz_granule(int r, int g) { return g ^ ((r & 3) << 2); }
 
 // Two transposed 8-byte reads of a swizzled V block give the V^T MFMA fragment
 // of keys {kb .. kb+3, kb+8 .. kb+11} at channel dbase + (lane % 16), where the
@@ -51,15 +57,15 @@ __device__ __forceinline__ u32x4 vt_frag(const uint8_t* vblk, int kb, int dbase,
   const int off = (ch & 7) * 2;  // 0 or 8 bytes into the granule
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)(vblk + key * kRowB + (((ch >> 3) ^ (key & 15)) << 4) + off));
+      (lds_i16x4*)(vblk + key * kRowB + (v_swz_granule(key, ch >> 3) << 4) + off));
   const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)(vblk + (key + 8) * kRowB + (((ch >> 3) ^ ((key + 8) & 15)) << 4) + off));
+      (lds_i16x4*)(vblk + (key + 8) * kRowB + (v_swz_granule(key + 8, ch >> 3) << 4) + off));
   const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
   return u32x4{ua.x, ua.y, ub.x, ub.y};
 }
 
-template <int NT>
-__device__ __forceinline__ void load_k_lds(const uint8_t* __restrict__ src_block, uint8_t* dst) {
+template <int NT, bool kV>
+__device__ __forceinline__ void load_block_lds(const uint8_t* __restrict__ src_block, uint8_t* dst) {
   // 64 rows x 16 granules = 1024 slots; NT threads, one 16-byte slot each per step
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -67,7 +73,7 @@ __device__ __forceinline__ void load_k_lds(const uint8_t* __restrict__ src_block
   for (int it = 0; it < 1024 / NT; ++it) {
     const int pos = (it * (NT / kWave) + wave) * kWave + lane;
     const int r = pos >> 4;
-    const int g = (pos & 15) ^ (r & 15);
+    const int g = kV ? v_swz_granule(r, pos & 15) : (pos & 15) ^ (r & 15);
     __builtin_amdgcn_global_load_lds(src_block + r * kRowB + g * 16,
                                      (__attribute__((address_space(3))) void*)(dst + (it * (NT / kWave) + wave) * kWave * 16),
                                      16, 0, 0);
@@ -77,64 +83,69 @@ __device__ __forceinline__ void load_k_lds(const uint8_t* __restrict__ src_block
 }  // namespace
 
 template <int HPW>
-__global__ __launch_bounds__(64 * HPW) void attn_prefill_kernel(
+__global__ __launch_bounds__(128 * HPW) void attn_prefill_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ kbuf, const uint8_t* __restrict__ vbuf,
     const int32_t* __restrict__ idx, uint8_t* __restrict__ out, int G, int Tq, int q_start, int T, int nB,
     int n_tiles, int k, float scale) {
-  constexpr int NT = 64 * HPW;  // threads: one wave per head of the workgroup's head group
+  constexpr int NT = 128 * HPW;  // threads: two waves (query halves) per head of the workgroup's head group
   __shared__ __attribute__((aligned(16))) uint8_t s_k[3][kKBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[2][kKBytes];
 
   const long row = blockIdx.x;  // (b, kv head)
   const int tile = blockIdx.y;
-  const int g = blockIdx.z * HPW + threadIdx.x / kWave;  // head within the GQA group
+  const int wv = threadIdx.x / kWave;
+  const int g = blockIdx.z * HPW + wv % HPW;  // head within the GQA group
   const int lane = threadIdx.x % kWave;
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int q0 = tile * kTile;
-  const int p_first = q_start + q0;  // position of the tile's first query
+  const int q0 = tile * kTile + 32 * (wv / HPW);  // this wave's 32 queries
+  const int p_tile = q_start + tile * kTile;     // position of the tile's first query
+  const int p_first = q_start + q0;              // position of this wave's first query
   const int32_t* sel = idx + (row * n_tiles + tile) * (long)k;
 
-  // Q fragments (B operand of S^T = K Q^T): head g, 2 query tiles x 8 k-steps
+  // Q fragments (B operand of S^T = K Q^T): head g, this wave's 32 queries x 8 k-steps
   const long qrow0 = (row * G + g) * (long)Tq + q0;
-  u32x4 qf[2][8];
+  u32x4 qf[8];
+  {
+    const uint8_t* src = q + (qrow0 + l32) * kRowB + half * 16;
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const uint8_t* src = q + (qrow0 + 32 * n + l32) * kRowB + half * 16;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qf[n][s] = load16(src + s * 32);
+    for (int s = 0; s < 8; ++s) qf[s] = load16(src + s * 32);
   }
 
-  f32x16 o[4][2];
+  f32x16 o[4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int n = 0; n < 2; ++n) o[dt][n] = f32x16{};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
 
-  // usable slots: valid, in range, not wholly after the tile
+  // usable slots: valid, in range, not wholly after the tile (the same for
+  // every wave of the workgroup, which shares the staged blocks)
   auto usable = [&](int j) {
     const int b = sel[j];
-    return b >= 0 && b < nB && b * kBlock <= p_first + kTile - 1;
+    return b >= 0 && b < nB && b * kBlock <= p_tile + kTile - 1;
   };
   auto next_usable = [&](int j) {
     while (j < k && !usable(j)) ++j;
     return j;
   };
-  auto load_block = [&](const uint8_t* base, int j, uint8_t* dst) {
-    load_k_lds<NT>(base + (row * (long)T + (long)sel[j] * kBlock) * kRowB, dst);
+  auto load_k = [&](int j, uint8_t* dst) {
+    load_block_lds<NT, false>(kbuf + (row * (long)T + (long)sel[j] * kBlock) * kRowB, dst);
   };
-  // S^T for key half h (keys 32h .. 32h+31 of the block) x both query tiles
-  auto scores_half = [&](const uint8_t* kblk, int h, f32x16 (&sa)[2]) {
+  auto load_v = [&](int j, uint8_t* dst) {
+    load_block_lds<NT, true>(vbuf + (row * (long)T + (long)sel[j] * kBlock) * kRowB, dst);
+  };
+  // S^T for key half h (keys 32h .. 32h+31 of the block) x this wave's queries;
+  // two accumulators (even and odd k-steps) keep two MFMA chains in flight
+  auto scores_half = [&](const uint8_t* kblk, int h, f32x16& sa) {
+    f32x16 sb = f32x16{};
+    sa = f32x16{};
 #pragma unroll
-    for (int n = 0; n < 2; ++n) sa[n] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < 8; s += 2) {
       const u32x4 ka = *reinterpret_cast<const u32x4*>(kblk + swz(32 * h + l32, 2 * s + half));
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-        sa[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8(ka), as_v8(qf[n][s]), sa[n], 0, 0, 0);
+      const u32x4 kb = *reinterpret_cast<const u32x4*>(kblk + swz(32 * h + l32, 2 * s + 2 + half));
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8(ka), as_v8(qf[s]), sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8(kb), as_v8(qf[s + 1]), sb, 0, 0, 0);
     }
+    sa += sb;
   };
   // Online softmax of one key half per query column, on raw scores: the
   // reference m_run is kept in raw units and p = exp2(x * c - m * c) with
@@ -144,66 +155,54 @@ __global__ __launch_bounds__(64 * HPW) void attn_prefill_kernel(
   // units, so most halves leave the accumulators alone; numerator and
   // denominator share it, so the result does not depend on where it sits.
   const float c2 = scale * 1.4426950408889634f;
-  auto softmax_half = [&](f32x16 (&sa)[2], int key0, bool diag, uint32_t (&ph)[2][8]) {
-    float alphas[2];
-    bool rescale = false;
+  auto softmax_half = [&](f32x16& sa, int key0, bool diag, uint32_t (&ph)[8]) {
+    const int pq = p_first + l32;  // this lane's query position
+    float mx = -INFINITY;
+    if (diag) {
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int pq = p_first + 32 * n + l32;  // this lane's query position
-      float mx = -INFINITY;
-      if (diag) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const float x = key <= pq ? sa[n][r] : -INFINITY;
-          sa[n][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[n][r]);
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const float x = key <= pq ? sa[r] : -INFINITY;
+        sa[r] = x;
+        mx = fmaxf(mx, x);
       }
-      mx = max32(mx);
-      const bool grow = (mx - m_run[n]) * c2 > 8.f || (m_run[n] == -INFINITY && mx != -INFINITY);
-      const float mn = grow ? mx : m_run[n];
-      const bool none = mn == -INFINITY;  // only possible on a diagonal block
-      const float alpha = grow && m_run[n] != -INFINITY ? __builtin_amdgcn_exp2f((m_run[n] - mn) * c2) : 1.f;
-      rescale |= alpha != 1.f;
-      const float mc = none ? 0.f : mn * c2;
-      float sum = 0.f;
+    } else {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sa[n][r], c2, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sa[n][r + 1], c2, -mc));
-        sum += p0 + p1;
-        ph[n][r >> 1] = pack_bf16(p0, p1);
-      }
-      sum = sum32(sum);
-      l_run[n] = l_run[n] * alpha + sum;
-      m_run[n] = mn;
-      alphas[n] = alpha;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[r]);
     }
-    if (__ballot(rescale)) {  // wave-uniform; lanes that keep their reference have alpha 1
+    mx = max32(mx);
+    const bool grow = (mx - m_run) * c2 > 8.f || (m_run == -INFINITY && mx != -INFINITY);
+    const float mn = grow ? mx : m_run;
+    const bool none = mn == -INFINITY;  // only possible on a diagonal block
+    const float alpha = grow && m_run != -INFINITY ? __builtin_amdgcn_exp2f((m_run - mn) * c2) : 1.f;
+    const float mc = none ? 0.f : mn * c2;
+    float sum = 0.f;
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sa[r], c2, -mc));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sa[r + 1], c2, -mc));
+      sum += p0 + p1;
+      ph[r >> 1] = pack_bf16(p0, p1);
+    }
+    sum = sum32(sum);
+    l_run = l_run * alpha + sum;
+    m_run = mn;
+    if (__ballot(alpha != 1.f)) {  // wave-uniform; lanes that keep their reference have alpha 1
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[dt][n] *= alphas[n];
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
   };
   // O^T += V^T P^T for key half h: 2 k-steps of 16 keys
-  auto pv_half = [&](const uint8_t* vblk, int h, const uint32_t (&ph)[2][8]) {
+  auto pv_half = [&](const uint8_t* vblk, int h, const uint32_t (&ph)[8]) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int kb = 32 * h + 16 * s + 4 * half;
+      const u32x4 pb = {ph[4 * s], ph[4 * s + 1], ph[4 * s + 2], ph[4 * s + 3]};
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         // lane group (lane / 16): channels 32 dt + 16 ((lane / 16) % 2) .. +15
         const u32x4 va = vt_frag(vblk, kb, 32 * dt + 16 * ((lane >> 4) & 1), lane);
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          const u32x4 pb = {ph[n][4 * s], ph[n][4 * s + 1], ph[n][4 * s + 2], ph[n][4 * s + 3]};
-          o[dt][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8(va), as_v8(pb), o[dt][n], 0, 0, 0);
-        }
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8(va), as_v8(pb), o[dt], 0, 0, 0);
       }
     }
   };
@@ -215,13 +214,13 @@ __global__ __launch_bounds__(64 * HPW) void attn_prefill_kernel(
   int jc = next_usable(0);
   int jn = jc < k ? next_usable(jc + 1) : k;
   if (jc < k) {
-    load_block(kbuf, jc, s_k[0]);
-    load_block(vbuf, jc, s_v[0]);
+    load_k(jc, s_k[0]);
+    load_v(jc, s_v[0]);
   }
-  if (jn < k) load_block(kbuf, jn, s_k[1]);
+  if (jn < k) load_k(jn, s_k[1]);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
-  f32x16 sa0[2], sa1[2];  // scores of the half being normalised / being computed
+  f32x16 sa0, sa1;  // scores of the half being normalised / being computed
   if (jc < k) scores_half(s_k[0], 0, sa0);
 
   int t = 0, kc = 0;  // kc = t % 3
@@ -229,11 +228,11 @@ __global__ __launch_bounds__(64 * HPW) void attn_prefill_kernel(
     const int kn = kc == 2 ? 0 : kc + 1, kn2 = kn == 2 ? 0 : kn + 1;
     const int vc = t & 1;
     const int jn2 = jn < k ? next_usable(jn + 1) : k;
-    if (jn2 < k) load_block(kbuf, jn2, s_k[kn2]);
-    if (jn < k) load_block(vbuf, jn, s_v[vc ^ 1]);
+    if (jn2 < k) load_k(jn2, s_k[kn2]);
+    if (jn < k) load_v(jn, s_v[vc ^ 1]);
     const int key_base = sel[jc] * kBlock;
     const bool diag = key_base + kBlock - 1 > p_first;
-    uint32_t ph[2][8];
+    uint32_t ph[8];
     // half 0: scores of half 1 on the matrix cores, softmax of half 0 on the ALUs
     scores_half(s_k[kc], 1, sa1);
     softmax_half(sa0, key_base, diag, ph);
@@ -251,18 +250,17 @@ __global__ __launch_bounds__(64 * HPW) void attn_prefill_kernel(
   }
 
   // O = O^T / l, written as 4 consecutive channels (8 B) per accumulator group
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const float inv = l_run[n] > 0.f ? 1.f / l_run[n] : 0.f;
-    uint8_t* dst = out + (qrow0 + 32 * n + l32) * kRowB;
+  {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint8_t* dst = out + (qrow0 + l32) * kRowB;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int d = 32 * dt + 8 * rg + 4 * half;
         uint2 v;
-        v.x = pack_bf16(o[dt][n][4 * rg] * inv, o[dt][n][4 * rg + 1] * inv);
-        v.y = pack_bf16(o[dt][n][4 * rg + 2] * inv, o[dt][n][4 * rg + 3] * inv);
+        v.x = pack_bf16(o[dt][4 * rg] * inv, o[dt][4 * rg + 1] * inv);
+        v.y = pack_bf16(o[dt][4 * rg + 2] * inv, o[dt][4 * rg + 3] * inv);
         *reinterpret_cast<uint2*>(dst + d * 2) = v;
       }
   }
@@ -274,7 +272,7 @@ hipError_t launch_attn_prefill(const void* q, const void* k, const void* v, cons
   const int hpw = G < 4 ? G : 4;  // heads per workgroup; G = 8 runs as two groups of 4
   const dim3 grid(d.B * d.Hkv, d.n_tiles, G / hpw);
 #define SPARDA_AP(HPW)                                                                                          \
-  hipLaunchKernelGGL(attn_prefill_kernel<HPW>, grid, dim3(64 * HPW), 0, s, (const uint8_t*)q, (const uint8_t*)k, \
+  hipLaunchKernelGGL(attn_prefill_kernel<HPW>, grid, dim3(128 * HPW), 0, s, (const uint8_t*)q, (const uint8_t*)k, \
                      (const uint8_t*)v, idx, (uint8_t*)out, G, d.Tq, d.q_start, d.T, d.nB, d.n_tiles, d.k, d.scale)
   switch (hpw) {
     case 1: SPARDA_AP(1); break;
