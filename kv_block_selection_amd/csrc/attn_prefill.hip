@@ -19,8 +19,8 @@
 // Each 64-key block is worked as two 32-key halves in a software pipeline: the
 // matrix cores compute the scores of the next half while the vector ALUs run
 // the softmax of the current one, then its PV products. K and V blocks arrive
-// in LDS by direct global->LDS loads a block ahead (three K buffers, two V
-// buffers; 80 KiB), rows granule-swizzled so that both fragment reads are free
+// in LDS by direct global->LDS loads two blocks ahead (four K buffers, three V
+// buffers; 112 KiB), rows granule-swizzled so that both fragment reads are free
 // of bank conflicts: 16-byte granule g of K row r sits at g ^ (r & 15) (a K
 // fragment read takes one granule of 16 consecutive rows), of V row r at
 // g ^ 4 (r & 3) (a transposed V read takes 4 consecutive granules of 4
@@ -64,6 +64,17 @@ __device__ __forceinline__ u32x4 vt_frag(const uint8_t* vblk, int kb, int dbase,
   return u32x4{ua.x, ua.y, ub.x, ub.y};
 }
 
+// One direct global->LDS load of 16 bytes per lane: lane i's bytes land at
+// lds_wave_dst + 16 i. Written as an asm statement so that the compiler, which
+// cannot tell which LDS buffer such a load fills, does not make every later
+// LDS read wait for it; the kernel waits for these loads itself (vmcnt) before
+// the barrier that publishes them.
+__device__ __forceinline__ void dma16(const uint8_t* gsrc, const uint8_t* lds_wave_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds_wave_dst);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(base) : "memory");
+}
+
 template <int NT, bool kV>
 __device__ __forceinline__ void load_block_lds(const uint8_t* __restrict__ src_block, uint8_t* dst) {
   // 64 rows x 16 granules = 1024 slots; NT threads, one 16-byte slot each per step
@@ -74,9 +85,7 @@ __device__ __forceinline__ void load_block_lds(const uint8_t* __restrict__ src_b
     const int pos = (it * (NT / kWave) + wave) * kWave + lane;
     const int r = pos >> 4;
     const int g = kV ? v_swz_granule(r, pos & 15) : (pos & 15) ^ (r & 15);
-    __builtin_amdgcn_global_load_lds(src_block + r * kRowB + g * 16,
-                                     (__attribute__((address_space(3))) void*)(dst + (it * (NT / kWave) + wave) * kWave * 16),
-                                     16, 0, 0);
+    dma16(src_block + r * kRowB + g * 16, dst + (it * (NT / kWave) + wave) * kWave * 16);
   }
 }
 
@@ -88,8 +97,9 @@ __global__ __launch_bounds__(128 * HPW) void attn_prefill_kernel(
     const int32_t* __restrict__ idx, uint8_t* __restrict__ out, int G, int Tq, int q_start, int T, int nB,
     int n_tiles, int k, float scale) {
   constexpr int NT = 128 * HPW;  // threads: two waves (query halves) per head of the workgroup's head group
-  __shared__ __attribute__((aligned(16))) uint8_t s_k[3][kKBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[2][kKBytes];
+  constexpr int DMA = 1024 / NT;  // direct-to-LDS load instructions per wave per block
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[4][kKBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[3][kKBytes];
 
   const long row = blockIdx.x;  // (b, kv head)
   const int tile = blockIdx.y;
@@ -119,8 +129,12 @@ __global__ __launch_bounds__(128 * HPW) void attn_prefill_kernel(
 
   // usable slots: valid, in range, not wholly after the tile (the same for
   // every wave of the workgroup, which shares the staged blocks)
+  // Block index of slot j, read with a scalar load (j is wave-uniform): a
+  // vector load would count against vmcnt, which tracks the direct-to-LDS
+  // loads below.
+  auto sel_at = [&](int j) { return sel[__builtin_amdgcn_readfirstlane(j)]; };
   auto usable = [&](int j) {
-    const int b = sel[j];
+    const int b = sel_at(j);
     return b >= 0 && b < nB && b * kBlock <= p_tile + kTile - 1;
   };
   auto next_usable = [&](int j) {
@@ -128,10 +142,10 @@ __global__ __launch_bounds__(128 * HPW) void attn_prefill_kernel(
     return j;
   };
   auto load_k = [&](int j, uint8_t* dst) {
-    load_block_lds<NT, false>(kbuf + (row * (long)T + (long)sel[j] * kBlock) * kRowB, dst);
+    load_block_lds<NT, false>(kbuf + (row * (long)T + (long)sel_at(j) * kBlock) * kRowB, dst);
   };
   auto load_v = [&](int j, uint8_t* dst) {
-    load_block_lds<NT, true>(vbuf + (row * (long)T + (long)sel[j] * kBlock) * kRowB, dst);
+    load_block_lds<NT, true>(vbuf + (row * (long)T + (long)sel_at(j) * kBlock) * kRowB, dst);
   };
   // S^T for key half h (keys 32h .. 32h+31 of the block) x this wave's queries;
   // two accumulators (even and odd k-steps) keep two MFMA chains in flight
@@ -207,46 +221,84 @@ __global__ __launch_bounds__(128 * HPW) void attn_prefill_kernel(
     }
   };
 
-  // Usable blocks t = 0, 1, ...: K(t) in s_k[t % 3], V(t) in s_v[t % 2].
-  // Iteration t issues K(t+2) (into the buffer of K(t-1)) and V(t+1) (into
-  // the buffer of V(t-1)), both last read before the previous barrier, and
-  // drains them at its end: they are first read in iteration t+1.
-  int jc = next_usable(0);
-  int jn = jc < k ? next_usable(jc + 1) : k;
-  if (jc < k) {
-    load_k(jc, s_k[0]);
-    load_v(jc, s_v[0]);
-  }
-  if (jn < k) load_k(jn, s_k[1]);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();
   f32x16 sa0, sa1;  // scores of the half being normalised / being computed
-  if (jc < k) scores_half(s_k[0], 0, sa0);
-
-  int t = 0, kc = 0;  // kc = t % 3
-  while (jc < k) {
-    const int kn = kc == 2 ? 0 : kc + 1, kn2 = kn == 2 ? 0 : kn + 1;
-    const int vc = t & 1;
-    const int jn2 = jn < k ? next_usable(jn + 1) : k;
-    if (jn2 < k) load_k(jn2, s_k[kn2]);
-    if (jn < k) load_v(jn, s_v[vc ^ 1]);
-    const int key_base = sel[jc] * kBlock;
+  // One block t: scores of its second key half, both softmax halves and PV
+  // products, and the scores of block t+1's first half; meanwhile it issues
+  // K(t+3) and V(t+2) into the buffers of K(t-1) and V(t-1). The LDS pointers
+  // and the global sources of the loads are restrict parameters. Returns the
+  // load instructions this wave issued.
+  auto block_step = [&](const uint8_t* __restrict__ k_cur, const uint8_t* __restrict__ k_next,
+                        const uint8_t* __restrict__ v_cur, uint8_t* __restrict__ k_fill,
+                        uint8_t* __restrict__ v_fill, const uint8_t* __restrict__ k_src,
+                        const uint8_t* __restrict__ v_src, int jc, int j_next) -> int {
+    int issued = 0;
+    if (k_src != nullptr) {
+      load_block_lds<NT, false>(k_src, k_fill);
+      issued += DMA;
+    }
+    if (v_src != nullptr) {
+      load_block_lds<NT, true>(v_src, v_fill);
+      issued += DMA;
+    }
+    const int key_base = sel_at(jc) * kBlock;
     const bool diag = key_base + kBlock - 1 > p_first;
     uint32_t ph[8];
     // half 0: scores of half 1 on the matrix cores, softmax of half 0 on the ALUs
-    scores_half(s_k[kc], 1, sa1);
+    scores_half(k_cur, 1, sa1);
     softmax_half(sa0, key_base, diag, ph);
-    pv_half(s_v[vc], 0, ph);
-    // half 1: scores of the next block's half 0 (its K landed last iteration)
-    if (jn < k) scores_half(s_k[kn], 0, sa0);
+    pv_half(v_cur, 0, ph);
+    // half 1: scores of the next block's half 0
+    if (j_next < k) scores_half(k_next, 0, sa0);
     softmax_half(sa1, key_base + 32, diag, ph);
-    pv_half(s_v[vc], 1, ph);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // K(t+2) and V(t+1) have landed
-    __syncthreads();                           // and this iteration's LDS reads are done
-    jc = jn;
-    jn = jn2;
+    pv_half(v_cur, 1, ph);
+    return issued;
+  };
+
+  // Usable blocks t = 0, 1, ...: K(t) in s_k[t % 4], V(t) in s_v[t % 3].
+  // Block step t reads K(t), K(t+1), V(t) and fills K(t+3), V(t+2); at its
+  // end each wave waits for its loads issued one step earlier (K(t+2),
+  // V(t+1)), leaving this step's in flight, and a barrier makes them visible
+  // to every wave. A load thus has two block steps to land.
+  int j0 = next_usable(0);
+  int j1 = j0 < k ? next_usable(j0 + 1) : k;
+  int j2 = j1 < k ? next_usable(j1 + 1) : k;
+  if (j0 < k) {
+    load_k(j0, s_k[0]);
+    load_v(j0, s_v[0]);
+  }
+  if (j1 < k) {
+    load_k(j1, s_k[1]);
+    load_v(j1, s_v[1]);
+  }
+  if (j2 < k) load_k(j2, s_k[2]);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  if (j0 < k) scores_half(s_k[0], 0, sa0);
+
+  int kc = 0, vc = 0;  // t % 4, t % 3
+  while (j0 < k) {
+    const int j3 = j2 < k ? next_usable(j2 + 1) : k;
+    const int kn = (kc + 1) & 3, kf = (kc + 3) & 3;
+    const int vf = vc == 0 ? 2 : vc - 1;  // (t + 2) % 3
+    const uint8_t* k_src = j3 < k ? kbuf + (row * (long)T + (long)sel_at(j3) * kBlock) * kRowB : nullptr;
+    const uint8_t* v_src = j2 < k ? vbuf + (row * (long)T + (long)sel_at(j2) * kBlock) * kRowB : nullptr;
+    const int issued = block_step(s_k[kc], s_k[kn], s_v[vc], s_k[kf], s_v[vf], k_src, v_src, j0, j1);
+    if (issued == 2 * DMA) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA));
+    } else if (issued == DMA) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(DMA));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    // No fence: a release fence would also wait for the loads just issued.
+    // The memory clobber keeps LDS accesses on their side of the barrier;
+    // every fragment read of this step has been consumed by its MFMA.
+    asm volatile("s_barrier" ::: "memory");
+    j0 = j1;
+    j1 = j2;
+    j2 = j3;
     kc = kn;
-    ++t;
+    vc = vc == 2 ? 0 : vc + 1;
   }
 
   // O = O^T / l, written as 4 consecutive channels (8 B) per accumulator group
