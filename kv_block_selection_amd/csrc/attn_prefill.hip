@@ -16,11 +16,12 @@
 //                register order. The MFMA k index then runs over the keys in
 //                the accumulator's row order (groups of 4); V^T fragments are
 //                read from LDS in that same order, so the sum is unchanged.
-// Each 64-key block is worked as two 32-key halves in a software pipeline: the
-// matrix cores compute the scores of the next half while the vector ALUs run
-// the softmax of the current one, then its PV products. K and V blocks arrive
-// in LDS by direct global->LDS loads two blocks ahead (four K buffers, three V
-// buffers; 112 KiB), rows granule-swizzled so that both fragment reads are free
+// Each 64-key block is worked as two 32-key halves in a software pipeline:
+// while the vector ALUs run the softmax of half s, the matrix cores take the
+// PV products of half s-1 and the scores of half s+1, interleaved in one
+// instruction stream so that a wave keeps both units busy. K and V blocks arrive
+// in LDS by direct global->LDS loads two blocks ahead (four K and four V
+// buffers; 128 KiB), rows granule-swizzled so that both fragment reads are free
 // of bank conflicts: 16-byte granule g of K row r sits at g ^ (r & 15) (a K
 // fragment read takes one granule of 16 consecutive rows), of V row r at
 // g ^ 4 (r & 3) (a transposed V read takes 4 consecutive granules of 4
@@ -29,6 +30,8 @@
 // 4e + q points at 4 consecutive channels of key kbase + e, and lane j receives
 // channel dbase + j of keys kbase .. kbase + 3. A workgroup holds at most 4
 // heads; a group of 8 runs as two workgroups.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_prefill_kernel(
   constexpr int NT = 128 * HPW;  // threads: two waves (query halves) per head of the workgroup's head group
   constexpr int DMA = 1024 / NT;  // direct-to-LDS load instructions per wave per block
   __shared__ __attribute__((aligned(16))) uint8_t s_k[4][kKBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[3][kKBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[4][kKBytes];
 
   const long row = blockIdx.x;  // (b, kv head)
   const int tile = blockIdx.y;
@@ -150,16 +153,12 @@ __global__ __launch_bounds__(128 * HPW) void attn_prefill_kernel(
   // S^T for key half h (keys 32h .. 32h+31 of the block) x this wave's queries;
   // two accumulators (even and odd k-steps) keep two MFMA chains in flight
   auto scores_half = [&](const uint8_t* kblk, int h, f32x16& sa) {
-    f32x16 sb = f32x16{};
     sa = f32x16{};
 #pragma unroll
-    for (int s = 0; s < 8; s += 2) {
+    for (int s = 0; s < 8; ++s) {
       const u32x4 ka = *reinterpret_cast<const u32x4*>(kblk + swz(32 * h + l32, 2 * s + half));
-      const u32x4 kb = *reinterpret_cast<const u32x4*>(kblk + swz(32 * h + l32, 2 * s + 2 + half));
       sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8(ka), as_v8(qf[s]), sa, 0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8(kb), as_v8(qf[s + 1]), sb, 0, 0, 0);
     }
-    sa += sb;
   };
   // Online softmax of one key half per query column, on raw scores: the
   // reference m_run is kept in raw units and p = exp2(x * c - m * c) with
@@ -169,10 +168,13 @@ __global__ __launch_bounds__(128 * HPW) void attn_prefill_kernel(
   // units, so most halves leave the accumulators alone; numerator and
   // denominator share it, so the result does not depend on where it sits.
   const float c2 = scale * 1.4426950408889634f;
-  auto softmax_half = [&](f32x16& sa, int key0, bool diag, uint32_t (&ph)[8]) {
+  // Returns alpha, the factor that moves O and l to the new reference; l is
+  // already updated, O is rescaled by the caller once the previous half's PV
+  // products have been added to it.
+  auto softmax_half = [&](auto kMask, f32x16& sa, int key0, uint32_t (&ph)[8]) -> float {
     const int pq = p_first + l32;  // this lane's query position
     float mx = -INFINITY;
-    if (diag) {
+    if constexpr (decltype(kMask)::value) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -185,11 +187,13 @@ __global__ __launch_bounds__(128 * HPW) void attn_prefill_kernel(
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[r]);
     }
     mx = max32(mx);
-    const bool grow = (mx - m_run) * c2 > 8.f || (m_run == -INFINITY && mx != -INFINITY);
+    // branch-free (bitwise, selects) so that the stage stays one basic block
+    // for the scheduler: exp2(0) = 1 when the reference stays, exp2(-inf) = 0
+    // when it is set for the first time
+    const bool grow = ((mx - m_run) * c2 > 8.f) | ((m_run == -INFINITY) & (mx != -INFINITY));
     const float mn = grow ? mx : m_run;
-    const bool none = mn == -INFINITY;  // only possible on a diagonal block
-    const float alpha = grow && m_run != -INFINITY ? __builtin_amdgcn_exp2f((m_run - mn) * c2) : 1.f;
-    const float mc = none ? 0.f : mn * c2;
+    const float alpha = __builtin_amdgcn_exp2f(grow ? (m_run - mn) * c2 : 0.f);
+    const float mc = mn == -INFINITY ? 0.f : mn * c2;  // -inf only on a masked block with nothing seen
     float sum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
@@ -201,10 +205,7 @@ __global__ __launch_bounds__(128 * HPW) void attn_prefill_kernel(
     sum = sum32(sum);
     l_run = l_run * alpha + sum;
     m_run = mn;
-    if (__ballot(alpha != 1.f)) {  // wave-uniform; lanes that keep their reference have alpha 1
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-    }
+    return alpha;
   };
   // O^T += V^T P^T for key half h: 2 k-steps of 16 keys
   auto pv_half = [&](const uint8_t* vblk, int h, const uint32_t (&ph)[8]) {
@@ -221,44 +222,46 @@ __global__ __launch_bounds__(128 * HPW) void attn_prefill_kernel(
     }
   };
 
-  f32x16 sa0, sa1;  // scores of the half being normalised / being computed
-  // One block t: scores of its second key half, both softmax halves and PV
-  // products, and the scores of block t+1's first half; meanwhile it issues
-  // K(t+3) and V(t+2) into the buffers of K(t-1) and V(t-1). The LDS pointers
-  // and the global sources of the loads are restrict parameters. Returns the
-  // load instructions this wave issued.
-  auto block_step = [&](const uint8_t* __restrict__ k_cur, const uint8_t* __restrict__ k_next,
-                        const uint8_t* __restrict__ v_cur, uint8_t* __restrict__ k_fill,
-                        uint8_t* __restrict__ v_fill, const uint8_t* __restrict__ k_src,
-                        const uint8_t* __restrict__ v_src, int jc, int j_next) -> int {
-    int issued = 0;
-    if (k_src != nullptr) {
-      load_block_lds<NT, false>(k_src, k_fill);
-      issued += DMA;
-    }
-    if (v_src != nullptr) {
-      load_block_lds<NT, true>(v_src, v_fill);
-      issued += DMA;
-    }
-    const int key_base = sel_at(jc) * kBlock;
-    const bool diag = key_base + kBlock - 1 > p_first;
+  // The work runs in stages, one per key half s of the usable blocks: stage s
+  // issues the PV products of half s-1 and the scores of half s+1 on the
+  // matrix cores and, in between (sched_group_barrier), the softmax of half s
+  // on the vector ALUs; O is rescaled at the stage's end, after half s-1's
+  // products are in. Before the first stage P is all zero (adds exactly 0).
+  f32x16 sa_cur;           // scores of the half whose softmax runs now
+  uint32_t ph_prev[8];     // P of the previous half, awaiting its PV products
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ph_prev[i] = 0u;
+  auto stage = [&](auto kMask, const uint8_t* __restrict__ k_nxt, int h_nxt, const uint8_t* __restrict__ v_prv,
+                   int h_prv, int key0) {
+    f32x16 sa_next;
     uint32_t ph[8];
-    // half 0: scores of half 1 on the matrix cores, softmax of half 0 on the ALUs
-    scores_half(k_cur, 1, sa1);
-    softmax_half(sa0, key_base, diag, ph);
-    pv_half(v_cur, 0, ph);
-    // half 1: scores of the next block's half 0
-    if (j_next < k) scores_half(k_next, 0, sa0);
-    softmax_half(sa1, key_base + 32, diag, ph);
-    pv_half(v_cur, 1, ph);
-    return issued;
+    pv_half(v_prv, h_prv, ph_prev);
+    scores_half(k_nxt, h_nxt, sa_next);
+    const float alpha = softmax_half(kMask, sa_cur, key0, ph);
+    // 16 MFMAs, each followed by a share of the softmax (plain VALU and one
+    // exponential, which the scheduler counts apart) and of the fragment reads
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);  // transcendental (exp2)
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // other VALU
+    }
+    if (__ballot(alpha != 1.f)) {  // wave-uniform; lanes that keep their reference have alpha 1
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ph_prev[i] = ph[i];
+    sa_cur = sa_next;
   };
 
-  // Usable blocks t = 0, 1, ...: K(t) in s_k[t % 4], V(t) in s_v[t % 3].
-  // Block step t reads K(t), K(t+1), V(t) and fills K(t+3), V(t+2); at its
+  // Usable blocks t = 0, 1, ...: K(t) in s_k[t % 4], V(t) in s_v[t % 4].
+  // Block step t (stages of t's two halves) reads K(t), K(t+1), V(t-1), V(t)
+  // and fills K(t+3) and V(t+2) into the buffers of K(t-1) and V(t-2). At its
   // end each wave waits for its loads issued one step earlier (K(t+2),
   // V(t+1)), leaving this step's in flight, and a barrier makes them visible
-  // to every wave. A load thus has two block steps to land.
+  // to every wave: a load has two block steps to land.
   int j0 = next_usable(0);
   int j1 = j0 < k ? next_usable(j0 + 1) : k;
   int j2 = j1 < k ? next_usable(j1 + 1) : k;
@@ -273,16 +276,32 @@ __global__ __launch_bounds__(128 * HPW) void attn_prefill_kernel(
   if (j2 < k) load_k(j2, s_k[2]);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
-  if (j0 < k) scores_half(s_k[0], 0, sa0);
+  if (j0 < k) scores_half(s_k[0], 0, sa_cur);
 
-  int kc = 0, vc = 0;  // t % 4, t % 3
+  int bc = 0;          // t % 4
+  int v_last = 0;      // buffer of V(t - 1) (V(0)'s before the first step: P is 0 then)
   while (j0 < k) {
     const int j3 = j2 < k ? next_usable(j2 + 1) : k;
-    const int kn = (kc + 1) & 3, kf = (kc + 3) & 3;
-    const int vf = vc == 0 ? 2 : vc - 1;  // (t + 2) % 3
-    const uint8_t* k_src = j3 < k ? kbuf + (row * (long)T + (long)sel_at(j3) * kBlock) * kRowB : nullptr;
-    const uint8_t* v_src = j2 < k ? vbuf + (row * (long)T + (long)sel_at(j2) * kBlock) * kRowB : nullptr;
-    const int issued = block_step(s_k[kc], s_k[kn], s_v[vc], s_k[kf], s_v[vf], k_src, v_src, j0, j1);
+    const int bn = (bc + 1) & 3, bf3 = (bc + 3) & 3, bf2 = (bc + 2) & 3;
+    int issued = 0;
+    if (j3 < k) {
+      load_k(j3, s_k[bf3]);
+      issued += DMA;
+    }
+    if (j2 < k) {
+      load_v(j2, s_v[bf2]);
+      issued += DMA;
+    }
+    const int key_base = sel_at(j0) * kBlock;
+    // the next block's K buffer holds stale (finite) data after the last block:
+    // its scores are computed and never used
+    if (key_base + kBlock - 1 > p_first) {  // some key after some query of this wave
+      stage(std::true_type{}, s_k[bc], 1, s_v[v_last], 1, key_base);
+      stage(std::true_type{}, s_k[bn], 0, s_v[bc], 0, key_base + 32);
+    } else {
+      stage(std::false_type{}, s_k[bc], 1, s_v[v_last], 1, key_base);
+      stage(std::false_type{}, s_k[bn], 0, s_v[bc], 0, key_base + 32);
+    }
     if (issued == 2 * DMA) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA));
     } else if (issued == DMA) {
@@ -294,12 +313,13 @@ __global__ __launch_bounds__(128 * HPW) void attn_prefill_kernel(
     // The memory clobber keeps LDS accesses on their side of the barrier;
     // every fragment read of this step has been consumed by its MFMA.
     asm volatile("s_barrier" ::: "memory");
+    v_last = bc;
     j0 = j1;
     j1 = j2;
     j2 = j3;
-    kc = kn;
-    vc = vc == 2 ? 0 : vc + 1;
+    bc = bn;
   }
+  pv_half(s_v[v_last], 1, ph_prev);  // the last half's products
 
   // O = O^T / l, written as 4 consecutive channels (8 B) per accumulator group
   {
