@@ -67,17 +67,6 @@ __device__ __forceinline__ u32x4 vt_frag(const uint8_t* vblk, int kb, int dbase,
   return u32x4{ua.x, ua.y, ub.x, ub.y};
 }
 
-// One direct global->LDS load of 16 bytes per lane: lane i's bytes land at
-// lds_wave_dst + 16 i. Written as an asm statement so that the compiler, which
-// cannot tell which LDS buffer such a load fills, does not make every later
-// LDS read wait for it; the kernel waits for these loads itself (vmcnt) before
-// the barrier that publishes them.
-__device__ __forceinline__ void dma16(const uint8_t* gsrc, const uint8_t* lds_wave_dst) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds_wave_dst);
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(base) : "memory");
-}
-
 template <int NT, bool kV>
 __device__ __forceinline__ void load_block_lds(const uint8_t* __restrict__ src_block, uint8_t* dst) {
   // 64 rows x 16 granules = 1024 slots; NT threads, one 16-byte slot each per step

@@ -202,6 +202,17 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // s_waitcnt immediate that waits until at most n vector-memory loads are
 // outstanding and leaves the other counters alone (gfx9 encoding: vmcnt bits
 // 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+// One direct global->LDS load of 16 bytes per lane: lane i's bytes land at
+// lds_wave_dst + 16 i. Written as an asm statement so that the compiler, which
+// cannot tell which LDS buffer such a load fills, does not make every later
+// LDS read (and every workgroup barrier) wait for it: a kernel that uses it
+// waits for its own loads (vmcnt) before the barrier that publishes them.
+__device__ __forceinline__ void dma16(const uint8_t* gsrc, const uint8_t* lds_wave_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds_wave_dst);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(base) : "memory");
+}
+
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 __device__ __forceinline__ float fast_exp(float x) {

@@ -37,8 +37,7 @@ __device__ __forceinline__ void load_chunk_lds(const uint8_t* __restrict__ kc_ro
     const int g = (pos & 15) ^ (r & 15);
     const int w = min(w0 + r, W - 1);
     const uint8_t* src = kc_row + (long)w * kRowBytes + g * 16;
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + (it * NWAVES + wave) * kWave * 16),
-                                     16, 0, 0);
+    dma16(src, dst + (it * NWAVES + wave) * kWave * 16);
   }
 }
 
