@@ -17,9 +17,9 @@
 //                the accumulator's row order (groups of 4); V^T fragments are
 //                read from LDS in that same order, so the sum is unchanged.
 // Each 64-key block is worked as two 32-key halves in a software pipeline:
-// while the vector ALUs run the softmax of half s, the matrix cores take the
-// PV products of half s-1 and the scores of half s+1, interleaved in one
-// instruction stream so that a wave keeps both units busy. K and V blocks arrive
+// the softmax of half s shares a basic block with the PV products of half s-1
+// and the scores of half s+1, so that a wave has matrix-core and vector-ALU
+// work in flight together. K and V blocks arrive
 // in LDS by direct global->LDS loads two blocks ahead (four K and four V
 // buffers; 128 KiB), rows granule-swizzled so that both fragment reads are free
 // of bank conflicts: 16-byte granule g of K row r sits at g ^ (r & 15) (a K
@@ -213,9 +213,11 @@ __global__ __launch_bounds__(128 * HPW) void attn_prefill_kernel(
 
   // The work runs in stages, one per key half s of the usable blocks: stage s
   // issues the PV products of half s-1 and the scores of half s+1 on the
-  // matrix cores and, in between (sched_group_barrier), the softmax of half s
-  // on the vector ALUs; O is rescaled at the stage's end, after half s-1's
-  // products are in. Before the first stage P is all zero (adds exactly 0).
+  // matrix cores and the softmax of half s on the vector ALUs, in one basic
+  // block that the compiler schedules (explicit interleaving by
+  // sched_group_barrier measured slower); O is rescaled at the stage's end,
+  // after half s-1's products are in. Before the first stage P is all zero
+  // (adds exactly 0).
   f32x16 sa_cur;           // scores of the half whose softmax runs now
   uint32_t ph_prev[8];     // P of the previous half, awaiting its PV products
 #pragma unroll
@@ -227,15 +229,6 @@ __global__ __launch_bounds__(128 * HPW) void attn_prefill_kernel(
     pv_half(v_prv, h_prv, ph_prev);
     scores_half(k_nxt, h_nxt, sa_next);
     const float alpha = softmax_half(kMask, sa_cur, key0, ph);
-    // 16 MFMAs, each followed by a share of the softmax (plain VALU and one
-    // exponential, which the scheduler counts apart) and of the fragment reads
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);  // transcendental (exp2)
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // other VALU
-    }
     if (__ballot(alpha != 1.f)) {  // wave-uniform; lanes that keep their reference have alpha 1
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
