@@ -66,7 +66,9 @@ enum sparda_dtype { SPARDA_F32 = 0, SPARDA_BF16 = 1 };
 
 enum sparda_kv_mode {
   SPARDA_KV_CACHE = 0,   /* k, v: the layer's cache [B, Hkv, T, d]; blocks read at idx */
-  SPARDA_KV_STAGING = 1  /* k, v: staging [B, Hkv, k, block, d]; slot j holds block idx[.., j] */
+  SPARDA_KV_STAGING = 1, /* k, v: staging [B, Hkv, k, block, d]; slot j holds block idx[.., j] */
+  SPARDA_KV_SLOTS = 2    /* k, v: staging kept as a block cache [B, Hkv, n_slots, block, d];
+                            block idx[.., j] sits in slot slot_of[.., j] */
 };
 
 enum sparda_op {
@@ -186,6 +188,9 @@ int sparda_topk_blocks(const float* blk_scores, int32_t* idx, int rows, int nB, 
  *   q     [B, Hq, Tq, d]
  *   k, v  kv_mode SPARDA_KV_CACHE:   [B, Hkv, T, d]
  *         kv_mode SPARDA_KV_STAGING: [B, Hkv, k, block, d], slot j = block idx[b, h, 0, j] (Tq = 1 only)
+ *         kv_mode SPARDA_KV_SLOTS:   [B, Hkv, n_slots, block, d], block idx[b, h, 0, j] in slot
+ *                                    slot_of[b, h, j] (Tq = 1 only; as sparda_prefetch_blocks_cached
+ *                                    leaves it); slot_of and n_slots are ignored in the other modes
  *   idx   [B, Hkv, nTiles, k] int32, -1 = unused slot
  *   out   [B, Hq, Tq, d] (dtype of q)
  * Query i (position p = q_start + i) of head qh attends, with softmax of
@@ -197,7 +202,8 @@ int sparda_topk_blocks(const float* blk_scores, int32_t* idx, int rows, int nB, 
  * results of the block ranges a row is split into; no initial contents needed).
  */
 int sparda_block_sparse_attn(const void* q, const void* k, const void* v, int kv_mode,
-                             const int32_t* idx, void* out, int dtype, int B, int Hq, int Hkv,
+                             const int32_t* idx, const int32_t* slot_of, int n_slots, void* out,
+                             int dtype, int B, int Hq, int Hkv,
                              int Tq, int q_start, const int* q_pos, int T, int d, int block, int tile,
                              int k_sel, float scale, void* ws, size_t ws_bytes, void* stream);
 
@@ -218,6 +224,28 @@ int sparda_block_sparse_attn(const void* q, const void* k, const void* v, int kv
 int sparda_prefetch_blocks(const void* host_k, const void* host_v, const int32_t* idx,
                            void* stage_k, void* stage_v, int dtype, int B, int Hkv, int nB,
                            int block, int d, int k_sel, int num_workgroups, void* side_stream);
+
+/*
+ * Step 5 with the staging buffer kept as a cache of host blocks across calls
+ * (the pages fetch every selected block each step; successive selections
+ * often share blocks, and the host link is the step's bound).
+ *   slot_tags  [B, Hkv, n_slots] int32 device memory, in/out: the block each
+ *              staging slot holds, -1 = empty. Fill with -1 once before the
+ *              first call; the calls keep it up to date.
+ *   slot_of    [B, Hkv, k] int32 device memory, out: the slot holding block
+ *              idx[.., j] after the call, -1 where idx is -1 or out of range
+ *   stage_k/stage_v [B, Hkv, n_slots, block, d] device memory
+ * A selected block already held keeps its slot and is not fetched again; each
+ * other selected block takes a slot that no selected block holds (lowest
+ * slot first) and is fetched. Needs k <= n_slots <= 1024 and k <= 256. The
+ * host blocks are assumed unchanged since they were fetched. Same stream and
+ * ordering rules as sparda_prefetch_blocks; the attention then reads the
+ * blocks with kv_mode SPARDA_KV_SLOTS.
+ */
+int sparda_prefetch_blocks_cached(const void* host_k, const void* host_v, const int32_t* idx,
+                                  int32_t* slot_tags, int32_t* slot_of, void* stage_k, void* stage_v,
+                                  int dtype, int B, int Hkv, int nB, int block, int d, int k_sel,
+                                  int n_slots, int num_workgroups, void* side_stream);
 
 /* Workspace bytes the call `op` needs for these sizes (0 when none). */
 size_t sparda_workspace_bytes(int op, int B, int Hq, int Hkv, int Tq, int T, int d, int k_sel);

@@ -19,6 +19,7 @@ SPARDA_F32 = 0
 SPARDA_BF16 = 1
 KV_CACHE = 0
 KV_STAGING = 1
+KV_SLOTS = 2
 OP_SELECT_FORECAST = 1
 OP_SELECT_MULTIHEAD = 2
 OP_BLOCK_SPARSE_ATTN = 3
@@ -42,9 +43,11 @@ SIGNATURES = {
     "sparda_select_multihead": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _i, _i, _f, _vp,
                                      _sz, _vp]),
     "sparda_topk_blocks": (_i, [_vp, _vp, _i, _i, _i, _vp]),
-    "sparda_block_sparse_attn": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _i,
-                                      _f, _vp, _sz, _vp]),
+    "sparda_block_sparse_attn": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _i, _i,
+                                      _i, _i, _f, _vp, _sz, _vp]),
     "sparda_prefetch_blocks": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "sparda_prefetch_blocks_cached": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
+                                           _vp]),
     "sparda_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "sparda_status_string": (_c.c_char_p, [_i]),
     "sparda_last_error": (_c.c_char_p, []),
@@ -232,8 +235,10 @@ def topk_blocks(scores, k: int, out=None, stream=None):
 
 
 def block_sparse_attn(q, k, v, idx, T: int, q_start: int, scale: float | None = None, kv_mode: int = KV_CACHE,
-                      out=None, ws=None, stream=None, q_pos=None):
-    """GQA block-sparse attention; O [B, Hq, Tq, 128] in q's dtype."""
+                      out=None, ws=None, stream=None, q_pos=None, slot_of=None):
+    """GQA block-sparse attention; O [B, Hq, Tq, 128] in q's dtype. With
+    kv_mode KV_SLOTS, k/v are the cached staging [B, Hkv, n_slots, 64, 128]
+    and slot_of [B, Hkv, k] (int32) says where each selected block sits."""
     torch = _torch()
     B, Hq, Tq, d = q.shape
     Hkv = k.shape[1]
@@ -242,9 +247,10 @@ def block_sparse_attn(q, k, v, idx, T: int, q_start: int, scale: float | None = 
     if out is None:
         out = torch.empty_like(q)
     ws, nbytes = _workspace(ws, workspace_bytes(OP_BLOCK_SPARSE_ATTN, B, Hq, Hkv, Tq, T, k_sel), q)
-    _call("sparda_block_sparse_attn", _ptr(q), _ptr(k), _ptr(v), kv_mode, _ptr(idx), _ptr(out), _dtype_code(q), B,
-          Hq, Hkv, Tq, q_start, _positions(q_pos, B), T, d, BLOCK, TILE, k_sel, scale, _ptr(ws), nbytes,
-          _stream(q, stream))
+    n_slots = k.shape[2] if kv_mode == KV_SLOTS else 0
+    _call("sparda_block_sparse_attn", _ptr(q), _ptr(k), _ptr(v), kv_mode, _ptr(idx), _ptr(slot_of), n_slots,
+          _ptr(out), _dtype_code(q), B, Hq, Hkv, Tq, q_start, _positions(q_pos, B), T, d, BLOCK, TILE, k_sel, scale,
+          _ptr(ws), nbytes, _stream(q, stream))
     return out
 
 
@@ -258,3 +264,25 @@ def prefetch_blocks(host_k, host_v, idx, stage_k, stage_v, num_workgroups: int =
     _call("sparda_prefetch_blocks", host_k.data_ptr(), host_v.data_ptr(), _ptr(idx), _ptr(stage_k), _ptr(stage_v),
           _dtype_code(host_k), B, Hkv, T // BLOCK, BLOCK, d, k_sel, num_workgroups, _stream(idx, stream))
     return stage_k, stage_v
+
+
+def prefetch_blocks_cached(host_k, host_v, idx, slot_tags, slot_of, stage_k, stage_v, num_workgroups: int = 0,
+                           stream=None):
+    """Fetch into the cached staging [B, Hkv, n_slots, 64, 128] only the
+    blocks of idx [B, Hkv, k] that its slot_tags [B, Hkv, n_slots] (int32,
+    -1 = empty; updated) do not hold; slot_of [B, Hkv, k] (int32) receives
+    each selected block's slot."""
+    torch = _torch()
+    B, Hkv, T, d = host_k.shape
+    if not (host_k.is_pinned() and host_v.is_pinned()):
+        raise ValueError("host_k / host_v must be pinned host tensors")
+    k_sel = idx.shape[-1]
+    n_slots = stage_k.shape[2]
+    if slot_tags.dtype != torch.int32 or slot_tags.numel() != B * Hkv * n_slots:
+        raise ValueError("slot_tags must be int32 [B, Hkv, n_slots]")
+    if slot_of.dtype != torch.int32 or slot_of.numel() != B * Hkv * k_sel:
+        raise ValueError("slot_of must be int32 [B, Hkv, k]")
+    _call("sparda_prefetch_blocks_cached", host_k.data_ptr(), host_v.data_ptr(), _ptr(idx), _ptr(slot_tags),
+          _ptr(slot_of), _ptr(stage_k), _ptr(stage_v), _dtype_code(host_k), B, Hkv, T // BLOCK, BLOCK, d, k_sel,
+          n_slots, num_workgroups, _stream(idx, stream))
+    return slot_of

@@ -116,6 +116,8 @@ sparda::AttnDims attn_dims(int B, int Hq, int Hkv, int Tq, int q_start, int T, i
   a.q_start = q_start;
   a.T = T;
   a.q_pos = nullptr;
+  a.slot_of = nullptr;
+  a.n_slots = 0;
   a.nB = T / sparda::kBlock;
   a.n_tiles = (Tq + sparda::kTile - 1) / sparda::kTile;
   a.k = k;
@@ -297,7 +299,8 @@ SPARDA_EXPORT int sparda_topk_blocks(const float* blk_scores, int32_t* idx, int 
 }
 
 SPARDA_EXPORT int sparda_block_sparse_attn(const void* q, const void* k, const void* v, int kv_mode,
-                                           const int32_t* idx, void* out, int dtype, int B, int Hq, int Hkv,
+                                           const int32_t* idx, const int32_t* slot_of, int n_slots, void* out,
+                                           int dtype, int B, int Hq, int Hkv,
                                            int Tq, int q_start, const int* q_pos, int T, int d, int block, int tile,
                                            int k_sel, float scale, void* ws, size_t ws_bytes, void* stream) {
   if (int e = check_dtype(dtype)) return e;
@@ -305,10 +308,17 @@ SPARDA_EXPORT int sparda_block_sparse_attn(const void* q, const void* k, const v
   CHECK(block == sparda::kBlock, SPARDA_ERR_UNSUPPORTED, "block %d != 64", block);
   CHECK(tile == sparda::kTile, SPARDA_ERR_UNSUPPORTED, "tile %d != 64", tile);
   CHECK(std::isfinite(scale), SPARDA_ERR_INVALID_ARG, "scale is not finite");
-  CHECK(kv_mode == SPARDA_KV_CACHE || kv_mode == SPARDA_KV_STAGING, SPARDA_ERR_INVALID_ARG, "kv_mode %d", kv_mode);
+  CHECK(kv_mode == SPARDA_KV_CACHE || kv_mode == SPARDA_KV_STAGING || kv_mode == SPARDA_KV_SLOTS,
+        SPARDA_ERR_INVALID_ARG, "kv_mode %d", kv_mode);
   CHECK(k_sel >= 1 && k_sel <= T / sparda::kBlock, SPARDA_ERR_INVALID_ARG, "k = %d outside 1..nB (%d)", k_sel,
         T / sparda::kBlock);
   CHECK(kv_mode == SPARDA_KV_CACHE || Tq == 1, SPARDA_ERR_UNSUPPORTED, "staging mode is decode-only (Tq = 1)");
+  if (kv_mode == SPARDA_KV_SLOTS) {
+    CHECK(n_slots >= k_sel && n_slots <= sparda::kCacheMaxSlots, SPARDA_ERR_INVALID_ARG,
+          "n_slots = %d outside k (%d) .. %d", n_slots, k_sel, sparda::kCacheMaxSlots);
+    CHECK(B == 0 || (slot_of != nullptr && ((uintptr_t)slot_of & 3u) == 0), SPARDA_ERR_INVALID_ARG,
+          "slot_of is NULL or not 4-byte aligned");
+  }
   if (B == 0) return ok();
   CHECK_PTR(q);
   CHECK_PTR(k);
@@ -322,6 +332,8 @@ SPARDA_EXPORT int sparda_block_sparse_attn(const void* q, const void* k, const v
   if (int e = check_q_pos(q_pos, Tq)) return e;
   sparda::AttnDims ad = attn_dims(B, Hq, Hkv, Tq, q_start, T, k_sel, scale, kv_mode);
   ad.q_pos = q_pos;
+  ad.slot_of = kv_mode == SPARDA_KV_SLOTS ? slot_of : nullptr;
+  ad.n_slots = kv_mode == SPARDA_KV_SLOTS ? n_slots : 0;
   if (Tq != 1) {
     CHECK(dtype == SPARDA_BF16, SPARDA_ERR_UNSUPPORTED, "block_sparse_attn: a query chunk (Tq > 1) needs bf16 inputs");
     CHECK(ad.n_tiles <= 65535, SPARDA_ERR_UNSUPPORTED, "too many query tiles");
@@ -371,4 +383,41 @@ SPARDA_EXPORT int sparda_prefetch_blocks(const void* host_k, const void* host_v,
   return hip_status(sparda::launch_prefetch(dk, dv, idx, stage_k, stage_v, dtype == SPARDA_BF16 ? 2 : 4, B, Hkv,
                                             nB, k_sel, nwg, (hipStream_t)side_stream),
                     "prefetch_blocks launch");
+}
+
+SPARDA_EXPORT int sparda_prefetch_blocks_cached(const void* host_k, const void* host_v, const int32_t* idx,
+                                                int32_t* slot_tags, int32_t* slot_of, void* stage_k, void* stage_v,
+                                                int dtype, int B, int Hkv, int nB, int block, int d, int k_sel,
+                                                int n_slots, int num_workgroups, void* side_stream) {
+  if (int e = check_dtype(dtype)) return e;
+  CHECK(B >= 0 && Hkv >= 1, SPARDA_ERR_INVALID_ARG, "B %d / Hkv %d out of range", B, Hkv);
+  CHECK(block == sparda::kBlock, SPARDA_ERR_UNSUPPORTED, "block %d != 64", block);
+  CHECK(d == sparda::kHeadDim, SPARDA_ERR_UNSUPPORTED, "head dim %d != 128", d);
+  CHECK(nB >= 1, SPARDA_ERR_INVALID_ARG, "nB = %d < 1", nB);
+  CHECK(k_sel >= 1 && k_sel <= nB, SPARDA_ERR_INVALID_ARG, "k = %d outside 1..nB (%d)", k_sel, nB);
+  CHECK(k_sel <= sparda::kCacheMaxK, SPARDA_ERR_UNSUPPORTED, "k = %d above %d for the cached gather", k_sel,
+        sparda::kCacheMaxK);
+  CHECK(n_slots >= k_sel && n_slots <= sparda::kCacheMaxSlots, SPARDA_ERR_INVALID_ARG,
+        "n_slots = %d outside k (%d) .. %d", n_slots, k_sel, sparda::kCacheMaxSlots);
+  CHECK(num_workgroups >= 0 && num_workgroups <= 4096, SPARDA_ERR_INVALID_ARG, "num_workgroups %d outside 0..4096",
+        num_workgroups);
+  if (B == 0) return ok();
+  CHECK_PTR(host_k);
+  CHECK_PTR(host_v);
+  CHECK_PTR(stage_k);
+  CHECK_PTR(stage_v);
+  CHECK(idx != nullptr && ((uintptr_t)idx & 3u) == 0, SPARDA_ERR_INVALID_ARG, "idx is NULL or not 4-byte aligned");
+  CHECK(slot_tags != nullptr && ((uintptr_t)slot_tags & 3u) == 0, SPARDA_ERR_INVALID_ARG,
+        "slot_tags is NULL or not 4-byte aligned");
+  CHECK(slot_of != nullptr && ((uintptr_t)slot_of & 3u) == 0, SPARDA_ERR_INVALID_ARG,
+        "slot_of is NULL or not 4-byte aligned");
+  const void* dk = mapped_host_ptr(host_k);
+  const void* dv = mapped_host_ptr(host_v);
+  CHECK(dk != nullptr, SPARDA_ERR_INVALID_ARG, "host_k is not pinned host memory (use hipHostMalloc)");
+  CHECK(dv != nullptr, SPARDA_ERR_INVALID_ARG, "host_v is not pinned host memory (use hipHostMalloc)");
+  const int nwg = num_workgroups ? num_workgroups : (B < 32 ? 16 : 32);
+  return hip_status(sparda::launch_prefetch_cached(dk, dv, idx, slot_tags, slot_of, stage_k, stage_v,
+                                                   dtype == SPARDA_BF16 ? 2 : 4, B, Hkv, nB, k_sel, n_slots, nwg,
+                                                   (hipStream_t)side_stream),
+                    "prefetch_blocks_cached launch");
 }

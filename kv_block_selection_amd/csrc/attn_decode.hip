@@ -87,7 +87,7 @@ void attn_decode_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ kbuf, const uint8_t* __restrict__ vbuf,
     const int32_t* __restrict__ idx, float* __restrict__ part_o, float2* __restrict__ part_ml,
     uint8_t* __restrict__ out, int T, int nB, int k, int kv_mode, int p_all, const int* __restrict__ q_pos,
-    int hkv, int bps, int splits, float scale) {
+    int hkv, const int32_t* __restrict__ slot_of, int n_slots, int bps, int splits, float scale) {
   constexpr int E = DT<Tag>::kElems;
   constexpr int LPK = kHeadDim / E;  // lanes per key row
   constexpr int KPI = kWave / LPK;   // keys per load instruction
@@ -130,9 +130,13 @@ void attn_decode_kernel(
     const int j = j0 + (q >> 1);
     const int h = q & 1;
     const int b = idx_row[j];
-    const bool ok = b >= 0 && b < nB && b * kBlock <= p;
+    // kv_mode 2 (staging used as a block cache): the block sits in slot slot_of
+    const int sl = kv_mode == 2 ? slot_of[row * k + j] : 0;
+    const bool ok = b >= 0 && b < nB && b * kBlock <= p && (kv_mode != 2 || (sl >= 0 && sl < n_slots));
     nvalid = ok ? max(0, min(CK, p - b * kBlock - h * CK + 1)) : 0;
-    const long base = kv_mode != 0 ? (row * k + j) * (long)kBlock : row * (long)T + (long)(ok ? b : 0) * kBlock;
+    const long base = kv_mode == 1   ? (row * k + j) * (long)kBlock
+                      : kv_mode == 2 ? (row * (long)n_slots + (ok ? sl : 0)) * kBlock
+                                     : row * (long)T + (long)(ok ? b : 0) * kBlock;
     return base + h * CK;
   };
   const int nstage = 2 * (j1 - j0);
@@ -435,7 +439,8 @@ static void launch_attn_g(const void* q, const void* k, const void* v, const int
   }
   hipLaunchKernelGGL((attn_decode_kernel<Tag, G>), dim3(rows, splits), dim3(kWave), 0, s,
                      (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, part_o, part_ml,
-                     (uint8_t*)out, d.T, d.nB, d.k, d.kv_mode, d.q_start, d.q_pos, d.Hkv, bps, splits, d.scale);
+                     (uint8_t*)out, d.T, d.nB, d.k, d.kv_mode, d.q_start, d.q_pos, d.Hkv, d.slot_of, d.n_slots, bps, splits,
+                     d.scale);
   if (splits > 1 && SPARDA_COMBINE_ROW && G * (kHeadDim / 4) <= 256) {
     if (splits <= 16)
       hipLaunchKernelGGL((attn_combine_row_kernel<Tag, 16>), dim3(rows), dim3(G * (kHeadDim / 4)), 0, s, part_o,

@@ -26,6 +26,8 @@ struct AttnDims {
   float scale;
   int kv_mode;
   const int* q_pos;  // decode only: per-sequence query positions [B], or NULL
+  const int32_t* slot_of;  // kv_mode 2: staging slot of each selected block [B*Hkv, k]
+  int n_slots;             // kv_mode 2: staging slots per row
 };
 
 // compress.hip: windows [w_begin, w_end) of rows holding T tokens and W windows
@@ -68,7 +70,12 @@ hipError_t launch_attn_decode(const void* q, const void* k, const void* v, const
 hipError_t launch_attn_prefill(const void* q, const void* k, const void* v, const int32_t* idx, void* out,
                                const AttnDims& d, hipStream_t s);
 
-// prefetch.hip
+// prefetch.hip (the cached variant: k <= kCacheMaxK, k <= n_slots <= kCacheMaxSlots)
+constexpr int kCacheMaxK = 256;
+constexpr int kCacheMaxSlots = 1024;
+hipError_t launch_prefetch_cached(const void* host_k, const void* host_v, const int32_t* idx, int32_t* slot_tags,
+                                  int32_t* slot_of, void* stage_k, void* stage_v, int elem_bytes, int B, int Hkv,
+                                  int nB, int k, int n_slots, int num_workgroups, hipStream_t s);
 hipError_t launch_prefetch(const void* host_k, const void* host_v, const int32_t* idx, void* stage_k,
                            void* stage_v, int elem_bytes, int B, int Hkv, int nB, int k,
                            int num_workgroups, hipStream_t s);

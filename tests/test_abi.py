@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in kbs.SIGNATURES, f"binding lacks {n}"
@@ -96,13 +96,18 @@ def test_multihead_and_attention_validation(lib):
     assert st == 2 and b"q_pos" in lib.sparda_last_error()
     # attention: k out of range, bad kv_mode, staging with a prefill chunk
     a = lambda **kw: lib.sparda_block_sparse_attn(
-        P, P, P, kw.get("mode", 0), P, P, 1, 1, 32, 8, kw.get("Tq", 1), 4096 - kw.get("Tq", 1), kw.get("q_pos"),
-        4096, 128, 64, 64, kw.get("k", 64), 0.1, P, 1 << 30, None)
+        P, P, P, kw.get("mode", 0), P, kw.get("slot_of", P), kw.get("n_slots", 64), P, 1, 1, 32, 8, kw.get("Tq", 1),
+        4096 - kw.get("Tq", 1), kw.get("q_pos"), 4096, 128, 64, 64, kw.get("k", 64), 0.1, P, 1 << 30, None)
     assert a(k=0) == 1 and b"k = 0" in lib.sparda_last_error()
     assert a(k=65) == 1
-    assert a(mode=2) == 1 and b"kv_mode" in lib.sparda_last_error()
     assert a(mode=1, Tq=64) == 2 and b"staging" in lib.sparda_last_error()
     assert a(Tq=64, q_pos=P) == 2 and b"q_pos" in lib.sparda_last_error()
+    # cached staging: enough slots, a slot map, decode only
+    assert a(mode=3) == 1 and b"kv_mode" in lib.sparda_last_error()
+    assert a(mode=2, n_slots=63) == 1 and b"n_slots" in lib.sparda_last_error()
+    assert a(mode=2, n_slots=2048) == 1 and b"n_slots" in lib.sparda_last_error()
+    assert a(mode=2, slot_of=None) == 1 and b"slot_of" in lib.sparda_last_error()
+    assert a(mode=2, Tq=64) == 2 and b"staging" in lib.sparda_last_error()
 
 
 def test_topk_and_prefetch_validation(lib):
@@ -187,3 +192,23 @@ def test_append_kv_empty_is_a_noop(lib):
     # no compressed keys: W_cap is not used
     assert lib.sparda_append_kv(None, None, None, None, None, None, None, 1, 0, 8, 1, 4096, 0, 128, 32, 16,
                                 None) == 0
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    (dict(k_sel=300), 2, b"cached gather"),
+    (dict(n_slots=32), 1, b"n_slots"),
+    (dict(n_slots=2000), 1, b"n_slots"),
+    (dict(tags=0), 1, b"slot_tags"),
+    (dict(slot_of=P + 2), 1, b"slot_of"),
+    (dict(block=32), 2, b"block"),
+    (dict(nwg=-1), 1, b"num_workgroups"),
+])
+def test_prefetch_cached_validation(lib, args, status, needle):
+    a = dict(hk=P, hv=P, idx=P, tags=P, slot_of=P, sk=P, sv=P, dtype=1, B=2, Hkv=8, nB=2048, block=64, d=128,
+             k_sel=64, n_slots=64, nwg=0)
+    a.update(args)
+    st = lib.sparda_prefetch_blocks_cached(a["hk"], a["hv"], a["idx"], a["tags"], a["slot_of"], a["sk"], a["sv"],
+                                           a["dtype"], a["B"], a["Hkv"], a["nB"], a["block"], a["d"], a["k_sel"],
+                                           a["n_slots"], a["nwg"], None)
+    assert st == status
+    assert needle in lib.sparda_last_error()

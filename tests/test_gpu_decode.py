@@ -279,6 +279,96 @@ def test_prefetch_gather_and_staging_attention(gpu, nwg):
     assert torch.equal(o_cache.view(torch.int16), o_stage.view(torch.int16))
 
 
+def _cache_model(tags, idx_row):
+    """Expected slot assignment of one row: a selected block already held keeps
+    its (first) slot; each other selected block takes the lowest slot that no
+    selected block holds. Returns (slot_of, new tags, fetched js)."""
+    tags = list(tags)
+    slot_of = [-1] * len(idx_row)
+    keep = set()
+    for j, b in enumerate(idx_row):
+        if b >= 0 and b in tags:
+            slot_of[j] = tags.index(b)
+            keep.add(slot_of[j])
+    free = [s for s in range(len(tags)) if s not in keep]
+    fetched = [j for j, b in enumerate(idx_row) if b >= 0 and slot_of[j] < 0]
+    for m, j in enumerate(fetched):
+        slot_of[j] = free[m]
+        tags[free[m]] = idx_row[j]
+    return slot_of, tags, fetched
+
+
+@pytest.mark.parametrize("nwg,extra_slots", [(0, 0), (3, 5), (64, 6)])
+def test_prefetch_cached_across_steps(gpu, nwg, extra_slots):
+    """Four gathers into a staging buffer kept as a block cache, with selections
+    that share blocks from call to call: slot assignment and tags follow the
+    host model, every selected block's staged copy equals its host block, kept
+    blocks are not fetched again, and attention over the cache equals
+    attention over the device cache bit for bit."""
+    w = small("bf16", B=3, k=6)
+    n_slots = w.k + extra_slots
+    say("prefetch cached", nwg, n_slots)
+    Kh = sg.pinned_tensor(w.recipe("K"), w.shape("K"), DEV)
+    Vh = sg.pinned_tensor(w.recipe("V"), w.shape("V"), DEV)
+    rows = w.B * w.Hkv
+    rng = np.random.default_rng(40 + nwg)
+    first = np.stack([np.sort(rng.choice(w.nB, w.k, replace=False)) for _ in range(rows)])
+    calls = [first]
+    nxt = first.copy()
+    for r in range(rows):  # half the blocks stay
+        pool = np.setdiff1d(np.arange(w.nB), nxt[r])
+        nxt[r, w.k // 2:] = rng.choice(pool, w.k - w.k // 2, replace=False)
+    calls.append(np.sort(nxt, axis=1))
+    third = calls[-1][:, ::-1].copy()  # same blocks, other order, one unused slot
+    third[0, 1] = -1
+    calls.append(third)
+    calls.append(np.stack([np.sort(rng.choice(w.nB, w.k, replace=False)) for _ in range(rows)]))
+    tags = torch.full((w.B, w.Hkv, n_slots), -1, dtype=torch.int32, device=DEV)
+    slot_of = torch.empty((w.B, w.Hkv, w.k), dtype=torch.int32, device=DEV)
+    sk = torch.full((w.B, w.Hkv, n_slots, 64, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    sv = torch.full_like(sk, float("nan"))
+    model_tags = [[-1] * n_slots for _ in range(rows)]
+    side = torch.cuda.Stream()
+    Q = gen(w, "Q")
+    fetched_total = 0
+    for c, idx_np in enumerate(calls):
+        if c == 2:  # change the host copy of a block that stays selected: it must not be fetched again
+            b_kept = int(calls[1][0, 0])
+            Kh[0, 0, 64 * b_kept:64 * (b_kept + 1)] = 7.0
+        idx = torch.from_numpy(idx_np.reshape(w.B, w.Hkv, w.k).astype(np.int32)).to(DEV)
+        side.wait_stream(torch.cuda.current_stream())
+        gpu.prefetch_blocks_cached(Kh, Vh, idx, tags, slot_of, sk, sv, num_workgroups=nwg, stream=side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        got_slot = slot_of.view(rows, w.k).cpu().numpy()
+        got_tags = tags.view(rows, n_slots).cpu().numpy()
+        kb = sk.view(rows, n_slots, 64 * 128).view(torch.int16).cpu().numpy()
+        vb = sv.view(rows, n_slots, 64 * 128).view(torch.int16).cpu().numpy()
+        hk = Kh.view(rows, w.nB, 64 * 128).view(torch.int16).numpy()
+        hv = Vh.view(rows, w.nB, 64 * 128).view(torch.int16).numpy()
+        for r in range(rows):
+            exp_slot, model_tags[r], fetched = _cache_model(model_tags[r], list(idx_np[r]))
+            fetched_total += len(fetched)
+            np.testing.assert_array_equal(got_slot[r], exp_slot, err_msg=f"call {c} row {r}")
+            np.testing.assert_array_equal(got_tags[r], model_tags[r], err_msg=f"call {c} row {r}")
+            for j, b in enumerate(idx_np[r]):
+                if b < 0:
+                    continue
+                if c >= 2 and r == 0 and b == b_kept:  # kept since call 1: the old host data
+                    assert not np.array_equal(kb[r, exp_slot[j]], hk[r, b]), "kept block was fetched again"
+                    continue
+                np.testing.assert_array_equal(kb[r, exp_slot[j]], hk[r, b], err_msg=f"K call {c} row {r} j {j}")
+                np.testing.assert_array_equal(vb[r, exp_slot[j]], hv[r, b], err_msg=f"V call {c} row {r} j {j}")
+        if c == 1:  # attention over the cache == over the device cache (host data still untouched here)
+            idx4 = idx.view(w.B, w.Hkv, 1, w.k)
+            o_cache = gpu.block_sparse_attn(Q, Kh.to(DEV), Vh.to(DEV), idx4, w.T, w.q_start, kv_mode=gpu.KV_CACHE)
+            o_slots = gpu.block_sparse_attn(Q, sk, sv, idx4, w.T, w.q_start, kv_mode=gpu.KV_SLOTS, slot_of=slot_of)
+            torch.cuda.synchronize()
+            assert torch.equal(o_cache.view(torch.int16), o_slots.view(torch.int16))
+    say(f"  blocks fetched over 4 calls: {fetched_total} of {4 * rows * w.k} selected")
+    assert fetched_total < 4 * rows * w.k
+
+
 def test_prefetch_rejects_unpinned_host_memory(gpu):
     w = small("bf16", B=1, k=2)
     Kh = torch.zeros(w.shape("K"), dtype=torch.bfloat16)  # pageable
