@@ -23,6 +23,11 @@ every step runs in libsparda's kernels. Per step, on the caller's stream
 Layer 1's selection goes first because only it gates the gather, which is the
 long pole (it crosses the host link); all of layer 0's work then runs beside it.
 
+With ``cache_slots`` set, the staging buffer is kept as a cache of host blocks
+across steps (sparda_prefetch_blocks_cached): a block the previous steps
+already staged is not fetched again, and layer 1 attends through the slot map
+the gather writes.
+
 Hazards across steps are covered by stream order: e_idx1 of step n+1 is
 recorded after the layer-1 attention of step n was enqueued on main, so the
 prefetch of step n+1 cannot overwrite staging still being read; and main waited
@@ -32,8 +37,8 @@ prefetch reads.
 
 from __future__ import annotations
 
-from . import (BLOCK, HEAD_DIM, KV_STAGING, OP_BLOCK_SPARSE_ATTN, block_sparse_attn, prefetch_blocks,
-               select_forecast, topk_blocks, workspace_bytes)
+from . import (BLOCK, HEAD_DIM, KV_SLOTS, KV_STAGING, OP_BLOCK_SPARSE_ATTN, block_sparse_attn, prefetch_blocks,
+               prefetch_blocks_cached, select_forecast, topk_blocks, workspace_bytes)
 
 
 class LookaheadStep:
@@ -49,7 +54,7 @@ class LookaheadStep:
     """
 
     def __init__(self, B: int, Hq: int, Hkv: int, T: int, k: int, dtype, device="cuda",
-                 num_workgroups: int = 0):
+                 num_workgroups: int = 0, cache_slots: int = 0):
         import torch
         self.B, self.Hq, self.Hkv, self.T, self.k = B, Hq, Hkv, T, k
         self.device = torch.device(device)
@@ -61,8 +66,15 @@ class LookaheadStep:
         self.scores1 = torch.empty((B, Hkv, 1, nB), dtype=f32, device=dev)
         self.idx0 = torch.empty((B, Hkv, 1, k), dtype=i32, device=dev)
         self.idx1 = torch.empty((B, Hkv, 1, k), dtype=i32, device=dev)
-        self.stage_k = torch.empty((B, Hkv, k, BLOCK, HEAD_DIM), dtype=dtype, device=dev)
+        self.cache_slots = cache_slots
+        slots = cache_slots if cache_slots else k
+        self.stage_k = torch.empty((B, Hkv, slots, BLOCK, HEAD_DIM), dtype=dtype, device=dev)
         self.stage_v = torch.empty_like(self.stage_k)
+        if cache_slots:
+            if cache_slots < k:
+                raise ValueError("cache_slots must be at least k")
+            self.slot_tags = torch.full((B, Hkv, cache_slots), -1, dtype=i32, device=dev)  # all empty
+            self.slot_of = torch.empty((B, Hkv, k), dtype=i32, device=dev)
         self.out0 = torch.empty((B, Hq, 1, HEAD_DIM), dtype=dtype, device=dev)
         self.out1 = torch.empty_like(self.out0)
         # both attentions run on the main stream, one after the other: one workspace
@@ -91,8 +103,23 @@ class LookaheadStep:
 
     def prefetch(self, layer1: dict) -> None:
         """Gather layer 1's selected blocks into staging on the side stream."""
-        prefetch_blocks(layer1["host_K"], layer1["host_V"], self.idx1.view(self.B, self.Hkv, self.k), self.stage_k,
-                        self.stage_v, num_workgroups=self.num_workgroups, stream=self.side)
+        idx = self.idx1.view(self.B, self.Hkv, self.k)
+        if self.cache_slots:
+            prefetch_blocks_cached(layer1["host_K"], layer1["host_V"], idx, self.slot_tags, self.slot_of,
+                                   self.stage_k, self.stage_v, num_workgroups=self.num_workgroups, stream=self.side)
+        else:
+            prefetch_blocks(layer1["host_K"], layer1["host_V"], idx, self.stage_k, self.stage_v,
+                            num_workgroups=self.num_workgroups, stream=self.side)
+
+    def attend_next(self, layer1: dict, main) -> None:
+        """Layer 1's attention from staging on ``main``."""
+        T, q = self.T, self.T - 1
+        if self.cache_slots:
+            block_sparse_attn(layer1["Q"], self.stage_k, self.stage_v, self.idx1, T, q, kv_mode=KV_SLOTS,
+                              slot_of=self.slot_of, out=self.out1, ws=self.ws, stream=main)
+        else:
+            block_sparse_attn(layer1["Q"], self.stage_k, self.stage_v, self.idx1, T, q, kv_mode=KV_STAGING,
+                              out=self.out1, ws=self.ws, stream=main)
 
     def step(self, layer0: dict, layer1: dict, stream=None):
         """Enqueue one step; returns (out0, out1, idx0, idx1), valid once ``stream`` reaches this point."""
@@ -108,6 +135,5 @@ class LookaheadStep:
         block_sparse_attn(layer0["Q"], layer0["K"], layer0["V"], self.idx0, T, q, out=self.out0, ws=self.ws,
                           stream=main)
         main.wait_event(self.e_stage)
-        block_sparse_attn(layer1["Q"], self.stage_k, self.stage_v, self.idx1, T, q, kv_mode=KV_STAGING,
-                          out=self.out1, ws=self.ws, stream=main)
+        self.attend_next(layer1, main)
         return self.out0, self.out1, self.idx0, self.idx1

@@ -102,6 +102,44 @@ def test_lookahead_staging_equals_device_cache(gpu, nwg):
     assert torch.equal(bits(o1), bits(ref))
 
 
+def test_lookahead_with_block_cache(gpu):
+    """The two-layer step with the staging kept as a block cache: layer 1's KV
+    stays put while layer 0's Forecast changes (two input sets alternate), so
+    successive selections share some blocks. Three steps enqueued without a
+    host sync, staging poisoned at the start; each step's layer-1 output,
+    indices and scores equal those of the step with plain staging, and the
+    output equals attention on a device copy of layer 1's KV, bit for bit."""
+    from kv_block_selection_amd.lookahead import LookaheadStep
+    wa, wb = small(seed=3), small(seed=103)
+    l0a, l1 = offload_layers(wa, gpu.compress_keys, DEV)
+    l0b, _ = offload_layers(wb, gpu.compress_keys, DEV)
+    cached = LookaheadStep(wa.B, wa.Hq, wa.Hkv, wa.T, wa.k, torch.bfloat16, DEV, cache_slots=wa.k + 3)
+    plain = LookaheadStep(wa.B, wa.Hq, wa.Hkv, wa.T, wa.k, torch.bfloat16, DEV)
+    cached.stage_k.fill_(float("nan"))
+    cached.stage_v.fill_(float("nan"))
+    got, want = [], []
+    for l0 in (l0a, l0b, l0a):
+        cached.step(l0, l1)
+        got.append([t.clone() for t in (cached.out1, cached.idx1, cached.scores1)])
+        plain.step(l0, l1)
+        want.append([t.clone() for t in (plain.out1, plain.idx1, plain.scores1)])
+    Kd, Vd = l1["host_K"].to(DEV), l1["host_V"].to(DEV)
+    refs = [gpu.block_sparse_attn(l1["Q"], Kd, Vd, g[1], wa.T, wa.q_start) for g in got]
+    torch.cuda.synchronize()
+    for n, (g, w_, r) in enumerate(zip(got, want, refs)):
+        say("cached step", n)
+        assert torch.equal(g[1], w_[1]) and torch.equal(g[2], w_[2])
+        assert torch.equal(bits(g[0]), bits(w_[0]))
+        assert torch.equal(bits(g[0]), bits(r))
+    # the cache holds every block of the last selection, at the slot the map gives
+    tags = cached.slot_tags.view(wa.B * wa.Hkv, -1).cpu().numpy()
+    sel = got[-1][1].view(wa.B * wa.Hkv, -1).cpu().numpy()
+    slot = cached.slot_of.view(wa.B * wa.Hkv, -1).cpu().numpy()
+    for r in range(sel.shape[0]):
+        live = sel[r] >= 0
+        np.testing.assert_array_equal(tags[r][slot[r][live]], sel[r][live])
+
+
 def test_c4_full_size_sampled_parity(gpu):
     """The batch-64, 128K-context offload workload in the launch configuration the
     benchmark times (32 GiB of layer-1 KV in pinned host memory); the oracle
