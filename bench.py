@@ -9,6 +9,7 @@ JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --workload offload   # two-layer step, layer-1 KV in pinned host memory
     python bench.py --workload prefill   # 4096-query chunk at 128K on the matrix cores
+    python bench.py --workload pipeline  # four-layer step, layers 1-3 KV in pinned host memory
 
 Timing: W untimed steps, then K steps between two HIP events on the stream the
 kernels run on, with a device synchronisation on both sides. Input sets rotate
@@ -173,7 +174,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "offload", "prefill"), default="decode",
+    ap.add_argument("--workload", choices=("decode", "offload", "prefill", "pipeline"), default="decode",
                     help="decode: the batch-16 128K decode step (the headline line); offload: the batch-64 two-layer "
                          "step with lookahead prefetch from pinned host memory; prefill: a 4096-query chunk at 128K")
     ap.add_argument("--kernel-iters", type=int, default=100)
@@ -188,6 +189,8 @@ def main() -> int:
 
     if args.workload == "offload":
         return bench_offload(args)
+    if args.workload == "pipeline":
+        return bench_pipeline(args)
     if args.workload == "prefill":
         return bench_prefill(args)
     return bench_decode(args)
@@ -475,6 +478,74 @@ def bench_cached_gather(kbs, w, l1, st, stream, dev, steps: int = 8) -> dict:
                                             "link_GBps": round(moved / (ms * 1e-3) / 1e9, 2)}
         log(f"[bench] cached gather, {int(keep * 100)}% of blocks kept: {ms:.3f} ms, {moved} B")
     return out
+
+
+def bench_pipeline(args, L: int = 4, B: int = 16) -> int:
+    """An L-layer offloaded decode step (layer 0 in HBM, layers 1 .. L-1 with
+    K/V in pinned host memory, B=16, T=128K, top-64): each layer's blocks are
+    gathered into one of two staging buffers while the previous layer attends
+    from the other. Also times each layer's gather and the device work alone."""
+    import torch
+    import kv_block_selection_amd as kbs
+    from kv_block_selection_amd.pipeline import LayerPipeline
+    from synth import workloads as wl
+    from synth.offload import offload_stack
+
+    kbs.load()
+    w = wl.scaled(wl.C4_OFFLOAD, B=B)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating a {L}-layer stack at B={B} ({L - 1} x {B * 8 * 2 * w.T * 256 >> 30} GiB pinned host)")
+    layers = offload_stack(w, L, kbs.compress_keys, dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    pipe = LayerPipeline(L, w.B, w.Hq, w.Hkv, w.T, w.k, torch.bfloat16, dev)
+    T, q = w.T, w.q_start
+    link_bytes = (L - 1) * 2 * w.B * w.Hkv * w.k * w.block * w.d * 2
+    for i in range(args.warmup):
+        pipe.step(layers, stream)
+    torch.cuda.synchronize()
+    n = max(5, args.steps)
+    ms_step = time_loop(lambda i: pipe.step(layers, stream), n, stream)
+    sk, sv = pipe.stage[0]
+
+    def gather_only(i):
+        for l in range(1, L):
+            kbs.prefetch_blocks(layers[l]["host_K"], layers[l]["host_V"], pipe.idx[l].view(w.B, w.Hkv, w.k), sk, sv,
+                                stream=stream)
+
+    def device_only(i):
+        kbs.select_forecast(layers[0]["F_self"], layers[0]["Kc"], T, q, out=pipe.scores[0], stream=stream)
+        kbs.topk_blocks(pipe.scores[0], w.k, out=pipe.idx[0], stream=stream)
+        kbs.block_sparse_attn(layers[0]["Q"], layers[0]["K"], layers[0]["V"], pipe.idx[0], T, q, out=pipe.out[0],
+                              ws=pipe.ws, stream=stream)
+        for l in range(1, L):
+            kbs.select_forecast(layers[l - 1]["F_next"], layers[l]["Kc"], T, q, out=pipe.scores[l], stream=stream)
+            kbs.topk_blocks(pipe.scores[l], w.k, out=pipe.idx[l], stream=stream)
+            kbs.block_sparse_attn(layers[l]["Q"], sk, sv, pipe.idx[l], T, q, kv_mode=kbs.KV_STAGING,
+                                  out=pipe.out[l], ws=pipe.ws, stream=stream)
+
+    ms_gather = time_loop(gather_only, max(3, n // 4), stream)
+    ms_device = time_loop(device_only, max(3, n // 4), stream)
+    link_gbps = link_bytes / (ms_gather * 1e-3) / 1e9
+    result = {
+        "metric": f"offloaded decode steps/s/layer at 128K ctx, B={B}, {L}-layer stack with lookahead prefetch",
+        "value": round(L * 1e3 / ms_step, 3), "unit": "steps/s/layer",
+        "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{L}-layer offloaded decode stack, bf16: B={B}, T={w.T}, {w.Hq}/{w.Hkv} heads, "
+                               f"d={w.d}, top-{w.k}; layer 0 KV in HBM, layers 1-{L - 1} KV in pinned host memory",
+                   "layers": L, "B": B, "T": w.T, "top_k": w.k, "staging_buffers": 2},
+        "roofline": {"bound": "host_link", "kernel": "prefetch", "achieved": round(link_gbps, 2),
+                     "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s", "frac": round(link_gbps / HOST_LINK_PEAK_GBPS, 4),
+                     "traffic": None},
+        "link_bytes_per_step": link_bytes,
+        "gather_all_layers_ms": round(ms_gather, 4),
+        "device_work_all_layers_ms": round(ms_device, 4),
+        "serial_ms": round(ms_gather + ms_device, 4),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
 
 
 def prefill_flops(w, idx) -> dict:

@@ -36,3 +36,31 @@ def offload_layers(w, compress, device="cuda", chunk_B: int = 8):
     l1["host_K"] = sg.pinned_tensor(w.recipe("K", 1), kshape, device)
     l1["host_V"] = sg.pinned_tensor(w.recipe("V", 1), kshape, device)
     return l0, l1
+
+
+def offload_stack(w, L: int, compress, device="cuda", chunk_B: int = 8):
+    """Inputs of an L-layer offloaded decode step for workload ``w``: layer 0
+    entirely in HBM (Q, F_self, F_next, K, V, Kc); layers 1 .. L-1 with Q and
+    Kc in HBM, K/V in pinned host memory (host_K, host_V), and, except the
+    last, F_next (the layer's Forecast of the next layer's blocks)."""
+    import torch
+    layers = list(offload_layers(w, compress, device, chunk_B))
+    kshape = w.shape("K")
+    per_seq = kshape[1] * kshape[2] * kshape[3]
+    for l in range(2, L):
+        lay = {"Q": sg.tensor(w.recipe("Q", l), w.shape("Q"), device)}
+        kc = torch.empty(w.shape("Kc"), dtype=layers[0]["Kc"].dtype, device=device)
+        buf = torch.empty((min(chunk_B, w.B),) + kshape[1:], dtype=layers[0]["K"].dtype, device=device)
+        for b0 in range(0, w.B, chunk_B):
+            b1 = min(w.B, b0 + chunk_B)
+            part = buf[: b1 - b0]
+            sg.fill_(part, w.recipe("K", l), kshape, start=b0 * per_seq)
+            compress(part, out=kc[b0:b1])
+        del buf
+        lay["Kc"] = kc
+        lay["host_K"] = sg.pinned_tensor(w.recipe("K", l), kshape, device)
+        lay["host_V"] = sg.pinned_tensor(w.recipe("V", l), kshape, device)
+        layers.append(lay)
+    for l in range(1, L - 1):
+        layers[l]["F_next"] = sg.tensor(w.recipe("F", l), w.shape("F"), device)
+    return layers[:L]

@@ -177,3 +177,37 @@ def test_c4_full_size_sampled_parity(gpu):
             ref1 = oracle.attend(parity.to_f64(l1["Q"][b, qh, 0]), k1[J1], v1[J1], w.scale)
             parity.check_attention(parity.to_f64(st.out0[b, qh, 0]), ref0, parity.ATTN_ATOL_BF16)
             parity.check_attention(parity.to_f64(st.out1[b, qh, 0]), ref1, parity.ATTN_ATOL_BF16)
+
+
+@pytest.mark.parametrize("L", [2, 4])
+def test_layer_pipeline_parity(gpu, L):
+    """The L-layer step with two staging buffers used in turn: two steps
+    enqueued back to back; every layer's selection, top-k and attention
+    against the oracle, layer l >= 1 selected by layer l-1's Forecast of it."""
+    from kv_block_selection_amd.pipeline import LayerPipeline
+    from synth.offload import offload_stack
+    w = small(seed=11, B=2, k=12)
+    layers = offload_stack(w, L, gpu.compress_keys, DEV)
+    pipe = LayerPipeline(L, w.B, w.Hq, w.Hkv, w.T, w.k, torch.bfloat16, DEV)
+    for s in pipe.stage:
+        s[0].fill_(float("nan"))
+        s[1].fill_(float("nan"))
+    pipe.step(layers)
+    first = [o.clone() for o in pipe.out]
+    pipe.step(layers)  # again, without a host sync in between
+    torch.cuda.synchronize()
+    q = w.q_start
+    for l in range(L):
+        lay = layers[l]
+        f = parity.to_f64(lay["F_self"] if l == 0 else layers[l - 1]["F_next"])
+        kc = parity.to_f64(lay["Kc"])
+        ref_s = oracle.select_forecast(f, kc, w.T, q, w.scale)
+        parity.check_scores(parity.to_f64(pipe.scores[l]), ref_s)
+        idx = pipe.idx[l].cpu().numpy()
+        parity.check_topk_band(idx, ref_s, w.k)
+        K = parity.to_f64(lay["K"] if l == 0 else lay["host_K"])
+        V = parity.to_f64(lay["V"] if l == 0 else lay["host_V"])
+        ref_o = oracle.block_sparse_attention(parity.to_f64(lay["Q"]), K, V, idx, q, w.scale)
+        err = parity.check_attention(parity.to_f64(pipe.out[l]), ref_o, parity.ATTN_ATOL_BF16)
+        assert torch.equal(bits(first[l]), bits(pipe.out[l]))
+        say(f"  layer {l}: attention err {err:.2e}")
