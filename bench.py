@@ -527,6 +527,15 @@ def bench_pipeline(args, L: int = 4, B: int = 16) -> int:
 
     ms_gather = time_loop(gather_only, max(3, n // 4), stream)
     ms_device = time_loop(device_only, max(3, n // 4), stream)
+    sweep = {}
+    for nwg in (16, 32, 64, 128, 256):
+        def g(i, nwg=nwg):
+            for l in range(1, L):
+                kbs.prefetch_blocks(layers[l]["host_K"], layers[l]["host_V"], pipe.idx[l].view(w.B, w.Hkv, w.k), sk,
+                                    sv, num_workgroups=nwg, stream=stream)
+        t = time_loop(g, max(3, n // 4), stream)
+        sweep[nwg] = {"gather_ms": round(t, 4), "gather_GBps": round(link_bytes / (t * 1e-3) / 1e9, 2)}
+        log(f"[bench] gather of {L - 1} layers with {nwg} workgroups: {t:.3f} ms")
     link_gbps = link_bytes / (ms_gather * 1e-3) / 1e9
     result = {
         "metric": f"offloaded decode steps/s/layer at 128K ctx, B={B}, {L}-layer stack with lookahead prefetch",
@@ -543,6 +552,7 @@ def bench_pipeline(args, L: int = 4, B: int = 16) -> int:
         "gather_all_layers_ms": round(ms_gather, 4),
         "device_work_all_layers_ms": round(ms_device, 4),
         "serial_ms": round(ms_gather + ms_device, 4),
+        "workgroup_sweep": sweep,
     }
     print(json.dumps(result), flush=True)
     return 0

@@ -217,7 +217,7 @@ int sparda_block_sparse_attn(const void* q, const void* k, const void* v, int kv
  *                   read by the kernel over the host link
  *   idx             [B, Hkv, k] int32 device memory, -1 = leave the slot untouched
  *   stage_k/stage_v [B, Hkv, k, block, d] device memory, out: a bit copy
- *   num_workgroups  0 = library default (16 if B < 32 else 32), else 1..4096
+ *   num_workgroups  0 = library default (128), else 1..4096
  * Enqueued on side_stream; order it against producers and consumers of idx
  * and the staging buffers with events.
  */

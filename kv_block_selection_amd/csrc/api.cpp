@@ -83,6 +83,13 @@ int check_select_params(int kernel, int stride, int block, int tile, float scale
   return SPARDA_OK;
 }
 
+// Default workgroups of the host-memory gathers. The techwalker.com article
+// (section 三) sizes the grid by batch for H100 (16 below batch 32, else 32);
+// on MI355X the host link
+// saturates from 32 workgroups at any batch measured (16 and 64 sequences),
+// and 128 sits in the middle of that plateau.
+constexpr int kGatherWorkgroups = 128;
+
 int check_q_pos(const int* q_pos, int Tq) {
   if (q_pos == nullptr) return SPARDA_OK;
   CHECK(Tq == 1, SPARDA_ERR_UNSUPPORTED, "per-sequence positions (q_pos) need Tq = 1, got Tq = %d", Tq);
@@ -379,7 +386,7 @@ SPARDA_EXPORT int sparda_prefetch_blocks(const void* host_k, const void* host_v,
   const void* dv = mapped_host_ptr(host_v);
   CHECK(dk != nullptr, SPARDA_ERR_INVALID_ARG, "host_k is not pinned host memory (use hipHostMalloc)");
   CHECK(dv != nullptr, SPARDA_ERR_INVALID_ARG, "host_v is not pinned host memory (use hipHostMalloc)");
-  const int nwg = num_workgroups ? num_workgroups : (B < 32 ? 16 : 32);
+  const int nwg = num_workgroups ? num_workgroups : kGatherWorkgroups;
   return hip_status(sparda::launch_prefetch(dk, dv, idx, stage_k, stage_v, dtype == SPARDA_BF16 ? 2 : 4, B, Hkv,
                                             nB, k_sel, nwg, (hipStream_t)side_stream),
                     "prefetch_blocks launch");
@@ -415,7 +422,7 @@ SPARDA_EXPORT int sparda_prefetch_blocks_cached(const void* host_k, const void* 
   const void* dv = mapped_host_ptr(host_v);
   CHECK(dk != nullptr, SPARDA_ERR_INVALID_ARG, "host_k is not pinned host memory (use hipHostMalloc)");
   CHECK(dv != nullptr, SPARDA_ERR_INVALID_ARG, "host_v is not pinned host memory (use hipHostMalloc)");
-  const int nwg = num_workgroups ? num_workgroups : (B < 32 ? 16 : 32);
+  const int nwg = num_workgroups ? num_workgroups : kGatherWorkgroups;
   return hip_status(sparda::launch_prefetch_cached(dk, dv, idx, slot_tags, slot_of, stage_k, stage_v,
                                                    dtype == SPARDA_BF16 ? 2 : 4, B, Hkv, nB, k_sel, n_slots, nwg,
                                                    (hipStream_t)side_stream),
