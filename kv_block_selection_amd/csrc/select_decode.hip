@@ -124,27 +124,6 @@ size_t multihead_decode_ws_bytes(const SelectDims& d) {
   return align256(rows * G * d.W * sizeof(float)) + align256(rows * chunks * G * sizeof(float2));
 }
 
-__device__ __forceinline__ float block_reduce_max(float v, float* red) {
-  v = wave_max(v);
-  const int wid = threadIdx.x / kWave;
-  __syncthreads();
-  if (threadIdx.x % kWave == 0) red[wid] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int i = 1; i < (int)blockDim.x / kWave; ++i) r = fmaxf(r, red[i]);
-  return r;
-}
-__device__ __forceinline__ float block_reduce_sum(float v, float* red) {
-  v = wave_sum(v);
-  const int wid = threadIdx.x / kWave;
-  __syncthreads();
-  if (threadIdx.x % kWave == 0) red[wid] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int i = 1; i < (int)blockDim.x / kWave; ++i) r += red[i];
-  return r;
-}
-
 template <typename Tag, int G>
 __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __restrict__ q,
                                                            const uint8_t* __restrict__ kc, MhWs ws,
@@ -152,8 +131,9 @@ __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __rest
                                                            int hkv, int T, int chunks, float scale) {
   using R = RowGeom<Tag>;
   constexpr int ITER = kMhChunk / R::SLOTS;
+  static_assert(kMhChunk == 4 * kWave, "one window per thread, four waves");
   __shared__ float s_log[G][kMhChunk];
-  __shared__ float red[4];
+  __shared__ float red_m[4][G], red_z[4][G];
 
   const long row = blockIdx.y;  // (b, kv head)
   if (q_pos != nullptr) n_vis = visible_windows(row_position(q_pos, row, hkv, 0, T), W);
@@ -184,16 +164,36 @@ __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __rest
     }
   }
   __syncthreads();
+  // Chunk statistics of all G heads at once: wave max and sum per head, one
+  // LDS exchange of the four waves' partials each (the waves' partial sums
+  // are added in wave order).
   const int t = threadIdx.x;
+  const int wid = t / kWave;
   const int w = w0 + t;
+  float x[G], m[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float x = s_log[g][t];
-    const float m = block_reduce_max(x, red);
-    const float e = (m == -INFINITY || x == -INFINITY) ? 0.f : fast_exp(x - m);
-    const float z = block_reduce_sum(e, red);
-    if (w < W) ws.logits[(row * G + g) * W + w] = x;
-    if (t == 0) ws.stats[(row * chunks + chunk) * G + g] = make_float2(m, z);
+    x[g] = s_log[g][t];
+    m[g] = wave_max(x[g]);
+    if (w < W) ws.logits[(row * G + g) * W + w] = x[g];
+  }
+  if (t % kWave == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) red_m[wid][g] = m[g];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = fmaxf(fmaxf(red_m[0][g], red_m[1][g]), fmaxf(red_m[2][g], red_m[3][g]));
+    const float e = (m[g] == -INFINITY || x[g] == -INFINITY) ? 0.f : fast_exp(x[g] - m[g]);
+    const float z = wave_sum(e);
+    if (t % kWave == 0) red_z[wid][g] = z;
+  }
+  __syncthreads();
+  if (t < G) {
+    const float mt = fmaxf(fmaxf(red_m[0][t], red_m[1][t]), fmaxf(red_m[2][t], red_m[3][t]));
+    const float z = ((red_z[0][t] + red_z[1][t]) + red_z[2][t]) + red_z[3][t];
+    ws.stats[(row * chunks + chunk) * G + t] = make_float2(mt, z);
   }
 }
 
