@@ -4,15 +4,16 @@
 // gain comes from the cheaper selection itself).
 //
 // A dense contraction: per KV head, F [Tq x 128] times K_cmp^T [128 x W], so it
-// runs on the matrix cores (v_mfma_f32_32x32x16_bf16). One 256-thread
-// workgroup owns one (sequence, KV head, query tile) and sweeps the windows in
-// chunks of 128:
+// runs on the matrix cores (v_mfma_f32_32x32x16_bf16). One workgroup owns one
+// (sequence, KV head) and TPW query tiles (two when the chunk has two or more;
+// 4 waves per tile), and sweeps the windows in chunks of 128, so each chunk
+// staged in LDS serves every tile of the workgroup:
 //   * the chunk's compressed keys (128 x 256 B) land in LDS through direct
 //     global->LDS loads, double-buffered; each 16-byte granule of row r is
 //     stored at position (granule ^ (r & 15)), so the fragment reads of 16
 //     consecutive rows hit 16 different bank groups;
-//   * wave w computes the 64 x 32 score block of windows [32w, 32w + 32) for
-//     the tile's 64 queries, with the tile's F fragments held in registers;
+//   * wave w computes the 64 x 32 score block of windows [32 (w % 4), +32) for
+//     the 64 queries of tile w / 4, with that tile's F fragments in registers;
 //   * each window's score is masked where the window is not visible to the
 //     query, and reduced to the max over the tile's queries (in-lane, then one
 //     swap of the two lane halves);
@@ -23,17 +24,20 @@
 
 namespace sparda {
 
-__global__ __launch_bounds__(256) void fsel_prefill_kernel(const uint8_t* __restrict__ f,
-                                                           const uint8_t* __restrict__ kc,
-                                                           float* __restrict__ scores, int Tq,
-                                                           int q_start, int W, int nB, int n_tiles,
-                                                           float scale) {
+template <int TPW>
+__global__ __launch_bounds__(256 * TPW) void fsel_prefill_kernel(const uint8_t* __restrict__ f,
+                                                                 const uint8_t* __restrict__ kc,
+                                                                 float* __restrict__ scores, int Tq,
+                                                                 int q_start, int W, int nB, int n_tiles,
+                                                                 float scale) {
+  constexpr int NWAVES = 4 * TPW;
   __shared__ __attribute__((aligned(16))) uint8_t s_kc[2][kChunkBytes];
-  __shared__ float s_cmax[kChunkW + 1];  // [0] = carry: last window of the previous chunk
+  __shared__ float s_cmax[TPW][kChunkW + 1];  // [t][0] = carry: last window of the previous chunk
 
   const long row = blockIdx.x;  // (b, h): rows on the fast axis share an XCD
-  const int tile = blockIdx.y;
-  const int wave = threadIdx.x / kWave;
+  const int tl = threadIdx.x / (4 * kWave);  // this wave's tile in the workgroup
+  const int tile = blockIdx.y * TPW + tl;    // may be n_tiles (an odd count's last workgroup): no output
+  const int wave = (threadIdx.x / kWave) % 4;
   const int lane = threadIdx.x % kWave;
   const int half = lane >> 5;
   const int l32 = lane & 31;
@@ -60,14 +64,14 @@ __global__ __launch_bounds__(256) void fsel_prefill_kernel(const uint8_t* __rest
     }
 
   const int nchunks = (W + kChunkW - 1) / kChunkW;
-  if (threadIdx.x == 0) s_cmax[0] = -INFINITY;
-  load_chunk_lds<4>(kc_row, W, 0, s_kc[0]);
+  if (threadIdx.x < TPW) s_cmax[threadIdx.x][0] = -INFINITY;
+  load_chunk_lds<NWAVES>(kc_row, W, 0, s_kc[0]);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
   // The next chunk's loads go out at the top of an iteration and are awaited
   // with a full drain after this chunk's compute.
   for (int c = 0; c < nchunks; ++c) {
-    if (c + 1 < nchunks) load_chunk_lds<4>(kc_row, W, (c + 1) * kChunkW, s_kc[(c + 1) & 1]);
+    if (c + 1 < nchunks) load_chunk_lds<NWAVES>(kc_row, W, (c + 1) * kChunkW, s_kc[(c + 1) & 1]);
     const uint8_t* tileb = s_kc[c & 1];
     f32x16 acc0 = {}, acc1 = {};
     const int wr = 32 * wave + l32;  // this lane's window row in the chunk
@@ -86,29 +90,37 @@ __global__ __launch_bounds__(256) void fsel_prefill_kernel(const uint8_t* __rest
       if (w < vis_lim[1][r]) cm = fmaxf(cm, acc1[r] * scale);
     }
     cm = max32(cm);
-    if (half == 0) s_cmax[1 + wr] = cm;
+    if (half == 0) s_cmax[tl][1 + wr] = cm;
     __syncthreads();
     const int t = threadIdx.x;
-    if (t < kChunkW / 4) {
-      const int b = c * (kChunkW / 4) + t;
-      if (b < nB) {
-        float m = s_cmax[4 * t];
+    if (t < TPW * (kChunkW / 4)) {  // 32 blocks per tile
+      const int ot = t / (kChunkW / 4), bt = t % (kChunkW / 4);
+      const int b = c * (kChunkW / 4) + bt;
+      const int otile = blockIdx.y * TPW + ot;
+      if (b < nB && otile < n_tiles) {
+        float m = s_cmax[ot][4 * bt];
 #pragma unroll
-        for (int j = 1; j < 5; ++j) m = fmaxf(m, s_cmax[4 * t + j]);
-        scores[(row * n_tiles + tile) * (long)nB + b] = m;
+        for (int j = 1; j < 5; ++j) m = fmaxf(m, s_cmax[ot][4 * bt + j]);
+        scores[(row * n_tiles + otile) * (long)nB + b] = m;
       }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the next chunk has landed
     __syncthreads();
-    if (t == 0) s_cmax[0] = s_cmax[kChunkW];
+    if (t < TPW) s_cmax[t][0] = s_cmax[t][kChunkW];
   }
 }
 
 hipError_t launch_select_forecast_prefill(const void* f, const void* kc, float* scores, const SelectDims& d,
                                           hipStream_t s) {
-  dim3 grid(d.B * d.Hkv, d.n_tiles);
-  hipLaunchKernelGGL(fsel_prefill_kernel, grid, dim3(256), 0, s, (const uint8_t*)f, (const uint8_t*)kc, scores,
-                     d.Tq, d.q_start, d.W, d.nB, d.n_tiles, d.scale);
+  if (d.n_tiles >= 2) {
+    dim3 grid(d.B * d.Hkv, (d.n_tiles + 1) / 2);
+    hipLaunchKernelGGL(fsel_prefill_kernel<2>, grid, dim3(512), 0, s, (const uint8_t*)f, (const uint8_t*)kc, scores,
+                       d.Tq, d.q_start, d.W, d.nB, d.n_tiles, d.scale);
+  } else {
+    dim3 grid(d.B * d.Hkv, d.n_tiles);
+    hipLaunchKernelGGL(fsel_prefill_kernel<1>, grid, dim3(256), 0, s, (const uint8_t*)f, (const uint8_t*)kc, scores,
+                       d.Tq, d.q_start, d.W, d.nB, d.n_tiles, d.scale);
+  }
   return hipGetLastError();
 }
 
