@@ -54,6 +54,8 @@ __global__ __launch_bounds__(256 * TPW) void fsel_prefill_kernel(const uint8_t* 
     for (int s = 0; s < 8; ++s) fa[m][s] = load16(src + s * 32);
   }
   // visibility: window w is visible to query position p iff 16 w + 31 <= p
+  // the tile's first query sees the fewest windows
+  const int vis_min = visible_windows(q_start + min(q0, Tq - 1), W);
   int vis_lim[2][16];  // per accumulator row: number of visible windows
 #pragma unroll
   for (int m = 0; m < 2; ++m)
@@ -83,13 +85,23 @@ __global__ __launch_bounds__(256 * TPW) void fsel_prefill_kernel(const uint8_t* 
     }
     // column (window) max over the tile's visible queries
     const int w = c * kChunkW + wr;
-    float cm = -INFINITY;
+    float cm;
+    if (scale > 0.f && c * kChunkW + 32 * wave + 31 < vis_min) {
+      // every window of this wave is visible to every query of the tile, and
+      // with scale > 0 the max of the scaled scores is the scaled max (same bits)
+      float a = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (w < vis_lim[0][r]) cm = fmaxf(cm, acc0[r] * scale);
-      if (w < vis_lim[1][r]) cm = fmaxf(cm, acc1[r] * scale);
+      for (int r = 0; r < 16; ++r) a = fmaxf(a, fmaxf(acc0[r], acc1[r]));
+      cm = max32(a) * scale;
+    } else {
+      cm = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (w < vis_lim[0][r]) cm = fmaxf(cm, acc0[r] * scale);
+        if (w < vis_lim[1][r]) cm = fmaxf(cm, acc1[r] * scale);
+      }
+      cm = max32(cm);
     }
-    cm = max32(cm);
     if (half == 0) s_cmax[tl][1 + wr] = cm;
     __syncthreads();
     const int t = threadIdx.x;
