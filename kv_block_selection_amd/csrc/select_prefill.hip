@@ -9,9 +9,12 @@
 // 4 waves per tile), and sweeps the windows in chunks of 128, so each chunk
 // staged in LDS serves every tile of the workgroup:
 //   * the chunk's compressed keys (128 x 256 B) land in LDS through direct
-//     global->LDS loads, double-buffered; each 16-byte granule of row r is
+//     global->LDS loads, issued two chunks ahead into three buffers (one ahead
+//     into two for a one-tile workgroup); each 16-byte granule of row r is
 //     stored at position (granule ^ (r & 15)), so the fragment reads of 16
-//     consecutive rows hit 16 different bank groups;
+//     consecutive rows hit 16 different bank groups. Each wave waits for its
+//     own loads (vmcnt) and the barriers wait for LDS writes only, so the
+//     loads of later chunks stay in flight across them;
 //   * wave w computes the 64 x 32 score block of windows [32 (w % 4), +32) for
 //     the 64 queries of tile w / 4, with that tile's F fragments in registers;
 //   * each window's score is masked where the window is not visible to the
@@ -24,6 +27,10 @@
 
 namespace sparda {
 
+// Barrier that publishes this wave's LDS writes but leaves its global->LDS
+// loads in flight (a fence here would wait for those too).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int TPW>
 __global__ __launch_bounds__(256 * TPW) void fsel_prefill_kernel(const uint8_t* __restrict__ f,
                                                                  const uint8_t* __restrict__ kc,
@@ -31,7 +38,9 @@ __global__ __launch_bounds__(256 * TPW) void fsel_prefill_kernel(const uint8_t* 
                                                                  int q_start, int W, int nB, int n_tiles,
                                                                  float scale) {
   constexpr int NWAVES = 4 * TPW;
-  __shared__ __attribute__((aligned(16))) uint8_t s_kc[2][kChunkBytes];
+  constexpr int NBUF = TPW == 2 ? 3 : 2;  // chunk buffers; loads go NBUF - 1 chunks ahead
+  constexpr int LPC = kChunkBytes / (NWAVES * kWave * 16);  // direct loads per wave per chunk
+  __shared__ __attribute__((aligned(16))) uint8_t s_kc[NBUF][kChunkBytes];
   __shared__ float s_cmax[TPW][kChunkW + 1];  // [t][0] = carry: last window of the previous chunk
 
   const long row = blockIdx.x;  // (b, h): rows on the fast axis share an XCD
@@ -67,14 +76,16 @@ __global__ __launch_bounds__(256 * TPW) void fsel_prefill_kernel(const uint8_t* 
 
   const int nchunks = (W + kChunkW - 1) / kChunkW;
   if (threadIdx.x < TPW) s_cmax[threadIdx.x][0] = -INFINITY;
-  load_chunk_lds<NWAVES>(kc_row, W, 0, s_kc[0]);
+  for (int a = 0; a < NBUF - 1 && a < nchunks; ++a) load_chunk_lds<NWAVES>(kc_row, W, a * kChunkW, s_kc[a]);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
-  // The next chunk's loads go out at the top of an iteration and are awaited
-  // with a full drain after this chunk's compute.
+  // Chunk c + NBUF - 1 goes out at the top of iteration c, into the buffer
+  // that chunk c - 1 used (every wave left it at the previous barrier).
+  int bc = 0;  // buffer of chunk c
   for (int c = 0; c < nchunks; ++c) {
-    if (c + 1 < nchunks) load_chunk_lds<NWAVES>(kc_row, W, (c + 1) * kChunkW, s_kc[(c + 1) & 1]);
-    const uint8_t* tileb = s_kc[c & 1];
+    const int bl = bc == 0 ? NBUF - 1 : bc - 1;  // buffer for chunk c + NBUF - 1
+    if (c + NBUF - 1 < nchunks) load_chunk_lds<NWAVES>(kc_row, W, (c + NBUF - 1) * kChunkW, s_kc[bl]);
+    const uint8_t* tileb = s_kc[bc];
     f32x16 acc0 = {}, acc1 = {};
     const int wr = 32 * wave + l32;  // this lane's window row in the chunk
 #pragma unroll
@@ -103,7 +114,7 @@ __global__ __launch_bounds__(256 * TPW) void fsel_prefill_kernel(const uint8_t* 
       cm = max32(cm);
     }
     if (half == 0) s_cmax[tl][1 + wr] = cm;
-    __syncthreads();
+    lds_barrier();
     const int t = threadIdx.x;
     if (t < TPW * (kChunkW / 4)) {  // 32 blocks per tile
       const int ot = t / (kChunkW / 4), bt = t % (kChunkW / 4);
@@ -116,9 +127,16 @@ __global__ __launch_bounds__(256 * TPW) void fsel_prefill_kernel(const uint8_t* 
         scores[(row * n_tiles + otile) * (long)nB + b] = m;
       }
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the next chunk has landed
-    __syncthreads();
+    // chunk c + 1 has landed: loads complete in order, so at most LPC
+    // outstanding (the score store above counts too) leaves only chunk c + 2's
+    if (NBUF == 3 && c + 2 < nchunks) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPC));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    lds_barrier();
     if (t < TPW) s_cmax[t][0] = s_cmax[t][kChunkW];
+    bc = bc == NBUF - 1 ? 0 : bc + 1;
   }
 }
 
