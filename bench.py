@@ -489,7 +489,7 @@ def bench_pipeline(args, L: int = 4, B: int = 16) -> int:
     import kv_block_selection_amd as kbs
     from kv_block_selection_amd.pipeline import LayerPipeline
     from synth import workloads as wl
-    from synth.offload import offload_stack
+    from synth.offload import offload_stack, set_lookahead
 
     kbs.load()
     w = wl.scaled(wl.C4_OFFLOAD, B=B)
@@ -536,6 +536,20 @@ def bench_pipeline(args, L: int = 4, B: int = 16) -> int:
         t = time_loop(g, max(3, n // 4), stream)
         sweep[nwg] = {"gather_ms": round(t, 4), "gather_GBps": round(link_bytes / (t * 1e-3) / 1e9, 2)}
         log(f"[bench] gather of {L - 1} layers with {nwg} workgroups: {t:.3f} ms")
+    # lookahead of more than one layer: layer l's Forecast picks layer l + D's
+    # blocks, D + 1 staging buffers (inputs: the same stack plus those vectors)
+    depth_sweep = {1: {"ms_per_step": round(ms_step, 4), "staging_buffers": len(pipe.stage)}}
+    del pipe
+    for D in (2, 3):
+        set_lookahead(w, layers, D, dev)
+        pd = LayerPipeline(L, w.B, w.Hq, w.Hkv, w.T, w.k, torch.bfloat16, dev, depth=D)
+        for i in range(max(2, args.warmup // 4)):
+            pd.step(layers, stream)
+        torch.cuda.synchronize()
+        t = time_loop(lambda i: pd.step(layers, stream), max(3, n // 2), stream)
+        depth_sweep[D] = {"ms_per_step": round(t, 4), "staging_buffers": len(pd.stage)}
+        log(f"[bench] lookahead depth {D}: {t:.3f} ms per step")
+        del pd
     link_gbps = link_bytes / (ms_gather * 1e-3) / 1e9
     result = {
         "metric": f"offloaded decode steps/s/layer at 128K ctx, B={B}, {L}-layer stack with lookahead prefetch",
@@ -553,6 +567,7 @@ def bench_pipeline(args, L: int = 4, B: int = 16) -> int:
         "device_work_all_layers_ms": round(ms_device, 4),
         "serial_ms": round(ms_gather + ms_device, 4),
         "workgroup_sweep": sweep,
+        "lookahead_depth_sweep": depth_sweep,
     }
     print(json.dumps(result), flush=True)
     return 0

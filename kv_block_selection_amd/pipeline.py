@@ -1,5 +1,5 @@
 """A decode step over L layers whose KV (all but layer 0's) sits in pinned host
-memory, with lookahead prefetch into two staging buffers used in turn.
+memory, with lookahead prefetch into staging buffers used in turn.
 
 SparDA's runtime (bittide.aicompass.dev summary post, paragraphs on the
 decoupled Forecast and on prefetching over a separate stream; techwalker.com
@@ -25,6 +25,22 @@ for e_idx[l+1], recorded on main after that attention was enqueued. The next
 step's first gather likewise follows this step's last attention, and main has
 waited for every gather of this step before the next step's top-k rewrites the
 indices those gathers read.
+
+Lookahead of ``depth`` D > 1 layers (10100.com commentary, section 硅基观点,
+names a Forecast that looks several layers ahead instead of one as a next step):
+layer l's Forecast picks the blocks of layer l+D, so D gathers can be in
+flight while a layer attends, in D+1 staging buffers used in turn. The layers
+1 .. D have no layer D below them in the step; layer 0's input forecasts all
+of them (F_ahead[j-1] for layer j), and their selections and gathers go first:
+
+  main: for j = 1 .. D: select(F_0->j, K~j) -> idx[j]; side: gather j -> staging j % (D+1)
+  main: select(F_0 self, K~0) -> idx0; attention of layer 0 from HBM
+  for l = 1 .. L-1:
+    main: select(F_l->l+D, K~l+D) -> idx[l+D]; side: gather -> staging (l+D) % (D+1)   (l+D < L)
+    main: wait e_stage[l]; attention of layer l from staging l % (D+1)
+
+Staging (l+D) % (D+1) is the buffer of layer l-1, so the hazard argument above
+holds for every D.
 """
 
 from __future__ import annotations
@@ -43,11 +59,14 @@ class LayerPipeline:
     """
 
     def __init__(self, L: int, B: int, Hq: int, Hkv: int, T: int, k: int, dtype, device="cuda",
-                 num_workgroups: int = 0):
+                 num_workgroups: int = 0, depth: int = 1):
         import torch
         if L < 1:
             raise ValueError("L must be at least 1")
+        if depth < 1:
+            raise ValueError("depth must be at least 1")
         self.L, self.B, self.Hq, self.Hkv, self.T, self.k = L, B, Hq, Hkv, T, k
+        self.depth = depth
         self.device = torch.device(device)
         self.num_workgroups = num_workgroups
         dev = self.device
@@ -55,7 +74,7 @@ class LayerPipeline:
         self.scores = [torch.empty((B, Hkv, 1, nB), dtype=torch.float32, device=dev) for _ in range(L)]
         self.idx = [torch.empty((B, Hkv, 1, k), dtype=torch.int32, device=dev) for _ in range(L)]
         self.out = [torch.empty((B, Hq, 1, HEAD_DIM), dtype=dtype, device=dev) for _ in range(L)]
-        n_stage = min(2, L - 1)  # one buffer when only layer 1 is offloaded
+        n_stage = min(depth + 1, L - 1)  # never more than the offloaded layers
         self.stage = [(torch.empty((B, Hkv, k, BLOCK, HEAD_DIM), dtype=dtype, device=dev),
                        torch.empty((B, Hkv, k, BLOCK, HEAD_DIM), dtype=dtype, device=dev)) for _ in range(n_stage)]
         self.ws = torch.empty(workspace_bytes(OP_BLOCK_SPARSE_ATTN, B, Hq, Hkv, 1, T, k), dtype=torch.uint8,
@@ -67,6 +86,15 @@ class LayerPipeline:
     def _select(self, f, kc, l: int, main) -> None:
         select_forecast(f, kc, self.T, self.T - 1, out=self.scores[l], stream=main)
         topk_blocks(self.scores[l], self.k, out=self.idx[l], stream=main)
+
+    def _forecast(self, layers: list, src: int, dst: int):
+        """Layer src's Forecast vector of layer dst's blocks."""
+        fa = layers[src].get("F_ahead")
+        if fa is None:  # one layer ahead
+            if dst != src + 1:
+                raise ValueError(f"layer {src} has no F_ahead for lookahead depth {self.depth}")
+            return layers[src]["F_next"]
+        return fa[dst - 1] if src == 0 else fa
 
     def _gather(self, layer: dict, l: int, main) -> None:
         self.e_idx[l].record(main)
@@ -83,17 +111,17 @@ class LayerPipeline:
         if len(layers) != self.L:
             raise ValueError(f"expected {self.L} layers, got {len(layers)}")
         main = stream if stream is not None else torch.cuda.current_stream(self.device)
-        T, q = self.T, self.T - 1
+        T, q, D = self.T, self.T - 1, self.depth
         l0 = layers[0]
-        if self.L > 1:
-            self._select(l0["F_next"], layers[1]["Kc"], 1, main)
-            self._gather(layers[1], 1, main)
+        for j in range(1, min(D, self.L - 1) + 1):
+            self._select(self._forecast(layers, 0, j), layers[j]["Kc"], j, main)
+            self._gather(layers[j], j, main)
         self._select(l0["F_self"], l0["Kc"], 0, main)
         block_sparse_attn(l0["Q"], l0["K"], l0["V"], self.idx[0], T, q, out=self.out[0], ws=self.ws, stream=main)
         for l in range(1, self.L):
-            if l + 1 < self.L:
-                self._select(layers[l]["F_next"], layers[l + 1]["Kc"], l + 1, main)
-                self._gather(layers[l + 1], l + 1, main)
+            if l + D < self.L:
+                self._select(self._forecast(layers, l, l + D), layers[l + D]["Kc"], l + D, main)
+                self._gather(layers[l + D], l + D, main)
             main.wait_event(self.e_stage[l])
             sk, sv = self.stage[l % len(self.stage)]
             block_sparse_attn(layers[l]["Q"], sk, sv, self.idx[l], T, q, kv_mode=KV_STAGING, out=self.out[l],

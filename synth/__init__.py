@@ -49,6 +49,7 @@ TAG_F = 4
 TAG_K_OFFSET = 5
 TAG_V_OFFSET = 6
 TAG_F_SELF = 7
+TAG_F_AHEAD = 8  # Forecast of the layer j > 1 ahead: tag 8 + (j - 2), j <= 9
 LAYER_TAG_STRIDE = 16  # layer l uses tag + 16 * l
 
 

@@ -38,11 +38,15 @@ def offload_layers(w, compress, device="cuda", chunk_B: int = 8):
     return l0, l1
 
 
-def offload_stack(w, L: int, compress, device="cuda", chunk_B: int = 8):
+def offload_stack(w, L: int, compress, device="cuda", chunk_B: int = 8, depth: int = 1):
     """Inputs of an L-layer offloaded decode step for workload ``w``: layer 0
     entirely in HBM (Q, F_self, F_next, K, V, Kc); layers 1 .. L-1 with Q and
     Kc in HBM, K/V in pinned host memory (host_K, host_V), and, except the
-    last, F_next (the layer's Forecast of the next layer's blocks)."""
+    last, F_next (the layer's Forecast of the next layer's blocks).
+
+    With ``depth`` > 1 (Forecasts that look that many layers ahead) layer 0
+    also gets F_ahead, the list of its Forecasts of layers 1 .. depth, and
+    layer l >= 1 gets F_ahead, its Forecast of layer l + depth (if any)."""
     import torch
     layers = list(offload_layers(w, compress, device, chunk_B))
     kshape = w.shape("K")
@@ -63,4 +67,21 @@ def offload_stack(w, L: int, compress, device="cuda", chunk_B: int = 8):
         layers.append(lay)
     for l in range(1, L - 1):
         layers[l]["F_next"] = sg.tensor(w.recipe("F", l), w.shape("F"), device)
-    return layers[:L]
+    layers = layers[:L]
+    if depth > 1:
+        set_lookahead(w, layers, depth, device)
+    return layers
+
+
+def set_lookahead(w, layers: list, depth: int, device="cuda") -> None:
+    """Give a stack the Forecast vectors of lookahead ``depth`` > 1 (replacing
+    any earlier F_ahead): layer 0's F_ahead lists its Forecasts of layers
+    1 .. depth (the first is F_next), layer l >= 1's is its Forecast of layer
+    l + depth."""
+    L = len(layers)
+    for lay in layers:
+        lay.pop("F_ahead", None)
+    layers[0]["F_ahead"] = [layers[0]["F_next"]] + [sg.tensor(w.recipe("F", 0, j), w.shape("F"), device)
+                                                    for j in range(2, min(depth, L - 1) + 1)]
+    for l in range(1, L - depth):
+        layers[l]["F_ahead"] = sg.tensor(w.recipe("F", l, depth), w.shape("F"), device)

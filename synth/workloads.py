@@ -10,7 +10,7 @@ from __future__ import annotations
 
 from dataclasses import dataclass, field
 
-from . import (LAYER_TAG_STRIDE, TAG_F, TAG_F_SELF, TAG_K, TAG_K_OFFSET, TAG_Q, TAG_V, TAG_V_OFFSET,
+from . import (LAYER_TAG_STRIDE, TAG_F, TAG_F_AHEAD, TAG_F_SELF, TAG_K, TAG_K_OFFSET, TAG_Q, TAG_V, TAG_V_OFFSET,
                Recipe)
 
 INV_SQRT_128 = 0.08838834764831845  # 1/sqrt(128); rounded to fp32 where applied
@@ -70,12 +70,18 @@ class Workload:
             return (self.B, self.Hkv, self.W, self.d)
         raise KeyError(name)
 
-    def recipe(self, name: str, layer: int = 0) -> Recipe:
+    def recipe(self, name: str, layer: int = 0, ahead: int = 1) -> Recipe:
+        """``ahead`` (for "F" only): how many layers ahead the Forecast looks."""
         tags = {"Q": TAG_Q, "K": TAG_K, "V": TAG_V, "F": TAG_F, "F_self": TAG_F_SELF}
         off = {"K": TAG_K_OFFSET, "V": TAG_V_OFFSET}
         shift = LAYER_TAG_STRIDE * layer
         offset_tag = off[name] + shift if (self.block_offsets and name in off) else None
-        return Recipe(seed=self.seed, tag=tags[name] + shift, dtype=self.dtype, scale=self.value_scale,
+        tag = tags[name]
+        if name == "F" and ahead != 1:
+            if not 2 <= ahead <= 9:
+                raise ValueError("a Forecast looks 1 to 9 layers ahead")
+            tag = TAG_F_AHEAD + ahead - 2
+        return Recipe(seed=self.seed, tag=tag + shift, dtype=self.dtype, scale=self.value_scale,
                       offset_tag=offset_tag, offset_std=0.5, block=self.block)
 
 

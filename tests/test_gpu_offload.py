@@ -179,16 +179,27 @@ def test_c4_full_size_sampled_parity(gpu):
             parity.check_attention(parity.to_f64(st.out1[b, qh, 0]), ref1, parity.ATTN_ATOL_BF16)
 
 
-@pytest.mark.parametrize("L", [2, 4])
-def test_layer_pipeline_parity(gpu, L):
-    """The L-layer step with two staging buffers used in turn: two steps
-    enqueued back to back; every layer's selection, top-k and attention
-    against the oracle, layer l >= 1 selected by layer l-1's Forecast of it."""
+@pytest.mark.parametrize("L,depth", [(2, 1), (4, 1), (4, 2), (5, 3), (3, 5)])
+def test_layer_pipeline_parity(gpu, L, depth):
+    """The L-layer step with lookahead of ``depth`` layers and min(depth + 1,
+    L - 1) staging buffers used in turn: two steps enqueued back to back;
+    every layer's selection, top-k and attention against the oracle. Layer l
+    is selected by layer l - depth's Forecast of it, layers 1 .. depth by
+    layer 0's."""
     from kv_block_selection_amd.pipeline import LayerPipeline
     from synth.offload import offload_stack
     w = small(seed=11, B=2, k=12)
-    layers = offload_stack(w, L, gpu.compress_keys, DEV)
-    pipe = LayerPipeline(L, w.B, w.Hq, w.Hkv, w.T, w.k, torch.bfloat16, DEV)
+    layers = offload_stack(w, L, gpu.compress_keys, DEV, depth=depth)
+    pipe = LayerPipeline(L, w.B, w.Hq, w.Hkv, w.T, w.k, torch.bfloat16, DEV, depth=depth)
+    assert len(pipe.stage) == min(depth + 1, L - 1)
+
+    def forecast_of(l):
+        if l == 0:
+            return layers[0]["F_self"]
+        src = max(0, l - depth)
+        if depth == 1:
+            return layers[src]["F_next"]
+        return layers[0]["F_ahead"][l - 1] if src == 0 else layers[src]["F_ahead"]
     for s in pipe.stage:
         s[0].fill_(float("nan"))
         s[1].fill_(float("nan"))
@@ -199,7 +210,7 @@ def test_layer_pipeline_parity(gpu, L):
     q = w.q_start
     for l in range(L):
         lay = layers[l]
-        f = parity.to_f64(lay["F_self"] if l == 0 else layers[l - 1]["F_next"])
+        f = parity.to_f64(forecast_of(l))
         kc = parity.to_f64(lay["Kc"])
         ref_s = oracle.select_forecast(f, kc, w.T, q, w.scale)
         parity.check_scores(parity.to_f64(pipe.scores[l]), ref_s)

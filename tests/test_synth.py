@@ -69,3 +69,20 @@ def test_workload_geometry():
     c5 = workloads.C5_PREFILL
     assert (c5.n_tiles, c5.q_start + c5.Tq) == (64, c5.T)
     assert workloads.C1_TINY.W == 255 and workloads.C2_DECODE_32K.W == 2047
+
+
+def test_layer_and_lookahead_tags_are_distinct():
+    # every (tensor, layer, lookahead distance) of a stack draws its own stream
+    w = workloads.C4_OFFLOAD
+    tags = []
+    for layer in range(4):
+        for name in ("Q", "K", "V", "F_self"):
+            tags.append(w.recipe(name, layer).tag)
+        tags += [w.recipe("F", layer, ahead).tag for ahead in range(1, 10)]
+    assert len(tags) == len(set(tags))
+    try:
+        w.recipe("F", 0, 10)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a lookahead of 10 layers must be refused")
