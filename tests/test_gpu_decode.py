@@ -208,6 +208,30 @@ def test_attention_decode_parity(gpu, G, dtype, k):
     say(f"  max abs err {err:.2e}")
 
 
+@pytest.mark.parametrize("k", [5, 37])
+def test_attention_decode_shared_workspace(gpu, k):
+    """Successive calls with new queries and selections on one workspace that
+    starts filled with garbage: 6 rows, split into 5 and 37 block ranges (the
+    merge's variants for at most 16 and for more ranges), each call against
+    the oracle."""
+    w = small("bf16", B=3, Hq=8, Hkv=2, k=k)
+    rows = w.B * w.Hkv
+    K, V = gen(w, "K"), gen(w, "V")
+    K64, V64 = parity.to_f64(K), parity.to_f64(V)
+    nbytes = gpu.workspace_bytes(gpu.OP_BLOCK_SPARSE_ATTN, w.B, w.Hq, w.Hkv, 1, w.T, w.k)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=DEV)
+    rng = np.random.default_rng(k)
+    for call in range(4):
+        Q = sg.tensor(wl.scaled(w, seed=300 + call).recipe("Q"), w.shape("Q"), DEV)
+        idx_np = np.stack([np.sort(rng.choice(w.nB, k, replace=False)) for _ in range(rows)])
+        idx_np = idx_np.reshape(w.B, w.Hkv, 1, k).astype(np.int32)
+        out = gpu.block_sparse_attn(Q, K, V, torch.from_numpy(idx_np).to(DEV), w.T, w.q_start, ws=ws)
+        torch.cuda.synchronize()
+        ref = oracle.block_sparse_attention(parity.to_f64(Q), K64, V64, idx_np, w.q_start, w.scale)
+        err = parity.check_attention(parity.to_f64(out), ref, parity.ATTN_ATOL_BF16)
+        say(f"k {k} call {call}: max abs err {err:.2e}")
+
+
 @pytest.mark.parametrize("w", [wl.C1_TINY, wl.C2_DECODE_32K], ids=lambda w: w.name)
 def test_decode_step_end_to_end(gpu, w):
     """select (Forecast) -> top-k -> attention, against the oracle run from K."""
