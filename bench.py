@@ -289,6 +289,7 @@ def bench_decode(args) -> int:
     for i in range(N_SETS):  # leave each set's Forecast scores / idx in place
         step(i)
     torch.cuda.synchronize()
+    projection = bench_projection(kbs, w, dev, kr)
 
     nbytes = algorithmic_bytes(w)
     gbps = {k: nbytes[k] / (ms[k] * 1e-3) / 1e9 for k in ms}
@@ -322,6 +323,7 @@ def bench_decode(args) -> int:
                          "multihead": round((ms["select_multihead"] + ms["topk"]) * 1e3, 2)},
         "forecast_vs_multihead_select_speedup": round(ms["select_multihead"] / ms["select_forecast"], 3),
         "state_maintenance_us": {k: round(v * 1e3, 2) for k, v in ms_extra.items()},
+        "upstream_projection": projection,
     }
     if args.calibration_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -335,6 +337,40 @@ def bench_decode(args) -> int:
         result["cpu_baseline"] = cpu_baseline(w, sets)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def bench_projection(kbs, w, dev, replays: int, D: int = 4096, n_layers: int = 8) -> dict:
+    """The Q/K/V/Forecast projection GEMM upstream of selection (not part of
+    the step): one decode token per sequence, hidden size D, one Forecast set.
+    Weights of n_layers layers rotate (470 MB at B = 16), so each launch
+    streams its weights from HBM as a real decode pass over the layers would;
+    algorithmic bytes = weights + hidden states + outputs."""
+    import torch
+    import synth.gpu as sg
+    from synth import workloads as wl
+    out = {}
+    for B in (w.B, 64):
+        wB = wl.scaled(w, B=B)
+        N = wl.qkvf_rows(wB, 1)
+        xs = [sg.tensor(wl.hidden_recipe(wB, layer=l), (B, D), dev) for l in range(n_layers)]
+        ws = [sg.tensor(wl.qkvf_weight_recipe(wB, D, layer=l), (N, D), dev) for l in range(n_layers)]
+        outs = (torch.empty((B, w.Hq, 1, w.d), dtype=torch.bfloat16, device=dev),
+                torch.empty((B, w.Hkv, 1, w.d), dtype=torch.bfloat16, device=dev),
+                torch.empty((B, w.Hkv, 1, w.d), dtype=torch.bfloat16, device=dev),
+                torch.empty((1, B, w.Hkv, 1, w.d), dtype=torch.bfloat16, device=dev))
+
+        def proj(i):
+            kbs.project_qkvf(xs[i % n_layers], ws[i % n_layers], w.Hq, w.Hkv, 1, out=outs)
+
+        ms = time_graph(proj, n_layers, max(1, replays))
+        nbytes = N * D * 2 + B * D * 2 + B * N * 2
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[f"B{B}"] = {"us": round(ms * 1e3, 2), "bytes": nbytes, "GBps": round(gbps, 1),
+                        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                        "TFLOPs": round(2.0 * B * N * D / (ms * 1e-3) / 1e12, 1)}
+        del xs, ws
+    out["shape"] = f"x [B, {D}] times W [{wl.qkvf_rows(w, 1)}, {D}] (32 Q + 8 K + 8 V + 8 Forecast heads of 128)"
+    return out
 
 
 HOST_LINK_PEAK_GBPS = 63.0   # PCIe 5.0 x16, one direction

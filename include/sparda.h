@@ -247,6 +247,28 @@ int sparda_prefetch_blocks_cached(const void* host_k, const void* host_v, const 
                                   int dtype, int B, int Hkv, int nB, int block, int d, int k_sel,
                                   int n_slots, int num_workgroups, void* side_stream);
 
+/*
+ * The projections upstream of the path at decode: Q, K, V and the Forecast
+ * vector from one hidden state per sequence, as one GEMM over the
+ * concatenated weights. [P1] paragraph on the four projections every layer
+ * emits (Q, K, V and a Forecast); [P1] abstract: the Forecast is a fourth
+ * projection per layer beside Query, Key and Value.
+ *   x  [B, D]                       hidden states (one token per sequence)
+ *   w  [(Hq + 2*Hkv + n_f*Hkv)*d, D] weight rows: Hq query heads, Hkv key
+ *                                   heads, Hkv value heads, then n_f sets of
+ *                                   Hkv Forecast heads, d rows per head
+ *   q  [B, Hq, 1, d]   k, v [B, Hkv, 1, d]   f [n_f, B, Hkv, 1, d]   (out)
+ * out[b, n] = sum over c of x[b, c] * w[n, c], accumulated in fp32 and
+ * rounded to nearest-even bf16. n_f = 1 for a layer whose Forecast looks one
+ * layer ahead; the first layer, which also scores its own blocks, has n_f = 2
+ * (set 0: its same-layer Forecast, set 1: the next layer's). n_f = 0 skips the
+ * Forecast (f may be NULL). Supported: bf16, d = 128, D a positive multiple of
+ * 512, 0 <= n_f <= 8. All pointers are device memory, 16-byte aligned; the
+ * outputs must not overlap the inputs. B = 0 is a no-op. Async on stream.
+ */
+int sparda_project_qkvf(const void* x, const void* w, void* q, void* k, void* v, void* f, int dtype, int B,
+                        int D, int Hq, int Hkv, int n_f, int d, void* stream);
+
 /* Workspace bytes the call `op` needs for these sizes (0 when none). */
 size_t sparda_workspace_bytes(int op, int B, int Hq, int Hkv, int Tq, int T, int d, int k_sel);
 

@@ -48,6 +48,7 @@ SIGNATURES = {
     "sparda_prefetch_blocks": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "sparda_prefetch_blocks_cached": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                                            _vp]),
+    "sparda_project_qkvf": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "sparda_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "sparda_status_string": (_c.c_char_p, [_i]),
     "sparda_last_error": (_c.c_char_p, []),
@@ -252,6 +253,27 @@ def block_sparse_attn(q, k, v, idx, T: int, q_start: int, scale: float | None = 
           _ptr(out), _dtype_code(q), B, Hq, Hkv, Tq, q_start, _positions(q_pos, B), T, d, BLOCK, TILE, k_sel, scale,
           _ptr(ws), nbytes, _stream(q, stream))
     return out
+
+
+def project_qkvf(x, w, Hq: int, Hkv: int, n_f: int = 1, out=None, stream=None):
+    """Q, K, V and n_f Forecast sets from hidden states x [B, D] and the
+    concatenated weight rows w [(Hq + 2 Hkv + n_f Hkv) * 128, D] (bf16).
+    Returns (q [B, Hq, 1, 128], k [B, Hkv, 1, 128], v [B, Hkv, 1, 128],
+    f [n_f, B, Hkv, 1, 128] or None); ``out`` may give those four tensors."""
+    torch = _torch()
+    B, D = x.shape
+    d = HEAD_DIM
+    if w.shape != ((Hq + 2 * Hkv + n_f * Hkv) * d, D):
+        raise ValueError(f"w has shape {tuple(w.shape)}, expected {((Hq + 2 * Hkv + n_f * Hkv) * d, D)}")
+    if out is None:
+        out = (torch.empty((B, Hq, 1, d), dtype=x.dtype, device=x.device),
+               torch.empty((B, Hkv, 1, d), dtype=x.dtype, device=x.device),
+               torch.empty((B, Hkv, 1, d), dtype=x.dtype, device=x.device),
+               torch.empty((n_f, B, Hkv, 1, d), dtype=x.dtype, device=x.device) if n_f else None)
+    q, k, v, f = out
+    _call("sparda_project_qkvf", _ptr(x), _ptr(w), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _dtype_code(x), B, D, Hq,
+          Hkv, n_f, d, _stream(x, stream))
+    return q, k, v, f
 
 
 def prefetch_blocks(host_k, host_v, idx, stage_k, stage_v, num_workgroups: int = 0, stream=None):

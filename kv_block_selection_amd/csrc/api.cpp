@@ -365,6 +365,29 @@ const void* mapped_host_ptr(const void* p) {
 }
 }  // namespace
 
+SPARDA_EXPORT int sparda_project_qkvf(const void* x, const void* w, void* q, void* k, void* v, void* f, int dtype,
+                                      int B, int D, int Hq, int Hkv, int n_f, int d, void* stream) {
+  if (int e = check_dtype(dtype)) return e;
+  CHECK(dtype == SPARDA_BF16, SPARDA_ERR_UNSUPPORTED, "project_qkvf: only bf16 inputs are supported");
+  CHECK(d == 128, SPARDA_ERR_UNSUPPORTED, "project_qkvf: head dim %d (only 128 supported)", d);
+  CHECK(B >= 0 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, SPARDA_ERR_INVALID_ARG,
+        "project_qkvf: need B >= 0, Hq and Hkv >= 1, Hq %% Hkv == 0 (B=%d Hq=%d Hkv=%d)", B, Hq, Hkv);
+  CHECK(D > 0 && D % 512 == 0, SPARDA_ERR_UNSUPPORTED, "project_qkvf: D=%d must be a positive multiple of 512", D);
+  CHECK(n_f >= 0 && n_f <= 8, SPARDA_ERR_INVALID_ARG, "project_qkvf: n_f=%d outside 0..8", n_f);
+  const long rows = (long)(Hq + 2L * Hkv + (long)n_f * Hkv) * d;
+  CHECK(rows / 16 <= 2147483647L && (long)B * D < (1L << 40) && rows * (long)D < (1L << 40), SPARDA_ERR_UNSUPPORTED,
+        "project_qkvf: sizes too large");
+  if (B == 0) return ok();
+  CHECK_PTR(x);
+  CHECK_PTR(w);
+  CHECK_PTR(q);
+  CHECK_PTR(k);
+  CHECK_PTR(v);
+  if (n_f > 0) CHECK_PTR(f);
+  return hip_status(sparda::launch_project_qkvf(x, w, q, k, v, f, B, D, Hq, Hkv, n_f, (hipStream_t)stream),
+                    "project_qkvf launch");
+}
+
 SPARDA_EXPORT int sparda_prefetch_blocks(const void* host_k, const void* host_v, const int32_t* idx,
                                          void* stage_k, void* stage_v, int dtype, int B, int Hkv, int nB,
                                          int block, int d, int k_sel, int num_workgroups, void* side_stream) {

@@ -70,6 +70,10 @@ hipError_t launch_attn_decode(const void* q, const void* k, const void* v, const
 hipError_t launch_attn_prefill(const void* q, const void* k, const void* v, const int32_t* idx, void* out,
                                const AttnDims& d, hipStream_t s);
 
+// project.hip (bf16; D % 512 == 0): x [B, D] times the rows of W [N, D]
+hipError_t launch_project_qkvf(const void* x, const void* w, void* q, void* k, void* v, void* f, int B, int D, int Hq,
+                               int Hkv, int n_f, hipStream_t s);
+
 // prefetch.hip (the cached variant: k <= kCacheMaxK, k <= n_slots <= kCacheMaxSlots)
 constexpr int kCacheMaxK = 256;
 constexpr int kCacheMaxSlots = 1024;

@@ -339,3 +339,29 @@ def lookahead_decode_step(layer0: dict, layer1: dict, T: int, k: int, scale: flo
     O0 = block_sparse_attention(layer0["Q"], layer0["K"], layer0["V"], idx0, q_start, scale, block)
     O1 = block_sparse_attention(layer1["Q"], layer1["K"], layer1["V"], idx1, q_start, scale, block)
     return O0, O1, idx0, idx1
+
+
+# ------------------------------------------ upstream: the four projections ----
+def project_qkvf(x: np.ndarray, w: np.ndarray, Hq: int, Hkv: int, n_f: int, d: int = 128):
+    """The projections a layer emits for one token per sequence: Q, K, V and
+    the Forecast vector ([P1] paragraph on the four projections per layer;
+    [P1] abstract: the Forecast is a fourth projection beside Query, Key and
+    Value; [P2] 二). The weights of all four are one matrix whose rows are
+    ordered [Hq query heads | Hkv key heads | Hkv value heads | n_f sets of
+    Hkv Forecast heads], d rows per head (n_f = 2 for the first layer, whose
+    extra set is its same-layer Forecast, [P2] 三).
+
+    x [B, D], w [(Hq + 2 Hkv + n_f Hkv) d, D] -> q [B, Hq, 1, d],
+    k and v [B, Hkv, 1, d], f [n_f, B, Hkv, 1, d] (None when n_f = 0).
+    """
+    B, D = x.shape
+    assert w.shape == ((Hq + 2 * Hkv + n_f * Hkv) * d, D)
+    y = np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T  # [B, N]
+    heads = y.reshape(B, Hq + 2 * Hkv + n_f * Hkv, d)
+    q = heads[:, :Hq].reshape(B, Hq, 1, d)
+    k = heads[:, Hq:Hq + Hkv].reshape(B, Hkv, 1, d)
+    v = heads[:, Hq + Hkv:Hq + 2 * Hkv].reshape(B, Hkv, 1, d)
+    f = None
+    if n_f:
+        f = heads[:, Hq + 2 * Hkv:].reshape(B, n_f, Hkv, 1, d).transpose(1, 0, 2, 3, 4).copy()
+    return q, k, v, f

@@ -51,6 +51,9 @@ TAG_V_OFFSET = 6
 TAG_F_SELF = 7
 TAG_F_AHEAD = 8  # Forecast of the layer j > 1 ahead: tag 8 + (j - 2), j <= 9
 LAYER_TAG_STRIDE = 16  # layer l uses tag + 16 * l
+# Hidden states and projection weights live in their own tag range (+ 16 * layer)
+TAG_HIDDEN = 4096
+TAG_W_QKVF = 4097
 
 
 def _mix64_int(z: int) -> int:

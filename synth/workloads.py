@@ -10,8 +10,8 @@ from __future__ import annotations
 
 from dataclasses import dataclass, field
 
-from . import (LAYER_TAG_STRIDE, TAG_F, TAG_F_AHEAD, TAG_F_SELF, TAG_K, TAG_K_OFFSET, TAG_Q, TAG_V, TAG_V_OFFSET,
-               Recipe)
+from . import (LAYER_TAG_STRIDE, TAG_F, TAG_F_AHEAD, TAG_F_SELF, TAG_HIDDEN, TAG_K, TAG_K_OFFSET, TAG_Q, TAG_V,
+               TAG_V_OFFSET, TAG_W_QKVF, Recipe)
 
 INV_SQRT_128 = 0.08838834764831845  # 1/sqrt(128); rounded to fp32 where applied
 
@@ -124,3 +124,23 @@ def scaled(w: Workload, **changes) -> Workload:
     """A smaller variant of a workload (same recipe), for parity at oracle-friendly sizes."""
     from dataclasses import replace
     return replace(w, **changes)
+
+
+# --------------------------------------------- the projections upstream ----
+MODEL_DIM = 4096  # hidden size of the 8B models the pages measure on
+
+
+def qkvf_rows(w: Workload, n_f: int = 1) -> int:
+    """Rows of the concatenated Q/K/V/Forecast weight matrix."""
+    return (w.Hq + 2 * w.Hkv + n_f * w.Hkv) * w.d
+
+
+def hidden_recipe(w: Workload, layer: int = 0) -> Recipe:
+    """Hidden states x [B, D] of one decode token per sequence, N(0, 1)."""
+    return Recipe(seed=w.seed, tag=TAG_HIDDEN + LAYER_TAG_STRIDE * layer, dtype=w.dtype)
+
+
+def qkvf_weight_recipe(w: Workload, D: int = MODEL_DIM, layer: int = 0) -> Recipe:
+    """Random projection weights [qkvf_rows, D], N(0, 1/D), so that the
+    projected vectors are about N(0, 1) like the other synthetic inputs."""
+    return Recipe(seed=w.seed, tag=TAG_W_QKVF + LAYER_TAG_STRIDE * layer, dtype=w.dtype, scale=D ** -0.5)

@@ -111,3 +111,16 @@ def check_compress(gpu: np.ndarray, ref: np.ndarray, dtype: str, mean_abs: np.nd
     tol = 32 * 2.0 ** -24 * mean_abs + 1e-30
     assert np.all(err <= tol), f"fp32 compressed keys beyond the summation bound: {float((err / tol).max())}"
     return float((err / tol).max())
+
+
+def check_projection(gpu: np.ndarray, ref: np.ndarray, abs_sum: np.ndarray, D: int) -> float:
+    """bf16 projections accumulated in fp32: each output may differ from the
+    exact fp64 dot product by the fp32 summation bound D * 2^-24 * sum|x w|
+    plus the final rounding to bf16 (half an ulp, 2^-9 |value|; 2^-8 |ref|
+    allows for the value itself being off by the summation error). Returns the
+    largest error as a fraction of its bound."""
+    bound = 2.0 ** -8 * np.abs(ref) + D * 2.0 ** -24 * abs_sum
+    err = np.abs(gpu - ref)
+    worst = float((err / bound).max()) if err.size else 0.0
+    assert worst <= 1.0, f"projection error {err.max():.3e} exceeds its bound (worst ratio {worst:.2f})"
+    return worst

@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in kbs.SIGNATURES, f"binding lacks {n}"
@@ -212,3 +212,28 @@ def test_prefetch_cached_validation(lib, args, status, needle):
                                            a["n_slots"], a["nwg"], None)
     assert st == status
     assert needle in lib.sparda_last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=0), 2, b"bf16"),
+    (dict(d=64), 2, b"head dim"),
+    (dict(D=500), 2, b"multiple of 512"),
+    (dict(Hq=6, Hkv=4), 1, b"Hq % Hkv"),
+    (dict(n_f=9), 1, b"n_f"),
+    (dict(x=None), 1, b"x is NULL"),
+    (dict(f=None), 1, b"f is NULL"),
+    (dict(q=P + 8), 1, b"q is not 16-byte aligned"),
+])
+def test_project_qkvf_validation(lib, kw, status, needle):
+    a = dict(x=P, w=P, q=P, k=P, v=P, f=P, dtype=1, B=16, D=4096, Hq=32, Hkv=8, n_f=1, d=128)
+    a.update(kw)
+    st = lib.sparda_project_qkvf(a["x"], a["w"], a["q"], a["k"], a["v"], a["f"], a["dtype"], a["B"], a["D"],
+                                 a["Hq"], a["Hkv"], a["n_f"], a["d"], None)
+    assert st == status and needle in lib.sparda_last_error(), lib.sparda_last_error()
+
+
+def test_project_qkvf_empty_batch_and_no_forecast(lib):
+    # B = 0 launches nothing and checks no pointer; n_f = 0 needs no f
+    assert lib.sparda_project_qkvf(None, None, None, None, None, None, 1, 0, 4096, 32, 8, 1, 128, None) == 0
+    assert lib.sparda_project_qkvf(P, P, P, P, P, None, 1, 0, 4096, 32, 8, 0, 128, None) == 0
+

@@ -359,3 +359,50 @@ def test_lookahead_step_structure():
     np.testing.assert_array_equal(i1b, i0)
     np.testing.assert_allclose(O1b, oracle.block_sparse_attention(L1["Q"], L["K"], L["V"], i0, T - 1, 0.3))
     assert W == 63
+
+
+# ------------------------------------------------ the four projections ----
+def test_project_qkvf_brute_force_and_layout():
+    """Every output element as a pure-Python sum over D, read back at the
+    position the weight-row order fixes (query heads, key heads, value heads,
+    then the Forecast sets), with small integers so the sums are exact."""
+    rng = np.random.default_rng(21)
+    B, D, Hq, Hkv, n_f, d = 3, 8, 4, 2, 2, 4
+    N = (Hq + 2 * Hkv + n_f * Hkv) * d
+    x = rng.integers(-4, 5, size=(B, D)).astype(np.float64)
+    w = rng.integers(-4, 5, size=(N, D)).astype(np.float64)
+    q, k, v, f = oracle.project_qkvf(x, w, Hq, Hkv, n_f, d)
+    assert q.shape == (B, Hq, 1, d) and k.shape == (B, Hkv, 1, d) and v.shape == (B, Hkv, 1, d)
+    assert f.shape == (n_f, B, Hkv, 1, d)
+
+    def y(b, n):
+        return sum(float(x[b, c]) * float(w[n, c]) for c in range(D))
+
+    for b in range(B):
+        for c in range(d):
+            for h in range(Hq):
+                assert q[b, h, 0, c] == y(b, h * d + c)
+            for h in range(Hkv):
+                assert k[b, h, 0, c] == y(b, (Hq + h) * d + c)
+                assert v[b, h, 0, c] == y(b, (Hq + Hkv + h) * d + c)
+                for s in range(n_f):
+                    assert f[s, b, h, 0, c] == y(b, (Hq + 2 * Hkv + s * Hkv + h) * d + c)
+
+
+def test_project_qkvf_unit_rows_pick_inputs():
+    """Weight rows that are unit vectors copy one input channel each: row n =
+    e_perm[n] gives output n = x[:, perm[n]] exactly; and n_f = 0 has no
+    Forecast output."""
+    rng = np.random.default_rng(22)
+    B, D, Hq, Hkv, d = 2, 64, 2, 1, 8
+    for n_f in (0, 1):
+        N = (Hq + 2 * Hkv + n_f * Hkv) * d
+        perm = rng.integers(0, D, size=N)
+        w = np.zeros((N, D))
+        w[np.arange(N), perm] = 1.0
+        x = rng.standard_normal((B, D))
+        q, k, v, f = oracle.project_qkvf(x, w, Hq, Hkv, n_f, d)
+        flat = np.concatenate([q.reshape(B, -1), k.reshape(B, -1), v.reshape(B, -1)]
+                              + ([f.transpose(1, 0, 2, 3, 4).reshape(B, -1)] if n_f else []), axis=1)
+        np.testing.assert_array_equal(flat, x[:, perm])
+        assert (f is None) == (n_f == 0)
