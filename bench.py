@@ -290,6 +290,7 @@ def bench_decode(args) -> int:
         step(i)
     torch.cuda.synchronize()
     projection = bench_projection(kbs, w, dev, kr)
+    decoupled = decoupled_layers(kbs, w, sets, ws_attn, dev, algorithmic_bytes(w)["step"], n_layers=3 * args.steps)
 
     nbytes = algorithmic_bytes(w)
     gbps = {k: nbytes[k] / (ms[k] * 1e-3) / 1e9 for k in ms}
@@ -324,6 +325,7 @@ def bench_decode(args) -> int:
         "forecast_vs_multihead_select_speedup": round(ms["select_multihead"] / ms["select_forecast"], 3),
         "state_maintenance_us": {k: round(v * 1e3, 2) for k, v in ms_extra.items()},
         "upstream_projection": projection,
+        "decoupled_layers": decoupled,
     }
     if args.calibration_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -337,6 +339,63 @@ def bench_decode(args) -> int:
         result["cpu_baseline"] = cpu_baseline(w, sets)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def decoupled_layers(kbs, w, sets, ws_attn, dev, step_bytes: int, n_layers: int) -> dict:
+    """Consecutive layers in the order the method runs them: layer j's Forecast
+    selects layer j+1's blocks, so at the start of layer j the selection and
+    top-k for layer j+1 go on a second stream while layer j attends with the
+    blocks selected during layer j-1. Layer j+1 begins when layer j's
+    attention has finished. The input sets stand in for the layers (set j % 3).
+    Each layer does the whole step (Forecast scoring, top-k, attention) on its
+    own data; timed with HIP events on the attention stream, after warm-up,
+    and beside the same layers run one after another on one stream."""
+    import torch
+    main = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(device=dev)
+    ev_sel = [torch.cuda.Event() for _ in range(N_SETS)]
+    ev_begin = torch.cuda.Event()
+
+    def select(j, stream):
+        s = sets[j % N_SETS]
+        kbs.select_forecast(s["F"], s["Kc"], w.T, w.q_start, out=s["scores"], stream=stream)
+        kbs.topk_blocks(s["scores"], w.k, out=s["idx"], stream=stream)
+
+    def attend(j):
+        s = sets[j % N_SETS]
+        kbs.block_sparse_attn(s["Q"], s["K"], s["V"], s["idx"], w.T, w.q_start, out=s["out"], ws=ws_attn,
+                              stream=main)
+
+    def layers(j0, n, overlap):
+        for j in range(j0, j0 + n):
+            if overlap:
+                side.wait_event(ev_begin)  # layer j has begun: its Forecast exists
+                select(j + 1, side)
+                ev_sel[(j + 1) % N_SETS].record(side)
+                main.wait_event(ev_sel[j % N_SETS])
+            else:
+                select(j + 1, main)
+            attend(j)
+            ev_begin.record(main)
+
+    out = {}
+    for name, overlap in (("sequential", False), ("overlapped", True)):
+        select(0, main)
+        ev_sel[0].record(main)
+        ev_begin.record(main)
+        layers(0, 6, overlap)  # warm-up
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(main)
+        layers(6, n_layers, overlap)
+        end.record(main)
+        torch.cuda.synchronize()
+        us = start.elapsed_time(end) * 1e3 / n_layers
+        out[name] = {"us_per_layer": round(us, 2), "steps_per_s_per_layer": round(1e6 / us, 1),
+                     "hbm_frac": round(step_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    out["layers_timed"] = n_layers
+    return out
 
 
 def bench_projection(kbs, w, dev, replays: int, D: int = 4096, n_layers: int = 8) -> dict:
