@@ -30,7 +30,7 @@ namespace sparda {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kProjRows = 16;   // rows of W per workgroup
+constexpr int kProjRows = 16;   // rows of W per tile
 constexpr int kProjStep = 128;  // columns per step
 constexpr int kProjMaxTiles = 4;  // 16-sequence tiles per workgroup
 
