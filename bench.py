@@ -54,6 +54,7 @@ def algorithmic_bytes(w) -> dict:
         "select_multihead": kc + q + scores,
         "topk": scores + idx,
         "attention": kv + q + idx + o,
+        "topk_attention": scores + idx + kv + q + o,
         "step": kc + f + scores + (scores + idx) + (kv + q + idx + o),
     }
 
@@ -152,15 +153,19 @@ def cpu_baseline(w, sets, min_seconds: float = 10.0, max_reps: int = 30) -> dict
                       f"on 1 thread, repeated {reps}x ({timed:.1f} s timed); fp64 conversion of inputs untimed"}
 
 
-def pmc_traffic(kernel_file: str, summary: str):
+def pmc_traffic(kernel_files, summary: str):
     """HBM bytes per launch from a committed rocprofv3 PMC summary, or None when
-    the kernel source changed since the counters were taken."""
+    a kernel source changed since the counters were taken (sha256 of the
+    sources' bytes, concatenated in the order given)."""
     import hashlib
     try:
         with open(os.path.join(ROOT, "profiles", summary)) as f:
             rec = json.load(f)
-        with open(os.path.join(ROOT, kernel_file), "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
+        h = hashlib.sha256()
+        for kernel_file in ([kernel_files] if isinstance(kernel_files, str) else kernel_files):
+            with open(os.path.join(ROOT, kernel_file), "rb") as f:
+                h.update(f.read())
+        digest = h.hexdigest()
     except (OSError, ValueError):
         return None
     if rec.get("source_sha256") != digest:
@@ -247,7 +252,16 @@ def bench_decode(args) -> int:
         s = sets[i % N_SETS]
         kbs.block_sparse_attn(s["Q"], s["K"], s["V"], s["idx"], w.T, w.q_start, out=s["out"], ws=ws_attn)
 
+    def topk_attn(i):  # top-k and attention in one launch
+        s = sets[i % N_SETS]
+        kbs.topk_block_sparse_attn(s["scores"], s["Q"], s["K"], s["V"], w.k, w.T, w.q_start, idx=s["idx"],
+                                   out=s["out"], ws=ws_attn)
+
     def step(i):
+        sel(i)
+        topk_attn(i)
+
+    def step_separate(i):  # the same step with top-k as a launch of its own
         sel(i)
         topk(i)
         attn(i)
@@ -267,7 +281,8 @@ def bench_decode(args) -> int:
         s = sets[i % N_SETS]
         kbs.select_forecast(s["F"], s["Kc"], w.T, 0, out=s["scores"], q_pos=pos_last)
         kbs.topk_blocks(s["scores"], w.k, out=s["idx"])
-        kbs.block_sparse_attn(s["Q"], s["K"], s["V"], s["idx"], w.T, 0, out=s["out"], ws=ws_attn, q_pos=pos_last)
+        kbs.topk_block_sparse_attn(s["scores"], s["Q"], s["K"], s["V"], w.k, w.T, 0, idx=s["idx"], out=s["out"],
+                                   ws=ws_attn, q_pos=pos_last)
 
     log("[bench] warmup (eager)")
     for i in range(args.warmup):
@@ -279,10 +294,13 @@ def bench_decode(args) -> int:
     replays = max(1, args.steps // per_graph)
     ms_step = time_graph(step, per_graph, replays)
     steps_timed = replays * per_graph
-    log(f"[bench] graph step {ms_step * 1e3:.1f} us; per-kernel graphs")
+    ms_step_separate = time_graph(step_separate, per_graph, replays)
+    log(f"[bench] graph step {ms_step * 1e3:.1f} us ({ms_step_separate * 1e3:.1f} us with top-k launched on its own); "
+        f"per-kernel graphs")
     kr = max(1, args.kernel_iters // per_graph)
     ms = {"select_forecast": time_graph(sel, per_graph, kr), "topk": time_graph(topk, per_graph, kr),
-          "attention": time_graph(attn, per_graph, kr), "select_multihead": time_graph(sel_mh, per_graph, kr)}
+          "attention": time_graph(attn, per_graph, kr), "select_multihead": time_graph(sel_mh, per_graph, kr),
+          "topk_attention": time_graph(topk_attn, per_graph, kr)}
     ms_extra = {"append_kv_with_window": time_graph(append_win, per_graph, kr),
                 "append_kv": time_graph(append_nowin, per_graph, kr),
                 "step_with_q_pos": time_graph(step_q_pos, per_graph, kr)}
@@ -294,7 +312,7 @@ def bench_decode(args) -> int:
 
     nbytes = algorithmic_bytes(w)
     gbps = {k: nbytes[k] / (ms[k] * 1e-3) / 1e9 for k in ms}
-    dominant = max(("select_forecast", "attention"), key=lambda k: ms[k])
+    dominant = max(("select_forecast", "topk_attention"), key=lambda k: ms[k])
     step_gbps = nbytes["step"] / (ms_step * 1e-3) / 1e9
     result = {
         "metric": METRIC,
@@ -313,11 +331,14 @@ def bench_decode(args) -> int:
                    "block": w.block, "top_k": w.k, "selector": "forecast", "input_sets_rotated": N_SETS},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(gbps[dominant], 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps[dominant] / HBM_PEAK_GBPS, 4),
-                     "traffic": pmc_traffic("kv_block_selection_amd/csrc/attn_decode.hip",
-                                            "attn_decode_c3_traffic.json") if dominant == "attention" else None},
+                     "traffic": pmc_traffic(["kv_block_selection_amd/csrc/attn_decode.hip",
+                                             "kv_block_selection_amd/csrc/topk_row.h"],
+                                            "attn_decode_c3_traffic.json") if dominant == "topk_attention"
+                     else None},
         "step_hbm_GBps": round(step_gbps, 1),
         "step_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
         "ms_per_step_eager": round(ms_step_eager, 5),
+        "ms_per_step_topk_separate": round(ms_step_separate, 5),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in ms.items()},
         "kernel_GBps": {k: round(v, 1) for k, v in gbps.items()},
         "selection_us": {"forecast": round((ms["select_forecast"] + ms["topk"]) * 1e3, 2),

@@ -208,6 +208,25 @@ int sparda_block_sparse_attn(const void* q, const void* k, const void* v, int kv
                              int k_sel, float scale, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Steps 3 and 4 of a decode step in one launch: the top-k blocks of each
+ * (sequence, KV head) row of blk_scores, exactly as sparda_topk_blocks picks
+ * them, then the attention of sparda_block_sparse_attn (cache mode, one query
+ * per sequence) over those blocks. [P1] paragraph on block-sparse attention:
+ * keep the top-k scored blocks and attend over them.
+ *   blk_scores [B, Hkv, 1, nB] float32, nB = T / block
+ *   idx        [B, Hkv, 1, k]  out: the selection (ascending, -1 padded)
+ *   q, k, v, out, q_pos, scale: as sparda_block_sparse_attn with Tq = 1
+ * idx and out hold the same bits as sparda_topk_blocks followed by
+ * sparda_block_sparse_attn. Needs nB <= 8192 and k <= 1024.
+ * ws: sparda_workspace_bytes(SPARDA_OP_BLOCK_SPARSE_ATTN, B, Hq, Hkv, 1, T,
+ * d, k) bytes, as for the attention call.
+ */
+int sparda_topk_block_sparse_attn(const float* blk_scores, const void* q, const void* k, const void* v,
+                                  int32_t* idx, void* out, int dtype, int B, int Hq, int Hkv, int q_start,
+                                  const int* q_pos, int T, int d, int block, int k_sel, float scale, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/*
  * Step 5 - lookahead prefetch of the selected blocks from host memory.
  * [P1] paragraph on prefetching on a separate stream; [P2] 二 and 三: the blocks
  * the Forecast picks for the next layer are pulled from CPU memory into GPU

@@ -49,6 +49,8 @@ SIGNATURES = {
     "sparda_prefetch_blocks_cached": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i,
                                            _vp]),
     "sparda_project_qkvf": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "sparda_topk_block_sparse_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _f,
+                                           _vp, _sz, _vp]),
     "sparda_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "sparda_status_string": (_c.c_char_p, [_i]),
     "sparda_last_error": (_c.c_char_p, []),
@@ -274,6 +276,28 @@ def project_qkvf(x, w, Hq: int, Hkv: int, n_f: int = 1, out=None, stream=None):
     _call("sparda_project_qkvf", _ptr(x), _ptr(w), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _dtype_code(x), B, D, Hq,
           Hkv, n_f, d, _stream(x, stream))
     return q, k, v, f
+
+
+def topk_block_sparse_attn(scores, q, k, v, k_sel: int, T: int, q_start: int, scale: float | None = None,
+                           idx=None, out=None, ws=None, stream=None, q_pos=None):
+    """Top-k blocks of the decode scores [B, Hkv, 1, nB] and attention of q
+    [B, Hq, 1, 128] over them, in one launch. Returns (idx [B, Hkv, 1, k_sel]
+    int32, O [B, Hq, 1, 128]), the same bits as topk_blocks + block_sparse_attn."""
+    torch = _torch()
+    B, Hq, Tq, d = q.shape
+    Hkv = k.shape[1]
+    if Tq != 1:
+        raise ValueError("topk_block_sparse_attn is a decode call (one query per sequence)")
+    scale = d ** -0.5 if scale is None else scale
+    if idx is None:
+        idx = torch.empty((B, Hkv, 1, k_sel), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    ws, nbytes = _workspace(ws, workspace_bytes(OP_BLOCK_SPARSE_ATTN, B, Hq, Hkv, 1, T, k_sel), q)
+    _call("sparda_topk_block_sparse_attn", _ptr(scores), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out),
+          _dtype_code(q), B, Hq, Hkv, q_start, _positions(q_pos, B), T, d, BLOCK, k_sel, scale, _ptr(ws), nbytes,
+          _stream(q, stream))
+    return idx, out
 
 
 def prefetch_blocks(host_k, host_v, idx, stage_k, stage_v, num_workgroups: int = 0, stream=None):

@@ -351,6 +351,37 @@ SPARDA_EXPORT int sparda_block_sparse_attn(const void* q, const void* k, const v
                     "block_sparse_attn launch");
 }
 
+SPARDA_EXPORT int sparda_topk_block_sparse_attn(const float* blk_scores, const void* q, const void* k, const void* v,
+                                                int32_t* idx, void* out, int dtype, int B, int Hq, int Hkv,
+                                                int q_start, const int* q_pos, int T, int d, int block, int k_sel,
+                                                float scale, void* ws, size_t ws_bytes, void* stream) {
+  if (int e = check_dtype(dtype)) return e;
+  if (int e = check_geometry(B, Hq, Hkv, 1, q_start, T, d)) return e;
+  CHECK(block == sparda::kBlock, SPARDA_ERR_UNSUPPORTED, "block %d != 64", block);
+  CHECK(std::isfinite(scale), SPARDA_ERR_INVALID_ARG, "scale is not finite");
+  const int nB = T / sparda::kBlock;
+  CHECK(nB <= 8192, SPARDA_ERR_UNSUPPORTED, "topk_block_sparse_attn: nB = %d above 8192", nB);
+  CHECK(k_sel >= 1 && k_sel <= nB, SPARDA_ERR_INVALID_ARG, "k = %d outside 1..nB (%d)", k_sel, nB);
+  CHECK(k_sel <= 1024, SPARDA_ERR_UNSUPPORTED, "topk_block_sparse_attn: k = %d above 1024", k_sel);
+  if (B == 0) return ok();
+  CHECK(blk_scores != nullptr && ((uintptr_t)blk_scores & 3u) == 0, SPARDA_ERR_INVALID_ARG,
+        "blk_scores is NULL or not 4-byte aligned");
+  CHECK_PTR(q);
+  CHECK_PTR(k);
+  CHECK_PTR(v);
+  CHECK_PTR(out);
+  CHECK(idx != nullptr && ((uintptr_t)idx & 3u) == 0, SPARDA_ERR_INVALID_ARG, "idx is NULL or not 4-byte aligned");
+  const size_t need = ws_bytes_for(SPARDA_OP_BLOCK_SPARSE_ATTN, B, Hq, Hkv, 1, T, k_sel);
+  CHECK(ws_bytes >= need, SPARDA_ERR_WORKSPACE, "topk_block_sparse_attn needs %zu workspace bytes, got %zu", need,
+        ws_bytes);
+  if (need) CHECK_PTR(ws);
+  sparda::AttnDims ad = attn_dims(B, Hq, Hkv, 1, q_start, T, k_sel, scale, SPARDA_KV_CACHE);
+  ad.q_pos = q_pos;
+  return hip_status(sparda::launch_topk_attn_decode(blk_scores, q, k, v, idx, out, dtype == SPARDA_BF16, ad, ws,
+                                                    (hipStream_t)stream),
+                    "topk_block_sparse_attn launch");
+}
+
 namespace {
 // Pinned, mapped host memory: returns the device-side address or nullptr.
 const void* mapped_host_ptr(const void* p) {

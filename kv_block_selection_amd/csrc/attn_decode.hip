@@ -22,6 +22,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "topk_row.h"
 
 namespace sparda {
 
@@ -32,6 +33,7 @@ namespace sparda {
 // many one-wave workgroups (8 resident per CU at ~250 VGPRs).
 constexpr int kAttnTargetWaves = SPARDA_ATTN_TARGET_WAVES;
 constexpr int kAttnMaxSplits = 64;
+constexpr int kFusedMaxK = 1024;  // top-k fused in front of attention: at most this many blocks
 constexpr float kLazyGrow = 5.545177444479562f;  // 8 ln 2
 
 // Reduce-scatter of G partial dot products over the 16 lanes of a key row.
@@ -81,13 +83,20 @@ __device__ __forceinline__ void reduce_scatter16(const float* part, float* out) 
 #define SPARDA_ATTN_WAVES_PER_EU 2
 #endif
 
-template <typename Tag, int G>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SPARDA_ATTN_WAVES_PER_EU)))
+// WPG waves per workgroup, one split each (split = blockIdx.y * WPG + wave).
+// NPT > 0: the workgroup first takes the row's top-k of `scores` itself (256
+// threads, NPT scores per thread; every workgroup of the row computes the
+// same selection, the first also writes it to idx_out) and the waves read the
+// selection from LDS; NPT = 0: the selection comes from idx.
+template <typename Tag, int G, int WPG, int NPT>
+__global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(SPARDA_ATTN_WAVES_PER_EU)))
 void attn_decode_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ kbuf, const uint8_t* __restrict__ vbuf,
-    const int32_t* __restrict__ idx, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    uint8_t* __restrict__ out, int T, int nB, int k, int kv_mode, int p_all, const int* __restrict__ q_pos,
-    int hkv, const int32_t* __restrict__ slot_of, int n_slots, int bps, int splits, float scale) {
+    const int32_t* __restrict__ idx, int32_t* __restrict__ idx_out, const float* __restrict__ scores,
+    float* __restrict__ part_o,
+    float2* __restrict__ part_ml, uint8_t* __restrict__ out, int T, int nB, int k, int kv_mode, int p_all,
+    const int* __restrict__ q_pos, int hkv, const int32_t* __restrict__ slot_of, int n_slots, int bps, int splits,
+    float scale) {
   constexpr int E = DT<Tag>::kElems;
   constexpr int LPK = kHeadDim / E;  // lanes per key row
   constexpr int KPI = kWave / LPK;   // keys per load instruction
@@ -96,19 +105,42 @@ void attn_decode_kernel(
   constexpr int RB = kHeadDim * DT<Tag>::kBytes;
   constexpr int GR = G < 4 ? 1 : G / 4;  // scores each lane holds after the reduce-scatter
   constexpr bool kBf16 = DT<Tag>::kBytes == 2;
-  __shared__ float s_p[CK * G];          // scores (and fp32 probabilities)
-  __shared__ uint32_t s_p2[CK / 2 * G];  // bf16 probability pairs
+  __shared__ float s_p_all[WPG][CK * G];          // scores (and fp32 probabilities), per wave
+  __shared__ uint32_t s_p2_all[WPG][CK / 2 * G];  // bf16 probability pairs, per wave
+  const int wv = WPG == 1 ? 0 : threadIdx.x / kWave;
+  float* s_p = s_p_all[wv];
+  uint32_t* s_p2 = s_p2_all[wv];
 
   const long row = blockIdx.x;  // rows on the fast axis: a row's splits share an XCD
-  const int split = blockIdx.y;
+  const int split = blockIdx.y * WPG + wv;
   const int p = row_position(q_pos, row, hkv, p_all, T);  // the row's query position
-  const int lane = threadIdx.x;
+  const int lane = WPG == 1 ? threadIdx.x : threadIdx.x % kWave;
   const int c = lane % LPK;
   const int r = lane / LPK;
 
+  const int32_t* idx_row = idx + row * k;
+  if constexpr (NPT > 0) {
+    __shared__ TopkShared sh;
+    __shared__ int32_t s_sel[kFusedMaxK];
+    topk_row<NPT>(scores + row * nB, blockIdx.y == 0 ? idx_out + row * k : nullptr, s_sel, nB, k, sh, threadIdx.x);
+    __syncthreads();
+    idx_row = s_sel;
+  }
+  if (split >= splits) return;  // a last workgroup with fewer splits than waves
   u32x4 qs[G];
 #pragma unroll
   for (int s = 0; s < G; ++s) qs[s] = load16(q + (row * G + slot_head<G>(s, c & 15)) * RB + c * 16);
+  // Hand-offs through s_p / s_p2 stay inside one wave: with one wave per
+  // workgroup a barrier is that wave's own; otherwise waiting for the wave's
+  // LDS operations is enough (its lanes run each LDS instruction together, in
+  // order), and the other waves of the workgroup run their splits freely.
+  auto stage_sync = [&]() {
+    if constexpr (WPG == 1) {
+      __syncthreads();
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+  };
 
   float acc[G][E];
   float m_run[G], l_run[G];
@@ -122,7 +154,6 @@ void attn_decode_kernel(
 
   const int j0 = split * bps;
   const int j1 = min(k, j0 + bps);  // >= j0 + 1: every split owns at least one slot
-  const int32_t* idx_row = idx + row * k;
   // Stage q = half h of slot j0 + q/2: its first token and its number of valid
   // keys. Padding, out-of-range and wholly-future slots read block 0 of the
   // row (a valid address) with every key masked.
@@ -176,7 +207,7 @@ void attn_decode_kernel(
           s_p[key * G + 4 * gr + h] = key < nvalid ? sc[gr] * scale : -INFINITY;
       }
     }
-    __syncthreads();
+    stage_sync();
     // online softmax, lane = key (lanes 32..63 idle)
     float alpha[G], pr[G];
 #pragma unroll
@@ -209,7 +240,7 @@ void attn_decode_kernel(
         for (int g = 0; g < G; ++g) s_p[lane * G + g] = pr[g];
       }
     }
-    __syncthreads();
+    stage_sync();
     if constexpr (decltype(prefetch)::value) {
       tok0 = stage_of(q + 1, nvalid);
 #pragma unroll
@@ -260,7 +291,7 @@ void attn_decode_kernel(
           for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pg[g], v[e], acc[g][e]);
       }
     }
-    __syncthreads();
+    stage_sync();
   };
   for (int q = 0; q < nstage - 1; ++q) body(q, std::true_type{});
   body(nstage - 1, std::false_type{});
@@ -425,8 +456,8 @@ size_t decode_attn_ws_bytes(const AttnDims& d) {
 }
 
 template <typename Tag, int G>
-static void launch_attn_g(const void* q, const void* k, const void* v, const int32_t* idx, void* out,
-                          const AttnDims& d, void* ws, hipStream_t s) {
+static void launch_attn_g(const void* q, const void* k, const void* v, const int32_t* idx, const float* scores,
+                          void* out, const AttnDims& d, void* ws, hipStream_t s) {
   const int splits = decode_attn_splits(d);
   const int bps = (d.k + splits - 1) / splits;
   const int rows = d.B * d.Hkv;
@@ -437,10 +468,25 @@ static void launch_attn_g(const void* q, const void* k, const void* v, const int
     part_o = (float*)ws;
     part_ml = (float2*)((char*)ws + align256(n * kHeadDim * sizeof(float)));
   }
-  hipLaunchKernelGGL((attn_decode_kernel<Tag, G>), dim3(rows, splits), dim3(kWave), 0, s,
-                     (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, part_o, part_ml,
-                     (uint8_t*)out, d.T, d.nB, d.k, d.kv_mode, d.q_start, d.q_pos, d.Hkv, d.slot_of, d.n_slots, bps, splits,
-                     d.scale);
+  if (scores == nullptr) {
+    hipLaunchKernelGGL((attn_decode_kernel<Tag, G, 1, 0>), dim3(rows, splits), dim3(kWave), 0, s,
+                       (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, nullptr, nullptr, part_o, part_ml, (uint8_t*)out, d.T, d.nB, d.k, d.kv_mode, d.q_start, d.q_pos, d.Hkv,
+                       d.slot_of, d.n_slots, bps, splits, d.scale);
+  } else {
+    // top-k fused in front: four splits per workgroup, each workgroup of a
+    // row selects the row's blocks itself
+    const dim3 grid(rows, (splits + 3) / 4);
+#define SPARDA_FUSED(N)                                                                                          \
+  hipLaunchKernelGGL((attn_decode_kernel<Tag, G, 4, N>), grid, dim3(4 * kWave), 0, s, (const uint8_t*)q,         \
+                     (const uint8_t*)k, (const uint8_t*)v, nullptr, const_cast<int32_t*>(idx), scores, part_o,    \
+                     part_ml,                                                                                    \
+                     (uint8_t*)out, d.T, d.nB, d.k, d.kv_mode, d.q_start, d.q_pos, d.Hkv, d.slot_of, d.n_slots, bps, \
+                     splits, d.scale)
+    if (d.nB <= 256) SPARDA_FUSED(1);
+    else if (d.nB <= 2048) SPARDA_FUSED(8);
+    else SPARDA_FUSED(32);
+#undef SPARDA_FUSED
+  }
   if (splits > 1 && SPARDA_COMBINE_ROW && G * (kHeadDim / 4) <= 256) {
     if (splits <= 16)
       hipLaunchKernelGGL((attn_combine_row_kernel<Tag, 16>), dim3(rows), dim3(G * (kHeadDim / 4)), 0, s, part_o,
@@ -461,8 +507,13 @@ static void launch_attn_g(const void* q, const void* k, const void* v, const int
 
 hipError_t launch_attn_decode(const void* q, const void* k, const void* v, const int32_t* idx,
                               void* out, bool bf16, const AttnDims& d, void* ws, hipStream_t s) {
+  return launch_topk_attn_decode(nullptr, q, k, v, const_cast<int32_t*>(idx), out, bf16, d, ws, s);
+}
+
+hipError_t launch_topk_attn_decode(const float* scores, const void* q, const void* k, const void* v, int32_t* idx,
+                                   void* out, bool bf16, const AttnDims& d, void* ws, hipStream_t s) {
   const int G = d.Hq / d.Hkv;
-#define SPARDA_AT(TAG, GG) launch_attn_g<TAG, GG>(q, k, v, idx, out, d, ws, s)
+#define SPARDA_AT(TAG, GG) launch_attn_g<TAG, GG>(q, k, v, idx, scores, out, d, ws, s)
 #define SPARDA_AT_G(TAG)                  \
   switch (G) {                            \
     case 1: SPARDA_AT(TAG, 1); break;     \

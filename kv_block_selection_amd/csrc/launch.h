@@ -65,6 +65,10 @@ int decode_attn_splits(const AttnDims& d);
 size_t decode_attn_ws_bytes(const AttnDims& d);
 hipError_t launch_attn_decode(const void* q, const void* k, const void* v, const int32_t* idx,
                               void* out, bool bf16, const AttnDims& d, void* ws, hipStream_t s);
+// the same after the row's top-k of scores [rows, nB] (written to idx), in one
+// launch; needs nB <= 8192 and k <= 1024
+hipError_t launch_topk_attn_decode(const float* scores, const void* q, const void* k, const void* v, int32_t* idx,
+                                   void* out, bool bf16, const AttnDims& d, void* ws, hipStream_t s);
 
 // attn_prefill.hip (bf16, cache mode, Tq % 64 == 0)
 hipError_t launch_attn_prefill(const void* q, const void* k, const void* v, const int32_t* idx, void* out,
