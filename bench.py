@@ -183,6 +183,9 @@ def main() -> int:
                     help="decode: the batch-16 128K decode step (the headline line); offload: the batch-64 two-layer "
                          "step with lookahead prefetch from pinned host memory; prefill: a 4096-query chunk at 128K")
     ap.add_argument("--kernel-iters", type=int, default=100)
+    ap.add_argument("--decoupled-layers", action="store_true",
+                    help="decode: also time consecutive layers with the next layer's selection on a second stream "
+                         "beside this layer's attention, against the same layers on one stream")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (torch copy_) ten times, as the known-size reference "
                          "for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters")
@@ -308,7 +311,8 @@ def bench_decode(args) -> int:
         step(i)
     torch.cuda.synchronize()
     projection = bench_projection(kbs, w, dev, kr)
-    decoupled = decoupled_layers(kbs, w, sets, ws_attn, dev, algorithmic_bytes(w)["step"], n_layers=3 * args.steps)
+    decoupled = (decoupled_layers(kbs, w, sets, ws_attn, dev, algorithmic_bytes(w)["step"], n_layers=3 * args.steps)
+                 if args.decoupled_layers else None)
 
     nbytes = algorithmic_bytes(w)
     gbps = {k: nbytes[k] / (ms[k] * 1e-3) / 1e9 for k in ms}
@@ -346,8 +350,9 @@ def bench_decode(args) -> int:
         "forecast_vs_multihead_select_speedup": round(ms["select_multihead"] / ms["select_forecast"], 3),
         "state_maintenance_us": {k: round(v * 1e3, 2) for k, v in ms_extra.items()},
         "upstream_projection": projection,
-        "decoupled_layers": decoupled,
     }
+    if decoupled is not None:
+        result["decoupled_layers"] = decoupled
     if args.calibration_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
