@@ -45,7 +45,8 @@ def test_attention_workspace_reuse_across_calls(gpu):
         say(f"call {call}: err {err:.2e}")
 
 
-def test_graph_replay_matches_eager(gpu):
+@pytest.mark.parametrize("fused", [False, True], ids=["topk-launch", "topk-fused"])
+def test_graph_replay_matches_eager(gpu, fused):
     """A decode step captured in a HIP graph gives the eager bits on every replay,
     with eager work and synchronisations between replays."""
     w = wl.C2_DECODE_32K
@@ -59,8 +60,11 @@ def test_graph_replay_matches_eager(gpu):
 
     def step():
         gpu.select_forecast(F, Kc, w.T, w.q_start, out=scores)
-        gpu.topk_blocks(scores, w.k, out=idx)
-        gpu.block_sparse_attn(Q, K, V, idx, w.T, w.q_start, out=out, ws=ws)
+        if fused:
+            gpu.topk_block_sparse_attn(scores, Q, K, V, w.k, w.T, w.q_start, idx=idx, out=out, ws=ws)
+        else:
+            gpu.topk_blocks(scores, w.k, out=idx)
+            gpu.block_sparse_attn(Q, K, V, idx, w.T, w.q_start, out=out, ws=ws)
 
     step()
     torch.cuda.synchronize()
