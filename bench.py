@@ -283,7 +283,6 @@ def bench_decode(args) -> int:
     def step_q_pos(i):  # the same step with per-sequence positions (all at T - 1)
         s = sets[i % N_SETS]
         kbs.select_forecast(s["F"], s["Kc"], w.T, 0, out=s["scores"], q_pos=pos_last)
-        kbs.topk_blocks(s["scores"], w.k, out=s["idx"])
         kbs.topk_block_sparse_attn(s["scores"], s["Q"], s["K"], s["V"], w.k, w.T, 0, idx=s["idx"], out=s["out"],
                                    ws=ws_attn, q_pos=pos_last)
 
