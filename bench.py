@@ -269,6 +269,16 @@ def bench_decode(args) -> int:
         topk(i)
         attn(i)
 
+    def step_pipelined(i):
+        # layer i in the method's layer order: its selection (from the layer
+        # before's Forecast) shares a launch with the merge of the layer
+        # before's attention, which leaves its block-range results in ws_attn
+        s, prev = sets[i % N_SETS], sets[(i - 1) % N_SETS]
+        kbs.select_forecast(s["F"], s["Kc"], w.T, w.q_start, out=s["scores"],
+                            merge_from=(ws_attn, prev["out"], w.T, w.k))
+        kbs.topk_block_sparse_attn(s["scores"], s["Q"], s["K"], s["V"], w.k, w.T, w.q_start, idx=s["idx"],
+                                   out=s["out"], ws=ws_attn, merge=False)
+
     # Decode-time state maintenance: append the step's token to K, V and
     # compress the window it completes (every 16th step) or none. The tokens
     # written are the ones already there, so the inputs stay as they are.
@@ -289,16 +299,19 @@ def bench_decode(args) -> int:
     log("[bench] warmup (eager)")
     for i in range(args.warmup):
         step(i)
+    for i in range(args.warmup):
+        step_pipelined(i)
     torch.cuda.synchronize()
-    ms_step_eager = time_loop(step, args.steps, stream)
+    ms_step_eager = time_loop(step_pipelined, args.steps, stream)
     log(f"[bench] eager step {ms_step_eager * 1e3:.1f} us; timing {args.steps} steps through a HIP graph")
     per_graph = 3 * N_SETS
     replays = max(1, args.steps // per_graph)
-    ms_step = time_graph(step, per_graph, replays)
+    ms_step = time_graph(step_pipelined, per_graph, replays)
     steps_timed = replays * per_graph
+    ms_step_layer = time_graph(step, per_graph, replays)
     ms_step_separate = time_graph(step_separate, per_graph, replays)
-    log(f"[bench] graph step {ms_step * 1e3:.1f} us ({ms_step_separate * 1e3:.1f} us with top-k launched on its own); "
-        f"per-kernel graphs")
+    log(f"[bench] graph step {ms_step * 1e3:.1f} us (one layer at a time {ms_step_layer * 1e3:.1f} us, with top-k "
+        f"launched on its own {ms_step_separate * 1e3:.1f} us); per-kernel graphs")
     kr = max(1, args.kernel_iters // per_graph)
     ms = {"select_forecast": time_graph(sel, per_graph, kr), "topk": time_graph(topk, per_graph, kr),
           "attention": time_graph(attn, per_graph, kr), "select_multihead": time_graph(sel_mh, per_graph, kr),
@@ -331,7 +344,9 @@ def bench_decode(args) -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.description, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
-                   "block": w.block, "top_k": w.k, "selector": "forecast", "input_sets_rotated": N_SETS},
+                   "block": w.block, "top_k": w.k, "selector": "forecast", "input_sets_rotated": N_SETS,
+                   "schedule": "consecutive layers (the input sets in turn): layer l's Forecast selection shares a "
+                               "launch with the merge of layer l-1's attention, then layer l's top-k + attention"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(gbps[dominant], 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps[dominant] / HBM_PEAK_GBPS, 4),
                      "traffic": pmc_traffic(["kv_block_selection_amd/csrc/attn_decode.hip",
@@ -341,6 +356,7 @@ def bench_decode(args) -> int:
         "step_hbm_GBps": round(step_gbps, 1),
         "step_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
         "ms_per_step_eager": round(ms_step_eager, 5),
+        "ms_per_step_one_layer_at_a_time": round(ms_step_layer, 5),
         "ms_per_step_topk_separate": round(ms_step_separate, 5),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in ms.items()},
         "kernel_GBps": {k: round(v, 1) for k, v in gbps.items()},

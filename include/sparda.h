@@ -227,6 +227,40 @@ int sparda_topk_block_sparse_attn(const float* blk_scores, const void* q, const 
                                   size_t ws_bytes, void* stream);
 
 /*
+ * The decode step in the order of the method's layers. Layer L's Forecast
+ * selects layer L+1's blocks ([P1] paragraph on the Forecast predicting the
+ * next layer's blocks; [P2] 二), so layer L+1's selection needs nothing from
+ * layer L's attention output. These three calls let that selection share a
+ * launch with the last part of layer L's attention, the merge of its block
+ * ranges:
+ *
+ * sparda_topk_block_sparse_attn_partial: as sparda_topk_block_sparse_attn,
+ *   but leaves the block ranges' results in ws; `out` is complete only after
+ *   sparda_merge_partials or sparda_select_forecast_merge has merged them.
+ *   (When a row is not split into ranges, which needs few blocks and a large
+ *   batch, the call writes `out` itself and the merge does nothing.)
+ * sparda_merge_partials: that merge on its own. ws, out, dtype, B, Hq, Hkv,
+ *   T, d, k_sel: those of the partial call, whose results ws holds.
+ * sparda_select_forecast_merge: sparda_select_forecast for one query per
+ *   sequence, plus the merge of a partial attention call with the same B,
+ *   Hkv and dtype (m_ws, m_out, m_Hq, m_T, m_k_sel: that call's ws, out, Hq,
+ *   T, k_sel), in one launch.
+ * Every call gives the same bits as sparda_topk_block_sparse_attn and
+ * sparda_select_forecast. ws must not be reused until the merge has run (same
+ * stream, or ordered by events).
+ */
+int sparda_topk_block_sparse_attn_partial(const float* blk_scores, const void* q, const void* k, const void* v,
+                                          int32_t* idx, void* out, int dtype, int B, int Hq, int Hkv, int q_start,
+                                          const int* q_pos, int T, int d, int block, int k_sel, float scale,
+                                          void* ws, size_t ws_bytes, void* stream);
+int sparda_merge_partials(void* ws, size_t ws_bytes, void* out, int dtype, int B, int Hq, int Hkv, int T, int d,
+                          int k_sel, void* stream);
+int sparda_select_forecast_merge(const void* f, const void* k_cmp, float* blk_scores, int dtype, int B, int Hkv,
+                                 int q_start, const int* q_pos, int T, int d, int kernel, int stride, int block,
+                                 float scale, void* m_ws, size_t m_ws_bytes, void* m_out, int m_Hq, int m_T,
+                                 int m_k_sel, void* stream);
+
+/*
  * Step 5 - lookahead prefetch of the selected blocks from host memory.
  * [P1] paragraph on prefetching on a separate stream; [P2] 二 and 三: the blocks
  * the Forecast picks for the next layer are pulled from CPU memory into GPU

@@ -51,6 +51,11 @@ SIGNATURES = {
     "sparda_project_qkvf": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "sparda_topk_block_sparse_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _f,
                                            _vp, _sz, _vp]),
+    "sparda_topk_block_sparse_attn_partial": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _i, _i,
+                                                   _i, _f, _vp, _sz, _vp]),
+    "sparda_merge_partials": (_i, [_vp, _sz, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "sparda_select_forecast_merge": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp,
+                                          _i, _i, _i, _vp]),
     "sparda_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "sparda_status_string": (_c.c_char_p, [_i]),
     "sparda_last_error": (_c.c_char_p, []),
@@ -196,15 +201,26 @@ def append_kv(k_new, v_new, k_cache, v_cache, seq_len, k_cmp=None, status=None, 
           _ptr(status), _dtype_code(k_new), B, Hkv, n_new, T_cap, W_cap, d, KERNEL, STRIDE, _stream(k_new, stream))
 
 
-def select_forecast(f, k_cmp, T: int, q_start: int, scale: float | None = None, out=None, stream=None, q_pos=None):
+def select_forecast(f, k_cmp, T: int, q_start: int, scale: float | None = None, out=None, stream=None, q_pos=None,
+                    merge_from=None):
     """Forecast block scores [B, Hkv, nTiles, nB] (float32) for F [B, Hkv, Tq, 128].
-    q_pos (int32 device [B], decode only) gives each sequence its own position."""
+    q_pos (int32 device [B], decode only) gives each sequence its own position.
+    merge_from = (ws, out, T, k_sel) of a topk_block_sparse_attn(..., merge=False)
+    call with the same B and Hkv (decode only): that attention's merge runs in
+    the same launch."""
     torch = _torch()
     B, Hkv, Tq, d = f.shape
     scale = d ** -0.5 if scale is None else scale
     n_tiles = -(-Tq // TILE)
     if out is None:
         out = torch.empty((B, Hkv, n_tiles, T // BLOCK), dtype=torch.float32, device=f.device)
+    if merge_from is not None:
+        m_ws, m_out, m_T, m_k = merge_from
+        m_bytes = m_ws.numel() * m_ws.element_size() if m_ws is not None else 0
+        _call("sparda_select_forecast_merge", _ptr(f), _ptr(k_cmp), _ptr(out), _dtype_code(f), B, Hkv, q_start,
+              _positions(q_pos, B), T, d, KERNEL, STRIDE, BLOCK, scale, _ptr(m_ws), m_bytes, _ptr(m_out),
+              m_out.shape[1], m_T, m_k, _stream(f, stream))
+        return out
     _call("sparda_select_forecast", _ptr(f), _ptr(k_cmp), _ptr(out), _dtype_code(f), B, Hkv, Tq, q_start,
           _positions(q_pos, B), T, d, KERNEL, STRIDE, BLOCK, TILE, scale, None, 0, _stream(f, stream))
     return out
@@ -279,10 +295,12 @@ def project_qkvf(x, w, Hq: int, Hkv: int, n_f: int = 1, out=None, stream=None):
 
 
 def topk_block_sparse_attn(scores, q, k, v, k_sel: int, T: int, q_start: int, scale: float | None = None,
-                           idx=None, out=None, ws=None, stream=None, q_pos=None):
+                           idx=None, out=None, ws=None, stream=None, q_pos=None, merge: bool = True):
     """Top-k blocks of the decode scores [B, Hkv, 1, nB] and attention of q
     [B, Hq, 1, 128] over them, in one launch. Returns (idx [B, Hkv, 1, k_sel]
-    int32, O [B, Hq, 1, 128]), the same bits as topk_blocks + block_sparse_attn."""
+    int32, O [B, Hq, 1, 128]), the same bits as topk_blocks + block_sparse_attn.
+    merge=False leaves the block ranges' results in ``ws`` (pass one): O is
+    complete after merge_partials or select_forecast(..., merge_from=...)."""
     torch = _torch()
     B, Hq, Tq, d = q.shape
     Hkv = k.shape[1]
@@ -293,11 +311,25 @@ def topk_block_sparse_attn(scores, q, k, v, k_sel: int, T: int, q_start: int, sc
         idx = torch.empty((B, Hkv, 1, k_sel), dtype=torch.int32, device=q.device)
     if out is None:
         out = torch.empty_like(q)
-    ws, nbytes = _workspace(ws, workspace_bytes(OP_BLOCK_SPARSE_ATTN, B, Hq, Hkv, 1, T, k_sel), q)
-    _call("sparda_topk_block_sparse_attn", _ptr(scores), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out),
+    need = workspace_bytes(OP_BLOCK_SPARSE_ATTN, B, Hq, Hkv, 1, T, k_sel)
+    if not merge and ws is None and need > 0:
+        raise ValueError("merge=False needs the workspace that will be merged later")
+    ws, nbytes = _workspace(ws, need, q)
+    name = "sparda_topk_block_sparse_attn" if merge else "sparda_topk_block_sparse_attn_partial"
+    _call(name, _ptr(scores), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out),
           _dtype_code(q), B, Hq, Hkv, q_start, _positions(q_pos, B), T, d, BLOCK, k_sel, scale, _ptr(ws), nbytes,
           _stream(q, stream))
     return idx, out
+
+
+def merge_partials(ws, out, T: int, k_sel: int, Hkv: int, stream=None):
+    """Merge the block-range results a topk_block_sparse_attn(..., merge=False)
+    call left in ws into its output out [B, Hq, 1, 128]."""
+    B, Hq = out.shape[0], out.shape[1]
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _call("sparda_merge_partials", _ptr(ws), nbytes, _ptr(out), _dtype_code(out), B, Hq, Hkv, T, HEAD_DIM, k_sel,
+          _stream(out, stream))
+    return out
 
 
 def prefetch_blocks(host_k, host_v, idx, stage_k, stage_v, num_workgroups: int = 0, stream=None):

@@ -351,18 +351,18 @@ SPARDA_EXPORT int sparda_block_sparse_attn(const void* q, const void* k, const v
                     "block_sparse_attn launch");
 }
 
-SPARDA_EXPORT int sparda_topk_block_sparse_attn(const float* blk_scores, const void* q, const void* k, const void* v,
-                                                int32_t* idx, void* out, int dtype, int B, int Hq, int Hkv,
-                                                int q_start, const int* q_pos, int T, int d, int block, int k_sel,
-                                                float scale, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+int topk_attn_impl(const float* blk_scores, const void* q, const void* k, const void* v, int32_t* idx, void* out,
+                   int dtype, int B, int Hq, int Hkv, int q_start, const int* q_pos, int T, int d, int block,
+                   int k_sel, float scale, void* ws, size_t ws_bytes, bool merge, void* stream, const char* name) {
   if (int e = check_dtype(dtype)) return e;
   if (int e = check_geometry(B, Hq, Hkv, 1, q_start, T, d)) return e;
   CHECK(block == sparda::kBlock, SPARDA_ERR_UNSUPPORTED, "block %d != 64", block);
   CHECK(std::isfinite(scale), SPARDA_ERR_INVALID_ARG, "scale is not finite");
   const int nB = T / sparda::kBlock;
-  CHECK(nB <= 8192, SPARDA_ERR_UNSUPPORTED, "topk_block_sparse_attn: nB = %d above 8192", nB);
+  CHECK(nB <= 8192, SPARDA_ERR_UNSUPPORTED, "%s: nB = %d above 8192", name, nB);
   CHECK(k_sel >= 1 && k_sel <= nB, SPARDA_ERR_INVALID_ARG, "k = %d outside 1..nB (%d)", k_sel, nB);
-  CHECK(k_sel <= 1024, SPARDA_ERR_UNSUPPORTED, "topk_block_sparse_attn: k = %d above 1024", k_sel);
+  CHECK(k_sel <= 1024, SPARDA_ERR_UNSUPPORTED, "%s: k = %d above 1024", name, k_sel);
   if (B == 0) return ok();
   CHECK(blk_scores != nullptr && ((uintptr_t)blk_scores & 3u) == 0, SPARDA_ERR_INVALID_ARG,
         "blk_scores is NULL or not 4-byte aligned");
@@ -372,14 +372,80 @@ SPARDA_EXPORT int sparda_topk_block_sparse_attn(const float* blk_scores, const v
   CHECK_PTR(out);
   CHECK(idx != nullptr && ((uintptr_t)idx & 3u) == 0, SPARDA_ERR_INVALID_ARG, "idx is NULL or not 4-byte aligned");
   const size_t need = ws_bytes_for(SPARDA_OP_BLOCK_SPARSE_ATTN, B, Hq, Hkv, 1, T, k_sel);
-  CHECK(ws_bytes >= need, SPARDA_ERR_WORKSPACE, "topk_block_sparse_attn needs %zu workspace bytes, got %zu", need,
-        ws_bytes);
+  CHECK(ws_bytes >= need, SPARDA_ERR_WORKSPACE, "%s needs %zu workspace bytes, got %zu", name, need, ws_bytes);
   if (need) CHECK_PTR(ws);
   sparda::AttnDims ad = attn_dims(B, Hq, Hkv, 1, q_start, T, k_sel, scale, SPARDA_KV_CACHE);
   ad.q_pos = q_pos;
   return hip_status(sparda::launch_topk_attn_decode(blk_scores, q, k, v, idx, out, dtype == SPARDA_BF16, ad, ws,
-                                                    (hipStream_t)stream),
-                    "topk_block_sparse_attn launch");
+                                                    merge, (hipStream_t)stream),
+                    name);
+}
+
+// The partial results a decode attention of these sizes left in ws, checked.
+int pending_merge(const void* ws, size_t ws_bytes, int dtype, int B, int Hq, int Hkv, int T, int d, int k_sel,
+                  sparda::AttnDims* ad) {
+  if (int e = check_dtype(dtype)) return e;
+  if (int e = check_geometry(B, Hq, Hkv, 1, T - 1, T, d)) return e;
+  CHECK(k_sel >= 1 && k_sel <= T / sparda::kBlock, SPARDA_ERR_INVALID_ARG, "k = %d outside 1..nB (%d)", k_sel,
+        T / sparda::kBlock);
+  const size_t need = ws_bytes_for(SPARDA_OP_BLOCK_SPARSE_ATTN, B, Hq, Hkv, 1, T, k_sel);
+  CHECK(ws_bytes >= need, SPARDA_ERR_WORKSPACE, "the merged attention's workspace needs %zu bytes, got %zu", need,
+        ws_bytes);
+  *ad = attn_dims(B, Hq, Hkv, 1, T - 1, T, k_sel, 1.f, SPARDA_KV_CACHE);
+  return SPARDA_OK;
+}
+}  // namespace
+
+SPARDA_EXPORT int sparda_topk_block_sparse_attn(const float* blk_scores, const void* q, const void* k, const void* v,
+                                                int32_t* idx, void* out, int dtype, int B, int Hq, int Hkv,
+                                                int q_start, const int* q_pos, int T, int d, int block, int k_sel,
+                                                float scale, void* ws, size_t ws_bytes, void* stream) {
+  return topk_attn_impl(blk_scores, q, k, v, idx, out, dtype, B, Hq, Hkv, q_start, q_pos, T, d, block, k_sel, scale,
+                        ws, ws_bytes, true, stream, "topk_block_sparse_attn");
+}
+
+SPARDA_EXPORT int sparda_topk_block_sparse_attn_partial(const float* blk_scores, const void* q, const void* k,
+                                                        const void* v, int32_t* idx, void* out, int dtype, int B,
+                                                        int Hq, int Hkv, int q_start, const int* q_pos, int T, int d,
+                                                        int block, int k_sel, float scale, void* ws, size_t ws_bytes,
+                                                        void* stream) {
+  return topk_attn_impl(blk_scores, q, k, v, idx, out, dtype, B, Hq, Hkv, q_start, q_pos, T, d, block, k_sel, scale,
+                        ws, ws_bytes, false, stream, "topk_block_sparse_attn_partial");
+}
+
+SPARDA_EXPORT int sparda_merge_partials(void* ws, size_t ws_bytes, void* out, int dtype, int B, int Hq, int Hkv,
+                                        int T, int d, int k_sel, void* stream) {
+  sparda::AttnDims ad;
+  if (int e = pending_merge(ws, ws_bytes, dtype, B, Hq, Hkv, T, d, k_sel, &ad)) return e;
+  if (B == 0) return ok();
+  CHECK_PTR(out);
+  if (ws_bytes) CHECK_PTR(ws);
+  return hip_status(sparda::launch_merge_partials(ws, out, dtype == SPARDA_BF16, ad, (hipStream_t)stream),
+                    "merge_partials launch");
+}
+
+SPARDA_EXPORT int sparda_select_forecast_merge(const void* f, const void* k_cmp, float* blk_scores, int dtype, int B,
+                                               int Hkv, int q_start, const int* q_pos, int T, int d, int kernel,
+                                               int stride, int block, float scale, void* m_ws, size_t m_ws_bytes,
+                                               void* m_out, int m_Hq, int m_T, int m_k_sel, void* stream) {
+  if (int e = check_dtype(dtype)) return e;
+  if (int e = check_geometry(B, Hkv, Hkv, 1, q_start, T, d)) return e;
+  if (int e = check_select_params(kernel, stride, block, sparda::kTile, scale)) return e;
+  sparda::AttnDims ad;
+  if (int e = pending_merge(m_ws, m_ws_bytes, dtype, B, m_Hq, Hkv, m_T, d, m_k_sel, &ad)) return e;
+  if (B == 0) return ok();
+  CHECK_PTR(f);
+  CHECK_PTR(k_cmp);
+  CHECK_PTR(blk_scores);
+  CHECK_PTR(m_out);
+  if (m_ws_bytes) CHECK_PTR(m_ws);
+  if (int e = check_q_pos(q_pos, 1)) return e;
+  sparda::SelectDims sd = select_dims(B, Hkv, Hkv, 1, q_start, T, scale);
+  sd.q_pos = q_pos;
+  const sparda::DecodePartials p = sparda::decode_attn_partials(m_ws, ad);
+  return hip_status(sparda::launch_select_forecast_decode(f, k_cmp, blk_scores, dtype == SPARDA_BF16, sd,
+                                                          (hipStream_t)stream, &p, m_out),
+                    "select_forecast_merge launch");
 }
 
 namespace {

@@ -22,6 +22,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "merge_row.h"
 #include "topk_row.h"
 
 namespace sparda {
@@ -335,102 +336,11 @@ void attn_decode_kernel(
   }
 }
 
-// Merge the splits of one (row, head): thread = output channel. All the
-// row's (max, sum) pairs and the channel's partial sums are loaded in one
-// batch (independent loads), so the kernel costs one memory round trip.
-template <typename Tag, int MAXS>
-__global__ __launch_bounds__(kHeadDim) void attn_combine_kernel(const float* __restrict__ part_o,
-                                                                const float2* __restrict__ part_ml,
-                                                                uint8_t* __restrict__ out, int G,
-                                                                int splits) {
-  const long row = blockIdx.x;
-  const int g = blockIdx.y;
-  const int ch = threadIdx.x;
-  float2 ml[MAXS];
-  float po[MAXS];
-#pragma unroll
-  for (int s = 0; s < MAXS; ++s) {
-    if (s < splits) {
-      ml[s] = part_ml[(row * splits + s) * G + g];
-      po[s] = part_o[((row * splits + s) * G + g) * kHeadDim + ch];
-    }
-  }
-  float M = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < MAXS; ++s)
-    if (s < splits) M = fmaxf(M, ml[s].x);
-  float L = 0.f, O = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll
-    for (int s = 0; s < MAXS; ++s) {
-      if (s < splits && ml[s].x != -INFINITY) {
-        const float w = fast_exp(ml[s].x - M);
-        L = fmaf(ml[s].y, w, L);
-        O = fmaf(po[s], w, O);
-      }
-    }
-  }
-  const float o = L > 0.f ? O / L : 0.f;
-  const long off = (row * G + g) * kHeadDim + ch;
-  if constexpr (DT<Tag>::kBytes == 2) {
-    reinterpret_cast<__bf16*>(out)[off] = (__bf16)o;
-  } else {
-    reinterpret_cast<float*>(out)[off] = o;
-  }
-}
-
-// The same merge with one workgroup per row: thread = (head, 4 channels),
-// float4 partial loads and one 8-byte bf16 store (or 16-byte fp32) per thread.
-#ifndef SPARDA_COMBINE_ROW
-#define SPARDA_COMBINE_ROW 1
-#endif
 template <typename Tag, int MAXS>
 __global__ __launch_bounds__(256) void attn_combine_row_kernel(const float* __restrict__ part_o,
                                                                const float2* __restrict__ part_ml,
                                                                uint8_t* __restrict__ out, int G, int splits) {
-  const long row = blockIdx.x;
-  const int g = threadIdx.x / (kHeadDim / 4);
-  const int ch = (threadIdx.x % (kHeadDim / 4)) * 4;
-  if (g >= G) return;
-  float2 ml[MAXS];
-  float4 po[MAXS];
-#pragma unroll
-  for (int s = 0; s < MAXS; ++s) {
-    if (s < splits) {
-      ml[s] = part_ml[(row * splits + s) * G + g];
-      po[s] = *reinterpret_cast<const float4*>(part_o + ((row * splits + s) * G + g) * kHeadDim + ch);
-    }
-  }
-  float M = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < MAXS; ++s)
-    if (s < splits) M = fmaxf(M, ml[s].x);
-  float L = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
-  if (M != -INFINITY) {
-#pragma unroll
-    for (int s = 0; s < MAXS; ++s) {
-      if (s < splits && ml[s].x != -INFINITY) {
-        const float w = fast_exp(ml[s].x - M);
-        L = fmaf(ml[s].y, w, L);
-        O[0] = fmaf(po[s].x, w, O[0]);
-        O[1] = fmaf(po[s].y, w, O[1]);
-        O[2] = fmaf(po[s].z, w, O[2]);
-        O[3] = fmaf(po[s].w, w, O[3]);
-      }
-    }
-  }
-  float o[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = L > 0.f ? O[e] / L : 0.f;
-  const long off = (row * G + g) * kHeadDim + ch;
-  if constexpr (DT<Tag>::kBytes == 2) {
-    uint2 v;
-    v.x = pack_bf16(o[0], o[1]);
-    v.y = pack_bf16(o[2], o[3]);
-    *reinterpret_cast<uint2*>(out + off * 2) = v;
-  } else {
-    *reinterpret_cast<float4*>(out + off * 4) = make_float4(o[0], o[1], o[2], o[3]);
-  }
+  merge_row<Tag, MAXS>(blockIdx.x, threadIdx.x, part_o, part_ml, out, G, splits);
 }
 
 int decode_attn_splits(const AttnDims& d) {
@@ -455,19 +365,45 @@ size_t decode_attn_ws_bytes(const AttnDims& d) {
   return align256(n * kHeadDim * sizeof(float)) + align256(n * sizeof(float2));
 }
 
+DecodePartials decode_attn_partials(void* ws, const AttnDims& d) {
+  DecodePartials p{nullptr, nullptr, decode_attn_splits(d), d.Hq / d.Hkv, d.B * d.Hkv};
+  if (p.splits > 1) {
+    const size_t n = (size_t)p.rows * p.splits * p.G;
+    p.part_o = (float*)ws;
+    p.part_ml = (float2*)((char*)ws + align256(n * kHeadDim * sizeof(float)));
+  }
+  return p;
+}
+
+template <typename Tag>
+static void launch_merge(const DecodePartials& p, void* out, hipStream_t s) {
+  if (p.splits <= 1) return;  // one range per row: the attention wrote the output itself
+  if (p.splits <= 16)
+    hipLaunchKernelGGL((attn_combine_row_kernel<Tag, 16>), dim3(p.rows), dim3(p.G * (kHeadDim / 4)), 0, s, p.part_o,
+                       p.part_ml, (uint8_t*)out, p.G, p.splits);
+  else
+    hipLaunchKernelGGL((attn_combine_row_kernel<Tag, kAttnMaxSplits>), dim3(p.rows), dim3(p.G * (kHeadDim / 4)), 0,
+                       s, p.part_o, p.part_ml, (uint8_t*)out, p.G, p.splits);
+}
+
+hipError_t launch_merge_partials(void* ws, void* out, bool bf16, const AttnDims& d, hipStream_t s) {
+  const DecodePartials p = decode_attn_partials(ws, d);
+  if (bf16)
+    launch_merge<BF16Tag>(p, out, s);
+  else
+    launch_merge<F32Tag>(p, out, s);
+  return hipGetLastError();
+}
+
 template <typename Tag, int G>
 static void launch_attn_g(const void* q, const void* k, const void* v, const int32_t* idx, const float* scores,
-                          void* out, const AttnDims& d, void* ws, hipStream_t s) {
-  const int splits = decode_attn_splits(d);
+                          void* out, const AttnDims& d, void* ws, bool merge, hipStream_t s) {
+  const DecodePartials pp = decode_attn_partials(ws, d);
+  const int splits = pp.splits;
   const int bps = (d.k + splits - 1) / splits;
-  const int rows = d.B * d.Hkv;
-  float* part_o = nullptr;
-  float2* part_ml = nullptr;
-  if (splits > 1) {
-    const size_t n = (size_t)rows * splits * G;
-    part_o = (float*)ws;
-    part_ml = (float2*)((char*)ws + align256(n * kHeadDim * sizeof(float)));
-  }
+  const int rows = pp.rows;
+  float* part_o = pp.part_o;
+  float2* part_ml = pp.part_ml;
   if (scores == nullptr) {
     hipLaunchKernelGGL((attn_decode_kernel<Tag, G, 1, 0>), dim3(rows, splits), dim3(kWave), 0, s,
                        (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, nullptr, nullptr, part_o, part_ml, (uint8_t*)out, d.T, d.nB, d.k, d.kv_mode, d.q_start, d.q_pos, d.Hkv,
@@ -487,33 +423,18 @@ static void launch_attn_g(const void* q, const void* k, const void* v, const int
     else SPARDA_FUSED(32);
 #undef SPARDA_FUSED
   }
-  if (splits > 1 && SPARDA_COMBINE_ROW && G * (kHeadDim / 4) <= 256) {
-    if (splits <= 16)
-      hipLaunchKernelGGL((attn_combine_row_kernel<Tag, 16>), dim3(rows), dim3(G * (kHeadDim / 4)), 0, s, part_o,
-                         part_ml, (uint8_t*)out, G, splits);
-    else
-      hipLaunchKernelGGL((attn_combine_row_kernel<Tag, kAttnMaxSplits>), dim3(rows), dim3(G * (kHeadDim / 4)), 0, s,
-                         part_o, part_ml, (uint8_t*)out, G, splits);
-  } else if (splits > 1) {
-    const dim3 grid(rows, G);
-    if (splits <= 16)
-      hipLaunchKernelGGL((attn_combine_kernel<Tag, 16>), grid, dim3(kHeadDim), 0, s, part_o, part_ml,
-                         (uint8_t*)out, G, splits);
-    else
-      hipLaunchKernelGGL((attn_combine_kernel<Tag, kAttnMaxSplits>), grid, dim3(kHeadDim), 0, s, part_o,
-                         part_ml, (uint8_t*)out, G, splits);
-  }
+  if (merge) launch_merge<Tag>(pp, out, s);
 }
 
 hipError_t launch_attn_decode(const void* q, const void* k, const void* v, const int32_t* idx,
                               void* out, bool bf16, const AttnDims& d, void* ws, hipStream_t s) {
-  return launch_topk_attn_decode(nullptr, q, k, v, const_cast<int32_t*>(idx), out, bf16, d, ws, s);
+  return launch_topk_attn_decode(nullptr, q, k, v, const_cast<int32_t*>(idx), out, bf16, d, ws, true, s);
 }
 
 hipError_t launch_topk_attn_decode(const float* scores, const void* q, const void* k, const void* v, int32_t* idx,
-                                   void* out, bool bf16, const AttnDims& d, void* ws, hipStream_t s) {
+                                   void* out, bool bf16, const AttnDims& d, void* ws, bool merge, hipStream_t s) {
   const int G = d.Hq / d.Hkv;
-#define SPARDA_AT(TAG, GG) launch_attn_g<TAG, GG>(q, k, v, idx, scores, out, d, ws, s)
+#define SPARDA_AT(TAG, GG) launch_attn_g<TAG, GG>(q, k, v, idx, scores, out, d, ws, merge, s)
 #define SPARDA_AT_G(TAG)                  \
   switch (G) {                            \
     case 1: SPARDA_AT(TAG, 1); break;     \

@@ -30,6 +30,13 @@ struct AttnDims {
   int n_slots;             // kv_mode 2: staging slots per row
 };
 
+// where a decode attention's block-range results sit in its workspace
+struct DecodePartials {
+  float* part_o;    // [rows, splits, G, 128]
+  float2* part_ml;  // [rows, splits, G] (max, sum)
+  int splits, G, rows;
+};
+
 // compress.hip: windows [w_begin, w_end) of rows holding T tokens and W windows
 hipError_t launch_compress(const void* k, void* kc, bool bf16, int rows, int T, int W, int w_begin, int w_end,
                            hipStream_t s);
@@ -44,7 +51,8 @@ int append_grid_y(bool bf16, int n_new, bool with_windows);  // workgroups per r
 
 // select_decode.hip
 hipError_t launch_select_forecast_decode(const void* f, const void* kc, float* scores, bool bf16,
-                                         const SelectDims& d, hipStream_t s);
+                                         const SelectDims& d, hipStream_t s,
+                                         const DecodePartials* merge = nullptr, void* merge_out = nullptr);
 size_t multihead_decode_ws_bytes(const SelectDims& d);
 hipError_t launch_select_multihead_decode(const void* q, const void* kc, float* scores, bool bf16,
                                           const SelectDims& d, void* ws, hipStream_t s);
@@ -66,9 +74,12 @@ size_t decode_attn_ws_bytes(const AttnDims& d);
 hipError_t launch_attn_decode(const void* q, const void* k, const void* v, const int32_t* idx,
                               void* out, bool bf16, const AttnDims& d, void* ws, hipStream_t s);
 // the same after the row's top-k of scores [rows, nB] (written to idx), in one
-// launch; needs nB <= 8192 and k <= 1024
+// launch; needs nB <= 8192 and k <= 1024. merge = false leaves the block
+// ranges' results in ws (the output is complete once they are merged).
 hipError_t launch_topk_attn_decode(const float* scores, const void* q, const void* k, const void* v, int32_t* idx,
-                                   void* out, bool bf16, const AttnDims& d, void* ws, hipStream_t s);
+                                   void* out, bool bf16, const AttnDims& d, void* ws, bool merge, hipStream_t s);
+DecodePartials decode_attn_partials(void* ws, const AttnDims& d);
+hipError_t launch_merge_partials(void* ws, void* out, bool bf16, const AttnDims& d, hipStream_t s);
 
 // attn_prefill.hip (bf16, cache mode, Tq % 64 == 0)
 hipError_t launch_attn_prefill(const void* q, const void* k, const void* v, const int32_t* idx, void* out,

@@ -19,6 +19,7 @@
 // normalise, sum over the group, pool into blocks.
 #include "common.h"
 #include "launch.h"
+#include "merge_row.h"
 
 namespace sparda {
 
@@ -38,12 +39,24 @@ struct RowGeom {
 };
 
 // ---------------------------------------------------------------- Forecast --
-template <typename Tag>
-__global__ __launch_bounds__(256) void fsel_decode_kernel(const uint8_t* __restrict__ f,
+// MERGE: the grid has one more row of workgroups, dispatched first (y = 0),
+// each merging one row of a previous decode attention's block-range results
+// (merge_row_lean, the merge kernel's bits); the others score as usual.
+template <typename Tag, bool MERGE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void fsel_decode_kernel(const uint8_t* __restrict__ f,
                                                           const uint8_t* __restrict__ kc,
                                                           float* __restrict__ scores, int W, int nB,
                                                           int n_vis, const int* __restrict__ q_pos, int hkv,
-                                                          int T, float scale) {
+                                                          int T, float scale, const float* __restrict__ m_part_o,
+                                                          const float2* __restrict__ m_part_ml,
+                                                          uint8_t* __restrict__ m_out, int m_G, int m_splits) {
+  if constexpr (MERGE) {
+    if (blockIdx.y == 0) {
+      merge_row_lean<Tag>(blockIdx.x, threadIdx.x, m_part_o, m_part_ml, m_out, m_G, m_splits);
+      return;
+    }
+  }
+  const int chunk = blockIdx.y - (MERGE ? 1 : 0);
   using R = RowGeom<Tag>;
   constexpr int NWIN = 4 * kFselBlocks + 1;
   constexpr int ITER = (NWIN + R::SLOTS - 1) / R::SLOTS;
@@ -51,7 +64,7 @@ __global__ __launch_bounds__(256) void fsel_decode_kernel(const uint8_t* __restr
 
   const long row = blockIdx.x;  // rows on the fast axis: a row's chunks share an XCD
   if (q_pos != nullptr) n_vis = visible_windows(row_position(q_pos, row, hkv, 0, T), W);
-  const int beta0 = blockIdx.y * kFselBlocks;
+  const int beta0 = chunk * kFselBlocks;
   const int nblk = min(kFselBlocks, nB - beta0);
   const int nwin = 4 * nblk + 1;
   const int wstart = 4 * beta0 - 1;
@@ -88,15 +101,25 @@ __global__ __launch_bounds__(256) void fsel_decode_kernel(const uint8_t* __restr
 }
 
 hipError_t launch_select_forecast_decode(const void* f, const void* kc, float* scores, bool bf16,
-                                         const SelectDims& d, hipStream_t s) {
+                                         const SelectDims& d, hipStream_t s, const DecodePartials* merge,
+                                         void* merge_out) {
   const int n_vis = min(d.W, (d.q_start - kKernel + 1) >= 0 ? (d.q_start - kKernel + 1) / kStride + 1 : 0);
-  dim3 grid(d.B * d.Hkv, (d.nB + kFselBlocks - 1) / kFselBlocks);
-  if (bf16)
-    hipLaunchKernelGGL(fsel_decode_kernel<BF16Tag>, grid, dim3(256), 0, s, (const uint8_t*)f,
-                       (const uint8_t*)kc, scores, d.W, d.nB, n_vis, d.q_pos, d.Hkv, d.T, d.scale);
-  else
-    hipLaunchKernelGGL(fsel_decode_kernel<F32Tag>, grid, dim3(256), 0, s, (const uint8_t*)f,
-                       (const uint8_t*)kc, scores, d.W, d.nB, n_vis, d.q_pos, d.Hkv, d.T, d.scale);
+  // a merge is only needed when the attention split its rows (it wrote the
+  // output itself otherwise); its rows are this call's rows
+  const bool m = merge != nullptr && merge->splits > 1;
+  dim3 grid(d.B * d.Hkv, (d.nB + kFselBlocks - 1) / kFselBlocks + (m ? 1 : 0));
+  const float* mo = m ? merge->part_o : nullptr;
+  const float2* mml = m ? merge->part_ml : nullptr;
+  const int mG = m ? merge->G : 0, ms = m ? merge->splits : 0;
+#define SPARDA_FSEL(TAG, MM)                                                                                  \
+  hipLaunchKernelGGL((fsel_decode_kernel<TAG, MM>), grid, dim3(256), 0, s, (const uint8_t*)f, (const uint8_t*)kc, \
+                     scores, d.W, d.nB, n_vis, d.q_pos, d.Hkv, d.T, d.scale, mo, mml, (uint8_t*)merge_out, mG, ms)
+  if (bf16) {
+    if (m) SPARDA_FSEL(BF16Tag, true); else SPARDA_FSEL(BF16Tag, false);
+  } else {
+    if (m) SPARDA_FSEL(F32Tag, true); else SPARDA_FSEL(F32Tag, false);
+  }
+#undef SPARDA_FSEL
   return hipGetLastError();
 }
 

@@ -97,3 +97,116 @@ def test_fused_ragged_positions(gpu):
     w = small("bf16", B=4, Hq=8, Hkv=2, k=6)
     q_pos = torch.tensor([w.T - 1, 70, 64 * 20 + 5, 31], dtype=torch.int32, device=DEV)
     _case(gpu, w, q_pos=q_pos)
+
+
+# ------------------------------------------- merge deferred to the next layer ----
+def _layers(gpu, w, n, seed0=40):
+    """n layers' inputs of one decode shape: Q, K, V, F, compressed keys."""
+    out = []
+    for l in range(n):
+        wl_ = wl.scaled(w, seed=seed0 + l)
+        Q, K, V, F = (sg.tensor(wl_.recipe(nm), wl_.shape(nm), DEV) for nm in ("Q", "K", "V", "F"))
+        out.append(dict(Q=Q, K=K, V=V, F=F, Kc=gpu.compress_keys(K)))
+    return out
+
+
+@pytest.mark.parametrize("dtype,G,k", [("bf16", 4, 5), ("bf16", 4, 37), ("bf16", 8, 20), ("fp32", 2, 9),
+                                       ("bf16", 4, 1)])
+def test_merge_deferred_to_next_selection(gpu, dtype, G, k):
+    """Layer 0 attends without merging; layer 1's selection merges it in the
+    same launch; layer 1 attends and is merged on its own. Every output, score
+    and selection holds the bits of the unpipelined calls (k = 1: rows are
+    not split, the attention writes its output and the merge does nothing)."""
+    w = small(dtype, B=3, Hq=2 * G, Hkv=2, k=k)
+    L = _layers(gpu, w, 2)
+    ref = []
+    for l in range(2):
+        s = gpu.select_forecast(L[l]["F"], L[l]["Kc"], w.T, w.q_start)
+        i, o = gpu.topk_block_sparse_attn(s, L[l]["Q"], L[l]["K"], L[l]["V"], w.k, w.T, w.q_start)
+        ref.append((s, i, o))
+    nbytes = gpu.workspace_bytes(gpu.OP_BLOCK_SPARSE_ATTN, w.B, w.Hq, w.Hkv, 1, w.T, w.k)
+    ws = torch.full((max(nbytes, 1),), 0x55, dtype=torch.uint8, device=DEV) if nbytes else None
+    outs = [torch.full_like(L[l]["Q"], 7.0) for l in range(2)]
+    s0 = gpu.select_forecast(L[0]["F"], L[0]["Kc"], w.T, w.q_start)
+    i0, _ = gpu.topk_block_sparse_attn(s0, L[0]["Q"], L[0]["K"], L[0]["V"], w.k, w.T, w.q_start, out=outs[0], ws=ws,
+                                       merge=False)
+    s1 = gpu.select_forecast(L[1]["F"], L[1]["Kc"], w.T, w.q_start, merge_from=(ws, outs[0], w.T, w.k))
+    i1, _ = gpu.topk_block_sparse_attn(s1, L[1]["Q"], L[1]["K"], L[1]["V"], w.k, w.T, w.q_start, out=outs[1], ws=ws,
+                                       merge=False)
+    gpu.merge_partials(ws, outs[1], w.T, w.k, w.Hkv)
+    torch.cuda.synchronize()
+    for l, (s, i) in enumerate(((s0, i0), (s1, i1))):
+        assert torch.equal(s, ref[l][0]), f"layer {l}: scores"
+        assert torch.equal(i, ref[l][1]), f"layer {l}: selection"
+        assert torch.equal(bits(outs[l]), bits(ref[l][2])), f"layer {l}: attention output"
+    say(f"deferred merge {dtype} G {G} k {k}: same bits")
+
+
+def test_merge_deferred_with_positions(gpu):
+    """Per-sequence positions in both layers: the same bits as without deferral."""
+    w = small("bf16", B=4, Hq=8, Hkv=2, k=6)
+    L = _layers(gpu, w, 2, seed0=60)
+    q_pos = torch.tensor([w.T - 1, 70, 64 * 20 + 5, 300], dtype=torch.int32, device=DEV)
+    ref = []
+    for l in range(2):
+        s = gpu.select_forecast(L[l]["F"], L[l]["Kc"], w.T, 0, q_pos=q_pos)
+        ref.append(gpu.topk_block_sparse_attn(s, L[l]["Q"], L[l]["K"], L[l]["V"], w.k, w.T, 0, q_pos=q_pos)[1])
+    ws = torch.zeros(gpu.workspace_bytes(gpu.OP_BLOCK_SPARSE_ATTN, w.B, w.Hq, w.Hkv, 1, w.T, w.k), dtype=torch.uint8,
+                     device=DEV)
+    outs = [torch.empty_like(L[l]["Q"]) for l in range(2)]
+    s0 = gpu.select_forecast(L[0]["F"], L[0]["Kc"], w.T, 0, q_pos=q_pos)
+    gpu.topk_block_sparse_attn(s0, L[0]["Q"], L[0]["K"], L[0]["V"], w.k, w.T, 0, out=outs[0], ws=ws, q_pos=q_pos,
+                               merge=False)
+    s1 = gpu.select_forecast(L[1]["F"], L[1]["Kc"], w.T, 0, q_pos=q_pos, merge_from=(ws, outs[0], w.T, w.k))
+    gpu.topk_block_sparse_attn(s1, L[1]["Q"], L[1]["K"], L[1]["V"], w.k, w.T, 0, out=outs[1], ws=ws, q_pos=q_pos,
+                               merge=False)
+    gpu.merge_partials(ws, outs[1], w.T, w.k, w.Hkv)
+    torch.cuda.synchronize()
+    for l in range(2):
+        assert torch.equal(bits(outs[l]), bits(ref[l])), f"layer {l}"
+
+
+def test_merge_deferred_graph_replay(gpu):
+    """Two pipelined layers captured in a HIP graph give the eager bits on every
+    replay, with eager work and synchronisations between replays."""
+    w = wl.C2_DECODE_32K
+    L = _layers(gpu, w, 2, seed0=80)
+    ws = torch.zeros(gpu.workspace_bytes(gpu.OP_BLOCK_SPARSE_ATTN, w.B, w.Hq, w.Hkv, 1, w.T, w.k), dtype=torch.uint8,
+                     device=DEV)
+    sc = [torch.empty((w.B, w.Hkv, 1, w.nB), dtype=torch.float32, device=DEV) for _ in range(2)]
+    ix = [torch.empty((w.B, w.Hkv, 1, w.k), dtype=torch.int32, device=DEV) for _ in range(2)]
+    outs = [torch.empty_like(L[l]["Q"]) for l in range(2)]
+
+    def run():
+        gpu.select_forecast(L[0]["F"], L[0]["Kc"], w.T, w.q_start, out=sc[0])
+        gpu.topk_block_sparse_attn(sc[0], L[0]["Q"], L[0]["K"], L[0]["V"], w.k, w.T, w.q_start, idx=ix[0],
+                                   out=outs[0], ws=ws, merge=False)
+        gpu.select_forecast(L[1]["F"], L[1]["Kc"], w.T, w.q_start, out=sc[1], merge_from=(ws, outs[0], w.T, w.k))
+        gpu.topk_block_sparse_attn(sc[1], L[1]["Q"], L[1]["K"], L[1]["V"], w.k, w.T, w.q_start, idx=ix[1],
+                                   out=outs[1], ws=ws, merge=False)
+        gpu.merge_partials(ws, outs[1], w.T, w.k, w.Hkv)
+
+    run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in sc + ix + outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(4):
+        for t in sc + outs:
+            t.zero_()
+        for t in ix:
+            t.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(sc + ix + outs, ref):
+            assert torch.equal(bits(got) if got.dtype == torch.bfloat16 else got,
+                               bits(want) if want.dtype == torch.bfloat16 else want), f"replay {rep}"
+        run()  # eager work between replays
+        torch.cuda.synchronize()
