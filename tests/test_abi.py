@@ -237,3 +237,64 @@ def test_project_qkvf_empty_batch_and_no_forecast(lib):
     assert lib.sparda_project_qkvf(None, None, None, None, None, None, 1, 0, 4096, 32, 8, 1, 128, None) == 0
     assert lib.sparda_project_qkvf(P, P, P, P, P, None, 1, 0, 4096, 32, 8, 0, 128, None) == 0
 
+
+
+def _topk_attn(lib, name="sparda_topk_block_sparse_attn", **kw):
+    a = dict(s=P, q=P, k=P, v=P, idx=P, out=P, dtype=1, B=16, Hq=32, Hkv=8, q_start=131071, q_pos=None, T=131072,
+             d=128, block=64, k_sel=64, scale=0.088, ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    return getattr(lib, name)(a["s"], a["q"], a["k"], a["v"], a["idx"], a["out"], a["dtype"], a["B"], a["Hq"],
+                              a["Hkv"], a["q_start"], a["q_pos"], a["T"], a["d"], a["block"], a["k_sel"], a["scale"],
+                              a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("name", ["sparda_topk_block_sparse_attn", "sparda_topk_block_sparse_attn_partial"])
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=5), 1, b"dtype"),
+    (dict(T=64 * 8193, q_start=64 * 8193 - 1), 2, b"above 8192"),
+    (dict(k_sel=1025, T=64 * 2000, q_start=64 * 2000 - 1), 2, b"above 1024"),
+    (dict(k_sel=0), 1, b"outside 1..nB"),
+    (dict(block=32), 2, b"block"),
+    (dict(s=None), 1, b"blk_scores is NULL"),
+    (dict(idx=P + 2), 1, b"idx is NULL or not 4-byte aligned"),
+    (dict(ws_bytes=100), 3, b"workspace"),
+])
+def test_topk_attn_validation(lib, name, kw, status, needle):
+    st = _topk_attn(lib, name, **kw)
+    assert st == status and needle in lib.sparda_last_error(), lib.sparda_last_error()
+
+
+def test_topk_attn_empty_batch(lib):
+    assert _topk_attn(lib, B=0, s=None, q=None, k=None, v=None, idx=None, out=None, ws=None, ws_bytes=0) == 0
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(ws_bytes=100), 3, b"workspace"),
+    (dict(out=None), 1, b"out is NULL"),
+    (dict(k_sel=0), 1, b"outside 1..nB"),
+    (dict(Hq=12), 1, b"not a multiple of Hkv"),
+])
+def test_merge_partials_validation(lib, kw, status, needle):
+    a = dict(ws=P, ws_bytes=1 << 30, out=P, dtype=1, B=16, Hq=32, Hkv=8, T=131072, d=128, k_sel=64)
+    a.update(kw)
+    st = lib.sparda_merge_partials(a["ws"], a["ws_bytes"], a["out"], a["dtype"], a["B"], a["Hq"], a["Hkv"], a["T"],
+                                   a["d"], a["k_sel"], None)
+    assert st == status and needle in lib.sparda_last_error(), lib.sparda_last_error()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(m_ws_bytes=100), 3, b"workspace"),
+    (dict(m_out=None), 1, b"m_out is NULL"),
+    (dict(kernel=16), 2, b"kernel/stride"),
+    (dict(m_k_sel=4096), 1, b"outside 1..nB"),
+    (dict(f=None), 1, b"f is NULL"),
+])
+def test_select_forecast_merge_validation(lib, kw, status, needle):
+    a = dict(f=P, kc=P, s=P, dtype=1, B=16, Hkv=8, q_start=131071, q_pos=None, T=131072, d=128, kernel=32, stride=16,
+             block=64, scale=0.088, m_ws=P, m_ws_bytes=1 << 30, m_out=P, m_Hq=32, m_T=131072, m_k_sel=64)
+    a.update(kw)
+    st = lib.sparda_select_forecast_merge(a["f"], a["kc"], a["s"], a["dtype"], a["B"], a["Hkv"], a["q_start"],
+                                          a["q_pos"], a["T"], a["d"], a["kernel"], a["stride"], a["block"], a["scale"],
+                                          a["m_ws"], a["m_ws_bytes"], a["m_out"], a["m_Hq"], a["m_T"], a["m_k_sel"],
+                                          None)
+    assert st == status and needle in lib.sparda_last_error(), lib.sparda_last_error()
