@@ -17,7 +17,11 @@
 //         the wave once at the end.
 //   PV  - the same lane layout over V; each lane accumulates G x 8 outputs for
 //         its key row, reading p[key][0..G) from LDS as one broadcast.
-// A combine kernel merges the per-split (max, sum, unnormalised output).
+// Each split leaves its (max, sum, unnormalised output); a merge kernel
+// (merge_row.h) combines a row's splits. Two more forms of the same kernel:
+// four splits per workgroup with the row's top-k taken first by the whole
+// workgroup (topk_row.h; the selection then comes from LDS), and the merge
+// left to a later launch, such as the next layer's selection.
 #include <type_traits>
 
 #include "common.h"

@@ -11,7 +11,9 @@
 // 4b-1 .. 4b+3), so it finishes its block scores with no exchange between
 // workgroups. 16 lanes hold one 256-byte window row (8 bf16 each); a wave reads
 // 4 rows (1 KiB contiguous) per load. The dot products use v_dot2_f32_bf16 and a
-// DPP butterfly across the 16 lanes.
+// DPP butterfly across the 16 lanes. The Forecast kernel can also merge a
+// previous decode attention's split results (extra workgroups dispatched
+// first), since the next layer's selection needs nothing from that output.
 //
 // The multi-head selector needs each head's softmax normaliser over all
 // windows before it can sum heads, so it runs in two passes: (1) logits to the
