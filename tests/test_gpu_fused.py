@@ -93,9 +93,11 @@ def test_fused_ties_and_non_candidates(gpu):
 
 
 def test_fused_ragged_positions(gpu):
-    """Per-sequence query positions: the same bits as the separate calls."""
-    w = small("bf16", B=4, Hq=8, Hkv=2, k=6)
-    q_pos = torch.tensor([w.T - 1, 70, 64 * 20 + 5, 31], dtype=torch.int32, device=DEV)
+    """Per-sequence query positions, one of them before its first complete
+    window (no candidate block: all -1, output 0): the same bits as the
+    separate calls."""
+    w = small("bf16", B=5, Hq=8, Hkv=2, k=6)
+    q_pos = torch.tensor([w.T - 1, 70, 64 * 20 + 5, 31, 5], dtype=torch.int32, device=DEV)
     _case(gpu, w, q_pos=q_pos)
 
 
@@ -143,10 +145,11 @@ def test_merge_deferred_to_next_selection(gpu, dtype, G, k):
 
 
 def test_merge_deferred_with_positions(gpu):
-    """Per-sequence positions in both layers: the same bits as without deferral."""
-    w = small("bf16", B=4, Hq=8, Hkv=2, k=6)
+    """Per-sequence positions in both layers, one sequence with no candidate
+    block yet: the same bits as without deferral."""
+    w = small("bf16", B=5, Hq=8, Hkv=2, k=6)
     L = _layers(gpu, w, 2, seed0=60)
-    q_pos = torch.tensor([w.T - 1, 70, 64 * 20 + 5, 300], dtype=torch.int32, device=DEV)
+    q_pos = torch.tensor([w.T - 1, 70, 64 * 20 + 5, 300, 5], dtype=torch.int32, device=DEV)
     ref = []
     for l in range(2):
         s = gpu.select_forecast(L[l]["F"], L[l]["Kc"], w.T, 0, q_pos=q_pos)
@@ -164,6 +167,7 @@ def test_merge_deferred_with_positions(gpu):
     torch.cuda.synchronize()
     for l in range(2):
         assert torch.equal(bits(outs[l]), bits(ref[l])), f"layer {l}"
+        assert not outs[l][4].float().any(), "a sequence with no visible block attends to nothing"
 
 
 def test_merge_deferred_graph_replay(gpu):
