@@ -128,9 +128,17 @@ def test_c3_full_size_sampled_parity(gpu):
         for g in range(w.G):
             ref_o = oracle.attend(q_rows[g, 0], k64[J], v64[J], w.scale)
             parity.check_attention(parity.to_f64(out[b, h * w.G + g, 0]), ref_o, parity.ATTN_ATOL_BF16)
-    # the fused top-k + attention launch the benchmark's step uses: same bits
+    # the fused top-k + attention launch: same bits
     idx_f, out_f = gpu.topk_block_sparse_attn(sf, Q, K, V, w.k, w.T, w.q_start, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(idx_f, idx), "fused top-k differs from sparda_topk_blocks"
     assert torch.equal(bits(out_f), bits(out)), "fused attention differs from sparda_block_sparse_attn"
+    # the benchmark's layer order: the attention leaves its merge to the next
+    # layer's selection launch (here the same inputs stand in for that layer)
+    out_p = torch.zeros_like(out)
+    idx_p, _ = gpu.topk_block_sparse_attn(sf, Q, K, V, w.k, w.T, w.q_start, out=out_p, ws=ws, merge=False)
+    sf_next = gpu.select_forecast(F, Kc, w.T, w.q_start, merge_from=(ws, out_p, w.T, w.k))
+    torch.cuda.synchronize()
+    assert torch.equal(idx_p, idx) and torch.equal(sf_next, sf), "layer-order selection or top-k differs"
+    assert torch.equal(bits(out_p), bits(out)), "attention merged in the next selection launch differs"
 
