@@ -57,6 +57,8 @@ def algorithmic_bytes(w) -> dict:
         "topk_attention": scores + idx + kv + q + o,
         "topk_attention_partial": scores + idx + kv + q,
         "select_forecast_merge": kc + f + scores + o,
+        # one launch: the next layer's selection, this layer's top-k + attention, the merge of the layer before
+        "decode_layer": (kc + f + scores) + (scores + idx + kv + q) + o,
         "step": kc + f + scores + (scores + idx) + (kv + q + idx + o),
     }
 
@@ -281,6 +283,16 @@ def bench_decode(args) -> int:
         kbs.select_forecast(s["F"], s["Kc"], w.T, w.q_start, out=s["scores"],
                             merge_from=(ws_attn, prev["out"], w.T, w.k))
 
+    ws_pair = [ws_attn, torch.zeros_like(ws_attn)]
+
+    def step_one_launch(i):
+        # layer i in one launch: the merge of layer i-1 (its results in the
+        # other workspace), layer i's top-k + attention, layer i+1's selection
+        s, prev, nxt = sets[i % N_SETS], sets[(i - 1) % N_SETS], sets[(i + 1) % N_SETS]
+        kbs.decode_layer(s["scores"], s["Q"], s["K"], s["V"], w.k, w.T, w.q_start, ws_pair[i % 2], idx=s["idx"],
+                         out=s["out"], merge_from=(ws_pair[(i - 1) % 2], prev["out"], w.T, w.k),
+                         select_next=(nxt["F"], nxt["Kc"], nxt["scores"], w.T, w.q_start))
+
     def step_pipelined(i):
         # layer i in the method's layer order: its selection (from the layer
         # before's Forecast) shares a launch with the merge of the layer
@@ -314,22 +326,29 @@ def bench_decode(args) -> int:
     for i in range(args.warmup):
         step_pipelined(i)
     torch.cuda.synchronize()
-    ms_step_eager = time_loop(step_pipelined, args.steps, stream)
+    for i in range(6):
+        step_one_launch(i)
+    torch.cuda.synchronize()
+    ms_step_eager = time_loop(step_one_launch, 6 * max(1, args.steps // 6), stream)
     log(f"[bench] eager step {ms_step_eager * 1e3:.1f} us; timing {args.steps} steps through a HIP graph")
     per_graph = 3 * N_SETS
     replays = max(1, args.steps // per_graph)
-    ms_step = time_graph(step_pipelined, per_graph, replays)
-    steps_timed = replays * per_graph
+    # six layers per graph: the three input sets and the two workspaces both cycle
+    ms_step = time_graph(step_one_launch, 6, max(1, args.steps // 6))
+    steps_timed = 6 * max(1, args.steps // 6)
+    ms_step_two_launches = time_graph(step_pipelined, per_graph, replays)
     ms_step_layer = time_graph(step, per_graph, replays)
     ms_step_separate = time_graph(step_separate, per_graph, replays)
-    log(f"[bench] graph step {ms_step * 1e3:.1f} us (one layer at a time {ms_step_layer * 1e3:.1f} us, with top-k "
-        f"launched on its own {ms_step_separate * 1e3:.1f} us); per-kernel graphs")
+    log(f"[bench] graph step {ms_step * 1e3:.1f} us (two launches per layer {ms_step_two_launches * 1e3:.1f} us, one "
+        f"layer at a time {ms_step_layer * 1e3:.1f} us, with top-k launched on its own {ms_step_separate * 1e3:.1f} "
+        f"us); per-kernel graphs")
     kr = max(1, args.kernel_iters // per_graph)
     ms = {"select_forecast": time_graph(sel, per_graph, kr), "topk": time_graph(topk, per_graph, kr),
           "attention": time_graph(attn, per_graph, kr), "select_multihead": time_graph(sel_mh, per_graph, kr),
           "topk_attention": time_graph(topk_attn, per_graph, kr),
           "topk_attention_partial": time_graph(topk_attn_partial, per_graph, kr),
-          "select_forecast_merge": time_graph(sel_merge, per_graph, kr)}
+          "select_forecast_merge": time_graph(sel_merge, per_graph, kr),
+          "decode_layer": ms_step}
     ms_extra = {"append_kv_with_window": time_graph(append_win, per_graph, kr),
                 "append_kv": time_graph(append_nowin, per_graph, kr),
                 "step_with_q_pos": time_graph(step_q_pos, per_graph, kr)}
@@ -342,8 +361,8 @@ def bench_decode(args) -> int:
 
     nbytes = algorithmic_bytes(w)
     gbps = {k: nbytes[k] / (ms[k] * 1e-3) / 1e9 for k in ms}
-    # the two launches of the timed step; the longer one is the roofline kernel
-    dominant = max(("select_forecast_merge", "topk_attention_partial"), key=lambda k: ms[k])
+    # the timed step is one launch per layer: that launch is the roofline kernel
+    dominant = "decode_layer"
     step_gbps = nbytes["step"] / (ms_step * 1e-3) / 1e9
     result = {
         "metric": METRIC,
@@ -360,17 +379,19 @@ def bench_decode(args) -> int:
         "data": "synthetic",
         "config": {"workload": w.description, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
                    "block": w.block, "top_k": w.k, "selector": "forecast", "input_sets_rotated": N_SETS,
-                   "schedule": "consecutive layers (the input sets in turn): layer l's Forecast selection shares a "
-                               "launch with the merge of layer l-1's attention, then layer l's top-k + attention"},
+                   "schedule": "consecutive layers (the input sets in turn), one launch per layer: the merge of "
+                               "layer l-1's attention, layer l+1's Forecast selection, layer l's top-k + attention"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(gbps[dominant], 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps[dominant] / HBM_PEAK_GBPS, 4),
                      "traffic": pmc_traffic(["kv_block_selection_amd/csrc/attn_decode.hip",
-                                             "kv_block_selection_amd/csrc/topk_row.h"],
-                                            "attn_decode_c3_traffic.json") if dominant == "topk_attention_partial"
-                     else None},
+                                             "kv_block_selection_amd/csrc/topk_row.h",
+                                             "kv_block_selection_amd/csrc/select_row.h",
+                                             "kv_block_selection_amd/csrc/merge_row.h"],
+                                            "decode_layer_c3_traffic.json")},
         "step_hbm_GBps": round(step_gbps, 1),
         "step_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
         "ms_per_step_eager": round(ms_step_eager, 5),
+        "ms_per_step_two_launches_per_layer": round(ms_step_two_launches, 5),
         "ms_per_step_one_layer_at_a_time": round(ms_step_layer, 5),
         "ms_per_step_topk_separate": round(ms_step_separate, 5),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in ms.items()},

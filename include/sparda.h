@@ -261,6 +261,28 @@ int sparda_select_forecast_merge(const void* f, const void* k_cmp, float* blk_sc
                                  int m_k_sel, void* stream);
 
 /*
+ * One decode layer in one launch, in the same layer order: the merge of the
+ * layer before (m_ws, m_out, m_Hq, m_T, m_k_sel as for
+ * sparda_select_forecast_merge; m_out NULL: none), this layer's top-k +
+ * attention as sparda_topk_block_sparse_attn_partial (blk_scores ... ws_bytes;
+ * its results stay in ws, to be merged by the next layer's call or
+ * sparda_merge_partials), and the selection of the next layer as
+ * sparda_select_forecast with Tq = 1 (f_next, k_cmp_next, blk_scores_next,
+ * q_start_next, q_pos_next, T_next, scale_next; f_next NULL: none). The next
+ * layer's selection needs only this layer's Forecast, so it goes first and
+ * this layer's attention workgroups take their top-k under its last loads,
+ * with no launch boundary between them. The same bits as those calls. bf16
+ * only; B and Hkv are shared by the three parts; ws and m_ws must be
+ * different buffers (two workspaces used in turn).
+ */
+int sparda_decode_layer(void* m_ws, size_t m_ws_bytes, void* m_out, int m_Hq, int m_T, int m_k_sel,
+                        const float* blk_scores, const void* q, const void* k, const void* v, int32_t* idx,
+                        void* out, int Hq, int q_start, const int* q_pos, int T, int k_sel, float scale, void* ws,
+                        size_t ws_bytes, const void* f_next, const void* k_cmp_next, float* blk_scores_next,
+                        int q_start_next, const int* q_pos_next, int T_next, float scale_next, int dtype, int B,
+                        int Hkv, int d, int block, int kernel, int stride, void* stream);
+
+/*
  * Step 5 - lookahead prefetch of the selected blocks from host memory.
  * [P1] paragraph on prefetching on a separate stream; [P2] 二 and 三: the blocks
  * the Forecast picks for the next layer are pulled from CPU memory into GPU

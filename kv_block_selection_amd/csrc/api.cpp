@@ -374,6 +374,7 @@ int topk_attn_impl(const float* blk_scores, const void* q, const void* k, const 
   const size_t need = ws_bytes_for(SPARDA_OP_BLOCK_SPARSE_ATTN, B, Hq, Hkv, 1, T, k_sel);
   CHECK(ws_bytes >= need, SPARDA_ERR_WORKSPACE, "%s needs %zu workspace bytes, got %zu", name, need, ws_bytes);
   if (need) CHECK_PTR(ws);
+  if (int e = check_q_pos(q_pos, 1)) return e;
   sparda::AttnDims ad = attn_dims(B, Hq, Hkv, 1, q_start, T, k_sel, scale, SPARDA_KV_CACHE);
   ad.q_pos = q_pos;
   return hip_status(sparda::launch_topk_attn_decode(blk_scores, q, k, v, idx, out, dtype == SPARDA_BF16, ad, ws,
@@ -446,6 +447,85 @@ SPARDA_EXPORT int sparda_select_forecast_merge(const void* f, const void* k_cmp,
   return hip_status(sparda::launch_select_forecast_decode(f, k_cmp, blk_scores, dtype == SPARDA_BF16, sd,
                                                           (hipStream_t)stream, &p, m_out),
                     "select_forecast_merge launch");
+}
+
+SPARDA_EXPORT int sparda_decode_layer(void* m_ws, size_t m_ws_bytes, void* m_out, int m_Hq, int m_T, int m_k_sel,
+                                      const float* blk_scores, const void* q, const void* k, const void* v,
+                                      int32_t* idx, void* out, int Hq, int q_start, const int* q_pos, int T, int k_sel,
+                                      float scale, void* ws, size_t ws_bytes, const void* f_next,
+                                      const void* k_cmp_next, float* blk_scores_next, int q_start_next,
+                                      const int* q_pos_next, int T_next, float scale_next, int dtype, int B, int Hkv,
+                                      int d, int block, int kernel, int stride, void* stream) {
+  if (int e = check_dtype(dtype)) return e;
+  CHECK(dtype == SPARDA_BF16, SPARDA_ERR_UNSUPPORTED, "decode_layer: only bf16 inputs are supported");
+  // this layer's top-k + attention
+  if (int e = check_geometry(B, Hq, Hkv, 1, q_start, T, d)) return e;
+  CHECK(block == sparda::kBlock, SPARDA_ERR_UNSUPPORTED, "block %d != 64", block);
+  CHECK(std::isfinite(scale), SPARDA_ERR_INVALID_ARG, "scale is not finite");
+  const int nB = T / sparda::kBlock;
+  CHECK(nB <= 8192, SPARDA_ERR_UNSUPPORTED, "decode_layer: nB = %d above 8192", nB);
+  CHECK(k_sel >= 1 && k_sel <= nB, SPARDA_ERR_INVALID_ARG, "k = %d outside 1..nB (%d)", k_sel, nB);
+  CHECK(k_sel <= 1024, SPARDA_ERR_UNSUPPORTED, "decode_layer: k = %d above 1024", k_sel);
+  const size_t need = ws_bytes_for(SPARDA_OP_BLOCK_SPARSE_ATTN, B, Hq, Hkv, 1, T, k_sel);
+  CHECK(ws_bytes >= need, SPARDA_ERR_WORKSPACE, "decode_layer needs %zu workspace bytes, got %zu", need, ws_bytes);
+  // the merge of the layer before
+  sparda::AttnDims mad;
+  const bool merge = m_out != nullptr;
+  if (merge) {
+    if (int e = pending_merge(m_ws, m_ws_bytes, dtype, B, m_Hq, Hkv, m_T, d, m_k_sel, &mad)) return e;
+    CHECK(m_ws == nullptr || ws == nullptr || m_ws != ws || need == 0, SPARDA_ERR_INVALID_ARG,
+          "decode_layer: the merged layer's workspace must not be this layer's");
+  }
+  // the next layer's selection
+  const bool next = f_next != nullptr;
+  if (next) {
+    if (int e = check_geometry(B, Hkv, Hkv, 1, q_start_next, T_next, d)) return e;
+    if (int e = check_select_params(kernel, stride, block, sparda::kTile, scale_next)) return e;
+  }
+  if (B == 0) return ok();
+  CHECK(blk_scores != nullptr && ((uintptr_t)blk_scores & 3u) == 0, SPARDA_ERR_INVALID_ARG,
+        "blk_scores is NULL or not 4-byte aligned");
+  CHECK_PTR(q);
+  CHECK_PTR(k);
+  CHECK_PTR(v);
+  CHECK_PTR(out);
+  CHECK(idx != nullptr && ((uintptr_t)idx & 3u) == 0, SPARDA_ERR_INVALID_ARG, "idx is NULL or not 4-byte aligned");
+  if (need) CHECK_PTR(ws);
+  if (int e = check_q_pos(q_pos, 1)) return e;
+  if (next)
+    if (int e = check_q_pos(q_pos_next, 1)) return e;
+  if (merge) {
+    CHECK_PTR(m_out);
+    if (m_ws_bytes) CHECK_PTR(m_ws);
+  }
+  if (next) {
+    CHECK_PTR(k_cmp_next);
+    CHECK_PTR(blk_scores_next);
+  }
+  sparda::LayerLaunch L{};
+  sparda::DecodePartials mp{};
+  if (merge) {
+    mp = sparda::decode_attn_partials(m_ws, mad);
+    L.merge = &mp;
+    L.merge_out = m_out;
+  }
+  L.attn = attn_dims(B, Hq, Hkv, 1, q_start, T, k_sel, scale, SPARDA_KV_CACHE);
+  L.attn.q_pos = q_pos;
+  L.scores = blk_scores;
+  L.q = q;
+  L.k = k;
+  L.v = v;
+  L.idx = idx;
+  L.out = out;
+  L.ws = ws;
+  if (next) {
+    L.sel = select_dims(B, Hkv, Hkv, 1, q_start_next, T_next, scale_next);
+    L.sel.q_pos = q_pos_next;
+    L.f_next = f_next;
+    L.kc_next = k_cmp_next;
+    L.scores_next = blk_scores_next;
+  }
+  return hip_status(sparda::launch_decode_layer(L, true, (hipStream_t)stream), "decode_layer launch");
 }
 
 namespace {

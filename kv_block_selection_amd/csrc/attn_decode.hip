@@ -27,6 +27,7 @@
 #include "common.h"
 #include "launch.h"
 #include "merge_row.h"
+#include "select_row.h"
 #include "topk_row.h"
 
 namespace sparda {
@@ -38,7 +39,8 @@ namespace sparda {
 // many one-wave workgroups (8 resident per CU at ~250 VGPRs).
 constexpr int kAttnTargetWaves = SPARDA_ATTN_TARGET_WAVES;
 constexpr int kAttnMaxSplits = 64;
-constexpr int kFusedMaxK = 1024;  // top-k fused in front of attention: at most this many blocks
+constexpr int kFusedMaxK = 1024;
+constexpr int SPARDA_KV_CACHE_MODE = 0;  // kv_mode of a cache read at the selected blocks  // top-k fused in front of attention: at most this many blocks
 constexpr float kLazyGrow = 5.545177444479562f;  // 8 ln 2
 
 // Reduce-scatter of G partial dot products over the 16 lanes of a key row.
@@ -94,14 +96,12 @@ __device__ __forceinline__ void reduce_scatter16(const float* part, float* out) 
 // same selection, the first also writes it to idx_out) and the waves read the
 // selection from LDS; NPT = 0: the selection comes from idx.
 template <typename Tag, int G, int WPG, int NPT>
-__global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(SPARDA_ATTN_WAVES_PER_EU)))
-void attn_decode_kernel(
-    const uint8_t* __restrict__ q, const uint8_t* __restrict__ kbuf, const uint8_t* __restrict__ vbuf,
-    const int32_t* __restrict__ idx, int32_t* __restrict__ idx_out, const float* __restrict__ scores,
-    float* __restrict__ part_o,
-    float2* __restrict__ part_ml, uint8_t* __restrict__ out, int T, int nB, int k, int kv_mode, int p_all,
-    const int* __restrict__ q_pos, int hkv, const int32_t* __restrict__ slot_of, int n_slots, int bps, int splits,
-    float scale) {
+__device__ __forceinline__ void attn_decode_body(
+    long row, int wg_split, const uint8_t* __restrict__ q, const uint8_t* __restrict__ kbuf,
+    const uint8_t* __restrict__ vbuf, const int32_t* __restrict__ idx, int32_t* __restrict__ idx_out,
+    const float* __restrict__ scores, float* __restrict__ part_o, float2* __restrict__ part_ml,
+    uint8_t* __restrict__ out, int T, int nB, int k, int kv_mode, int p_all, const int* __restrict__ q_pos, int hkv,
+    const int32_t* __restrict__ slot_of, int n_slots, int bps, int splits, float scale) {
   constexpr int E = DT<Tag>::kElems;
   constexpr int LPK = kHeadDim / E;  // lanes per key row
   constexpr int KPI = kWave / LPK;   // keys per load instruction
@@ -116,8 +116,7 @@ void attn_decode_kernel(
   float* s_p = s_p_all[wv];
   uint32_t* s_p2 = s_p2_all[wv];
 
-  const long row = blockIdx.x;  // rows on the fast axis: a row's splits share an XCD
-  const int split = blockIdx.y * WPG + wv;
+  const int split = wg_split * WPG + wv;
   const int p = row_position(q_pos, row, hkv, p_all, T);  // the row's query position
   const int lane = WPG == 1 ? threadIdx.x : threadIdx.x % kWave;
   const int c = lane % LPK;
@@ -127,7 +126,7 @@ void attn_decode_kernel(
   if constexpr (NPT > 0) {
     __shared__ TopkShared sh;
     __shared__ int32_t s_sel[kFusedMaxK];
-    topk_row<NPT>(scores + row * nB, blockIdx.y == 0 ? idx_out + row * k : nullptr, s_sel, nB, k, sh, threadIdx.x);
+    topk_row<NPT>(scores + row * nB, wg_split == 0 ? idx_out + row * k : nullptr, s_sel, nB, k, sh, threadIdx.x);
     __syncthreads();
     idx_row = s_sel;
   }
@@ -340,6 +339,78 @@ void attn_decode_kernel(
   }
 }
 
+template <typename Tag, int G, int WPG, int NPT>
+__global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(SPARDA_ATTN_WAVES_PER_EU)))
+void attn_decode_kernel(
+    const uint8_t* __restrict__ q, const uint8_t* __restrict__ kbuf, const uint8_t* __restrict__ vbuf,
+    const int32_t* __restrict__ idx, int32_t* __restrict__ idx_out, const float* __restrict__ scores,
+    float* __restrict__ part_o, float2* __restrict__ part_ml, uint8_t* __restrict__ out, int T, int nB, int k,
+    int kv_mode, int p_all, const int* __restrict__ q_pos, int hkv, const int32_t* __restrict__ slot_of, int n_slots,
+    int bps, int splits, float scale) {
+  // rows on the fast axis: a row's splits share an XCD
+  attn_decode_body<Tag, G, WPG, NPT>(blockIdx.x, blockIdx.y, q, kbuf, vbuf, idx, idx_out, scores, part_o, part_ml,
+                                     out, T, nB, k, kv_mode, p_all, q_pos, hkv, slot_of, n_slots, bps, splits, scale);
+}
+
+// One decode layer in one launch, in the method's layer order: the merge of
+// layer l-1's attention, the Forecast selection of layer l+1 (which needs
+// only layer l's Forecast and layer l+1's compressed keys) and the top-k +
+// attention of layer l, as workgroup roles of one 1D grid dispatched in that
+// order: attention workgroups start as selection workgroups retire, so their
+// top-k runs under the selection's last loads and no launch boundary
+// separates the two. The kernel runs at the attention's register allocation
+// (2 waves per SIMD), so a selection workgroup takes 128 blocks (513
+// windows, ~130 KB in flight) instead of 16. Each role's arithmetic is that
+// of its own kernel, so the bits are those of the separate calls.
+constexpr int kLayerSelBlocks = 128;
+
+struct LayerRoles {
+  int n_merge, n_attn, n_sel;
+  // role of workgroup i: 0 merge, 1 attention, 2 selection; *r = index in the role
+  __device__ __forceinline__ int of(int i, int* r) const {
+    if (i < n_merge) {
+      *r = i;
+      return 0;
+    }
+    const int j = i - n_merge;
+    if (j < n_sel) {
+      *r = j;
+      return 2;
+    }
+    *r = j - n_sel;
+    return 1;
+  }
+};
+
+template <typename Tag, int G, int NPT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SPARDA_ATTN_WAVES_PER_EU)))
+void decode_layer_kernel(LayerRoles roles, int rows,
+                         // merge of layer l-1
+                         const float* __restrict__ m_part_o, const float2* __restrict__ m_part_ml,
+                         uint8_t* __restrict__ m_out, int m_G, int m_splits,
+                         // top-k + attention of layer l
+                         const uint8_t* __restrict__ q, const uint8_t* __restrict__ kbuf,
+                         const uint8_t* __restrict__ vbuf, int32_t* __restrict__ idx_out,
+                         const float* __restrict__ scores, float* __restrict__ part_o, float2* __restrict__ part_ml,
+                         uint8_t* __restrict__ out, int T, int nB, int k, int p_all, const int* __restrict__ q_pos,
+                         int hkv, int bps, int splits, float scale,
+                         // selection of layer l+1
+                         const uint8_t* __restrict__ f_n, const uint8_t* __restrict__ kc_n, float* __restrict__ scores_n,
+                         int W_n, int nB_n, int n_vis_n, const int* __restrict__ q_pos_n, int T_n, float scale_n) {
+  int r;
+  const int role = roles.of(blockIdx.x, &r);
+  if (role == 0) {
+    merge_row_lean<Tag>(r, threadIdx.x, m_part_o, m_part_ml, m_out, m_G, m_splits);
+  } else if (role == 1) {
+    attn_decode_body<Tag, G, 4, NPT>(r % rows, r / rows, q, kbuf, vbuf, nullptr, idx_out, scores, part_o, part_ml, out,
+                                     T, nB, k, SPARDA_KV_CACHE_MODE, p_all, q_pos, hkv, nullptr, 0, bps, splits, scale);
+  } else {
+    __shared__ float s_win[fsel_lds_floats<Tag, kLayerSelBlocks>()];
+    fsel_blocks<Tag, kLayerSelBlocks>(f_n, kc_n, scores_n, W_n, nB_n, n_vis_n, q_pos_n, hkv, T_n, scale_n, r % rows,
+                                      r / rows, s_win, threadIdx.x);
+  }
+}
+
 template <typename Tag, int MAXS>
 __global__ __launch_bounds__(256) void attn_combine_row_kernel(const float* __restrict__ part_o,
                                                                const float2* __restrict__ part_ml,
@@ -428,6 +499,55 @@ static void launch_attn_g(const void* q, const void* k, const void* v, const int
 #undef SPARDA_FUSED
   }
   if (merge) launch_merge<Tag>(pp, out, s);
+}
+
+template <typename Tag, int G>
+static void launch_layer_g(const LayerLaunch& L, hipStream_t s) {
+  const AttnDims& d = L.attn;
+  const DecodePartials pp = decode_attn_partials(L.ws, d);
+  const int rows = pp.rows;
+  const bool merge = L.merge != nullptr && L.merge->splits > 1;
+  LayerRoles roles;
+  roles.n_merge = merge ? rows : 0;
+  roles.n_attn = rows * ((pp.splits + 3) / 4);
+  roles.n_sel = L.f_next ? rows * ((L.sel.nB + kLayerSelBlocks - 1) / kLayerSelBlocks) : 0;
+  const int bps = (d.k + pp.splits - 1) / pp.splits;
+  const int n_vis_n = L.f_next ? min(L.sel.W, (L.sel.q_start - kKernel + 1) >= 0
+                                                  ? (L.sel.q_start - kKernel + 1) / kStride + 1 : 0)
+                               : 0;
+  const dim3 grid(roles.n_merge + roles.n_attn + roles.n_sel);
+#define SPARDA_LAYER(N)                                                                                            \
+  hipLaunchKernelGGL((decode_layer_kernel<Tag, G, N>), grid, dim3(256), 0, s, roles, rows,                        \
+                     merge ? L.merge->part_o : nullptr, merge ? L.merge->part_ml : nullptr, (uint8_t*)L.merge_out,  \
+                     merge ? L.merge->G : 0, merge ? L.merge->splits : 0, (const uint8_t*)L.q, (const uint8_t*)L.k, \
+                     (const uint8_t*)L.v, L.idx, L.scores, pp.part_o, pp.part_ml, (uint8_t*)L.out, d.T, d.nB, d.k,    \
+                     d.q_start, d.q_pos, d.Hkv, bps, pp.splits, d.scale, (const uint8_t*)L.f_next,                   \
+                     (const uint8_t*)L.kc_next, L.scores_next, L.sel.W, L.sel.nB, n_vis_n, L.sel.q_pos, L.sel.T,      \
+                     L.sel.scale)
+  if (d.nB <= 256) SPARDA_LAYER(1);
+  else if (d.nB <= 2048) SPARDA_LAYER(8);
+  else SPARDA_LAYER(32);
+#undef SPARDA_LAYER
+}
+
+hipError_t launch_decode_layer(const LayerLaunch& L, bool bf16, hipStream_t s) {
+  const int G = L.attn.Hq / L.attn.Hkv;
+#define SPARDA_LG(TAG, GG) launch_layer_g<TAG, GG>(L, s)
+#define SPARDA_LG_G(TAG)                  \
+  switch (G) {                            \
+    case 1: SPARDA_LG(TAG, 1); break;     \
+    case 2: SPARDA_LG(TAG, 2); break;     \
+    case 4: SPARDA_LG(TAG, 4); break;     \
+    case 8: SPARDA_LG(TAG, 8); break;     \
+    default: return hipErrorInvalidValue; \
+  }
+  // bf16 only: an fp32 selection workgroup of 128 blocks would not fit the
+  // attention's register allocation
+  if (!bf16) return hipErrorInvalidValue;
+  SPARDA_LG_G(BF16Tag)
+#undef SPARDA_LG_G
+#undef SPARDA_LG
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_decode(const void* q, const void* k, const void* v, const int32_t* idx,

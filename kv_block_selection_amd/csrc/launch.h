@@ -80,6 +80,23 @@ hipError_t launch_topk_attn_decode(const float* scores, const void* q, const voi
                                    void* out, bool bf16, const AttnDims& d, void* ws, bool merge, hipStream_t s);
 DecodePartials decode_attn_partials(void* ws, const AttnDims& d);
 hipError_t launch_merge_partials(void* ws, void* out, bool bf16, const AttnDims& d, hipStream_t s);
+// one decode layer in one launch: merge of the layer before (merge may be
+// NULL), top-k + attention of this layer (results left in ws), selection of
+// the next layer (f_next may be NULL)
+struct LayerLaunch {
+  const DecodePartials* merge;
+  void* merge_out;
+  AttnDims attn;
+  const float* scores;
+  const void *q, *k, *v;
+  int32_t* idx;
+  void* out;
+  void* ws;
+  SelectDims sel;
+  const void *f_next, *kc_next;
+  float* scores_next;
+};
+hipError_t launch_decode_layer(const LayerLaunch& L, bool bf16, hipStream_t s);
 
 // attn_prefill.hip (bf16, cache mode, Tq % 64 == 0)
 hipError_t launch_attn_prefill(const void* q, const void* k, const void* v, const int32_t* idx, void* out,

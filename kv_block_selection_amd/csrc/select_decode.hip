@@ -22,6 +22,7 @@
 #include "common.h"
 #include "launch.h"
 #include "merge_row.h"
+#include "select_row.h"
 
 namespace sparda {
 
@@ -32,13 +33,6 @@ constexpr int kFselBlocks = SPARDA_FSEL_BLOCKS;  // blocks per workgroup, Foreca
 constexpr int kMhChunk = 256;     // windows per workgroup, multi-head pass 1
 constexpr int kMhPoolBlocks = 64; // blocks per workgroup, multi-head pass 2
 
-template <typename Tag>
-struct RowGeom {
-  static constexpr int E = DT<Tag>::kElems;
-  static constexpr int LPR = kHeadDim / E;   // lanes per 128-channel row
-  static constexpr int SLOTS = 256 / LPR;    // rows per 256-thread pass
-  static constexpr int RB = kHeadDim * DT<Tag>::kBytes;
-};
 
 // ---------------------------------------------------------------- Forecast --
 // MERGE: the grid has one more row of workgroups, dispatched first (y = 0),
@@ -59,47 +53,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void f
     }
   }
   const int chunk = blockIdx.y - (MERGE ? 1 : 0);
-  using R = RowGeom<Tag>;
-  constexpr int NWIN = 4 * kFselBlocks + 1;
-  constexpr int ITER = (NWIN + R::SLOTS - 1) / R::SLOTS;
-  __shared__ float s_win[ITER * R::SLOTS];
-
-  const long row = blockIdx.x;  // rows on the fast axis: a row's chunks share an XCD
-  if (q_pos != nullptr) n_vis = visible_windows(row_position(q_pos, row, hkv, 0, T), W);
-  const int beta0 = chunk * kFselBlocks;
-  const int nblk = min(kFselBlocks, nB - beta0);
-  const int nwin = 4 * nblk + 1;
-  const int wstart = 4 * beta0 - 1;
-  const int lane = threadIdx.x % R::LPR;
-  const int slot = threadIdx.x / R::LPR;
-
-  const u32x4 fv = load16(f + row * R::RB + lane * 16);
-  const uint8_t* base = kc + row * (long)W * R::RB + lane * 16;
-
-  u32x4 kv[ITER];
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int lw = it * R::SLOTS + slot;
-    const int w = wstart + lw;
-    const bool ok = lw < nwin && w >= 0 && w < n_vis;
-    kv[it] = ok ? load16_nt(base + (long)w * R::RB) : u32x4{0, 0, 0, 0};
-  }
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int lw = it * R::SLOTS + slot;
-    const int w = wstart + lw;
-    const bool ok = lw < nwin && w >= 0 && w < n_vis;
-    const float s = group_sum<R::LPR>(dot16<Tag>(fv, kv[it], 0.f));
-    if (lane == 0) s_win[lw] = ok ? s * scale : -INFINITY;
-  }
-  __syncthreads();
-  const int t = threadIdx.x;
-  if (t < nblk) {
-    float m = s_win[4 * t];
-#pragma unroll
-    for (int j = 1; j < 5; ++j) m = fmaxf(m, s_win[4 * t + j]);
-    scores[row * nB + beta0 + t] = m;
-  }
+  __shared__ float s_win[fsel_lds_floats<Tag, kFselBlocks>()];
+  // rows on the fast axis: a row's chunks share an XCD
+  fsel_blocks<Tag, kFselBlocks>(f, kc, scores, W, nB, n_vis, q_pos, hkv, T, scale, blockIdx.x, chunk, s_win,
+                                threadIdx.x);
 }
 
 hipError_t launch_select_forecast_decode(const void* f, const void* kc, float* scores, bool bf16,

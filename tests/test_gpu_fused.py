@@ -214,3 +214,63 @@ def test_merge_deferred_graph_replay(gpu):
                                bits(want) if want.dtype == torch.bfloat16 else want), f"replay {rep}"
         run()  # eager work between replays
         torch.cuda.synchronize()
+
+
+# ------------------------------------------------ one launch per decode layer ----
+@pytest.mark.parametrize("G,k,ragged", [(4, 5, False), (4, 37, False), (2, 20, True), (8, 9, False), (4, 1, False)])
+def test_decode_layer_chain(gpu, G, k, ragged):
+    """Three layers, each one sparda_decode_layer launch (the merge of the layer
+    before, this layer's top-k + attention, the next layer's selection), two
+    workspaces in turn, a final sparda_merge_partials: every layer's scores,
+    selection and output hold the bits of the one-layer-at-a-time calls."""
+    w = small("bf16", B=3, Hq=2 * G, Hkv=2, k=k)
+    L = _layers(gpu, w, 3, seed0=90)
+    q_pos = torch.tensor([w.T - 1, 64 * 9 + 3, 300], dtype=torch.int32, device=DEV) if ragged else None
+    qs = 0 if ragged else w.q_start
+    ref = []
+    for l in range(3):
+        s = gpu.select_forecast(L[l]["F"], L[l]["Kc"], w.T, qs, q_pos=q_pos)
+        i, o = gpu.topk_block_sparse_attn(s, L[l]["Q"], L[l]["K"], L[l]["V"], w.k, w.T, qs, q_pos=q_pos)
+        ref.append((s, i, o))
+    nbytes = gpu.workspace_bytes(gpu.OP_BLOCK_SPARSE_ATTN, w.B, w.Hq, w.Hkv, 1, w.T, w.k)
+    ws = [torch.full((max(nbytes, 1),), 0x33, dtype=torch.uint8, device=DEV) if nbytes else None for _ in range(2)]
+    sc = [torch.full((w.B, w.Hkv, 1, w.nB), 7.0, dtype=torch.float32, device=DEV) for _ in range(3)]
+    outs = [torch.full_like(L[l]["Q"], 3.0) for l in range(3)]
+    ix = [torch.full((w.B, w.Hkv, 1, w.k), -9, dtype=torch.int32, device=DEV) for _ in range(3)]
+    gpu.select_forecast(L[0]["F"], L[0]["Kc"], w.T, qs, out=sc[0], q_pos=q_pos)
+    for l in range(3):
+        merge = (ws[(l - 1) % 2], outs[l - 1], w.T, w.k) if l > 0 else None
+        nxt = (L[l + 1]["F"], L[l + 1]["Kc"], sc[l + 1], w.T, qs, q_pos) if l < 2 else None
+        gpu.decode_layer(sc[l], L[l]["Q"], L[l]["K"], L[l]["V"], w.k, w.T, qs, ws[l % 2], idx=ix[l], out=outs[l],
+                         q_pos=q_pos, merge_from=merge, select_next=nxt)
+    gpu.merge_partials(ws[2 % 2], outs[2], w.T, w.k, w.Hkv)
+    torch.cuda.synchronize()
+    for l in range(3):
+        assert torch.equal(sc[l], ref[l][0]), f"layer {l}: scores"
+        assert torch.equal(ix[l], ref[l][1]), f"layer {l}: selection"
+        assert torch.equal(bits(outs[l]), bits(ref[l][2])), f"layer {l}: attention output"
+    say(f"decode_layer chain G {G} k {k} ragged {ragged}: same bits")
+
+
+def test_decode_layer_c3_shape(gpu):
+    """The batch-16 128K shape the benchmark times (two layers, sampled checks
+    are unnecessary: the bits are compared with the separate calls in full)."""
+    w = wl.C3_DECODE_128K
+    L = _layers(gpu, w, 2, seed0=5)
+    ref = []
+    for l in range(2):
+        s = gpu.select_forecast(L[l]["F"], L[l]["Kc"], w.T, w.q_start)
+        ref.append((s,) + gpu.topk_block_sparse_attn(s, L[l]["Q"], L[l]["K"], L[l]["V"], w.k, w.T, w.q_start))
+    nbytes = gpu.workspace_bytes(gpu.OP_BLOCK_SPARSE_ATTN, w.B, w.Hq, w.Hkv, 1, w.T, w.k)
+    ws = [torch.zeros(nbytes, dtype=torch.uint8, device=DEV) for _ in range(2)]
+    s0 = gpu.select_forecast(L[0]["F"], L[0]["Kc"], w.T, w.q_start)
+    s1 = torch.empty_like(s0)
+    i0, o0 = gpu.decode_layer(s0, L[0]["Q"], L[0]["K"], L[0]["V"], w.k, w.T, w.q_start, ws[0],
+                              select_next=(L[1]["F"], L[1]["Kc"], s1, w.T, w.q_start))
+    i1, o1 = gpu.decode_layer(s1, L[1]["Q"], L[1]["K"], L[1]["V"], w.k, w.T, w.q_start, ws[1],
+                              merge_from=(ws[0], o0, w.T, w.k))
+    gpu.merge_partials(ws[1], o1, w.T, w.k, w.Hkv)
+    torch.cuda.synchronize()
+    for l, (s, i, o) in enumerate(((s0, i0, o0), (s1, i1, o1))):
+        assert torch.equal(s, ref[l][0]) and torch.equal(i, ref[l][1]), f"layer {l}: scores/selection"
+        assert torch.equal(bits(o), bits(ref[l][2])), f"layer {l}: output"
