@@ -298,3 +298,36 @@ def test_select_forecast_merge_validation(lib, kw, status, needle):
                                           a["m_ws"], a["m_ws_bytes"], a["m_out"], a["m_Hq"], a["m_T"], a["m_k_sel"],
                                           None)
     assert st == status and needle in lib.sparda_last_error(), lib.sparda_last_error()
+
+
+def _layer(lib, **kw):
+    a = dict(m_ws=P + 4096, m_ws_bytes=1 << 30, m_out=P, m_Hq=32, m_T=131072, m_k=64, s=P, q=P, k=P, v=P, idx=P,
+             out=P, Hq=32, q_start=131071, q_pos=None, T=131072, k_sel=64, scale=0.088, ws=P, ws_bytes=1 << 30,
+             f_n=P, kc_n=P, s_n=P, q_start_n=131071, q_pos_n=None, T_n=131072, scale_n=0.088, dtype=1, B=16, Hkv=8,
+             d=128, block=64, kernel=32, stride=16)
+    a.update(kw)
+    return lib.sparda_decode_layer(a["m_ws"], a["m_ws_bytes"], a["m_out"], a["m_Hq"], a["m_T"], a["m_k"], a["s"],
+                                   a["q"], a["k"], a["v"], a["idx"], a["out"], a["Hq"], a["q_start"], a["q_pos"],
+                                   a["T"], a["k_sel"], a["scale"], a["ws"], a["ws_bytes"], a["f_n"], a["kc_n"],
+                                   a["s_n"], a["q_start_n"], a["q_pos_n"], a["T_n"], a["scale_n"], a["dtype"], a["B"],
+                                   a["Hkv"], a["d"], a["block"], a["kernel"], a["stride"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(dtype=0), 2, b"only bf16"),
+    (dict(m_ws=P), 1, b"must not be this layer's"),
+    (dict(ws_bytes=100), 3, b"workspace"),
+    (dict(m_ws_bytes=100), 3, b"workspace"),
+    (dict(k_sel=1025, T=64 * 2000, q_start=64 * 2000 - 1), 2, b"above 1024"),
+    (dict(kernel=16), 2, b"kernel/stride"),
+    (dict(s_n=None), 1, b"blk_scores_next is NULL"),
+    (dict(q=None), 1, b"q is NULL"),
+])
+def test_decode_layer_validation(lib, kw, status, needle):
+    st = _layer(lib, **kw)
+    assert st == status and needle in lib.sparda_last_error(), lib.sparda_last_error()
+
+
+def test_decode_layer_optional_parts(lib):
+    # no merge (m_out NULL) and no next selection (f_next NULL) with B = 0: valid, launches nothing
+    assert _layer(lib, m_out=None, f_n=None, B=0) == 0
