@@ -39,8 +39,8 @@ namespace sparda {
 // many one-wave workgroups (8 resident per CU at ~250 VGPRs).
 constexpr int kAttnTargetWaves = SPARDA_ATTN_TARGET_WAVES;
 constexpr int kAttnMaxSplits = 64;
-constexpr int kFusedMaxK = 1024;
-constexpr int SPARDA_KV_CACHE_MODE = 0;  // kv_mode of a cache read at the selected blocks  // top-k fused in front of attention: at most this many blocks
+constexpr int kFusedMaxK = 1024;  // top-k fused in front of attention: at most this many blocks
+constexpr int SPARDA_KV_CACHE_MODE = 0;  // kv_mode of a cache read at the selected blocks
 constexpr float kLazyGrow = 5.545177444479562f;  // 8 ln 2
 
 // Reduce-scatter of G partial dot products over the 16 lanes of a key row.
