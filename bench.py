@@ -386,7 +386,8 @@ def bench_decode(args) -> int:
                      "traffic": pmc_traffic(["kv_block_selection_amd/csrc/attn_decode.hip",
                                              "kv_block_selection_amd/csrc/topk_row.h",
                                              "kv_block_selection_amd/csrc/select_row.h",
-                                             "kv_block_selection_amd/csrc/merge_row.h"],
+                                             "kv_block_selection_amd/csrc/merge_row.h",
+                                             "kv_block_selection_amd/csrc/reduce16.h"],
                                             "decode_layer_c3_traffic.json")},
         "step_hbm_GBps": round(step_gbps, 1),
         "step_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),

@@ -22,6 +22,7 @@
 #include "common.h"
 #include "launch.h"
 #include "merge_row.h"
+#include "reduce16.h"
 #include "select_row.h"
 
 namespace sparda {
@@ -124,9 +125,10 @@ __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __rest
   const int lane = threadIdx.x % R::LPR;
   const int slot = threadIdx.x / R::LPR;
 
+  // query heads in the reduce-scatter's slot order for this lane
   u32x4 qv[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) qv[g] = load16(q + (row * G + g) * R::RB + lane * 16);
+  for (int s = 0; s < G; ++s) qv[s] = load16(q + (row * G + slot_head<G>(s, lane & 15)) * R::RB + lane * 16);
   const uint8_t* base = kc + row * (long)W * R::RB + lane * 16;
 
   u32x4 kv[ITER];
@@ -135,14 +137,28 @@ __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __rest
     const int w = w0 + it * R::SLOTS + slot;
     kv[it] = (w < n_vis) ? load16_nt(base + (long)w * R::RB) : u32x4{0, 0, 0, 0};
   }
+  // All G logits of a window in one reduce-scatter: afterwards lanes 4 apart
+  // (8 for G = 2, 16 for G = 1) hold different heads; the first lane of each
+  // such group writes its head(s).
+  constexpr int GR = G < 4 ? 1 : G / 4;
+  constexpr int HL = G >= 4 ? 4 : (G == 2 ? 8 : 16);
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
     const int lw = it * R::SLOTS + slot;
     const bool ok = w0 + lw < n_vis;
+    float part[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float s = group_sum<R::LPR>(dot16<Tag>(qv[g], kv[it], 0.f));
-      if (lane == g % R::LPR) s_log[g][lw] = ok ? s * scale : -INFINITY;
+    for (int s = 0; s < G; ++s) part[s] = dot16<Tag>(qv[s], kv[it], 0.f);
+    if constexpr (R::LPR == 32) {  // fp32: 32 lanes per row; fold the upper 16 first
+#pragma unroll
+      for (int s = 0; s < G; ++s) part[s] = sum16(part[s]);
+    }
+    float sc[GR];
+    reduce_scatter16<G>(part, sc);
+    if ((lane & (HL - 1)) == 0 && lane < 16) {
+      const int h = lane / HL;
+#pragma unroll
+      for (int gr = 0; gr < GR; ++gr) s_log[4 * gr + h][lw] = ok ? sc[gr] * scale : -INFINITY;
     }
   }
   __syncthreads();
