@@ -365,3 +365,59 @@ def project_qkvf(x: np.ndarray, w: np.ndarray, Hq: int, Hkv: int, n_f: int, d: i
     if n_f:
         f = heads[:, Hq + 2 * Hkv:].reshape(B, n_f, Hkv, 1, d).transpose(1, 0, 2, 3, 4).copy()
     return q, k, v, f
+
+
+# ------------------------------------------- token-level Forecast (variant) ----
+# [P2] 六 names, as future work for models with token-level sparse attention,
+# a forecaster that predicts importance scores per key token instead of per
+# block; [P1] compares the method with DSA, whose small indexer picks the
+# important tokens in place of the queries. The pages define neither the keys
+# such a forecaster reads nor how many tokens it keeps. Reading taken: the
+# layer's Forecast vector scores every visible key token directly (no
+# compression, no pooling), the same top-k rule keeps the best k_tok tokens,
+# and attention runs over exactly those tokens.
+def _positions(B: int, q_start: int, positions) -> list[int]:
+    return [int(q_start)] * B if positions is None else [int(x) for x in positions]
+
+
+def forecast_token_scores(F: np.ndarray, K: np.ndarray, q_start: int, scale: float, positions=None) -> np.ndarray:
+    """Decode-time token scores s[t] = scale * f . K[t] for every key token
+    t <= p, -inf after p (the query's own position bounds what it may see).
+
+    F [B, Hkv, 1, d]; K [B, Hkv, T, d] -> [B, Hkv, 1, T]. ``positions`` gives
+    each sequence's query position (default q_start for all)."""
+    B, Hkv, Tq, d = F.shape
+    assert Tq == 1
+    T = K.shape[2]
+    pos = _positions(B, q_start, positions)
+    out = np.full((B, Hkv, 1, T), NEG_INF)
+    for b in range(B):
+        p = min(pos[b], T - 1)
+        if p < 0:
+            continue
+        for h in range(Hkv):
+            out[b, h, 0, : p + 1] = scale * (np.asarray(K[b, h, : p + 1], np.float64) @ np.asarray(F[b, h, 0], np.float64))
+    return out
+
+
+def token_sparse_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, tok_idx: np.ndarray, q_start: int,
+                           scale: float, positions=None) -> np.ndarray:
+    """GQA attention at decode over the selected key tokens only: every query
+    head of a group attends, with its own query, over the tokens kept for its
+    KV head, restricted to positions <= p; -1 entries are padding, and a query
+    with no key gets zeros.
+
+    Q [B, Hq, 1, d]; K, V [B, Hkv, T, d]; tok_idx [B, Hkv, 1, k_tok]."""
+    B, Hq, Tq, d = Q.shape
+    assert Tq == 1
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    pos = _positions(B, q_start, positions)
+    out = np.zeros((B, Hq, 1, d))
+    for b in range(B):
+        for qh in range(Hq):
+            h = qh // G
+            J = np.array(sorted(set(int(t) for t in tok_idx[b, h, 0] if 0 <= t <= pos[b])), dtype=np.int64)
+            if J.size:
+                out[b, qh, 0] = attend(Q[b, qh, 0], K[b, h, J], V[b, h, J], scale)
+    return out

@@ -406,3 +406,91 @@ def test_project_qkvf_unit_rows_pick_inputs():
                               + ([f.transpose(1, 0, 2, 3, 4).reshape(B, -1)] if n_f else []), axis=1)
         np.testing.assert_array_equal(flat, x[:, perm])
         assert (f is None) == (n_f == 0)
+
+
+# ---- token-level Forecast variant -------------------------------------------
+def test_token_scores_ramp_closed_form():
+    # K[t] = t e_0 and f = e_0: the score of token t is scale * t up to the
+    # query's position and -inf after it
+    T, d, p = 40, 128, 30
+    K = np.zeros((1, 1, T, d))
+    K[0, 0, :, 0] = np.arange(T)
+    F = np.zeros((1, 1, 1, d))
+    F[0, 0, 0, 0] = 1.0
+    s = oracle.forecast_token_scores(F, K, p, 0.5)
+    assert np.array_equal(s[0, 0, 0, : p + 1], 0.5 * np.arange(p + 1))
+    assert np.all(s[0, 0, 0, p + 1:] == -np.inf)
+
+
+def test_token_scores_brute_force():
+    rng = np.random.default_rng(11)
+    B, Hkv, T, d = 2, 3, 24, 128
+    K = rng.standard_normal((B, Hkv, T, d))
+    F = rng.standard_normal((B, Hkv, 1, d))
+    pos = [17, 5]
+    s = oracle.forecast_token_scores(F, K, 0, 0.25, positions=pos)
+    for b in range(B):
+        for h in range(Hkv):
+            for t in range(T):
+                want = 0.25 * math.fsum(F[b, h, 0, c] * K[b, h, t, c] for c in range(d)) if t <= pos[b] else -np.inf
+                assert s[b, h, 0, t] == pytest.approx(want, rel=1e-12, abs=1e-12)
+
+
+def test_token_scores_nothing_visible():
+    s = oracle.forecast_token_scores(np.ones((1, 2, 1, 128)), np.ones((1, 2, 8, 128)), 0, 1.0, positions=[-1])
+    assert np.all(s == -np.inf)
+
+
+def test_token_topk_keeps_every_visible_token():
+    rng = np.random.default_rng(12)
+    K = rng.standard_normal((1, 1, 50, 128))
+    F = rng.standard_normal((1, 1, 1, 128))
+    s = oracle.forecast_token_scores(F, K, 20, 1.0)
+    idx = oracle.topk_blocks(s, 30)
+    assert np.array_equal(idx[0, 0, 0, :21], np.arange(21))
+    assert np.all(idx[0, 0, 0, 21:] == -1)
+
+
+def test_token_attention_all_tokens_is_dense_causal():
+    rng = np.random.default_rng(13)
+    B, Hq, Hkv, T, d = 2, 4, 2, 70, 128
+    Q = rng.standard_normal((B, Hq, 1, d))
+    K = rng.standard_normal((B, Hkv, T, d))
+    V = rng.standard_normal((B, Hkv, T, d))
+    p = 52
+    idx = np.broadcast_to(np.arange(T, dtype=np.int32), (B, Hkv, 1, T))  # tokens after p are ignored
+    got = oracle.token_sparse_attention(Q, K, V, idx, p, 0.1)
+    want = oracle.dense_causal_attention(Q, K[:, :, : p + 1], V[:, :, : p + 1], p, 0.1)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_token_attention_equals_block_attention_on_the_same_tokens():
+    rng = np.random.default_rng(14)
+    B, Hq, Hkv, T, d = 1, 4, 2, 256, 128
+    Q = rng.standard_normal((B, Hq, 1, d))
+    K = rng.standard_normal((B, Hkv, T, d))
+    V = rng.standard_normal((B, Hkv, T, d))
+    blocks = np.array([[[[3, 0, -1]]], [[[1, 2, -1]]]], dtype=np.int32).reshape(B, Hkv, 1, 3)
+    tok = np.full((B, Hkv, 1, 3 * 64), -1, dtype=np.int32)
+    for h in range(Hkv):
+        toks = np.concatenate([np.arange(64 * b, 64 * b + 64) for b in blocks[0, h, 0] if b >= 0])
+        tok[0, h, 0, : toks.size] = toks[::-1]  # any order
+    p = T - 30
+    got = oracle.token_sparse_attention(Q, K, V, tok, p, 0.2)
+    want = oracle.block_sparse_attention(Q, K, V, blocks, p, 0.2)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_token_attention_single_token_and_empty():
+    rng = np.random.default_rng(15)
+    Q = rng.standard_normal((1, 2, 1, 128))
+    K = rng.standard_normal((1, 1, 16, 128))
+    V = rng.standard_normal((1, 1, 16, 128))
+    one = np.array([-1, 9, -1], dtype=np.int32).reshape(1, 1, 1, 3)
+    got = oracle.token_sparse_attention(Q, K, V, one, 15, 1.0)
+    assert np.array_equal(got[0, 0, 0], V[0, 0, 9]) and np.array_equal(got[0, 1, 0], V[0, 0, 9])
+    none = np.full((1, 1, 1, 3), -1, dtype=np.int32)
+    assert np.all(oracle.token_sparse_attention(Q, K, V, none, 15, 1.0) == 0)
+    # a token after the query's position is not visible
+    late = np.array([12, -1, -1], dtype=np.int32).reshape(1, 1, 1, 3)
+    assert np.all(oracle.token_sparse_attention(Q, K, V, late, 10, 1.0) == 0)
