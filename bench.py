@@ -356,6 +356,7 @@ def bench_decode(args) -> int:
         step(i)
     torch.cuda.synchronize()
     projection = bench_projection(kbs, w, dev, kr)
+    token_level = bench_token_level(kbs, w, sets, dev, per_graph, kr)
     decoupled = (decoupled_layers(kbs, w, sets, ws_attn, dev, algorithmic_bytes(w)["step"], n_layers=3 * args.steps)
                  if args.decoupled_layers else None)
 
@@ -402,6 +403,7 @@ def bench_decode(args) -> int:
         "forecast_vs_multihead_select_speedup": round(ms["select_multihead"] / ms["select_forecast"], 3),
         "state_maintenance_us": {k: round(v * 1e3, 2) for k, v in ms_extra.items()},
         "upstream_projection": projection,
+        "token_level": token_level,
     }
     if decoupled is not None:
         result["decoupled_layers"] = decoupled
@@ -474,6 +476,56 @@ def decoupled_layers(kbs, w, sets, ws_attn, dev, step_bytes: int, n_layers: int)
                      "hbm_frac": round(step_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
     out["layers_timed"] = n_layers
     return out
+
+
+def bench_token_level(kbs, w, sets, dev, per_graph: int, kr: int) -> dict:
+    """The token-level Forecast variant at the same shape: the Forecast vector
+    scores all T key tokens of every row, the top k_tok = 64 * k tokens are
+    kept (the block path's token budget) and attended. Algorithmic bytes: all
+    of K plus the scores for the scoring, the scores and the kept indices for
+    the top-k, the kept K and V rows plus Q, O and the indices for the
+    attention (its staging copy is the implementation's own traffic)."""
+    import torch
+    k_tok = 64 * w.k
+    rows = w.B * w.Hkv
+    bufs = []
+    for s in sets:
+        bufs.append({"tok_scores": torch.empty((w.B, w.Hkv, 1, w.T), dtype=torch.float32, device=dev),
+                     "tok_idx": torch.empty((w.B, w.Hkv, 1, k_tok), dtype=torch.int32, device=dev),
+                     "out": torch.empty_like(s["Q"])})
+    need = kbs.workspace_bytes(kbs.OP_TOKEN_ATTN, w.B, w.Hq, w.Hkv, 1, w.T, k_tok)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def score(i):
+        s, b = sets[i % N_SETS], bufs[i % N_SETS]
+        kbs.select_tokens(s["F"], s["K"], w.q_start, scale=w.scale, out=b["tok_scores"])
+
+    def topk(i):
+        b = bufs[i % N_SETS]
+        kbs.topk_blocks(b["tok_scores"], k_tok, out=b["tok_idx"])
+
+    def attn(i):
+        s, b = sets[i % N_SETS], bufs[i % N_SETS]
+        kbs.token_sparse_attn(s["Q"], s["K"], s["V"], b["tok_idx"], w.q_start, scale=w.scale, out=b["out"], ws=ws)
+
+    for i in range(N_SETS):
+        score(i)
+        topk(i)
+        attn(i)
+    torch.cuda.synchronize()
+    ms = {"select_tokens": time_graph(score, per_graph, kr), "topk_tokens": time_graph(topk, per_graph, kr),
+          "token_attention": time_graph(attn, per_graph, kr)}
+    row_bytes = w.d * 2
+    nbytes = {"select_tokens": rows * w.T * row_bytes + rows * row_bytes + rows * w.T * 4,
+              "topk_tokens": rows * w.T * 4 + rows * k_tok * 4,
+              "token_attention": 2 * rows * k_tok * row_bytes + 2 * w.B * w.Hq * row_bytes + rows * k_tok * 4}
+    step = sum(ms.values())
+    log(f"[bench] token-level variant: {step * 1e3:.1f} us per layer-step")
+    return {"k_tok": k_tok,
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in ms.items()},
+            "kernel_GBps": {k: round(nbytes[k] / (ms[k] * 1e-3) / 1e9, 1) for k in ms},
+            "ms_per_step": round(step, 5),
+            "what": "token scores over all of K, top-k of 131072 scores per row, attention over the kept tokens"}
 
 
 def bench_projection(kbs, w, dev, replays: int, D: int = 4096, n_layers: int = 8) -> dict:

@@ -74,7 +74,8 @@ enum sparda_kv_mode {
 enum sparda_op {
   SPARDA_OP_SELECT_FORECAST = 1,
   SPARDA_OP_SELECT_MULTIHEAD = 2,
-  SPARDA_OP_BLOCK_SPARSE_ATTN = 3
+  SPARDA_OP_BLOCK_SPARSE_ATTN = 3,
+  SPARDA_OP_TOKEN_ATTN = 4 /* k_sel = k_tok; sized for fp32 staging (enough for bf16) */
 };
 
 /*
@@ -176,7 +177,9 @@ int sparda_select_multihead(const void* q, const void* k_cmp, float* blk_scores,
  * Candidates are the finite scores; ranked by score (higher first), ties to the
  * lower block index; the first min(k, #candidates) are written in ascending
  * block order, the rest of the row is -1. Scores must not be NaN.
- * Supported: 1 <= k <= nB <= 8192.
+ * Supported: 1 <= k <= nB <= 2^26. Rows longer than 8192 (token scores) go
+ * through a top-k that streams the row from memory (one workgroup per row):
+ * the same rule, the same result.
  */
 int sparda_topk_blocks(const float* blk_scores, int32_t* idx, int rows, int nB, int k,
                        void* stream);
@@ -343,6 +346,43 @@ int sparda_prefetch_blocks_cached(const void* host_k, const void* host_v, const 
  */
 int sparda_project_qkvf(const void* x, const void* w, void* q, void* k, void* v, void* f, int dtype, int B,
                         int D, int Hq, int Hkv, int n_f, int d, void* stream);
+
+/*
+ * Token-level Forecast (a variant). [P2] 六 names, as future work for models
+ * with token-level sparse attention, a forecaster that predicts an importance
+ * score per key token instead of per block; [P1] paragraph on DSA: a small
+ * indexer picks the important tokens in place of the queries. The pages fix
+ * neither the keys nor the number of tokens kept; here the Forecast vector
+ * scores every visible key token directly and the top k_tok tokens are kept
+ * by the top-k rule (sparda_topk_blocks on the token scores).
+ *
+ * sparda_select_tokens: decode token scores
+ *   f [B, Hkv, 1, d], k [B, Hkv, T, d] (the layer's keys)
+ *   tok_scores [B, Hkv, 1, T] float32 out: scale * f . k[t] for t <= p, -inf
+ *   for t > p, where p is the sequence's q_pos entry (clamped to -1..T-1) or
+ *   q_start when q_pos is NULL.
+ * Supported: fp32/bf16, d = 128, 1 <= T <= 2^26, -1 <= q_start < T,
+ * B * Hkv <= 65535. f and k 16-byte aligned; B = 0 is a no-op. Async on stream.
+ */
+int sparda_select_tokens(const void* f, const void* k, float* tok_scores, int dtype, int B, int Hkv, int T,
+                         int q_start, const int* q_pos, int d, float scale, void* stream);
+
+/*
+ * sparda_token_sparse_attn: GQA attention at decode over the kept tokens only
+ *   q [B, Hq, 1, d], k, v [B, Hkv, T, d], tok_idx [B, Hkv, 1, k_tok] int32
+ *   (token positions, any order; entries < 0 or > p are padding), out
+ *   [B, Hq, 1, d] written: softmax(scale q . k[j]) over the kept j, times
+ *   v[j]; a query with no kept token gets zeros.
+ * The kept rows are compacted into staging in ws, then attended as k_tok / 64
+ * blocks of staging. ws: sparda_workspace_bytes(SPARDA_OP_TOKEN_ATTN, B, Hq,
+ * Hkv, 1, T, d, k_tok) bytes, 256-byte aligned, owned by the caller; it must
+ * not be shared by calls in flight at once.
+ * Supported: fp32/bf16, d = 128, Hq / Hkv in {1, 2, 4, 8}, k_tok a multiple of
+ * 64 in 64..2^20, 1 <= T <= 2^26, B * Hkv <= 65535. Async on stream.
+ */
+int sparda_token_sparse_attn(const void* q, const void* k, const void* v, const int32_t* tok_idx, void* out,
+                             int dtype, int B, int Hq, int Hkv, int T, int q_start, const int* q_pos, int d,
+                             int k_tok, float scale, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes the call `op` needs for these sizes (0 when none). */
 size_t sparda_workspace_bytes(int op, int B, int Hq, int Hkv, int Tq, int T, int d, int k_sel);

@@ -23,6 +23,7 @@ KV_SLOTS = 2
 OP_SELECT_FORECAST = 1
 OP_SELECT_MULTIHEAD = 2
 OP_BLOCK_SPARSE_ATTN = 3
+OP_TOKEN_ATTN = 4
 
 HEAD_DIM = 128
 BLOCK = 64
@@ -58,6 +59,9 @@ SIGNATURES = {
                                  _sz, _vp, _vp, _vp, _i, _vp, _i, _f, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "sparda_select_forecast_merge": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp,
                                           _i, _i, _i, _vp]),
+    "sparda_select_tokens": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _f, _vp]),
+    "sparda_token_sparse_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _i, _f, _vp, _sz,
+                                      _vp]),
     "sparda_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "sparda_status_string": (_c.c_char_p, [_i]),
     "sparda_last_error": (_c.c_char_p, []),
@@ -272,6 +276,36 @@ def block_sparse_attn(q, k, v, idx, T: int, q_start: int, scale: float | None = 
     _call("sparda_block_sparse_attn", _ptr(q), _ptr(k), _ptr(v), kv_mode, _ptr(idx), _ptr(slot_of), n_slots,
           _ptr(out), _dtype_code(q), B, Hq, Hkv, Tq, q_start, _positions(q_pos, B), T, d, BLOCK, TILE, k_sel, scale,
           _ptr(ws), nbytes, _stream(q, stream))
+    return out
+
+
+def select_tokens(f, k, q_start: int, scale: float | None = None, out=None, stream=None, q_pos=None):
+    """Token-level Forecast scores [B, Hkv, 1, T] float32 of every key token
+    (scale * f . k[t] up to the query's position, -inf after it)."""
+    torch = _torch()
+    B, Hkv, T, d = k.shape
+    scale = d ** -0.5 if scale is None else scale
+    if out is None:
+        out = torch.empty((B, Hkv, 1, T), dtype=torch.float32, device=k.device)
+    _call("sparda_select_tokens", _ptr(f), _ptr(k), _ptr(out), _dtype_code(k), B, Hkv, T, q_start,
+          _positions(q_pos, B), d, scale, _stream(k, stream))
+    return out
+
+
+def token_sparse_attn(q, k, v, tok_idx, q_start: int, scale: float | None = None, out=None, ws=None, stream=None,
+                      q_pos=None):
+    """GQA attention at decode over the kept tokens tok_idx [B, Hkv, 1, k_tok]
+    (int32, -1 padded); O [B, Hq, 1, 128] in q's dtype."""
+    torch = _torch()
+    B, Hq, Tq, d = q.shape
+    Hkv, T = k.shape[1], k.shape[2]
+    k_tok = tok_idx.shape[-1]
+    scale = d ** -0.5 if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    ws, nbytes = _workspace(ws, workspace_bytes(OP_TOKEN_ATTN, B, Hq, Hkv, 1, T, k_tok), q)
+    _call("sparda_token_sparse_attn", _ptr(q), _ptr(k), _ptr(v), _ptr(tok_idx), _ptr(out), _dtype_code(q), B, Hq,
+          Hkv, T, q_start, _positions(q_pos, B), d, k_tok, scale, _ptr(ws), nbytes, _stream(q, stream))
     return out
 
 

@@ -145,6 +145,10 @@ size_t ws_bytes_for(int op, int B, int Hq, int Hkv, int Tq, int T, int k) {
     case SPARDA_OP_BLOCK_SPARSE_ATTN:
       if (Tq == 1) return sparda::decode_attn_ws_bytes(attn_dims(B, Hq, Hkv, Tq, q_start, T, k, 1.f, 0));
       return 0;
+    case SPARDA_OP_TOKEN_ATTN:  // k = k_tok; staging sized for 4-byte elements (bf16 uses half)
+      if (Tq != 1 || k < sparda::kBlock || k % sparda::kBlock != 0) return 0;
+      return sparda::token_attn_ws(nullptr, attn_dims(B, Hq, Hkv, 1, k - 1, k, k / sparda::kBlock, 1.f, 1), k, false)
+          .bytes;
     default:
       return 0;
   }
@@ -295,13 +299,15 @@ SPARDA_EXPORT int sparda_select_multihead(const void* q, const void* k_cmp, floa
 
 SPARDA_EXPORT int sparda_topk_blocks(const float* blk_scores, int32_t* idx, int rows, int nB, int k, void* stream) {
   CHECK(rows >= 0, SPARDA_ERR_INVALID_ARG, "rows = %d < 0", rows);
-  CHECK(nB >= 1 && nB <= 8192, SPARDA_ERR_UNSUPPORTED, "nB = %d outside 1..8192", nB);
+  CHECK(nB >= 1 && nB <= (1 << 26), SPARDA_ERR_UNSUPPORTED, "row length %d outside 1..2^26", nB);
   CHECK(k >= 1 && k <= nB, SPARDA_ERR_INVALID_ARG, "k = %d outside 1..nB (%d)", k, nB);
   CHECK(rows <= 2147483647, SPARDA_ERR_UNSUPPORTED, "too many rows");
   if (rows == 0) return ok();
   CHECK(blk_scores != nullptr && ((uintptr_t)blk_scores & 3u) == 0, SPARDA_ERR_INVALID_ARG,
         "blk_scores is NULL or not 4-byte aligned");
   CHECK(idx != nullptr && ((uintptr_t)idx & 3u) == 0, SPARDA_ERR_INVALID_ARG, "idx is NULL or not 4-byte aligned");
+  if (nB > 8192)  // long rows (token scores): the streaming top-k
+    return hip_status(sparda::launch_topk_long(blk_scores, idx, rows, nB, k, (hipStream_t)stream), "topk launch");
   return hip_status(sparda::launch_topk(blk_scores, idx, rows, nB, k, (hipStream_t)stream), "topk launch");
 }
 
@@ -627,4 +633,67 @@ SPARDA_EXPORT int sparda_prefetch_blocks_cached(const void* host_k, const void* 
                                                    dtype == SPARDA_BF16 ? 2 : 4, B, Hkv, nB, k_sel, n_slots, nwg,
                                                    (hipStream_t)side_stream),
                     "prefetch_blocks_cached launch");
+}
+
+// ---- token-level Forecast variant ----
+
+SPARDA_EXPORT int sparda_select_tokens(const void* f, const void* k, float* tok_scores, int dtype, int B, int Hkv,
+                                       int T, int q_start, const int* q_pos, int d, float scale, void* stream) {
+  if (int e = check_dtype(dtype)) return e;
+  CHECK(B >= 0 && Hkv >= 1, SPARDA_ERR_INVALID_ARG, "B %d / Hkv %d out of range", B, Hkv);
+  CHECK(d == sparda::kHeadDim, SPARDA_ERR_UNSUPPORTED, "head dim %d != 128", d);
+  CHECK(T >= 1 && T <= (1 << 26), SPARDA_ERR_UNSUPPORTED, "T = %d outside 1..2^26", T);
+  CHECK(q_start >= -1 && q_start < T, SPARDA_ERR_INVALID_ARG, "q_start %d outside -1..T-1", q_start);
+  CHECK(std::isfinite(scale), SPARDA_ERR_INVALID_ARG, "scale is not finite");
+  CHECK((long)B * Hkv <= 65535, SPARDA_ERR_UNSUPPORTED, "B * Hkv = %ld rows > 65535", (long)B * Hkv);
+  if (int e = check_q_pos(q_pos, 1)) return e;
+  if (B == 0) return ok();
+  CHECK_PTR(f);
+  CHECK_PTR(k);
+  CHECK(tok_scores != nullptr && ((uintptr_t)tok_scores & 3u) == 0, SPARDA_ERR_INVALID_ARG,
+        "tok_scores is NULL or not 4-byte aligned");
+  return hip_status(sparda::launch_token_scores(f, k, tok_scores, dtype == SPARDA_BF16, B * Hkv, T, q_start, q_pos,
+                                                Hkv, scale, (hipStream_t)stream),
+                    "select_tokens launch");
+}
+
+SPARDA_EXPORT int sparda_token_sparse_attn(const void* q, const void* k, const void* v, const int32_t* tok_idx,
+                                           void* out, int dtype, int B, int Hq, int Hkv, int T, int q_start,
+                                           const int* q_pos, int d, int k_tok, float scale, void* ws,
+                                           size_t ws_bytes, void* stream) {
+  if (int e = check_dtype(dtype)) return e;
+  CHECK(B >= 0 && Hkv >= 1 && Hq >= Hkv, SPARDA_ERR_INVALID_ARG, "B %d / Hq %d / Hkv %d out of range", B, Hq, Hkv);
+  CHECK(Hq % Hkv == 0, SPARDA_ERR_INVALID_ARG, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
+  const int G = Hq / Hkv;
+  CHECK(G == 1 || G == 2 || G == 4 || G == 8, SPARDA_ERR_UNSUPPORTED, "group size %d not in {1, 2, 4, 8}", G);
+  CHECK(d == sparda::kHeadDim, SPARDA_ERR_UNSUPPORTED, "head dim %d != 128", d);
+  CHECK(T >= 1 && T <= (1 << 26), SPARDA_ERR_UNSUPPORTED, "T = %d outside 1..2^26", T);
+  CHECK(q_start >= -1 && q_start < T, SPARDA_ERR_INVALID_ARG, "q_start %d outside -1..T-1", q_start);
+  CHECK(k_tok >= sparda::kBlock && k_tok % sparda::kBlock == 0 && k_tok <= (1 << 20), SPARDA_ERR_UNSUPPORTED,
+        "k_tok = %d must be a multiple of 64 in 64..2^20", k_tok);
+  CHECK(std::isfinite(scale), SPARDA_ERR_INVALID_ARG, "scale is not finite");
+  CHECK((long)B * Hkv <= 65535, SPARDA_ERR_UNSUPPORTED, "B * Hkv = %ld rows > 65535", (long)B * Hkv);
+  if (int e = check_q_pos(q_pos, 1)) return e;
+  if (B == 0) return ok();
+  CHECK_PTR(q);
+  CHECK_PTR(k);
+  CHECK_PTR(v);
+  CHECK_PTR(out);
+  CHECK(tok_idx != nullptr && ((uintptr_t)tok_idx & 3u) == 0, SPARDA_ERR_INVALID_ARG,
+        "tok_idx is NULL or not 4-byte aligned");
+  const bool bf16 = dtype == SPARDA_BF16;
+  // the attention over staging: T = k_tok slots read as k_tok / 64 blocks, each
+  // row's visible slots given as its own position
+  sparda::AttnDims td = attn_dims(B, Hq, Hkv, 1, k_tok - 1, k_tok, k_tok / sparda::kBlock, scale, SPARDA_KV_STAGING);
+  sparda::TokenAttnWs w = sparda::token_attn_ws(ws, td, k_tok, bf16);
+  CHECK(ws != nullptr && ((uintptr_t)ws & 255u) == 0 && ws_bytes >= w.bytes, SPARDA_ERR_INVALID_ARG,
+        "workspace: need %zu bytes, 256-byte aligned (got %zu)", w.bytes, ws_bytes);
+  td.q_pos = w.pos_eff;
+  td.q_pos_per_row = true;
+  hipError_t e = sparda::launch_token_gather(k, v, tok_idx, w, bf16, B * Hkv, T, k_tok, q_start, q_pos, Hkv,
+                                             (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "token gather launch");
+  return hip_status(sparda::launch_attn_decode(q, w.stage_k, w.stage_v, w.blk_idx, out, bf16, td, w.attn_ws,
+                                               (hipStream_t)stream),
+                    "token attention launch");
 }

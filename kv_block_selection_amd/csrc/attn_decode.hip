@@ -439,7 +439,7 @@ static void launch_attn_g(const void* q, const void* k, const void* v, const int
   float2* part_ml = pp.part_ml;
   if (scores == nullptr) {
     hipLaunchKernelGGL((attn_decode_kernel<Tag, G, 1, 0>), dim3(rows, splits), dim3(kWave), 0, s,
-                       (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, nullptr, nullptr, part_o, part_ml, (uint8_t*)out, d.T, d.nB, d.k, d.kv_mode, d.q_start, d.q_pos, d.Hkv,
+                       (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, idx, nullptr, nullptr, part_o, part_ml, (uint8_t*)out, d.T, d.nB, d.k, d.kv_mode, d.q_start, d.q_pos, d.q_pos_per_row ? 1 : d.Hkv,
                        d.slot_of, d.n_slots, bps, splits, d.scale);
   } else {
     // top-k fused in front: four splits per workgroup, each workgroup of a
@@ -449,7 +449,7 @@ static void launch_attn_g(const void* q, const void* k, const void* v, const int
   hipLaunchKernelGGL((attn_decode_kernel<Tag, G, 4, N>), grid, dim3(4 * kWave), 0, s, (const uint8_t*)q,         \
                      (const uint8_t*)k, (const uint8_t*)v, nullptr, const_cast<int32_t*>(idx), scores, part_o,    \
                      part_ml,                                                                                    \
-                     (uint8_t*)out, d.T, d.nB, d.k, d.kv_mode, d.q_start, d.q_pos, d.Hkv, d.slot_of, d.n_slots, bps, \
+                     (uint8_t*)out, d.T, d.nB, d.k, d.kv_mode, d.q_start, d.q_pos, d.q_pos_per_row ? 1 : d.Hkv, d.slot_of, d.n_slots, bps, \
                      splits, d.scale)
     if (d.nB <= 256) SPARDA_FUSED(1);
     else if (d.nB <= 2048) SPARDA_FUSED(8);

@@ -28,6 +28,7 @@ struct AttnDims {
   const int* q_pos;  // decode only: per-sequence query positions [B], or NULL
   const int32_t* slot_of;  // kv_mode 2: staging slot of each selected block [B*Hkv, k]
   int n_slots;             // kv_mode 2: staging slots per row
+  bool q_pos_per_row = false;  // q_pos holds one position per (sequence, KV head) row
 };
 
 // where a decode attention's block-range results sit in its workspace
@@ -115,5 +116,24 @@ hipError_t launch_prefetch_cached(const void* host_k, const void* host_v, const 
 hipError_t launch_prefetch(const void* host_k, const void* host_v, const int32_t* idx, void* stage_k,
                            void* stage_v, int elem_bytes, int B, int Hkv, int nB, int k,
                            int num_workgroups, hipStream_t s);
+
+// token.hip: the token-level Forecast variant. Token scores of rows [rows, T]
+// at the query position (per sequence: q_pos, else p); the top-k of rows
+// longer than 8192 (any length); the workspace of a token attention and the
+// compaction of the kept token rows into its staging.
+struct TokenAttnWs {
+  void* stage_k;     // [rows, k_tok, 128] in the storage dtype
+  void* stage_v;
+  int32_t* blk_idx;  // [rows, k_tok / 64]: 0, 1, ...
+  int* pos_eff;      // [rows]: valid staging slots - 1
+  void* attn_ws;     // the staging-mode attention's own workspace
+  size_t bytes;
+};
+hipError_t launch_token_scores(const void* f, const void* k, float* scores, bool bf16, int rows, int T, int p,
+                               const int* q_pos, int hkv, float scale, hipStream_t s);
+hipError_t launch_topk_long(const float* scores, int32_t* idx, int rows, int n, int k, hipStream_t s);
+TokenAttnWs token_attn_ws(void* ws, const AttnDims& token_d, int k_tok, bool bf16);
+hipError_t launch_token_gather(const void* k, const void* v, const int32_t* tok_idx, const TokenAttnWs& w, bool bf16,
+                               int rows, int T, int k_tok, int p, const int* q_pos, int hkv, hipStream_t s);
 
 }  // namespace sparda

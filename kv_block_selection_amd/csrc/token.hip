@@ -1,0 +1,298 @@
+// Token-level Forecast, the variant the pages name as future work
+// (techwalker.com article, section 六: for models whose sparse attention is
+// token-level, the forecaster would predict an importance score per key token
+// instead of per block; bittide.aicompass.dev summary post, paragraph on DSA:
+// a small indexer picks the important tokens in place of the queries). The
+// pages define neither the keys such a forecaster reads nor how many tokens it
+// keeps. Here the layer's Forecast vector scores every visible key token (no
+// compression, no pooling), the same top-k rule as for blocks keeps the best
+// k_tok tokens, and attention runs over exactly those tokens.
+//
+// token_scores_kernel: scores [rows, T] = scale * f . K[t] for t <= p and -inf
+//   after p; an HBM-bound GEMV over every key row (16 lanes per 256-byte row,
+//   all of a workgroup's loads in flight before the first is used).
+// topk_long_kernel: the top-k rule for rows too long for the LDS-resident
+//   top-k (any length): one 1024-thread workgroup per row, four 8-bit radix
+//   passes over the order keys streamed from memory, then the kept indices in
+//   ascending order by a scan in index order (ties to the lower index).
+// token_gather_kernel: the kept token rows of K and V compacted into staging
+//   [rows, k_tok, 128] (valid entries in their order, the slots past the
+//   row's count zeroed), the row's count of valid entries, and the block list
+//   0 .. k_tok/64 - 1 through which the staging-mode attention reads it.
+#include "common.h"
+#include "launch.h"
+#include "select_row.h"
+#include "topk_row.h"
+
+namespace sparda {
+
+constexpr int kTokIter = 16;       // key rows per thread group in flight
+constexpr int kLongThreads = 1024;  // threads of a long-row top-k workgroup
+constexpr int kLongEPT = 8;         // consecutive elements per thread in the output scan
+
+template <typename Tag>
+__global__ __launch_bounds__(256) void token_scores_kernel(const uint8_t* __restrict__ f,
+                                                           const uint8_t* __restrict__ kbuf,
+                                                           float* __restrict__ scores, int T, int p_all,
+                                                           const int* __restrict__ q_pos, int hkv, float scale) {
+  using R = RowGeom<Tag>;
+  const long row = blockIdx.y;
+  const int p = row_position(q_pos, row, hkv, p_all, T);  // -1 .. T - 1
+  const int lane = threadIdx.x % R::LPR;
+  const int slot = threadIdx.x / R::LPR;
+  const long t0 = (long)blockIdx.x * (kTokIter * R::SLOTS);
+  const u32x4 fv = load16(f + row * R::RB + lane * 16);
+  const uint8_t* base = kbuf + row * (long)T * R::RB + lane * 16;
+  u32x4 kv[kTokIter];
+#pragma unroll
+  for (int it = 0; it < kTokIter; ++it) {
+    const long t = t0 + it * R::SLOTS + slot;
+    kv[it] = t <= p ? load16_nt(base + t * R::RB) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int it = 0; it < kTokIter; ++it) {
+    const long t = t0 + it * R::SLOTS + slot;
+    const float s = group_sum<R::LPR>(dot16<Tag>(fv, kv[it], 0.f));
+    if (lane == 0 && t < T) scores[row * (long)T + t] = t <= p ? s * scale : -INFINITY;
+  }
+}
+
+__global__ __launch_bounds__(kLongThreads) void topk_long_kernel(const float* __restrict__ scores,
+                                                                 int32_t* __restrict__ idx, int n, int k) {
+  __shared__ int hist[256];
+  __shared__ int s_tot[kLongThreads / kWave];
+  __shared__ int s_digit, s_above, s_ncand;
+  const int t = threadIdx.x;
+  const int lane = t % kWave;
+  const int wid = t / kWave;
+  const float* src = scores + (long)blockIdx.x * n;
+  int32_t* dst = idx + (long)blockIdx.x * k;
+
+  // Radix select of the k-th largest order key, 8 bits per pass from the top:
+  // after the passes, `prefix` is that key and `remaining` the number of keys
+  // equal to it still to take (the lowest indices first).
+  uint32_t prefix = 0;
+  int remaining = 0, n_cand = 0;
+  bool take_all = false;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    if (t < 256) hist[t] = 0;
+    __syncthreads();
+    for (long i = t; i < n; i += kLongThreads) {
+      const uint32_t key = order_key(src[i]);
+      if (key != 0u && (key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (wid == 0) {
+      // lane handles digits 255 - 4 lane .. 252 - 4 lane, descending
+      int h[4], sum = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[i] = hist[255 - 4 * lane - i];
+        sum += h[i];
+      }
+      const int incl = wave_incl_scan(sum);
+      const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+      const int want = pass == 0 ? min(k, total) : remaining;
+      int above = incl - sum;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (above < want && want <= above + h[i]) {  // one lane, one digit (want >= 1)
+          s_digit = 255 - 4 * lane - i;
+          s_above = above;
+        }
+        above += h[i];
+      }
+      if (pass == 0 && lane == 0) s_ncand = total;
+    }
+    __syncthreads();
+    if (pass == 0) {
+      n_cand = s_ncand;
+      remaining = min(k, n_cand);
+      take_all = remaining == n_cand;  // includes a row with no candidate
+      if (take_all) break;
+    }
+    prefix |= (uint32_t)s_digit << shift;
+    remaining -= s_above;
+  }
+
+  // Kept: every key above `prefix` and the first `remaining` keys equal to it
+  // (all candidates when take_all), written in index order.
+  const uint32_t tau = prefix;
+  const int take_eq = take_all ? 0 : remaining;
+  const int kk = min(k, n_cand);
+  int gt_base = 0, eq_base = 0;
+  for (long c0 = 0; c0 < n; c0 += (long)kLongThreads * kLongEPT) {
+    const long i0 = c0 + (long)t * kLongEPT;
+    uint32_t key[kLongEPT];
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < kLongEPT; ++j) {
+      key[j] = i0 + j < n ? order_key(src[i0 + j]) : 0u;
+      gt += take_all ? key[j] != 0u : key[j] > tau;
+      eq += !take_all && key[j] == tau;
+    }
+    const int packed = gt | (eq << 16);  // at most 8192 each
+    const int incl = wave_incl_scan(packed);
+    if (lane == kWave - 1) s_tot[wid] = incl;
+    __syncthreads();
+    int before = incl - packed, chunk = 0;
+#pragma unroll
+    for (int w = 0; w < kLongThreads / kWave; ++w) {
+      const int v = s_tot[w];
+      before += w < wid ? v : 0;
+      chunk += v;
+    }
+    int g_before = gt_base + (before & 0xFFFF);
+    int e_before = eq_base + (before >> 16);
+#pragma unroll
+    for (int j = 0; j < kLongEPT; ++j) {
+      const bool is_gt = take_all ? key[j] != 0u : key[j] > tau;
+      const bool is_eq = !take_all && key[j] == tau;
+      if (is_gt) {
+        const int pos = g_before + min(e_before, take_eq);
+        if (pos < kk) dst[pos] = (int32_t)(i0 + j);
+        ++g_before;
+      } else if (is_eq) {
+        if (e_before < take_eq && g_before + e_before < kk) dst[g_before + e_before] = (int32_t)(i0 + j);
+        ++e_before;
+      }
+    }
+    gt_base += chunk & 0xFFFF;
+    eq_base += chunk >> 16;
+    __syncthreads();  // s_tot is rewritten by the next chunk
+  }
+  for (int q = kk + t; q < k; q += kLongThreads) dst[q] = -1;
+}
+
+// Sum of one int per thread over a 256-thread workgroup (every thread gets it).
+__device__ __forceinline__ int sum256(int v, int* s_w) {
+  v = wave_isum(v);
+  __syncthreads();  // s_w may still be read from a previous use
+  if (threadIdx.x % kWave == 0) s_w[threadIdx.x / kWave] = v;
+  __syncthreads();
+  return s_w[0] + s_w[1] + s_w[2] + s_w[3];
+}
+
+template <typename Tag>
+__global__ __launch_bounds__(256) void token_gather_kernel(
+    const uint8_t* __restrict__ kbuf, const uint8_t* __restrict__ vbuf, const int32_t* __restrict__ tok_idx,
+    uint8_t* __restrict__ stage_k, uint8_t* __restrict__ stage_v, int32_t* __restrict__ blk_idx,
+    int* __restrict__ pos_eff, int T, int k_tok, int p_all, const int* __restrict__ q_pos, int hkv) {
+  using R = RowGeom<Tag>;
+  __shared__ int s_w[4];
+  __shared__ int32_t s_tok[256];
+  __shared__ int s_pos[256];
+  const long row = blockIdx.y;
+  const int p = row_position(q_pos, row, hkv, p_all, T);  // -1 .. T - 1
+  const int t = threadIdx.x;
+  const int32_t* ti = tok_idx + row * (long)k_tok;
+  const int c0 = blockIdx.x * 256;
+  auto valid = [&](int32_t x) { return x >= 0 && x <= p; };
+
+  // valid entries before this chunk and in the whole row
+  int pre = 0, all = 0;
+  for (int i = t; i < k_tok; i += 256) {
+    const int v = valid(ti[i]);
+    all += v;
+    pre += i < c0 ? v : 0;
+  }
+  pre = sum256(pre, s_w);
+  all = sum256(all, s_w);
+
+  // this chunk's entries: slot of each valid one = valid entries before it
+  const int i = c0 + t;
+  const int32_t tok = i < k_tok ? ti[i] : -1;
+  const int v = valid(tok);
+  const int incl = wave_incl_scan(v);
+  __syncthreads();
+  if (t % kWave == kWave - 1) s_w[t / kWave] = incl;
+  __syncthreads();
+  int before = incl - v;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) before += w < t / kWave ? s_w[w] : 0;
+  s_tok[t] = v ? tok : -1;
+  s_pos[t] = pre + before;
+  __syncthreads();
+
+  const int lane = t % R::LPR;
+  const int slot = t / R::LPR;
+  for (int e = slot; e < 256; e += R::SLOTS) {
+    const int32_t tk = s_tok[e];
+    if (tk >= 0) {
+      const long src = (row * (long)T + tk) * R::RB + lane * 16;
+      const long dst = (row * (long)k_tok + s_pos[e]) * R::RB + lane * 16;
+      store16(stage_k + dst, load16(kbuf + src));
+      store16(stage_v + dst, load16(vbuf + src));
+    }
+  }
+  // slots of this chunk's range past the row's count hold zeros
+  for (int e = slot; e < 256; e += R::SLOTS) {
+    const int s = c0 + e;
+    if (s < k_tok && s >= all) {
+      const long dst = (row * (long)k_tok + s) * R::RB + lane * 16;
+      store16(stage_k + dst, u32x4{0, 0, 0, 0});
+      store16(stage_v + dst, u32x4{0, 0, 0, 0});
+    }
+  }
+  if (blockIdx.x == 0) {
+    if (t == 0) pos_eff[row] = all - 1;  // staging slots 0 .. all - 1 are visible
+    const int nb = k_tok / kBlock;
+    for (int j = t; j < nb; j += 256) blk_idx[row * (long)nb + j] = j;
+  }
+}
+
+hipError_t launch_token_scores(const void* f, const void* k, float* scores, bool bf16, int rows, int T, int p,
+                               const int* q_pos, int hkv, float scale, hipStream_t s) {
+  if (bf16) {
+    using R = RowGeom<BF16Tag>;
+    const dim3 grid((unsigned)((T + kTokIter * R::SLOTS - 1) / (kTokIter * R::SLOTS)), rows);
+    hipLaunchKernelGGL(token_scores_kernel<BF16Tag>, grid, dim3(256), 0, s, (const uint8_t*)f, (const uint8_t*)k,
+                       scores, T, p, q_pos, hkv, scale);
+  } else {
+    using R = RowGeom<F32Tag>;
+    const dim3 grid((unsigned)((T + kTokIter * R::SLOTS - 1) / (kTokIter * R::SLOTS)), rows);
+    hipLaunchKernelGGL(token_scores_kernel<F32Tag>, grid, dim3(256), 0, s, (const uint8_t*)f, (const uint8_t*)k,
+                       scores, T, p, q_pos, hkv, scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_long(const float* scores, int32_t* idx, int rows, int n, int k, hipStream_t s) {
+  hipLaunchKernelGGL(topk_long_kernel, dim3(rows), dim3(kLongThreads), 0, s, scores, idx, n, k);
+  return hipGetLastError();
+}
+
+TokenAttnWs token_attn_ws(void* ws, const AttnDims& token_d, int k_tok, bool bf16) {
+  const size_t rows = (size_t)token_d.B * token_d.Hkv;
+  const size_t esz = bf16 ? 2 : 4;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  TokenAttnWs w;
+  char* b = (char*)ws;
+  const size_t stage = al(rows * k_tok * kHeadDim * esz);
+  const size_t blk = al(rows * (k_tok / kBlock) * sizeof(int32_t));
+  const size_t pos = al(rows * sizeof(int));
+  w.stage_k = b;
+  w.stage_v = b + stage;
+  w.blk_idx = (int32_t*)(b + 2 * stage);
+  w.pos_eff = (int*)(b + 2 * stage + blk);
+  w.attn_ws = b + 2 * stage + blk + pos;
+  w.bytes = 2 * stage + blk + pos + decode_attn_ws_bytes(token_d);
+  return w;
+}
+
+hipError_t launch_token_gather(const void* k, const void* v, const int32_t* tok_idx, const TokenAttnWs& w, bool bf16,
+                               int rows, int T, int k_tok, int p, const int* q_pos, int hkv, hipStream_t s) {
+  const dim3 grid((unsigned)((k_tok + 255) / 256), rows);
+#define SPARDA_GATHER(TAG)                                                                                          \
+  hipLaunchKernelGGL(token_gather_kernel<TAG>, grid, dim3(256), 0, s, (const uint8_t*)k, (const uint8_t*)v,       \
+                     tok_idx, (uint8_t*)w.stage_k, (uint8_t*)w.stage_v, w.blk_idx, w.pos_eff, T, k_tok, p, q_pos, \
+                     hkv)
+  if (bf16) SPARDA_GATHER(BF16Tag);
+  else SPARDA_GATHER(F32Tag);
+#undef SPARDA_GATHER
+  return hipGetLastError();
+}
+
+}  // namespace sparda

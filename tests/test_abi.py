@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in kbs.SIGNATURES, f"binding lacks {n}"
@@ -112,7 +112,7 @@ def test_multihead_and_attention_validation(lib):
 
 def test_topk_and_prefetch_validation(lib):
     assert lib.sparda_topk_blocks(P, P, 4, 0, 1, None) == 2
-    assert lib.sparda_topk_blocks(P, P, 4, 8193, 1, None) == 2
+    assert lib.sparda_topk_blocks(P, P, 4, (1 << 26) + 1, 1, None) == 2
     assert lib.sparda_topk_blocks(P, P, 4, 64, 65, None) == 1
     assert lib.sparda_topk_blocks(P, P, -1, 64, 4, None) == 1
     assert lib.sparda_topk_blocks(0, P, 4, 64, 4, None) == 1
@@ -331,3 +331,40 @@ def test_decode_layer_validation(lib, kw, status, needle):
 def test_decode_layer_optional_parts(lib):
     # no merge (m_out NULL) and no next selection (f_next NULL) with B = 0: valid, launches nothing
     assert _layer(lib, m_out=None, f_n=None, B=0) == 0
+
+
+def test_token_level_validation(lib):
+    # sparda_select_tokens(f, k, scores, dtype, B, Hkv, T, q_start, q_pos, d, scale, stream)
+    st = lib.sparda_select_tokens
+    assert st(P, P, P, 7, 1, 8, 4096, 4095, None, 128, 0.1, None) == 1
+    assert st(P, P, P, 1, 1, 8, 4096, 4095, None, 64, 0.1, None) == 2
+    assert st(P, P, P, 1, 1, 8, 4096, 4096, None, 128, 0.1, None) == 1 and b"q_start" in lib.sparda_last_error()
+    assert st(P, P, P, 1, 1, 8, 4096, 4095, None, 128, float("nan"), None) == 1
+    assert st(P, P, P, 1, 4096, 16, 4096, 4095, None, 128, 0.1, None) == 2 and b"rows" in lib.sparda_last_error()
+    assert st(None, P, P, 1, 1, 8, 4096, 4095, None, 128, 0.1, None) == 1
+    assert st(P, P, P + 2, 1, 1, 8, 4096, 4095, None, 128, 0.1, None) == 1
+    assert st(P, P, P, 1, 0, 8, 4096, 4095, None, 128, 0.1, None) == 0  # empty batch: no launch
+    # sparda_token_sparse_attn(q, k, v, tok_idx, out, dtype, B, Hq, Hkv, T, q_start, q_pos, d, k_tok, scale,
+    #                          ws, ws_bytes, stream)
+    ta = lib.sparda_token_sparse_attn
+
+    def call(**kw):
+        a = dict(dtype=1, B=1, Hq=32, Hkv=8, T=4096, q_start=4095, d=128, k_tok=256, ws=P, ws_bytes=1 << 40,
+                 tok=P)
+        a.update(kw)
+        return ta(P, P, P, a["tok"], P, a["dtype"], a["B"], a["Hq"], a["Hkv"], a["T"], a["q_start"], None,
+                  a["d"], a["k_tok"], 0.1, a["ws"], a["ws_bytes"], None)
+
+    assert call(dtype=9) == 1
+    assert call(Hq=12) == 1 and b"multiple" in lib.sparda_last_error()
+    assert call(Hq=128) == 2 and b"group size" in lib.sparda_last_error()
+    assert call(k_tok=100) == 2 and b"k_tok" in lib.sparda_last_error()
+    assert call(k_tok=0) == 2
+    assert call(tok=None) == 1 and b"tok_idx" in lib.sparda_last_error()
+    assert call(ws_bytes=1000) == 1 and b"workspace" in lib.sparda_last_error()
+    assert call(ws=P + 16) == 1 and b"workspace" in lib.sparda_last_error()
+    assert call(B=0) == 0
+    need = lib.sparda_workspace_bytes(4, 16, 32, 8, 1, 131072, 128, 4096)
+    assert need >= 2 * 128 * 4096 * 128 * 4  # fp32 staging of K and V
+    assert lib.sparda_workspace_bytes(4, 16, 32, 8, 1, 131072, 128, 100) == 0
+
