@@ -79,9 +79,19 @@ __global__ __launch_bounds__(kLongThreads) void topk_long_kernel(const float* __
     const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
     if (t < 256) hist[t] = 0;
     __syncthreads();
-    for (long i = t; i < n; i += kLongThreads) {
-      const uint32_t key = order_key(src[i]);
-      if (key != 0u && (key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    // kLongEPT independent loads per thread go out before their atomics
+    for (long c0 = 0; c0 < n; c0 += (long)kLongThreads * kLongEPT) {
+      float x[kLongEPT];
+#pragma unroll
+      for (int j = 0; j < kLongEPT; ++j) {
+        const long i = c0 + (long)j * kLongThreads + t;
+        x[j] = i < n ? src[i] : -INFINITY;
+      }
+#pragma unroll
+      for (int j = 0; j < kLongEPT; ++j) {
+        const uint32_t key = order_key(x[j]);
+        if (key != 0u && (key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+      }
     }
     __syncthreads();
     if (wid == 0) {
