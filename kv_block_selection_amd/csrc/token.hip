@@ -203,10 +203,19 @@ __global__ __launch_bounds__(256) void token_gather_kernel(
 
   // valid entries before this chunk and in the whole row
   int pre = 0, all = 0;
-  for (int i = t; i < k_tok; i += 256) {
-    const int v = valid(ti[i]);
-    all += v;
-    pre += i < c0 ? v : 0;
+  for (int i0 = 0; i0 < k_tok; i0 += 256 * 8) {  // 8 loads per thread in flight
+    int32_t x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 256 + t;
+      x[u] = i < k_tok ? ti[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int v = valid(x[u]);
+      all += v;
+      pre += i0 + u * 256 + t < c0 ? v : 0;
+    }
   }
   pre = sum256(pre, s_w);
   all = sum256(all, s_w);
