@@ -26,7 +26,7 @@
 
 namespace sparda {
 
-constexpr int kTokIter = 16;       // key rows per thread group in flight
+constexpr int kTokIter = 32;       // key rows per thread group in flight
 constexpr int kLongThreads = 1024;  // threads of a long-row top-k workgroup
 constexpr int kLongEPT = 8;         // consecutive elements per thread in the output scan
 
