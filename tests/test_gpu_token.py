@@ -184,3 +184,47 @@ def test_token_path_128k_rows(gpu):
         local = np.arange(k_tok, dtype=np.int32).reshape(1, 1, 1, k_tok)
         ref = oracle.token_sparse_attention(parity.to_f64(Q[:, G * h:G * h + G]), Kh, Vh, local, k_tok - 1, w.scale)
         parity.check_attention(parity.to_f64(out[:, G * h:G * h + G]), ref, tol("bf16"))
+
+
+def test_token_path_graph_replay(gpu):
+    """Scores, top-k of long rows and attention over the kept tokens captured
+    in one HIP graph: every replay (with eager work and synchronisations in
+    between, and the outputs overwritten first) gives the eager bits."""
+    w = small("bf16", T=64 * 160)  # rows of 10240 scores: the streaming top-k
+    k_tok = 512
+    F, K, V, Q = gen(w, "F"), gen(w, "K"), gen(w, "V"), gen(w, "Q")
+    scores = torch.empty((w.B, w.Hkv, 1, w.T), dtype=torch.float32, device=DEV)
+    idx = torch.empty((w.B, w.Hkv, 1, k_tok), dtype=torch.int32, device=DEV)
+    out = torch.empty_like(Q)
+    ws = torch.empty(kbs.workspace_bytes(kbs.OP_TOKEN_ATTN, w.B, w.Hq, w.Hkv, 1, w.T, k_tok), dtype=torch.uint8,
+                     device=DEV)
+
+    def step():
+        kbs.select_tokens(F, K, w.q_start, scale=w.scale, out=scores)
+        kbs.topk_blocks(scores, k_tok, out=idx)
+        kbs.token_sparse_attn(Q, K, V, idx, w.q_start, scale=w.scale, out=out, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_s, ref_i, ref_o = scores.clone(), idx.clone(), out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        scores.fill_(-1.0)
+        idx.fill_(-7)
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(scores, ref_s), f"replay {rep}: scores"
+        assert torch.equal(idx, ref_i), f"replay {rep}: idx"
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)), f"replay {rep}: attention"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16))
