@@ -283,15 +283,15 @@ def bench_decode(args) -> int:
         kbs.select_forecast(s["F"], s["Kc"], w.T, w.q_start, out=s["scores"],
                             merge_from=(ws_attn, prev["out"], w.T, w.k))
 
-    ws_pair = [ws_attn, torch.zeros_like(ws_attn)]
+    ws_layer = torch.zeros(max(1, kbs.workspace_bytes(kbs.OP_DECODE_LAYER, w.B, w.Hq, w.Hkv, 1, w.T, w.k)),
+                           dtype=torch.uint8, device=dev)
 
     def step_one_launch(i):
-        # layer i in one launch: the merge of layer i-1 (its results in the
-        # other workspace), layer i's top-k + attention, layer i+1's selection
-        s, prev, nxt = sets[i % N_SETS], sets[(i - 1) % N_SETS], sets[(i + 1) % N_SETS]
-        kbs.decode_layer(s["scores"], s["Q"], s["K"], s["V"], w.k, w.T, w.q_start, ws_pair[i % 2], idx=s["idx"],
-                         out=s["out"], merge_from=(ws_pair[(i - 1) % 2], prev["out"], w.T, w.k),
-                         select_next=(nxt["F"], nxt["Kc"], nxt["scores"], w.T, w.q_start))
+        # layer i in one launch: its top-k + attention (finished output) and
+        # layer i+1's Forecast selection, both from layer i's projections
+        s, nxt = sets[i % N_SETS], sets[(i + 1) % N_SETS]
+        kbs.decode_layer(s["scores"], s["Q"], s["K"], s["V"], w.k, w.T, w.q_start, ws_layer, idx=s["idx"],
+                         out=s["out"], select_next=(nxt["F"], nxt["Kc"], nxt["scores"], w.T, w.q_start))
 
     def step_pipelined(i):
         # layer i in the method's layer order: its selection (from the layer
@@ -380,8 +380,9 @@ def bench_decode(args) -> int:
         "data": "synthetic",
         "config": {"workload": w.description, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
                    "block": w.block, "top_k": w.k, "selector": "forecast", "input_sets_rotated": N_SETS,
-                   "schedule": "consecutive layers (the input sets in turn), one launch per layer: the merge of "
-                               "layer l-1's attention, layer l+1's Forecast selection, layer l's top-k + attention"},
+                   "schedule": "consecutive layers (the input sets in turn), one launch per layer: layer l's top-k + "
+                               "attention (finished output) and layer l+1's Forecast selection, both from layer l's "
+                               "projections"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(gbps[dominant], 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps[dominant] / HBM_PEAK_GBPS, 4),
                      "traffic": pmc_traffic(["kv_block_selection_amd/csrc/attn_decode.hip",

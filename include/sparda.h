@@ -75,7 +75,8 @@ enum sparda_op {
   SPARDA_OP_SELECT_FORECAST = 1,
   SPARDA_OP_SELECT_MULTIHEAD = 2,
   SPARDA_OP_BLOCK_SPARSE_ATTN = 3,
-  SPARDA_OP_TOKEN_ATTN = 4 /* k_sel = k_tok; sized for fp32 staging (enough for bf16) */
+  SPARDA_OP_TOKEN_ATTN = 4, /* k_sel = k_tok; sized for fp32 staging (enough for bf16) */
+  SPARDA_OP_DECODE_LAYER = 5 /* sparda_decode_layer (Tq = 1): 0 when each row gets a workgroup */
 };
 
 /*
@@ -264,22 +265,33 @@ int sparda_select_forecast_merge(const void* f, const void* k_cmp, float* blk_sc
                                  int m_k_sel, void* stream);
 
 /*
- * One decode layer in one launch, in the same layer order: the merge of the
- * layer before (m_ws, m_out, m_Hq, m_T, m_k_sel as for
- * sparda_select_forecast_merge; m_out NULL: none), this layer's top-k +
- * attention as sparda_topk_block_sparse_attn_partial (blk_scores ... ws_bytes;
- * its results stay in ws, to be merged by the next layer's call or
- * sparda_merge_partials), and the selection of the next layer as
- * sparda_select_forecast with Tq = 1 (f_next, k_cmp_next, blk_scores_next,
- * q_start_next, q_pos_next, T_next, scale_next; f_next NULL: none). The next
- * layer's selection needs only this layer's Forecast, so it goes first and
- * this layer's attention workgroups take their top-k under its last loads,
- * with no launch boundary between them. The same bits as those calls. bf16
- * only; B and Hkv are shared by the three parts; ws and m_ws must be
- * different buffers (two workspaces used in turn).
+ * One decode layer: this layer's top-k + attention and the next layer's
+ * Forecast selection, in one launch. Layer L's Forecast picks layer L+1's
+ * blocks ([P1] paragraph on the Forecast predicting the next layer's blocks;
+ * [P2] 二), and in a model both it and layer L's queries come from layer L's
+ * hidden state, so the two parts need the same inputs and nothing from each
+ * other; the next layer's queries need this layer's finished output (through
+ * the output projection and the MLP, outside this library), so `out` is
+ * complete when the call's work ends.
+ *   blk_scores, q, k, v, idx, out, q_pos, scale, k_sel: as
+ *     sparda_topk_block_sparse_attn (this layer; T, Hq, q_start its sizes)
+ *   f_next [B, Hkv, 1, d], k_cmp_next [B, Hkv, W_next, d], blk_scores_next
+ *     [B, Hkv, 1, nB_next] out, q_start_next, q_pos_next, T_next, scale_next:
+ *     as sparda_select_forecast with Tq = 1 for the next layer (f_next NULL:
+ *     no selection)
+ *   ws: sparda_workspace_bytes(SPARDA_OP_DECODE_LAYER, B, Hq, Hkv, 1, T, d,
+ *     k_sel) bytes, 0 when B * Hkv >= 96: each (sequence, KV head) row then
+ *     gets one workgroup that merges its block ranges itself. With fewer
+ *     rows the ranges' results go to ws and a second, small launch merges them.
+ * idx holds the bits sparda_topk_blocks gives and blk_scores_next those of
+ * sparda_select_forecast; out agrees with sparda_topk_block_sparse_attn to
+ * float32 rounding (the block ranges a row is split into differ). bf16 only;
+ * B, Hkv, d, block, kernel and stride are shared by both parts.
+ * Errors as the separate calls, and SPARDA_ERR_INVALID_ARG when
+ * blk_scores_next overlaps blk_scores, idx, out or ws, or out, idx and
+ * blk_scores overlap one another (both parts run in one grid).
  */
-int sparda_decode_layer(void* m_ws, size_t m_ws_bytes, void* m_out, int m_Hq, int m_T, int m_k_sel,
-                        const float* blk_scores, const void* q, const void* k, const void* v, int32_t* idx,
+int sparda_decode_layer(const float* blk_scores, const void* q, const void* k, const void* v, int32_t* idx,
                         void* out, int Hq, int q_start, const int* q_pos, int T, int k_sel, float scale, void* ws,
                         size_t ws_bytes, const void* f_next, const void* k_cmp_next, float* blk_scores_next,
                         int q_start_next, const int* q_pos_next, int T_next, float scale_next, int dtype, int B,
@@ -370,9 +382,11 @@ int sparda_select_tokens(const void* f, const void* k, float* tok_scores, int dt
 /*
  * sparda_token_sparse_attn: GQA attention at decode over the kept tokens only
  *   q [B, Hq, 1, d], k, v [B, Hkv, T, d], tok_idx [B, Hkv, 1, k_tok] int32
- *   (token positions, any order; entries < 0 or > p are padding), out
- *   [B, Hq, 1, d] written: softmax(scale q . k[j]) over the kept j, times
- *   v[j]; a query with no kept token gets zeros.
+ *   (token positions, any order; entries < 0 or > p are padding; a position
+ *   may appear at most once in a row, as sparda_topk_blocks leaves it: a
+ *   repeated position would be attended once per copy), out [B, Hq, 1, d]
+ *   written: softmax(scale q . k[j]) over the kept j, times v[j]; a query
+ *   with no kept token gets zeros.
  * The kept rows are compacted into staging in ws, then attended as k_tok / 64
  * blocks of staging. ws: sparda_workspace_bytes(SPARDA_OP_TOKEN_ATTN, B, Hq,
  * Hkv, 1, T, d, k_tok) bytes, 256-byte aligned, owned by the caller; it must

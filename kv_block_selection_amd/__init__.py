@@ -24,6 +24,7 @@ OP_SELECT_FORECAST = 1
 OP_SELECT_MULTIHEAD = 2
 OP_BLOCK_SPARSE_ATTN = 3
 OP_TOKEN_ATTN = 4
+OP_DECODE_LAYER = 5
 
 HEAD_DIM = 128
 BLOCK = 64
@@ -55,8 +56,8 @@ SIGNATURES = {
     "sparda_topk_block_sparse_attn_partial": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _i, _i,
                                                    _i, _f, _vp, _sz, _vp]),
     "sparda_merge_partials": (_i, [_vp, _sz, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
-    "sparda_decode_layer": (_i, [_vp, _sz, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _f, _vp,
-                                 _sz, _vp, _vp, _vp, _i, _vp, _i, _f, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "sparda_decode_layer": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _f, _vp, _sz, _vp, _vp, _vp, _i,
+                                 _vp, _i, _f, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "sparda_select_forecast_merge": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp,
                                           _i, _i, _i, _vp]),
     "sparda_select_tokens": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _f, _vp]),
@@ -358,14 +359,14 @@ def topk_block_sparse_attn(scores, q, k, v, k_sel: int, T: int, q_start: int, sc
     return idx, out
 
 
-def decode_layer(scores, q, k, v, k_sel: int, T: int, q_start: int, ws, idx=None, out=None, scale=None, q_pos=None,
-                 merge_from=None, select_next=None, stream=None):
-    """One decode layer in one launch (bf16): this layer's top-k of scores
-    [B, Hkv, 1, nB] and attention of q [B, Hq, 1, 128], its block-range results
-    left in ``ws``; optionally the merge of the layer before (merge_from =
-    (ws_prev, out_prev, T_prev, k_prev), ws_prev a different buffer) and the
-    next layer's Forecast selection (select_next = (f_next, k_cmp_next,
-    scores_next, T_next, q_start_next[, q_pos_next])). Returns (idx, out)."""
+def decode_layer(scores, q, k, v, k_sel: int, T: int, q_start: int, ws=None, idx=None, out=None, scale=None,
+                 q_pos=None, select_next=None, stream=None):
+    """One decode layer (bf16): this layer's top-k of scores [B, Hkv, 1, nB]
+    and attention of q [B, Hq, 1, 128], finished in ``out``, and optionally
+    the next layer's Forecast selection in the same launch (select_next =
+    (f_next, k_cmp_next, scores_next, T_next, q_start_next[, q_pos_next])).
+    ``ws`` is needed only for batches of fewer than 96 (sequence, KV head)
+    rows. Returns (idx, out)."""
     torch = _torch()
     B, Hq, Tq, d = q.shape
     Hkv = k.shape[1]
@@ -374,22 +375,15 @@ def decode_layer(scores, q, k, v, k_sel: int, T: int, q_start: int, ws, idx=None
         idx = torch.empty((B, Hkv, 1, k_sel), dtype=torch.int32, device=q.device)
     if out is None:
         out = torch.empty_like(q)
-    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
-    m_ws = m_out = None
-    m_bytes = m_Hq = m_T = m_k = 0
-    if merge_from is not None:
-        m_ws, m_out, m_T, m_k = merge_from
-        m_bytes = m_ws.numel() * m_ws.element_size() if m_ws is not None else 0
-        m_Hq = m_out.shape[1]
+    ws, nbytes = _workspace(ws, workspace_bytes(OP_DECODE_LAYER, B, Hq, Hkv, 1, T, k_sel), q)
     f_n = kc_n = s_n = qp_n = None
     T_n = q_n = 0
     if select_next is not None:
         f_n, kc_n, s_n, T_n, q_n = select_next[:5]
         qp_n = select_next[5] if len(select_next) > 5 else None
-    _call("sparda_decode_layer", _ptr(m_ws), m_bytes, _ptr(m_out), m_Hq, m_T, m_k, _ptr(scores), _ptr(q), _ptr(k),
-          _ptr(v), _ptr(idx), _ptr(out), Hq, q_start, _positions(q_pos, B), T, k_sel, scale, _ptr(ws), nbytes,
-          _ptr(f_n), _ptr(kc_n), _ptr(s_n), q_n, _positions(qp_n, B), T_n, scale, _dtype_code(q), B, Hkv, d, BLOCK,
-          KERNEL, STRIDE, _stream(q, stream))
+    _call("sparda_decode_layer", _ptr(scores), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out), Hq, q_start,
+          _positions(q_pos, B), T, k_sel, scale, _ptr(ws), nbytes, _ptr(f_n), _ptr(kc_n), _ptr(s_n), q_n,
+          _positions(qp_n, B), T_n, scale, _dtype_code(q), B, Hkv, d, BLOCK, KERNEL, STRIDE, _stream(q, stream))
     return idx, out
 
 

@@ -134,7 +134,13 @@ sparda::AttnDims attn_dims(int B, int Hq, int Hkv, int Tq, int q_start, int T, i
 }
 
 size_t ws_bytes_for(int op, int B, int Hq, int Hkv, int Tq, int T, int k) {
-  if (B <= 0 || Hkv <= 0 || Hq <= 0 || T < sparda::kBlock) return 0;
+  if (B <= 0 || Hkv <= 0 || Hq <= 0) return 0;
+  if (op == SPARDA_OP_TOKEN_ATTN) {  // k = k_tok; staging sized for 4-byte elements (bf16 uses half); any T >= 1
+    if (Tq != 1 || T < 1 || k < sparda::kBlock || k % sparda::kBlock != 0) return 0;
+    return sparda::token_attn_ws(nullptr, attn_dims(B, Hq, Hkv, 1, k - 1, k, k / sparda::kBlock, 1.f, 1), k, false)
+        .bytes;
+  }
+  if (T < sparda::kBlock) return 0;
   const int q_start = T - Tq;
   switch (op) {
     case SPARDA_OP_SELECT_FORECAST:
@@ -145,10 +151,10 @@ size_t ws_bytes_for(int op, int B, int Hq, int Hkv, int Tq, int T, int k) {
     case SPARDA_OP_BLOCK_SPARSE_ATTN:
       if (Tq == 1) return sparda::decode_attn_ws_bytes(attn_dims(B, Hq, Hkv, Tq, q_start, T, k, 1.f, 0));
       return 0;
-    case SPARDA_OP_TOKEN_ATTN:  // k = k_tok; staging sized for 4-byte elements (bf16 uses half)
-      if (Tq != 1 || k < sparda::kBlock || k % sparda::kBlock != 0) return 0;
-      return sparda::token_attn_ws(nullptr, attn_dims(B, Hq, Hkv, 1, k - 1, k, k / sparda::kBlock, 1.f, 1), k, false)
-          .bytes;
+    case SPARDA_OP_DECODE_LAYER: {  // none when every row has a workgroup of its own
+      const sparda::AttnDims ad = attn_dims(B, Hq, Hkv, 1, T - 1, T, k, 1.f, 0);
+      return sparda::decode_layer_row_form(ad) ? 0 : sparda::decode_attn_ws_bytes(ad);
+    }
     default:
       return 0;
   }
@@ -455,8 +461,15 @@ SPARDA_EXPORT int sparda_select_forecast_merge(const void* f, const void* k_cmp,
                     "select_forecast_merge launch");
 }
 
-SPARDA_EXPORT int sparda_decode_layer(void* m_ws, size_t m_ws_bytes, void* m_out, int m_Hq, int m_T, int m_k_sel,
-                                      const float* blk_scores, const void* q, const void* k, const void* v,
+namespace {
+// Byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+}  // namespace
+
+SPARDA_EXPORT int sparda_decode_layer(const float* blk_scores, const void* q, const void* k, const void* v,
                                       int32_t* idx, void* out, int Hq, int q_start, const int* q_pos, int T, int k_sel,
                                       float scale, void* ws, size_t ws_bytes, const void* f_next,
                                       const void* k_cmp_next, float* blk_scores_next, int q_start_next,
@@ -472,16 +485,8 @@ SPARDA_EXPORT int sparda_decode_layer(void* m_ws, size_t m_ws_bytes, void* m_out
   CHECK(nB <= 8192, SPARDA_ERR_UNSUPPORTED, "decode_layer: nB = %d above 8192", nB);
   CHECK(k_sel >= 1 && k_sel <= nB, SPARDA_ERR_INVALID_ARG, "k = %d outside 1..nB (%d)", k_sel, nB);
   CHECK(k_sel <= 1024, SPARDA_ERR_UNSUPPORTED, "decode_layer: k = %d above 1024", k_sel);
-  const size_t need = ws_bytes_for(SPARDA_OP_BLOCK_SPARSE_ATTN, B, Hq, Hkv, 1, T, k_sel);
+  const size_t need = ws_bytes_for(SPARDA_OP_DECODE_LAYER, B, Hq, Hkv, 1, T, k_sel);
   CHECK(ws_bytes >= need, SPARDA_ERR_WORKSPACE, "decode_layer needs %zu workspace bytes, got %zu", need, ws_bytes);
-  // the merge of the layer before
-  sparda::AttnDims mad;
-  const bool merge = m_out != nullptr;
-  if (merge) {
-    if (int e = pending_merge(m_ws, m_ws_bytes, dtype, B, m_Hq, Hkv, m_T, d, m_k_sel, &mad)) return e;
-    CHECK(m_ws == nullptr || ws == nullptr || m_ws != ws || need == 0, SPARDA_ERR_INVALID_ARG,
-          "decode_layer: the merged layer's workspace must not be this layer's");
-  }
   // the next layer's selection
   const bool next = f_next != nullptr;
   if (next) {
@@ -498,23 +503,25 @@ SPARDA_EXPORT int sparda_decode_layer(void* m_ws, size_t m_ws_bytes, void* m_out
   CHECK(idx != nullptr && ((uintptr_t)idx & 3u) == 0, SPARDA_ERR_INVALID_ARG, "idx is NULL or not 4-byte aligned");
   if (need) CHECK_PTR(ws);
   if (int e = check_q_pos(q_pos, 1)) return e;
-  if (next)
-    if (int e = check_q_pos(q_pos_next, 1)) return e;
-  if (merge) {
-    CHECK_PTR(m_out);
-    if (m_ws_bytes) CHECK_PTR(m_ws);
-  }
+  const size_t rows = (size_t)B * Hkv;
+  const size_t scores_b = rows * nB * 4, idx_b = rows * k_sel * 4, out_b = (size_t)B * Hq * d * 2;
+  CHECK(!overlaps(out, out_b, blk_scores, scores_b) && !overlaps(out, out_b, idx, idx_b) &&
+            !overlaps(idx, idx_b, blk_scores, scores_b),
+        SPARDA_ERR_INVALID_ARG, "decode_layer: out, idx and blk_scores must not overlap");
   if (next) {
+    if (int e = check_q_pos(q_pos_next, 1)) return e;
     CHECK_PTR(k_cmp_next);
     CHECK_PTR(blk_scores_next);
+    // the next layer's scores are written while this layer's are read, its
+    // selection and top-k running in the same grid
+    const size_t next_b = rows * (T_next / sparda::kBlock) * 4;
+    CHECK(!overlaps(blk_scores_next, next_b, blk_scores, scores_b) && !overlaps(blk_scores_next, next_b, idx, idx_b) &&
+              !overlaps(blk_scores_next, next_b, out, out_b) && !overlaps(blk_scores_next, next_b, ws, need),
+          SPARDA_ERR_INVALID_ARG,
+          "decode_layer: blk_scores_next must not overlap blk_scores, idx, out or the workspace (they are read or "
+          "written in the same launch)");
   }
   sparda::LayerLaunch L{};
-  sparda::DecodePartials mp{};
-  if (merge) {
-    mp = sparda::decode_attn_partials(m_ws, mad);
-    L.merge = &mp;
-    L.merge_out = m_out;
-  }
   L.attn = attn_dims(B, Hq, Hkv, 1, q_start, T, k_sel, scale, SPARDA_KV_CACHE);
   L.attn.q_pos = q_pos;
   L.scores = blk_scores;

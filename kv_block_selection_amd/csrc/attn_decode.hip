@@ -49,11 +49,14 @@ constexpr float kLazyGrow = 5.545177444479562f;  // 8 ln 2
 #endif
 
 // WPG waves per workgroup, one split each (split = blockIdx.y * WPG + wave).
-// NPT > 0: the workgroup first takes the row's top-k of `scores` itself (256
-// threads, NPT scores per thread; every workgroup of the row computes the
-// same selection, the first also writes it to idx_out) and the waves read the
-// selection from LDS; NPT = 0: the selection comes from idx.
-template <typename Tag, int G, int WPG, int NPT>
+// NPT > 0: the workgroup first takes the row's top-k of `scores` itself (all
+// WPG x 64 threads, NPT scores per thread; every workgroup of the row computes
+// the same selection, the first also writes it to idx_out) and the waves read
+// the selection from LDS; NPT = 0: the selection comes from idx.
+// LDSM: the workgroup holds all of the row's splits (one per wave; waves past
+// the last split contribute nothing) and merges them in LDS, with the merge
+// kernel's arithmetic, into the finished output: no partials, no second launch.
+template <typename Tag, int G, int WPG, int NPT, bool LDSM = false>
 __device__ __forceinline__ void attn_decode_body(
     long row, int wg_split, const uint8_t* __restrict__ q, const uint8_t* __restrict__ kbuf,
     const uint8_t* __restrict__ vbuf, const int32_t* __restrict__ idx, int32_t* __restrict__ idx_out,
@@ -82,13 +85,19 @@ __device__ __forceinline__ void attn_decode_body(
 
   const int32_t* idx_row = idx + row * k;
   if constexpr (NPT > 0) {
-    __shared__ TopkShared sh;
+    __shared__ TopkShared<WPG> sh;
     __shared__ int32_t s_sel[kFusedMaxK];
-    topk_row<NPT>(scores + row * nB, wg_split == 0 ? idx_out + row * k : nullptr, s_sel, nB, k, sh, threadIdx.x);
+    topk_row<NPT, WPG>(scores + row * nB, wg_split == 0 ? idx_out + row * k : nullptr, s_sel, nB, k, sh,
+                       threadIdx.x);
     __syncthreads();
     idx_row = s_sel;
   }
-  if (split >= splits) return;  // a last workgroup with fewer splits than waves
+  // a wave past the row's last split: none of the work below (with LDSM it
+  // still takes part in the merge, with nothing to add)
+  const bool active = split < splits;
+  if constexpr (!LDSM) {
+    if (!active) return;
+  }
   u32x4 qs[G];
 #pragma unroll
   for (int s = 0; s < G; ++s) qs[s] = load16(q + (row * G + slot_head<G>(s, c & 15)) * RB + c * 16);
@@ -115,7 +124,7 @@ __device__ __forceinline__ void attn_decode_body(
   }
 
   const int j0 = split * bps;
-  const int j1 = min(k, j0 + bps);  // >= j0 + 1: every split owns at least one slot
+  const int j1 = min(k, j0 + bps);  // >= j0 + 1 for an active split: it owns at least one slot
   // Stage q = half h of slot j0 + q/2: its first token and its number of valid
   // keys. Padding, out-of-range and wholly-future slots read block 0 of the
   // row (a valid address) with every key masked.
@@ -135,10 +144,13 @@ __device__ __forceinline__ void attn_decode_body(
   const int nstage = 2 * (j1 - j0);
 
   u32x4 kv[NIT], vv[NIT];
-  int nvalid;
-  long tok0 = stage_of(0, nvalid);
+  int nvalid = 0;
+  long tok0 = 0;
+  if (active) {  // an inactive wave reads no stage
+    tok0 = stage_of(0, nvalid);
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) kv[it] = load16_nt(kbuf + (tok0 + it * KPI + r) * RB + c * 16);
+    for (int it = 0; it < NIT; ++it) kv[it] = load16_nt(kbuf + (tok0 + it * KPI + r) * RB + c * 16);
+  }
 
   // One stage of 32 keys: V loads go out first, then QK on the keys already in
   // flight, the online softmax, the next stage's key loads (PREFETCH), then PV.
@@ -255,8 +267,10 @@ __device__ __forceinline__ void attn_decode_body(
     }
     stage_sync();
   };
-  for (int q = 0; q < nstage - 1; ++q) body(q, std::true_type{});
-  body(nstage - 1, std::false_type{});
+  if (active) {
+    for (int q = 0; q < nstage - 1; ++q) body(q, std::true_type{});
+    body(nstage - 1, std::false_type{});
+  }
 
 #pragma unroll
   for (int g = 0; g < G; ++g) l_run[g] = wave_sum(l_run[g]);
@@ -269,6 +283,62 @@ __device__ __forceinline__ void attn_decode_body(
       if constexpr (LPK == 16) x = sum16(x);
       acc[g][e] = sum32(x);
     }
+
+  if constexpr (LDSM) {
+    // each wave's (max, sum, unnormalised output) per head into LDS, then the
+    // merge of merge_row.h over the waves in order: thread t < 32 G takes head
+    // t / 32, channels 4 (t % 32) .. + 3
+    __shared__ float s_mo[WPG][G][kHeadDim];
+    __shared__ float2 s_ml[WPG][G];
+    if (r == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int e = 0; e < E; e += 4)
+          *reinterpret_cast<float4*>(&s_mo[wv][g][c * E + e]) =
+              make_float4(acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]);
+        if (c == 0) s_ml[wv][g] = make_float2(m_run[g], l_run[g]);
+      }
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < G * (kHeadDim / 4)) {
+      const int g = t / (kHeadDim / 4);
+      const int ch = (t % (kHeadDim / 4)) * 4;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < WPG; ++w) M = fmaxf(M, s_ml[w][g].x);
+      float L = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < WPG; ++w) {
+          const float2 ml = s_ml[w][g];
+          if (ml.x != -INFINITY) {
+            const float4 po = *reinterpret_cast<const float4*>(&s_mo[w][g][ch]);
+            const float wt = fast_exp(ml.x - M);
+            L = fmaf(ml.y, wt, L);
+            O[0] = fmaf(po.x, wt, O[0]);
+            O[1] = fmaf(po.y, wt, O[1]);
+            O[2] = fmaf(po.z, wt, O[2]);
+            O[3] = fmaf(po.w, wt, O[3]);
+          }
+        }
+      }
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = L > 0.f ? O[e] / L : 0.f;
+      const long off = (row * G + g) * kHeadDim + ch;
+      if constexpr (kBf16) {
+        uint2 v;
+        v.x = pack_bf16(o[0], o[1]);
+        v.y = pack_bf16(o[2], o[3]);
+        *reinterpret_cast<uint2*>(out + off * 2) = v;
+      } else {
+        *reinterpret_cast<float4*>(out + off * 4) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+    }
+    return;
+  }
 
   if (splits == 1) {
     // final: normalise and store in the storage dtype
@@ -310,43 +380,57 @@ void attn_decode_kernel(
                                      out, T, nB, k, kv_mode, p_all, q_pos, hkv, slot_of, n_slots, bps, splits, scale);
 }
 
-// One decode layer in one launch, in the method's layer order: the merge of
-// layer l-1's attention, the Forecast selection of layer l+1 (which needs
-// only layer l's Forecast and layer l+1's compressed keys) and the top-k +
-// attention of layer l, as workgroup roles of one 1D grid dispatched in that
-// order: attention workgroups start as selection workgroups retire, so their
-// top-k runs under the selection's last loads and no launch boundary
-// separates the two. The kernel runs at the attention's register allocation
-// (2 waves per SIMD), so a selection workgroup takes 128 blocks (513
-// windows, ~130 KB in flight) instead of 16. Each role's arithmetic is that
-// of its own kernel, so the bits are those of the separate calls.
+// One decode layer in one launch, in an order a model can run: layer l's
+// hidden state gives both its queries and the Forecast that scores layer
+// l+1's compressed keys, so this layer's top-k + attention and the next
+// layer's Forecast selection need the same inputs and nothing from each other
+// (bittide.aicompass.dev summary post, paragraph on layer L's Forecast
+// choosing layer L+1's blocks). Their workgroups share one 1D grid, and the
+// layer's output is complete when the launch ends: the next layer's work
+// needs it, through the output projection and the MLP.
+//
+// Row form (enough rows to fill half the chip): the attention comes first,
+// one 8-wave workgroup per (sequence, KV head) row that takes the row's top-k
+// with all 512 threads, gives each wave an equal block range and merges the
+// eight ranges in LDS; the selection workgroups follow and stream the next
+// layer's compressed keys on the CUs the attention leaves free, and on the
+// attention's CUs as they finish. Split form (few rows): selection first,
+// then 4-wave attention workgroups over shorter block ranges whose results
+// go to the workspace; the merge is a second, small launch.
+// Both run at the attention's register allocation (2 waves per SIMD), so a
+// selection workgroup takes 128 blocks (513 windows) instead of 16.
 constexpr int kLayerSelBlocks = 128;
+constexpr int kLayerRowWaves = 8;     // waves of a row-form attention workgroup
+constexpr int kLayerRowMinRows = 96;  // fewest rows for the row form
 
-struct LayerRoles {
-  int n_merge, n_attn, n_sel;
-  // role of workgroup i: 0 merge, 1 attention, 2 selection; *r = index in the role
-  __device__ __forceinline__ int of(int i, int* r) const {
-    if (i < n_merge) {
-      *r = i;
-      return 0;
-    }
-    const int j = i - n_merge;
-    if (j < n_sel) {
-      *r = j;
-      return 2;
-    }
-    *r = j - n_sel;
-    return 1;
+template <typename Tag, int G, int NPT>
+__global__ __launch_bounds__(kLayerRowWaves * 64) __attribute__((amdgpu_waves_per_eu(SPARDA_ATTN_WAVES_PER_EU)))
+void decode_layer_row_kernel(int rows,
+                             // top-k + attention of layer l, one workgroup per row
+                             const uint8_t* __restrict__ q, const uint8_t* __restrict__ kbuf,
+                             const uint8_t* __restrict__ vbuf, int32_t* __restrict__ idx_out,
+                             const float* __restrict__ scores, uint8_t* __restrict__ out, int T, int nB, int k,
+                             int p_all, const int* __restrict__ q_pos, int hkv, int bps, int splits, float scale,
+                             // selection of layer l+1
+                             const uint8_t* __restrict__ f_n, const uint8_t* __restrict__ kc_n,
+                             float* __restrict__ scores_n, int W_n, int nB_n, int n_vis_n,
+                             const int* __restrict__ q_pos_n, int T_n, float scale_n) {
+  if ((int)blockIdx.x < rows) {
+    attn_decode_body<Tag, G, kLayerRowWaves, NPT, true>(blockIdx.x, 0, q, kbuf, vbuf, nullptr, idx_out, scores,
+                                                        nullptr, nullptr, out, T, nB, k, SPARDA_KV_CACHE_MODE, p_all,
+                                                        q_pos, hkv, nullptr, 0, bps, splits, scale);
+  } else {
+    const int r = blockIdx.x - rows;
+    __shared__ float s_win[fsel_lds_floats<Tag, kLayerSelBlocks, kLayerRowWaves * 64>()];
+    fsel_blocks<Tag, kLayerSelBlocks, kLayerRowWaves * 64>(f_n, kc_n, scores_n, W_n, nB_n, n_vis_n, q_pos_n, hkv, T_n,
+                                                          scale_n, r % rows, r / rows, s_win, threadIdx.x);
   }
-};
+}
 
 template <typename Tag, int G, int NPT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SPARDA_ATTN_WAVES_PER_EU)))
-void decode_layer_kernel(LayerRoles roles, int rows,
-                         // merge of layer l-1
-                         const float* __restrict__ m_part_o, const float2* __restrict__ m_part_ml,
-                         uint8_t* __restrict__ m_out, int m_G, int m_splits,
-                         // top-k + attention of layer l
+void decode_layer_kernel(int n_sel, int rows,
+                         // top-k + attention of layer l, block ranges of 4 splits per workgroup
                          const uint8_t* __restrict__ q, const uint8_t* __restrict__ kbuf,
                          const uint8_t* __restrict__ vbuf, int32_t* __restrict__ idx_out,
                          const float* __restrict__ scores, float* __restrict__ part_o, float2* __restrict__ part_ml,
@@ -355,14 +439,12 @@ void decode_layer_kernel(LayerRoles roles, int rows,
                          // selection of layer l+1
                          const uint8_t* __restrict__ f_n, const uint8_t* __restrict__ kc_n, float* __restrict__ scores_n,
                          int W_n, int nB_n, int n_vis_n, const int* __restrict__ q_pos_n, int T_n, float scale_n) {
-  int r;
-  const int role = roles.of(blockIdx.x, &r);
-  if (role == 0) {
-    merge_row_lean<Tag>(r, threadIdx.x, m_part_o, m_part_ml, m_out, m_G, m_splits);
-  } else if (role == 1) {
+  if ((int)blockIdx.x >= n_sel) {
+    const int r = blockIdx.x - n_sel;
     attn_decode_body<Tag, G, 4, NPT>(r % rows, r / rows, q, kbuf, vbuf, nullptr, idx_out, scores, part_o, part_ml, out,
                                      T, nB, k, SPARDA_KV_CACHE_MODE, p_all, q_pos, hkv, nullptr, 0, bps, splits, scale);
   } else {
+    const int r = blockIdx.x;
     __shared__ float s_win[fsel_lds_floats<Tag, kLayerSelBlocks>()];
     fsel_blocks<Tag, kLayerSelBlocks>(f_n, kc_n, scores_n, W_n, nB_n, n_vis_n, q_pos_n, hkv, T_n, scale_n, r % rows,
                                       r / rows, s_win, threadIdx.x);
@@ -459,33 +541,49 @@ static void launch_attn_g(const void* q, const void* k, const void* v, const int
   if (merge) launch_merge<Tag>(pp, out, s);
 }
 
+bool decode_layer_row_form(const AttnDims& d) { return (long)d.B * d.Hkv >= kLayerRowMinRows; }
+
 template <typename Tag, int G>
 static void launch_layer_g(const LayerLaunch& L, hipStream_t s) {
   const AttnDims& d = L.attn;
-  const DecodePartials pp = decode_attn_partials(L.ws, d);
-  const int rows = pp.rows;
-  const bool merge = L.merge != nullptr && L.merge->splits > 1;
-  LayerRoles roles;
-  roles.n_merge = merge ? rows : 0;
-  roles.n_attn = rows * ((pp.splits + 3) / 4);
-  roles.n_sel = L.f_next ? rows * ((L.sel.nB + kLayerSelBlocks - 1) / kLayerSelBlocks) : 0;
-  const int bps = (d.k + pp.splits - 1) / pp.splits;
+  const int rows = d.B * d.Hkv;
+  const int n_sel_chunks = L.f_next ? (L.sel.nB + kLayerSelBlocks - 1) / kLayerSelBlocks : 0;
   const int n_vis_n = L.f_next ? min(L.sel.W, (L.sel.q_start - kKernel + 1) >= 0
                                                   ? (L.sel.q_start - kKernel + 1) / kStride + 1 : 0)
                                : 0;
-  const dim3 grid(roles.n_merge + roles.n_attn + roles.n_sel);
+  if (decode_layer_row_form(d)) {
+    // one workgroup per row: eight equal block ranges, merged in LDS
+    const int bps = (d.k + kLayerRowWaves - 1) / kLayerRowWaves;
+    const int splits = (d.k + bps - 1) / bps;
+    const dim3 grid(rows + rows * n_sel_chunks);
+#define SPARDA_ROWL(N)                                                                                            \
+  hipLaunchKernelGGL((decode_layer_row_kernel<Tag, G, N>), grid, dim3(kLayerRowWaves * 64), 0, s, rows,          \
+                     (const uint8_t*)L.q, (const uint8_t*)L.k, (const uint8_t*)L.v, L.idx, L.scores,               \
+                     (uint8_t*)L.out, d.T, d.nB, d.k, d.q_start, d.q_pos, d.Hkv, bps, splits, d.scale,             \
+                     (const uint8_t*)L.f_next, (const uint8_t*)L.kc_next, L.scores_next, L.sel.W, L.sel.nB,         \
+                     n_vis_n, L.sel.q_pos, L.sel.T, L.sel.scale)
+    if (d.nB <= 512) SPARDA_ROWL(1);
+    else if (d.nB <= 2048) SPARDA_ROWL(4);
+    else SPARDA_ROWL(16);
+#undef SPARDA_ROWL
+    return;
+  }
+  const DecodePartials pp = decode_attn_partials(L.ws, d);
+  const int n_sel = rows * n_sel_chunks;
+  const int n_attn = rows * ((pp.splits + 3) / 4);
+  const int bps = (d.k + pp.splits - 1) / pp.splits;
+  const dim3 grid(n_sel + n_attn);
 #define SPARDA_LAYER(N)                                                                                            \
-  hipLaunchKernelGGL((decode_layer_kernel<Tag, G, N>), grid, dim3(256), 0, s, roles, rows,                        \
-                     merge ? L.merge->part_o : nullptr, merge ? L.merge->part_ml : nullptr, (uint8_t*)L.merge_out,  \
-                     merge ? L.merge->G : 0, merge ? L.merge->splits : 0, (const uint8_t*)L.q, (const uint8_t*)L.k, \
-                     (const uint8_t*)L.v, L.idx, L.scores, pp.part_o, pp.part_ml, (uint8_t*)L.out, d.T, d.nB, d.k,    \
-                     d.q_start, d.q_pos, d.Hkv, bps, pp.splits, d.scale, (const uint8_t*)L.f_next,                   \
-                     (const uint8_t*)L.kc_next, L.scores_next, L.sel.W, L.sel.nB, n_vis_n, L.sel.q_pos, L.sel.T,      \
-                     L.sel.scale)
+  hipLaunchKernelGGL((decode_layer_kernel<Tag, G, N>), grid, dim3(256), 0, s, n_sel, rows, (const uint8_t*)L.q,   \
+                     (const uint8_t*)L.k, (const uint8_t*)L.v, L.idx, L.scores, pp.part_o, pp.part_ml,            \
+                     (uint8_t*)L.out, d.T, d.nB, d.k, d.q_start, d.q_pos, d.Hkv, bps, pp.splits, d.scale,          \
+                     (const uint8_t*)L.f_next, (const uint8_t*)L.kc_next, L.scores_next, L.sel.W, L.sel.nB,         \
+                     n_vis_n, L.sel.q_pos, L.sel.T, L.sel.scale)
   if (d.nB <= 256) SPARDA_LAYER(1);
   else if (d.nB <= 2048) SPARDA_LAYER(8);
   else SPARDA_LAYER(32);
 #undef SPARDA_LAYER
+  launch_merge<Tag>(pp, L.out, s);  // the output is complete when this launch ends
 }
 
 hipError_t launch_decode_layer(const LayerLaunch& L, bool bf16, hipStream_t s) {

@@ -81,12 +81,12 @@ hipError_t launch_topk_attn_decode(const float* scores, const void* q, const voi
                                    void* out, bool bf16, const AttnDims& d, void* ws, bool merge, hipStream_t s);
 DecodePartials decode_attn_partials(void* ws, const AttnDims& d);
 hipError_t launch_merge_partials(void* ws, void* out, bool bf16, const AttnDims& d, hipStream_t s);
-// one decode layer in one launch: merge of the layer before (merge may be
-// NULL), top-k + attention of this layer (results left in ws), selection of
-// the next layer (f_next may be NULL)
+// one decode layer: top-k + attention of this layer (finished output) and
+// the selection of the next layer (f_next may be NULL) in one launch, plus a
+// merge launch when the batch has too few rows for a workgroup per row (ws
+// then holds the block ranges' results)
+bool decode_layer_row_form(const AttnDims& d);
 struct LayerLaunch {
-  const DecodePartials* merge;
-  void* merge_out;
   AttnDims attn;
   const float* scores;
   const void *q, *k, *v;

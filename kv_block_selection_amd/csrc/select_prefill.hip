@@ -127,6 +127,12 @@ __global__ __launch_bounds__(256 * TPW) void fsel_prefill_kernel(const uint8_t* 
         scores[(row * n_tiles + otile) * (long)nB + b] = m;
       }
     }
+    // The carry: this chunk's last window becomes the next chunk's window 0.
+    // Its readers above are lanes of wave 0 too, earlier in program order (the
+    // wait keeps the compiler from moving the copy above them), and the next
+    // chunk's writes of s_cmax come after the barrier below.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (t < TPW) s_cmax[t][0] = s_cmax[t][kChunkW];
     // chunk c + 1 has landed: loads complete in order, so at most LPC
     // outstanding (the score store above counts too) leaves only chunk c + 2's
     if (NBUF == 3 && c + 2 < nchunks) {
@@ -135,7 +141,6 @@ __global__ __launch_bounds__(256 * TPW) void fsel_prefill_kernel(const uint8_t* 
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
     lds_barrier();
-    if (t < TPW) s_cmax[t][0] = s_cmax[t][kChunkW];
     bc = bc == NBUF - 1 ? 0 : bc + 1;
   }
 }

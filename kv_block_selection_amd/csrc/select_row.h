@@ -18,20 +18,22 @@ struct RowGeom {
 };
 
 // Forecast scores of blocks [NBLK * chunk, NBLK * chunk + NBLK) of one row by
-// 256 threads (t = thread index): the windows they meet, scored into s_win
-// (LDS, at least fsel_lds_floats<Tag, NBLK>() floats), max-pooled per block.
-template <typename Tag, int NBLK>
+// NT threads (t = thread index): the windows they meet, scored into s_win
+// (LDS, at least fsel_lds_floats<Tag, NBLK, NT>() floats), max-pooled per block.
+template <typename Tag, int NBLK, int NT = 256>
 constexpr int fsel_lds_floats() {
-  return ((4 * NBLK + 1 + RowGeom<Tag>::SLOTS - 1) / RowGeom<Tag>::SLOTS) * RowGeom<Tag>::SLOTS;
+  constexpr int slots = NT / RowGeom<Tag>::LPR;
+  return ((4 * NBLK + 1 + slots - 1) / slots) * slots;
 }
-template <typename Tag, int NBLK>
+template <typename Tag, int NBLK, int NT = 256>
 __device__ __forceinline__ void fsel_blocks(const uint8_t* __restrict__ f, const uint8_t* __restrict__ kc,
                                             float* __restrict__ scores, int W, int nB, int n_vis,
                                             const int* __restrict__ q_pos, int hkv, int T, float scale, long row,
                                             int chunk, float* s_win, int t) {
   using R = RowGeom<Tag>;
+  constexpr int SLOTS = NT / R::LPR;  // window rows per pass of the NT threads
   constexpr int NWIN = 4 * NBLK + 1;
-  constexpr int ITER = (NWIN + R::SLOTS - 1) / R::SLOTS;
+  constexpr int ITER = (NWIN + SLOTS - 1) / SLOTS;
   if (q_pos != nullptr) n_vis = visible_windows(row_position(q_pos, row, hkv, 0, T), W);
   const int beta0 = chunk * NBLK;
   const int nblk = min(NBLK, nB - beta0);
@@ -46,14 +48,14 @@ __device__ __forceinline__ void fsel_blocks(const uint8_t* __restrict__ f, const
   u32x4 kv[ITER];
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
-    const int lw = it * R::SLOTS + slot;
+    const int lw = it * SLOTS + slot;
     const int w = wstart + lw;
     const bool ok = lw < nwin && w >= 0 && w < n_vis;
     kv[it] = ok ? load16_nt(base + (long)w * R::RB) : u32x4{0, 0, 0, 0};
   }
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
-    const int lw = it * R::SLOTS + slot;
+    const int lw = it * SLOTS + slot;
     const int w = wstart + lw;
     const bool ok = lw < nwin && w >= 0 && w < n_vis;
     const float s = group_sum<R::LPR>(dot16<Tag>(fv, kv[it], 0.f));

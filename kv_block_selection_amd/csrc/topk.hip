@@ -29,7 +29,7 @@ namespace sparda {
 template <int NPT>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores,
                                                    int32_t* __restrict__ idx, int nB, int k) {
-  __shared__ TopkShared sh;
+  __shared__ TopkShared<> sh;
   const long row = blockIdx.x;
   topk_row<NPT>(scores + row * nB, idx + row * k, nullptr, nB, k, sh, threadIdx.x);
 }

@@ -62,19 +62,29 @@ __device__ __forceinline__ uint32_t wave_rank_bound(uint32_t x, int r, int bits)
   return v;
 }
 
+template <int NW = 4>
 struct TopkShared {
-  int hist[3][4][256];  // [rotation][wave][digit]
-  int wave_tot[4];
-  uint32_t wave_max[4], wave_bound[4];
-  int wave_cnt[4];
+  int hist[3][NW][256];  // [rotation][wave][digit]
+  int wave_tot[NW];
+  uint32_t wave_max[NW], wave_bound[NW];
+  int wave_cnt[NW];
 };
 
-// The k best blocks of one row of nB scores, by the 256 threads of a
-// workgroup (t = thread index). The indices go to dst_g (global memory) and/or
-// dst_s (LDS), either of which may be NULL, ascending with -1 padding.
-template <int NPT>
+// Clears histogram buffer `b` (NW x 256 counters) with the workgroup's NW x 64 threads.
+template <int NW>
+__device__ __forceinline__ void clear_hist(TopkShared<NW>& sh, int b, int t) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) (&sh.hist[b][0][0])[t + j * NW * kWave] = 0;
+}
+
+// The k best blocks of one row of nB scores, by the NW x 64 threads of a
+// workgroup (t = thread index; NPT scores per thread, NW x 64 x NPT >= nB).
+// The indices go to dst_g (global memory) and/or dst_s (LDS), either of which
+// may be NULL, ascending with -1 padding.
+template <int NPT, int NW = 4>
 __device__ __forceinline__ void topk_row(const float* __restrict__ src, int32_t* __restrict__ dst_g,
-                                         int32_t* dst_s, int nB, int k, TopkShared& sh, int t) {
+                                         int32_t* dst_s, int nB, int k, TopkShared<NW>& sh, int t) {
+  constexpr int NT = NW * kWave;
   const int lane = t % kWave;
   const int wid = t / kWave;
 
@@ -93,9 +103,10 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ src, int32_t*
     cnt += key[j] != 0u;
     kmax = max(kmax, key[j]);
   }
-#pragma unroll
-  for (int w = 0; w < 4; ++w) sh.hist[0][w][t] = 0;
-  const int rnk = (k + 3) / 4;
+  clear_hist(sh, 0, t);
+  // every wave holds at least rnk keys >= its bound, so NW x rnk >= k keys are
+  // >= the smallest bound: the k-th largest key is not below it
+  const int rnk = (k + NW - 1) / NW;
   const uint32_t wbound = rnk <= kWave ? wave_rank_bound(kmax, rnk, 8) : 0u;  // kmax: this thread's largest
   cnt = wave_isum(cnt);
   const uint32_t wmax = wave_umax(kmax);
@@ -109,7 +120,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ src, int32_t*
   kmax = 0u;
   uint32_t lb = 0xFFFFFFFFu;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     n_cand += sh.wave_cnt[w];
     kmax = max(kmax, sh.wave_max[w]);
     lb = min(lb, sh.wave_bound[w]);
@@ -141,15 +152,16 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ src, int32_t*
     }
     // the buffer for the next pass was last read two passes ago, before the
     // previous pass's barrier
-#pragma unroll
-    for (int w = 0; w < 4; ++w) sh.hist[nxt][w][t] = 0;
+    clear_hist(sh, nxt, t);
     __syncthreads();
     // every wave: lane handles digits 255-4*lane .. 252-4*lane (descending)
     int h[4], sum = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d = 255 - 4 * lane - i;
-      h[i] = sh.hist[cur][0][d] + sh.hist[cur][1][d] + sh.hist[cur][2][d] + sh.hist[cur][3][d];
+      h[i] = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) h[i] += sh.hist[cur][w][d];
       sum += h[i];
     }
     int above = wave_incl_scan(sum) - sum;
@@ -191,7 +203,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ src, int32_t*
   __syncthreads();
   int before = incl - packed;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) before += w < wid ? sh.wave_tot[w] : 0;
+  for (int w = 0; w < NW; ++w) before += w < wid ? sh.wave_tot[w] : 0;
   int eq_rank = before >> 16;
   int pos = (before & 0xFFFF) + min(eq_rank, remaining);
   auto put = [&](int at, int32_t v) {
@@ -212,7 +224,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ src, int32_t*
       }
     }
   }
-  for (int q = kk + t; q < k; q += 256) put(q, -1);
+  for (int q = kk + t; q < k; q += NT) put(q, -1);
 }
 
 

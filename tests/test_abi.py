@@ -301,36 +301,48 @@ def test_select_forecast_merge_validation(lib, kw, status, needle):
 
 
 def _layer(lib, **kw):
-    a = dict(m_ws=P + 4096, m_ws_bytes=1 << 30, m_out=P, m_Hq=32, m_T=131072, m_k=64, s=P, q=P, k=P, v=P, idx=P,
-             out=P, Hq=32, q_start=131071, q_pos=None, T=131072, k_sel=64, scale=0.088, ws=P, ws_bytes=1 << 30,
-             f_n=P, kc_n=P, s_n=P, q_start_n=131071, q_pos_n=None, T_n=131072, scale_n=0.088, dtype=1, B=16, Hkv=8,
-             d=128, block=64, kernel=32, stride=16)
+    # distinct, non-overlapping fake addresses: validation fails before any use
+    a = dict(s=P, q=P + (1 << 24), k=P + (2 << 24), v=P + (3 << 24), idx=P + (4 << 24), out=P + (5 << 24), Hq=32,
+             q_start=131071, q_pos=None, T=131072, k_sel=64, scale=0.088, ws=P + (6 << 24), ws_bytes=0,
+             f_n=P + (7 << 24), kc_n=P + (8 << 24), s_n=P + (9 << 24), q_start_n=131071, q_pos_n=None, T_n=131072,
+             scale_n=0.088, dtype=1, B=16, Hkv=8, d=128, block=64, kernel=32, stride=16)
     a.update(kw)
-    return lib.sparda_decode_layer(a["m_ws"], a["m_ws_bytes"], a["m_out"], a["m_Hq"], a["m_T"], a["m_k"], a["s"],
-                                   a["q"], a["k"], a["v"], a["idx"], a["out"], a["Hq"], a["q_start"], a["q_pos"],
-                                   a["T"], a["k_sel"], a["scale"], a["ws"], a["ws_bytes"], a["f_n"], a["kc_n"],
-                                   a["s_n"], a["q_start_n"], a["q_pos_n"], a["T_n"], a["scale_n"], a["dtype"], a["B"],
-                                   a["Hkv"], a["d"], a["block"], a["kernel"], a["stride"], None)
+    return lib.sparda_decode_layer(a["s"], a["q"], a["k"], a["v"], a["idx"], a["out"], a["Hq"], a["q_start"],
+                                   a["q_pos"], a["T"], a["k_sel"], a["scale"], a["ws"], a["ws_bytes"], a["f_n"],
+                                   a["kc_n"], a["s_n"], a["q_start_n"], a["q_pos_n"], a["T_n"], a["scale_n"],
+                                   a["dtype"], a["B"], a["Hkv"], a["d"], a["block"], a["kernel"], a["stride"], None)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(dtype=0), 2, b"only bf16"),
-    (dict(m_ws=P), 1, b"must not be this layer's"),
-    (dict(ws_bytes=100), 3, b"workspace"),
-    (dict(m_ws_bytes=100), 3, b"workspace"),
+    (dict(B=4, ws_bytes=100), 3, b"workspace"),  # 32 rows: block ranges merged through the workspace
     (dict(k_sel=1025, T=64 * 2000, q_start=64 * 2000 - 1), 2, b"above 1024"),
     (dict(kernel=16), 2, b"kernel/stride"),
     (dict(s_n=None), 1, b"blk_scores_next is NULL"),
     (dict(q=None), 1, b"q is NULL"),
+    # one launch reads this layer's scores while it writes the next layer's
+    (dict(s_n=P), 1, b"must not overlap"),
+    (dict(s_n=P + 4096), 1, b"must not overlap"),      # partly overlapping
+    (dict(s_n=P + (4 << 24)), 1, b"must not overlap"),  # the selection's own idx buffer
+    (dict(out=P + 1024), 1, b"must not overlap"),      # out over this layer's scores
+    (dict(idx=P + (5 << 24) + 64), 1, b"must not overlap"),
 ])
 def test_decode_layer_validation(lib, kw, status, needle):
     st = _layer(lib, **kw)
     assert st == status and needle in lib.sparda_last_error(), lib.sparda_last_error()
 
 
+def test_decode_layer_workspace_sizes(lib):
+    # one workgroup per row from 96 rows on: no workspace; fewer rows merge through one
+    ws = lib.sparda_workspace_bytes
+    assert ws(5, 16, 32, 8, 1, 131072, 128, 64) == 0
+    assert ws(5, 12, 32, 8, 1, 4096, 128, 16) == 0
+    assert ws(5, 11, 32, 8, 1, 4096, 128, 16) == ws(3, 11, 32, 8, 1, 4096, 128, 16) > 0
+
+
 def test_decode_layer_optional_parts(lib):
-    # no merge (m_out NULL) and no next selection (f_next NULL) with B = 0: valid, launches nothing
-    assert _layer(lib, m_out=None, f_n=None, B=0) == 0
+    # no next selection (f_next NULL) with B = 0: valid, launches nothing
+    assert _layer(lib, f_n=None, B=0) == 0
 
 
 def test_token_level_validation(lib):

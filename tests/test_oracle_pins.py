@@ -361,6 +361,58 @@ def test_lookahead_step_structure():
     assert W == 63
 
 
+def test_lookahead_step_layer_wiring():
+    """Which Forecast scores which layer's compressed keys, and which layer's
+    queries attend over which layer's K and V, with every input distinct.
+    The compressed keys are spikes: window 4b + 1 lies inside block b alone
+    (tokens 64b + 16 .. 64b + 47), so a Forecast along e0 or e1 picks exactly
+    the blocks holding its spikes. Expected indices are written by hand:
+
+      Kc0: e0 spikes at blocks 3 (10) and 7 (5); e1 spikes at blocks 5 (10) and 12 (5)
+      Kc1: e0 spikes at blocks 9 (10) and 2 (5); e1 spikes at blocks 11 (10) and 14 (5)
+      F_self = e0 (layer 0's own blocks), F_next = e1 (layer 1's blocks)
+
+    so idx0 = [3, 7] and idx1 = [11, 14]. Swapping F_self and F_next gives
+    [5, 12] and [2, 9]; scoring the other layer's Kc gives [2, 9] and [5, 12];
+    every such swap fails here. The outputs are the textbook softmax of each
+    layer's own queries over its own keys of those blocks; swapping Q, K or V
+    between the layers changes them."""
+    rng = np.random.default_rng(41)
+    T, d, k, G = 1024, 8, 2, 2
+    W = oracle.num_windows(T)
+    e0, e1 = np.eye(d)[0], np.eye(d)[1]
+
+    def spikes(pairs):
+        kc = np.zeros((1, 1, W, d))
+        for vec, blk, mag in pairs:
+            kc[0, 0, 4 * blk + 1] = mag * vec
+        return kc
+
+    L0 = {"Q": rng.standard_normal((1, G, 1, d)), "K": rng.standard_normal((1, 1, T, d)),
+          "V": rng.standard_normal((1, 1, T, d)),
+          "Kc": spikes([(e0, 3, 10.0), (e0, 7, 5.0), (e1, 5, 10.0), (e1, 12, 5.0)]),
+          "F_self": e0.reshape(1, 1, 1, d).copy(), "F_next": e1.reshape(1, 1, 1, d).copy()}
+    L1 = {"Q": rng.standard_normal((1, G, 1, d)), "K": rng.standard_normal((1, 1, T, d)) + 1.0,
+          "V": rng.standard_normal((1, 1, T, d)) - 1.0,
+          "Kc": spikes([(e0, 9, 10.0), (e0, 2, 5.0), (e1, 11, 10.0), (e1, 14, 5.0)])}
+    O0, O1, idx0, idx1 = oracle.lookahead_decode_step(L0, L1, T, k, 0.5)
+    assert idx0.tolist() == [[[[3, 7]]]]
+    assert idx1.tolist() == [[[[11, 14]]]]
+
+    def softmax_attend(q, K, V, blocks):
+        toks = np.concatenate([np.arange(64 * b, 64 * b + 64) for b in blocks])
+        s = 0.5 * np.array([sum(q[c] * K[t, c] for c in range(d)) for t in toks])
+        e = np.exp(s - s.max())
+        return (e[:, None] * V[toks]).sum(axis=0) / e.sum()
+
+    for g in range(G):
+        np.testing.assert_allclose(O0[0, g, 0], softmax_attend(L0["Q"][0, g, 0], L0["K"][0, 0], L0["V"][0, 0], [3, 7]),
+                                   rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(O1[0, g, 0],
+                                   softmax_attend(L1["Q"][0, g, 0], L1["K"][0, 0], L1["V"][0, 0], [11, 14]),
+                                   rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------ the four projections ----
 def test_project_qkvf_brute_force_and_layout():
     """Every output element as a pure-Python sum over D, read back at the
