@@ -231,6 +231,29 @@ int sparda_topk_block_sparse_attn(const float* blk_scores, const void* q, const 
                                   size_t ws_bytes, void* stream);
 
 /*
+ * sparda_topk_block_sparse_attn without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, serving
+ * loops or harnesses that forbid hipMalloc). Same arguments minus ws and
+ * ws_bytes, same selection and the same output bits. The block ranges'
+ * results go to a static device array of the library (16 MiB, one copy per
+ * GPU, held until the process ends); its address on the current device is
+ * looked up on the first call there. The call itself allocates nothing.
+ * The stream must belong to the current device. Every call on one GPU
+ * shares that array and leaves its contents behind (nothing in it needs
+ * initial contents): calls that may run at the same time on one GPU (other
+ * streams, other threads) race and must be ordered by the caller.
+ * Errors: as sparda_topk_block_sparse_attn, and SPARDA_ERR_UNSUPPORTED when
+ * the sizes need more than the array's 16 MiB (sparda_workspace_bytes(
+ * SPARDA_OP_BLOCK_SPARSE_ATTN, ...) > 16 << 20; of the sizes the call
+ * accepts, only groups of 8 query heads with 2017 to 2047 (sequence, KV
+ * head) rows and k >= 2 do): nothing is then looked up or launched.
+ */
+int sparda_topk_block_sparse_attn_noalloc(const float* blk_scores, const void* q, const void* k, const void* v,
+                                          int32_t* idx, void* out, int dtype, int B, int Hq, int Hkv, int q_start,
+                                          const int* q_pos, int T, int d, int block, int k_sel, float scale,
+                                          void* stream);
+
+/*
  * The decode step in the order of the method's layers. Layer L's Forecast
  * selects layer L+1's blocks ([P1] paragraph on the Forecast predicting the
  * next layer's blocks; [P2] 二), so layer L+1's selection needs nothing from

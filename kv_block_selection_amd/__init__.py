@@ -53,6 +53,8 @@ SIGNATURES = {
     "sparda_project_qkvf": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "sparda_topk_block_sparse_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _f,
                                            _vp, _sz, _vp]),
+    "sparda_topk_block_sparse_attn_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _i, _i,
+                                                   _i, _f, _vp]),
     "sparda_topk_block_sparse_attn_partial": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _i, _i,
                                                    _i, _f, _vp, _sz, _vp]),
     "sparda_merge_partials": (_i, [_vp, _sz, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
@@ -356,6 +358,24 @@ def topk_block_sparse_attn(scores, q, k, v, k_sel: int, T: int, q_start: int, sc
     _call(name, _ptr(scores), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out),
           _dtype_code(q), B, Hq, Hkv, q_start, _positions(q_pos, B), T, d, BLOCK, k_sel, scale, _ptr(ws), nbytes,
           _stream(q, stream))
+    return idx, out
+
+
+def topk_block_sparse_attn_noalloc(scores, q, k, v, k_sel: int, T: int, q_start: int, idx=None, out=None,
+                                    scale=None, q_pos=None, stream=None):
+    """topk_block_sparse_attn without a workspace: the library's static
+    device array holds the block ranges' results (calls on one GPU share it
+    and must not overlap). Returns (idx, out)."""
+    torch = _torch()
+    B, Hq, Tq, d = q.shape
+    Hkv = k.shape[1]
+    scale = d ** -0.5 if scale is None else scale
+    if idx is None:
+        idx = torch.empty((B, Hkv, 1, k_sel), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _call("sparda_topk_block_sparse_attn_noalloc", _ptr(scores), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(out),
+          _dtype_code(q), B, Hq, Hkv, q_start, _positions(q_pos, B), T, d, BLOCK, k_sel, scale, _stream(q, stream))
     return idx, out
 
 

@@ -417,6 +417,31 @@ SPARDA_EXPORT int sparda_topk_block_sparse_attn(const float* blk_scores, const v
                         ws, ws_bytes, true, stream, "topk_block_sparse_attn");
 }
 
+SPARDA_EXPORT int sparda_topk_block_sparse_attn_noalloc(const float* blk_scores, const void* q, const void* k,
+                                                        const void* v, int32_t* idx, void* out, int dtype, int B,
+                                                        int Hq, int Hkv, int q_start, const int* q_pos, int T, int d,
+                                                        int block, int k_sel, float scale, void* stream) {
+  // validated against the static array's size first, so nothing is looked up
+  // or launched for a request that does not fit
+  if (int e = check_dtype(dtype)) return e;
+  if (int e = check_geometry(B, Hq, Hkv, 1, q_start, T, d)) return e;
+  const int nB = T / sparda::kBlock;
+  CHECK(k_sel >= 1 && k_sel <= nB, SPARDA_ERR_INVALID_ARG, "k = %d outside 1..nB (%d)", k_sel, nB);
+  const size_t need = ws_bytes_for(SPARDA_OP_BLOCK_SPARSE_ATTN, B, Hq, Hkv, 1, T, k_sel);
+  CHECK(need <= sparda::kStaticScratchBytes, SPARDA_ERR_UNSUPPORTED,
+        "topk_block_sparse_attn_noalloc: these sizes need %zu bytes of scratch, the static array holds %zu; use "
+        "sparda_topk_block_sparse_attn with a workspace",
+        need, sparda::kStaticScratchBytes);
+  if (B == 0) return ok();
+  void* ws = nullptr;
+  if (need) {
+    const hipError_t e = sparda::static_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "topk_block_sparse_attn_noalloc: static scratch address");
+  }
+  return topk_attn_impl(blk_scores, q, k, v, idx, out, dtype, B, Hq, Hkv, q_start, q_pos, T, d, block, k_sel, scale,
+                        ws, need, true, stream, "topk_block_sparse_attn_noalloc");
+}
+
 SPARDA_EXPORT int sparda_topk_block_sparse_attn_partial(const float* blk_scores, const void* q, const void* k,
                                                         const void* v, int32_t* idx, void* out, int dtype, int B,
                                                         int Hq, int Hkv, int q_start, const int* q_pos, int T, int d,

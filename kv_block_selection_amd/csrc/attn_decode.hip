@@ -22,6 +22,7 @@
 // four splits per workgroup with the row's top-k taken first by the whole
 // workgroup (topk_row.h; the selection then comes from LDS), and the merge
 // left to a later launch, such as the next layer's selection.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -631,6 +632,37 @@ hipError_t launch_topk_attn_decode(const float* scores, const void* q, const voi
 #undef SPARDA_AT_G
 #undef SPARDA_AT
   return hipGetLastError();
+}
+
+// ---- the decode attention's block-range results in a static device array ----
+// For callers that cannot allocate (code under graph capture, serving loops
+// that forbid hipMalloc): the partial results live in `scratch`, one copy per
+// GPU, held until the process ends. In host code `scratch` names a host-side
+// stand-in, not device memory, so the kernels receive the device address
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace sparda

@@ -80,6 +80,10 @@ hipError_t launch_attn_decode(const void* q, const void* k, const void* v, const
 hipError_t launch_topk_attn_decode(const float* scores, const void* q, const void* k, const void* v, int32_t* idx,
                                    void* out, bool bf16, const AttnDims& d, void* ws, bool merge, hipStream_t s);
 DecodePartials decode_attn_partials(void* ws, const AttnDims& d);
+// A static device array (one per GPU) that can stand in for a decode
+// attention's workspace: its device address on the current device.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+hipError_t static_scratch(void** ptr);
 hipError_t launch_merge_partials(void* ws, void* out, bool bf16, const AttnDims& d, hipStream_t s);
 // one decode layer: top-k + attention of this layer (finished output) and
 // the selection of the next layer (f_next may be NULL) in one launch, plus a

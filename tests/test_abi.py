@@ -26,7 +26,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in kbs.SIGNATURES, f"binding lacks {n}"
@@ -380,3 +380,15 @@ def test_token_level_validation(lib):
     assert need >= 2 * 128 * 4096 * 128 * 4  # fp32 staging of K and V
     assert lib.sparda_workspace_bytes(4, 16, 32, 8, 1, 131072, 128, 100) == 0
 
+
+
+def test_noalloc_attention_rejects_sizes_beyond_its_array(lib):
+    # sparda_topk_block_sparse_attn_noalloc(scores, q, k, v, idx, out, dtype, B, Hq, Hkv, q_start, q_pos, T, d,
+    # block, k, scale, stream): 2040 rows of 8 query heads split in two ranges need 16.2 MiB > 16 MiB
+    f = lib.sparda_topk_block_sparse_attn_noalloc
+    assert lib.sparda_workspace_bytes(3, 2040, 8, 1, 1, 4096, 128, 2) > 16 << 20
+    assert f(P, P, P, P, P, P, 1, 2040, 8, 1, 4095, None, 4096, 128, 64, 2, 0.088, None) == 2
+    assert b"static array holds" in lib.sparda_last_error()
+    # the same call's other checks come first: a wrong head dim, then k beyond nB
+    assert f(P, P, P, P, P, P, 1, 16, 32, 8, 4095, None, 4096, 64, 64, 2, 0.088, None) == 2
+    assert f(P, P, P, P, P, P, 1, 16, 32, 8, 4095, None, 4096, 128, 64, 65, 0.088, None) == 1
