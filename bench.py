@@ -1,20 +1,24 @@
-"""Benchmark of the SparDA decode hot path on one MI355X.
+"""Benchmark of the SparDA hot path on one MI355X; prints one JSON line.
 
-One step = Forecast block scoring of every compressed key window, top-k block
-choice and GQA block-sparse attention over the chosen blocks, for one layer of
-the batched 128K-context decode workload (B=16, T=131072, 32 query / 8 KV
-heads, d=128, 64-token blocks, top-64), inputs resident in HBM. Prints one
-JSON line.
+The headline (the metric's workload): one decode layer-step of the batched
+128K-context workload (B=16, T=131072, 32 query / 8 KV heads, d=128, 64-token
+blocks, top-64): Forecast block scoring of the next layer's compressed keys,
+top-k and GQA block-sparse attention of this layer, inputs resident in HBM,
+one ``sparda_decode_layer`` launch per layer. The same run measures the other
+four workloads (tiny fp32 decode, 32K single-sequence decode, the two-layer
+offloaded decode with lookahead prefetch, the 4096-query chunked prefill) as
+extra keys, each with its own roofline, the parity of every workload against
+the fp64 oracle, and the oracle itself on the host cores (one core, and all
+of them).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --workload offload   # two-layer step, layer-1 KV in pinned host memory
-    python bench.py --workload prefill   # 4096-query chunk at 128K on the matrix cores
-    python bench.py --workload pipeline  # four-layer step, layers 1-3 KV in pinned host memory
+    python bench.py --workload decode|offload|prefill|pipeline   # one workload only
 
-Timing: W untimed steps, then K steps between two HIP events on the stream the
-kernels run on, with a device synchronisation on both sides. Input sets rotate
-(3 independent sets) so no step finds its data in the 256 MB last-level cache.
-Per-kernel averages come from their own event-bracketed loops.
+Timing: W untimed steps, then exactly K steps captured in one HIP graph,
+replayed 5 times, each replay between two HIP events on the launch stream
+with a device synchronisation on both sides; ms_per_step is the median
+replay / K (the spread is reported). Input sets rotate (3 independent sets)
+so no step finds its data in the 256 MB last-level cache.
 """
 
 from __future__ import annotations
@@ -22,6 +26,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -31,16 +36,240 @@ if ROOT not in sys.path:
 
 METRIC = "decode steps/s/layer at 128K ctx (select+sparse attn); % of HBM peak GB/s"
 HBM_PEAK_GBPS = 8000.0
+HOST_LINK_PEAK_GBPS = 63.0   # PCIe 5.0 x16, one direction
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 N_SETS = 3
+REPEATS = 5
+MAX_POOL = 16  # host threads a GPU machine grants one GPU
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# ------------------------------------------------------------------ timing ----
+def _stats(per_call_ms) -> dict:
+    xs = sorted(per_call_ms)
+    return {"median": statistics.median(xs), "min": xs[0], "max": xs[-1], "n": len(xs)}
+
+
+def time_graph_stats(fn, n: int, repeats: int = REPEATS) -> dict:
+    """fn(0) .. fn(n-1) captured once in a HIP graph (no host launch cost
+    inside), replayed `repeats` times, each replay between HIP events on the
+    replay stream with a device synchronisation on both sides. Returns the
+    median / min / max ms per fn call over the replays."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(n):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    stream = torch.cuda.current_stream()
+    g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(repeats):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        out.append(start.elapsed_time(end) / n)
+    del g
+    return _stats(out)
+
+
+def time_graph(fn, n: int, repeats: int = REPEATS) -> float:
+    """Median ms per fn call (see time_graph_stats)."""
+    return time_graph_stats(fn, n, repeats)["median"]
+
+
+def time_loop_stats(fn, n: int, stream, repeats: int = REPEATS) -> dict:
+    """fn(0) .. fn(n-1) launched eagerly, `repeats` times, each run between HIP
+    events on `stream`; median / min / max ms per call."""
+    import torch
+    out = []
+    for _ in range(repeats):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(n):
+            fn(i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        out.append(start.elapsed_time(end) / n)
+    return _stats(out)
+
+
+def time_loop(fn, n: int, stream, repeats: int = REPEATS) -> float:
+    return time_loop_stats(fn, n, stream, repeats)["median"]
+
+
+def _us(st: dict) -> dict:
+    return {k: (round(v * 1e3, 2) if k != "n" else v) for k, v in st.items()}
+
+
+# ------------------------------------------------- the oracle on the host ----
+def _f64(u16):
+    """bf16 bit patterns (uint16) -> exact fp64 values."""
+    import numpy as np
+    return (np.asarray(u16, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def oracle_step_rows(rows, meta, reps: int) -> float:
+    """The oracle, as it stands, on (sequence, KV head) rows of a decode step:
+    Forecast scoring of every visible window, top-k of the blocks, the union
+    of their tokens up to the query, and attention of the group's query
+    heads over them. rows: per row (F, Kc, Q, K_sel, V_sel) as bf16 bit
+    patterns, K_sel / V_sel being the keys and values of the oracle's own
+    selection (gathered beforehand). Inputs are widened to fp64 outside the
+    timed region; one thread. Returns the seconds of the `reps` timed passes."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    T, q_start, scale, k = meta["T"], meta["q_start"], meta["scale"], meta["k"]
+    data = [tuple(_f64(a) for a in r) for r in rows]
+    timed = 0.0
+    with threadpool_limits(limits=1):
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            for F, Kc, Q, KJ, VJ in data:
+                sc = oracle.select_forecast_tile(F[None, :], Kc, [q_start], T, scale)
+                idx = oracle.topk_row(sc, k)
+                oracle.selected_keys(idx, q_start)
+                for g in range(Q.shape[0]):
+                    oracle.attend(Q[g], KJ, VJ, scale)
+            timed += time.perf_counter() - t0
+    return timed
+
+
+def start_oracle_pool():
+    """Worker processes for the all-cores oracle, started before anything
+    touches the GPU (spawned interpreters that import numpy and the oracle
+    only). As many as the host cores this process may use, up to MAX_POOL."""
+    import multiprocessing as mp
+    n = min(MAX_POOL, len(os.sched_getaffinity(0)))
+    return mp.get_context("spawn").Pool(n), n
+
+
+def cpu_baseline(w, s, pool, n_workers: int, reps: int = 20) -> dict:
+    """The oracle timed on the benchmark's own step (all B x Hkv rows of input
+    set 0): on one thread in this process, and split over the pool's worker
+    processes (one thread each). The selection the oracle attends over is its
+    own; the keys and values of those blocks are gathered from the GPU copy
+    before timing."""
+    import numpy as np
+    import torch
+    import oracle
+    rows = []
+    meta = {"T": w.T, "q_start": w.q_start, "scale": w.scale, "k": w.k}
+
+    def u16(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            F, Kc, Q = u16(s["F"][b, h, 0]), u16(s["Kc"][b, h]), u16(s["Q"][b, h * w.G:(h + 1) * w.G, 0])
+            sc = oracle.select_forecast_tile(_f64(F)[None, :], _f64(Kc), [w.q_start], w.T, w.scale)
+            J = oracle.selected_keys(oracle.topk_row(sc, w.k), w.q_start)
+            Jt = torch.from_numpy(J).to(s["K"].device)
+            rows.append((F, Kc, Q, u16(s["K"][b, h].index_select(0, Jt)), u16(s["V"][b, h].index_select(0, Jt))))
+    one = oracle_step_rows(rows, meta, reps) / reps
+    out = {"value": None, "unit": "steps/s/layer", "cores": 1, "kind": "oracle",
+           "sample": f"the full step, all {len(rows)} (sequence, KV head) rows of one input set: Forecast scoring of "
+                     f"{w.W} windows, top-{w.k} of {w.nB} blocks, attention of {w.G} heads over {w.k * w.block} keys; "
+                     f"fp64 numpy, {reps} passes timed per configuration; fp64 widening of the inputs untimed",
+           "single_core": {"value": round(1.0 / one, 4), "cores": 1, "s_per_step": round(one, 4),
+                           "seconds_timed": round(one * reps, 2)},
+           "nproc": len(os.sched_getaffinity(0)), "hardware_concurrency": os.cpu_count()}
+    if pool is not None:
+        chunks = [rows[i::n_workers] for i in range(n_workers)]
+        t0 = time.perf_counter()
+        secs = pool.starmap(oracle_step_rows, [(c, meta, reps) for c in chunks if c])
+        wall = time.perf_counter() - t0
+        per_step = max(secs) / reps  # a step ends when the slowest worker's rows are done
+        out.update(value=round(1.0 / per_step, 4), cores=n_workers)
+        out["all_cores"] = {"value": round(1.0 / per_step, 4), "cores": n_workers, "s_per_step": round(per_step, 4),
+                            "cpu_seconds_timed": round(sum(secs), 2), "wall_seconds_with_transfer": round(wall, 2)}
+    else:
+        out["value"] = out["single_core"]["value"]
+    return out
+
+
+# ------------------------------------------------------------ parity ----
+def _check(fn, *a, **kw):
+    """Run a parity check; a failure is reported in the JSON line, not raised."""
+    try:
+        return fn(*a, **kw)
+    except AssertionError as e:
+        return f"FAIL: {e}"
+
+
+def parity_decode(w, kbs, s, rows=None, mh_scores=None, positions=None) -> dict:
+    """The GPU's own results of one decode input set against the oracle:
+    block scores (the oracle scores the GPU's compressed keys), the selection
+    by the band rule, and attention run by the oracle over the GPU's
+    selection, for the given (sequence, KV head) rows (all by default)."""
+    import numpy as np
+    import torch
+    import oracle
+    from tests import parity
+    rows = rows if rows is not None else [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+    positions = positions or [w.q_start] * w.B
+    worst = worst_mh = err = 0.0
+    banded = 0
+    status = "ok"
+    for b, h in rows:
+        p = positions[b]
+        Kc = parity.to_f64(s["Kc"][b, h])
+        ref = oracle.select_forecast_tile(parity.to_f64(s["F"][b, h]), Kc, [p], w.T, w.scale)[None, :]
+        got = parity.to_f64(s["scores"][b, h])
+        idx = s["idx"][b, h].cpu().numpy()
+        r1 = _check(parity.check_scores, got, ref)
+        r2 = _check(parity.check_topk_band, idx, ref, w.k)
+        J = oracle.selected_keys(idx[0], p)
+        Q = parity.to_f64(s["Q"][b, h * w.G:(h + 1) * w.G, 0])
+        o_ref = np.zeros((w.G, w.d))
+        if J.size:
+            Jt = torch.from_numpy(J).to(s["K"].device)
+            KJ, VJ = parity.to_f64(s["K"][b, h].index_select(0, Jt)), parity.to_f64(s["V"][b, h].index_select(0, Jt))
+            for g in range(w.G):
+                o_ref[g] = oracle.attend(Q[g], KJ, VJ, w.scale)
+        tol = parity.ATTN_ATOL_BF16 if w.dtype == "bf16" else 1e-4
+        r3 = _check(parity.check_attention, parity.to_f64(s["out"][b, h * w.G:(h + 1) * w.G, 0]), o_ref, tol)
+        for r in (r1, r2, r3):
+            if isinstance(r, str):
+                status = r
+        worst = max(worst, r1) if not isinstance(r1, str) else worst
+        banded += r2 if not isinstance(r2, str) else 0
+        err = max(err, r3) if not isinstance(r3, str) else err
+        if mh_scores is not None:
+            ref_mh = oracle.select_multihead_tile(parity.to_f64(s["Q"][b, h * w.G:(h + 1) * w.G]), Kc, [p], w.T,
+                                                  w.scale)[None, :]
+            r4 = _check(parity.check_scores, parity.to_f64(mh_scores[b, h]), ref_mh)
+            if isinstance(r4, str):
+                status = r4
+            else:
+                worst_mh = max(worst_mh, r4)
+    out = {"status": status, "rows_checked": len(rows), "score_worst_rel": float(f"{worst:.3g}"),
+           "banded_rows": int(banded), "attn_max_abs": float(f"{err:.3g}")}
+    if mh_scores is not None:
+        out["multihead_score_worst_rel"] = float(f"{worst_mh:.3g}")
+    return out
+
+
+# ------------------------------------------------------ algorithmic bytes ----
 def algorithmic_bytes(w) -> dict:
-    """Bytes each kernel must move for one layer-step (bf16 = 2 B)."""
-    e = 2
+    """Bytes each kernel must move for one layer-step (storage dtype)."""
+    e = 2 if w.dtype == "bf16" else 4
     rows = w.B * w.Hkv
     kc = rows * w.W * w.d * e
     f = rows * w.d * e
@@ -57,104 +286,10 @@ def algorithmic_bytes(w) -> dict:
         "topk_attention": scores + idx + kv + q + o,
         "topk_attention_partial": scores + idx + kv + q,
         "select_forecast_merge": kc + f + scores + o,
-        # one launch: the next layer's selection, this layer's top-k + attention, the merge of the layer before
-        "decode_layer": (kc + f + scores) + (scores + idx + kv + q) + o,
+        # one launch: the next layer's selection and this layer's top-k + attention
+        "decode_layer": (kc + f + scores) + (scores + idx + kv + q + o),
         "step": kc + f + scores + (scores + idx) + (kv + q + idx + o),
     }
-
-
-def time_loop(fn, iters: int, stream) -> float:
-    """Average ms of fn(i) over iters eager launches, HIP events on `stream`."""
-    import torch
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(iters):
-        fn(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / iters
-
-
-def time_graph(fn, per_graph: int, replays: int) -> float:
-    """Average ms per fn(i) call: fn(0..per_graph-1) captured once in a HIP graph
-    (no host launch cost inside), replayed `replays` times between HIP events on
-    the replay stream."""
-    import torch
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for i in range(per_graph):
-            fn(i)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(per_graph):
-            fn(i)
-    stream = torch.cuda.current_stream()
-    g.replay()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(replays):
-        g.replay()
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / (replays * per_graph)
-
-
-def cpu_baseline(w, sets, min_seconds: float = 10.0, max_reps: int = 30) -> dict:
-    """The fp64 oracle, as it stands, on the benchmark's own step: Forecast
-    scoring + top-k + attention for every (sequence, KV head) row of the first
-    input set, single-threaded. The whole step is repeated until about
-    min_seconds of CPU time have accumulated; inputs are converted to fp64
-    outside the timed region (the blocks an attention row reads are gathered
-    after the oracle's own selection)."""
-    import oracle
-    from tests import parity
-    from threadpoolctl import threadpool_limits
-    s = sets[0]
-    cache = []
-    timed = 0.0
-    with threadpool_limits(limits=1):
-        for b in range(w.B):
-            for h in range(w.Hkv):
-                F = parity.to_f64(s["F"][b, h])
-                Kc = parity.to_f64(s["Kc"][b, h])
-                Q = parity.to_f64(s["Q"][b, h * w.G:(h + 1) * w.G])
-                t0 = time.perf_counter()
-                sc = oracle.select_forecast_tile(F, Kc, [w.q_start], w.T, w.scale)
-                idx = oracle.topk_row(sc, w.k)
-                J = oracle.selected_keys(idx, w.q_start)
-                timed += time.perf_counter() - t0
-                import torch
-                Jt = torch.from_numpy(J).to(s["K"].device)
-                KJ = parity.to_f64(s["K"][b, h].index_select(0, Jt))
-                VJ = parity.to_f64(s["V"][b, h].index_select(0, Jt))
-                t0 = time.perf_counter()
-                for g in range(w.G):
-                    oracle.attend(Q[g, 0], KJ, VJ, w.scale)
-                timed += time.perf_counter() - t0
-                cache.append((F, Kc, Q, KJ, VJ))
-        reps = 1
-        while timed < min_seconds and reps < max_reps:
-            t0 = time.perf_counter()
-            for F, Kc, Q, KJ, VJ in cache:
-                sc = oracle.select_forecast_tile(F, Kc, [w.q_start], w.T, w.scale)
-                idx = oracle.topk_row(sc, w.k)
-                oracle.selected_keys(idx, w.q_start)
-                for g in range(w.G):
-                    oracle.attend(Q[g, 0], KJ, VJ, w.scale)
-            timed += time.perf_counter() - t0
-            reps += 1
-    per_step = timed / reps
-    return {"value": round(1.0 / per_step, 4), "unit": "steps/s/layer", "cores": 1, "kind": "oracle",
-            "sample": f"the full step ({w.B * w.Hkv} (sequence, KV head) rows: Forecast scoring of {w.W} windows, "
-                      f"top-{w.k} of {w.nB} blocks, attention of {w.G} heads over {w.k * w.block} keys), fp64 numpy "
-                      f"on 1 thread, repeated {reps}x ({timed:.1f} s timed); fp64 conversion of inputs untimed"}
 
 
 def pmc_traffic(kernel_files, summary: str):
@@ -177,41 +312,104 @@ def pmc_traffic(kernel_files, summary: str):
     return rec.get("traffic_bytes_per_launch")
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=("decode", "offload", "prefill", "pipeline"), default="decode",
-                    help="decode: the batch-16 128K decode step (the headline line); offload: the batch-64 two-layer "
-                         "step with lookahead prefetch from pinned host memory; prefill: a 4096-query chunk at 128K")
-    ap.add_argument("--kernel-iters", type=int, default=100)
-    ap.add_argument("--decoupled-layers", action="store_true",
-                    help="decode: also time consecutive layers with the next layer's selection on a second stream "
-                         "beside this layer's attention, against the same layers on one stream")
-    ap.add_argument("--calibration-copy", action="store_true",
-                    help="also run a plain 1 GiB device copy (torch copy_) ten times, as the known-size reference "
-                         "for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this path is built and timed on a single "
-              f"MI355X; sharding across GPUs is not implemented.", file=sys.stderr)
-        return 2
-
-    if args.workload == "offload":
-        return bench_offload(args)
-    if args.workload == "pipeline":
-        return bench_pipeline(args)
-    if args.workload == "prefill":
-        return bench_prefill(args)
-    return bench_decode(args)
+LAYER_SOURCES = ["kv_block_selection_amd/csrc/attn_decode.hip", "kv_block_selection_amd/csrc/topk_row.h",
+                 "kv_block_selection_amd/csrc/select_row.h", "kv_block_selection_amd/csrc/reduce16.h",
+                 "kv_block_selection_amd/csrc/common.h"]
 
 
-def bench_decode(args) -> int:
+def make_sets(kbs, w, dev, n_sets: int):
+    import synth.gpu as sg
+    import torch
+    from synth import workloads as wl
+    sets = []
+    for i in range(n_sets):
+        wi = wl.scaled(w, seed=w.seed + 1000 * i)
+        s = {n: sg.tensor(wi.recipe(n), wi.shape(n), dev) for n in ("Q", "F", "K", "V")}
+        s["Kc"] = kbs.compress_keys(s["K"])
+        s["scores"] = torch.empty((w.B, w.Hkv, 1, w.nB), dtype=torch.float32, device=dev)
+        s["idx"] = torch.empty((w.B, w.Hkv, 1, w.k), dtype=torch.int32, device=dev)
+        s["out"] = torch.empty_like(s["Q"])
+        sets.append(s)
+    return sets
+
+
+# --------------------------------------------- small decode configs (c1, c2) ----
+def bench_small_decode(kbs, w, dev, steps: int, warmup: int) -> dict:
+    """One decode layer-step of a one-sequence workload (the tiny fp32 one and
+    the 32K bf16 one): Forecast selection, top-k and attention per step. bf16
+    runs one sparda_decode_layer call per layer (its few rows keep block ranges,
+    merged by a second launch); fp32 runs the selection and the fused top-k +
+    attention (the layer call is bf16 only). Three input sets rotate. Both
+    selectors' cost (scoring + top-k) is timed too, and parity of the step's
+    own results against the oracle (every row)."""
+    import torch
+    sets = make_sets(kbs, w, dev, N_SETS)
+    ws_mh = torch.empty(max(1, kbs.workspace_bytes(kbs.OP_SELECT_MULTIHEAD, w.B, w.Hq, w.Hkv, 1, w.T)),
+                        dtype=torch.uint8, device=dev)
+    ws_l = torch.empty(max(1, kbs.workspace_bytes(kbs.OP_DECODE_LAYER, w.B, w.Hq, w.Hkv, 1, w.T, w.k)),
+                       dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(1, kbs.workspace_bytes(kbs.OP_BLOCK_SPARSE_ATTN, w.B, w.Hq, w.Hkv, 1, w.T, w.k)),
+                       dtype=torch.uint8, device=dev)
+    mh = [torch.empty_like(s["scores"]) for s in sets]
+    idx_mh = [torch.empty_like(s["idx"]) for s in sets]
+    bf16 = w.dtype == "bf16"
+    for s in sets:
+        kbs.select_forecast(s["F"], s["Kc"], w.T, w.q_start, out=s["scores"])
+
+    def step(i):
+        s, nxt = sets[i % N_SETS], sets[(i + 1) % N_SETS]
+        if bf16:
+            kbs.decode_layer(s["scores"], s["Q"], s["K"], s["V"], w.k, w.T, w.q_start, ws_l, idx=s["idx"],
+                             out=s["out"], select_next=(nxt["F"], nxt["Kc"], nxt["scores"], w.T, w.q_start))
+        else:
+            kbs.select_forecast(s["F"], s["Kc"], w.T, w.q_start, out=s["scores"])
+            kbs.topk_block_sparse_attn(s["scores"], s["Q"], s["K"], s["V"], w.k, w.T, w.q_start, idx=s["idx"],
+                                       out=s["out"], ws=ws_a)
+
+    def sel_f(i):
+        s = sets[i % N_SETS]
+        kbs.select_forecast(s["F"], s["Kc"], w.T, w.q_start, out=s["scores"])
+        kbs.topk_blocks(s["scores"], w.k, out=s["idx"])
+
+    def sel_m(i):
+        s = sets[i % N_SETS]
+        kbs.select_multihead(s["Q"], s["Kc"], w.T, w.q_start, out=mh[i % N_SETS], ws=ws_mh)
+        kbs.topk_blocks(mh[i % N_SETS], w.k, out=idx_mh[i % N_SETS])
+
+    for i in range(max(warmup, N_SETS)):
+        step(i)
+    torch.cuda.synchronize()
+    n = max(N_SETS, steps)
+    st = time_graph_stats(step, n)
+    sf = time_graph_stats(sel_f, 3 * N_SETS * 10)
+    sm = time_graph_stats(sel_m, 3 * N_SETS * 10)
+    # each set's scores, selection and output as the step leaves them (every
+    # set's scores were computed from its own Forecast and compressed keys)
+    for i in range(N_SETS + 1):
+        step(i)
+    kbs.select_multihead(sets[0]["Q"], sets[0]["Kc"], w.T, w.q_start, out=mh[0], ws=ws_mh)
+    torch.cuda.synchronize()
+    nbytes = algorithmic_bytes(w)["step"]
+    gbps = nbytes / (st["median"] * 1e-3) / 1e9
+    par = parity_decode(w, kbs, sets[0], mh_scores=mh[0])
+    del sets
+    return {"workload": w.description, "steps_per_s_per_layer": round(1e3 / st["median"], 1),
+            "us_per_step": _us(st), "steps": n,
+            "step": "sparda_decode_layer (+ its merge launch)" if bf16 else
+                    "sparda_select_forecast + sparda_topk_block_sparse_attn (fp32)",
+            "selection_us": {"forecast": round(sf["median"] * 1e3, 2), "multihead": round(sm["median"] * 1e3, 2)},
+            "forecast_vs_multihead_select_speedup": round(sm["median"] / sf["median"], 3),
+            "roofline": {"bound": "hbm", "kernel": "step", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "algorithmic_bytes": nbytes,
+                         "note": "launch-latency bound at this size: the bytes take a few microseconds at peak"},
+            "parity": par}
+
+
+# -------------------------------------------------- the headline (c3) ----
+def bench_decode(args, pool=None, n_workers: int = 0) -> dict:
     import torch
     import kv_block_selection_amd as kbs
-    import synth.gpu as sg
     from synth import workloads as wl
 
     kbs.load()
@@ -219,20 +417,13 @@ def bench_decode(args) -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"[bench] generating {N_SETS} input sets of {w.name}")
-    sets = []
-    for i in range(N_SETS):
-        wi = wl.scaled(w, seed=w.seed + 1000 * i)
-        s = {n: sg.tensor(wi.recipe(n), wi.shape(n), dev) for n in ("Q", "F", "K", "V")}
-        s["Kc"] = kbs.compress_keys(s["K"])
-        s["scores"] = torch.empty((w.B, w.Hkv, 1, w.nB), dtype=torch.float32, device=dev)
-        s["idx"] = torch.empty((w.B, w.Hkv, 1, w.k), dtype=torch.int32, device=dev)
-        s["out"] = torch.empty_like(s["Q"])
+    sets = make_sets(kbs, w, dev, N_SETS)
+    for s in sets:
         # the newest token of every sequence again, for the cache-append timings
         s["Knew1"] = s["K"][:, :, w.T - 1:].contiguous()
         s["Vnew1"] = s["V"][:, :, w.T - 1:].contiguous()
         s["Knew2"] = s["K"][:, :, w.T - 2:w.T - 1].contiguous()
         s["Vnew2"] = s["V"][:, :, w.T - 2:w.T - 1].contiguous()
-        sets.append(s)
     pos_last = torch.full((w.B,), w.q_start, dtype=torch.int32, device=dev)
     len_win = torch.full((w.B,), w.T - 1, dtype=torch.int32, device=dev)  # token T-1 completes window W-1
     len_nowin = torch.full((w.B,), w.T - 2, dtype=torch.int32, device=dev)  # token T-2 completes none
@@ -242,6 +433,9 @@ def bench_decode(args) -> int:
                           dtype=torch.uint8, device=dev)
     ws_mh = torch.empty(max(1, kbs.workspace_bytes(kbs.OP_SELECT_MULTIHEAD, w.B, w.Hq, w.Hkv, 1, w.T)),
                         dtype=torch.uint8, device=dev)
+    ws_layer = torch.zeros(max(1, kbs.workspace_bytes(kbs.OP_DECODE_LAYER, w.B, w.Hq, w.Hkv, 1, w.T, w.k)),
+                           dtype=torch.uint8, device=dev)
+    mh_scores = [torch.empty_like(s["scores"]) for s in sets]
 
     def sel(i):
         s = sets[i % N_SETS]
@@ -249,7 +443,7 @@ def bench_decode(args) -> int:
 
     def sel_mh(i):
         s = sets[i % N_SETS]
-        kbs.select_multihead(s["Q"], s["Kc"], w.T, w.q_start, out=s["scores"], ws=ws_mh)
+        kbs.select_multihead(s["Q"], s["Kc"], w.T, w.q_start, out=mh_scores[i % N_SETS], ws=ws_mh)
 
     def topk(i):
         s = sets[i % N_SETS]
@@ -259,19 +453,10 @@ def bench_decode(args) -> int:
         s = sets[i % N_SETS]
         kbs.block_sparse_attn(s["Q"], s["K"], s["V"], s["idx"], w.T, w.q_start, out=s["out"], ws=ws_attn)
 
-    def topk_attn(i):  # top-k and attention in one launch
+    def topk_attn(i):  # top-k and attention in one launch, then the merge launch
         s = sets[i % N_SETS]
         kbs.topk_block_sparse_attn(s["scores"], s["Q"], s["K"], s["V"], w.k, w.T, w.q_start, idx=s["idx"],
                                    out=s["out"], ws=ws_attn)
-
-    def step(i):
-        sel(i)
-        topk_attn(i)
-
-    def step_separate(i):  # the same step with top-k as a launch of its own
-        sel(i)
-        topk(i)
-        attn(i)
 
     def topk_attn_partial(i):  # the same without the merge (left in ws_attn)
         s = sets[i % N_SETS]
@@ -283,9 +468,6 @@ def bench_decode(args) -> int:
         kbs.select_forecast(s["F"], s["Kc"], w.T, w.q_start, out=s["scores"],
                             merge_from=(ws_attn, prev["out"], w.T, w.k))
 
-    ws_layer = torch.zeros(max(1, kbs.workspace_bytes(kbs.OP_DECODE_LAYER, w.B, w.Hq, w.Hkv, 1, w.T, w.k)),
-                           dtype=torch.uint8, device=dev)
-
     def step_one_launch(i):
         # layer i in one launch: its top-k + attention (finished output) and
         # layer i+1's Forecast selection, both from layer i's projections
@@ -293,15 +475,23 @@ def bench_decode(args) -> int:
         kbs.decode_layer(s["scores"], s["Q"], s["K"], s["V"], w.k, w.T, w.q_start, ws_layer, idx=s["idx"],
                          out=s["out"], select_next=(nxt["F"], nxt["Kc"], nxt["scores"], w.T, w.q_start))
 
-    def step_pipelined(i):
-        # layer i in the method's layer order: its selection (from the layer
-        # before's Forecast) shares a launch with the merge of the layer
-        # before's attention, which leaves its block-range results in ws_attn
-        s, prev = sets[i % N_SETS], sets[(i - 1) % N_SETS]
-        kbs.select_forecast(s["F"], s["Kc"], w.T, w.q_start, out=s["scores"],
-                            merge_from=(ws_attn, prev["out"], w.T, w.k))
+    def step_two_launches(i):
+        # layer i as two launches: top-k + attention leaving its block ranges
+        # in ws_attn, then the next layer's selection merging them
+        s, nxt = sets[i % N_SETS], sets[(i + 1) % N_SETS]
         kbs.topk_block_sparse_attn(s["scores"], s["Q"], s["K"], s["V"], w.k, w.T, w.q_start, idx=s["idx"],
                                    out=s["out"], ws=ws_attn, merge=False)
+        kbs.select_forecast(nxt["F"], nxt["Kc"], w.T, w.q_start, out=nxt["scores"],
+                            merge_from=(ws_attn, s["out"], w.T, w.k))
+
+    def step_layer(i):  # one layer at a time: selection, then top-k + attention + merge
+        sel(i)
+        topk_attn(i)
+
+    def step_separate(i):  # the same with top-k as a launch of its own
+        sel(i)
+        topk(i)
+        attn(i)
 
     # Decode-time state maintenance: append the step's token to K, V and
     # compress the window it completes (every 16th step) or none. The tokens
@@ -314,63 +504,63 @@ def bench_decode(args) -> int:
         s = sets[i % N_SETS]
         kbs.append_kv(s["Knew2"], s["Vnew2"], s["K"], s["V"], len_nowin, k_cmp=s["Kc"])
 
-    def step_q_pos(i):  # the same step with per-sequence positions (all at T - 1)
-        s = sets[i % N_SETS]
-        kbs.select_forecast(s["F"], s["Kc"], w.T, 0, out=s["scores"], q_pos=pos_last)
-        kbs.topk_block_sparse_attn(s["scores"], s["Q"], s["K"], s["V"], w.k, w.T, 0, idx=s["idx"], out=s["out"],
-                                   ws=ws_attn, q_pos=pos_last)
+    def step_q_pos(i):  # the one-launch step with per-sequence positions (all at T - 1)
+        s, nxt = sets[i % N_SETS], sets[(i + 1) % N_SETS]
+        kbs.decode_layer(s["scores"], s["Q"], s["K"], s["V"], w.k, w.T, 0, ws_layer, idx=s["idx"], out=s["out"],
+                         q_pos=pos_last, select_next=(nxt["F"], nxt["Kc"], nxt["scores"], w.T, 0, pos_last))
 
     log("[bench] warmup (eager)")
-    for i in range(args.warmup):
-        step(i)
-    for i in range(args.warmup):
-        step_pipelined(i)
-    torch.cuda.synchronize()
-    for i in range(6):
+    for i in range(N_SETS):
+        sel(i)
+    for i in range(max(args.warmup, 2 * N_SETS)):
         step_one_launch(i)
     torch.cuda.synchronize()
-    ms_step_eager = time_loop(step_one_launch, 6 * max(1, args.steps // 6), stream)
-    log(f"[bench] eager step {ms_step_eager * 1e3:.1f} us; timing {args.steps} steps through a HIP graph")
-    per_graph = 3 * N_SETS
-    replays = max(1, args.steps // per_graph)
-    # six layers per graph: the three input sets and the two workspaces both cycle
-    ms_step = time_graph(step_one_launch, 6, max(1, args.steps // 6))
-    steps_timed = 6 * max(1, args.steps // 6)
-    ms_step_two_launches = time_graph(step_pipelined, per_graph, replays)
-    ms_step_layer = time_graph(step, per_graph, replays)
-    ms_step_separate = time_graph(step_separate, per_graph, replays)
-    log(f"[bench] graph step {ms_step * 1e3:.1f} us (two launches per layer {ms_step_two_launches * 1e3:.1f} us, one "
-        f"layer at a time {ms_step_layer * 1e3:.1f} us, with top-k launched on its own {ms_step_separate * 1e3:.1f} "
-        f"us); per-kernel graphs")
-    kr = max(1, args.kernel_iters // per_graph)
-    ms = {"select_forecast": time_graph(sel, per_graph, kr), "topk": time_graph(topk, per_graph, kr),
-          "attention": time_graph(attn, per_graph, kr), "select_multihead": time_graph(sel_mh, per_graph, kr),
-          "topk_attention": time_graph(topk_attn, per_graph, kr),
-          "topk_attention_partial": time_graph(topk_attn_partial, per_graph, kr),
-          "select_forecast_merge": time_graph(sel_merge, per_graph, kr),
-          "decode_layer": ms_step}
-    ms_extra = {"append_kv_with_window": time_graph(append_win, per_graph, kr),
-                "append_kv": time_graph(append_nowin, per_graph, kr),
-                "step_with_q_pos": time_graph(step_q_pos, per_graph, kr)}
-    for i in range(N_SETS):  # leave each set's Forecast scores / idx in place
-        step(i)
+    eager = time_loop_stats(step_one_launch, args.steps, stream)
+    log(f"[bench] eager step {eager['median'] * 1e3:.1f} us; timing {args.steps} steps x {REPEATS} graph replays")
+    main_st = time_graph_stats(step_one_launch, args.steps)
+    ms_step = main_st["median"]
+    n_var = 3 * N_SETS * max(1, 60 // (3 * N_SETS))  # 54 calls per graph for the comparisons
+    variants = {"two_launches_per_layer": time_graph_stats(step_two_launches, n_var),
+                "one_layer_at_a_time": time_graph_stats(step_layer, n_var),
+                "topk_separate": time_graph_stats(step_separate, n_var)}
+    log(f"[bench] graph step {ms_step * 1e3:.1f} us (median of {REPEATS} x {args.steps}; two launches per layer "
+        f"{variants['two_launches_per_layer']['median'] * 1e3:.1f} us, one layer at a time "
+        f"{variants['one_layer_at_a_time']['median'] * 1e3:.1f} us, top-k on its own "
+        f"{variants['topk_separate']['median'] * 1e3:.1f} us); per-kernel graphs")
+    for i in range(N_SETS):
+        sel(i)
+    kn = {"select_forecast": sel, "topk": topk, "attention": attn, "select_multihead": sel_mh,
+          "topk_attention": topk_attn, "topk_attention_partial": topk_attn_partial,
+          "select_forecast_merge": sel_merge}
+    kst = {k: time_graph_stats(fn, n_var) for k, fn in kn.items()}
+    kst["decode_layer"] = main_st
+    ms = {k: v["median"] for k, v in kst.items()}
+    ms_extra = {"append_kv_with_window": time_graph(append_win, n_var), "append_kv": time_graph(append_nowin, n_var),
+                "step_with_q_pos": time_graph(step_q_pos, n_var)}
+    # leave every set's Forecast scores, selection and output as the step makes them
+    for i in range(N_SETS):
+        sel(i)
+    for i in range(N_SETS + 1):
+        step_one_launch(i)
+    sel_mh(0)
     torch.cuda.synchronize()
-    projection = bench_projection(kbs, w, dev, kr)
-    token_level = bench_token_level(kbs, w, sets, dev, per_graph, kr)
+    projection = bench_projection(kbs, w, dev, REPEATS)
+    token_level = bench_token_level(kbs, w, sets, dev, n_var)
     decoupled = (decoupled_layers(kbs, w, sets, ws_attn, dev, algorithmic_bytes(w)["step"], n_layers=3 * args.steps)
                  if args.decoupled_layers else None)
+    log("[bench] parity of the step's results (all rows of one input set) against the oracle")
+    par = parity_decode(w, kbs, sets[0], mh_scores=mh_scores[0])
 
     nbytes = algorithmic_bytes(w)
     gbps = {k: nbytes[k] / (ms[k] * 1e-3) / 1e9 for k in ms}
-    # the timed step is one launch per layer: that launch is the roofline kernel
-    dominant = "decode_layer"
+    dominant = "decode_layer"  # the step is one launch per layer: that launch is the roofline kernel
     step_gbps = nbytes["step"] / (ms_step * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": round(1e3 / ms_step, 2),
         "unit": "steps/s/layer",
         "n_gpus": 1,
-        "steps": steps_timed,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
@@ -383,28 +573,27 @@ def bench_decode(args) -> int:
                    "schedule": "consecutive layers (the input sets in turn), one launch per layer: layer l's top-k + "
                                "attention (finished output) and layer l+1's Forecast selection, both from layer l's "
                                "projections"},
+        "timing": {"repeats": REPEATS, "steps_per_repeat": args.steps, "ms_per_step_min": round(main_st["min"], 5),
+                   "ms_per_step_max": round(main_st["max"], 5), "ms_per_step_eager": round(eager["median"], 5)},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(gbps[dominant], 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps[dominant] / HBM_PEAK_GBPS, 4),
-                     "traffic": pmc_traffic(["kv_block_selection_amd/csrc/attn_decode.hip",
-                                             "kv_block_selection_amd/csrc/topk_row.h",
-                                             "kv_block_selection_amd/csrc/select_row.h",
-                                             "kv_block_selection_amd/csrc/merge_row.h",
-                                             "kv_block_selection_amd/csrc/reduce16.h"],
-                                            "decode_layer_c3_traffic.json")},
+                     "traffic": pmc_traffic(LAYER_SOURCES, "decode_layer_c3_traffic.json"),
+                     "algorithmic_bytes_per_launch": nbytes[dominant]},
         "step_hbm_GBps": round(step_gbps, 1),
         "step_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
-        "ms_per_step_eager": round(ms_step_eager, 5),
-        "ms_per_step_two_launches_per_layer": round(ms_step_two_launches, 5),
-        "ms_per_step_one_layer_at_a_time": round(ms_step_layer, 5),
-        "ms_per_step_topk_separate": round(ms_step_separate, 5),
+        "ms_per_step_variants": {k: round(v["median"], 5) for k, v in variants.items()},
         "kernel_us": {k: round(v * 1e3, 2) for k, v in ms.items()},
+        "kernel_us_spread": {k: [round(v["min"] * 1e3, 2), round(v["max"] * 1e3, 2)] for k, v in kst.items()},
         "kernel_GBps": {k: round(v, 1) for k, v in gbps.items()},
         "selection_us": {"forecast": round((ms["select_forecast"] + ms["topk"]) * 1e3, 2),
                          "multihead": round((ms["select_multihead"] + ms["topk"]) * 1e3, 2)},
         "forecast_vs_multihead_select_speedup": round(ms["select_multihead"] / ms["select_forecast"], 3),
+        "multihead_bytes_bound_ratio": round((nbytes["select_multihead"] + 2 * w.B * w.Hkv * w.G * w.W * 4) /
+                                             nbytes["select_forecast"], 3),
         "state_maintenance_us": {k: round(v * 1e3, 2) for k, v in ms_extra.items()},
         "upstream_projection": projection,
         "token_level": token_level,
+        "parity": par,
     }
     if decoupled is not None:
         result["decoupled_layers"] = decoupled
@@ -415,11 +604,14 @@ def bench_decode(args) -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         result["calibration_copy_bytes"] = 1 << 30
+        del src, dst
     if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle sample)")
-        result["cpu_baseline"] = cpu_baseline(w, sets)
-    print(json.dumps(result), flush=True)
-    return 0
+        log(f"[bench] cpu baseline: the oracle on the step's rows, 1 thread and {n_workers} worker processes")
+        result["cpu_baseline"] = cpu_baseline(w, sets[0], pool, n_workers)
+    del sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return result
 
 
 def decoupled_layers(kbs, w, sets, ws_attn, dev, step_bytes: int, n_layers: int) -> dict:
@@ -479,7 +671,7 @@ def decoupled_layers(kbs, w, sets, ws_attn, dev, step_bytes: int, n_layers: int)
     return out
 
 
-def bench_token_level(kbs, w, sets, dev, per_graph: int, kr: int) -> dict:
+def bench_token_level(kbs, w, sets, dev, per_graph: int) -> dict:
     """The token-level Forecast variant at the same shape: the Forecast vector
     scores all T key tokens of every row, the top k_tok = 64 * k tokens are
     kept (the block path's token budget) and attended. Algorithmic bytes: all
@@ -514,8 +706,8 @@ def bench_token_level(kbs, w, sets, dev, per_graph: int, kr: int) -> dict:
         topk(i)
         attn(i)
     torch.cuda.synchronize()
-    ms = {"select_tokens": time_graph(score, per_graph, kr), "topk_tokens": time_graph(topk, per_graph, kr),
-          "token_attention": time_graph(attn, per_graph, kr)}
+    ms = {"select_tokens": time_graph(score, per_graph), "topk_tokens": time_graph(topk, per_graph),
+          "token_attention": time_graph(attn, per_graph)}
     row_bytes = w.d * 2
     nbytes = {"select_tokens": rows * w.T * row_bytes + rows * row_bytes + rows * w.T * 4,
               "topk_tokens": rows * w.T * 4 + rows * k_tok * 4,
@@ -563,16 +755,18 @@ def bench_projection(kbs, w, dev, replays: int, D: int = 4096, n_layers: int = 8
     return out
 
 
-HOST_LINK_PEAK_GBPS = 63.0   # PCIe 5.0 x16, one direction
-MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def bench_offload(args) -> int:
+# ------------------------------------------------------ offload (c4) ----
+def bench_offload_cfg(args) -> dict:
     """Two-layer decode step at B=64, T=128K with layer 1's KV (32 GiB) in pinned
     host memory: both selections, layer 0's attention from HBM overlapped with
     the gather of layer 1's selected blocks over the host link on a side stream,
     then layer 1's attention from staging. Also times each part alone, a plain
-    1 GiB pinned host-to-device copy, and a sweep of the gather's workgroups."""
+    1 GiB pinned host-to-device copy (the link's practical rate), a sweep of the
+    gather's workgroups and the staging buffer kept as a block cache; parity of
+    both layers' results on sampled rows."""
+    import numpy as np
     import torch
     import kv_block_selection_amd as kbs
     from kv_block_selection_amd.lookahead import LookaheadStep
@@ -608,56 +802,223 @@ def bench_offload(args) -> int:
         return lambda i: kbs.prefetch_blocks(l1["host_K"], l1["host_V"], st.idx1.view(w.B, w.Hkv, w.k),
                                              st.stage_k, st.stage_v, num_workgroups=nwg, stream=stream)
 
-    log("[bench] warmup")
-    for i in range(args.warmup):
+    for i in range(max(2, args.warmup)):
         step(i)
     torch.cuda.synchronize()
-    n = max(5, args.steps)
-    ms_step = time_loop(step, n, stream)
-    log(f"[bench] step {ms_step:.3f} ms; parts alone")
+    n = 4
+    step_st = time_loop_stats(step, n, stream)
+    ms_step = step_st["median"]
+    log(f"[bench] offload step {ms_step:.3f} ms; parts alone")
     parts = {"select_both_layers": time_loop(select, n, stream), "attn_layer0_hbm": time_loop(attn0, n, stream),
              "gather_layer1": time_loop(gather(0), n, stream), "attn_layer1_staging": time_loop(attn1, n, stream)}
     host = l1["host_K"].view(-1).view(torch.uint8)[: 1 << 30]
     dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    ms_copy = time_loop(lambda i: dst.copy_(host, non_blocking=True), max(5, n // 4), stream)
+    ms_copy = time_loop(lambda i: dst.copy_(host, non_blocking=True), 2, stream)
     del dst
     sweep = {}
-    for nwg in (8, 16, 32, 64, 128, 256):
-        st.num_workgroups = nwg
-        g = time_loop(gather(nwg), max(5, n // 4), stream)
-        s_ms = time_loop(step, max(5, n // 4), stream)
-        sweep[nwg] = {"gather_ms": round(g, 4), "gather_GBps": round(link_bytes / (g * 1e-3) / 1e9, 2),
-                      "step_ms": round(s_ms, 4)}
-        log(f"[bench] gather with {nwg} workgroups: {g:.3f} ms, step {s_ms:.3f} ms")
-    st.num_workgroups = 0
+    for nwg in (16, 32, 64, 128, 256):
+        g = time_loop(gather(nwg), 1, stream, repeats=3)
+        sweep[nwg] = {"gather_ms": round(g, 4), "gather_GBps": round(link_bytes / (g * 1e-3) / 1e9, 2)}
     cached = bench_cached_gather(kbs, w, l1, st, stream, dev)
+    # results of one step, for parity (sampled rows of both layers)
+    step(0)
+    torch.cuda.synchronize()
+    par = parity_offload(w, kbs, l0, l1, st)
+    serial = sum(parts.values())
     # the gather waits only for layer 1's selection; layer 0's selection and
     # attention can hide behind it
-    serial = sum(parts.values())
     hideable = min(parts["select_both_layers"] / 2 + parts["attn_layer0_hbm"], parts["gather_layer1"])
     link_gbps = link_bytes / (parts["gather_layer1"] * 1e-3) / 1e9
-    result = {
-        "metric": "offloaded decode steps/s/layer at 128K ctx, B=64, two layers with lookahead prefetch",
-        "value": round(2e3 / ms_step, 3),
-        "unit": "steps/s/layer",
-        "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.description, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
-                   "block": w.block, "top_k": w.k, "layers": 2, "gather_workgroups": "library default"},
-        "roofline": {"bound": "host_link", "kernel": "prefetch", "achieved": round(link_gbps, 2),
-                     "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s", "frac": round(link_gbps / HOST_LINK_PEAK_GBPS, 4),
-                     "traffic": None},
-        "link_bytes_per_step": link_bytes,
-        "h2d_memcpy_1GiB_GBps": round((1 << 30) / (ms_copy * 1e-3) / 1e9, 2),
-        "parts_ms": {k: round(v, 4) for k, v in parts.items()},
-        "serial_ms": round(serial, 4),
-        "overlap_hidden_frac": round((serial - ms_step) / hideable, 3) if hideable > 0 else None,
-        "overlap_note": "hideable = layer 0 selection (half of both selections) + layer 0 attention",
-        "workgroup_sweep": sweep,
-        "cached_gather": cached,
-    }
-    print(json.dumps(result), flush=True)
-    return 0
+    h2d = (1 << 30) / (ms_copy * 1e-3) / 1e9
+    out = {"workload": w.description, "steps_per_s_per_layer": round(2e3 / ms_step, 3),
+           "ms_per_step": {k: (round(v, 4) if k != "n" else v) for k, v in step_st.items()},
+           "roofline": {"bound": "host_link", "kernel": "prefetch", "achieved": round(link_gbps, 2),
+                        "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s", "frac": round(link_gbps / HOST_LINK_PEAK_GBPS, 4),
+                        "traffic": None, "frac_of_measured_h2d": round(link_gbps / h2d, 4)},
+           "link_bytes_per_step": link_bytes,
+           "h2d_memcpy_1GiB_GBps": round(h2d, 2),
+           "parts_ms": {k: round(v, 4) for k, v in parts.items()},
+           "serial_ms": round(serial, 4),
+           "overlap_hidden_frac": round((serial - ms_step) / hideable, 3) if hideable > 0 else None,
+           "overlap_note": "hideable = layer 0 selection (half of both selections) + layer 0 attention",
+           "workgroup_sweep": sweep,
+           "cached_gather": cached,
+           "parity": par}
+    del l0, l1, st, host
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def parity_offload(w, kbs, l0, l1, st, n_rows: int = 32) -> dict:
+    """Both layers of the offloaded step on sampled (sequence, KV head) rows:
+    scores (layer 0 by its own Forecast, layer 1 by layer 0's Forecast of the
+    next layer), selection by the band rule, attention of layer 1 from the
+    host copy of its KV over the GPU's selection."""
+    import numpy as np
+    import torch
+    import oracle
+    from tests import parity
+    rng = np.random.default_rng(0)
+    flat = rng.choice(w.B * w.Hkv, n_rows, replace=False)
+    worst = err = 0.0
+    banded = 0
+    status = "ok"
+    for layer in (0, 1):
+        F = l0["F_self"] if layer == 0 else l0["F_next"]
+        Kc = l0["Kc"] if layer == 0 else l1["Kc"]
+        scores = st.scores0 if layer == 0 else st.scores1
+        idx = st.idx0 if layer == 0 else st.idx1
+        out = st.out0 if layer == 0 else st.out1
+        Q = l0["Q"] if layer == 0 else l1["Q"]
+        for r in flat:
+            b, h = divmod(int(r), w.Hkv)
+            ref = oracle.select_forecast_tile(parity.to_f64(F[b, h]), parity.to_f64(Kc[b, h]), [w.q_start], w.T,
+                                              w.scale)[None, :]
+            r1 = _check(parity.check_scores, parity.to_f64(scores[b, h]), ref)
+            gi = idx[b, h].cpu().numpy()
+            r2 = _check(parity.check_topk_band, gi, ref, w.k)
+            J = oracle.selected_keys(gi[0], w.q_start)
+            if layer == 0:
+                Jt = torch.from_numpy(J).to(Q.device)
+                KJ, VJ = l0["K"][b, h].index_select(0, Jt), l0["V"][b, h].index_select(0, Jt)
+            else:
+                Jt = torch.from_numpy(J)
+                KJ, VJ = l1["host_K"][b, h].index_select(0, Jt), l1["host_V"][b, h].index_select(0, Jt)
+            KJ, VJ = parity.to_f64(KJ), parity.to_f64(VJ)
+            Qr = parity.to_f64(Q[b, h * w.G:(h + 1) * w.G, 0])
+            o_ref = np.stack([oracle.attend(Qr[g], KJ, VJ, w.scale) for g in range(w.G)]) if J.size else 0 * Qr
+            r3 = _check(parity.check_attention, parity.to_f64(out[b, h * w.G:(h + 1) * w.G, 0]), o_ref,
+                        parity.ATTN_ATOL_BF16)
+            for x in (r1, r2, r3):
+                if isinstance(x, str):
+                    status = x
+            worst = max(worst, r1) if not isinstance(r1, str) else worst
+            banded += r2 if not isinstance(r2, str) else 0
+            err = max(err, r3) if not isinstance(r3, str) else err
+    return {"status": status, "rows_checked": 2 * n_rows, "score_worst_rel": float(f"{worst:.3g}"),
+            "banded_rows": int(banded), "attn_max_abs": float(f"{err:.3g}")}
+
+
+# ------------------------------------------------------- prefill (c5) ----
+def bench_prefill_cfg(args) -> dict:
+    """A 4096-query chunk at the end of a 128K context (B=1, 32/8 heads): Forecast
+    scoring of every 64-query tile, top-64 per tile, block-sparse attention,
+    each on the matrix cores except top-k; inputs resident in HBM. The
+    multi-head selector is timed beside the Forecast."""
+    import torch
+    import kv_block_selection_amd as kbs
+    import synth.gpu as sg
+    from synth import workloads as wl
+
+    kbs.load()
+    w = wl.C5_PREFILL
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating {w.name}")
+    s = {n: sg.tensor(w.recipe(n), w.shape(n), dev) for n in ("Q", "F", "K", "V")}
+    s["Kc"] = kbs.compress_keys(s["K"])
+    scores = torch.empty((w.B, w.Hkv, w.n_tiles, w.nB), dtype=torch.float32, device=dev)
+    mh = torch.empty_like(scores)
+    idx = torch.empty((w.B, w.Hkv, w.n_tiles, w.k), dtype=torch.int32, device=dev)
+    out = torch.empty_like(s["Q"])
+
+    def sel(i):
+        kbs.select_forecast(s["F"], s["Kc"], w.T, w.q_start, out=scores)
+
+    def topk(i):
+        kbs.topk_blocks(scores, w.k, out=idx)
+
+    def attn(i):
+        kbs.block_sparse_attn(s["Q"], s["K"], s["V"], idx, w.T, w.q_start, out=out)
+
+    def sel_mh(i):
+        kbs.select_multihead(s["Q"], s["Kc"], w.T, w.q_start, out=mh)
+
+    def step(i):
+        sel(i)
+        topk(i)
+        attn(i)
+
+    for i in range(max(3, args.warmup)):
+        step(i)
+    torch.cuda.synchronize()
+    n = 20
+    step_st = time_graph_stats(step, n)
+    kst = {"select_forecast": time_graph_stats(sel, n), "topk": time_graph_stats(topk, n),
+           "attention": time_graph_stats(attn, n), "select_multihead": time_graph_stats(sel_mh, 5)}
+    ms = {k: v["median"] for k, v in kst.items()}
+    step(0)
+    sel_mh(0)
+    torch.cuda.synchronize()
+    fl = prefill_flops(w, idx.cpu().numpy())
+    tf = {k: fl[k] / (ms[k] * 1e-3) / 1e12 for k in fl}
+    roof = {k: {"bound": "mfma", "kernel": k, "achieved": round(tf[k], 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf[k] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+            for k in fl}
+    par = parity_prefill(w, s, scores, mh, idx, out)
+    del s
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"workload": w.description, "chunks_per_s": round(1e3 / step_st["median"], 3),
+            "us_per_chunk": _us(step_st),
+            "roofline": roof["attention"], "roofline_per_kernel": roof,
+            "kernel_us": {k: round(v * 1e3, 2) for k, v in ms.items()},
+            "kernel_us_spread": {k: [round(v["min"] * 1e3, 2), round(v["max"] * 1e3, 2)] for k, v in kst.items()},
+            "algorithmic_gflop": {k: round(v / 1e9, 3) for k, v in fl.items()},
+            "mfma_utilisation": {k: round(v / MFMA_BF16_PEAK_TFLOPS, 4) for k, v in tf.items()},
+            "selection_us": {"forecast": round((ms["select_forecast"] + ms["topk"]) * 1e3, 2),
+                             "multihead": round((ms["select_multihead"] + ms["topk"]) * 1e3, 2)},
+            "forecast_vs_multihead_select_speedup": round(ms["select_multihead"] / ms["select_forecast"], 3),
+            "multihead_exp_per_chunk": 2 * w.G * fl["select_forecast"] // (2 * w.d),
+            "parity": par}
+
+
+def parity_prefill(w, s, scores, mh, idx, out, n_pairs: int = 12) -> dict:
+    """Sampled (KV head, query tile) pairs of the chunk, all 64 queries of
+    each: Forecast and multi-head tile scores (the oracle scores the GPU's
+    compressed keys), the selection by the band rule, and attention of every
+    query head of the group over the GPU's selection."""
+    import numpy as np
+    import oracle
+    from tests import parity
+    rng = np.random.default_rng(1)
+    pairs = [(0, 0), (w.Hkv - 1, w.n_tiles - 1)] + [(int(h), int(t)) for h, t in
+                                                    zip(rng.integers(0, w.Hkv, n_pairs - 2),
+                                                        rng.integers(0, w.n_tiles, n_pairs - 2))]
+    worst = worst_mh = err = 0.0
+    banded = 0
+    status = "ok"
+    for h, t in pairs:
+        i0, i1 = t * w.tile, min(w.Tq, (t + 1) * w.tile)
+        pos = [w.q_start + i for i in range(i0, i1)]
+        Kc = parity.to_f64(s["Kc"][0, h])
+        ref = oracle.select_forecast_tile(parity.to_f64(s["F"][0, h, i0:i1]), Kc, pos, w.T, w.scale)[None, :]
+        Qg = parity.to_f64(s["Q"][0, h * w.G:(h + 1) * w.G, i0:i1])
+        ref_mh = oracle.select_multihead_tile(Qg, Kc, pos, w.T, w.scale)[None, :]
+        r1 = _check(parity.check_scores, parity.to_f64(scores[0, h, t])[None, :], ref)
+        r4 = _check(parity.check_scores, parity.to_f64(mh[0, h, t])[None, :], ref_mh)
+        gi = idx[0, h, t].cpu().numpy()
+        r2 = _check(parity.check_topk_band, gi[None, :], ref, w.k)
+        K64, V64 = parity.to_f64(s["K"][0, h, : pos[-1] + 1]), parity.to_f64(s["V"][0, h, : pos[-1] + 1])
+        o_ref = np.zeros((w.G, i1 - i0, w.d))
+        for qi, p in enumerate(pos):
+            J = oracle.selected_keys(gi, p)
+            if J.size:
+                for g in range(w.G):
+                    o_ref[g, qi] = oracle.attend(Qg[g, qi], K64[J], V64[J], w.scale)
+        r3 = _check(parity.check_attention, parity.to_f64(out[0, h * w.G:(h + 1) * w.G, i0:i1]), o_ref,
+                    parity.ATTN_ATOL_BF16)
+        for x in (r1, r2, r3, r4):
+            if isinstance(x, str):
+                status = x
+        worst = max(worst, r1) if not isinstance(r1, str) else worst
+        worst_mh = max(worst_mh, r4) if not isinstance(r4, str) else worst_mh
+        banded += r2 if not isinstance(r2, str) else 0
+        err = max(err, r3) if not isinstance(r3, str) else err
+    return {"status": status, "tiles_checked": len(pairs), "queries_per_tile": w.tile,
+            "score_worst_rel": float(f"{worst:.3g}"), "multihead_score_worst_rel": float(f"{worst_mh:.3g}"),
+            "banded_tiles": int(banded), "attn_max_abs": float(f"{err:.3g}")}
 
 
 def bench_cached_gather(kbs, w, l1, st, stream, dev, steps: int = 8) -> dict:
@@ -731,7 +1092,7 @@ def bench_pipeline(args, L: int = 4, B: int = 16) -> int:
     for i in range(args.warmup):
         pipe.step(layers, stream)
     torch.cuda.synchronize()
-    n = max(5, args.steps)
+    n = max(3, min(args.steps, 10))
     ms_step = time_loop(lambda i: pipe.step(layers, stream), n, stream)
     sk, sv = pipe.stage[0]
 
@@ -820,77 +1181,85 @@ def prefill_flops(w, idx) -> dict:
     return {"select_forecast": sel, "select_multihead": 2 * w.G * sel, "attention": 4 * w.d * keys * w.G}
 
 
-def bench_prefill(args) -> int:
-    """A 4096-query chunk at the end of a 128K context (B=1, 32/8 heads): Forecast
-    scoring of every 64-query tile, top-64 per tile, block-sparse attention,
-    each on the matrix cores except top-k; inputs resident in HBM."""
-    import torch
-    import kv_block_selection_amd as kbs
-    import synth.gpu as sg
-    from synth import workloads as wl
 
-    kbs.load()
-    w = wl.C5_PREFILL
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    log(f"[bench] generating {w.name}")
-    s = {n: sg.tensor(w.recipe(n), w.shape(n), dev) for n in ("Q", "F", "K", "V")}
-    Kc = kbs.compress_keys(s["K"])
-    scores = torch.empty((w.B, w.Hkv, w.n_tiles, w.nB), dtype=torch.float32, device=dev)
-    idx = torch.empty((w.B, w.Hkv, w.n_tiles, w.k), dtype=torch.int32, device=dev)
-    out = torch.empty_like(s["Q"])
-    stream = torch.cuda.current_stream(dev)
 
-    def sel(i):
-        kbs.select_forecast(s["F"], Kc, w.T, w.q_start, out=scores)
+# ------------------------------------------------------------------ main ----
+def _line(metric: str, value, unit: str, ms_per_step, steps: int, args, workload: str, extra: dict) -> dict:
+    out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+           "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic", "config": {"workload": workload}}
+    out.update(extra)
+    return out
 
-    def topk(i):
-        kbs.topk_blocks(scores, w.k, out=idx)
 
-    def attn(i):
-        kbs.block_sparse_attn(s["Q"], s["K"], s["V"], idx, w.T, w.q_start, out=out)
-
-    def sel_mh(i):
-        kbs.select_multihead(s["Q"], Kc, w.T, w.q_start, out=scores)
-
-    def step(i):
-        sel(i)
-        topk(i)
-        attn(i)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    n = max(5, args.steps)
-    ms_step = time_loop(step, n, stream)
-    ms = {"select_forecast": time_loop(sel, n, stream), "topk": time_loop(topk, n, stream),
-          "attention": time_loop(attn, n, stream), "select_multihead": time_loop(sel_mh, n, stream)}
-    step(0)
-    torch.cuda.synchronize()
-    fl = prefill_flops(w, idx.cpu().numpy())
-    tf = {k: fl[k] / (ms[k] * 1e-3) / 1e12 for k in fl}
-    result = {
-        "metric": "chunked-prefill chunks/s at 128K ctx (4096 queries, select+sparse attn)",
-        "value": round(1e3 / ms_step, 3),
-        "unit": "chunks/s",
-        "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.description, "B": w.B, "T": w.T, "Tq": w.Tq, "q_start": w.q_start, "Hq": w.Hq,
-                   "Hkv": w.Hkv, "d": w.d, "block": w.block, "tile": w.tile, "top_k": w.k},
-        "roofline": {"bound": "mfma", "kernel": "attention", "achieved": round(tf["attention"], 1),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf["attention"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
-        "kernel_us": {k: round(v * 1e3, 2) for k, v in ms.items()},
-        "algorithmic_gflop": {k: round(v / 1e9, 3) for k, v in fl.items()},
-        "kernel_TFLOPs": {k: round(v, 1) for k, v in tf.items()},
-        "mfma_utilisation": {k: round(v / MFMA_BF16_PEAK_TFLOPS, 4) for k, v in tf.items()},
-        "selection_us": {"forecast": round((ms["select_forecast"] + ms["topk"]) * 1e3, 2),
-                         "multihead": round((ms["select_multihead"] + ms["topk"]) * 1e3, 2)},
-        "forecast_vs_multihead_select_speedup": round(ms["select_multihead"] / ms["select_forecast"], 3),
-        "multihead_exp_per_chunk": 2 * w.G * prefill_flops(w, idx.cpu().numpy())["select_forecast"] // (2 * w.d),
-    }
-    print(json.dumps(result), flush=True)
-    return 0
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=("all", "decode", "offload", "prefill", "pipeline"), default="all",
+                    help="all (default): the batch-16 128K decode step as the headline, the other four workloads "
+                         "as extra keys; decode: the headline only; offload: the batch-64 two-layer step with "
+                         "lookahead prefetch from pinned host memory; prefill: a 4096-query chunk at 128K; "
+                         "pipeline: a four-layer offloaded stack")
+    ap.add_argument("--decoupled-layers", action="store_true",
+                    help="decode: also time consecutive layers with the next layer's selection on a second stream "
+                         "beside this layer's attention, against the same layers on one stream")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (torch copy_) ten times, as the known-size reference "
+                         "for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this path is built and timed on a single "
+              f"MI355X; sharding across GPUs is not implemented.", file=sys.stderr)
+        return 2
+    if args.steps < 1:
+        print("--steps must be at least 1", file=sys.stderr)
+        return 2
+    # the all-cores oracle's worker processes start before anything touches the GPU
+    pool, n_workers = (None, 0)
+    if args.workload in ("all", "decode") and not args.no_cpu_baseline:
+        pool, n_workers = start_oracle_pool()
+    try:
+        if args.workload == "pipeline":
+            return bench_pipeline(args)
+        if args.workload == "offload":
+            r = bench_offload_cfg(args)
+            print(json.dumps(_line("offloaded decode steps/s/layer at 128K ctx, B=64, two layers with lookahead "
+                                   "prefetch", r["steps_per_s_per_layer"], "steps/s/layer",
+                                   r["ms_per_step"]["median"], 4, args, r["workload"], r)), flush=True)
+            return 0
+        if args.workload == "prefill":
+            r = bench_prefill_cfg(args)
+            print(json.dumps(_line("chunked-prefill chunks/s at 128K ctx (4096 queries, select+sparse attn)",
+                                   r["chunks_per_s"], "chunks/s", round(r["us_per_chunk"]["median"] / 1e3, 5), 20,
+                                   args, r["workload"], r)), flush=True)
+            return 0
+        import torch
+        from synth import workloads as wl
+        configs = {}
+        if args.workload == "all":
+            import kv_block_selection_amd as kbs
+            kbs.load()
+            dev = torch.device("cuda:0")
+            torch.cuda.set_device(dev)
+            for w in (wl.C1_TINY, wl.C2_DECODE_32K):
+                log(f"[bench] {w.name}")
+                configs[w.name] = bench_small_decode(kbs, w, dev, args.steps, args.warmup)
+        result = bench_decode(args, pool, n_workers)
+        if args.workload == "all":
+            log("[bench] c5: chunked prefill")
+            configs[wl.C5_PREFILL.name] = bench_prefill_cfg(args)
+            log("[bench] c4: offloaded decode with lookahead prefetch")
+            configs[wl.C4_OFFLOAD.name] = bench_offload_cfg(args)
+            result["other_configs"] = configs
+        print(json.dumps(result), flush=True)
+        return 0
+    finally:
+        if pool is not None:
+            pool.terminate()
+            pool.join()
 
 
 if __name__ == "__main__":
