@@ -16,9 +16,11 @@ of them).
 
 Timing: W untimed steps, then exactly K steps captured in one HIP graph,
 replayed 5 times, each replay between two HIP events on the launch stream
-with a device synchronisation on both sides; ms_per_step is the median
-replay / K (the spread is reported). Input sets rotate (3 independent sets)
-so no step finds its data in the 256 MB last-level cache.
+with a device synchronisation on both sides (three untimed steps run between
+the synchronisation and the start event, so the timed steps do not begin on
+an idle GPU); ms_per_step is the median replay / K (the spread is reported).
+Input sets rotate (3 independent sets) so no step finds its data in the
+256 MB last-level cache.
 """
 
 from __future__ import annotations
@@ -53,11 +55,14 @@ def _stats(per_call_ms) -> dict:
     return {"median": statistics.median(xs), "min": xs[0], "max": xs[-1], "n": len(xs)}
 
 
-def time_graph_stats(fn, n: int, repeats: int = REPEATS) -> dict:
+def time_graph_stats(fn, n: int, repeats: int = REPEATS, prime: int = 3) -> dict:
     """fn(0) .. fn(n-1) captured once in a HIP graph (no host launch cost
     inside), replayed `repeats` times, each replay between HIP events on the
-    replay stream with a device synchronisation on both sides. Returns the
-    median / min / max ms per fn call over the replays."""
+    replay stream with a device synchronisation on both sides. Before each
+    replay's start event, `prime` untimed fn calls run eagerly, so that the
+    GPU is busy (clocks up) when the timed region begins rather than idle
+    after the synchronisation. Returns the median / min / max ms per fn call
+    over the replays."""
     import torch
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -78,6 +83,8 @@ def time_graph_stats(fn, n: int, repeats: int = REPEATS) -> dict:
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        for i in range(prime):
+            fn(i)
         start.record(stream)
         g.replay()
         end.record(stream)
@@ -94,13 +101,15 @@ def time_graph(fn, n: int, repeats: int = REPEATS) -> float:
 
 def time_loop_stats(fn, n: int, stream, repeats: int = REPEATS) -> dict:
     """fn(0) .. fn(n-1) launched eagerly, `repeats` times, each run between HIP
-    events on `stream`; median / min / max ms per call."""
+    events on `stream` (after one untimed call that keeps the GPU busy up to
+    the start event); median / min / max ms per call."""
     import torch
     out = []
     for _ in range(repeats):
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        fn(0)
         start.record(stream)
         for i in range(n):
             fn(i)

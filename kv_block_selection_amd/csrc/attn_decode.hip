@@ -90,7 +90,7 @@ __device__ __forceinline__ void attn_decode_body(
     __shared__ int32_t s_sel[kFusedMaxK];
     topk_row<NPT, WPG>(scores + row * nB, wg_split == 0 ? idx_out + row * k : nullptr, s_sel, nB, k, sh,
                        threadIdx.x);
-    __syncthreads();
+    lds_sync();  // the selection is in LDS
     idx_row = s_sel;
   }
   // a wave past the row's last split: none of the work below (with LDSM it
@@ -400,7 +400,10 @@ void attn_decode_kernel(
 // go to the workspace; the merge is a second, small launch.
 // Both run at the attention's register allocation (2 waves per SIMD), so a
 // selection workgroup takes 128 blocks (513 windows) instead of 16.
-constexpr int kLayerSelBlocks = 128;
+#ifndef SPARDA_LAYER_SEL_BLOCKS
+#define SPARDA_LAYER_SEL_BLOCKS 128
+#endif
+constexpr int kLayerSelBlocks = SPARDA_LAYER_SEL_BLOCKS;
 constexpr int kLayerRowWaves = 8;     // waves of a row-form attention workgroup
 constexpr int kLayerRowMinRows = 96;  // fewest rows for the row form
 
@@ -416,15 +419,16 @@ void decode_layer_row_kernel(int rows,
                              const uint8_t* __restrict__ f_n, const uint8_t* __restrict__ kc_n,
                              float* __restrict__ scores_n, int W_n, int nB_n, int n_vis_n,
                              const int* __restrict__ q_pos_n, int T_n, float scale_n) {
+  constexpr int NT = kLayerRowWaves * 64;
   if ((int)blockIdx.x < rows) {
     attn_decode_body<Tag, G, kLayerRowWaves, NPT, true>(blockIdx.x, 0, q, kbuf, vbuf, nullptr, idx_out, scores,
                                                         nullptr, nullptr, out, T, nB, k, SPARDA_KV_CACHE_MODE, p_all,
                                                         q_pos, hkv, nullptr, 0, bps, splits, scale);
   } else {
     const int r = blockIdx.x - rows;
-    __shared__ float s_win[fsel_lds_floats<Tag, kLayerSelBlocks, kLayerRowWaves * 64>()];
-    fsel_blocks<Tag, kLayerSelBlocks, kLayerRowWaves * 64>(f_n, kc_n, scores_n, W_n, nB_n, n_vis_n, q_pos_n, hkv, T_n,
-                                                          scale_n, r % rows, r / rows, s_win, threadIdx.x);
+    __shared__ float s_win[fsel_lds_floats<Tag, kLayerSelBlocks, NT>()];
+    fsel_blocks<Tag, kLayerSelBlocks, NT>(f_n, kc_n, scores_n, W_n, nB_n, n_vis_n, q_pos_n, hkv, T_n, scale_n,
+                                          r % rows, r / rows, s_win, threadIdx.x);
   }
 }
 

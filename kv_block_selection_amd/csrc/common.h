@@ -213,6 +213,11 @@ __device__ __forceinline__ void dma16(const uint8_t* gsrc, const uint8_t* lds_wa
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(base) : "memory");
 }
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations, not for its global loads (a __syncthreads fence would wait for
+// every load in flight, including ones issued ahead on purpose).
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 __device__ __forceinline__ float fast_exp(float x) {

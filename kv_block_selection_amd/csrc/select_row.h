@@ -61,7 +61,7 @@ __device__ __forceinline__ void fsel_blocks(const uint8_t* __restrict__ f, const
     const float s = group_sum<R::LPR>(dot16<Tag>(fv, kv[it], 0.f));
     if (lane == 0) s_win[lw] = ok ? s * scale : -INFINITY;
   }
-  __syncthreads();
+  lds_sync();
   if (t < nblk) {
     float m = s_win[4 * t];
 #pragma unroll
@@ -71,3 +71,4 @@ __device__ __forceinline__ void fsel_blocks(const uint8_t* __restrict__ f, const
 }
 
 }  // namespace sparda
+

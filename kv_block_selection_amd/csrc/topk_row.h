@@ -79,6 +79,8 @@ __device__ __forceinline__ void clear_hist(TopkShared<NW>& sh, int b, int t) {
 
 // The k best blocks of one row of nB scores, by the NW x 64 threads of a
 // workgroup (t = thread index; NPT scores per thread, NW x 64 x NPT >= nB).
+// Its barriers order LDS only, so global loads the caller issued before it
+// stay in flight.
 // The indices go to dst_g (global memory) and/or dst_s (LDS), either of which
 // may be NULL, ascending with -1 padding.
 template <int NPT, int NW = 4>
@@ -115,7 +117,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ src, int32_t*
     sh.wave_max[wid] = wmax;
     sh.wave_bound[wid] = wbound;
   }
-  __syncthreads();
+  lds_sync();
   int n_cand = 0;
   kmax = 0u;
   uint32_t lb = 0xFFFFFFFFu;
@@ -153,7 +155,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ src, int32_t*
     // the buffer for the next pass was last read two passes ago, before the
     // previous pass's barrier
     clear_hist(sh, nxt, t);
-    __syncthreads();
+    lds_sync();
     // every wave: lane handles digits 255-4*lane .. 252-4*lane (descending)
     int h[4], sum = 0;
 #pragma unroll
@@ -200,7 +202,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ src, int32_t*
   const int packed = gt | (eq << 16);
   const int incl = wave_incl_scan(packed);
   if (lane == kWave - 1) sh.wave_tot[wid] = incl;
-  __syncthreads();
+  lds_sync();
   int before = incl - packed;
 #pragma unroll
   for (int w = 0; w < NW; ++w) before += w < wid ? sh.wave_tot[w] : 0;
