@@ -31,8 +31,14 @@ namespace sparda {
 #define SPARDA_FSEL_BLOCKS 16
 #endif
 constexpr int kFselBlocks = SPARDA_FSEL_BLOCKS;  // blocks per workgroup, Forecast pass
-constexpr int kMhChunk = 256;     // windows per workgroup, multi-head pass 1
-constexpr int kMhPoolBlocks = 64; // blocks per workgroup, multi-head pass 2
+#ifndef SPARDA_MH_CHUNK
+#define SPARDA_MH_CHUNK 128
+#endif
+constexpr int kMhChunk = SPARDA_MH_CHUNK;  // windows per workgroup, multi-head pass 1
+#ifndef SPARDA_MH_POOL
+#define SPARDA_MH_POOL 256
+#endif
+constexpr int kMhPoolBlocks = SPARDA_MH_POOL;  // blocks per workgroup, multi-head pass 2
 
 
 // ---------------------------------------------------------------- Forecast --
@@ -84,9 +90,15 @@ hipError_t launch_select_forecast_decode(const void* f, const void* kc, float* s
 }
 
 // -------------------------------------------------------------- multi-head --
+// Pass 1 leaves, per window, each head's exp(logit - chunk max) as fp16
+// (between 0 and 1: at most 2^-11 relative rounding, well inside the scores'
+// 1e-3 tolerance), and per (chunk, head) the max and the sum of those
+// exponentials; pass 2 turns the chunk statistics into one normaliser per head
+// and sums the group's probabilities e * exp(chunk max - max) / sum.
 struct MhWs {
-  float* logits;  // [rows, G, W]
-  float2* stats;  // [rows, chunks, G] (max, sum of exp)
+  uint16_t* e;    // [rows, chunks * kMhChunk, G] fp16: the G heads' exponentials of a window side by
+                  // side; a row's records padded to whole chunks, so each chunk's are one aligned run
+  float2* stats;  // [rows, chunks, G] (chunk max, sum of exp over the chunk)
 };
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -95,8 +107,9 @@ static MhWs mh_ws(void* ws, const SelectDims& d) {
   const int G = d.Hq / d.Hkv;
   const size_t rows = (size_t)d.B * d.Hkv;
   MhWs r;
-  r.logits = (float*)ws;
-  r.stats = (float2*)((char*)ws + align256(rows * G * d.W * sizeof(float)));
+  r.e = (uint16_t*)ws;
+  const size_t chunks = (d.W + kMhChunk - 1) / kMhChunk;
+  r.stats = (float2*)((char*)ws + align256(rows * chunks * kMhChunk * G * sizeof(uint16_t)));
   return r;
 }
 
@@ -104,9 +117,24 @@ size_t multihead_decode_ws_bytes(const SelectDims& d) {
   const int G = d.Hq / d.Hkv;
   const size_t rows = (size_t)d.B * d.Hkv;
   const size_t chunks = (d.W + kMhChunk - 1) / kMhChunk;
-  return align256(rows * G * d.W * sizeof(float)) + align256(rows * chunks * G * sizeof(float2));
+  return align256(rows * chunks * kMhChunk * G * sizeof(uint16_t)) + align256(rows * chunks * G * sizeof(float2));
 }
 
+__device__ __forceinline__ uint16_t to_f16_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+__device__ __forceinline__ float from_f16_bits(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// A record of G fp16 values, stored and loaded whole.
+template <int G>
+struct alignas(2 * G) MhRec {
+  uint16_t v[G];
+};
+
+// Pass 1: a workgroup scores kMhChunk windows of one row for all G heads. After
+// the reduce-scatter each lane holds the logits of GR heads (lanes that share a
+// head hold the same bits) and keeps them in registers: the chunk's max per
+// head (lane, then the wave's slots by lane-pair swaps, then the four waves),
+// the exponentials and their sum (the same order), then the records go out
+// through LDS so that consecutive threads store consecutive windows.
 template <typename Tag, int G>
 __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __restrict__ q,
                                                            const uint8_t* __restrict__ kc, MhWs ws,
@@ -114,21 +142,32 @@ __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __rest
                                                            int hkv, int T, int chunks, float scale) {
   using R = RowGeom<Tag>;
   constexpr int ITER = kMhChunk / R::SLOTS;
-  static_assert(kMhChunk == 4 * kWave, "one window per thread, four waves");
-  __shared__ float s_log[G][kMhChunk];
+  constexpr int GR = G < 4 ? 1 : G / 4;              // heads a lane holds after the reduce-scatter
+  constexpr int HL = G >= 4 ? 4 : (G == 2 ? 8 : 16);  // lanes that share a head
+  static_assert(kMhChunk % R::SLOTS == 0, "whole passes of the 256 threads");
   __shared__ float red_m[4][G], red_z[4][G];
+  __shared__ MhRec<G> s_e[kMhChunk];
 
-  const long row = blockIdx.y;  // (b, kv head)
+  // rows on the fast axis: a row's chunks run on one XCD, so its records
+  // meet in that XCD's L2 (and pass 2 of the row reads them there)
+  const long row = blockIdx.x;  // (b, kv head)
   if (q_pos != nullptr) n_vis = visible_windows(row_position(q_pos, row, hkv, 0, T), W);
-  const int chunk = blockIdx.x;
+  const int chunk = blockIdx.y;
   const int w0 = chunk * kMhChunk;
   const int lane = threadIdx.x % R::LPR;
   const int slot = threadIdx.x / R::LPR;
+  const int c = lane & 15;
+  const int hsub = (c / HL) & 3;  // this lane's head within each group of four
+  const int wid = threadIdx.x / kWave;
+  // one lane per (slot, head) records exponentials; one per (wave, head) the
+  // wave's statistics (after the swaps every slot of the wave holds them)
+  const bool rec_writer = lane < 16 && (c & (HL - 1)) == 0;
+  const bool writer = (threadIdx.x % kWave) < 16 && (c & (HL - 1)) == 0;
 
   // query heads in the reduce-scatter's slot order for this lane
   u32x4 qv[G];
 #pragma unroll
-  for (int s = 0; s < G; ++s) qv[s] = load16(q + (row * G + slot_head<G>(s, lane & 15)) * R::RB + lane * 16);
+  for (int s = 0; s < G; ++s) qv[s] = load16(q + (row * G + slot_head<G>(s, c)) * R::RB + lane * 16);
   const uint8_t* base = kc + row * (long)W * R::RB + lane * 16;
 
   u32x4 kv[ITER];
@@ -137,15 +176,13 @@ __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __rest
     const int w = w0 + it * R::SLOTS + slot;
     kv[it] = (w < n_vis) ? load16_nt(base + (long)w * R::RB) : u32x4{0, 0, 0, 0};
   }
-  // All G logits of a window in one reduce-scatter: afterwards lanes 4 apart
-  // (8 for G = 2, 16 for G = 1) hold different heads; the first lane of each
-  // such group writes its head(s).
-  constexpr int GR = G < 4 ? 1 : G / 4;
-  constexpr int HL = G >= 4 ? 4 : (G == 2 ? 8 : 16);
+  float lg[ITER][GR];
+  float m[GR];
+#pragma unroll
+  for (int gr = 0; gr < GR; ++gr) m[gr] = -INFINITY;
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
-    const int lw = it * R::SLOTS + slot;
-    const bool ok = w0 + lw < n_vis;
+    const int w = w0 + it * R::SLOTS + slot;
     float part[G];
 #pragma unroll
     for (int s = 0; s < G; ++s) part[s] = dot16<Tag>(qv[s], kv[it], 0.f);
@@ -155,100 +192,161 @@ __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __rest
     }
     float sc[GR];
     reduce_scatter16<G>(part, sc);
-    if ((lane & (HL - 1)) == 0 && lane < 16) {
-      const int h = lane / HL;
 #pragma unroll
-      for (int gr = 0; gr < GR; ++gr) s_log[4 * gr + h][lw] = ok ? sc[gr] * scale : -INFINITY;
+    for (int gr = 0; gr < GR; ++gr) {
+      lg[it][gr] = w < n_vis ? sc[gr] * scale : -INFINITY;
+      m[gr] = fmaxf(m[gr], lg[it][gr]);
     }
   }
-  __syncthreads();
-  // Chunk statistics of all G heads at once: wave max and sum per head, one
-  // LDS exchange of the four waves' partials each (the waves' partial sums
-  // are added in wave order).
+  // the chunk's max per head: across the wave's slots (bf16 rows are 16 lanes,
+  // four slots per wave; fp32 rows 32 lanes, two slots, lanes 16..31 repeating
+  // lanes 0..15), then across the waves
+#pragma unroll
+  for (int gr = 0; gr < GR; ++gr) {
+    if constexpr (R::LPR == 16) m[gr] = max16(m[gr]);
+    m[gr] = max32(m[gr]);
+    if (writer) red_m[wid][4 * gr + hsub] = m[gr];
+  }
+  lds_sync();
+  float z[GR];
+#pragma unroll
+  for (int gr = 0; gr < GR; ++gr) {
+    const int h = 4 * gr + hsub;
+    m[gr] = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
+    z[gr] = 0.f;
+  }
+  if constexpr (G >= 4 && ITER % 4 == 0) {
+    // the four lanes that share a head split its windows: lane j of the quad
+    // takes iterations j, j + 4, ..., so each exponential is computed once;
+    // the quad's sums then meet by a butterfly (the same bits in all four)
+    const int j = c & 3;
+#pragma unroll
+    for (int k = 0; k < ITER / 4; ++k) {
+      const int lw = (4 * k + j) * R::SLOTS + slot;
+#pragma unroll
+      for (int gr = 0; gr < GR; ++gr) {
+        const float x = j == 0 ? lg[4 * k][gr] : j == 1 ? lg[4 * k + 1][gr] : j == 2 ? lg[4 * k + 2][gr]
+                                                                                   : lg[4 * k + 3][gr];
+        const float e = x == -INFINITY ? 0.f : fast_exp(x - m[gr]);
+        z[gr] += e;
+        if (lane < 16) s_e[lw].v[4 * gr + hsub] = to_f16_bits(e);
+      }
+    }
+#pragma unroll
+    for (int gr = 0; gr < GR; ++gr) {
+      z[gr] += dpp<0xB1>(z[gr]);  // quad_perm [1,0,3,2]
+      z[gr] += dpp<0x4E>(z[gr]);  // quad_perm [2,3,0,1]
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int lw = it * R::SLOTS + slot;
+#pragma unroll
+      for (int gr = 0; gr < GR; ++gr) {
+        const float e = lg[it][gr] == -INFINITY ? 0.f : fast_exp(lg[it][gr] - m[gr]);
+        z[gr] += e;
+        if (rec_writer) s_e[lw].v[4 * gr + hsub] = to_f16_bits(e);
+      }
+    }
+  }
+#pragma unroll
+  for (int gr = 0; gr < GR; ++gr) {
+    if constexpr (R::LPR == 16) z[gr] = sum16(z[gr]);
+    z[gr] = sum32(z[gr]);
+    if (writer) red_z[wid][4 * gr + hsub] = z[gr];
+  }
+  lds_sync();
   const int t = threadIdx.x;
-  const int wid = t / kWave;
-  const int w = w0 + t;
-  float x[G], m[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    x[g] = s_log[g][t];
-    m[g] = wave_max(x[g]);
-    if (w < W) ws.logits[(row * G + g) * W + w] = x[g];
-  }
-  if (t % kWave == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) red_m[wid][g] = m[g];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = fmaxf(fmaxf(red_m[0][g], red_m[1][g]), fmaxf(red_m[2][g], red_m[3][g]));
-    const float e = (m[g] == -INFINITY || x[g] == -INFINITY) ? 0.f : fast_exp(x[g] - m[g]);
-    const float z = wave_sum(e);
-    if (t % kWave == 0) red_z[wid][g] = z;
-  }
-  __syncthreads();
   if (t < G) {
-    const float mt = fmaxf(fmaxf(red_m[0][t], red_m[1][t]), fmaxf(red_m[2][t], red_m[3][t]));
-    const float z = ((red_z[0][t] + red_z[1][t]) + red_z[2][t]) + red_z[3][t];
-    ws.stats[(row * chunks + chunk) * G + t] = make_float2(mt, z);
+    const float mc = fmaxf(fmaxf(red_m[0][t], red_m[1][t]), fmaxf(red_m[2][t], red_m[3][t]));
+    const float zc = ((red_z[0][t] + red_z[1][t]) + red_z[2][t]) + red_z[3][t];
+    ws.stats[(row * chunks + chunk) * G + t] = make_float2(mc, zc);
   }
+  const int nw = min(kMhChunk, W - w0);
+  MhRec<G>* dst = reinterpret_cast<MhRec<G>*>(ws.e) + row * (long)chunks * kMhChunk + w0;
+  for (int i = t; i < nw; i += 256) dst[i] = s_e[i];
 }
 
+// Pass 2: a workgroup combines the row's chunk statistics into each head's max
+// M and sum Z (one wave per head), the weight exp(chunk max - M) / Z of each
+// chunk its windows fall in, then for each window sums the G heads'
+// probabilities e * weight and pools them into block scores.
 template <typename Tag, int G>
 __global__ __launch_bounds__(256) void mhsel_pool_kernel(MhWs ws, float* __restrict__ scores,
                                                          int W, int nB, int n_vis,
                                                          const int* __restrict__ q_pos, int hkv, int T,
                                                          int chunks) {
   constexpr int NWIN = 4 * kMhPoolBlocks + 1;
+  constexpr int PER = (NWIN + 255) / 256;                    // windows per thread
+  constexpr int NCH = (NWIN + kMhChunk - 2) / kMhChunk + 1;  // chunks a run of NWIN windows can meet
+  static_assert(NCH <= kWave, "one lane per chunk weight");
   __shared__ float s_sum[NWIN];
-  __shared__ float s_m[G], s_iz[G];
-  const long row = blockIdx.y;
+  __shared__ float s_wt[NCH][G];
+  const long row = blockIdx.x;  // rows on the fast axis, as in pass 1
   if (q_pos != nullptr) n_vis = visible_windows(row_position(q_pos, row, hkv, 0, T), W);
-  const int beta0 = blockIdx.x * kMhPoolBlocks;
+  const int beta0 = blockIdx.y * kMhPoolBlocks;
   const int nblk = min(kMhPoolBlocks, nB - beta0);
   const int nwin = 4 * nblk + 1;
   const int wstart = 4 * beta0 - 1;
+  const int c0 = max(wstart, 0) / kMhChunk;
+  const int t = threadIdx.x;
 
-  // Combine the per-chunk (max, sum of exp) of each head: one wave per head,
-  // lanes read chunks in parallel.
+  // the records of this thread's windows go out first, beside the statistics
+  const MhRec<G>* src = reinterpret_cast<const MhRec<G>*>(ws.e) + row * (long)chunks * kMhChunk;
+  MhRec<G> rec[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int w = wstart + t + 256 * i;
+    if (t + 256 * i < nwin && w >= 0 && w < n_vis) rec[i] = src[w];
+  }
+  // each head's max M and sum Z over the row's chunks (one wave per head),
+  // then the weight exp(chunk max - M) / Z of the chunks these windows meet
   {
-    const int lane = threadIdx.x % kWave;
-    for (int g = threadIdx.x / kWave; g < G; g += (int)blockDim.x / kWave) {
-      float m = -INFINITY;
-      for (int c = lane; c < chunks; c += kWave) m = fmaxf(m, ws.stats[(row * chunks + c) * G + g].x);
-      m = wave_max(m);
+    const int lane = t % kWave;
+    for (int g = t / kWave; g < G; g += 256 / kWave) {
+      float mx = -INFINITY;
+      for (int cc = lane; cc < chunks; cc += kWave) mx = fmaxf(mx, ws.stats[(row * chunks + cc) * G + g].x);
+      mx = wave_max(mx);
       float z = 0.f;
-      for (int c = lane; c < chunks; c += kWave) {
-        const float2 st = ws.stats[(row * chunks + c) * G + g];
-        if (st.x != -INFINITY) z += st.y * fast_exp(st.x - m);
+      for (int cc = lane; cc < chunks; cc += kWave) {
+        const float2 st = ws.stats[(row * chunks + cc) * G + g];
+        if (st.x != -INFINITY) z += st.y * fast_exp(st.x - mx);
       }
       z = wave_sum(z);
-      if (lane == 0) {
-        s_m[g] = m;
-        s_iz[g] = 1.f / z;
+      const float iz = 1.f / z;
+      if (lane < NCH) {
+        const int cc = c0 + lane;
+        float wt = 0.f;
+        if (cc < chunks) {
+          const float mc = ws.stats[(row * chunks + cc) * G + g].x;
+          if (mc != -INFINITY) wt = fast_exp(mc - mx) * iz;
+        }
+        s_wt[lane][g] = wt;
       }
     }
   }
   __syncthreads();
-  for (int lw = threadIdx.x; lw < nwin; lw += blockDim.x) {
-    const int w = wstart + lw;
-    float S = -INFINITY;
-    if (w >= 0 && w < n_vis) {
-      S = 0.f;
 #pragma unroll
-      for (int g = 0; g < G; ++g)
-        S += fast_exp(ws.logits[(row * G + g) * W + w] - s_m[g]) * s_iz[g];
+  for (int i = 0; i < PER; ++i) {
+    const int lw = t + 256 * i;
+    const int w = wstart + lw;
+    if (lw < nwin) {
+      float S = -INFINITY;
+      if (w >= 0 && w < n_vis) {
+        const float* wt = s_wt[w / kMhChunk - c0];
+        S = 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) S = fmaf(from_f16_bits(rec[i].v[g]), wt[g], S);
+      }
+      s_sum[lw] = S;
     }
-    s_sum[lw] = S;
   }
   __syncthreads();
-  const int t = threadIdx.x;
   if (t < nblk) {
-    float m = s_sum[4 * t];
+    float mx = s_sum[4 * t];
 #pragma unroll
-    for (int j = 1; j < 5; ++j) m = fmaxf(m, s_sum[4 * t + j]);
-    scores[row * nB + beta0 + t] = m;
+    for (int j = 1; j < 5; ++j) mx = fmaxf(mx, s_sum[4 * t + j]);
+    scores[row * nB + beta0 + t] = mx;
   }
 }
 
@@ -257,10 +355,10 @@ static void launch_mh(const void* q, const void* kc, float* scores, const Select
                       int n_vis, hipStream_t s) {
   const int chunks = (d.W + kMhChunk - 1) / kMhChunk;
   const int rows = d.B * d.Hkv;
-  hipLaunchKernelGGL((mhsel_logits_kernel<Tag, G>), dim3(chunks, rows), dim3(256), 0, s,
+  hipLaunchKernelGGL((mhsel_logits_kernel<Tag, G>), dim3(rows, chunks), dim3(256), 0, s,
                      (const uint8_t*)q, (const uint8_t*)kc, w, d.W, n_vis, d.q_pos, d.Hkv, d.T, chunks, d.scale);
   hipLaunchKernelGGL((mhsel_pool_kernel<Tag, G>),
-                     dim3((d.nB + kMhPoolBlocks - 1) / kMhPoolBlocks, rows), dim3(256), 0, s, w,
+                     dim3(rows, (d.nB + kMhPoolBlocks - 1) / kMhPoolBlocks), dim3(256), 0, s, w,
                      scores, d.W, d.nB, n_vis, d.q_pos, d.Hkv, d.T, chunks);
 }
 
