@@ -14,8 +14,9 @@ of them).
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --workload decode|offload|prefill|pipeline   # one workload only
 
-Timing: W untimed steps, then exactly K steps captured in one HIP graph,
-replayed 5 times, each replay between two HIP events on the launch stream
+Timing: W untimed steps, then exactly K steps captured in one HIP graph
+(replayed three times untimed after capture: a new graph's first replays run
+slower), replayed 5 times, each replay between two HIP events on the launch stream
 with a device synchronisation on both sides (three untimed steps run between
 the synchronisation and the start event, so the timed steps do not begin on
 an idle GPU); ms_per_step is the median replay / K (the spread is reported).
@@ -76,7 +77,8 @@ def time_graph_stats(fn, n: int, repeats: int = REPEATS, prime: int = 3) -> dict
         for i in range(n):
             fn(i)
     stream = torch.cuda.current_stream()
-    g.replay()
+    for _ in range(3):  # the first replays of a new graph run slower: untimed
+        g.replay()
     torch.cuda.synchronize()
     out = []
     for _ in range(repeats):
