@@ -29,7 +29,13 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibility=
 # Per-source extras. Prefill attention keeps its matrix-core accumulators in
 # VGPRs (it normalises them on the vector ALUs); left to itself the register
 # allocator fills the AGPRs as well and spills.
-FILE_FLAGS = {"attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+FILE_FLAGS = {
+    "attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    # window maxima of matrix-core results: no NaN quieting before each max
+    "select_prefill.hip": ["-fno-honor-nans"],
+    # products stay in VGPRs for the softmax arithmetic that follows them
+    "mhsel_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 
 def hipcc() -> str:

@@ -23,6 +23,8 @@
 //
 // A wave owns 64 rows = (64 / G queries) x G heads of one tile; a workgroup
 // is G waves per tile, with 4 / G tiles per workgroup when G < 4.
+#include <type_traits>
+
 #include "prefill_lds.h"
 
 namespace sparda {
@@ -115,30 +117,51 @@ __global__ __launch_bounds__(MhLayout<G>::kThreads) void mhsel_prefill_kernel(
           for (int n = 0; n < 2; ++n)
             acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(qa[n][s]), acc[m][n], 0, 0, 0);
         }
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
+      // Per column: the chunk half's max, then the sum of exp2 relative to
+      // the new running max. Off the diagonal (every window visible to every
+      // query) and with a positive scale the max is taken on the raw products
+      // (the scaled max is the max of the scaled values) and the scale folds
+      // into the exponent's fma; the masked form is a separate body so that
+      // the common one carries no per-element selects.
+      auto column = [&](auto kMask, int n) {
         float cmax = -INFINITY;
+        if constexpr (decltype(kMask)::value) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+          for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float v = acc[m][n][r] * sl2;
-            if (masked) {
+            for (int r = 0; r < 16; ++r) {
               const int w = c0 + 64 * mh + 32 * m + 8 * (r >> 2) + 4 * half + (r & 3);
-              v = w < nv_col[n] ? v : -INFINITY;
+              const float v = w < nv_col[n] ? acc[m][n][r] * sl2 : -INFINITY;
+              acc[m][n][r] = v;
+              cmax = fmaxf(cmax, v);
             }
-            acc[m][n][r] = v;
-            cmax = fmaxf(cmax, v);
-          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) cmax = fmaxf(cmax, fmaxf(acc[0][n][r], acc[1][n][r]));
+          cmax *= sl2;
+        }
         const float mn = fmaxf(m_run[n], cmax);
         const float ms = mn == -INFINITY ? 0.f : mn;
         float z = z_run[n] * __builtin_amdgcn_exp2f(m_run[n] - ms);
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) z += __builtin_amdgcn_exp2f(acc[m][n][r] - ms);
+          for (int r = 0; r < 16; ++r) {
+            if constexpr (decltype(kMask)::value) {
+              z += __builtin_amdgcn_exp2f(acc[m][n][r] - ms);
+            } else {
+              z += __builtin_amdgcn_exp2f(fmaf(acc[m][n][r], sl2, -ms));
+            }
+          }
         z_run[n] = z;
         m_run[n] = mn;
+      };
+      if (masked || !(sl2 > 0.f)) {
+        column(std::true_type{}, 0);
+        column(std::true_type{}, 1);
+      } else {
+        column(std::false_type{}, 0);
+        column(std::false_type{}, 1);
       }
     }
     if (more) {
@@ -187,8 +210,10 @@ __global__ __launch_bounds__(MhLayout<G>::kThreads) void mhsel_prefill_kernel(
           for (int m = 0; m < 2; ++m)
             acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[m][s]), bfr, acc[m][n], 0, 0, 0);
         }
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
+      // Per column (window): the normalised group sum of each of the lane's
+      // queries, max over them; the visibility mask only near the diagonal,
+      // as a separate body.
+      auto column = [&](auto kMask, int n) {
         const int wl = 64 * nh + 32 * n + l32;  // window within the chunk
         const int w = c0 + wl;
         float best = -INFINITY;
@@ -198,11 +223,12 @@ __global__ __launch_bounds__(MhLayout<G>::kThreads) void mhsel_prefill_kernel(
           constexpr int kRegsPerQ = G >= 4 ? 4 : G;  // registers holding one query's heads
 #pragma unroll
           for (int r0 = 0; r0 < 16; r0 += kRegsPerQ) {
-            float sum = __builtin_amdgcn_exp2f(acc[m][n][r0] * sl2 - offr[m][r0]);
+            float sum = __builtin_amdgcn_exp2f(fmaf(acc[m][n][r0], sl2, -offr[m][r0]));
 #pragma unroll
-            for (int u = 1; u < kRegsPerQ; ++u) sum += __builtin_amdgcn_exp2f(acc[m][n][r0 + u] * sl2 - offr[m][r0 + u]);
+            for (int u = 1; u < kRegsPerQ; ++u)
+              sum += __builtin_amdgcn_exp2f(fmaf(acc[m][n][r0 + u], sl2, -offr[m][r0 + u]));
             if constexpr (G == 8) sum = sum32(sum);  // heads 4..7 sit in the other lane half
-            if (masked) {
+            if constexpr (decltype(kMask)::value) {
               const int rowc = 32 * m + 8 * (r0 >> 2) + 4 * half + (r0 & 3);
               sum = w < visible_windows(q_start + qbase + rowc / G, W) ? sum : -INFINITY;
             }
@@ -211,6 +237,13 @@ __global__ __launch_bounds__(MhLayout<G>::kThreads) void mhsel_prefill_kernel(
         }
         if constexpr (G != 8) best = max32(best);  // the other half holds other queries
         if (half == 0) s_cm[wave][wl] = best;
+      };
+      if (masked) {
+        column(std::true_type{}, 0);
+        column(std::true_type{}, 1);
+      } else {
+        column(std::false_type{}, 0);
+        column(std::false_type{}, 1);
       }
     }
     __syncthreads();

@@ -1,5 +1,5 @@
-// Staging of compressed-key chunks in LDS for the prefill selectors: 128
-// windows x 128 bf16 channels (32 KiB) per chunk, loaded straight from global
+// Staging of compressed-key chunks in LDS for the prefill selectors: 128 (or
+// 256) windows x 128 bf16 channels (32 or 64 KiB) per chunk, loaded straight from global
 // memory into LDS, with a granule swizzle so the matrix-core fragment reads of
 // 16 consecutive rows hit 16 different bank groups.
 #pragma once
@@ -21,17 +21,18 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_b
 // Byte offset of logical 16-byte granule g of row r inside a swizzled chunk.
 __device__ __forceinline__ int swz(int r, int g) { return r * kRowBytes + ((g ^ (r & 15)) << 4); }
 
-// Direct global->LDS load of rows [w0, w0 + 128) of one (b, h) row of K_cmp
+// Direct global->LDS load of rows [w0, w0 + CW) of one (b, h) row of K_cmp
 // into `dst` by a workgroup of NWAVES waves. Lane l of a wave instruction fills
 // LDS bytes [base + 16 l, base + 16 l + 16) from the global granule the swizzle
 // maps there. Rows at or beyond W read row W - 1 (callers mask them).
-template <int NWAVES>
+template <int NWAVES, int CW = kChunkW>
 __device__ __forceinline__ void load_chunk_lds(const uint8_t* __restrict__ kc_row, int W, int w0, uint8_t* dst) {
-  static_assert(kChunkBytes % (NWAVES * kWave * 16) == 0, "chunk must split evenly over the waves");
+  constexpr int kBytes = CW * kRowBytes;
+  static_assert(kBytes % (NWAVES * kWave * 16) == 0, "chunk must split evenly over the waves");
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
 #pragma unroll
-  for (int it = 0; it < kChunkBytes / (NWAVES * kWave * 16); ++it) {
+  for (int it = 0; it < kBytes / (NWAVES * kWave * 16); ++it) {
     const int pos = (it * NWAVES + wave) * kWave + lane;  // 16-byte slot in the chunk
     const int r = pos >> 4;
     const int g = (pos & 15) ^ (r & 15);
