@@ -33,8 +33,9 @@ FILE_FLAGS = {
     "attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     # window maxima of matrix-core results: no NaN quieting before each max
     "select_prefill.hip": ["-fno-honor-nans"],
-    # products stay in VGPRs for the softmax arithmetic that follows them
-    "mhsel_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    # products stay in VGPRs for the softmax arithmetic that follows them, and
+    # no NaN quieting before each max
+    "mhsel_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
 }
 
 
