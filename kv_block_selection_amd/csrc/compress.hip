@@ -16,7 +16,7 @@
 
 namespace sparda {
 
-constexpr int kCompressChunk = 32;  // windows per lane group
+constexpr int kCompressChunk = 64;  // windows per lane group (64: 4% faster than 32 at 128K, 8: 12% slower)
 
 template <typename Tag>
 __global__ __launch_bounds__(256) void compress_kernel(const uint8_t* __restrict__ k,
