@@ -835,6 +835,7 @@ def bench_offload_cfg(args) -> dict:
     step(0)
     torch.cuda.synchronize()
     par = parity_offload(w, kbs, l0, l1, st)
+    cpu_loop = bench_cpu_in_loop_gather(w, l1, st, stream)
     serial = sum(parts.values())
     # the gather waits only for layer 1's selection; layer 0's selection and
     # attention can hide behind it
@@ -854,11 +855,65 @@ def bench_offload_cfg(args) -> dict:
            "overlap_note": "hideable = layer 0 selection (half of both selections) + layer 0 attention",
            "workgroup_sweep": sweep,
            "cached_gather": cached,
+           "cpu_in_the_loop_gather": cpu_loop,
            "parity": par}
     del l0, l1, st, host
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return out
+
+
+def bench_cpu_in_loop_gather(w, l1, st, stream, n_rows: int = 64) -> dict:
+    """The gather with the CPU in the loop, for contrast with the device-side
+    gather: the host copies layer 1's selected indices back (a sync on the
+    step's path) and issues one hipMemcpyAsync per selected K and V block from
+    pinned host memory into the staging slots. Timed over n_rows (sequence, KV
+    head) rows and scaled to the step's B * Hkv rows (the cost is per copy);
+    the staged bytes of those rows are checked against the device gather's."""
+    import ctypes
+    import os
+    import time
+    import torch
+    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    hip.hipMemcpyAsync.restype = ctypes.c_int
+    h2d = 1  # hipMemcpyHostToDevice
+    blk = w.block * w.d * 2
+    rows = [(r // w.Hkv, r % w.Hkv) for r in range(0, w.B * w.Hkv, (w.B * w.Hkv) // n_rows)][:n_rows]
+    hk, hv = l1["host_K"], l1["host_V"]
+    ref_k = torch.stack([st.stage_k[b, h].clone() for b, h in rows])
+    ref_v = torch.stack([st.stage_v[b, h].clone() for b, h in rows])
+    for b, h in rows:
+        st.stage_k[b, h].zero_()
+        st.stage_v[b, h].zero_()
+    torch.cuda.synchronize()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    times = []
+    for rep in range(3):
+        t0 = time.perf_counter()
+        idx = st.idx1.view(w.B, w.Hkv, w.k).cpu()  # device -> host, waits for the selection
+        for b, h in rows:
+            for j in range(w.k):
+                bi = int(idx[b, h, j])
+                if bi < 0:
+                    continue
+                for src, dst in ((hk, st.stage_k), (hv, st.stage_v)):
+                    rc = hip.hipMemcpyAsync(dst[b, h, j].data_ptr(), src[b, h, bi * w.block].data_ptr(), blk, h2d,
+                                            sptr)
+                    if rc != 0:
+                        raise RuntimeError(f"hipMemcpyAsync failed ({rc})")
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    same = all(torch.equal(st.stage_k[b, h], ref_k[i]) and torch.equal(st.stage_v[b, h], ref_v[i])
+               for i, (b, h) in enumerate(rows))
+    t = sorted(times)[1]
+    copies = 2 * w.k * len(rows)
+    scale = (w.B * w.Hkv) / len(rows)
+    return {"rows_timed": len(rows), "copies_timed": copies, "ms_rows_timed": round(t * 1e3, 3),
+            "ms_per_step_scaled": round(t * 1e3 * scale, 2), "us_per_copy": round(t * 1e6 / copies, 2),
+            "GBps": round(copies * blk / t / 1e9, 2), "staged_bytes_match_device_gather": bool(same),
+            "how": "D2H of the indices, then one hipMemcpyAsync per selected 16 KiB K or V block from pinned "
+                   "host memory, issued from a Python loop through ctypes (median of 3)"}
 
 
 def parity_offload(w, kbs, l0, l1, st, n_rows: int = 32) -> dict:
