@@ -133,8 +133,9 @@ struct alignas(2 * G) MhRec {
 // the reduce-scatter each lane holds the logits of GR heads (lanes that share a
 // head hold the same bits) and keeps them in registers: the chunk's max per
 // head (lane, then the wave's slots by lane-pair swaps, then the four waves),
-// the exponentials and their sum (the same order), then the records go out
-// through LDS so that consecutive threads store consecutive windows.
+// the exponentials and their sum (the same order). With four lanes per head
+// each lane stores its exponentials straight to the records; the other
+// layouts stage a chunk's records in LDS and store them whole.
 template <typename Tag, int G>
 __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __restrict__ q,
                                                            const uint8_t* __restrict__ kc, MhWs ws,
@@ -145,8 +146,9 @@ __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __rest
   constexpr int GR = G < 4 ? 1 : G / 4;              // heads a lane holds after the reduce-scatter
   constexpr int HL = G >= 4 ? 4 : (G == 2 ? 8 : 16);  // lanes that share a head
   static_assert(kMhChunk % R::SLOTS == 0, "whole passes of the 256 threads");
+  constexpr bool kQuad = G >= 4 && ITER % 4 == 0;  // exponentials split over the four lanes of a head
   __shared__ float red_m[4][G], red_z[4][G];
-  __shared__ MhRec<G> s_e[kMhChunk];
+  __shared__ MhRec<G> s_e[kQuad ? 1 : kMhChunk];  // record staging of the other layouts
 
   // rows on the fast axis: a row's chunks run on one XCD, so its records
   // meet in that XCD's L2 (and pass 2 of the row reads them there)
@@ -169,6 +171,7 @@ __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __rest
 #pragma unroll
   for (int s = 0; s < G; ++s) qv[s] = load16(q + (row * G + slot_head<G>(s, c)) * R::RB + lane * 16);
   const uint8_t* base = kc + row * (long)W * R::RB + lane * 16;
+  MhRec<G>* rec_row = reinterpret_cast<MhRec<G>*>(ws.e) + row * (long)chunks * kMhChunk;
 
   u32x4 kv[ITER];
 #pragma unroll
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __rest
     m[gr] = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
     z[gr] = 0.f;
   }
-  if constexpr (G >= 4 && ITER % 4 == 0) {
+  if constexpr (kQuad) {
     // the four lanes that share a head split its windows: lane j of the quad
     // takes iterations j, j + 4, ..., so each exponential is computed once;
     // the quad's sums then meet by a butterfly (the same bits in all four)
@@ -229,7 +232,9 @@ __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __rest
                                                                                    : lg[4 * k + 3][gr];
         const float e = x == -INFINITY ? 0.f : fast_exp(x - m[gr]);
         z[gr] += e;
-        if (lane < 16) s_e[lw].v[4 * gr + hsub] = to_f16_bits(e);
+        // straight to the row's records, 2 bytes a lane (an LDS staging for
+        // whole-record stores measured 0.6 us slower at 128K)
+        if (lane < 16 && w0 + lw < W) rec_row[w0 + lw].v[4 * gr + hsub] = to_f16_bits(e);
       }
     }
 #pragma unroll
@@ -262,9 +267,10 @@ __global__ __launch_bounds__(256) void mhsel_logits_kernel(const uint8_t* __rest
     const float zc = ((red_z[0][t] + red_z[1][t]) + red_z[2][t]) + red_z[3][t];
     ws.stats[(row * chunks + chunk) * G + t] = make_float2(mc, zc);
   }
-  const int nw = min(kMhChunk, W - w0);
-  MhRec<G>* dst = reinterpret_cast<MhRec<G>*>(ws.e) + row * (long)chunks * kMhChunk + w0;
-  for (int i = t; i < nw; i += 256) dst[i] = s_e[i];
+  if constexpr (!kQuad) {
+    const int nw = min(kMhChunk, W - w0);
+    for (int i = t; i < nw; i += 256) rec_row[w0 + i] = s_e[i];
+  }
 }
 
 // Pass 2: a workgroup combines the row's chunk statistics into each head's max
