@@ -59,6 +59,11 @@ __global__ __launch_bounds__(256) void token_scores_kernel(const uint8_t* __rest
 
 __global__ __launch_bounds__(kLongThreads) void topk_long_kernel(const float* __restrict__ scores,
                                                                  int32_t* __restrict__ idx, int n, int k) {
+  // 16 copies of each digit's counter, lane l of a wave counting into copy
+  // l % 16: the lanes of one atomic instruction that meet the same digit
+  // (the top byte of similar scores is often shared) then spread over 16
+  // addresses instead of queueing on one
+  __shared__ int hist16[256 * 16];
   __shared__ int hist[256];
   __shared__ int s_tot[kLongThreads / kWave];
   __shared__ int s_digit, s_above, s_ncand;
@@ -77,9 +82,10 @@ __global__ __launch_bounds__(kLongThreads) void topk_long_kernel(const float* __
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    if (t < 256) hist[t] = 0;
+    for (int i = t; i < 256 * 16; i += kLongThreads) hist16[i] = 0;
     __syncthreads();
-    // kLongEPT independent loads per thread go out before their atomics
+    // kLongEPT independent loads per thread go out before their atomics (16
+    // or 64 measured the same: the atomics, not the loads, set the pace)
     for (long c0 = 0; c0 < n; c0 += (long)kLongThreads * kLongEPT) {
       float x[kLongEPT];
 #pragma unroll
@@ -90,8 +96,15 @@ __global__ __launch_bounds__(kLongThreads) void topk_long_kernel(const float* __
 #pragma unroll
       for (int j = 0; j < kLongEPT; ++j) {
         const uint32_t key = order_key(x[j]);
-        if (key != 0u && (key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+        if (key != 0u && (key & hi_mask) == prefix) atomicAdd(&hist16[((key >> shift) & 255u) * 16 + (lane & 15)], 1);
       }
+    }
+    __syncthreads();
+    if (t < 256) {
+      int h = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) h += hist16[t * 16 + ((j + t) & 15)];  // rotated: distinct banks per lane
+      hist[t] = h;
     }
     __syncthreads();
     if (wid == 0) {
