@@ -34,6 +34,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace sparda {
 
@@ -67,9 +68,16 @@ __device__ __forceinline__ u32x4 vt_frag(const uint8_t* vblk, int kb, int dbase,
   return u32x4{ua.x, ua.y, ub.x, ub.y};
 }
 
+// A block's 64 rows x 16 granules = 1024 16-byte slots, NT threads filling
+// one slot each per load: this lane's source offsets within the block (the
+// same for every block), in the K or the V swizzle.
 template <int NT, bool kV>
-__device__ __forceinline__ void load_block_lds(const uint8_t* __restrict__ src_block, uint8_t* dst) {
-  // 64 rows x 16 granules = 1024 slots; NT threads, one 16-byte slot each per step
+struct BlockOffsets {
+  uint32_t off[1024 / NT];
+};
+template <int NT, bool kV>
+__device__ __forceinline__ BlockOffsets<NT, kV> block_lds_offsets() {
+  BlockOffsets<NT, kV> o;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
 #pragma unroll
@@ -77,8 +85,16 @@ __device__ __forceinline__ void load_block_lds(const uint8_t* __restrict__ src_b
     const int pos = (it * (NT / kWave) + wave) * kWave + lane;
     const int r = pos >> 4;
     const int g = kV ? v_swz_granule(r, pos & 15) : (pos & 15) ^ (r & 15);
-    dma16(src_block + r * kRowB + g * 16, dst + (it * (NT / kWave) + wave) * kWave * 16);
+    o.off[it] = (uint32_t)(r * kRowB + g * 16);
   }
+  return o;
+}
+template <int NT, bool kV>
+__device__ __forceinline__ void load_block_lds(const uint8_t* __restrict__ src_block, const BlockOffsets<NT, kV>& o,
+                                               uint8_t* dst) {
+  const int wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int it = 0; it < 1024 / NT; ++it) dma16_sv(src_block, o.off[it], dst + (it * (NT / kWave) + wave) * kWave * 16);
 }
 
 }  // namespace
@@ -133,11 +149,13 @@ __global__ __launch_bounds__(128 * HPW) void attn_prefill_kernel(
     while (j < k && !usable(j)) ++j;
     return j;
   };
+  const BlockOffsets<NT, false> k_offs = block_lds_offsets<NT, false>();
+  const BlockOffsets<NT, true> v_offs = block_lds_offsets<NT, true>();
   auto load_k = [&](int j, uint8_t* dst) {
-    load_block_lds<NT, false>(kbuf + (row * (long)T + (long)sel_at(j) * kBlock) * kRowB, dst);
+    load_block_lds<NT, false>(kbuf + (row * (long)T + (long)sel_at(j) * kBlock) * kRowB, k_offs, dst);
   };
   auto load_v = [&](int j, uint8_t* dst) {
-    load_block_lds<NT, true>(vbuf + (row * (long)T + (long)sel_at(j) * kBlock) * kRowB, dst);
+    load_block_lds<NT, true>(vbuf + (row * (long)T + (long)sel_at(j) * kBlock) * kRowB, v_offs, dst);
   };
   // S^T for key half h (keys 32h .. 32h+31 of the block) x this wave's queries;
   // two accumulators (even and odd k-steps) keep two MFMA chains in flight

@@ -6,6 +6,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace sparda {
 
@@ -40,6 +41,37 @@ __device__ __forceinline__ void load_chunk_lds(const uint8_t* __restrict__ kc_ro
     const uint8_t* src = kc_row + (long)w * kRowBytes + g * 16;
     dma16(src, dst + (it * NWAVES + wave) * kWave * 16);
   }
+}
+
+// The same load of a whole chunk (rows w0 .. w0 + CW - 1 all below W) from a
+// scalar base: off[it] holds this lane's offset within the chunk for load
+// `it`, from chunk_lds_offsets.
+template <int NWAVES, int CW>
+struct ChunkOffsets {
+  static constexpr int kLoads = CW * kRowBytes / (NWAVES * kWave * 16);
+  uint32_t off[kLoads];
+};
+template <int NWAVES, int CW>
+__device__ __forceinline__ ChunkOffsets<NWAVES, CW> chunk_lds_offsets() {
+  ChunkOffsets<NWAVES, CW> o;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int it = 0; it < ChunkOffsets<NWAVES, CW>::kLoads; ++it) {
+    const int pos = (it * NWAVES + wave) * kWave + lane;
+    const int r = pos >> 4;
+    o.off[it] = (uint32_t)(r * kRowBytes + (((pos & 15) ^ (r & 15)) << 4));
+  }
+  return o;
+}
+template <int NWAVES, int CW>
+__device__ __forceinline__ void load_full_chunk_lds(const uint8_t* __restrict__ kc_row, int w0,
+                                                    const ChunkOffsets<NWAVES, CW>& o, uint8_t* dst) {
+  const int wave = threadIdx.x / kWave;
+  const uint8_t* base = kc_row + (long)w0 * kRowBytes;
+#pragma unroll
+  for (int it = 0; it < ChunkOffsets<NWAVES, CW>::kLoads; ++it)
+    dma16_sv(base, o.off[it], dst + (it * NWAVES + wave) * kWave * 16);
 }
 
 // Fragment of a chunk row for a 32x32x16 MFMA operand whose rows (A) or columns

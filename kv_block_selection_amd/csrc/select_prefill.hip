@@ -68,8 +68,17 @@ __global__ __launch_bounds__(256 * TPW) void fsel_prefill_kernel(const uint8_t* 
   const int vis_min = visible_windows(q_start + min(q0, Tq - 1), W);
 
   const int nchunks = (W + CW - 1) / CW;
+  const ChunkOffsets<NWAVES, CW> offs = chunk_lds_offsets<NWAVES, CW>();
+  // whole chunks from a scalar base, the last partial one with clamped rows
+  auto load = [&](int c, uint8_t* dst) {
+    if ((c + 1) * CW <= W) {
+      load_full_chunk_lds<NWAVES, CW>(kc_row, c * CW, offs, dst);
+    } else {
+      load_chunk_lds<NWAVES, CW>(kc_row, W, c * CW, dst);
+    }
+  };
   if (threadIdx.x < TPW) s_cmax[0][threadIdx.x][0] = -INFINITY;
-  load_chunk_lds<NWAVES, CW>(kc_row, W, 0, s_kc[0]);
+  load(0, s_kc[0]);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
   // One barrier per chunk. Iteration c issues chunk c + 1 into the buffer
@@ -80,7 +89,7 @@ __global__ __launch_bounds__(256 * TPW) void fsel_prefill_kernel(const uint8_t* 
   // maxima are double-buffered so those writes go to the other half.
   for (int c = 0; c < nchunks; ++c) {
     const int bc = c & 1;
-    if (c + 1 < nchunks) load_chunk_lds<NWAVES, CW>(kc_row, W, (c + 1) * CW, s_kc[bc ^ 1]);
+    if (c + 1 < nchunks) load(c + 1, s_kc[bc ^ 1]);
     const uint8_t* tileb = s_kc[bc];
     f32x16 acc[2][2] = {};  // [query half m][window half n]
 #pragma unroll
