@@ -368,8 +368,11 @@ __device__ __forceinline__ void attn_decode_body(
   }
 }
 
+// fp32 rows hold twice the bytes in flight: one wave per SIMD, so the
+// registers past 256 spill to AGPRs instead of scratch memory
 template <typename Tag, int G, int WPG, int NPT>
-__global__ __launch_bounds__(64 * WPG) __attribute__((amdgpu_waves_per_eu(SPARDA_ATTN_WAVES_PER_EU)))
+__global__ __launch_bounds__(64 * WPG)
+__attribute__((amdgpu_waves_per_eu(DT<Tag>::kBytes == 2 ? SPARDA_ATTN_WAVES_PER_EU : 1)))
 void attn_decode_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ kbuf, const uint8_t* __restrict__ vbuf,
     const int32_t* __restrict__ idx, int32_t* __restrict__ idx_out, const float* __restrict__ scores,
