@@ -54,9 +54,12 @@ class LookaheadStep:
     """
 
     def __init__(self, B: int, Hq: int, Hkv: int, T: int, k: int, dtype, device="cuda",
-                 num_workgroups: int = 0, cache_slots: int = 0):
+                 num_workgroups: int = 0, cache_slots: int = 0, markers: bool = False):
         import torch
         self.B, self.Hq, self.Hkv, self.T, self.k = B, Hq, Hkv, T, k
+        # markers: host-side ranges around each phase's enqueue (roctx through
+        # torch.cuda.nvtx; rocprofv3 --marker-trace shows them)
+        self.markers = markers
         self.device = torch.device(device)
         self.num_workgroups = num_workgroups
         nB = T // BLOCK
@@ -121,19 +124,32 @@ class LookaheadStep:
             block_sparse_attn(layer1["Q"], self.stage_k, self.stage_v, self.idx1, T, q, kv_mode=KV_STAGING,
                               out=self.out1, ws=self.ws, stream=main)
 
+    def _phase(self, name: str):
+        """A marker range around one phase's enqueue (no-op unless ``markers``)."""
+        import contextlib
+        if not self.markers:
+            return contextlib.nullcontext()
+        import torch
+        return torch.cuda.nvtx.range(name)
+
     def step(self, layer0: dict, layer1: dict, stream=None):
         """Enqueue one step; returns (out0, out1, idx0, idx1), valid once ``stream`` reaches this point."""
         import torch
         main = stream if stream is not None else torch.cuda.current_stream(self.device)
         T, q = self.T, self.T - 1
-        self.select_next(layer0, layer1, main)
-        self.e_idx1.record(main)
-        self.side.wait_event(self.e_idx1)
-        self.prefetch(layer1)
-        self.e_stage.record(self.side)
-        self.select_self(layer0, main)
-        block_sparse_attn(layer0["Q"], layer0["K"], layer0["V"], self.idx0, T, q, out=self.out0, ws=self.ws,
-                          stream=main)
-        main.wait_event(self.e_stage)
-        self.attend_next(layer1, main)
+        with self._phase("select_layer1"):
+            self.select_next(layer0, layer1, main)
+            self.e_idx1.record(main)
+        with self._phase("prefetch_layer1"):
+            self.side.wait_event(self.e_idx1)
+            self.prefetch(layer1)
+            self.e_stage.record(self.side)
+        with self._phase("select_layer0"):
+            self.select_self(layer0, main)
+        with self._phase("attend_layer0"):
+            block_sparse_attn(layer0["Q"], layer0["K"], layer0["V"], self.idx0, T, q, out=self.out0, ws=self.ws,
+                              stream=main)
+        with self._phase("attend_layer1"):
+            main.wait_event(self.e_stage)
+            self.attend_next(layer1, main)
         return self.out0, self.out1, self.idx0, self.idx1

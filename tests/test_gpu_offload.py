@@ -58,14 +58,16 @@ def check_step(w, r0, r1, got):
     say(f"  banded rows {banded}, attention err {e0:.2e} / {e1:.2e}")
 
 
-def test_lookahead_step_parity_back_to_back(gpu):
+@pytest.mark.parametrize("markers", [False, True])
+def test_lookahead_step_parity_back_to_back(gpu, markers):
     """Three steps enqueued without a host sync, alternating two input sets, so
     that a missing wait between the side stream's gather and the main stream's
-    attention (or the next step's gather) would mix the sets' data."""
+    attention (or the next step's gather) would mix the sets' data; with and
+    without the phase marker ranges."""
     from kv_block_selection_amd.lookahead import LookaheadStep
     wa, wb = small(seed=3), small(seed=103)
     sets = [offload_layers(w, gpu.compress_keys, DEV) for w in (wa, wb)]
-    st = LookaheadStep(wa.B, wa.Hq, wa.Hkv, wa.T, wa.k, torch.bfloat16, DEV)
+    st = LookaheadStep(wa.B, wa.Hq, wa.Hkv, wa.T, wa.k, torch.bfloat16, DEV, markers=markers)
     st.stage_k.fill_(float("nan"))  # poisoned staging must not matter
     st.stage_v.fill_(float("nan"))
     order = [0, 1, 0]
