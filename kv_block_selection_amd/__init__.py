@@ -12,7 +12,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparda.so")
+# SPARDA_LIB names another build of the same library (the host-sanitized one
+# of the CPU tests); by default the in-tree build
+LIB_PATH = os.environ.get("SPARDA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparda.so")
 
 SPARDA_OK = 0
 SPARDA_F32 = 0

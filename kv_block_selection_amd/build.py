@@ -77,6 +77,46 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the ABI layer
+# (argument validation, workspace sizing, messages), for a CPU test: api.cpp is
+# compiled with host instrumentation only (each -fsanitize= behind -Xarch_host;
+# device code is untouched) and linked with the regular build's other objects.
+# Load it with the sanitizer runtime preloaded (sanitizer_runtime()).
+SAN_BUILD = os.path.join(ROOT, "_build", "host_sanitized")
+SAN_LIB = os.path.join(SAN_BUILD, "libsparda_host_sanitized.so")
+HOST_SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                  "-shared-libasan"]
+
+
+def sanitizer_runtime() -> str:
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the ASan runtime of the ROCm clang was not found")
+    return path
+
+
+def build_host_sanitized() -> str:
+    """libsparda with api.cpp built under host ASan + UBSan; needs build() first."""
+    os.makedirs(SAN_BUILD, exist_ok=True)
+    api = os.path.join(CSRC, "api.cpp")
+    obj = os.path.join(SAN_BUILD, "api.cpp.o")
+    cmd = [hipcc(), "-x", "hip", *COMMON, *DEVICE_FLAGS, *HOST_SAN_FLAGS, "-c", api, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {api}:\n{r.stderr}")
+    others = [os.path.join(BUILD, os.path.basename(src) + ".o") for src in sources() if not src.endswith("api.cpp")]
+    missing = [o for o in others if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"run build() first: missing {missing[0]}")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *HOST_SAN_FLAGS, "-o", SAN_LIB, obj, *others]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)
