@@ -1269,6 +1269,10 @@ def main() -> int:
                          "as extra keys; decode: the headline only; offload: the batch-64 two-layer step with "
                          "lookahead prefetch from pinned host memory; prefill: a 4096-query chunk at 128K; "
                          "pipeline: a four-layer offloaded stack")
+    ap.add_argument("--config", type=int, choices=(1, 2, 3, 4, 5), default=None,
+                    help="one benchmark configuration alone: 1 tiny fp32 decode, 2 single-sequence 32K decode, "
+                         "3 batch-16 128K decode (the headline; as --workload decode), 4 offloaded batch-64 decode "
+                         "(as --workload offload), 5 chunked prefill (as --workload prefill)")
     ap.add_argument("--decoupled-layers", action="store_true",
                     help="decode: also time consecutive layers with the next layer's selection on a second stream "
                          "beside this layer's attention, against the same layers on one stream")
@@ -1283,6 +1287,21 @@ def main() -> int:
     if args.steps < 1:
         print("--steps must be at least 1", file=sys.stderr)
         return 2
+    if args.config in (3, 4, 5):
+        args.workload = {3: "decode", 4: "offload", 5: "prefill"}[args.config]
+    elif args.config in (1, 2):
+        import torch
+        import kv_block_selection_amd as kbs
+        from synth import workloads as wl
+        kbs.load()
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        w = wl.C1_TINY if args.config == 1 else wl.C2_DECODE_32K
+        r = bench_small_decode(kbs, w, dev, args.steps, args.warmup)
+        print(json.dumps(_line("decode steps/s/layer (select+sparse attn)", r["steps_per_s_per_layer"],
+                               "steps/s/layer", round(r["us_per_step"]["median"] / 1e3, 5), r["steps"], args,
+                               r["workload"], r)), flush=True)
+        return 0
     # the all-cores oracle's worker processes start before anything touches the GPU
     pool, n_workers = (None, 0)
     if args.workload in ("all", "decode") and not args.no_cpu_baseline:
