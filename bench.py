@@ -323,6 +323,22 @@ def pmc_traffic(kernel_files, summary: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+def calibration_copy(dev) -> None:
+    """A plain 1 GiB device copy, ten times: the known-size reference for the
+    profiler's FETCH_SIZE / WRITE_SIZE counters in the same run."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+PREFILL_ATTN_SOURCES = ["kv_block_selection_amd/csrc/attn_prefill.hip", "kv_block_selection_amd/csrc/lds_dma.h",
+                        "kv_block_selection_amd/csrc/launch.h",
+                        "kv_block_selection_amd/csrc/common.h"]
+
 LAYER_SOURCES = ["kv_block_selection_amd/csrc/attn_decode.hip", "kv_block_selection_amd/csrc/topk_row.h",
                  "kv_block_selection_amd/csrc/select_row.h", "kv_block_selection_amd/csrc/reduce16.h",
                  "kv_block_selection_amd/csrc/common.h"]
@@ -609,13 +625,8 @@ def bench_decode(args, pool=None, n_workers: int = 0) -> dict:
     if decoupled is not None:
         result["decoupled_layers"] = decoupled
     if args.calibration_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(10):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+        calibration_copy(dev)
         result["calibration_copy_bytes"] = 1 << 30
-        del src, dst
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: the oracle on the step's rows, 1 thread and {n_workers} worker processes")
         result["cpu_baseline"] = cpu_baseline(w, sets[0], pool, n_workers)
@@ -1022,6 +1033,11 @@ def bench_prefill_cfg(args) -> dict:
     roof = {k: {"bound": "mfma", "kernel": k, "achieved": round(tf[k], 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tf[k] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
             for k in fl}
+    # HBM bytes of the attention launch from the committed PMC record (null
+    # when its source changed since the counters were taken)
+    roof["attention"]["traffic"] = pmc_traffic(PREFILL_ATTN_SOURCES, "prefill_attn_c5_traffic.json")
+    if args.calibration_copy:
+        calibration_copy(dev)
     par = parity_prefill(w, s, scores, mh, idx, out)
     del s
     torch.cuda.synchronize()
