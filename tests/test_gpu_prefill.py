@@ -60,6 +60,28 @@ def test_select_multihead_prefill_parity(gpu, w):
     say(f"  worst rel err {worst:.2e}, banded rows {banded}")
 
 
+@pytest.mark.parametrize("scale", [-0.07, 0.0, 0.3])
+def test_prefill_selectors_any_scale(gpu, scale):
+    """Both prefill selectors with a negative, a zero and a large scale (the
+    Forecast kernel takes the max of the raw products only when the scale is
+    positive; at zero every visible window ties), over 319 windows: one whole
+    256-window chunk from the scalar-base loads and a partial one."""
+    w = prefill(64 * 80, 256, k=9, seed=71)
+    say("prefill selectors, scale", scale)
+    Q, F, K = gen(w, "Q"), gen(w, "F"), gen(w, "K")
+    Kc = gpu.compress_keys(K)
+    s = gpu.select_forecast(F, Kc, w.T, w.q_start, scale=scale)
+    m = gpu.select_multihead(Q, Kc, w.T, w.q_start, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.select_forecast(parity.to_f64(F), parity.to_f64(Kc), w.T, w.q_start, scale)
+    worst = parity.check_scores(parity.to_f64(s), ref)
+    parity.check_topk_band(gpu.topk_blocks(s, w.k).cpu().numpy(), ref, w.k)
+    ref_m = oracle.select_multihead(parity.to_f64(Q), parity.to_f64(Kc), w.T, w.q_start, scale)
+    worst_m = parity.check_scores(parity.to_f64(m), ref_m)
+    parity.check_topk_band(gpu.topk_blocks(m, w.k).cpu().numpy(), ref_m, w.k)
+    say(f"  worst rel err {worst:.2e} / {worst_m:.2e}")
+
+
 @pytest.mark.parametrize("G", [1, 2, 8])
 def test_select_multihead_prefill_groups(gpu, G):
     """Every group size; 5 tiles, so the workgroups that hold several tiles
