@@ -129,6 +129,30 @@ def test_select_multihead_workloads(gpu, w):
     parity.check_topk_band(gpu.topk_blocks(s, w.k).cpu().numpy(), ref, w.k)
 
 
+@pytest.mark.parametrize("scale", [-0.07, 0.0])
+def test_decode_path_any_scale(gpu, scale):
+    """Both decode selectors, then the fused top-k + attention, with a
+    negative and a zero scale (at zero every visible window ties and the
+    attention weights are uniform over the selected keys)."""
+    w = small("bf16", B=3, T=64 * 40, k=7)
+    say("decode path, scale", scale)
+    F, K, Q, V = gen(w, "F"), gen(w, "K"), gen(w, "Q"), gen(w, "V")
+    Kc = gpu.compress_keys(K)
+    s = gpu.select_forecast(F, Kc, w.T, w.q_start, scale=scale)
+    m = gpu.select_multihead(Q, Kc, w.T, w.q_start, scale=scale)
+    idx, out = gpu.topk_block_sparse_attn(s, Q, K, V, w.k, w.T, w.q_start, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.select_forecast(parity.to_f64(F), parity.to_f64(Kc), w.T, w.q_start, scale)
+    parity.check_scores(parity.to_f64(s), ref)
+    parity.check_topk_band(idx.cpu().numpy(), ref, w.k)
+    ref_m = oracle.select_multihead(parity.to_f64(Q), parity.to_f64(Kc), w.T, w.q_start, scale)
+    parity.check_scores(parity.to_f64(m), ref_m)
+    ref_o = oracle.block_sparse_attention(parity.to_f64(Q), parity.to_f64(K), parity.to_f64(V), idx.cpu().numpy(),
+                                          w.q_start, scale)
+    err = parity.check_attention(parity.to_f64(out), ref_o, parity.ATTN_ATOL_BF16)
+    say(f"  attention err {err:.2e}")
+
+
 # ------------------------------------------------------------------ top-k ---
 @pytest.mark.parametrize("nB", [1, 7, 64, 255, 256, 257, 512, 2048, 4097, 8192])
 def test_topk_exact(gpu, nB):
