@@ -1,23 +1,102 @@
 // Step 1: mean-pooled key windows, kernel 32 and stride 16 (techwalker.com
 // article on SparDA, section 四: compressed-key windows used at inference).
 //
-// HBM-bound stream: read K once, write K_cmp (1/16 of K). The same kernel
-// serves a window range [w_begin, w_end) of a cache whose rows hold T_cap
+// HBM-bound stream: read K once, write K_cmp (1/16 of K). The same kernels
+// serve a window range [w_begin, w_end) of a cache whose rows hold T_cap
 // tokens and W_cap windows (incremental compression while decoding: a
-// sequence that has grown past 16 w + 31 tokens completes window w). A 16-lane group
-// (bf16; 32 lanes for fp32) owns one (row, window chunk) and walks its tokens
-// in order; each lane keeps 8 (or 4) channels. Each 16-token half-window sum is
-// formed once and shared by the two windows that contain it. Per load
-// instruction a wave reads 4 (bf16) or 2 (fp32) whole 256-byte token rows:
-// 1 KiB contiguous per row group, fully used.
+// sequence that has grown past 16 w + 31 tokens completes window w). Each
+// 16-token half-window sum is formed once, in token order (the bits of
+// half_window_sum, which the append path uses too), and shared by the two
+// windows that contain it. bf16: one wave per (row, run of windows), four
+// consecutive halves per step, 16 KiB contiguous; fp32: a 32-lane group per
+// (row, run of windows), 4 channels a lane, walking its tokens in order.
 #include "common.h"
 #include "launch.h"
 #include "window_mean.h"
 
 namespace sparda {
 
-constexpr int kCompressChunk = 64;  // windows per lane group (64: 4% faster than 32 at 128K, 8: 12% slower)
+// windows per wave (bf16) or lane group (fp32); bf16 at 128K: 32 853 µs, 64
+// 829, 128 815, 256 816
+constexpr int kCompressChunk = 128;
 
+// bf16, one wave per (row, run of kCompressChunk windows): a step takes four
+// consecutive half windows, lane group g (16 lanes, 8 channels each) summing
+// half 4 s + g over its 16 tokens in token order, so the wave's 16 load
+// instructions of a step cover 16 KiB contiguous and each half's sum has the
+// bits of half_window_sum. Window 4 s + g then adds the half of lane group
+// g + 1 (the next step's group 0 for g = 3), fetched across lanes.
+__global__ __launch_bounds__(256) void compress_wave_kernel(const uint8_t* __restrict__ k, uint8_t* __restrict__ kc,
+                                                            int rows, int T, int W, int w_begin, int w_end,
+                                                            int chunks_per_row) {
+  constexpr int RB = kHeadDim * 2;  // bf16 row bytes
+  const int lane = threadIdx.x % kWave;
+  const int c16 = lane & 15;  // 16-byte slice of a row: channels 8 c16 .. + 7
+  const int g = lane >> 4;    // lane group: half 4 s + g of step s
+  const long item = (long)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (item >= (long)rows * chunks_per_row) return;
+  const long row = item / chunks_per_row;
+  const int w0 = w_begin + (int)(item % chunks_per_row) * kCompressChunk;
+  const int w1 = min(w_end, w0 + kCompressChunk);  // windows [w0, w1); halves w0 .. w1
+  const uint8_t* src = k + row * (long)T * RB + c16 * 16;
+  uint8_t* dst = kc + row * (long)W * RB + c16 * 16;
+
+  // the 16 token rows of half h (rows past the last half needed are not read)
+  auto load_half = [&](int h, u32x4 (&v)[kStride]) {
+    const bool ok = h <= w1;
+#pragma unroll
+    for (int t = 0; t < kStride; ++t) v[t] = ok ? load16_nt(src + (long)(h * kStride + t) * RB) : u32x4{0, 0, 0, 0};
+  };
+  auto half_sum = [&](const u32x4 (&v)[kStride], float* acc) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int t = 0; t < kStride; ++t) {
+      float x[8];
+      unpack<BF16Tag>(v[t], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += x[e];
+    }
+  };
+  // the value of lane (lane + 16) % 64: group g + 1's half, group 0's for g = 3
+  auto from_next_group = [&](float x) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(((lane + 16) & 63) << 2, __float_as_int(x)));
+  };
+
+  // Step s covers windows w0 + 4 s + g. Its halves' sums (a) come from the
+  // step before; the halves of step s + 1 (one step ahead of use) were loaded
+  // during step s - 1, and step s issues the loads of step s + 2.
+  const int nsteps = (w1 - w0 + 3) / 4;
+  u32x4 v_next[kStride], v_after[kStride];
+  float a[8], n[8];
+  {
+    u32x4 v0[kStride];
+    load_half(w0 + g, v0);
+    load_half(w0 + 4 + g, v_next);
+    half_sum(v0, a);
+  }
+  for (int st = 0; st < nsteps; ++st) {
+    const int hb = w0 + 4 * st;  // this step's first half
+    load_half(hb + 8 + g, v_after);
+    half_sum(v_next, n);  // halves hb + 4 .. hb + 7
+    // window hb + g = half hb + g + half hb + g + 1: group g + 1's sum of this
+    // step, or for g = 3 group 0's of the next
+    float b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pa = from_next_group(a[e]), pn = from_next_group(n[e]);
+      b[e] = g < 3 ? pa : pn;
+    }
+    const int w = hb + g;
+    if (w < w1) store16(dst + (long)w * RB, window_from_halves<BF16Tag>(a, b));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = n[e];
+#pragma unroll
+    for (int t = 0; t < kStride; ++t) v_next[t] = v_after[t];
+  }
+}
+
+// fp32 (a 32-lane group per run of windows; the bf16 form above)
 template <typename Tag>
 __global__ __launch_bounds__(256) void compress_kernel(const uint8_t* __restrict__ k,
                                                        uint8_t* __restrict__ kc, int rows, int T,
@@ -56,10 +135,10 @@ hipError_t launch_compress(const void* k, void* kc, bool bf16, int rows, int T, 
   const int chunks = (w_end - w_begin + kCompressChunk - 1) / kCompressChunk;
   const long groups = (long)rows * chunks;
   if (bf16) {
-    const int gpb = 256 / (kHeadDim / DT<BF16Tag>::kElems);
-    dim3 grid((unsigned)((groups + gpb - 1) / gpb));
-    hipLaunchKernelGGL(compress_kernel<BF16Tag>, grid, dim3(256), 0, s, (const uint8_t*)k,
-                       (uint8_t*)kc, rows, T, W, w_begin, w_end, chunks);
+    const int wpb = 256 / kWave;  // one wave per (row, run of windows)
+    dim3 grid((unsigned)((groups + wpb - 1) / wpb));
+    hipLaunchKernelGGL(compress_wave_kernel, grid, dim3(256), 0, s, (const uint8_t*)k, (uint8_t*)kc, rows, T, W,
+                       w_begin, w_end, chunks);
   } else {
     const int gpb = 256 / (kHeadDim / DT<F32Tag>::kElems);
     dim3 grid((unsigned)((groups + gpb - 1) / gpb));
