@@ -43,36 +43,35 @@ __device__ __forceinline__ void load_chunk_lds(const uint8_t* __restrict__ kc_ro
   }
 }
 
-// The same load of a whole chunk (rows w0 .. w0 + CW - 1 all below W) from a
-// scalar base: off[it] holds this lane's offset within the chunk for load
-// `it`, from chunk_lds_offsets.
+// Direct loads of a chunk by NWAVES waves (a multiple of 4): load `it` of
+// wave v fills LDS bytes [(it NWAVES + v) KiB, +1 KiB), i.e. rows
+// 4 (it NWAVES + v) .. +3 of the chunk. Those rows start at a multiple of 16
+// plus 4 v, so the swizzle does not depend on `it`: a lane's source is row
+// w0 + it * 4 NWAVES + r0 at a fixed granule offset, and the loader keeps two
+// registers per lane (no 64-bit address per load). Each lane's row is clamped
+// to W - 1, so the last, partial chunk takes the same code (callers mask the
+// rows past W - 1). Offsets are 32-bit: a row of K_cmp (or F) is under 2 GiB.
 template <int NWAVES, int CW>
-struct ChunkOffsets {
+struct ChunkLoader {
   static constexpr int kLoads = CW * kRowBytes / (NWAVES * kWave * 16);
-  uint32_t off[kLoads];
-};
-template <int NWAVES, int CW>
-__device__ __forceinline__ ChunkOffsets<NWAVES, CW> chunk_lds_offsets() {
-  ChunkOffsets<NWAVES, CW> o;
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-#pragma unroll
-  for (int it = 0; it < ChunkOffsets<NWAVES, CW>::kLoads; ++it) {
-    const int pos = (it * NWAVES + wave) * kWave + lane;
-    const int r = pos >> 4;
-    o.off[it] = (uint32_t)(r * kRowBytes + (((pos & 15) ^ (r & 15)) << 4));
+  static constexpr int kRowsPerLoad = 4 * NWAVES;
+  static_assert(NWAVES % 4 == 0 && kLoads * NWAVES * kWave * 16 == CW * kRowBytes, "chunk must split evenly");
+  int r0;         // this lane's row within a load's rows
+  uint32_t gran;  // this lane's byte offset within its row
+  __device__ __forceinline__ ChunkLoader() {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    r0 = 4 * wave + (lane >> 4);
+    gran = (uint32_t)(((lane & 15) ^ (r0 & 15)) << 4);
   }
-  return o;
-}
-template <int NWAVES, int CW>
-__device__ __forceinline__ void load_full_chunk_lds(const uint8_t* __restrict__ kc_row, int w0,
-                                                    const ChunkOffsets<NWAVES, CW>& o, uint8_t* dst) {
-  const int wave = threadIdx.x / kWave;
-  const uint8_t* base = kc_row + (long)w0 * kRowBytes;
-#pragma unroll
-  for (int it = 0; it < ChunkOffsets<NWAVES, CW>::kLoads; ++it)
-    dma16_sv(base, o.off[it], dst + (it * NWAVES + wave) * kWave * 16);
-}
+  // load `it` of this wave: rows from w0 of the row block at `base`, into the
+  // chunk buffer at LDS address m0
+  __device__ __forceinline__ void one(int it, const uint8_t* __restrict__ base, int W, int w0, uint32_t m0) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t r = min(w0 + it * kRowsPerLoad + r0, W - 1);
+    dma16_sv_m0(base, r * kRowBytes + gran, m0 + (uint32_t)((it * NWAVES + wave) * kWave * 16));
+  }
+};
 
 // Fragment of a chunk row for a 32x32x16 MFMA operand whose rows (A) or columns
 // (B) are windows: lane l reads window row `r` (= 32 * tile + l % 32), channels

@@ -4,26 +4,33 @@
 // gain comes from the cheaper selection itself).
 //
 // A dense contraction: per KV head, F [Tq x 128] times K_cmp^T [128 x W], so it
-// runs on the matrix cores (v_mfma_f32_32x32x16_bf16). One workgroup owns one
-// (sequence, KV head) and TPW query tiles (two when the chunk has two or more;
-// 4 waves per tile), and sweeps the windows in chunks of 256, so each chunk
-// staged in LDS serves every tile of the workgroup:
-//   * the chunk's compressed keys (256 x 256 B) land in LDS through direct
-//     global->LDS loads issued one chunk ahead into two buffers; each 16-byte
-//     granule of row r is stored at position (granule ^ (r & 15)), so the
-//     fragment reads of 16 consecutive rows hit 16 different bank groups. Each
-//     wave waits for its own loads (vmcnt) and the barriers wait for LDS
-//     writes only, so the next chunk's loads stay in flight across them;
-//   * wave w computes the 64 x 64 score block of windows [64 (w % 4), +64) for
-//     the 64 queries of tile w / 4 (four products per K step: each window
-//     fragment serves both query halves and each F fragment both window
-//     halves), with that tile's F fragments in registers;
+// runs on the matrix cores (v_mfma_f32_32x32x16_bf16). One 512-thread
+// workgroup owns one (sequence, KV head) and two query tiles (128 queries) and
+// sweeps the windows in chunks of 256, so each chunk staged in LDS serves both
+// tiles:
+//   * the workgroup's 128 rows of F are staged once through LDS, and every wave
+//     keeps the fragments of all 128 queries in registers (4 x 32 queries);
+//   * each chunk's compressed keys (256 x 256 B) land in LDS through direct
+//     global->LDS loads into two buffers; each 16-byte granule of row r is
+//     stored at position (granule ^ (r & 15)), so the fragment reads of 16
+//     consecutive rows hit 16 different bank groups;
+//   * wave v owns windows [32 v, 32 v + 32) of every chunk: one key fragment
+//     per K step serves four products (the 4 x 32 queries);
 //   * each window's score is masked where the window is not visible to the
-//     query, and reduced to the max over the tile's queries (in-lane, then one
+//     query, and reduced to the max over each tile's queries (in-lane, then one
 //     swap of the two lane halves);
 //   * block b takes the max over windows 4b-1 .. 4b+3: chunk c finishes blocks
 //     64c .. 64c+63, reusing the previous chunk's last window (a one-window
 //     carry), so no window is computed twice and no workgroup waits on another.
+//
+// The two waves of a SIMD work out of phase. Waves 0-3 (group 0) and 4-7
+// (group 1) share the SIMDs pairwise, and each chunk takes two phases, each
+// ended by a barrier. In a phase one group runs its 32 products per wave from
+// registers while the other reduces its previous chunk to window maxima, pools
+// a finished chunk into block scores and reads its next chunk's key fragments
+// into registers; so the matrix cores of a SIMD alternate between its two
+// waves instead of idling while both reduce. The loads of chunk c + 1 go out
+// in phase 2c: group 0's in its memory phase, group 1's between its products.
 #include "prefill_lds.h"
 
 namespace sparda {
@@ -32,140 +39,202 @@ namespace sparda {
 // loads in flight (a fence here would wait for those too).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int TPW>
-__global__ __launch_bounds__(256 * TPW) void fsel_prefill_kernel(const uint8_t* __restrict__ f,
-                                                                 const uint8_t* __restrict__ kc,
-                                                                 float* __restrict__ scores, int Tq,
-                                                                 int q_start, int W, int nB, int n_tiles,
-                                                                 float scale) {
-  constexpr int NWAVES = 4 * TPW;
-  constexpr int CW = 2 * kChunkW;                 // windows per chunk: 64 per wave
-  constexpr int CB = CW * kRowBytes;              // bytes per chunk
+// A phase boundary: nothing is scheduled across it, so the products stay in
+// their phase.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__global__ __launch_bounds__(512) void fsel_prefill_kernel(const uint8_t* __restrict__ f,
+                                                           const uint8_t* __restrict__ kc,
+                                                           float* __restrict__ scores, int Tq, int q_start, int W,
+                                                           int nB, int n_tiles, float scale) {
+  constexpr int CW = 2 * kChunkW;  // windows per chunk: 32 per wave
+  constexpr int CB = CW * kRowBytes;
   __shared__ __attribute__((aligned(16))) uint8_t s_kc[2][CB];
-  __shared__ float s_cmax[2][TPW][CW + 1];  // [c % 2][t][0] = carry: last window of chunk c - 1
+  __shared__ float s_cmax[2][2][CW + 1];  // [c % 2][tile][0] = carry: last window of chunk c - 1
 
   const long row = blockIdx.x;  // (b, h): rows on the fast axis share an XCD
-  const int tl = threadIdx.x / (4 * kWave);  // this wave's tile in the workgroup
-  const int tile = blockIdx.y * TPW + tl;    // may be n_tiles (an odd count's last workgroup): no output
-  const int wave = (threadIdx.x / kWave) % 4;
+  const int v = threadIdx.x / kWave;
+  const int grp = v / 4;
   const int lane = threadIdx.x % kWave;
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const uint8_t* kc_row = kc + row * (long)W * kRowBytes;
-  const int q0 = tile * kTile;  // first query of the tile (relative to the chunk)
+  const int tile0 = blockIdx.y * 2;  // tile0 + 1 may be n_tiles (an odd count's last workgroup): no output
+  const int q0 = tile0 * kTile;      // first query of the workgroup (relative to the chunk)
 
-  // F fragments: A operand of the 64 x 128 tile, 2 M-tiles x 8 k-steps
-  u32x4 fa[2][8];
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int q = min(q0 + 32 * m + l32, Tq - 1);
-    const uint8_t* src = f + (row * Tq + q) * (long)kRowBytes + half * 16;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) fa[m][s] = load16(src + s * 32);
-  }
   // visibility: window w is visible to query position p iff 16 w + 31 <= p;
-  // the tile's first query sees the fewest windows
-  const int vis_min = visible_windows(q_start + min(q0, Tq - 1), W);
+  // a tile's first query sees the fewest windows
+  int vis_min[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) vis_min[t] = visible_windows(q_start + min(q0 + t * kTile, Tq - 1), W);
+  const int n = (W + CW - 1) / CW;
 
-  const int nchunks = (W + CW - 1) / CW;
-  const ChunkOffsets<NWAVES, CW> offs = chunk_lds_offsets<NWAVES, CW>();
-  // whole chunks from a scalar base, the last partial one with clamped rows
-  auto load = [&](int c, uint8_t* dst) {
-    if ((c + 1) * CW <= W) {
-      load_full_chunk_lds<NWAVES, CW>(kc_row, c * CW, offs, dst);
-    } else {
-      load_chunk_lds<NWAVES, CW>(kc_row, W, c * CW, dst);
-    }
+  u32x4 fa[4][8];  // A operands: 4 M-tiles of 32 queries x 8 K steps
+  u32x4 bf[8];     // B operands: this wave's 32 windows x 8 K steps
+  f32x16 acc[4];   // [M-tile]: queries 32 m .. 32 m + 31 x this wave's windows
+
+  const ChunkLoader<8, CW> ld;
+  const uint32_t kc_lds = lds_addr(s_kc[0]);
+  // this wave's eighth of chunk c (rows past W - 1 read row W - 1; masked)
+  auto load_one = [&](int it, int c) { ld.one(it, kc_row, W, c * CW, kc_lds + (uint32_t)((c & 1) * CB)); };
+  auto load = [&](int c) {
+#pragma unroll
+    for (int it = 0; it < ChunkLoader<8, CW>::kLoads; ++it) load_one(it, c);
   };
-  if (threadIdx.x < TPW) s_cmax[0][threadIdx.x][0] = -INFINITY;
-  load(0, s_kc[0]);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();
-  // One barrier per chunk. Iteration c issues chunk c + 1 into the buffer
-  // chunk c - 1 used, scores chunk c into window maxima s_cmax[c % 2], waits
-  // for its own loads and meets the other waves: chunk c + 1 and the maxima
-  // are then visible, and chunk c's buffer is read by none. The block pooling
-  // of chunk c runs after that barrier, beside the next chunk's products; the
-  // maxima are double-buffered so those writes go to the other half.
-  for (int c = 0; c < nchunks; ++c) {
-    const int bc = c & 1;
-    if (c + 1 < nchunks) load(c + 1, s_kc[bc ^ 1]);
-    const uint8_t* tileb = s_kc[bc];
-    f32x16 acc[2][2] = {};  // [query half m][window half n]
+  auto read_frags = [&](int c) {
+    const uint8_t* tileb = s_kc[c & 1];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) bf[s] = chunk_frag(tileb, 32 * v + l32, s, half);
+  };
+  // the products of the chunk whose fragments are in bf
+  auto products = [&]() {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[m][s]), as_bf16x8(bf[s]), acc[m], 0, 0, 0);
+  };
+  // the same with this wave's loads of chunk load_c between the K steps
+  auto products_load = [&](int load_c) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = f32x16{};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const u32x4 b0 = chunk_frag(tileb, 64 * wave + l32, s, half);
-      const u32x4 b1 = chunk_frag(tileb, 64 * wave + 32 + l32, s, half);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[m][s]), as_bf16x8(b0), acc[m][0], 0, 0, 0);
-        acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[m][s]), as_bf16x8(b1), acc[m][1], 0, 0, 0);
-      }
+      for (int m = 0; m < 4; ++m)
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[m][s]), as_bf16x8(bf[s]), acc[m], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_one(s, load_c);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    float* cmax = s_cmax[bc][tl];
-    // column (window) max over the tile's visible queries
+  };
+  // window maxima of chunk c over each tile's visible queries
+  auto reduce = [&](int c) {
+    const int wr = 32 * v + l32;  // this lane's window row in the chunk
+    const int w = c * CW + wr;
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int wr = 64 * wave + 32 * n + l32;  // this lane's window row in the chunk
-      const int w = c * CW + wr;
+    for (int t = 0; t < 2; ++t) {
       float cm;
-      if (scale > 0.f && c * CW + 64 * wave + 32 * n + 31 < vis_min) {
-        // every window of this lane group is visible to every query of the
-        // tile, and with scale > 0 the max of the scaled scores is the scaled
-        // max (same bits)
+      if (scale > 0.f && c * CW + 32 * v + 31 < vis_min[t]) {
+        // every window of this wave is visible to every query of the tile, and
+        // with scale > 0 the max of the scaled scores is the scaled max (same
+        // bits)
         float a = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) a = fmaxf(a, fmaxf(acc[0][n][r], acc[1][n][r]));
+        for (int r = 0; r < 16; ++r) a = fmaxf(a, fmaxf(acc[2 * t][r], acc[2 * t + 1][r]));
         cm = max32(a) * scale;
       } else {
+        // accumulator row r of M-tile m holds query 32 m + 8 (r / 4) + 4 half +
+        // r % 4. Window w is visible to query q iff w < W and 16 w + 31 <=
+        // q_start + min(q, Tq - 1); with q = q0 + 64 t + 4 half + k, k = 32 m' +
+        // 8 (r / 4) + r % 4 a compile-time offset, that is k >= d for this
+        // lane's bound d
+        const int th = 16 * w + 31 - q_start;
+        const int d = (w < W && Tq - 1 >= th) ? th - q0 - 64 * t - 4 * half : 64;
         cm = -INFINITY;
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            // accumulator row r of M-tile m holds query 32 m + 8 (r / 4) + 4 half + r % 4
-            const int q = q0 + 32 * m + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (w < visible_windows(q_start + min(q, Tq - 1), W)) cm = fmaxf(cm, acc[m][n][r] * scale);
-          }
+          for (int r = 0; r < 16; ++r)
+            if (32 * m + 8 * (r >> 2) + (r & 3) >= d) cm = fmaxf(cm, acc[2 * t + m][r] * scale);
         cm = max32(cm);
       }
-      if (half == 0) cmax[1 + wr] = cm;
+      if (half == 0) s_cmax[c & 1][t][1 + wr] = cm;
     }
-    // chunk c + 1 has landed for this wave's loads; after the barrier for
-    // every wave, with this chunk's maxima
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    lds_barrier();
-    const int t = threadIdx.x;
-    if (t < TPW * (CW / 4)) {  // 64 blocks per tile
-      const int ot = t / (CW / 4), bt = t % (CW / 4);
-      const int b = c * (CW / 4) + bt;
-      const int otile = blockIdx.y * TPW + ot;
-      const float* cm = s_cmax[bc][ot];
-      if (b < nB && otile < n_tiles) {
-        float m = cm[4 * bt];
+  };
+  // blocks of chunk c for tile t (one wave), and the carry into chunk c + 1:
+  // slot 0 of a chunk's maxima is read only by the lane of its block 0
+  auto pool = [&](int c, int t) {
+    const int tile = tile0 + t;
+    const float* cm = s_cmax[c & 1][t];
+    const int b = c * (CW / 4) + lane;
+    if (b < nB && tile < n_tiles) {
+      float m = cm[4 * lane];
 #pragma unroll
-        for (int j = 1; j < 5; ++j) m = fmaxf(m, cm[4 * bt + j]);
-        scores[(row * n_tiles + otile) * (long)nB + b] = m;
+      for (int j = 1; j < 5; ++j) m = fmaxf(m, cm[4 * lane + j]);
+      scores[(row * n_tiles + tile) * (long)nB + b] = m;
+    }
+    if (lane == 0) s_cmax[(c + 1) & 1][t][0] = cm[CW];
+  };
+
+  // Prologue: the workgroup's 128 rows of F into the second buffer (the same
+  // row layout as a chunk of K_cmp; rows past Tq - 1 read row Tq - 1) and
+  // chunk 0 into the first; every wave takes its F fragments, and the second
+  // buffer is free again after the barrier.
+  if (threadIdx.x < 2) s_cmax[0][threadIdx.x][0] = -INFINITY;
+  {
+    const ChunkLoader<8, 2 * kTile> fld;
+#pragma unroll
+    for (int it = 0; it < ChunkLoader<8, 2 * kTile>::kLoads; ++it)
+      fld.one(it, f + row * Tq * (long)kRowBytes, Tq, q0, kc_lds + (uint32_t)CB);
+  }
+  load(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) fa[m][s] = chunk_frag(s_kc[1], 32 * m + l32, s, half);
+  __syncthreads();
+
+  // Phases 2c and 2c + 1 of chunk c. Chunk c sits in buffer c % 2 from the
+  // end of phase 2c - 1 (its loads went out in phase 2c - 2, and each wave
+  // waits for its own at the end of phase 2c - 1); group 0 reads its
+  // fragments in phase 2c and group 1 in phase 2c + 1, so the buffer takes
+  // chunk c + 2 from phase 2c + 2 on. The maxima of chunk c come from group 0
+  // in phase 2c + 2 and from group 1 in phase 2c + 3; wave 0 (tile 0) and
+  // wave 4 (tile 1) pool the chunk in phases 2c + 4 and 2c + 5, while the
+  // maxima of chunk c + 1 go to the other half of s_cmax.
+  if (grp == 0) {
+    for (int c = 0; c <= n + 1; ++c) {
+      // memory phase 2c: maxima of c - 1, blocks of c - 2, loads of c + 1,
+      // fragments of c (after the maxima, so they reuse the accumulators'
+      // registers)
+      if (c >= 1 && c <= n) reduce(c - 1);
+      if (c >= 2 && v == 0) pool(c - 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c + 1 < n) load(c + 1);
+      if (c < n) read_frags(c);
+      phase_barrier();
+      // compute phase 2c + 1: products of chunk c
+      if (c < n) products();
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      phase_barrier();
+    }
+  } else {
+    if (1 < n) load(1);  // phase 0 has no products for this group
+    for (int c = 0; c <= n + 1; ++c) {
+      // compute phase 2c: products of chunk c - 1 with the loads of c + 1
+      if (c >= 1 && c <= n) {
+        if (c + 1 < n) {
+          products_load(c + 1);
+        } else {
+          products();
+        }
       }
-      // The carry: this chunk's last window becomes window 0 of the next
-      // chunk's half. Slot 0 of a half is read only by the thread of block 0,
-      // this thread, after the barrier that follows this write.
-      if (bt == 0) s_cmax[bc ^ 1][ot][0] = cm[CW];
+      phase_barrier();
+      // memory phase 2c + 1: maxima of c - 1, blocks of c - 2, fragments of c
+      if (c >= 1 && c <= n) reduce(c - 1);
+      if (c >= 2 && v == 4) pool(c - 2, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c < n) read_frags(c);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      phase_barrier();
     }
   }
 }
 
 hipError_t launch_select_forecast_prefill(const void* f, const void* kc, float* scores, const SelectDims& d,
                                           hipStream_t s) {
-  if (d.n_tiles >= 2) {
-    dim3 grid(d.B * d.Hkv, (d.n_tiles + 1) / 2);
-    hipLaunchKernelGGL(fsel_prefill_kernel<2>, grid, dim3(512), 0, s, (const uint8_t*)f, (const uint8_t*)kc, scores,
-                       d.Tq, d.q_start, d.W, d.nB, d.n_tiles, d.scale);
-  } else {
-    dim3 grid(d.B * d.Hkv, d.n_tiles);
-    hipLaunchKernelGGL(fsel_prefill_kernel<1>, grid, dim3(256), 0, s, (const uint8_t*)f, (const uint8_t*)kc, scores,
-                       d.Tq, d.q_start, d.W, d.nB, d.n_tiles, d.scale);
-  }
+  dim3 grid(d.B * d.Hkv, (d.n_tiles + 1) / 2);
+  hipLaunchKernelGGL(fsel_prefill_kernel, grid, dim3(512), 0, s, (const uint8_t*)f, (const uint8_t*)kc, scores, d.Tq,
+                     d.q_start, d.W, d.nB, d.n_tiles, d.scale);
   return hipGetLastError();
 }
 
