@@ -28,7 +28,10 @@ def gen(w, name):
     return sg.tensor(w.recipe(name), w.shape(name), DEV)
 
 
-CASES = [prefill(64 * 37, 128), prefill(64 * 37, 64 * 37, k=7), prefill(2048, 64, B=2), prefill(4096, 1024, k=16)]
+CASES = [prefill(64 * 37, 128), prefill(64 * 37, 64 * 37, k=7), prefill(2048, 64, B=2), prefill(4096, 1024, k=16),
+         # five 256-window chunks of the scoring sweep, the last one partial,
+         # and an odd tile count (the last workgroup's second tile is empty)
+         prefill(64 * 258, 320, B=2, k=9)]
 
 
 @pytest.mark.parametrize("w", CASES, ids=lambda w: f"T{w.T}-Tq{w.Tq}-B{w.B}")
