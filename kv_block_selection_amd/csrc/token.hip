@@ -12,9 +12,16 @@
 //   after p; an HBM-bound GEMV over every key row (16 lanes per 256-byte row,
 //   all of a workgroup's loads in flight before the first is used).
 // topk_long_kernel: the top-k rule for rows too long for the LDS-resident
-//   top-k (any length): one 1024-thread workgroup per row, four 8-bit radix
-//   passes over the order keys streamed from memory, then the kept indices in
-//   ascending order by a scan in index order (ties to the lower index).
+//   top-k (any length): one 1024-thread workgroup per row. A strided sample
+//   of 4096 scores gives a threshold t whose count in the row is expected a
+//   little above k; one streaming pass keeps every score at or above t, in
+//   index order, in LDS; when they are at least k (so t is at or below the
+//   k-th largest score, and every kept score is among them) and fit, the
+//   rule runs on them alone. Otherwise (heavy ties, a k near the row length,
+//   few candidates) four 8-bit radix passes run over the order keys streamed
+//   from memory. Either way the kept indices are written in ascending order
+//   by a scan in index order (ties to the lower index), so the two paths give
+//   the same result.
 // token_gather_kernel: the kept token rows of K and V compacted into staging
 //   [rows, k_tok, 128] (valid entries in their order, the slots past the
 //   row's count zeroed), the row's count of valid entries, and the block list
@@ -29,6 +36,9 @@ namespace sparda {
 constexpr int kTokIter = 32;       // key rows per thread group in flight
 constexpr int kLongThreads = 1024;  // threads of a long-row top-k workgroup
 constexpr int kLongEPT = 8;         // consecutive elements per thread in the output scan
+constexpr int kLongSample = 4096;   // sampled scores for the threshold
+constexpr int kLongCand = 8192;     // candidates the sampled path keeps in LDS (8 per thread)
+constexpr int kLongSeg = 32;        // segments of kLongThreads scores per batch of the candidate pass
 
 template <typename Tag>
 __global__ __launch_bounds__(256) void token_scores_kernel(const uint8_t* __restrict__ f,
@@ -57,6 +67,82 @@ __global__ __launch_bounds__(256) void token_scores_kernel(const uint8_t* __rest
   }
 }
 
+// Exclusive prefix over the workgroup of one int per thread, and the total;
+// s_tot holds a slot per wave and is free again when this returns.
+__device__ __forceinline__ int block_excl_scan(int v, int* s_tot, int& total) {
+  const int lane = threadIdx.x % kWave;
+  const int wid = threadIdx.x / kWave;
+  const int incl = wave_incl_scan(v);
+  if (lane == kWave - 1) s_tot[wid] = incl;
+  __syncthreads();
+  int before = incl - v;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kLongThreads / kWave; ++w) {
+    const int x = s_tot[w];
+    before += w < wid ? x : 0;
+    total += x;
+  }
+  __syncthreads();
+  return before;
+}
+
+// The want-th largest of the order keys keys[0 .. m) in LDS (0 = not a
+// candidate; 1 <= want <= the number of nonzero keys), by 8-bit radix passes
+// from the top: with all four passes tau is that key and take_eq the number
+// of keys equal to it among the want largest; with fewer, tau is its top
+// 8 PASSES bits (the rest zero), a key at or below it. Every thread of the
+// workgroup calls it.
+template <int PASSES>
+__device__ void lds_radix_select(const uint32_t* keys, int m, int want, int* hist16, int* hist, int* s_digit,
+                                 int* s_above, uint32_t& tau, int& take_eq) {
+  const int t = threadIdx.x;
+  const int lane = t % kWave;
+  const int wid = t / kWave;
+  uint32_t prefix = 0;
+  int remaining = want;
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    for (int i = t; i < 256 * 16; i += kLongThreads) hist16[i] = 0;
+    __syncthreads();
+    for (int i = t; i < m; i += kLongThreads) {
+      const uint32_t key = keys[i];
+      if (key != 0u && (key & hi_mask) == prefix) atomicAdd(&hist16[((key >> shift) & 255u) * 16 + (lane & 15)], 1);
+    }
+    __syncthreads();
+    if (t < 256) {
+      int h = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) h += hist16[t * 16 + ((j + t) & 15)];
+      hist[t] = h;
+    }
+    __syncthreads();
+    if (wid == 0) {
+      int h[4], sum = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[i] = hist[255 - 4 * lane - i];
+        sum += h[i];
+      }
+      int above = wave_incl_scan(sum) - sum;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (above < remaining && remaining <= above + h[i]) {
+          *s_digit = 255 - 4 * lane - i;
+          *s_above = above;
+        }
+        above += h[i];
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)*s_digit << shift;
+    remaining -= *s_above;
+  }
+  tau = prefix;
+  take_eq = remaining;
+}
+
 __global__ __launch_bounds__(kLongThreads) void topk_long_kernel(const float* __restrict__ scores,
                                                                  int32_t* __restrict__ idx, int n, int k) {
   // 16 copies of each digit's counter, lane l of a wave counting into copy
@@ -67,11 +153,117 @@ __global__ __launch_bounds__(kLongThreads) void topk_long_kernel(const float* __
   __shared__ int hist[256];
   __shared__ int s_tot[kLongThreads / kWave];
   __shared__ int s_digit, s_above, s_ncand;
+  __shared__ uint32_t s_key[kLongCand];
+  __shared__ int32_t s_pos[kLongCand];
+  __shared__ int s_cnt[kLongSeg * (kLongThreads / kWave)];
   const int t = threadIdx.x;
   const int lane = t % kWave;
   const int wid = t / kWave;
   const float* src = scores + (long)blockIdx.x * n;
   int32_t* dst = idx + (long)blockIdx.x * k;
+
+  // Sampled path, taken when the expected candidate count (1.2 k plus the
+  // sample's slack of 16 positions) fits well inside the LDS store.
+  const int r_sample = (int)(((long)6 * k * kLongSample + 5L * n - 1) / (5L * n)) + 16;
+  if ((long)r_sample * n <= (long)kLongSample * (kLongCand * 4 / 5)) {
+    // the threshold: the r-th largest of kLongSample evenly spread scores
+    int ns = 0;
+    for (int j = t; j < kLongSample; j += kLongThreads) {
+      const uint32_t key = order_key(src[((long)j * n) / kLongSample]);
+      s_key[j] = key;
+      ns += key != 0u;
+    }
+    int n_sampled;
+    block_excl_scan(ns, s_tot, n_sampled);
+    if (n_sampled > 0) {
+      uint32_t t0;
+      int unused;
+      // the top 16 bits of the sample's r-th largest key are enough: a lower
+      // threshold only admits a few more candidates
+      lds_radix_select<2>(s_key, kLongSample, min(r_sample, n_sampled), hist16, hist, &s_digit, &s_above, t0,
+                          unused);
+      // one pass over the row: every key >= t0 (t0 > 0: the r-th key is not
+      // -inf, so its top 16 bits are not all zero) into
+      // LDS in index order. A batch is kLongSeg segments of kLongThreads
+      // consecutive scores, one per thread (coalesced loads, all in flight);
+      // a candidate's place is its lane's rank in its wave (ballot) plus an
+      // exclusive prefix over the batch's (segment, wave) counts.
+      constexpr int kWaves = kLongThreads / kWave;
+      int count = 0;
+      for (long c0 = 0; c0 < n && count <= kLongCand; c0 += (long)kLongThreads * kLongSeg) {
+        float x[kLongSeg];
+#pragma unroll
+        for (int j = 0; j < kLongSeg; ++j) {
+          const long i = c0 + (long)j * kLongThreads + t;
+          x[j] = i < n ? src[i] : -INFINITY;
+        }
+        int rank[kLongSeg];
+#pragma unroll
+        for (int j = 0; j < kLongSeg; ++j) {
+          const uint64_t m = __ballot(order_key(x[j]) >= t0);
+          rank[j] = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+          if (lane == 0) s_cnt[j * kWaves + wid] = __popcll(m);
+        }
+        __syncthreads();
+        // exclusive prefix over the kLongSeg x kWaves counts (threads 0 .. 255)
+        const int v = t < kLongSeg * kWaves ? s_cnt[t] : 0;
+        const int incl = wave_incl_scan(v);
+        if (lane == kWave - 1 && wid < kLongSeg * kWaves / kWave) s_tot[wid] = incl;
+        __syncthreads();
+        int batch = 0, prior = 0;
+#pragma unroll
+        for (int w = 0; w < kLongSeg * kWaves / kWave; ++w) {
+          batch += s_tot[w];
+          prior += w < wid ? s_tot[w] : 0;
+        }
+        if (t < kLongSeg * kWaves) s_cnt[t] = incl - v + prior;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kLongSeg; ++j) {
+          const uint32_t key = order_key(x[j]);
+          const int pos = count + s_cnt[j * kWaves + wid] + rank[j];
+          if (key >= t0 && pos < kLongCand) {
+            s_key[pos] = key;
+            s_pos[pos] = (int32_t)(c0 + (long)j * kLongThreads + t);
+          }
+        }
+        count += batch;
+        __syncthreads();  // s_cnt and s_tot are rewritten by the next batch
+      }
+      __syncthreads();  // the candidates are in
+      if (count >= k && count <= kLongCand) {
+        uint32_t tau;
+        int take_eq;
+        lds_radix_select<4>(s_key, count, k, hist16, hist, &s_digit, &s_above, tau, take_eq);
+        // kept: every candidate above tau and the first take_eq equal to it,
+        // in index order (the candidates' order)
+        const int c0 = t * (kLongCand / kLongThreads);
+        uint32_t key[kLongCand / kLongThreads];
+        int gt = 0, eq = 0;
+#pragma unroll
+        for (int j = 0; j < kLongCand / kLongThreads; ++j) {
+          key[j] = c0 + j < count ? s_key[c0 + j] : 0u;
+          gt += key[j] > tau;
+          eq += key[j] == tau;  // tau > 0: a padding 0 never matches
+        }
+        int total;
+        const int before = block_excl_scan(gt | (eq << 16), s_tot, total);
+        int g_before = before & 0xFFFF, e_before = before >> 16;
+#pragma unroll
+        for (int j = 0; j < kLongCand / kLongThreads; ++j) {
+          if (key[j] > tau) {
+            const int pos = g_before + min(e_before, take_eq);
+            if (pos < k) dst[pos] = s_pos[c0 + j];
+            ++g_before;
+          } else if (key[j] == tau) {
+            if (e_before < take_eq && g_before + e_before < k) dst[g_before + e_before] = s_pos[c0 + j];
+            ++e_before;
+          }
+        }
+        return;
+      }
+    }
+  }
 
   // Radix select of the k-th largest order key, 8 bits per pass from the top:
   // after the passes, `prefix` is that key and `remaining` the number of keys

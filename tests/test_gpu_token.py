@@ -82,6 +82,18 @@ def test_topk_long_rows_exact(gpu, n):
         np.testing.assert_array_equal(got, want)
 
 
+@pytest.mark.parametrize("n,k", [(131072, 4096), (50000, 1000), (8193, 64)])
+def test_topk_long_rows_sampled_path(gpu, n, k):
+    """Distinct scores, so the candidates above the sampled threshold are
+    enough and fit: exact against the oracle (one row a third -inf)."""
+    rng = np.random.default_rng(n + k)
+    x = rng.standard_normal((3, n)).astype(np.float32)
+    x[1, rng.choice(n, size=n // 3, replace=False)] = -np.inf
+    say("topk long sampled", n, "k", k)
+    got = kbs.topk_blocks(torch.from_numpy(x).to(DEV), k).cpu().numpy()
+    np.testing.assert_array_equal(got, oracle.topk_blocks(x.astype(np.float64), k))
+
+
 def test_topk_long_rows_degenerate(gpu):
     n = 10000
     x = np.full((3, n), -np.inf, dtype=np.float32)
