@@ -75,7 +75,7 @@ enum sparda_op {
   SPARDA_OP_SELECT_FORECAST = 1,
   SPARDA_OP_SELECT_MULTIHEAD = 2,
   SPARDA_OP_BLOCK_SPARSE_ATTN = 3,
-  SPARDA_OP_TOKEN_ATTN = 4, /* k_sel = k_tok; sized for fp32 staging (enough for bf16) */
+  SPARDA_OP_TOKEN_ATTN = 4, /* k_sel = k_tok: the block-range results of the attention over the kept tokens */
   SPARDA_OP_DECODE_LAYER = 5 /* sparda_decode_layer (Tq = 1): 0 when each row gets a workgroup */
 };
 
@@ -410,10 +410,11 @@ int sparda_select_tokens(const void* f, const void* k, float* tok_scores, int dt
  *   repeated position would be attended once per copy), out [B, Hq, 1, d]
  *   written: softmax(scale q . k[j]) over the kept j, times v[j]; a query
  *   with no kept token gets zeros.
- * The kept rows are compacted into staging in ws, then attended as k_tok / 64
- * blocks of staging. ws: sparda_workspace_bytes(SPARDA_OP_TOKEN_ATTN, B, Hq,
- * Hkv, 1, T, d, k_tok) bytes, 256-byte aligned, owned by the caller; it must
- * not be shared by calls in flight at once.
+ * The kept rows are read where they sit in k and v, the list taken as k_tok / 64
+ * ranges of 64 entries split over workgroups whose results ws holds until a
+ * second launch merges them. ws: sparda_workspace_bytes(SPARDA_OP_TOKEN_ATTN,
+ * B, Hq, Hkv, 1, T, d, k_tok) bytes (0: ws may be NULL), 256-byte aligned,
+ * owned by the caller; it must not be shared by calls in flight at once.
  * Supported: fp32/bf16, d = 128, Hq / Hkv in {1, 2, 4, 8}, k_tok a multiple of
  * 64 in 64..2^20, 1 <= T <= 2^26, B * Hkv <= 65535. Async on stream.
  */

@@ -135,10 +135,9 @@ sparda::AttnDims attn_dims(int B, int Hq, int Hkv, int Tq, int q_start, int T, i
 
 size_t ws_bytes_for(int op, int B, int Hq, int Hkv, int Tq, int T, int k) {
   if (B <= 0 || Hkv <= 0 || Hq <= 0) return 0;
-  if (op == SPARDA_OP_TOKEN_ATTN) {  // k = k_tok; staging sized for 4-byte elements (bf16 uses half); any T >= 1
+  if (op == SPARDA_OP_TOKEN_ATTN) {  // k = k_tok: the attention's block-range results over k_tok / 64 slots; any T >= 1
     if (Tq != 1 || T < 1 || k < sparda::kBlock || k % sparda::kBlock != 0) return 0;
-    return sparda::token_attn_ws(nullptr, attn_dims(B, Hq, Hkv, 1, k - 1, k, k / sparda::kBlock, 1.f, 1), k, false)
-        .bytes;
+    return sparda::decode_attn_ws_bytes(attn_dims(B, Hq, Hkv, 1, T - 1, T, k / sparda::kBlock, 1.f, 0));
   }
   if (T < sparda::kBlock) return 0;
   const int q_start = T - Tq;
@@ -714,18 +713,13 @@ SPARDA_EXPORT int sparda_token_sparse_attn(const void* q, const void* k, const v
   CHECK(tok_idx != nullptr && ((uintptr_t)tok_idx & 3u) == 0, SPARDA_ERR_INVALID_ARG,
         "tok_idx is NULL or not 4-byte aligned");
   const bool bf16 = dtype == SPARDA_BF16;
-  // the attention over staging: T = k_tok slots read as k_tok / 64 blocks, each
-  // row's visible slots given as its own position
-  sparda::AttnDims td = attn_dims(B, Hq, Hkv, 1, k_tok - 1, k_tok, k_tok / sparda::kBlock, scale, SPARDA_KV_STAGING);
-  sparda::TokenAttnWs w = sparda::token_attn_ws(ws, td, k_tok, bf16);
-  CHECK(ws != nullptr && ((uintptr_t)ws & 255u) == 0 && ws_bytes >= w.bytes, SPARDA_ERR_INVALID_ARG,
-        "workspace: need %zu bytes, 256-byte aligned (got %zu)", w.bytes, ws_bytes);
-  td.q_pos = w.pos_eff;
-  td.q_pos_per_row = true;
-  hipError_t e = sparda::launch_token_gather(k, v, tok_idx, w, bf16, B * Hkv, T, k_tok, q_start, q_pos, Hkv,
-                                             (hipStream_t)stream);
-  if (e != hipSuccess) return hip_status(e, "token gather launch");
-  return hip_status(sparda::launch_attn_decode(q, w.stage_k, w.stage_v, w.blk_idx, out, bf16, td, w.attn_ws,
-                                               (hipStream_t)stream),
+  // the split attention over k_tok / 64 slots of 64 list entries, each key
+  // read where it sits in the cache
+  sparda::AttnDims td = attn_dims(B, Hq, Hkv, 1, q_start, T, k_tok / sparda::kBlock, scale, SPARDA_KV_CACHE);
+  td.q_pos = q_pos;
+  const size_t need = sparda::decode_attn_ws_bytes(td);
+  CHECK(need == 0 || (ws != nullptr && ((uintptr_t)ws & 255u) == 0 && ws_bytes >= need), SPARDA_ERR_INVALID_ARG,
+        "workspace: need %zu bytes, 256-byte aligned (got %zu)", need, ws_bytes);
+  return hip_status(sparda::launch_attn_tokens(q, k, v, tok_idx, out, bf16, td, ws, (hipStream_t)stream),
                     "token attention launch");
 }

@@ -21,7 +21,10 @@
 // (merge_row.h) combines a row's splits. Two more forms of the same kernel:
 // four splits per workgroup with the row's top-k taken first by the whole
 // workgroup (topk_row.h; the selection then comes from LDS), and the merge
-// left to a later launch, such as the next layer's selection.
+// left to a later launch, such as the next layer's selection. A token mode
+// (template flag TOK) reads a list of single tokens instead of blocks, for the
+// token-level Forecast variant (techwalker.com article, section 六): each
+// lane loads the indices of its stage's keys a stage ahead of their rows.
 #include <mutex>
 #include <type_traits>
 
@@ -57,7 +60,7 @@ constexpr float kLazyGrow = 5.545177444479562f;  // 8 ln 2
 // LDSM: the workgroup holds all of the row's splits (one per wave; waves past
 // the last split contribute nothing) and merges them in LDS, with the merge
 // kernel's arithmetic, into the finished output: no partials, no second launch.
-template <typename Tag, int G, int WPG, int NPT, bool LDSM = false>
+template <typename Tag, int G, int WPG, int NPT, bool LDSM = false, bool TOK = false>
 __device__ __forceinline__ void attn_decode_body(
     long row, int wg_split, const uint8_t* __restrict__ q, const uint8_t* __restrict__ kbuf,
     const uint8_t* __restrict__ vbuf, const int32_t* __restrict__ idx, int32_t* __restrict__ idx_out,
@@ -84,7 +87,9 @@ __device__ __forceinline__ void attn_decode_body(
   const int c = lane % LPK;
   const int r = lane / LPK;
 
-  const int32_t* idx_row = idx + row * k;
+  // TOK: idx holds k * 64 token indices per row (slot j = entries 64 j ..
+  // 64 j + 63) instead of k block indices
+  const int32_t* idx_row = idx + row * (long)k * (TOK ? kBlock : 1);
   if constexpr (NPT > 0) {
     __shared__ TopkShared<WPG> sh;
     __shared__ int32_t s_sel[kFusedMaxK];
@@ -144,13 +149,43 @@ __device__ __forceinline__ void attn_decode_body(
   };
   const int nstage = 2 * (j1 - j0);
 
+  // TOK: each stage's keys are the tokens its 32 list entries name; a lane
+  // loads the indices of its keys (it KPI + r) a stage ahead of their rows.
+  // An entry that is -1 or after the query position reads token 0 (a valid
+  // address) and is masked.
+  const long tok_row = row * (long)T;
+  int tk_cur[TOK ? NIT : 1], tk_nxt[TOK ? NIT : 1];
+  uint32_t vm_cur = 0, vm_nxt = 0;  // bit it: key it KPI + r is a valid token
+  auto load_tok = [&](int q, int (&tk)[TOK ? NIT : 1], uint32_t& vm) {
+    const int e0 = (j0 + (q >> 1)) * kBlock + (q & 1) * CK;
+    vm = 0;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int t = idx_row[e0 + it * KPI + r];
+      const bool ok = t >= 0 && t <= p;
+      tk[it] = ok ? t : 0;
+      vm |= (uint32_t)ok << it;
+    }
+  };
+  auto key_row = [&](long base, int it, const int (&tk)[TOK ? NIT : 1]) -> long {
+    if constexpr (TOK) {
+      return tok_row + tk[it];
+    } else {
+      return base + it * KPI + r;
+    }
+  };
+
   u32x4 kv[NIT], vv[NIT];
   int nvalid = 0;
   long tok0 = 0;
   if (active) {  // an inactive wave reads no stage
-    tok0 = stage_of(0, nvalid);
+    if constexpr (TOK) {
+      load_tok(0, tk_cur, vm_cur);
+    } else {
+      tok0 = stage_of(0, nvalid);
+    }
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) kv[it] = load16_nt(kbuf + (tok0 + it * KPI + r) * RB + c * 16);
+    for (int it = 0; it < NIT; ++it) kv[it] = load16_nt(kbuf + key_row(tok0, it, tk_cur) * RB + c * 16);
   }
 
   // One stage of 32 keys: V loads go out first, then QK on the keys already in
@@ -159,7 +194,8 @@ __device__ __forceinline__ void attn_decode_body(
   // unconditional and the compiler's wait counts stay exact.
   auto body = [&](int q, auto prefetch) {
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) vv[it] = load16_nt(vbuf + (tok0 + it * KPI + r) * RB + c * 16);
+    for (int it = 0; it < NIT; ++it) vv[it] = load16_nt(vbuf + key_row(tok0, it, tk_cur) * RB + c * 16);
+    if constexpr (TOK && decltype(prefetch)::value) load_tok(q + 1, tk_nxt, vm_nxt);
 
     // QK: scores -> LDS [key][g]
 #pragma unroll
@@ -177,9 +213,10 @@ __device__ __forceinline__ void attn_decode_body(
       constexpr int HL = G >= 4 ? 4 : (G == 2 ? 8 : 16);  // lanes per head after the scatter
       if ((c & (HL - 1)) == 0 && c < 16) {
         const int h = (c & 15) / HL;
+        const bool valid = TOK ? ((vm_cur >> it) & 1u) != 0 : key < nvalid;
 #pragma unroll
         for (int gr = 0; gr < GR; ++gr)
-          s_p[key * G + 4 * gr + h] = key < nvalid ? sc[gr] * scale : -INFINITY;
+          s_p[key * G + 4 * gr + h] = valid ? sc[gr] * scale : -INFINITY;
       }
     }
     stage_sync();
@@ -217,9 +254,15 @@ __device__ __forceinline__ void attn_decode_body(
     }
     stage_sync();
     if constexpr (decltype(prefetch)::value) {
-      tok0 = stage_of(q + 1, nvalid);
+      if constexpr (TOK) {
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) kv[it] = load16_nt(kbuf + (tok0 + it * KPI + r) * RB + c * 16);
+        for (int it = 0; it < NIT; ++it) tk_cur[it] = tk_nxt[it];
+        vm_cur = vm_nxt;
+      } else {
+        tok0 = stage_of(q + 1, nvalid);
+      }
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) kv[it] = load16_nt(kbuf + key_row(tok0, it, tk_cur) * RB + c * 16);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -370,7 +413,7 @@ __device__ __forceinline__ void attn_decode_body(
 
 // fp32 rows hold twice the bytes in flight: one wave per SIMD, so the
 // registers past 256 spill to AGPRs instead of scratch memory
-template <typename Tag, int G, int WPG, int NPT>
+template <typename Tag, int G, int WPG, int NPT, bool TOK = false>
 __global__ __launch_bounds__(64 * WPG)
 __attribute__((amdgpu_waves_per_eu(DT<Tag>::kBytes == 2 ? SPARDA_ATTN_WAVES_PER_EU : 1)))
 void attn_decode_kernel(
@@ -380,8 +423,9 @@ void attn_decode_kernel(
     int kv_mode, int p_all, const int* __restrict__ q_pos, int hkv, const int32_t* __restrict__ slot_of, int n_slots,
     int bps, int splits, float scale) {
   // rows on the fast axis: a row's splits share an XCD
-  attn_decode_body<Tag, G, WPG, NPT>(blockIdx.x, blockIdx.y, q, kbuf, vbuf, idx, idx_out, scores, part_o, part_ml,
-                                     out, T, nB, k, kv_mode, p_all, q_pos, hkv, slot_of, n_slots, bps, splits, scale);
+  attn_decode_body<Tag, G, WPG, NPT, false, TOK>(blockIdx.x, blockIdx.y, q, kbuf, vbuf, idx, idx_out, scores, part_o,
+                                                 part_ml, out, T, nB, k, kv_mode, p_all, q_pos, hkv, slot_of, n_slots,
+                                                 bps, splits, scale);
 }
 
 // One decode layer in one launch, in an order a model can run: layer l's
@@ -611,6 +655,43 @@ hipError_t launch_decode_layer(const LayerLaunch& L, bool bf16, hipStream_t s) {
   SPARDA_LG_G(BF16Tag)
 #undef SPARDA_LG_G
 #undef SPARDA_LG
+  return hipGetLastError();
+}
+
+// Attention over a list of tokens per row (d.k = list length / 64 slots),
+// read where they sit in the cache: the split attention in token mode, then
+// the merge.
+template <typename Tag, int G>
+static void launch_attn_tokens_g(const void* q, const void* k, const void* v, const int32_t* tok_idx, void* out,
+                                 const AttnDims& d, void* ws, hipStream_t s) {
+  const DecodePartials pp = decode_attn_partials(ws, d);
+  const int bps = (d.k + pp.splits - 1) / pp.splits;
+  hipLaunchKernelGGL((attn_decode_kernel<Tag, G, 1, 0, true>), dim3(pp.rows, pp.splits), dim3(kWave), 0, s,
+                     (const uint8_t*)q, (const uint8_t*)k, (const uint8_t*)v, tok_idx, nullptr, nullptr, pp.part_o,
+                     pp.part_ml, (uint8_t*)out, d.T, d.nB, d.k, SPARDA_KV_CACHE_MODE, d.q_start, d.q_pos,
+                     d.q_pos_per_row ? 1 : d.Hkv, nullptr, 0, bps, pp.splits, d.scale);
+  launch_merge<Tag>(pp, out, s);
+}
+
+hipError_t launch_attn_tokens(const void* q, const void* k, const void* v, const int32_t* tok_idx, void* out,
+                              bool bf16, const AttnDims& d, void* ws, hipStream_t s) {
+  const int G = d.Hq / d.Hkv;
+#define SPARDA_AT(TAG, GG) launch_attn_tokens_g<TAG, GG>(q, k, v, tok_idx, out, d, ws, s)
+#define SPARDA_AT_G(TAG)                  \
+  switch (G) {                            \
+    case 1: SPARDA_AT(TAG, 1); break;     \
+    case 2: SPARDA_AT(TAG, 2); break;     \
+    case 4: SPARDA_AT(TAG, 4); break;     \
+    case 8: SPARDA_AT(TAG, 8); break;     \
+    default: return hipErrorInvalidValue; \
+  }
+  if (bf16) {
+    SPARDA_AT_G(BF16Tag)
+  } else {
+    SPARDA_AT_G(F32Tag)
+  }
+#undef SPARDA_AT_G
+#undef SPARDA_AT
   return hipGetLastError();
 }
 

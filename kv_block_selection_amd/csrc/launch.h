@@ -72,6 +72,11 @@ hipError_t launch_topk(const float* scores, int32_t* idx, int rows, int nB, int 
 // attn_decode.hip
 int decode_attn_splits(const AttnDims& d);
 size_t decode_attn_ws_bytes(const AttnDims& d);
+// The decode attention over a list of d.k * 64 tokens per row [rows, d.k * 64]
+// (-1 and entries after the row's position are skipped), read in place from
+// the cache; ws as for launch_attn_decode.
+hipError_t launch_attn_tokens(const void* q, const void* k, const void* v, const int32_t* tok_idx, void* out,
+                              bool bf16, const AttnDims& d, void* ws, hipStream_t s);
 hipError_t launch_attn_decode(const void* q, const void* k, const void* v, const int32_t* idx,
                               void* out, bool bf16, const AttnDims& d, void* ws, hipStream_t s);
 // the same after the row's top-k of scores [rows, nB] (written to idx), in one
@@ -123,21 +128,10 @@ hipError_t launch_prefetch(const void* host_k, const void* host_v, const int32_t
 
 // token.hip: the token-level Forecast variant. Token scores of rows [rows, T]
 // at the query position (per sequence: q_pos, else p); the top-k of rows
-// longer than 8192 (any length); the workspace of a token attention and the
-// compaction of the kept token rows into its staging.
-struct TokenAttnWs {
-  void* stage_k;     // [rows, k_tok, 128] in the storage dtype
-  void* stage_v;
-  int32_t* blk_idx;  // [rows, k_tok / 64]: 0, 1, ...
-  int* pos_eff;      // [rows]: valid staging slots - 1
-  void* attn_ws;     // the staging-mode attention's own workspace
-  size_t bytes;
-};
+// longer than 8192 (any length). The attention over the kept tokens is
+// launch_attn_tokens (attn_decode.hip).
 hipError_t launch_token_scores(const void* f, const void* k, float* scores, bool bf16, int rows, int T, int p,
                                const int* q_pos, int hkv, float scale, hipStream_t s);
 hipError_t launch_topk_long(const float* scores, int32_t* idx, int rows, int n, int k, hipStream_t s);
-TokenAttnWs token_attn_ws(void* ws, const AttnDims& token_d, int k_tok, bool bf16);
-hipError_t launch_token_gather(const void* k, const void* v, const int32_t* tok_idx, const TokenAttnWs& w, bool bf16,
-                               int rows, int T, int k_tok, int p, const int* q_pos, int hkv, hipStream_t s);
 
 }  // namespace sparda

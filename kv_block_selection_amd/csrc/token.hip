@@ -22,10 +22,8 @@
 //   from memory. Either way the kept indices are written in ascending order
 //   by a scan in index order (ties to the lower index), so the two paths give
 //   the same result.
-// token_gather_kernel: the kept token rows of K and V compacted into staging
-//   [rows, k_tok, 128] (valid entries in their order, the slots past the
-//   row's count zeroed), the row's count of valid entries, and the block list
-//   0 .. k_tok/64 - 1 through which the staging-mode attention reads it.
+// The attention over the kept tokens reads their K and V rows where they sit
+//   in the cache (the decode attention's token mode, attn_decode.hip).
 #include "common.h"
 #include "launch.h"
 #include "select_row.h"
@@ -381,92 +379,6 @@ __global__ __launch_bounds__(kLongThreads) void topk_long_kernel(const float* __
   for (int q = kk + t; q < k; q += kLongThreads) dst[q] = -1;
 }
 
-// Sum of one int per thread over a 256-thread workgroup (every thread gets it).
-__device__ __forceinline__ int sum256(int v, int* s_w) {
-  v = wave_isum(v);
-  __syncthreads();  // s_w may still be read from a previous use
-  if (threadIdx.x % kWave == 0) s_w[threadIdx.x / kWave] = v;
-  __syncthreads();
-  return s_w[0] + s_w[1] + s_w[2] + s_w[3];
-}
-
-template <typename Tag>
-__global__ __launch_bounds__(256) void token_gather_kernel(
-    const uint8_t* __restrict__ kbuf, const uint8_t* __restrict__ vbuf, const int32_t* __restrict__ tok_idx,
-    uint8_t* __restrict__ stage_k, uint8_t* __restrict__ stage_v, int32_t* __restrict__ blk_idx,
-    int* __restrict__ pos_eff, int T, int k_tok, int p_all, const int* __restrict__ q_pos, int hkv) {
-  using R = RowGeom<Tag>;
-  __shared__ int s_w[4];
-  __shared__ int32_t s_tok[256];
-  __shared__ int s_pos[256];
-  const long row = blockIdx.y;
-  const int p = row_position(q_pos, row, hkv, p_all, T);  // -1 .. T - 1
-  const int t = threadIdx.x;
-  const int32_t* ti = tok_idx + row * (long)k_tok;
-  const int c0 = blockIdx.x * 256;
-  auto valid = [&](int32_t x) { return x >= 0 && x <= p; };
-
-  // valid entries before this chunk and in the whole row
-  int pre = 0, all = 0;
-  for (int i0 = 0; i0 < k_tok; i0 += 256 * 8) {  // 8 loads per thread in flight
-    int32_t x[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * 256 + t;
-      x[u] = i < k_tok ? ti[i] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int v = valid(x[u]);
-      all += v;
-      pre += i0 + u * 256 + t < c0 ? v : 0;
-    }
-  }
-  pre = sum256(pre, s_w);
-  all = sum256(all, s_w);
-
-  // this chunk's entries: slot of each valid one = valid entries before it
-  const int i = c0 + t;
-  const int32_t tok = i < k_tok ? ti[i] : -1;
-  const int v = valid(tok);
-  const int incl = wave_incl_scan(v);
-  __syncthreads();
-  if (t % kWave == kWave - 1) s_w[t / kWave] = incl;
-  __syncthreads();
-  int before = incl - v;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) before += w < t / kWave ? s_w[w] : 0;
-  s_tok[t] = v ? tok : -1;
-  s_pos[t] = pre + before;
-  __syncthreads();
-
-  const int lane = t % R::LPR;
-  const int slot = t / R::LPR;
-  for (int e = slot; e < 256; e += R::SLOTS) {
-    const int32_t tk = s_tok[e];
-    if (tk >= 0) {
-      const long src = (row * (long)T + tk) * R::RB + lane * 16;
-      const long dst = (row * (long)k_tok + s_pos[e]) * R::RB + lane * 16;
-      store16(stage_k + dst, load16(kbuf + src));
-      store16(stage_v + dst, load16(vbuf + src));
-    }
-  }
-  // slots of this chunk's range past the row's count hold zeros
-  for (int e = slot; e < 256; e += R::SLOTS) {
-    const int s = c0 + e;
-    if (s < k_tok && s >= all) {
-      const long dst = (row * (long)k_tok + s) * R::RB + lane * 16;
-      store16(stage_k + dst, u32x4{0, 0, 0, 0});
-      store16(stage_v + dst, u32x4{0, 0, 0, 0});
-    }
-  }
-  if (blockIdx.x == 0) {
-    if (t == 0) pos_eff[row] = all - 1;  // staging slots 0 .. all - 1 are visible
-    const int nb = k_tok / kBlock;
-    for (int j = t; j < nb; j += 256) blk_idx[row * (long)nb + j] = j;
-  }
-}
-
 hipError_t launch_token_scores(const void* f, const void* k, float* scores, bool bf16, int rows, int T, int p,
                                const int* q_pos, int hkv, float scale, hipStream_t s) {
   if (bf16) {
@@ -485,37 +397,6 @@ hipError_t launch_token_scores(const void* f, const void* k, float* scores, bool
 
 hipError_t launch_topk_long(const float* scores, int32_t* idx, int rows, int n, int k, hipStream_t s) {
   hipLaunchKernelGGL(topk_long_kernel, dim3(rows), dim3(kLongThreads), 0, s, scores, idx, n, k);
-  return hipGetLastError();
-}
-
-TokenAttnWs token_attn_ws(void* ws, const AttnDims& token_d, int k_tok, bool bf16) {
-  const size_t rows = (size_t)token_d.B * token_d.Hkv;
-  const size_t esz = bf16 ? 2 : 4;
-  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  TokenAttnWs w;
-  char* b = (char*)ws;
-  const size_t stage = al(rows * k_tok * kHeadDim * esz);
-  const size_t blk = al(rows * (k_tok / kBlock) * sizeof(int32_t));
-  const size_t pos = al(rows * sizeof(int));
-  w.stage_k = b;
-  w.stage_v = b + stage;
-  w.blk_idx = (int32_t*)(b + 2 * stage);
-  w.pos_eff = (int*)(b + 2 * stage + blk);
-  w.attn_ws = b + 2 * stage + blk + pos;
-  w.bytes = 2 * stage + blk + pos + decode_attn_ws_bytes(token_d);
-  return w;
-}
-
-hipError_t launch_token_gather(const void* k, const void* v, const int32_t* tok_idx, const TokenAttnWs& w, bool bf16,
-                               int rows, int T, int k_tok, int p, const int* q_pos, int hkv, hipStream_t s) {
-  const dim3 grid((unsigned)((k_tok + 255) / 256), rows);
-#define SPARDA_GATHER(TAG)                                                                                          \
-  hipLaunchKernelGGL(token_gather_kernel<TAG>, grid, dim3(256), 0, s, (const uint8_t*)k, (const uint8_t*)v,       \
-                     tok_idx, (uint8_t*)w.stage_k, (uint8_t*)w.stage_v, w.blk_idx, w.pos_eff, T, k_tok, p, q_pos, \
-                     hkv)
-  if (bf16) SPARDA_GATHER(BF16Tag);
-  else SPARDA_GATHER(F32Tag);
-#undef SPARDA_GATHER
   return hipGetLastError();
 }
 

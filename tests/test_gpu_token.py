@@ -149,24 +149,23 @@ def test_token_attention_ragged_positions_and_padding(gpu):
 
 
 def test_token_attention_short_cache(gpu):
-    """A cache shorter than one 64-token block (T = 40, 1 and 63): the
-    workspace is sized by the kept-token budget alone, and the kept list
-    (written by hand: the top-k needs k <= T) is padded with -1."""
+    """A cache shorter than one 64-token block (T = 40, 1 and 63): the kept
+    list (written by hand: the top-k needs k <= T) is padded with -1, and the
+    64-entry list is one range, so the call needs no workspace."""
     for T in (40, 1, 63):
         w = small("bf16", T=T)
         k_tok = 64
         say("token attention, short cache T =", T)
         Q, K, V = gen(w, "Q"), gen(w, "K"), gen(w, "V")
         need = kbs.workspace_bytes(kbs.OP_TOKEN_ATTN, w.B, w.Hq, w.Hkv, 1, T, k_tok)
-        assert need > 0
+        assert need == 0
         rng = np.random.default_rng(T)
         idx = np.full((w.B, w.Hkv, 1, k_tok), -1, dtype=np.int32)
         for b in range(w.B):
             for h in range(w.Hkv):
                 keep = rng.permutation(T)[: max(1, T // 2)]
                 idx[b, h, 0, rng.choice(k_tok, keep.size, replace=False)] = keep
-        ws = torch.empty(need, dtype=torch.uint8, device=DEV)
-        out = kbs.token_sparse_attn(Q, K, V, torch.from_numpy(idx).to(DEV), w.q_start, scale=w.scale, ws=ws)
+        out = kbs.token_sparse_attn(Q, K, V, torch.from_numpy(idx).to(DEV), w.q_start, scale=w.scale)
         torch.cuda.synchronize()
         ref = oracle.token_sparse_attention(parity.to_f64(Q), parity.to_f64(K), parity.to_f64(V), idx, w.q_start,
                                             w.scale)
