@@ -12,9 +12,10 @@
 //   after p; an HBM-bound GEMV over every key row (16 lanes per 256-byte row,
 //   all of a workgroup's loads in flight before the first is used).
 // topk_long_kernel: the top-k rule for rows too long for the LDS-resident
-//   top-k (any length): one 1024-thread workgroup per row. A strided sample
-//   of 4096 scores gives a threshold t whose count in the row is expected a
-//   little above k; one streaming pass keeps every score at or above t, in
+//   top-k (any length): one 1024-thread workgroup per row. A sample of 4096
+//   scores (256 runs of 16 spread over the row) gives a threshold t whose
+//   count in the row is expected a little above k; one streaming pass keeps
+//   every score at or above t, in
 //   index order, in LDS; when they are at least k (so t is at or below the
 //   k-th largest score, and every kept score is among them) and fit, the
 //   rule runs on them alone. Otherwise (heavy ties, a k near the row length,
@@ -35,6 +36,7 @@ constexpr int kTokIter = 32;       // key rows per thread group in flight
 constexpr int kLongThreads = 1024;  // threads of a long-row top-k workgroup
 constexpr int kLongEPT = 8;         // consecutive elements per thread in the output scan
 constexpr int kLongSample = 4096;   // sampled scores for the threshold
+constexpr int kLongSampleRuns = 256;  // runs of kLongSample / 256 consecutive scores
 constexpr int kLongCand = 8192;     // candidates the sampled path keeps in LDS (8 per thread)
 constexpr int kLongSeg = 32;        // segments of kLongThreads scores per batch of the candidate pass
 
@@ -164,10 +166,15 @@ __global__ __launch_bounds__(kLongThreads) void topk_long_kernel(const float* __
   // sample's slack of 16 positions) fits well inside the LDS store.
   const int r_sample = (int)(((long)6 * k * kLongSample + 5L * n - 1) / (5L * n)) + 16;
   if ((long)r_sample * n <= (long)kLongSample * (kLongCand * 4 / 5)) {
-    // the threshold: the r-th largest of kLongSample evenly spread scores
+    // the threshold: the r-th largest of kLongSample scores, taken as
+    // kLongSampleRuns runs of consecutive scores spread evenly over the row
+    // (16 lanes read one 64-byte run; a single strided score per 128-byte
+    // line would touch every line of the row)
     int ns = 0;
     for (int j = t; j < kLongSample; j += kLongThreads) {
-      const uint32_t key = order_key(src[((long)j * n) / kLongSample]);
+      constexpr int kRun = kLongSample / kLongSampleRuns;
+      const long i = ((long)(j / kRun) * n) / kLongSampleRuns + j % kRun;  // n > 8192: runs never overlap
+      const uint32_t key = order_key(src[i]);
       s_key[j] = key;
       ns += key != 0u;
     }
