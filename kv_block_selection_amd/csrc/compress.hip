@@ -41,11 +41,12 @@ __global__ __launch_bounds__(256) void compress_wave_kernel(const uint8_t* __res
   const uint8_t* src = k + row * (long)T * RB + c16 * 16;
   uint8_t* dst = kc + row * (long)W * RB + c16 * 16;
 
-  // the 16 token rows of half h (rows past the last half needed are not read)
+  // the 16 token rows of half h; halves past w1 (never summed into a stored
+  // window) read half w1 instead, so every load is unconditional
   auto load_half = [&](int h, u32x4 (&v)[kStride]) {
-    const bool ok = h <= w1;
+    const long t0 = (long)min(h, w1) * kStride;
 #pragma unroll
-    for (int t = 0; t < kStride; ++t) v[t] = ok ? load16_nt(src + (long)(h * kStride + t) * RB) : u32x4{0, 0, 0, 0};
+    for (int t = 0; t < kStride; ++t) v[t] = load16_nt(src + (t0 + t) * RB);
   };
   auto half_sum = [&](const u32x4 (&v)[kStride], float* acc) {
 #pragma unroll
@@ -64,21 +65,21 @@ __global__ __launch_bounds__(256) void compress_wave_kernel(const uint8_t* __res
   };
 
   // Step s covers windows w0 + 4 s + g. Its halves' sums (a) come from the
-  // step before; the halves of step s + 1 (one step ahead of use) were loaded
-  // during step s - 1, and step s issues the loads of step s + 2.
+  // step before; the halves of step s + 1 were loaded during step s - 1, and
+  // step s issues the loads of step s + 2 into the buffer its own halves left
+  // (summed during step s - 1). The two buffers alternate, so no register that
+  // a load in flight fills is copied, and the loads of step s + 2 stay in
+  // flight while step s sums.
   const int nsteps = (w1 - w0 + 3) / 4;
-  u32x4 v_next[kStride], v_after[kStride];
+  u32x4 vA[kStride], vB[kStride];
   float a[8], n[8];
-  {
-    u32x4 v0[kStride];
-    load_half(w0 + g, v0);
-    load_half(w0 + 4 + g, v_next);
-    half_sum(v0, a);
-  }
-  for (int st = 0; st < nsteps; ++st) {
+  load_half(w0 + g, vA);
+  load_half(w0 + 4 + g, vB);
+  half_sum(vA, a);
+  auto step = [&](int st, const u32x4 (&cur)[kStride], u32x4 (&fre)[kStride]) {
     const int hb = w0 + 4 * st;  // this step's first half
-    load_half(hb + 8 + g, v_after);
-    half_sum(v_next, n);  // halves hb + 4 .. hb + 7
+    load_half(hb + 8 + g, fre);
+    half_sum(cur, n);  // halves hb + 4 .. hb + 7
     // window hb + g = half hb + g + half hb + g + 1: group g + 1's sum of this
     // step, or for g = 3 group 0's of the next
     float b[8];
@@ -91,9 +92,13 @@ __global__ __launch_bounds__(256) void compress_wave_kernel(const uint8_t* __res
     if (w < w1) store16(dst + (long)w * RB, window_from_halves<BF16Tag>(a, b));
 #pragma unroll
     for (int e = 0; e < 8; ++e) a[e] = n[e];
-#pragma unroll
-    for (int t = 0; t < kStride; ++t) v_next[t] = v_after[t];
+  };
+  int st = 0;
+  for (; st + 1 < nsteps; st += 2) {
+    step(st, vB, vA);
+    step(st + 1, vA, vB);
   }
+  if (st < nsteps) step(st, vB, vA);
 }
 
 // fp32 (a 32-lane group per run of windows; the bf16 form above)
