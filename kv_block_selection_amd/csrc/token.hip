@@ -12,15 +12,14 @@
 //   after p; an HBM-bound GEMV over every key row (16 lanes per 256-byte row,
 //   all of a workgroup's loads in flight before the first is used).
 // topk_long_kernel: the top-k rule for rows too long for the LDS-resident
-//   top-k (any length): one 1024-thread workgroup per row. A sample of 4096
-//   scores (256 runs of 16 spread over the row) gives a threshold t whose
-//   count in the row is expected a little above k; one streaming pass keeps
-//   every score at or above t, in
-//   index order, in LDS; when they are at least k (so t is at or below the
-//   k-th largest score, and every kept score is among them) and fit, the
-//   rule runs on them alone. Otherwise (heavy ties, a k near the row length,
-//   few candidates) four 8-bit radix passes run over the order keys streamed
-//   from memory. Either way the kept indices are written in ascending order
+//   top-k (any length): one 1024-thread workgroup per row. A sample of 2048
+//   scores spread evenly over the row gives a threshold t whose count in the
+//   row is expected a little above k; one streaming pass keeps every score
+//   at or above t, in index order, in LDS; when they are at least k (so t is
+//   at or below the k-th largest score, and every kept score is among them)
+//   and fit, the rule runs on them alone. Otherwise (heavy ties, a k near the
+//   row length, few candidates) four 8-bit radix passes run over the order
+//   keys streamed from memory. Either way the kept indices are written in ascending order
 //   by a scan in index order (ties to the lower index), so the two paths give
 //   the same result.
 // The attention over the kept tokens reads their K and V rows where they sit
@@ -35,8 +34,7 @@ namespace sparda {
 constexpr int kTokIter = 32;       // key rows per thread group in flight
 constexpr int kLongThreads = 1024;  // threads of a long-row top-k workgroup
 constexpr int kLongEPT = 8;         // consecutive elements per thread in the output scan
-constexpr int kLongSample = 4096;   // sampled scores for the threshold
-constexpr int kLongSampleRuns = 256;  // runs of kLongSample / 256 consecutive scores
+constexpr int kLongSample = 2048;   // sampled scores for the threshold
 constexpr int kLongCand = 8192;     // candidates the sampled path keeps in LDS (8 per thread)
 constexpr int kLongSeg = 32;        // segments of kLongThreads scores per batch of the candidate pass
 
@@ -166,15 +164,13 @@ __global__ __launch_bounds__(kLongThreads) void topk_long_kernel(const float* __
   // sample's slack of 16 positions) fits well inside the LDS store.
   const int r_sample = (int)(((long)6 * k * kLongSample + 5L * n - 1) / (5L * n)) + 16;
   if ((long)r_sample * n <= (long)kLongSample * (kLongCand * 4 / 5)) {
-    // the threshold: the r-th largest of kLongSample scores, taken as
-    // kLongSampleRuns runs of consecutive scores spread evenly over the row
-    // (16 lanes read one 64-byte run; a single strided score per 128-byte
-    // line would touch every line of the row)
+    // the threshold: the r-th largest of kLongSample scores spread evenly over
+    // the row (one per 64 at 128K: every 64-key block of a token row is
+    // represented, since neighbouring scores can be correlated, and only half
+    // of the row's 128-byte lines are touched)
     int ns = 0;
     for (int j = t; j < kLongSample; j += kLongThreads) {
-      constexpr int kRun = kLongSample / kLongSampleRuns;
-      const long i = ((long)(j / kRun) * n) / kLongSampleRuns + j % kRun;  // n > 8192: runs never overlap
-      const uint32_t key = order_key(src[i]);
+      const uint32_t key = order_key(src[((long)j * n) / kLongSample]);
       s_key[j] = key;
       ns += key != 0u;
     }
