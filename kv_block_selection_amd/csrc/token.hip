@@ -183,12 +183,12 @@ __global__ __launch_bounds__(kLongThreads) void topk_long_kernel(const float* __
       // threshold only admits a few more candidates
       lds_radix_select<2>(s_key, kLongSample, min(r_sample, n_sampled), hist16, hist, &s_digit, &s_above, t0,
                           unused);
-      // one pass over the row: every key >= t0 (t0 > 0: the r-th key is not
-      // -inf, so its top 16 bits are not all zero) into
-      // LDS in index order. A batch is kLongSeg segments of kLongThreads
-      // consecutive scores, one per thread (coalesced loads, all in flight);
-      // a candidate's place is its lane's rank in its wave (ballot) plus an
-      // exclusive prefix over the batch's (segment, wave) counts.
+      // One pass over the row: every key >= t0 into LDS in index order (t0 >
+      // 0: the r-th key is not -inf, so its top 16 bits are not all zero). A
+      // batch is kLongSeg segments of kLongThreads consecutive scores, one per
+      // thread (coalesced loads, all in flight); a candidate's place is its
+      // lane's rank in its wave (ballot) plus an exclusive prefix over the
+      // batch's (segment, wave) counts.
       constexpr int kWaves = kLongThreads / kWave;
       int count = 0;
       for (long c0 = 0; c0 < n && count <= kLongCand; c0 += (long)kLongThreads * kLongSeg) {
@@ -206,7 +206,8 @@ __global__ __launch_bounds__(kLongThreads) void topk_long_kernel(const float* __
           if (lane == 0) s_cnt[j * kWaves + wid] = __popcll(m);
         }
         __syncthreads();
-        // exclusive prefix over the kLongSeg x kWaves counts (threads 0 .. 255)
+        // exclusive prefix over the kLongSeg x kWaves counts, in index order
+        // (one count per thread of the first kLongSeg * kWaves)
         const int v = t < kLongSeg * kWaves ? s_cnt[t] : 0;
         const int incl = wave_incl_scan(v);
         if (lane == kWave - 1 && wid < kLongSeg * kWaves / kWave) s_tot[wid] = incl;
@@ -231,8 +232,7 @@ __global__ __launch_bounds__(kLongThreads) void topk_long_kernel(const float* __
         count += batch;
         __syncthreads();  // s_cnt and s_tot are rewritten by the next batch
       }
-      __syncthreads();  // the candidates are in
-      if (count >= k && count <= kLongCand) {
+      if (count >= k && count <= kLongCand) {  // the last batch's barrier published them
         uint32_t tau;
         int take_eq;
         lds_radix_select<4>(s_key, count, k, hist16, hist, &s_digit, &s_above, tau, take_eq);
