@@ -10,7 +10,8 @@
 //
 // token_scores_kernel: scores [rows, T] = scale * f . K[t] for t <= p and -inf
 //   after p; an HBM-bound GEMV over every key row (16 lanes per 256-byte row,
-//   all of a workgroup's loads in flight before the first is used).
+//   all of a workgroup's loads in flight before the first is used; the
+//   workgroup's scores leave through LDS as 16-byte pieces).
 // topk_long_kernel: the top-k rule for rows too long for the LDS-resident
 //   top-k (any length): one 1024-thread workgroup per row. A sample of 2048
 //   scores spread evenly over the row gives a threshold t whose count in the
@@ -57,11 +58,35 @@ __global__ __launch_bounds__(256) void token_scores_kernel(const uint8_t* __rest
     const long t = t0 + it * R::SLOTS + slot;
     kv[it] = t <= p ? load16_nt(base + t * R::RB) : u32x4{0, 0, 0, 0};
   }
+  // The workgroup's scores are gathered in LDS and leave as 16-byte pieces
+  // through buffer stores with the sc1 cache-policy bit (device scope): at
+  // 128K this takes the kernel from 0.70 to 0.66 ms against one 4-byte store
+  // per key row (0.72 ms with plain 16-byte stores). A row whose scores do not
+  // start 16-byte aligned takes plain 4-byte stores.
+  constexpr int kRun = kTokIter * R::SLOTS;  // scores of one workgroup
+  __shared__ float s_sc[kRun];
 #pragma unroll
   for (int it = 0; it < kTokIter; ++it) {
     const long t = t0 + it * R::SLOTS + slot;
     const float s = group_sum<R::LPR>(dot16<Tag>(fv, kv[it], 0.f));
-    if (lane == 0 && t < T) scores[row * (long)T + t] = t <= p ? s * scale : -INFINITY;
+    if (lane == 0) s_sc[it * R::SLOTS + slot] = t <= p ? s * scale : -INFINITY;
+  }
+  __syncthreads();
+  static_assert(kRun / 4 <= 256, "one 16-byte piece per thread");
+  const int i = threadIdx.x;
+  if (i < kRun / 4) {
+    float* run = scores + row * (long)T + t0;
+    const long t = t0 + 4 * i;
+    const float4 v = *reinterpret_cast<const float4*>(&s_sc[4 * i]);
+    if (((uintptr_t)run & 15) == 0 && t + 3 < T) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(run, (short)0, kRun * 4, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, 16 * i, 0, 16);
+    } else {
+      const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (t + j < T) run[4 * i + j] = e[j];
+    }
   }
 }
 

@@ -53,6 +53,26 @@ def test_select_tokens_parity(gpu, dtype, ragged):
     parity.check_scores(parity.to_f64(s), ref)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_select_tokens_unaligned_rows(gpu, dtype):
+    """Rows of an odd length T, and an output that starts 4 bytes past a
+    16-byte boundary: the scores that cannot leave as aligned 16-byte pieces
+    take the kernel's 4-byte stores. The floats around the output stay
+    untouched."""
+    w = small(dtype, T=64 * 9 + 13)
+    say("select_tokens unaligned", dtype, "T", w.T)
+    F, K = gen(w, "F"), gen(w, "K")
+    n = w.B * w.Hkv * w.T
+    buf = torch.full((n + 2,), 7.0, dtype=torch.float32, device=DEV)
+    out = buf[1 : n + 1].view(w.B, w.Hkv, 1, w.T)
+    assert out.data_ptr() % 16 != 0
+    kbs.select_tokens(F, K, w.q_start, scale=w.scale, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.forecast_token_scores(parity.to_f64(F), parity.to_f64(K), w.q_start, w.scale)
+    parity.check_scores(parity.to_f64(out), ref)
+    assert float(buf[0]) == 7.0 and float(buf[-1]) == 7.0
+
+
 def test_select_tokens_nothing_visible(gpu):
     w = small()
     F, K = gen(w, "F"), gen(w, "K")
