@@ -376,7 +376,7 @@ int sparda_prefetch_blocks_cached(const void* host_k, const void* host_v, const 
  * layer ahead; the first layer, which also scores its own blocks, has n_f = 2
  * (set 0: its same-layer Forecast, set 1: the next layer's). n_f = 0 skips the
  * Forecast (f may be NULL). Supported: bf16, d = 128, D a positive multiple of
- * 512, 0 <= n_f <= 8. All pointers are device memory, 16-byte aligned; the
+ * 512 up to 2^24, 0 <= n_f <= 8 (else SPARDA_ERR_UNSUPPORTED / _INVALID_ARG). All pointers are device memory, 16-byte aligned; the
  * outputs must not overlap the inputs. B = 0 is a no-op. Async on stream.
  */
 int sparda_project_qkvf(const void* x, const void* w, void* q, void* k, void* v, void* f, int dtype, int B,

@@ -586,7 +586,8 @@ SPARDA_EXPORT int sparda_project_qkvf(const void* x, const void* w, void* q, voi
   CHECK(d == 128, SPARDA_ERR_UNSUPPORTED, "project_qkvf: head dim %d (only 128 supported)", d);
   CHECK(B >= 0 && Hkv >= 1 && Hq >= 1 && Hq % Hkv == 0, SPARDA_ERR_INVALID_ARG,
         "project_qkvf: need B >= 0, Hq and Hkv >= 1, Hq %% Hkv == 0 (B=%d Hq=%d Hkv=%d)", B, Hq, Hkv);
-  CHECK(D > 0 && D % 512 == 0, SPARDA_ERR_UNSUPPORTED, "project_qkvf: D=%d must be a positive multiple of 512", D);
+  CHECK(D > 0 && D % 512 == 0 && D <= (1 << 24), SPARDA_ERR_UNSUPPORTED,
+        "project_qkvf: D=%d must be a positive multiple of 512 up to 2^24", D);
   CHECK(n_f >= 0 && n_f <= 8, SPARDA_ERR_INVALID_ARG, "project_qkvf: n_f=%d outside 0..8", n_f);
   const long rows = (long)(Hq + 2L * Hkv + (long)n_f * Hkv) * d;
   CHECK(rows / 16 <= 2147483647L && (long)B * D < (1L << 40) && rows * (long)D < (1L << 40), SPARDA_ERR_UNSUPPORTED,

@@ -14,14 +14,18 @@
 // At decode the batch is small (16 to 64 sequences), so the GEMM streams W once
 // from HBM (N x D x 2 bytes) and is HBM-bound; the products run on the matrix
 // cores (v_mfma_f32_16x16x32_bf16) with rows of W as the A operand and rows of x
-// as the B operand. A workgroup owns 32 rows of W (two 16-row tiles) and up
-// to 64 sequences; its four waves take a quarter of D each and add their
-// partial tiles in LDS. Each x fragment a wave loads feeds both row tiles:
-// x is re-read once per workgroup, so its bytes are B/32 of W's. A 128-column step is four MFMAs; MFMA j of a step consumes columns
-// 32 j + 8 g .. 32 j + 8 g + 7 in lane group g (lanes 16 g .. 16 g + 15), in W
-// and in x alike (the sum over c may run in any order as long as both
-// operands follow the same one), so each load instruction reads 64 contiguous
-// bytes from each of 16 rows. W streams a chunk of steps ahead of use.
+// as the B operand. A workgroup owns ROWS rows of W (16-row tiles; 32 in use)
+// and up to 64 sequences, and walks D in chunks of 128 columns. Each chunk's 32 weight
+// rows and the sequences' hidden-state rows (256 bytes each) come straight
+// from global memory into an LDS ring by direct loads, DEPTH - 1 chunks ahead
+// of the one being multiplied, so a wave never waits on a load it has just
+// issued and no register holds data in flight. Within a chunk, wave v takes
+// the 32-column slice v: MFMA fragments of the two row tiles and of every
+// sequence tile come from LDS (lane group g holds columns 8 g .. 8 g + 7 of the
+// slice, in W and in x alike: the sum over c may run in any order as long as
+// both operands follow the same one), and the four waves' partial tiles are
+// summed in LDS at the end. x is read once per workgroup, so its bytes are
+// B/ROWS of W's.
 #include "common.h"
 #include "launch.h"
 #include "prefill_lds.h"
@@ -30,129 +34,116 @@ namespace sparda {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kProjRows = 16;   // rows of W per tile
-constexpr int kProjStep = 128;  // columns per step
+constexpr int kProjChunk = 128;   // columns per chunk: 256 bytes of a row
 constexpr int kProjMaxTiles = 4;  // 16-sequence tiles per workgroup
 
-template <int MT, int NT, int CS>
+// MT sequence tiles; DEPTH chunk buffers in LDS. A chunk buffer holds ROWS + 16 MT
+// rows of 256 bytes (W's rows, then the sequences'), granule q of row r at
+// slot q ^ (r % 16) (the swizzle of prefill_lds.h), so that the 16 rows of a
+// fragment read hit 16 different bank groups.
+template <int ROWS, int MT, int DEPTH>
 __global__ __launch_bounds__(256) void qkvf_kernel(const uint8_t* __restrict__ x, const uint8_t* __restrict__ w,
                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ k,
                                                    uint8_t* __restrict__ v, uint8_t* __restrict__ f, int B, int D,
                                                    int Hq, int Hkv) {
-  __shared__ f32x4 s_acc[3][NT][MT][kWave];
+  constexpr int NT = ROWS / 16;
+  constexpr int kRows = ROWS + 16 * MT;  // rows of a chunk buffer
+  constexpr int kBufBytes = kRows * kRowBytes;
+  constexpr int kPerWave = kRows / 16;        // direct loads (4 rows each) per wave per chunk
+  constexpr int kWLoads = ROWS / 16;     // of them, loads of W's rows
+  static_assert(ROWS % 16 == 0 && kRows % 16 == 0, "rows split evenly over four waves");
+  static_assert(DEPTH >= 2 && (DEPTH - 2) * kPerWave <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[DEPTH][kBufBytes];
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int r16 = lane & 15;  // row of W (A) and sequence of the tile (B)
   const int g = lane >> 4;    // column group
-  const long n0 = (long)blockIdx.x * (kProjRows * NT);
+  const long n0 = (long)blockIdx.x * ROWS;
   const int b0 = blockIdx.y * (16 * kProjMaxTiles);
-  const int kq = D / 4;
-  const int c0 = wave * kq, c1 = c0 + kq;
+  const uint8_t* wbase = w + n0 * D * 2;
+  const uint8_t* xbase = x + (long)b0 * D * 2;
 
-  const uint8_t* wrow[NT];
+  // Load u of this wave fills LDS bytes [(4 u + wave) KiB, + 1 KiB) of a buffer:
+  // buffer rows 4 (4 u + wave) .. + 3, W's for the first ROWS / 16 loads, the
+  // sequences' after (sequences past B read row B - 1; their outputs are not
+  // stored). Offsets are 32-bit: with D <= 2^24, 64 rows stay under 2 GiB.
+  uint32_t roff[kPerWave];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) wrow[nt] = w + ((n0 + 16 * nt + r16) * (long)D) * 2;
-  const uint8_t* xrow[MT];
-  bool xok[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int b = b0 + 16 * mt + r16;
-    xok[mt] = b < B;
-    xrow[mt] = x + ((long)min(b, B - 1) * D) * 2;
+  for (int u = 0; u < kPerWave; ++u) {
+    const int rr = 4 * (4 * u + wave) + (lane >> 4);
+    const uint32_t gran = (uint32_t)(((lane & 15) ^ (rr & 15)) << 4);
+    const int src_row = u < kWLoads ? rr : min(b0 + rr - ROWS, B - 1) - b0;
+    roff[u] = (uint32_t)src_row * (uint32_t)D * 2u + gran;
   }
+  auto issue = [&](int c, int buf) {
+    const uint32_t m0 = lds_addr(s_ring[buf]);
+#pragma unroll
+    for (int u = 0; u < kPerWave; ++u)
+      dma16_sv_m0(u < kWLoads ? wbase : xbase, roff[u] + (uint32_t)c * (kProjChunk * 2),
+                  m0 + (uint32_t)((4 * u + wave) * kWave * 16));
+  };
+  // wait until at most n of this wave's direct loads are in flight
+  auto wait_loads = [&](int chunks_after) {
+    switch (chunks_after) {
+#define SPARDA_WAIT(N) \
+  case N:              \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(N * kPerWave)); break;
+      SPARDA_WAIT(0) SPARDA_WAIT(1) SPARDA_WAIT(2) SPARDA_WAIT(3) SPARDA_WAIT(4) SPARDA_WAIT(5) SPARDA_WAIT(6)
+      SPARDA_WAIT(7) SPARDA_WAIT(8)
+#undef SPARDA_WAIT
+      default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+  };
+  static_assert(DEPTH - 2 <= 8, "wait_loads covers up to 8 chunks in flight behind the awaited one");
 
-  // Steps come in chunks of CS (CS * 128 columns). A chunk's x fragments are
-  // loaded first, then the next chunk's W fragments, then the chunk is
-  // computed: loads complete in issue order, so waiting for this chunk's x
-  // never waits for the W loads in flight behind it. Each x fragment serves
-  // the NT row tiles of the wave.
   f32x4 acc[NT][MT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // lane group g takes 8 columns of each 32-column slice j: one load
-  // instruction reads 64 contiguous bytes of each of 16 rows
-  auto wload_chunk = [&](u32x4 (&wf)[NT][CS][4], int c) {
+  const int nch = D / kProjChunk;
+#pragma unroll
+  for (int c = 0; c < DEPTH - 1; ++c)
+    if (c < nch) issue(c, c);
+  const int q_slice = 4 * wave + g;  // this lane's logical granule in every row
+  for (int c = 0, buf = 0; c < nch; ++c, buf = buf + 1 == DEPTH ? 0 : buf + 1) {
+    // chunk c's loads (each wave waits for its own) are in; the barrier makes
+    // them visible to every wave and tells that chunk c - 1's buffer is free
+    wait_loads(min(DEPTH - 2, nch - 1 - c));
+    lds_sync();
+    if (c + DEPTH - 1 < nch) issue(c + DEPTH - 1, buf == 0 ? DEPTH - 1 : buf - 1);
+    const uint8_t* cb = s_ring[buf];
+    u32x4 af[NT], bf[MT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) af[nt] = *reinterpret_cast<const u32x4*>(cb + swz(16 * nt + r16, q_slice));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) bf[mt] = *reinterpret_cast<const u32x4*>(cb + swz(ROWS + 16 * mt + r16, q_slice));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int s = 0; s < CS; ++s)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wf[nt][s][j] = load16(wrow[nt] + (c + s * kProjStep + 32 * j + 8 * g) * 2);
-  };
-  const int nchunks = kq / (CS * kProjStep);
-  // workgroups start at different chunks, so at any moment they read
-  // different parts of x (every wave of a quarter reads the same x columns)
-  const int rot = (int)(blockIdx.x % (unsigned)max(nchunks, 1));
-  auto chunk_col = [&](int i) { const int r = i + rot; return c0 + (r >= nchunks ? r - nchunks : r) * CS * kProjStep; };
-  u32x4 wa[NT][CS][4], wb[NT][CS][4];
-  if (nchunks > 0) wload_chunk(wa, chunk_col(0));
-  for (int i = 0; i < nchunks; ++i) {
-    const int c = chunk_col(i);
-    u32x4 xf[CS][MT][4];
-#pragma unroll
-    for (int s = 0; s < CS; ++s)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          xf[s][mt][j] = load16(xrow[mt] + (c + s * kProjStep + 32 * j + 8 * g) * 2);
-          if (!xok[mt]) xf[s][mt][j] = u32x4{0, 0, 0, 0};
-        }
-    if (i + 1 < nchunks) wload_chunk(wb, chunk_col(i + 1));
-#pragma unroll
-    for (int s = 0; s < CS; ++s)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[nt][s][j]), as_bf16x8(xf[s][mt][j]),
-                                                                  acc[nt][mt], 0, 0, 0);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int s = 0; s < CS; ++s)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wa[nt][s][j] = wb[nt][s][j];
-  }
-  // steps left over when a quarter of D is not a whole number of chunks
-  for (int c = c0 + nchunks * CS * kProjStep; c < c1; c += kProjStep) {
-    u32x4 wf[NT][4];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) wf[nt][j] = load16(wrow[nt] + (c + 32 * j + 8 * g) * 2);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x4 xf = load16(xrow[mt] + (c + 32 * j + 8 * g) * 2);
-        if (!xok[mt]) xf = u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wf[nt][j]), as_bf16x8(xf), acc[nt][mt], 0,
-                                                                0, 0);
-      }
+        acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[nt]), as_bf16x8(bf[mt]), acc[nt][mt], 0, 0, 0);
   }
 
-  // sum the four quarters of D
+  // sum the four waves' partial tiles (the ring is free once every wave is past
+  // its last chunk)
+  lds_sync();
+  f32x4* s_acc = reinterpret_cast<f32x4*>(&s_ring[0][0]);  // [3][NT][MT][kWave]
+  static_assert(3 * NT * MT * kWave * 16 <= DEPTH * kBufBytes, "partial tiles fit the ring");
   if (wave > 0) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) s_acc[wave - 1][nt][mt][lane] = acc[nt][mt];
+      for (int mt = 0; mt < MT; ++mt) s_acc[((wave - 1) * NT + nt) * MT * kWave + mt * kWave + lane] = acc[nt][mt];
   }
-  __syncthreads();
+  lds_sync();
   if (wave != 0) return;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 3; ++r) acc[nt][mt] += s_acc[r][nt][mt][lane];
+      for (int r = 0; r < 3; ++r) acc[nt][mt] += s_acc[(r * NT + nt) * MT * kWave + mt * kWave + lane];
 
   // The workgroup's 16 * NT rows sit inside one head of one output (they divide 128).
   const int head = (int)(n0 / kHeadDim);
@@ -193,16 +184,18 @@ hipError_t launch_project_qkvf(const void* x, const void* w, void* q, void* k, v
   const long rows = (long)(Hq + 2 * Hkv + n_f * Hkv) * kHeadDim;
   const int tiles = (B + 15) / 16;
   const int by = (B + 16 * kProjMaxTiles - 1) / (16 * kProjMaxTiles);
-  // a wave takes two row tiles, so each x fragment it loads feeds two
-  // products; from 48 sequences on, chunks are one step (register budget)
-#define SPARDA_PROJ(MT, NT, CS)                                                                                \
-  hipLaunchKernelGGL((qkvf_kernel<MT, NT, CS>), dim3((unsigned)(rows / (kProjRows * NT)), by), dim3(256), 0, s, \
+  // 32 rows of W per workgroup and 5 or 4 chunk buffers (60 to 96 KiB of LDS):
+  // at B = 16 and 64, 13.0 and 18.1 us against 13.8 and 18.7 with 10 to 6
+  // buffers, 13.1 and 18.8 with 4 and 3, 14.0 and 22.1 with 16 rows and 15.7
+  // and 22.2 with 64 rows per workgroup
+#define SPARDA_PROJ(R, MT, DEPTH)                                                                                \
+  hipLaunchKernelGGL((qkvf_kernel<R, MT, DEPTH>), dim3((unsigned)(rows / R), by), dim3(256), 0, s,               \
                      (const uint8_t*)x, (const uint8_t*)w, (uint8_t*)q, (uint8_t*)k, (uint8_t*)v, (uint8_t*)f, B, \
                      D, Hq, Hkv)
-  if (tiles <= 1) SPARDA_PROJ(1, 2, 2);
-  else if (tiles <= 2) SPARDA_PROJ(2, 2, 2);
-  else if (tiles <= 3) SPARDA_PROJ(3, 2, 1);
-  else SPARDA_PROJ(4, 2, 1);
+  if (tiles <= 1) SPARDA_PROJ(32, 1, 5);
+  else if (tiles <= 2) SPARDA_PROJ(32, 2, 5);
+  else if (tiles <= 3) SPARDA_PROJ(32, 3, 4);
+  else SPARDA_PROJ(32, 4, 4);
 #undef SPARDA_PROJ
   return hipGetLastError();
 }

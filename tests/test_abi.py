@@ -218,6 +218,7 @@ def test_prefetch_cached_validation(lib, args, status, needle):
     (dict(dtype=0), 2, b"bf16"),
     (dict(d=64), 2, b"head dim"),
     (dict(D=500), 2, b"multiple of 512"),
+    (dict(D=1 << 25), 2, b"up to 2^24"),
     (dict(Hq=6, Hkv=4), 1, b"Hq % Hkv"),
     (dict(n_f=9), 1, b"n_f"),
     (dict(x=None), 1, b"x is NULL"),
