@@ -336,7 +336,6 @@ def calibration_copy(dev) -> None:
 
 
 PREFILL_ATTN_SOURCES = ["kv_block_selection_amd/csrc/attn_prefill.hip", "kv_block_selection_amd/csrc/lds_dma.h",
-                        "kv_block_selection_amd/csrc/launch.h",
                         "kv_block_selection_amd/csrc/common.h"]
 
 LAYER_SOURCES = ["kv_block_selection_amd/csrc/attn_decode.hip", "kv_block_selection_amd/csrc/topk_row.h",
