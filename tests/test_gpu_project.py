@@ -54,7 +54,7 @@ def _case(gpu, w, B, D, n_f, sentinel=False):
 
 
 @pytest.mark.parametrize("B,D,n_f", [(16, wl.MODEL_DIM, 1), (64, wl.MODEL_DIM, 2), (3, 512, 0), (70, 1024, 1),
-                                     (17, 2048, 1)])
+                                     (17, 2048, 1), (40, 1536, 1), (33, 512, 1)])
 def test_projection_parity(gpu, B, D, n_f):
     say("project_qkvf B", B, "D", D, "n_f", n_f)
     worst = _case(gpu, wl.C3_DECODE_128K, B, D, n_f)
