@@ -35,7 +35,7 @@ namespace sparda {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kProjChunk = 128;   // columns per chunk: 256 bytes of a row
-constexpr int kProjMaxTiles = 4;  // 16-sequence tiles per workgroup
+constexpr int kProjMaxTiles = 4;  // 16-sequence tiles per workgroup, at most
 
 // MT sequence tiles; DEPTH chunk buffers in LDS. A chunk buffer holds ROWS + 16 MT
 // rows of 256 bytes (W's rows, then the sequences'), granule q of row r at
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void qkvf_kernel(const uint8_t* __restrict__ x
   const int r16 = lane & 15;  // row of W (A) and sequence of the tile (B)
   const int g = lane >> 4;    // column group
   const long n0 = (long)blockIdx.x * ROWS;
-  const int b0 = blockIdx.y * (16 * kProjMaxTiles);
+  const int b0 = blockIdx.y * (16 * MT);
   const uint8_t* wbase = w + n0 * D * 2;
   const uint8_t* xbase = x + (long)b0 * D * 2;
 
@@ -183,13 +183,13 @@ hipError_t launch_project_qkvf(const void* x, const void* w, void* q, void* k, v
                                int Hkv, int n_f, hipStream_t s) {
   const long rows = (long)(Hq + 2 * Hkv + n_f * Hkv) * kHeadDim;
   const int tiles = (B + 15) / 16;
-  const int by = (B + 16 * kProjMaxTiles - 1) / (16 * kProjMaxTiles);
   // 32 rows of W per workgroup and 5 or 4 chunk buffers (60 to 96 KiB of LDS):
   // at B = 16 and 64, 13.0 and 18.1 us against 13.8 and 18.7 with 10 to 6
   // buffers, 13.1 and 18.8 with 4 and 3, 14.0 and 22.1 with 16 rows and 15.7
   // and 22.2 with 64 rows per workgroup
 #define SPARDA_PROJ(R, MT, DEPTH)                                                                                \
-  hipLaunchKernelGGL((qkvf_kernel<R, MT, DEPTH>), dim3((unsigned)(rows / R), by), dim3(256), 0, s,               \
+  hipLaunchKernelGGL((qkvf_kernel<R, MT, DEPTH>), dim3((unsigned)(rows / R), (B + 16 * MT - 1) / (16 * MT)),   \
+                     dim3(256), 0, s,                                                                            \
                      (const uint8_t*)x, (const uint8_t*)w, (uint8_t*)q, (uint8_t*)k, (uint8_t*)v, (uint8_t*)f, B, \
                      D, Hq, Hkv)
   if (tiles <= 1) SPARDA_PROJ(32, 1, 5);
