@@ -306,29 +306,38 @@ __global__ __launch_bounds__(256) void mhsel_pool_kernel(MhWs ws, float* __restr
     if (t + 256 * i < nwin && w >= 0 && w < n_vis) rec[i] = src[w];
   }
   // each head's max M and sum Z over the row's chunks (one wave per head),
-  // then the weight exp(chunk max - M) / Z of the chunks these windows meet
+  // then the weight exp(chunk max - M) / Z of the chunks these windows meet.
+  // A lane's statistics (kHeld chunks, rows of up to 64 kHeld chunks) and the
+  // chunk max its weight needs are all loaded at once, so the max, the sum and
+  // the weights cost one memory round trip; longer rows read the rest twice.
   {
+    constexpr int kHeld = 4;
     const int lane = t % kWave;
+    const float2* st_row = ws.stats + row * chunks * G;
     for (int g = t / kWave; g < G; g += 256 / kWave) {
+      const float mc = lane < NCH && c0 + lane < chunks ? st_row[(c0 + lane) * G + g].x : -INFINITY;
+      float2 st[kHeld];
+#pragma unroll
+      for (int j = 0; j < kHeld; ++j) {
+        const int cc = lane + kWave * j;
+        st[j] = cc < chunks ? st_row[cc * G + g] : make_float2(-INFINITY, 0.f);
+      }
       float mx = -INFINITY;
-      for (int cc = lane; cc < chunks; cc += kWave) mx = fmaxf(mx, ws.stats[(row * chunks + cc) * G + g].x);
+#pragma unroll
+      for (int j = 0; j < kHeld; ++j) mx = fmaxf(mx, st[j].x);
+      for (int cc = lane + kWave * kHeld; cc < chunks; cc += kWave) mx = fmaxf(mx, st_row[cc * G + g].x);
       mx = wave_max(mx);
       float z = 0.f;
-      for (int cc = lane; cc < chunks; cc += kWave) {
-        const float2 st = ws.stats[(row * chunks + cc) * G + g];
-        if (st.x != -INFINITY) z += st.y * fast_exp(st.x - mx);
+#pragma unroll
+      for (int j = 0; j < kHeld; ++j)
+        if (st[j].x != -INFINITY) z += st[j].y * fast_exp(st[j].x - mx);
+      for (int cc = lane + kWave * kHeld; cc < chunks; cc += kWave) {
+        const float2 sc = st_row[cc * G + g];
+        if (sc.x != -INFINITY) z += sc.y * fast_exp(sc.x - mx);
       }
       z = wave_sum(z);
       const float iz = 1.f / z;
-      if (lane < NCH) {
-        const int cc = c0 + lane;
-        float wt = 0.f;
-        if (cc < chunks) {
-          const float mc = ws.stats[(row * chunks + cc) * G + g].x;
-          if (mc != -INFINITY) wt = fast_exp(mc - mx) * iz;
-        }
-        s_wt[lane][g] = wt;
-      }
+      if (lane < NCH) s_wt[lane][g] = mc != -INFINITY ? fast_exp(mc - mx) * iz : 0.f;
     }
   }
   __syncthreads();
